@@ -1,0 +1,190 @@
+/*
+ * coll.h - collective communication primitives over p logical ranks whose
+ * buffers all live in one MI355X's HBM.
+ *
+ * Each call carries all p ranks at once: rank r is index r of the pointer
+ * arrays, so the communicator of the pages reduces to (p, ordered pointer
+ * arrays) and rank order is array order.  Semantics follow
+ *   [A] "集合通信：原语、算法、NCCL 实现与拓扑映射" (llm-infra-atlas, hpc/04):
+ *       notation p, [n], elementwise + in {sum,min,max} (chapter preamble);
+ *       primitive table (section 0); sections 1.1-1.6; ring all-reduce 2.2;
+ *       bus-bandwidth factors 2.5.
+ *   [B] "Collective Communication：AllReduce、AllGather、ReduceScatter 与
+ *       All-to-All" (charlestar.github.io): ragged All-to-All; CUDA-stream
+ *       semantics ("API return is not completion"); in-place offset rules;
+ *       failure semantics (a collective is not a transaction).
+ *
+ * Common contract
+ * ---------------
+ * - Arguments typed `const void* const*` / `void* const*` are HOST arrays
+ *   of length p holding DEVICE pointers; index = rank.  The caller owns
+ *   every device buffer; the library neither allocates nor frees them.
+ * - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *   validates on the host and enqueues kernels; it returns before the work
+ *   is done.  Results may be read after the stream is synchronised or
+ *   after an event recorded on it has completed ([B], CUDA Stream).
+ * - Validation is synchronous and complete before anything is enqueued; a
+ *   call that returns an error has enqueued nothing.  n == 0 is a no-op
+ *   returning COLL_OK (pointers are then not inspected).
+ * - Pointers need no particular alignment beyond the element size; 16-byte
+ *   aligned buffers take the vector path.
+ * - Aliasing: the output ranges must be pairwise disjoint and may not
+ *   overlap any input range, except the in-place forms listed with each
+ *   call ([B], In-place).  Input ranges may overlap each other.  A
+ *   violation returns COLL_ERR_ALIAS.
+ * - Errors are not transactional ([B], failure semantics): if the device
+ *   faults mid-call, outputs may be partially written.
+ * - Calls that run concurrently on different streams over the same buffers
+ *   race; ordering is the caller's (stream order or events).
+ * - Thread safety: every entry point may be called from several host
+ *   threads, except coll_finalize, which must not run concurrently with
+ *   any other call.
+ */
+#ifndef COLL_H_
+#define COLL_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types.  bf16 is reduced in fp32 and narrowed once with
+ * round-to-nearest-even. */
+typedef enum { COLL_F32 = 0, COLL_BF16 = 1, COLL_I32 = 2 } coll_dtype_t;
+
+/* Elementwise reduction ([A] preamble: + is sum, min or max). */
+typedef enum { COLL_SUM = 0, COLL_MIN = 1, COLL_MAX = 2 } coll_op_t;
+
+typedef enum {
+  COLL_OK = 0,
+  COLL_ERR_INVALID_ARG = 1,  /* bad p, null pointer, bad enum, root out of range, size overflow */
+  COLL_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement */
+  COLL_ERR_ALIAS = 3,        /* illegal overlap between buffers */
+  COLL_ERR_HIP = 4           /* the HIP runtime reported an error; see coll_last_hip_error */
+} coll_status_t;
+
+/* AllReduce schedules ([A] 2.2 ring; 2.3 table of algorithms).
+ * RING: each chunk c of q = ceil(n/p) elements is folded in the ring
+ *   order x_{c+1}, x_{c+2}, ..., x_c (indices mod p) with the partial kept
+ *   on chip across the p-1 combine steps, then stored to all p outputs in
+ *   the same pass (reduce-scatter and all-gather fused).  Bit-exact with
+ *   the ring all-reduce of [A] 2.2 read with chunk c ending on rank c.
+ * ONEPASS: all p inputs read at once and summed as a balanced pairwise
+ *   tree in rank order (another correct summation order, [B] numerics);
+ *   fp32/bf16 sum only differs from RING in rounding.  p in {2,4,8,16}.
+ * RING_LITERAL: the 2(p-1) neighbour steps of [A] 2.2 run one step per
+ *   kernel launch through HBM, partials stored in the receive buffers.
+ *   Bit-exact with RING.  fp32 and int32 only. */
+typedef enum {
+  COLL_ALGO_RING = 0,
+  COLL_ALGO_ONEPASS = 1,
+  COLL_ALGO_RING_LITERAL = 2
+} coll_algo_t;
+
+#define COLL_MAX_RANKS 64
+
+/* AllReduce ([A] 1.4, [B] AllReduce): recv[r][i] = (+)_{r'} send[r'][i]
+ * for every rank r and i < n.  Same as coll_allreduce_algo with
+ * COLL_ALGO_RING.  send[r], recv[r]: n elements each.
+ * In place: recv[r] == send[r]. */
+coll_status_t coll_allreduce(const void* const* send, void* const* recv, int p, size_t n,
+                             coll_dtype_t dtype, coll_op_t op, void* stream);
+
+/* AllReduce with an explicit schedule (see coll_algo_t). */
+coll_status_t coll_allreduce_algo(const void* const* send, void* const* recv, int p, size_t n,
+                                  coll_dtype_t dtype, coll_op_t op, coll_algo_t algo,
+                                  void* stream);
+
+/* Reduce ([A] 1.3 with its worked example): recv_root[i] = (+)_r send[r][i];
+ * only the root's buffer is written.  Same summation order as
+ * coll_allreduce, so Reduce then Broadcast equals AllReduce bit for bit.
+ * root in [0, p) is a rank index.  In place: recv_root == send[root]. */
+coll_status_t coll_reduce(const void* const* send, void* recv_root, int p, size_t n,
+                          coll_dtype_t dtype, coll_op_t op, int root, void* stream);
+
+/* Broadcast ([A] 1.1): recv[r][i] = send_root[i] for every r, i < n.
+ * root in [0, p).  In place: recv[root] == send_root. */
+coll_status_t coll_broadcast(const void* send_root, void* const* recv, int p, size_t n,
+                             coll_dtype_t dtype, int root, void* stream);
+
+/* ReduceScatter ([A] 1.5): send[r] holds p*n elements, recv[r] holds n;
+ * recv[r][j] = (+)_k send[k][r*n + j], block r folded in the ring order
+ * x_{r+1}, ..., x_r.  In place: recv[r] == send[r] + r*n elements. */
+coll_status_t coll_reduce_scatter(const void* const* send, void* const* recv, int p, size_t n,
+                                  coll_dtype_t dtype, coll_op_t op, void* stream);
+
+/* AllGather ([A] 1.2): send[s] holds n elements, recv[r] holds p*n;
+ * recv[r][s*n + j] = send[s][j] (rank-order concatenation).
+ * In place: send[r] == recv[r] + r*n elements. */
+coll_status_t coll_allgather(const void* const* send, void* const* recv, int p, size_t n,
+                             coll_dtype_t dtype, void* stream);
+
+/* All-to-All, equal split ([A] 1.6): send[i] and recv[j] hold p blocks of
+ * n_block elements; recv[j][i*n_block + k] = send[i][j*n_block + k], the
+ * transpose of the p x p block matrix.  No in-place form. */
+coll_status_t coll_alltoall(const void* const* send, void* const* recv, int p, size_t n_block,
+                            coll_dtype_t dtype, void* stream);
+
+/* Variable-split All-to-All ([B] Ragged All-to-All).
+ * counts_dev: DEVICE array of p*p int64, row-major, counts[i*p + j] =
+ *   elements source i sends to destination j (as produced on the device by
+ *   a router).  Send offsets are the exclusive prefix sums along row i;
+ *   recv[j] receives the blocks of sources 0..p-1 packed in source order.
+ * send_cap, recv_cap: HOST arrays of p int64, the capacity in elements of
+ *   send[i] and recv[j].  The kernel checks on the device that every count
+ *   is >= 0, that row sums fit send_cap and column sums fit recv_cap; if
+ *   not it writes no payload at all.
+ * status_dev: optional DEVICE int32 (may be NULL).  The kernel stores 0 on
+ *   success or COLL_ERR_INVALID_ARG when the counts were rejected.
+ * No in-place form; the counts array may not overlap any recv buffer. */
+coll_status_t coll_alltoallv(const void* const* send, void* const* recv, int p,
+                             const int64_t* counts_dev, const int64_t* send_cap,
+                             const int64_t* recv_cap, int32_t* status_dev,
+                             coll_dtype_t dtype, void* stream);
+
+/* One AllReduce of a batch (host-side view). */
+typedef struct {
+  const void* const* send;  /* host array of p device pointers */
+  void* const* recv;        /* host array of p device pointers */
+  size_t n;                 /* elements per rank */
+  coll_dtype_t dtype;
+  coll_op_t op;
+} coll_call_t;
+
+/* Flags for coll_allreduce_batch. */
+#define COLL_BATCH_CHECK_ALIAS 1u  /* also reject overlaps between calls (O(m log m) host work) */
+
+/* Batched AllReduce ([B] group calls; [A] 4.2 bucketing/fusion): ncalls
+ * independent AllReduces over the same p, enqueued as one kernel launch so
+ * that the fixed per-call cost is paid once.  Each call has the semantics
+ * and summation order of coll_allreduce; calls may mix dtypes and ops.
+ * Within a call the coll_allreduce aliasing rules always apply; overlaps
+ * between calls are checked only with COLL_BATCH_CHECK_ALIAS (otherwise
+ * overlapping calls race).  The library copies the descriptors into a
+ * device buffer it owns (grown on demand, released by coll_finalize); a
+ * call waits on the host for the previous batch's kernel to finish before
+ * reusing that buffer. */
+coll_status_t coll_allreduce_batch(const coll_call_t* calls, int ncalls, int p,
+                                   unsigned flags, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* coll_status_string(coll_status_t status);
+
+/* The last hipError_t recorded by a call on this host thread that
+ * returned COLL_ERR_HIP (0 if none). */
+int coll_last_hip_error(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int coll_version(void);
+
+/* Release library-owned device and pinned host memory (batch descriptors).
+ * Synchronises on the work that used them. */
+void coll_finalize(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* COLL_H_ */

@@ -1,0 +1,274 @@
+"""CPU oracle for the collective primitives.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports this file:
+only the tests, the smoke check and the benchmark's CPU-baseline leg do.
+It shares no code with the HIP path; the two meet only at the seeded input
+generators, which hold none of the arithmetic below.
+
+Everything here is plain NumPy, written to be checked by eye against the
+definitions on the pages it follows:
+
+* "集合通信：原语、算法、NCCL 实现与拓扑映射" (llm-infra-atlas, hpc/04):
+  notation p, [n], elementwise + in {sum, min, max} (chapter preamble);
+  primitive table (section 0); Broadcast 1.1, AllGather 1.2, Reduce 1.3
+  with its worked example, AllReduce 1.4, ReduceScatter 1.5, AllToAll 1.6,
+  the forward/backward duality table 1.7; ring all-reduce 2.2.
+* "Collective Communication：AllReduce、AllGather、ReduceScatter 与 All-to-All"
+  (charlestar.github.io): ragged All-to-All (counts c_ij, prefix-sum
+  offsets), B convention for volumes, numerics of reduction order.
+
+Readings taken where the pages are silent or inconsistent:
+
+1. Ring order.  The p=4 ring trace in section 2.2 of the hpc/04 page
+   contradicts itself about which chunk a rank sends first.  The reading
+   used: chunk c starts at rank c+1 and its partial travels c+1, c+2, ...,
+   ending on rank c, so that ReduceScatter's block c ends on rank c as
+   section 1.5 requires.  Element i of chunk c is therefore reduced in the
+   order x_{c+1}, x_{c+2}, ..., x_{c+p-1}, x_c (indices mod p), left fold.
+2. Chunking when p does not divide n: q = ceil(n/p), chunk(i) = i // q;
+   trailing chunks may be short or empty.
+3. bf16: widen exactly to fp32, fold in fp32 (IEEE add, round to nearest
+   even), narrow once with round-to-nearest-even.
+4. min/max: compare-select, acc = v if v < acc (min) / v > acc (max), in
+   fp32 for bf16.  int32 sum wraps modulo 2^32.
+5. Reduce uses the AllReduce chunking, so Reduce then Broadcast equals
+   AllReduce bit for bit.
+6. Alltoallv: recv counts are the columns of the send-count matrix; the
+   receive buffer of rank j holds the blocks from sources 0..p-1 in source
+   order, packed.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+SUM, MIN, MAX = 0, 1, 2
+F32, BF16, I32 = 0, 1, 2
+
+
+# ----------------------------------------------------------------------------
+# bf16 <-> fp32 (IEEE-754 binary16-brain: sign, 8-bit exponent, 7-bit fraction)
+# ----------------------------------------------------------------------------
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening: the bf16 pattern is the upper half of the fp32 pattern."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def f32_to_bf16_rne(x: np.ndarray) -> np.ndarray:
+    """Narrow fp32 to bf16 with round-to-nearest, ties-to-even.
+
+    The kept part is the upper 16 bits of the fp32 pattern; the dropped
+    part is the lower 16 bits.  Round up when the dropped part exceeds half
+    an ulp (0x8000), or equals it and the kept part is odd.  Carry out of
+    the fraction moves into the exponent, which gives the right result up
+    to and including overflow to infinity.  NaN maps to a quiet NaN with
+    the same sign.
+    """
+    u = np.asarray(x, dtype=np.float32).view(np.uint32)
+    kept = u >> np.uint32(16)
+    dropped = u & np.uint32(0xFFFF)
+    up = (dropped > 0x8000) | ((dropped == 0x8000) & ((kept & np.uint32(1)) == 1))
+    out = (kept + up.astype(np.uint32)).astype(np.uint32)
+    nan = np.isnan(np.asarray(x, dtype=np.float32))
+    out = np.where(nan, (kept & np.uint32(0x8000)) | np.uint32(0x7FC0), out)
+    return out.astype(np.uint16)
+
+
+# ----------------------------------------------------------------------------
+# The reduction: a left fold in a given rank order
+# ----------------------------------------------------------------------------
+
+def ring_order(c: int, p: int) -> list[int]:
+    """Ranks visited by chunk c's partial: c+1, c+2, ..., c (mod p)."""
+    return [(c + k) % p for k in range(1, p + 1)]
+
+
+def _widen(v: np.ndarray, dtype: int) -> np.ndarray:
+    if dtype == BF16:
+        return bf16_to_f32(v)
+    if dtype == F32:
+        return np.asarray(v, dtype=np.float32)
+    if dtype == I32:
+        return np.asarray(v, dtype=np.int32)
+    raise ValueError(dtype)
+
+
+def _combine(acc: np.ndarray, v: np.ndarray, op: int) -> np.ndarray:
+    if op == SUM:
+        with np.errstate(over="ignore"):
+            return acc + v          # fp32 IEEE add (RNE) / int32 add mod 2^32
+    if op == MIN:
+        return np.where(v < acc, v, acc)
+    if op == MAX:
+        return np.where(v > acc, v, acc)
+    raise ValueError(op)
+
+
+def fold(vals_in_order: list[np.ndarray], op: int, dtype: int) -> np.ndarray:
+    """acc = v0; acc = acc (+) v1; ...; then narrow once for bf16."""
+    acc = _widen(vals_in_order[0], dtype).copy()
+    for v in vals_in_order[1:]:
+        acc = _combine(acc, _widen(v, dtype), op)
+    if dtype == BF16:
+        return f32_to_bf16_rne(acc)
+    return acc
+
+
+def reduce_elements(cols: np.ndarray, chunk: np.ndarray, op: int, dtype: int) -> np.ndarray:
+    """Reduce selected elements.
+
+    cols[r, e] is rank r's value of element e; chunk[e] is the chunk that
+    element belongs to.  Element e is folded in ring_order(chunk[e], p).
+    Used both for whole buffers and for sampled elements of large ones.
+    """
+    cols = np.asarray(cols)
+    p, m = cols.shape
+    chunk = np.asarray(chunk, dtype=np.int64)
+    e = np.arange(m)
+    ordered = [cols[(chunk + k) % p, e] for k in range(1, p + 1)]
+    return fold(ordered, op, dtype)
+
+
+def chunk_len(n: int, p: int) -> int:
+    """q = ceil(n / p) elements per chunk."""
+    return -(-n // p) if n > 0 else 0
+
+
+def chunk_of(idx: np.ndarray, n: int, p: int) -> np.ndarray:
+    q = chunk_len(n, p)
+    return np.asarray(idx, dtype=np.int64) // max(q, 1)
+
+
+# ----------------------------------------------------------------------------
+# The primitives (section 0 primitive table of the hpc/04 page)
+# ----------------------------------------------------------------------------
+
+def allreduce(xs: list[np.ndarray], op: int, dtype: int) -> list[np.ndarray]:
+    """out_r[i] = (+)_{r'} x_{r'}[i] on every rank r (section 1.4)."""
+    p = len(xs)
+    n = len(xs[0])
+    if n == 0:
+        return [xs[0][:0].copy() for _ in range(p)]
+    res = reduce_elements(np.stack(xs), chunk_of(np.arange(n), n, p), op, dtype)
+    return [res.copy() for _ in range(p)]
+
+
+def reduce(xs: list[np.ndarray], op: int, dtype: int, root: int) -> np.ndarray:
+    """Only the root receives (+)_r x_r (section 1.3).  Same order as allreduce."""
+    assert 0 <= root < len(xs)
+    return allreduce(xs, op, dtype)[root]
+
+
+def broadcast(x_root: np.ndarray, p: int) -> list[np.ndarray]:
+    """Every rank receives the root's [n] (section 1.1)."""
+    return [np.array(x_root, copy=True) for _ in range(p)]
+
+
+def reduce_scatter(xs: list[np.ndarray], op: int, dtype: int) -> list[np.ndarray]:
+    """Each rank holds [p*n]; rank r keeps block r of the reduction (section 1.5).
+
+    Block r is reduced in ring_order(r, p).
+    """
+    p = len(xs)
+    total = len(xs[0])
+    assert total % p == 0
+    n = total // p
+    out = []
+    for r in range(p):
+        blk = [xs[k][r * n:(r + 1) * n] for k in ring_order(r, p)]
+        out.append(fold(blk, op, dtype) if n > 0 else xs[0][:0].copy())
+    return out
+
+
+def allgather(xs: list[np.ndarray]) -> list[np.ndarray]:
+    """Every rank receives [x_0 | x_1 | ... | x_{p-1}] in rank order (section 1.2)."""
+    cat = np.concatenate(xs)
+    return [cat.copy() for _ in xs]
+
+
+def alltoall(xs: list[np.ndarray]) -> list[np.ndarray]:
+    """recv[j] block i = send[i] block j: a transpose of the block matrix (section 1.6)."""
+    p = len(xs)
+    m = len(xs[0]) // p
+    return [np.concatenate([xs[i][j * m:(j + 1) * m] for i in range(p)]) for j in range(p)]
+
+
+def alltoallv(xs: list[np.ndarray], counts: np.ndarray) -> list[np.ndarray]:
+    """Variable-split All-to-All.
+
+    counts[i][j] elements go from source i to destination j.  Send offsets
+    are the exclusive prefix sums along each row; destination j packs the
+    blocks from sources 0..p-1 in source order.
+    """
+    counts = np.asarray(counts, dtype=np.int64)
+    p = len(xs)
+    send_off = np.zeros((p, p), dtype=np.int64)
+    for i in range(p):
+        for j in range(1, p):
+            send_off[i, j] = send_off[i, j - 1] + counts[i, j - 1]
+    out = []
+    for j in range(p):
+        parts = [xs[i][send_off[i, j]:send_off[i, j] + counts[i, j]] for i in range(p)]
+        out.append(np.concatenate(parts) if parts else xs[0][:0].copy())
+    return out
+
+
+def alltoallv_recv_counts(counts: np.ndarray) -> np.ndarray:
+    """Elements each destination receives: the column sums of the count matrix."""
+    return np.asarray(counts, dtype=np.int64).sum(axis=0)
+
+
+# ----------------------------------------------------------------------------
+# The ring all-reduce of section 2.2, simulated step by step
+# ----------------------------------------------------------------------------
+
+def ring_allreduce_simulated(xs: list[np.ndarray], op: int, dtype: int,
+                             return_after_rs: bool = False):
+    """2(p-1) neighbour steps over per-rank buffers.
+
+    Each rank's buffer is cut into p chunks of q = ceil(n/p) elements.
+    Reduce-scatter phase, step s = 1..p-1: every rank X sends its current
+    copy of chunk (X - s) mod p to rank X+1, which combines it with its own
+    copy (received partial on the left).  All-gather phase, step t =
+    1..p-1: every rank X sends chunk (X + 1 - t) mod p, which it holds in
+    final form, to rank X+1, which stores it.  Sends of a step read the
+    buffers as they were before that step.
+
+    Partials stay in fp32 for bf16 and are narrowed once at the end.
+    With return_after_rs the per-rank buffers after the first phase are
+    returned (widened), so tests can check where each reduced chunk lands.
+    """
+    p = len(xs)
+    n = len(xs[0])
+    q = chunk_len(n, p)
+    buf = [_widen(x, dtype).copy() for x in xs]
+
+    def sl(c):
+        return slice(min(c * q, n), min((c + 1) * q, n))
+
+    for s in range(1, p):
+        snap = [b.copy() for b in buf]
+        for x in range(p):
+            c = (x - s) % p
+            dst = (x + 1) % p
+            buf[dst][sl(c)] = _combine(snap[x][sl(c)], buf[dst][sl(c)], op)
+    if return_after_rs:
+        return buf
+    for t in range(1, p):
+        snap = [b.copy() for b in buf]
+        for x in range(p):
+            c = (x + 1 - t) % p
+            dst = (x + 1) % p
+            buf[dst][sl(c)] = snap[x][sl(c)]
+    if dtype == BF16:
+        return [f32_to_bf16_rne(b) for b in buf]
+    return buf
+
+
+# ----------------------------------------------------------------------------
+# Batched small AllReduce: each call independently
+# ----------------------------------------------------------------------------
+
+def allreduce_batch(calls: list[tuple[list[np.ndarray], int, int]]) -> list[np.ndarray]:
+    """calls: (per-rank inputs, op, dtype).  Returns the reduced vector per call."""
+    return [allreduce(xs, op, dt)[0] for xs, op, dt in calls]

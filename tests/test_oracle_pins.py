@@ -1,0 +1,475 @@
+"""Pins for the CPU oracle: values the pages print, closed forms, invariants
+and brute force on tiny inputs.  Each test is chosen so that a plausible
+mistake in the oracle (a dropped rank, a wrong rotation, a transposed
+block, a bad rounding rule) fails it.  No value here comes from the GPU.
+"""
+import itertools
+import math
+import struct
+
+import numpy as np
+import pytest
+
+from conftest import read_golden
+from oracle import ref
+from collective_communication_primitives_coll_amd import inputs, metrics
+
+OPS = (ref.SUM, ref.MIN, ref.MAX)
+DTYPES = (ref.F32, ref.BF16, ref.I32)
+
+
+def _as_dtype(int_vals, dtype):
+    a = np.asarray(int_vals, dtype=np.int64)
+    if dtype == ref.I32:
+        return a.astype(np.int32)
+    if dtype == ref.F32:
+        return a.astype(np.float32)
+    # small integers are exact in bf16: take the upper half of the fp32 bits
+    return (a.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _to_float(vals, dtype):
+    if dtype == ref.BF16:
+        return ref.bf16_to_f32(vals).astype(np.float64)
+    return np.asarray(vals).astype(np.float64)
+
+
+def _bits(a):
+    a = np.asarray(a)
+    return a.view(np.uint32) if a.dtype == np.float32 else a
+
+
+# ----------------------------------------------------------------------------
+# The pages' worked example (hpc/04 sections 1.3 and 1.4)
+# ----------------------------------------------------------------------------
+
+def _worked_example():
+    rows = read_golden("reduce_worked_example.txt")
+    xs = [[int(v) for v in r[2:]] for r in rows if r[0] == "in"]
+    out = [int(v) for r in rows if r[0] == "out" for v in r[2:]]
+    return xs, out
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_worked_example_sum(dtype):
+    xs, expect = _worked_example()
+    arrs = [_as_dtype(x, dtype) for x in xs]
+    for r_out in ref.allreduce(arrs, ref.SUM, dtype):
+        assert list(_to_float(r_out, dtype)) == expect
+    for root in range(len(xs)):
+        assert list(_to_float(ref.reduce(arrs, ref.SUM, dtype, root), dtype)) == expect
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_worked_example_min_max(dtype):
+    # Derived from the same inputs with the definition of min / max.
+    xs, _ = _worked_example()
+    arrs = [_as_dtype(x, dtype) for x in xs]
+    assert list(_to_float(ref.allreduce(arrs, ref.MIN, dtype)[0], dtype)) == [0, 1]
+    assert list(_to_float(ref.allreduce(arrs, ref.MAX, dtype)[0], dtype)) == [6, 7]
+
+
+# ----------------------------------------------------------------------------
+# Brute force over every small integer input (order-independent ops)
+# ----------------------------------------------------------------------------
+
+def _py_reduce(vals, op):
+    return {ref.SUM: sum, ref.MIN: min, ref.MAX: max}[op](vals)
+
+
+@pytest.mark.parametrize("p,n", [(1, 1), (1, 2), (2, 1), (2, 2), (3, 1), (3, 2), (4, 1), (4, 2)])
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_bruteforce_all_small_inputs(p, n, dtype):
+    """Every input in {-2..2}^(p*n): reduce_elements against Python's
+    sum/min/max, plus allreduce() on a sample of the cases."""
+    vals = np.array(list(itertools.product(range(-2, 3), repeat=p * n)), dtype=np.int64)  # cases x (p*n)
+    cases = vals.shape[0]
+    per_rank = vals.reshape(cases, p, n)                       # case, rank, elem
+    cols = per_rank.transpose(1, 0, 2).reshape(p, cases * n)   # rank, (case, elem)
+    chunk = ref.chunk_of(np.tile(np.arange(n), cases), n, p)
+    for op in OPS:
+        got = _to_float(ref.reduce_elements(_as_dtype(cols, dtype), chunk, op, dtype), dtype)
+        expect = [_py_reduce(list(cols[:, e]), op) for e in range(cols.shape[1])]
+        assert got.tolist() == expect
+    rng = np.random.default_rng(p * 10 + n)
+    for case in rng.choice(cases, size=min(cases, 300), replace=False):
+        xs = [_as_dtype(per_rank[case, r], dtype) for r in range(p)]
+        for op in OPS:
+            expect = [_py_reduce(list(per_rank[case, :, e]), op) for e in range(n)]
+            for out in ref.allreduce(xs, op, dtype):
+                assert _to_float(out, dtype).tolist() == expect
+
+
+# ----------------------------------------------------------------------------
+# Order-dependent fp32 / bf16 sums: pure-Python fold with exact rounding
+# ----------------------------------------------------------------------------
+
+def _f32(x: float) -> float:
+    """Round a Python float (binary64) to binary32, nearest-even."""
+    return struct.unpack("<f", struct.pack("<f", x))[0]
+
+
+def _py_add_f32(a: float, b: float) -> float:
+    # a + b is exact or correctly rounded in binary64; rounding that to
+    # binary32 equals one correct rounding of the exact sum because 53 >=
+    # 2*24 + 2 (double rounding is innocuous for +).
+    return _f32(a + b)
+
+
+def _py_bf16_rne(x: float) -> float:
+    """Nearest bf16 to the binary32 value x, ties to the even pattern,
+    found by comparing distances to the two bf16 neighbours."""
+    if x == 0.0 or math.isinf(x):
+        return x
+    bits = struct.unpack("<I", struct.pack("<f", x))[0]
+    lo_bits = bits & 0xFFFF0000
+    hi_bits = lo_bits + 0x10000
+    lo = struct.unpack("<f", struct.pack("<I", lo_bits))[0]
+    # the next bf16 away from zero; past the largest finite value it is inf
+    hi = struct.unpack("<f", struct.pack("<I", hi_bits & 0xFFFFFFFF))[0]
+    dlo, dhi = abs(x - lo), abs(hi - x)
+    if dlo < dhi:
+        return lo
+    if dhi < dlo:
+        return hi
+    return lo if ((lo_bits >> 16) & 1) == 0 else hi
+
+
+def _py_ring_fold(vals_by_rank, c, dtype):
+    p = len(vals_by_rank)
+    order = [(c + k) % p for k in range(1, p + 1)]
+    acc = vals_by_rank[order[0]]
+    for r in order[1:]:
+        acc = _py_add_f32(acc, vals_by_rank[r])
+    return _py_bf16_rne(acc) if dtype == ref.BF16 else acc
+
+
+@pytest.mark.parametrize("dtype", [ref.F32, ref.BF16])
+def test_fp_sum_order_against_pure_python(dtype):
+    rng = np.random.default_rng(1234)
+    for trial in range(60):
+        p = int(rng.integers(1, 7))
+        n = int(rng.integers(1, 12))
+        scale = float(10.0 ** rng.integers(-3, 4))
+        xs = [(rng.standard_normal(n) * scale).astype(np.float32) for _ in range(p)]
+        if dtype == ref.BF16:
+            xs = [(x.view(np.uint32) >> 16).astype(np.uint16) for x in xs]
+        got = _to_float(ref.allreduce(xs, ref.SUM, dtype)[0], dtype)
+        q = -(-n // p)
+        widened = [_to_float(x, dtype) for x in xs]
+        for i in range(n):
+            expect = _py_ring_fold([float(w[i]) for w in widened], i // q, dtype)
+            assert got[i] == expect, (trial, p, n, i)
+
+
+def test_fp_sum_order_matters_here():
+    """Guard for the previous test: the chosen data does distinguish orders."""
+    rng = np.random.default_rng(5)
+    xs = [rng.standard_normal(4096).astype(np.float32) for _ in range(8)]
+    ring = ref.allreduce(xs, ref.SUM, ref.F32)[0]
+    natural = xs[0].copy()
+    for x in xs[1:]:
+        natural = natural + x
+    assert not np.array_equal(ring.view(np.uint32), natural.view(np.uint32))
+
+
+def test_bf16_rne_pins():
+    one = 1.0
+    cases = [  # (fp32 value, bf16 pattern); a list because 0.0 == -0.0 as dict keys
+        (one, 0x3F80),
+        (one + 2.0 ** -8, 0x3F80),                # exact tie, even kept part
+        (one + 3 * 2.0 ** -8, 0x3F82),            # exact tie, odd kept part rounds up
+        (one + 2.0 ** -8 + 2.0 ** -20, 0x3F81),   # just above the tie
+        (one + 2.0 ** -9, 0x3F80),                # below the tie
+        (-(one + 3 * 2.0 ** -8), 0xBF82),
+        (float.fromhex("0x1.fffffep127"), 0x7F80),  # largest fp32 rounds to +inf
+        (float.fromhex("0x1.fefffep127"), 0x7F7F),
+        (0.0, 0x0000),
+        (-0.0, 0x8000),
+        (float("inf"), 0x7F80),
+        (2.0 ** -133, 0x0001),                    # smallest bf16 subnormal, exact
+        (2.0 ** -134, 0x0000),                    # half of it: tie, even kept part (zero)
+        (2.0 ** -134 + 2.0 ** -149, 0x0001),      # just above that tie
+        (2.0 ** -126, 0x0080),
+    ]
+    xs = np.array([c[0] for c in cases], dtype=np.float32)
+    got = ref.f32_to_bf16_rne(xs)
+    assert [int(g) for g in got] == [c[1] for c in cases]
+    nan = ref.f32_to_bf16_rne(np.array([np.nan, -np.nan], dtype=np.float32))
+    assert all((int(v) & 0x7F80) == 0x7F80 and (int(v) & 0x7F) != 0 for v in nan)
+
+
+def test_bf16_rne_against_pure_python_and_torch():
+    rng = np.random.default_rng(9)
+    base = rng.standard_normal(20000).astype(np.float32) * np.float32(1e3)
+    # add exact ties and near-ties
+    u = base.view(np.uint32)
+    ties = ((u & np.uint32(0xFFFF0000)) | np.uint32(0x8000)).view(np.float32)
+    near = ((u & np.uint32(0xFFFF0000)) | np.uint32(0x7FFF)).view(np.float32)
+    xs = np.concatenate([base, ties, near])
+    got = ref.f32_to_bf16_rne(xs)
+    py = np.array([_py_bf16_rne(float(v)) for v in xs[:3000]])
+    assert np.array_equal(ref.bf16_to_f32(got[:3000]).astype(np.float64), py)
+    torch = pytest.importorskip("torch")
+    tb = torch.from_numpy(xs.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, tb)
+
+
+# ----------------------------------------------------------------------------
+# The ring of section 2.2 simulated step by step == the closed-form order
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("op", OPS)
+def test_ring_simulator_equals_closed_form(dtype, op):
+    rng = np.random.default_rng(100 + dtype * 3 + op)
+    for p in range(1, 10):
+        for n in (1, p - 1 if p > 1 else 1, p, 2 * p + 1, 37, 64):
+            xs = inputs.rank_buffers(inputs.WL_TEST, p, n, dtype, dist="normal", extra=(p, n))
+            sim = ref.ring_allreduce_simulated(xs, op, dtype)
+            closed = ref.allreduce(xs, op, dtype)
+            for r in range(p):
+                assert np.array_equal(_bits(sim[r]), _bits(closed[r])), (p, n, r)
+
+
+def test_ring_reduce_scatter_phase_lands_chunk_c_on_rank_c():
+    """After the p-1 reduce-scatter steps, rank c holds chunk c fully
+    reduced (section 1.5 placement), checked with exact integer data."""
+    for p in (2, 3, 4, 5, 8):
+        n = 4 * p + (p // 2)
+        xs = inputs.rank_buffers(inputs.WL_TEST, p, n, ref.I32, extra=(7, p))
+        bufs = ref.ring_allreduce_simulated(xs, ref.SUM, ref.I32, return_after_rs=True)
+        total = np.sum(np.stack(xs).astype(np.int64), axis=0)
+        q = -(-n // p)
+        for c in range(p):
+            sl = slice(min(c * q, n), min((c + 1) * q, n))
+            assert np.array_equal(bufs[c][sl].astype(np.int64), total[sl])
+            # and no other rank holds it complete (p > 1 and values non-trivial)
+            if p > 2:
+                other = (c + 1) % p
+                assert not np.array_equal(bufs[other][sl].astype(np.int64), total[sl]) or sl.start == sl.stop
+
+
+def test_ring_message_count_and_volume():
+    """Section 2.2: 2(p-1) messages, 2n(p-1)/p bytes per rank (n bytes per rank)."""
+    for p in (2, 4, 8, 16):
+        n_bytes = 1024 * p
+        sends_per_rank = 2 * (p - 1)            # one chunk per step, 2(p-1) steps
+        assert sends_per_rank * (n_bytes // p) == 2 * n_bytes * (p - 1) // p
+
+
+# ----------------------------------------------------------------------------
+# Identities (section 0: AllReduce == Reduce then Broadcast ==
+# ReduceScatter then AllGather) and duality (section 1.7)
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("op", OPS)
+def test_identity_allreduce_is_rs_then_ag(dtype, op):
+    for p in (1, 2, 3, 4, 8):
+        nb = 5
+        xs = inputs.rank_buffers(inputs.WL_TEST, p, p * nb, dtype, dist="normal", extra=(11, p))
+        ar = ref.allreduce(xs, op, dtype)
+        ag = ref.allgather(ref.reduce_scatter(xs, op, dtype))
+        for r in range(p):
+            assert np.array_equal(_bits(ar[r]), _bits(ag[r]))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("op", OPS)
+def test_identity_allreduce_is_reduce_then_broadcast(dtype, op):
+    for p in (1, 2, 3, 5, 8):
+        n = 3 * p + 2
+        xs = inputs.rank_buffers(inputs.WL_TEST, p, n, dtype, dist="normal", extra=(12, p))
+        ar = ref.allreduce(xs, op, dtype)
+        for root in range(p):
+            bc = ref.broadcast(ref.reduce(xs, op, dtype, root), p)
+            for r in range(p):
+                assert np.array_equal(_bits(ar[r]), _bits(bc[r]))
+
+
+def test_duality_allgather_reduce_scatter_adjoint():
+    rng = np.random.default_rng(3)
+    for p in (1, 2, 3, 4, 8):
+        n = 6
+        x = [rng.integers(-50, 50, n).astype(np.int32) for _ in range(p)]
+        y = [rng.integers(-50, 50, p * n).astype(np.int32) for _ in range(p)]
+        lhs = sum(int(np.dot(a.astype(np.int64), b.astype(np.int64))) for a, b in zip(ref.allgather(x), y))
+        rs = ref.reduce_scatter(y, ref.SUM, ref.I32)
+        rhs = sum(int(np.dot(a.astype(np.int64), b.astype(np.int64))) for a, b in zip(x, rs))
+        assert lhs == rhs
+
+
+def test_duality_broadcast_reduce_adjoint():
+    rng = np.random.default_rng(4)
+    for p in (1, 2, 5, 8):
+        n = 7
+        x = rng.integers(-50, 50, n).astype(np.int32)
+        y = [rng.integers(-50, 50, n).astype(np.int32) for _ in range(p)]
+        lhs = sum(int(np.dot(a.astype(np.int64), b.astype(np.int64))) for a, b in zip(ref.broadcast(x, p), y))
+        for root in range(p):
+            red = ref.reduce(y, ref.SUM, ref.I32, root)
+            assert lhs == int(np.dot(x.astype(np.int64), red.astype(np.int64)))
+
+
+# ----------------------------------------------------------------------------
+# Symbolic layouts printed on the pages
+# ----------------------------------------------------------------------------
+
+def _symbol_codes(rows):
+    syms = sorted({s for r in rows if r[0] == "in" for s in r[2:]})
+    return {s: 1 << i for i, s in enumerate(syms)}
+
+
+def test_allgather_symbolic():
+    rows = read_golden("allgather_symbolic.txt")
+    code = _symbol_codes(rows)
+    xs = [np.array([code[s] for s in r[2:]], dtype=np.int32) for r in rows if r[0] == "in"]
+    expect = [code[s] for r in rows if r[0] == "out" for s in r[2:]]
+    for out in ref.allgather(xs):
+        assert out.tolist() == expect
+
+
+def test_reduce_scatter_symbolic():
+    rows = read_golden("reduce_scatter_symbolic.txt")
+    code = _symbol_codes(rows)
+    xs = [np.array([code[s] for s in r[2:]], dtype=np.int32) for r in rows if r[0] == "in"]
+    got = ref.reduce_scatter(xs, ref.SUM, ref.I32)
+    for r in rows:
+        if r[0] == "out":
+            expect = sum(code[s] for s in r[2].split("+"))
+            assert got[int(r[1])].tolist() == [expect]
+
+
+@pytest.mark.parametrize("name", ["alltoall_symbolic.txt", "alltoall_three_rank.txt"])
+def test_alltoall_symbolic(name):
+    rows = read_golden(name)
+    code = _symbol_codes(rows)
+    xs = [np.array([code[s] for s in r[2:]], dtype=np.int32) for r in rows if r[0] == "in"]
+    got = ref.alltoall(xs)
+    for r in rows:
+        if r[0] == "out":
+            assert got[int(r[1])].tolist() == [code[s] for s in r[2:]]
+
+
+def test_broadcast_symbolic():
+    rows = read_golden("broadcast_symbolic.txt")
+    code = _symbol_codes(rows)
+    root = int([r for r in rows if r[0] == "root"][0][1])
+    x = np.array([code[s] for r in rows if r[0] == "in" for s in r[2:]], dtype=np.int32)
+    expect = [code[s] for r in rows if r[0] == "out" for s in r[2:]]
+    for out in ref.broadcast(x, 4):
+        assert out.tolist() == expect
+    assert root == 0
+
+
+def test_alltoall_twice_is_identity():
+    for p in (1, 2, 3, 8):
+        for m in (0, 1, 5):
+            xs = inputs.rank_buffers(inputs.WL_TEST, p, p * m, ref.I32, extra=(21, p, m))
+            back = ref.alltoall(ref.alltoall(xs))
+            assert all(np.array_equal(a, b) for a, b in zip(xs, back))
+
+
+def test_alltoallv_then_transposed_counts_is_identity():
+    rng = np.random.default_rng(8)
+    for p in (1, 2, 3, 5, 8):
+        for _ in range(5):
+            counts = rng.integers(0, 6, size=(p, p))
+            counts[rng.random((p, p)) < 0.2] = 0
+            xs = [rng.integers(-100, 100, int(counts[i].sum())).astype(np.int32) for i in range(p)]
+            mid = ref.alltoallv(xs, counts)
+            assert [len(m) for m in mid] == ref.alltoallv_recv_counts(counts).tolist()
+            back = ref.alltoallv(mid, counts.T)
+            assert all(np.array_equal(a, b) for a, b in zip(xs, back))
+
+
+def test_alltoallv_small_explicit():
+    # p = 2: source 0 sends 1 element to 0 and 2 to 1; source 1 sends 3 to 0 and 0 to 1.
+    xs = [np.array([10, 11, 12], dtype=np.int32), np.array([20, 21, 22], dtype=np.int32)]
+    counts = np.array([[1, 2], [3, 0]])
+    out = ref.alltoallv(xs, counts)
+    assert out[0].tolist() == [10, 20, 21, 22]
+    assert out[1].tolist() == [11, 12]
+
+
+def test_alltoallv_equal_counts_match_alltoall():
+    for p in (2, 4, 8):
+        m = 3
+        xs = inputs.rank_buffers(inputs.WL_TEST, p, p * m, ref.I32, extra=(31, p))
+        a = ref.alltoall(xs)
+        b = ref.alltoallv(xs, np.full((p, p), m))
+        assert all(np.array_equal(u, v) for u, v in zip(a, b))
+
+
+# ----------------------------------------------------------------------------
+# Error bound of the fp32 fold against the exact sum
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("p", [2, 8, 16])
+def test_fp32_sum_within_recursive_summation_bound(p):
+    n = 2048
+    xs = inputs.rank_buffers(inputs.WL_TEST, p, n, ref.F32, dist="normal", extra=(41, p))
+    got = ref.allreduce(xs, ref.SUM, ref.F32)[0].astype(np.float64)
+    u = 2.0 ** -24
+    gamma = (p - 1) * u / (1 - (p - 1) * u)
+    for i in range(0, n, 7):
+        vals = [float(x[i]) for x in xs]
+        exact = math.fsum(vals)
+        bound = gamma * sum(abs(v) for v in vals)
+        assert abs(got[i] - exact) <= bound + 1e-45
+
+
+# ----------------------------------------------------------------------------
+# Bandwidth conventions (section 2.5 table)
+# ----------------------------------------------------------------------------
+
+def test_busbw_factors_match_table():
+    for name, a, b, den in read_golden("busbw_factors.txt"):
+        for p in (2, 4, 8, 16):
+            expect = int(a) * (p + int(b)) / p if den == "p" else float(a)
+            assert metrics.busbw_factor(name, p) == pytest.approx(expect, rel=0, abs=1e-15)
+
+
+def test_hbm_to_busbw_ratio():
+    # Out-of-place AllReduce: HBM bytes / busbw bytes = p^2/(p-1).
+    for p in (4, 8, 16):
+        n, d = 1 << 20, 4
+        hbm = metrics.hbm_bytes("allreduce", p, n, d)
+        bus = metrics.payload_bytes("allreduce", p, n, d) * metrics.busbw_factor("allreduce", p)
+        assert hbm / bus == pytest.approx(p * p / (p - 1))
+    # ReduceScatter / AllGather: p(p+1)/(p-1)
+    for coll in ("reduce_scatter", "allgather"):
+        p = 8
+        hbm = metrics.hbm_bytes(coll, p, 1000, 2)
+        bus = metrics.payload_bytes(coll, p, 1000, 2) * metrics.busbw_factor(coll, p)
+        assert hbm / bus == pytest.approx(p * (p + 1) / (p - 1))
+
+
+# ----------------------------------------------------------------------------
+# Input recipes
+# ----------------------------------------------------------------------------
+
+def test_input_recipes():
+    g = inputs.rng_for(inputs.WL_TEST, 0)
+    u = inputs.uniform_f32(g, 100000)
+    assert u.dtype == np.float32 and u.min() >= -1.0 and u.max() < 1.0
+    assert not np.any((u == 0) & np.signbit(u))
+    assert np.all(np.mod(u.astype(np.float64) * 2 ** 23, 1.0) == 0)
+    i = inputs.uniform_i32(g, 100000)
+    assert i.min() >= -1000 and i.max() <= 1000
+    nb = inputs.normal_bf16_bits(inputs.rng_for(2, 0), 200000, 1e-3)
+    vals = ref.bf16_to_f32(nb)
+    assert abs(float(np.std(vals)) - 1e-3) < 2e-5
+    # determinism
+    a = inputs.rank_buffers(inputs.WL_TEST, 3, 10, inputs.F32)
+    b = inputs.rank_buffers(inputs.WL_TEST, 3, 10, inputs.F32)
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
+    c = inputs.moe_token_counts()
+    assert c.shape == (8, 8) and np.all(c.sum(axis=1) == 4096)
+    calls, pool = inputs.small_batch_plan(2000)
+    sizes = np.array([c.n * 4 for c in calls])
+    assert sizes.min() >= 4096 - 3 and sizes.max() < 1 << 20
+    assert all(c.src_off % 64 == 0 and c.dst_off % 64 == 0 for c in calls)
+    assert [c.op for c in calls[:6]] == [0, 1, 2, 0, 1, 2]
+    assert [c.dtype for c in calls[:6]] == [0, 0, 0, 2, 2, 2]
