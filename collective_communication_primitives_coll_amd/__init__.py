@@ -1,0 +1,303 @@
+"""Collective communication primitives over p logical ranks in one MI355X.
+
+Thin ctypes binding of ``libcoll.so`` (C ABI in ``include/coll.h``).  The
+functions carry the C names and only marshal arguments: buffers may be
+torch tensors (their ``data_ptr()`` is passed) or raw device addresses
+(ints).  Every byte of the collective is moved by the library's HIP
+kernels; there is no CPU or torch fallback, and a missing library raises.
+
+Calls are asynchronous on ``stream`` (default: torch's current stream on
+the current device); synchronise before reading results.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Any, Sequence
+
+# Enum values of coll.h
+COLL_F32, COLL_BF16, COLL_I32 = 0, 1, 2
+COLL_SUM, COLL_MIN, COLL_MAX = 0, 1, 2
+COLL_OK, COLL_ERR_INVALID_ARG, COLL_ERR_UNSUPPORTED, COLL_ERR_ALIAS, COLL_ERR_HIP = 0, 1, 2, 3, 4
+COLL_ALGO_RING, COLL_ALGO_ONEPASS, COLL_ALGO_RING_LITERAL = 0, 1, 2
+COLL_MAX_RANKS = 64
+COLL_BATCH_CHECK_ALIAS = 1
+
+ELEM_BYTES = {COLL_F32: 4, COLL_BF16: 2, COLL_I32: 4}
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcoll.so")
+
+_lib = None
+
+
+class CollError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+class coll_call_t(ctypes.Structure):
+    _fields_ = [
+        ("send", ctypes.POINTER(ctypes.c_void_p)),
+        ("recv", ctypes.POINTER(ctypes.c_void_p)),
+        ("n", ctypes.c_size_t),
+        ("dtype", ctypes.c_int),
+        ("op", ctypes.c_int),
+    ]
+
+
+def lib() -> ctypes.CDLL:
+    """Load libcoll.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing; build it with __graft_entry__.build(). "
+                           "There is no fallback path.")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, pp, sz, i32 = ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t, ctypes.c_int
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    sig = {
+        "coll_allreduce": [pp, pp, i32, sz, i32, i32, vp],
+        "coll_allreduce_algo": [pp, pp, i32, sz, i32, i32, i32, vp],
+        "coll_reduce": [pp, vp, i32, sz, i32, i32, i32, vp],
+        "coll_broadcast": [vp, pp, i32, sz, i32, i32, vp],
+        "coll_reduce_scatter": [pp, pp, i32, sz, i32, i32, vp],
+        "coll_allgather": [pp, pp, i32, sz, i32, vp],
+        "coll_alltoall": [pp, pp, i32, sz, i32, vp],
+        "coll_alltoallv": [pp, pp, i32, vp, i64p, i64p, vp, i32, vp],
+        "coll_allreduce_batch": [ctypes.POINTER(coll_call_t), i32, i32, ctypes.c_uint, vp],
+    }
+    for name, args in sig.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int
+    L.coll_status_string.argtypes = [ctypes.c_int]
+    L.coll_status_string.restype = ctypes.c_char_p
+    L.coll_last_hip_error.argtypes = []
+    L.coll_last_hip_error.restype = ctypes.c_int
+    L.coll_version.argtypes = []
+    L.coll_version.restype = ctypes.c_int
+    L.coll_finalize.argtypes = []
+    L.coll_finalize.restype = None
+    L.coll_set_grid_limit.argtypes = [ctypes.c_int]
+    L.coll_set_grid_limit.restype = None
+    _lib = L
+    return L
+
+
+# ----------------------------------------------------------------------------
+# Marshalling helpers
+# ----------------------------------------------------------------------------
+
+def _addr(x: Any) -> int:
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        if not x.is_cuda:
+            raise ValueError("buffers must be device tensors")
+        if not x.is_contiguous():
+            raise ValueError("buffers must be contiguous")
+        return x.data_ptr()
+    raise TypeError(f"expected a tensor or a device address, got {type(x)}")
+
+
+def _ptr_array(xs: Sequence[Any]):
+    arr = (ctypes.c_void_p * len(xs))(*[_addr(x) for x in xs])
+    return ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)), arr
+
+
+def _dtype_of(x: Any, dtype: int | None) -> int:
+    if dtype is not None:
+        return int(dtype)
+    import torch
+    m = {torch.float32: COLL_F32, torch.bfloat16: COLL_BF16, torch.int32: COLL_I32}
+    if not hasattr(x, "dtype") or x.dtype not in m:
+        raise ValueError("dtype must be given for raw addresses, or tensors must be float32/bfloat16/int32")
+    return m[x.dtype]
+
+
+def _numel(x: Any, n: int | None) -> int:
+    if n is not None:
+        return int(n)
+    if hasattr(x, "numel"):
+        return int(x.numel())
+    raise ValueError("n must be given for raw addresses")
+
+
+def _stream(stream: Any) -> int:
+    if stream is None:
+        import torch
+        return int(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return stream
+    return int(stream.cuda_stream)
+
+
+def _check(status: int, what: str) -> None:
+    if status != COLL_OK:
+        L = lib()
+        msg = L.coll_status_string(status).decode()
+        if status == COLL_ERR_HIP:
+            msg += f" (hipError {L.coll_last_hip_error()})"
+        raise CollError(status, f"{what}: {msg}")
+
+
+def _check_sizes(xs: Sequence[Any], need: int, what: str) -> None:
+    for x in xs:
+        if hasattr(x, "numel") and x.numel() < need:
+            raise ValueError(f"{what}: buffer of {x.numel()} elements, {need} needed")
+
+
+def _same_dtype(xs: Sequence[Any], dt: int) -> None:
+    for x in xs:
+        if hasattr(x, "dtype") and _dtype_of(x, None) != dt:
+            raise ValueError("all buffers must share one dtype")
+
+
+# ----------------------------------------------------------------------------
+# The entry points (names and argument order of coll.h; n and dtype are
+# taken from the tensors when not given)
+# ----------------------------------------------------------------------------
+
+def coll_allreduce(send, recv, op: int = COLL_SUM, n: int | None = None, dtype: int | None = None,
+                   stream=None) -> None:
+    coll_allreduce_algo(send, recv, COLL_ALGO_RING, op, n, dtype, stream)
+
+
+def coll_allreduce_algo(send, recv, algo: int, op: int = COLL_SUM, n: int | None = None,
+                        dtype: int | None = None, stream=None) -> None:
+    p = len(send)
+    if len(recv) != p:
+        raise ValueError("send and recv must list the same ranks")
+    dt = _dtype_of(send[0], dtype)
+    n = _numel(send[0], n)
+    _same_dtype([*send, *recv], dt)
+    _check_sizes([*send, *recv], n, "allreduce")
+    s, _k1 = _ptr_array(send)
+    r, _k2 = _ptr_array(recv)
+    _check(lib().coll_allreduce_algo(s, r, p, n, dt, int(op), int(algo), _stream(stream)), "coll_allreduce")
+
+
+def coll_reduce(send, recv_root, root: int, op: int = COLL_SUM, n: int | None = None,
+                dtype: int | None = None, stream=None) -> None:
+    p = len(send)
+    dt = _dtype_of(send[0], dtype)
+    n = _numel(send[0], n)
+    _same_dtype([*send, recv_root], dt)
+    _check_sizes([*send, recv_root], n, "reduce")
+    s, _k = _ptr_array(send)
+    _check(lib().coll_reduce(s, _addr(recv_root), p, n, dt, int(op), int(root), _stream(stream)),
+           "coll_reduce")
+
+
+def coll_broadcast(send_root, recv, root: int, n: int | None = None, dtype: int | None = None,
+                   stream=None) -> None:
+    p = len(recv)
+    dt = _dtype_of(send_root, dtype)
+    n = _numel(send_root, n)
+    _same_dtype([send_root, *recv], dt)
+    _check_sizes([send_root, *recv], n, "broadcast")
+    r, _k = _ptr_array(recv)
+    _check(lib().coll_broadcast(_addr(send_root), r, p, n, dt, int(root), _stream(stream)), "coll_broadcast")
+
+
+def coll_reduce_scatter(send, recv, op: int = COLL_SUM, n: int | None = None, dtype: int | None = None,
+                        stream=None) -> None:
+    """n = elements each rank receives; send[r] holds p*n."""
+    p = len(send)
+    dt = _dtype_of(send[0], dtype)
+    n = _numel(recv[0], n)
+    _same_dtype([*send, *recv], dt)
+    _check_sizes(send, p * n, "reduce_scatter send")
+    _check_sizes(recv, n, "reduce_scatter recv")
+    s, _k1 = _ptr_array(send)
+    r, _k2 = _ptr_array(recv)
+    _check(lib().coll_reduce_scatter(s, r, p, n, dt, int(op), _stream(stream)), "coll_reduce_scatter")
+
+
+def coll_allgather(send, recv, n: int | None = None, dtype: int | None = None, stream=None) -> None:
+    """n = elements each rank sends; recv[r] holds p*n."""
+    p = len(send)
+    dt = _dtype_of(send[0], dtype)
+    n = _numel(send[0], n)
+    _same_dtype([*send, *recv], dt)
+    _check_sizes(send, n, "allgather send")
+    _check_sizes(recv, p * n, "allgather recv")
+    s, _k1 = _ptr_array(send)
+    r, _k2 = _ptr_array(recv)
+    _check(lib().coll_allgather(s, r, p, n, dt, _stream(stream)), "coll_allgather")
+
+
+def coll_alltoall(send, recv, n_block: int | None = None, dtype: int | None = None, stream=None) -> None:
+    """send[i] and recv[j] hold p blocks of n_block elements."""
+    p = len(send)
+    dt = _dtype_of(send[0], dtype)
+    if n_block is None:
+        n_block = _numel(send[0], None) // p
+    _same_dtype([*send, *recv], dt)
+    _check_sizes([*send, *recv], p * n_block, "alltoall")
+    s, _k1 = _ptr_array(send)
+    r, _k2 = _ptr_array(recv)
+    _check(lib().coll_alltoall(s, r, p, int(n_block), dt, _stream(stream)), "coll_alltoall")
+
+
+def coll_alltoallv(send, recv, counts_dev, send_cap: Sequence[int] | None = None,
+                   recv_cap: Sequence[int] | None = None, status_dev=None, dtype: int | None = None,
+                   stream=None) -> None:
+    """counts_dev: device int64 [p, p] (row = source).  Capacities default to
+    the tensors' sizes."""
+    p = len(send)
+    dt = _dtype_of(send[0], dtype)
+    if send_cap is None:
+        send_cap = [_numel(x, None) for x in send]
+    if recv_cap is None:
+        recv_cap = [_numel(x, None) for x in recv]
+    if hasattr(counts_dev, "dtype"):
+        import torch
+        if counts_dev.dtype != torch.int64 or counts_dev.numel() < p * p:
+            raise ValueError("counts must be a device int64 tensor with p*p entries")
+    _same_dtype([*send, *recv], dt)
+    s, _k1 = _ptr_array(send)
+    r, _k2 = _ptr_array(recv)
+    sc = (ctypes.c_int64 * p)(*[int(v) for v in send_cap])
+    rc = (ctypes.c_int64 * p)(*[int(v) for v in recv_cap])
+    st = _addr(status_dev) if status_dev is not None else None
+    _check(lib().coll_alltoallv(s, r, p, _addr(counts_dev), sc, rc, st, dt, _stream(stream)),
+           "coll_alltoallv")
+
+
+def coll_allreduce_batch(calls: Sequence[tuple], p: int, flags: int = 0, stream=None) -> None:
+    """calls: (send list, recv list, n, dtype, op) per AllReduce."""
+    keep = []
+    arr = (coll_call_t * len(calls))()
+    for k, (send, recv, n, dtype, op) in enumerate(calls):
+        if len(send) != p or len(recv) != p:
+            raise ValueError("every call must list p ranks")
+        s, ks = _ptr_array(send)
+        r, kr = _ptr_array(recv)
+        keep.append((ks, kr))
+        arr[k].send, arr[k].recv = s, r
+        arr[k].n, arr[k].dtype, arr[k].op = int(n), int(dtype), int(op)
+    _check(lib().coll_allreduce_batch(arr, len(calls), int(p), int(flags), _stream(stream)),
+           "coll_allreduce_batch")
+
+
+def coll_status_string(status: int) -> str:
+    return lib().coll_status_string(int(status)).decode()
+
+
+def coll_last_hip_error() -> int:
+    return lib().coll_last_hip_error()
+
+
+def coll_version() -> int:
+    return lib().coll_version()
+
+
+def coll_set_grid_limit(workgroups_per_cu: int) -> None:
+    lib().coll_set_grid_limit(int(workgroups_per_cu))
+
+
+def coll_finalize() -> None:
+    lib().coll_finalize()

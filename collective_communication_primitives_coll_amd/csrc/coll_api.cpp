@@ -1,0 +1,605 @@
+// Host side of the C ABI: argument validation, aliasing rules, grid sizing
+// and dispatch to the kernel launchers.  Everything that can be checked on
+// the host is checked before any HIP call, so an invalid call has no side
+// effect on the device.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "coll.h"
+#include "kernel_args.h"
+
+#define COLL_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using coll::kMaxRanks;
+static_assert(COLL_MAX_RANKS == coll::kMaxRanks, "rank limit mismatch");
+
+thread_local int g_last_hip = 0;
+
+coll_status_t hip_fail(int err) {
+  g_last_hip = err;
+  return COLL_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+// Device facts, cached per device.
+// ---------------------------------------------------------------------------
+struct DevInfo {
+  std::atomic<int> cus{0};
+  std::atomic<int> lds_per_block{0};
+};
+DevInfo g_dev[64];
+std::atomic<int> g_wg_per_cu{0};
+
+constexpr int kDefaultWgPerCu = 8;
+
+int current_device(int* dev) { return (int)hipGetDevice(dev); }
+
+int device_cus(int dev, int* out) {
+  if (dev < 0 || dev >= 64) return (int)hipErrorInvalidDevice;
+  int c = g_dev[dev].cus.load(std::memory_order_relaxed);
+  if (!c) {
+    hipError_t e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return (int)e;
+    int l = 0;
+    e = hipDeviceGetAttribute(&l, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+    if (e != hipSuccess) return (int)e;
+    g_dev[dev].lds_per_block.store(l, std::memory_order_relaxed);
+    g_dev[dev].cus.store(c, std::memory_order_relaxed);
+  }
+  *out = c;
+  return 0;
+}
+
+// Grid limit: workgroups per CU times CUs of the current device.
+int max_grid(int* out) {
+  int dev = 0, cus = 0;
+  int e = current_device(&dev);
+  if (e) return e;
+  e = device_cus(dev, &cus);
+  if (e) return e;
+  int w = g_wg_per_cu.load(std::memory_order_relaxed);
+  if (w <= 0) w = kDefaultWgPerCu;
+  *out = cus * w;
+  return 0;
+}
+
+// ---------------------------------------------------------------------------
+// Argument checks
+// ---------------------------------------------------------------------------
+bool dtype_ok(int d) { return d == COLL_F32 || d == COLL_BF16 || d == COLL_I32; }
+bool op_ok(int o) { return o == COLL_SUM || o == COLL_MIN || o == COLL_MAX; }
+size_t dsize(int d) { return d == COLL_BF16 ? 2 : 4; }
+
+// bytes = a * b * c without overflow, and below 2^62 so that every derived
+// offset stays representable.
+bool mul_ok(size_t a, size_t b, size_t c, size_t* out) {
+  size_t t;
+  if (__builtin_mul_overflow(a, b, &t)) return false;
+  if (__builtin_mul_overflow(t, c, &t)) return false;
+  if (t >= (size_t{1} << 62)) return false;
+  *out = t;
+  return true;
+}
+
+template <typename PtrT>
+bool all_non_null(PtrT const* arr, int p) {
+  if (!arr) return false;
+  for (int r = 0; r < p; ++r)
+    if (!arr[r]) return false;
+  return true;
+}
+
+// Every pointer aligned to the element size (the vector path relies on it).
+template <typename PtrT>
+bool elem_aligned(PtrT const* arr, int p, size_t d) {
+  for (int r = 0; r < p; ++r)
+    if ((uintptr_t)arr[r] % d) return false;
+  return true;
+}
+bool elem_aligned1(const void* ptr, size_t d) { return (uintptr_t)ptr % d == 0; }
+
+// Common byte misalignment (address mod 16) of a set of pointers, or -1.
+int common_mis(const void* const* arr, int p) {
+  const int m = (int)((uintptr_t)arr[0] & 15);
+  for (int r = 1; r < p; ++r)
+    if ((int)((uintptr_t)arr[r] & 15) != m) return -1;
+  return m;
+}
+int common_mis2(int a, int b) { return (a < 0 || b < 0 || a != b) ? -1 : a; }
+
+// ---------------------------------------------------------------------------
+// Aliasing.  Every buffer becomes a byte range tagged (input|output, rank).
+// Outputs must not overlap anything, except pairs the operation allows
+// (its in-place forms).  Inputs may overlap each other.
+// ---------------------------------------------------------------------------
+struct Range {
+  uintptr_t b, e;
+  bool out;
+  int rank;
+};
+
+template <typename Allowed>
+coll_status_t check_alias(const std::vector<Range>& rs, Allowed allowed) {
+  const size_t m = rs.size();
+  for (size_t i = 0; i < m; ++i) {
+    if (!rs[i].out || rs[i].b == rs[i].e) continue;
+    for (size_t j = 0; j < m; ++j) {
+      if (i == j || rs[j].b == rs[j].e) continue;
+      if (rs[j].out && j < i) continue;  // output pairs checked once
+      const bool overlap = rs[i].b < rs[j].e && rs[j].b < rs[i].e;
+      if (overlap && !allowed(rs[i], rs[j])) return COLL_ERR_ALIAS;
+    }
+  }
+  return COLL_OK;
+}
+
+Range rng(const void* p, size_t bytes, bool out, int rank) {
+  const uintptr_t b = (uintptr_t)p;
+  return Range{b, b + bytes, out, rank};
+}
+
+coll::RankPtrs make_ptrs(const void* const* src, int ns, void* const* dst, int nd) {
+  coll::RankPtrs P;
+  std::memset(&P, 0, sizeof(P));
+  for (int r = 0; r < ns; ++r) P.src[r] = src[r];
+  for (int r = 0; r < nd; ++r) P.dst[r] = dst[r];
+  return P;
+}
+
+coll_status_t finish(int err) { return err ? hip_fail(err) : COLL_OK; }
+
+// AllReduce validation shared by the single and the batched entry points.
+coll_status_t check_allreduce(const void* const* send, void* const* recv, int p, size_t n, int dtype,
+                              int op) {
+  if (p < 1 || p > kMaxRanks || !dtype_ok(dtype) || !op_ok(op)) return COLL_ERR_INVALID_ARG;
+  if (n == 0) return COLL_OK;
+  size_t bytes;
+  if (!mul_ok(n, dsize(dtype), (size_t)p, &bytes)) return COLL_ERR_INVALID_ARG;
+  if (!all_non_null(send, p) || !all_non_null(recv, p)) return COLL_ERR_INVALID_ARG;
+  if (!elem_aligned(send, p, dsize(dtype)) || !elem_aligned(recv, p, dsize(dtype))) return COLL_ERR_INVALID_ARG;
+  const size_t nb = n * dsize(dtype);
+  std::vector<Range> rs;
+  rs.reserve(2 * p);
+  for (int r = 0; r < p; ++r) rs.push_back(rng(send[r], nb, false, r));
+  for (int r = 0; r < p; ++r) rs.push_back(rng(recv[r], nb, true, r));
+  return check_alias(rs, [](const Range& o, const Range& x) {
+    return !x.out && x.rank == o.rank && x.b == o.b;  // recv[r] == send[r]
+  });
+}
+
+}  // namespace
+
+// ===========================================================================
+// Entry points
+// ===========================================================================
+
+COLL_EXPORT coll_status_t coll_allreduce_algo(const void* const* send, void* const* recv, int p, size_t n,
+                                              coll_dtype_t dtype, coll_op_t op, coll_algo_t algo,
+                                              void* stream) {
+  if ((int)algo < COLL_ALGO_RING || (int)algo > COLL_ALGO_RING_LITERAL) return COLL_ERR_INVALID_ARG;
+  coll_status_t st = check_allreduce(send, recv, p, n, dtype, op);
+  if (st != COLL_OK || n == 0) return st;
+  if (algo == COLL_ALGO_ONEPASS && !(p == 2 || p == 4 || p == 8 || p == 16)) return COLL_ERR_UNSUPPORTED;
+  if (algo == COLL_ALGO_RING_LITERAL && dtype == COLL_BF16) return COLL_ERR_UNSUPPORTED;
+  int grid;
+  int e = max_grid(&grid);
+  if (e) return hip_fail(e);
+  const int smis = common_mis(send, p), dmis = common_mis((const void* const*)recv, p);
+  if (algo == COLL_ALGO_RING_LITERAL) {
+    if (p == 1) {
+      if (send[0] == recv[0]) return COLL_OK;
+      coll::RankPtrs P = make_ptrs(send, 1, recv, 1);
+      coll::CopyGeom g{n, 1, coll::kCopyBroadcast, smis, dmis};
+      return finish(coll::launch_copy((int)dsize(dtype), P, g, grid, stream));
+    }
+    coll::RankPtrs P = make_ptrs(send, p, recv, p);
+    coll::RingStepGeom g{};
+    g.n = n;
+    g.q = (n + p - 1) / p;
+    g.p = p;
+    g.mis = common_mis2(smis, dmis);
+    for (int phase = 0; phase < 2; ++phase)
+      for (int s = 1; s < p; ++s) {
+        g.phase = phase;
+        g.step = s;
+        e = coll::launch_ring_step(dtype, op, P, g, grid, stream);
+        if (e) return hip_fail(e);
+      }
+    return COLL_OK;
+  }
+  coll::RankPtrs P = make_ptrs(send, p, recv, p);
+  coll::ReduceGeom g{};
+  g.stride = (n + p - 1) / p;
+  g.total = n;
+  g.p = p;
+  g.dst_mode = coll::kDstAll;
+  g.src_mis = smis;
+  g.dst_mis = dmis;
+  const bool tree = algo == COLL_ALGO_ONEPASS && dtype != COLL_I32 && op == COLL_SUM;
+  return finish(coll::launch_reduce(dtype, op, tree ? 1 : 0, P, g, grid, stream));
+}
+
+COLL_EXPORT coll_status_t coll_allreduce(const void* const* send, void* const* recv, int p, size_t n,
+                                         coll_dtype_t dtype, coll_op_t op, void* stream) {
+  return coll_allreduce_algo(send, recv, p, n, dtype, op, COLL_ALGO_RING, stream);
+}
+
+COLL_EXPORT coll_status_t coll_reduce(const void* const* send, void* recv_root, int p, size_t n,
+                                      coll_dtype_t dtype, coll_op_t op, int root, void* stream) {
+  if (p < 1 || p > kMaxRanks || !dtype_ok(dtype) || !op_ok(op) || root < 0 || root >= p)
+    return COLL_ERR_INVALID_ARG;
+  if (n == 0) return COLL_OK;
+  size_t bytes;
+  if (!mul_ok(n, dsize(dtype), (size_t)p, &bytes)) return COLL_ERR_INVALID_ARG;
+  if (!all_non_null(send, p) || !recv_root) return COLL_ERR_INVALID_ARG;
+  if (!elem_aligned(send, p, dsize(dtype)) || !elem_aligned1(recv_root, dsize(dtype))) return COLL_ERR_INVALID_ARG;
+  const size_t nb = n * dsize(dtype);
+  std::vector<Range> rs;
+  for (int r = 0; r < p; ++r) rs.push_back(rng(send[r], nb, false, r));
+  rs.push_back(rng(recv_root, nb, true, root));
+  coll_status_t st = check_alias(rs, [](const Range& o, const Range& x) {
+    return !x.out && x.rank == o.rank && x.b == o.b;  // recv_root == send[root]
+  });
+  if (st != COLL_OK) return st;
+  int grid;
+  int e = max_grid(&grid);
+  if (e) return hip_fail(e);
+  void* dst[1] = {recv_root};
+  coll::RankPtrs P = make_ptrs(send, p, dst, 1);
+  coll::ReduceGeom g{};
+  g.stride = (n + p - 1) / p;
+  g.total = n;
+  g.p = p;
+  g.dst_mode = coll::kDstFixed;
+  g.src_mis = common_mis(send, p);
+  g.dst_mis = (int)((uintptr_t)recv_root & 15);
+  return finish(coll::launch_reduce(dtype, op, 0, P, g, grid, stream));
+}
+
+COLL_EXPORT coll_status_t coll_broadcast(const void* send_root, void* const* recv, int p, size_t n,
+                                         coll_dtype_t dtype, int root, void* stream) {
+  if (p < 1 || p > kMaxRanks || !dtype_ok(dtype) || root < 0 || root >= p) return COLL_ERR_INVALID_ARG;
+  if (n == 0) return COLL_OK;
+  size_t bytes;
+  if (!mul_ok(n, dsize(dtype), (size_t)p, &bytes)) return COLL_ERR_INVALID_ARG;
+  if (!send_root || !all_non_null(recv, p)) return COLL_ERR_INVALID_ARG;
+  if (!elem_aligned1(send_root, dsize(dtype)) || !elem_aligned(recv, p, dsize(dtype))) return COLL_ERR_INVALID_ARG;
+  const size_t nb = n * dsize(dtype);
+  std::vector<Range> rs;
+  rs.push_back(rng(send_root, nb, false, root));
+  for (int r = 0; r < p; ++r) rs.push_back(rng(recv[r], nb, true, r));
+  coll_status_t st = check_alias(rs, [](const Range& o, const Range& x) {
+    return !x.out && x.rank == o.rank && x.b == o.b;  // recv[root] == send_root
+  });
+  if (st != COLL_OK) return st;
+  int grid;
+  int e = max_grid(&grid);
+  if (e) return hip_fail(e);
+  const void* src[1] = {send_root};
+  coll::RankPtrs P = make_ptrs(src, 1, recv, p);
+  coll::CopyGeom g{n, p, coll::kCopyBroadcast, (int)((uintptr_t)send_root & 15),
+                   common_mis((const void* const*)recv, p)};
+  return finish(coll::launch_copy((int)dsize(dtype), P, g, grid, stream));
+}
+
+COLL_EXPORT coll_status_t coll_reduce_scatter(const void* const* send, void* const* recv, int p, size_t n,
+                                              coll_dtype_t dtype, coll_op_t op, void* stream) {
+  if (p < 1 || p > kMaxRanks || !dtype_ok(dtype) || !op_ok(op)) return COLL_ERR_INVALID_ARG;
+  if (n == 0) return COLL_OK;
+  size_t bytes;
+  if (!mul_ok(n, dsize(dtype), (size_t)p * p, &bytes)) return COLL_ERR_INVALID_ARG;
+  if (!all_non_null(send, p) || !all_non_null(recv, p)) return COLL_ERR_INVALID_ARG;
+  if (!elem_aligned(send, p, dsize(dtype)) || !elem_aligned(recv, p, dsize(dtype))) return COLL_ERR_INVALID_ARG;
+  const size_t nb = n * dsize(dtype);
+  std::vector<Range> rs;
+  for (int r = 0; r < p; ++r) rs.push_back(rng(send[r], nb * p, false, r));
+  for (int r = 0; r < p; ++r) rs.push_back(rng(recv[r], nb, true, r));
+  coll_status_t st = check_alias(rs, [nb](const Range& o, const Range& x) {
+    // recv[r] == send[r] + r*n elements (the rank's own output block)
+    return !x.out && x.rank == o.rank && o.b == x.b + (uintptr_t)o.rank * nb;
+  });
+  if (st != COLL_OK) return st;
+  int grid;
+  int e = max_grid(&grid);
+  if (e) return hip_fail(e);
+  coll::RankPtrs P = make_ptrs(send, p, recv, p);
+  coll::ReduceGeom g{};
+  g.stride = n;
+  g.total = n * (uint64_t)p;
+  g.p = p;
+  g.dst_mode = coll::kDstOwner;
+  g.src_mis = common_mis(send, p);
+  g.dst_mis = common_mis((const void* const*)recv, p);
+  return finish(coll::launch_reduce(dtype, op, 0, P, g, grid, stream));
+}
+
+COLL_EXPORT coll_status_t coll_allgather(const void* const* send, void* const* recv, int p, size_t n,
+                                         coll_dtype_t dtype, void* stream) {
+  if (p < 1 || p > kMaxRanks || !dtype_ok(dtype)) return COLL_ERR_INVALID_ARG;
+  if (n == 0) return COLL_OK;
+  size_t bytes;
+  if (!mul_ok(n, dsize(dtype), (size_t)p * p, &bytes)) return COLL_ERR_INVALID_ARG;
+  if (!all_non_null(send, p) || !all_non_null(recv, p)) return COLL_ERR_INVALID_ARG;
+  if (!elem_aligned(send, p, dsize(dtype)) || !elem_aligned(recv, p, dsize(dtype))) return COLL_ERR_INVALID_ARG;
+  const size_t nb = n * dsize(dtype);
+  std::vector<Range> rs;
+  for (int r = 0; r < p; ++r) rs.push_back(rng(send[r], nb, false, r));
+  for (int r = 0; r < p; ++r) rs.push_back(rng(recv[r], nb * p, true, r));
+  coll_status_t st = check_alias(rs, [nb](const Range& o, const Range& x) {
+    // send[r] == recv[r] + r*n elements (the rank's own block of the output)
+    return !x.out && x.rank == o.rank && x.b == o.b + (uintptr_t)o.rank * nb;
+  });
+  if (st != COLL_OK) return st;
+  int grid;
+  int e = max_grid(&grid);
+  if (e) return hip_fail(e);
+  coll::RankPtrs P = make_ptrs(send, p, recv, p);
+  coll::CopyGeom g{n, p, coll::kCopyAllGather, common_mis(send, p), common_mis((const void* const*)recv, p)};
+  return finish(coll::launch_copy((int)dsize(dtype), P, g, grid, stream));
+}
+
+COLL_EXPORT coll_status_t coll_alltoall(const void* const* send, void* const* recv, int p, size_t n_block,
+                                        coll_dtype_t dtype, void* stream) {
+  if (p < 1 || p > kMaxRanks || !dtype_ok(dtype)) return COLL_ERR_INVALID_ARG;
+  if (n_block == 0) return COLL_OK;
+  size_t bytes;
+  if (!mul_ok(n_block, dsize(dtype), (size_t)p * p, &bytes)) return COLL_ERR_INVALID_ARG;
+  if (!all_non_null(send, p) || !all_non_null(recv, p)) return COLL_ERR_INVALID_ARG;
+  if (!elem_aligned(send, p, dsize(dtype)) || !elem_aligned(recv, p, dsize(dtype))) return COLL_ERR_INVALID_ARG;
+  const size_t nb = n_block * dsize(dtype) * p;
+  std::vector<Range> rs;
+  for (int r = 0; r < p; ++r) rs.push_back(rng(send[r], nb, false, r));
+  for (int r = 0; r < p; ++r) rs.push_back(rng(recv[r], nb, true, r));
+  coll_status_t st = check_alias(rs, [](const Range&, const Range&) { return false; });
+  if (st != COLL_OK) return st;
+  int grid;
+  int e = max_grid(&grid);
+  if (e) return hip_fail(e);
+  coll::RankPtrs P = make_ptrs(send, p, recv, p);
+  coll::CopyGeom g{n_block, p, coll::kCopyAllToAll, common_mis(send, p),
+                   common_mis((const void* const*)recv, p)};
+  return finish(coll::launch_copy((int)dsize(dtype), P, g, grid, stream));
+}
+
+COLL_EXPORT coll_status_t coll_alltoallv(const void* const* send, void* const* recv, int p,
+                                         const int64_t* counts_dev, const int64_t* send_cap,
+                                         const int64_t* recv_cap, int32_t* status_dev, coll_dtype_t dtype,
+                                         void* stream) {
+  if (p < 1 || p > kMaxRanks || !dtype_ok(dtype)) return COLL_ERR_INVALID_ARG;
+  if (!counts_dev || !send_cap || !recv_cap) return COLL_ERR_INVALID_ARG;
+  if (!all_non_null(send, p) || !all_non_null(recv, p)) return COLL_ERR_INVALID_ARG;
+  const size_t d = dsize(dtype);
+  if (!elem_aligned(send, p, d) || !elem_aligned(recv, p, d)) return COLL_ERR_INVALID_ARG;
+  if (!elem_aligned1(counts_dev, sizeof(int64_t)) || (status_dev && !elem_aligned1(status_dev, sizeof(int32_t))))
+    return COLL_ERR_INVALID_ARG;
+  std::vector<Range> rs;
+  for (int r = 0; r < p; ++r) {
+    size_t b;
+    if (send_cap[r] < 0 || recv_cap[r] < 0) return COLL_ERR_INVALID_ARG;
+    // p counts of at most a capacity each must sum without int64 overflow
+    // on the device: cap * d * 64 < 2^62.
+    if (!mul_ok((size_t)send_cap[r], d, kMaxRanks, &b) || !mul_ok((size_t)recv_cap[r], d, kMaxRanks, &b))
+      return COLL_ERR_INVALID_ARG;
+    rs.push_back(rng(send[r], (size_t)send_cap[r] * d, false, r));
+    rs.push_back(rng(recv[r], (size_t)recv_cap[r] * d, true, r));
+  }
+  rs.push_back(rng(counts_dev, (size_t)p * p * sizeof(int64_t), false, -1));
+  if (status_dev) rs.push_back(rng(status_dev, sizeof(int32_t), true, -1));
+  coll_status_t st = check_alias(rs, [](const Range&, const Range&) { return false; });
+  if (st != COLL_OK) return st;
+  int dev = 0, cus = 0;
+  int e = current_device(&dev);
+  if (!e) e = device_cus(dev, &cus);
+  if (e) return hip_fail(e);
+  const size_t lds = (size_t)3 * p * p * sizeof(int64_t) + 64;
+  if (lds > (size_t)g_dev[dev].lds_per_block.load()) return COLL_ERR_UNSUPPORTED;
+  int grid;
+  e = max_grid(&grid);
+  if (e) return hip_fail(e);
+  coll::RankPtrs P = make_ptrs(send, p, recv, p);
+  coll::A2avArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.counts = counts_dev;
+  a.status = status_dev;
+  for (int r = 0; r < p; ++r) {
+    a.send_cap[r] = send_cap[r];
+    a.recv_cap[r] = recv_cap[r];
+  }
+  a.p = p;
+  a.src_mis = common_mis(send, p);
+  a.dst_mis = common_mis((const void* const*)recv, p);
+  return finish(coll::launch_alltoallv((int)d, P, a, grid, stream));
+}
+
+// ---------------------------------------------------------------------------
+// Batched AllReduce
+// ---------------------------------------------------------------------------
+namespace {
+
+struct BatchState {
+  std::mutex mu;
+  void* dev_buf = nullptr;
+  size_t dev_cap = 0;
+  void* host_buf = nullptr;
+  size_t host_cap = 0;
+  hipEvent_t done = nullptr;  // recorded after the last batch kernel
+  int device = -1;
+};
+BatchState g_batch;
+
+// Release everything; caller holds the mutex.
+void batch_release() {
+  if (g_batch.done) {
+    hipEventSynchronize(g_batch.done);
+    hipEventDestroy(g_batch.done);
+    g_batch.done = nullptr;
+  }
+  if (g_batch.dev_buf) hipFree(g_batch.dev_buf);
+  if (g_batch.host_buf) hipHostFree(g_batch.host_buf);
+  g_batch.dev_buf = g_batch.host_buf = nullptr;
+  g_batch.dev_cap = g_batch.host_cap = 0;
+  g_batch.device = -1;
+}
+
+bool ranges_disjoint_sorted(std::vector<Range>& rs) {
+  std::sort(rs.begin(), rs.end(), [](const Range& a, const Range& b) { return a.b < b.b; });
+  // any overlap that involves an output is an error, except identical
+  // (in-place) input/output pairs of the same call, which were checked per
+  // call and are excluded by the caller.
+  uintptr_t max_end_out = 0, max_end_any = 0;
+  for (const Range& r : rs) {
+    if (r.b == r.e) continue;
+    if (r.b < max_end_out) return false;               // starts inside an output
+    if (r.out && r.b < max_end_any) return false;      // output starts inside anything
+    max_end_any = std::max(max_end_any, r.e);
+    if (r.out) max_end_out = std::max(max_end_out, r.e);
+  }
+  return true;
+}
+
+}  // namespace
+
+COLL_EXPORT coll_status_t coll_allreduce_batch(const coll_call_t* calls, int ncalls, int p, unsigned flags,
+                                               void* stream) {
+  if (p < 1 || p > kMaxRanks || ncalls < 0 || (ncalls > 0 && !calls)) return COLL_ERR_INVALID_ARG;
+  if (flags & ~COLL_BATCH_CHECK_ALIAS) return COLL_ERR_INVALID_ARG;
+  if (ncalls == 0) return COLL_OK;
+  for (int k = 0; k < ncalls; ++k) {
+    const coll_call_t& c = calls[k];
+    coll_status_t st = check_allreduce(c.send, c.recv, p, c.n, c.dtype, c.op);
+    if (st != COLL_OK) return st;
+  }
+  if (flags & COLL_BATCH_CHECK_ALIAS) {
+    std::vector<Range> rs;
+    rs.reserve((size_t)ncalls * 2 * p);
+    for (int k = 0; k < ncalls; ++k) {
+      const coll_call_t& c = calls[k];
+      if (c.n == 0) continue;
+      const size_t nb = c.n * dsize(c.dtype);
+      for (int r = 0; r < p; ++r) {
+        // an in-place pair (validated above) is one output range
+        if (c.send[r] != c.recv[r]) rs.push_back(rng(c.send[r], nb, false, r));
+        rs.push_back(rng(c.recv[r], nb, true, r));
+      }
+    }
+    if (!ranges_disjoint_sorted(rs)) return COLL_ERR_ALIAS;
+  }
+  // Pack: (ncalls + 1) BatchCall records, then ncalls * 2p pointers.
+  std::vector<coll::BatchCall> recs((size_t)ncalls + 1);
+  uint64_t tiles = 0;
+  for (int k = 0; k < ncalls; ++k) {
+    const coll_call_t& c = calls[k];
+    coll::BatchCall& b = recs[k];
+    b.n = c.n;
+    b.first_tile = tiles;
+    b.dtype = (uint32_t)c.dtype;
+    b.op = (uint32_t)c.op;
+    b.mis = c.n ? common_mis2(common_mis(c.send, p), common_mis((const void* const*)c.recv, p)) : -1;
+    const uint64_t te = (uint64_t)256 * (c.dtype == COLL_BF16 ? 8 : 4);
+    const uint64_t q = (c.n + p - 1) / p;
+    b.tiles_per_chunk = c.n ? (uint32_t)std::max<uint64_t>(1, (q + te - 1) / te) : 0;
+    if (c.n && (q + te - 1) / te > 0xffffffffull) return COLL_ERR_INVALID_ARG;
+    tiles += (uint64_t)p * b.tiles_per_chunk;
+  }
+  recs[ncalls] = coll::BatchCall{};
+  recs[ncalls].first_tile = tiles;
+  if (tiles == 0) return COLL_OK;
+  const size_t rec_bytes = recs.size() * sizeof(coll::BatchCall);
+  const size_t ptr_off = (rec_bytes + 255) & ~size_t(255);
+  const size_t total = ptr_off + (size_t)ncalls * 2 * p * sizeof(void*);
+
+  int dev = 0;
+  int e = current_device(&dev);
+  if (e) return hip_fail(e);
+  int grid;
+  e = max_grid(&grid);
+  if (e) return hip_fail(e);
+
+  std::lock_guard<std::mutex> lock(g_batch.mu);
+  if (g_batch.device != -1 && g_batch.device != dev) batch_release();
+  g_batch.device = dev;
+  if (g_batch.done) {
+    // the previous batch kernel reads the device buffer and its upload read
+    // the pinned staging buffer: both must be finished before reuse
+    e = (int)hipEventSynchronize(g_batch.done);
+    if (e) return hip_fail(e);
+  } else {
+    e = (int)hipEventCreateWithFlags(&g_batch.done, hipEventDisableTiming);
+    if (e) return hip_fail(e);
+  }
+  if (g_batch.dev_cap < total) {
+    const size_t cap = std::max(total, g_batch.dev_cap * 2);
+    if (g_batch.dev_buf) hipFree(g_batch.dev_buf);
+    g_batch.dev_buf = nullptr;
+    g_batch.dev_cap = 0;
+    e = (int)hipMalloc(&g_batch.dev_buf, cap);
+    if (e) return hip_fail(e);
+    g_batch.dev_cap = cap;
+  }
+  if (g_batch.host_cap < total) {
+    if (g_batch.host_buf) hipHostFree(g_batch.host_buf);
+    g_batch.host_buf = nullptr;
+    g_batch.host_cap = 0;
+    e = (int)hipHostMalloc(&g_batch.host_buf, g_batch.dev_cap, hipHostMallocDefault);
+    if (e) return hip_fail(e);
+    g_batch.host_cap = g_batch.dev_cap;
+  }
+  char* h = (char*)g_batch.host_buf;
+  std::memcpy(h, recs.data(), rec_bytes);
+  const void** hp = (const void**)(h + ptr_off);
+  for (int k = 0; k < ncalls; ++k) {
+    for (int r = 0; r < p; ++r) {
+      hp[(size_t)k * 2 * p + r] = calls[k].n ? calls[k].send[r] : nullptr;
+      hp[(size_t)k * 2 * p + p + r] = calls[k].n ? (const void*)calls[k].recv[r] : nullptr;
+    }
+  }
+  hipStream_t s = (hipStream_t)stream;
+  e = (int)hipMemcpyAsync(g_batch.dev_buf, h, total, hipMemcpyHostToDevice, s);
+  if (e) return hip_fail(e);
+  coll::BatchArgs a;
+  a.calls = (const coll::BatchCall*)g_batch.dev_buf;
+  a.ptrs = (const void* const*)((char*)g_batch.dev_buf + ptr_off);
+  a.ncalls = ncalls;
+  a.p = p;
+  const int g = (int)std::min<uint64_t>(tiles, (uint64_t)grid);
+  e = coll::launch_batch(a, g, stream);
+  if (e) return hip_fail(e);
+  e = (int)hipEventRecord(g_batch.done, s);
+  if (e) return hip_fail(e);
+  return COLL_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Misc
+// ---------------------------------------------------------------------------
+COLL_EXPORT const char* coll_status_string(coll_status_t s) {
+  switch (s) {
+    case COLL_OK: return "COLL_OK";
+    case COLL_ERR_INVALID_ARG: return "COLL_ERR_INVALID_ARG: invalid argument";
+    case COLL_ERR_UNSUPPORTED: return "COLL_ERR_UNSUPPORTED: valid request this build does not implement";
+    case COLL_ERR_ALIAS: return "COLL_ERR_ALIAS: illegal overlap between buffers";
+    case COLL_ERR_HIP: return "COLL_ERR_HIP: the HIP runtime reported an error";
+  }
+  return "unknown coll_status_t";
+}
+
+COLL_EXPORT int coll_last_hip_error(void) { return g_last_hip; }
+
+COLL_EXPORT int coll_version(void) { return 100; }
+
+COLL_EXPORT void coll_set_grid_limit(int workgroups_per_cu) {
+  g_wg_per_cu.store(workgroups_per_cu > 0 ? workgroups_per_cu : 0, std::memory_order_relaxed);
+}
+
+COLL_EXPORT void coll_finalize(void) {
+  std::lock_guard<std::mutex> lock(g_batch.mu);
+  batch_release();
+}

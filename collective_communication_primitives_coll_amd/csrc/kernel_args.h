@@ -1,0 +1,106 @@
+// Kernel argument blocks and launcher declarations (host and device).
+//
+// Rank pointer arrays travel in the kernel-argument segment, so a launch
+// needs no device-side descriptor and nothing is allocated per call.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace coll {
+
+constexpr int kMaxRanks = 64;
+
+enum DType : int { kF32 = 0, kBF16 = 1, kI32 = 2 };
+enum Op : int { kSum = 0, kMin = 1, kMax = 2 };
+
+// Destination selection of the reduction kernels.
+enum DstMode : int {
+  kDstAll = 0,    // every rank r: dst[r] + segment offset      (AllReduce)
+  kDstFixed = 1,  // dst[0] + segment offset                     (Reduce: root buffer)
+  kDstOwner = 2   // dst[c] + 0 for segment c                    (ReduceScatter)
+};
+
+struct RankPtrs {
+  const void* src[kMaxRanks];
+  void* dst[kMaxRanks];
+};
+
+// Reduction geometry: segment c covers source elements
+// [min(total, c*stride), min(total, (c+1)*stride)).
+struct ReduceGeom {
+  uint64_t stride;
+  uint64_t total;
+  int p;
+  int dst_mode;
+  int src_mis;  // common byte misalignment of the source bases, or -1
+  int dst_mis;  // common byte misalignment of the destination bases, or -1
+};
+
+// Copy kinds.
+enum CopyKind : int {
+  kCopyAllGather = 0,  // segment s: src[s] -> dst[r] + s*n, every r
+  kCopyBroadcast = 1,  // one segment: src[0] -> dst[r], every r
+  kCopyAllToAll = 2    // segment (i,j): src[i] + j*n -> dst[j] + i*n
+};
+
+struct CopyGeom {
+  uint64_t n;  // elements per segment
+  int p;
+  int kind;
+  int src_mis;
+  int dst_mis;
+};
+
+struct A2avArgs {
+  const int64_t* counts;         // device, p*p, row = source
+  int32_t* status;               // device, optional
+  int64_t send_cap[kMaxRanks];   // elements
+  int64_t recv_cap[kMaxRanks];
+  int p;
+  int src_mis;
+  int dst_mis;
+};
+
+// Literal ring: one neighbour step per launch.
+struct RingStepGeom {
+  uint64_t n;
+  uint64_t q;    // chunk length ceil(n/p)
+  int p;
+  int phase;     // 0 reduce-scatter, 1 all-gather
+  int step;      // 1..p-1
+  int mis;       // common misalignment of all send and recv bases, or -1
+};
+
+// Batched AllReduce descriptors (device resident).
+struct BatchCall {
+  uint64_t n;
+  uint64_t first_tile;   // flat index of the call's first tile
+  uint32_t dtype;
+  uint32_t op;
+  uint32_t tiles_per_chunk;
+  int32_t mis;           // common misalignment of the call's buffers, or -1
+};
+
+struct BatchArgs {
+  const BatchCall* calls;   // ncalls + 1 entries; the last holds the total tile count
+  const void* const* ptrs;  // per call: p sources then p destinations
+  int ncalls;
+  int p;
+};
+
+// Launchers (return a hipError_t as int).
+// max_grid bounds the number of workgroups; launchers shrink it to the
+// number of tiles.  launch_alltoallv and launch_batch take the grid as is.
+int launch_reduce(int dtype, int op, int algo_tree, const RankPtrs& ptrs, const ReduceGeom& g,
+                  int max_grid, void* stream);
+int launch_copy(int elem_bytes, const RankPtrs& ptrs, const CopyGeom& g, int max_grid, void* stream);
+int launch_alltoallv(int elem_bytes, const RankPtrs& ptrs, const A2avArgs& a, int grid, void* stream);
+int launch_ring_step(int dtype, int op, const RankPtrs& ptrs, const RingStepGeom& g, int max_grid,
+                     void* stream);
+int launch_batch(const BatchArgs& a, int grid, void* stream);
+
+// 16-byte vectors each lane of a copy kernel keeps in flight.
+constexpr uint64_t kCopyUnroll = 4;
+
+}  // namespace coll

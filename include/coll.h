@@ -26,8 +26,9 @@
  * - Validation is synchronous and complete before anything is enqueued; a
  *   call that returns an error has enqueued nothing.  n == 0 is a no-op
  *   returning COLL_OK (pointers are then not inspected).
- * - Pointers need no particular alignment beyond the element size; 16-byte
- *   aligned buffers take the vector path.
+ * - Every device pointer must be aligned to its element size (else
+ *   COLL_ERR_INVALID_ARG); buffers that share one 16-byte misalignment take
+ *   the 16-byte vector path, others an element-wide path.
  * - Aliasing: the output ranges must be pairwise disjoint and may not
  *   overlap any input range, except the in-place forms listed with each
  *   call ([B], In-place).  Input ranges may overlap each other.  A
@@ -178,6 +179,11 @@ int coll_last_hip_error(void);
 
 /* Library version, major*10000 + minor*100 + patch. */
 int coll_version(void);
+
+/* Occupancy target used to size grids: workgroups (256 threads) per
+ * compute unit; 0 restores the default (8).  Applies to later calls from
+ * every thread; results do not depend on it. */
+void coll_set_grid_limit(int workgroups_per_cu);
 
 /* Release library-owned device and pinned host memory (batch descriptors).
  * Synchronises on the work that used them. */

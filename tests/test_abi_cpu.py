@@ -1,0 +1,143 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads,
+exports every function coll.h declares, and rejects invalid calls before
+touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+import collective_communication_primitives_coll_amd as coll
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+# Calls below pass made-up device addresses.  They are all invalid and must
+# be rejected on the host; on a machine with a GPU they are not run at all,
+# so a regression that accepted one could never launch a kernel on them.
+host_only = pytest.mark.skipif(_gpu_visible(), reason="fake device addresses: host-only machine")
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "coll.h"), encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(coll_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    L = coll.lib()
+    names = declared_functions()
+    assert len(names) >= 14
+    for name in names:
+        assert hasattr(L, name), f"{name} declared in coll.h but not exported"
+
+
+def test_status_strings_and_version():
+    assert coll.coll_status_string(coll.COLL_OK) == "COLL_OK"
+    for s in range(1, 5):
+        assert coll.coll_status_string(s).startswith("COLL_ERR_")
+    assert "unknown" in coll.coll_status_string(99)
+    assert coll.coll_version() >= 100
+    assert coll.coll_last_hip_error() == 0
+
+
+def _arr(vals):
+    a = (ctypes.c_void_p * len(vals))(*vals)
+    return ctypes.cast(a, ctypes.POINTER(ctypes.c_void_p)), a
+
+
+def test_zero_elements_is_ok_without_pointers():
+    L = coll.lib()
+    assert L.coll_allreduce(None, None, 4, 0, 0, 0, None) == coll.COLL_OK
+    assert L.coll_reduce_scatter(None, None, 4, 0, 0, 0, None) == coll.COLL_OK
+    assert L.coll_allgather(None, None, 4, 0, 1, None) == coll.COLL_OK
+    assert L.coll_alltoall(None, None, 4, 0, 1, None) == coll.COLL_OK
+    assert L.coll_broadcast(None, None, 4, 0, 2, 0, None) == coll.COLL_OK
+    assert L.coll_reduce(None, None, 4, 0, 2, 1, 3, None) == coll.COLL_OK
+    assert L.coll_allreduce_batch(None, 0, 4, 0, None) == coll.COLL_OK
+
+
+@host_only
+def test_invalid_arguments_rejected():
+    L = coll.lib()
+    INV = coll.COLL_ERR_INVALID_ARG
+    base = 0x7F0000000000
+    s, _ks = _arr([base + 0x100000 * r for r in range(4)])
+    r, _kr = _arr([base + 0x10000000 + 0x100000 * i for i in range(4)])
+    n = 1000
+    assert L.coll_allreduce(s, r, 0, n, 0, 0, None) == INV            # p = 0
+    assert L.coll_allreduce(s, r, 65, n, 0, 0, None) == INV           # p > 64
+    assert L.coll_allreduce(s, r, 4, n, 3, 0, None) == INV            # bad dtype
+    assert L.coll_allreduce(s, r, 4, n, 0, 3, None) == INV            # bad op
+    assert L.coll_allreduce_algo(s, r, 4, n, 0, 0, 7, None) == INV    # bad algo
+    assert L.coll_allreduce(None, r, 4, n, 0, 0, None) == INV         # null array
+    assert L.coll_allreduce(s, r, 4, 1 << 61, 0, 0, None) == INV      # size overflow
+    z, _kz = _arr([base, 0, base + 0x200000, base + 0x300000])
+    assert L.coll_allreduce(z, r, 4, n, 0, 0, None) == INV            # null entry
+    m, _km = _arr([base + 2, base + 0x100000, base + 0x200000, base + 0x300000])
+    assert L.coll_allreduce(m, r, 4, n, 0, 0, None) == INV            # fp32 pointer not 4-byte aligned
+    assert L.coll_reduce(s, base + 0x20000000, 4, n, 0, 0, 4, None) == INV   # root out of range
+    assert L.coll_reduce(s, base + 0x20000000, 4, n, 0, 0, -1, None) == INV
+    assert L.coll_broadcast(base, r, 4, n, 0, 9, None) == INV
+    assert L.coll_broadcast(None, r, 4, n, 0, 0, None) == INV
+    caps = (ctypes.c_int64 * 4)(10, 10, 10, 10)
+    neg = (ctypes.c_int64 * 4)(10, -1, 10, 10)
+    huge = (ctypes.c_int64 * 4)(1 << 60, 10, 10, 10)
+    assert L.coll_alltoallv(s, r, 4, None, caps, caps, None, 0, None) == INV         # no counts
+    assert L.coll_alltoallv(s, r, 4, base + 0x40000000, neg, caps, None, 0, None) == INV
+    assert L.coll_alltoallv(s, r, 4, base + 0x40000000, huge, caps, None, 0, None) == INV
+    assert L.coll_alltoallv(s, r, 4, base + 0x40000004, caps, caps, None, 0, None) == INV  # counts misaligned
+    assert L.coll_allreduce_batch(None, 3, 4, 0, None) == INV
+    assert L.coll_allreduce_batch(None, 0, 4, 8, None) == INV        # unknown flag
+
+
+@host_only
+def test_illegal_aliasing_rejected():
+    L = coll.lib()
+    AL = coll.COLL_ERR_ALIAS
+    base = 0x7F0000000000
+    n, p, d = 256, 4, 4
+    nb = n * d
+    send = [base + 0x100000 * i for i in range(p)]
+    recv = [base + 0x10000000 + 0x100000 * i for i in range(p)]
+    s, _k1 = _arr(send)
+    # AllReduce: recv[0] overlaps send[1]
+    r, _k2 = _arr([send[1] + 4] + recv[1:])
+    assert L.coll_allreduce(s, r, p, n, 0, 0, None) == AL
+    # AllReduce: two outputs overlap
+    r, _k3 = _arr([recv[0], recv[0] + 8, recv[2], recv[3]])
+    assert L.coll_allreduce(s, r, p, n, 0, 0, None) == AL
+    # AllReduce: recv[1] == send[0] (in place only with its own rank)
+    r, _k4 = _arr([recv[0], send[0], recv[2], recv[3]])
+    assert L.coll_allreduce(s, r, p, n, 0, 0, None) == AL
+    # ReduceScatter: recv[2] inside send[2] but at block 0 instead of block 2
+    big = [base + 0x1000000 * i for i in range(p)]
+    sb, _k5 = _arr(big)
+    r, _k6 = _arr([recv[0], recv[1], big[2], recv[3]])
+    assert L.coll_reduce_scatter(sb, r, p, n, 0, 0, None) == AL
+    # AllGather: send[1] inside recv[1] at the wrong block
+    rg = [base + 0x1000000 * i for i in range(p)]
+    r, _k7 = _arr(rg)
+    sg, _k8 = _arr([send[0], rg[1], send[2], send[3]])
+    assert L.coll_allgather(sg, r, p, n, 0, None) == AL
+    # AllToAll: any overlap of recv with send
+    r, _k9 = _arr([send[0]] + recv[1:])
+    assert L.coll_alltoall(s, r, p, n // p, 0, None) == AL
+    # Broadcast: recv[1] == send_root while root is 0
+    r, _k10 = _arr([recv[0], send[0], recv[2], recv[3]])
+    assert L.coll_broadcast(send[0], r, p, n, 0, 0, None) == AL
+    # Reduce: root buffer overlaps a non-root input
+    assert L.coll_reduce(s, send[2], p, n, 0, 0, 1, None) == AL
+    # Alltoallv: counts array inside a receive buffer
+    caps = (ctypes.c_int64 * 4)(n, n, n, n)
+    r, _k11 = _arr(recv)
+    assert L.coll_alltoallv(s, r, p, recv[1] + 64, caps, caps, None, 0, None) == AL
+    assert nb > 0
