@@ -1,0 +1,481 @@
+#!/usr/bin/env python3
+"""Throughput of the collective primitives on one MI355X.
+
+The timed step is the ZeRO-style gradient path: ReduceScatter (sum) of
+p = 8 logical ranks' 2^26-element bf16 gradients (fp32 accumulation),
+then AllGather of the 2^23-element shards back to every rank.  All p
+ranks' buffers are resident in the one GPU's HBM, so HBM bandwidth plays
+the part of the network.  The JSON line reports
+
+* value: achieved HBM GB/s of the whole step (algorithmic bytes: every
+  input element read once, every output element written once, self
+  copies included), with busbw/algbw per collective after the bus
+  bandwidth conventions of "集合通信：原语、算法、NCCL 实现与拓扑映射"
+  (hpc/04, section 2.5);
+* roofline: the dominant kernel's algorithmic bytes per launch over its
+  mean duration (HIP events on the launch stream) against 8 TB/s, plus
+  the HBM traffic read from rocprofv3 FETCH_SIZE / WRITE_SIZE counters
+  when a counter summary for the current kernel sources is on file;
+* cpu_baseline: the CPU oracle on a bounded slice of the same workload;
+* collectives: the other p = 8 collectives (AllReduce three ways,
+  All-to-All, Alltoallv), the small AllReduce at p = 4, the 10,000-call
+  batched AllReduce at p = 16 and the box's copy ceiling, each timed
+  with HIP events.
+
+Only one GPU is used; --gpus above 1 is refused.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "busbw and achieved HBM GB/s (% of peak) per collective at p=8, 1 GPU"
+HBM_PEAK = 8000.0  # GB/s, MI355X HBM3E published peak
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "collective_communication_primitives_coll_amd", "csrc")
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-collectives", action="store_true", help="time only the main step")
+    ap.add_argument("--only", default=None,
+                    help="comma list of extra collectives to time (ar_ring, ar_onepass, ar_literal, "
+                         "a2a, a2av, ar_small, batch, copy)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
+    return ap.parse_args(argv)
+
+
+def source_hash() -> str:
+    """SHA-256 over the HIP/C++ sources: identifies the kernels a counter summary was taken on."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            h.update(name.encode())
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ----------------------------------------------------------------------------
+# Device plumbing
+# ----------------------------------------------------------------------------
+
+def to_dev(torch, a: np.ndarray, dev):
+    if a.dtype == np.uint16:   # bf16 bit patterns
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def to_host_bits(t) -> np.ndarray:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    if t.dtype == torch.float32:
+        return t.cpu().numpy().view(np.uint32)
+    return t.cpu().numpy()
+
+
+def time_launches(torch, fns, iters: int, warmup: int):
+    """Run the launch sequence fns warmup + iters times; per fn, the list of
+    durations (ms) between HIP events recorded on the launch stream."""
+    for _ in range(warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(iters)]
+    for i in range(iters):
+        ev[i][0].record()
+        for k, f in enumerate(fns):
+            f()
+            ev[i][k + 1].record()
+    torch.cuda.synchronize()
+    return [[ev[i][k].elapsed_time(ev[i][k + 1]) for i in range(iters)] for k in range(len(fns))]
+
+
+def stats_us(ms_list):
+    a = np.asarray(ms_list, dtype=np.float64) * 1e3
+    return float(np.median(a)), float(np.percentile(a, 95)), float(a.mean())
+
+
+def coll_entry(metrics, name, coll_kind, p, n, d, t_us, algo="ring", extra=None):
+    """One row of the per-collective table from a median time."""
+    s = t_us * 1e-6
+    hbm = metrics.hbm_bytes(coll_kind, p, n, d, algo)
+    row = {
+        "name": name, "p": p, "n": n, "elem_bytes": d,
+        "t_med_us": round(t_us, 2),
+        "algbw_GBps": round(metrics.algbw_gbps(coll_kind, p, n, d, s), 1),
+        "busbw_GBps": round(metrics.busbw_gbps(coll_kind, p, n, d, s), 1),
+        "hbm_bytes": hbm,
+        "hbm_GBps": round(hbm / s / 1e9, 1),
+        "pct_hbm_peak": round(100.0 * hbm / s / 1e9 / HBM_PEAK, 1),
+    }
+    if extra:
+        row.update(extra)
+    return row
+
+
+# ----------------------------------------------------------------------------
+# Counter summary (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE), if on file
+# ----------------------------------------------------------------------------
+
+def read_traffic(kernel_key: str, launches_bytes: int):
+    """HBM bytes per launch of kernel_key from profiles/hbm_traffic_*.txt.
+
+    The file holds `source_hash:`, `copy_fetch_factor:`, `copy_write_factor:`
+    and per-kernel `kernel <key> fetch_kib <F> write_kib <W>` lines; the
+    factors scale the raw counters by what they read for a plain copy of
+    known size.  Returns None when no summary matches the current sources.
+    """
+    if not os.path.isdir(PROFILES):
+        return None
+    cur = source_hash()
+    for name in sorted(os.listdir(PROFILES)):
+        if not (name.startswith("hbm_traffic_") and name.endswith(".txt")):
+            continue
+        kv, kern = {}, {}
+        with open(os.path.join(PROFILES, name), encoding="utf-8") as f:
+            for line in f:
+                line = line.strip()
+                m = re.match(r"^kernel\s+(\S+)\s+fetch_kib\s+([\d.]+)\s+write_kib\s+([\d.]+)", line)
+                if m:
+                    kern[m.group(1)] = (float(m.group(2)), float(m.group(3)))
+                    continue
+                m = re.match(r"^([a-z_]+):\s*(\S+)", line)
+                if m:
+                    kv[m.group(1)] = m.group(2)
+        if kv.get("source_hash") != cur or kernel_key not in kern:
+            continue
+        ff = float(kv.get("copy_fetch_factor", "1"))
+        wf = float(kv.get("copy_write_factor", "1"))
+        fk, wk = kern[kernel_key]
+        return int(round(fk * 1024 * ff + wk * 1024 * wf))
+    return None
+
+
+# ----------------------------------------------------------------------------
+# Workloads
+# ----------------------------------------------------------------------------
+
+def zero_workload(torch, coll, inputs, dev):
+    """ReduceScatter then AllGather, p = 8, 2^26 bf16 per rank ~ N(0, 1e-3)."""
+    p, total = 8, 1 << 26
+    n = total // p
+    hx = inputs.rank_buffers(inputs.WL_ZERO_RS_AG, p, total, inputs.BF16, dist="normal", sigma=1e-3)
+    send = [to_dev(torch, x, dev) for x in hx]
+    shard = [torch.empty(n, dtype=torch.bfloat16, device=dev) for _ in range(p)]
+    full = [torch.empty(total, dtype=torch.bfloat16, device=dev) for _ in range(p)]
+    rs = coll.coll_reduce_scatter(send, shard, coll.COLL_SUM, defer=True)
+    ag = coll.coll_allgather(shard, full, defer=True)
+    return dict(p=p, n=n, total=total, hx=hx, send=send, shard=shard, full=full, rs=rs, ag=ag)
+
+
+def cpu_baseline(wl, cpu_seconds: float):
+    """The CPU oracle on a slice of the ZeRO workload: the first m elements
+    of every rank's block r, for all r (ReduceScatter then AllGather of
+    that slice), repeated until cpu_seconds have passed.  Also checks the
+    GPU output on the same slice."""
+    from oracle import ref
+    from collective_communication_primitives_coll_amd import metrics
+
+    p, n, hx = wl["p"], wl["n"], wl["hx"]
+    m = 1 << 19
+    xs = [np.concatenate([x[r * n:r * n + m] for r in range(p)]) for x in hx]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        shards = ref.reduce_scatter(xs, ref.SUM, ref.BF16)
+        gathered = ref.allgather(shards)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= cpu_seconds:
+            break
+    per = el / reps
+    # algorithmic HBM-equivalent bytes of the slice: RS (p*p*m read, p*m written)
+    # plus AG (p*m read, p*p*m written), bf16
+    alg = metrics.hbm_bytes("reduce_scatter", p, m, 2) + metrics.hbm_bytes("allgather", p, m, 2)
+    agree = all(np.array_equal(to_host_bits(wl["shard"][r][:m]), shards[r]) for r in range(p))
+    j = p - 1
+    got = to_host_bits(wl["full"][j])
+    agree = agree and all(np.array_equal(got[r * n:r * n + m], gathered[j][r * m:(r + 1) * m])
+                          for r in range(p))
+    return {
+        "value": round(alg / per / 1e9, 3),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"oracle/ref.py (NumPy, single thread) ReduceScatter+AllGather on the first "
+                   f"{m} elements of each of the 8 blocks of every rank (1/16 of the step), "
+                   f"{reps} repetitions in {el:.1f} s; GB/s of the same algorithmic HBM bytes"),
+        "ms_per_sample": round(per * 1e3, 1),
+        "host_cpus": os.cpu_count(),
+        "gpu_matches_oracle_on_sample": bool(agree),
+    }
+
+
+def extra_collectives(torch, coll, inputs, metrics, dev, which, iters=10, warmup=3):
+    rows = []
+    want = lambda k: which is None or k in which  # noqa: E731
+
+    # --- DP gradient AllReduce, p = 8, 256 MiB fp32 per rank ~ N(0, 1) -------
+    if want("ar_ring") or want("ar_onepass") or want("ar_literal"):
+        p, n = 8, 1 << 26
+        send = [to_dev(torch, x, dev) for x in inputs.rank_buffers(inputs.WL_DP_RING_AR, p, n, inputs.F32,
+                                                                    dist="normal")]
+        recv = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(p)]
+        for key, algo, label, aname in (
+                ("ar_ring", coll.COLL_ALGO_RING, "allreduce_ring_fused", "ring"),
+                ("ar_onepass", coll.COLL_ALGO_ONEPASS, "allreduce_onepass_tree", "ring"),
+                ("ar_literal", coll.COLL_ALGO_RING_LITERAL, "allreduce_ring_literal_14_steps",
+                 "ring_literal")):
+            if not want(key):
+                continue
+            f = coll.coll_allreduce_algo(send, recv, algo, coll.COLL_SUM, defer=True)
+            med, p95, _ = stats_us(time_launches(torch, [f], iters, warmup)[0])
+            rows.append(coll_entry(metrics, label, "allreduce", p, n, 4, med, aname,
+                                   {"dtype": "f32", "op": "sum", "t_p95_us": round(p95, 2),
+                                    "workload": "DP gradient AllReduce, 256 MiB fp32 per rank"}))
+        del send, recv
+        torch.cuda.empty_cache()
+
+    # --- MoE dispatch All-to-All, p = 8, 4096 x 7168 bf16 per rank ----------
+    if want("a2a") or want("a2av"):
+        p, tokens, hidden = 8, 4096, 7168
+        per = tokens * hidden
+        send = [to_dev(torch, x, dev) for x in inputs.rank_buffers(inputs.WL_MOE_A2A, p, per, inputs.BF16,
+                                                                    dist="normal")]
+        if want("a2a"):
+            recv = [torch.empty(per, dtype=torch.bfloat16, device=dev) for _ in range(p)]
+            f = coll.coll_alltoall(send, recv, per // p, defer=True)
+            med, p95, _ = stats_us(time_launches(torch, [f], iters, warmup)[0])
+            rows.append(coll_entry(metrics, "alltoall_equal", "alltoall", p, per // p, 2, med, "ring",
+                                   {"dtype": "bf16", "t_p95_us": round(p95, 2),
+                                    "workload": "MoE dispatch, 512 tokens x 7168 per destination"}))
+            del recv
+        if want("a2av"):
+            ctok = inputs.moe_token_counts(p, tokens)
+            counts = ctok * hidden
+            cols = counts.sum(axis=0)
+            recv = [torch.empty(int(c), dtype=torch.bfloat16, device=dev) for c in cols]
+            cdev = torch.from_numpy(counts.reshape(-1).copy()).to(dev)
+            f = coll.coll_alltoallv(send, recv, cdev, defer=True)
+            med, p95, _ = stats_us(time_launches(torch, [f], iters, warmup)[0])
+            hbm = int(2 * counts.sum() * 2)
+            s = med * 1e-6
+            b_local = per * 2
+            rows.append({
+                "name": "alltoallv_multinomial", "p": p, "elem_bytes": 2, "dtype": "bf16",
+                "t_med_us": round(med, 2), "t_p95_us": round(p95, 2),
+                "algbw_GBps": round(b_local / s / 1e9, 1),
+                "busbw_GBps": round(b_local / s / 1e9 * metrics.busbw_factor("alltoallv", p), 1),
+                "hbm_bytes": hbm, "hbm_GBps": round(hbm / s / 1e9, 1),
+                "pct_hbm_peak": round(100.0 * hbm / s / 1e9 / HBM_PEAK, 1),
+                "max_row_tokens": int(ctok.sum(axis=1).max()), "max_col_tokens": int(ctok.sum(axis=0).max()),
+                "zero_ratio": float((ctok == 0).mean()),
+                "workload": "MoE dispatch, per-source token counts ~ Multinomial(4096, 1/8)",
+            })
+            del recv, cdev
+        del send
+        torch.cuda.empty_cache()
+
+    # --- small AllReduce, p = 4, 2^20 per rank (Infinity-Cache resident) ------
+    if want("ar_small"):
+        p, n = 4, 1 << 20
+        for dt, op, dname, oname in ((inputs.F32, coll.COLL_SUM, "f32", "sum"),
+                                     (inputs.I32, coll.COLL_MIN, "i32", "min"),
+                                     (inputs.I32, coll.COLL_MAX, "i32", "max")):
+            send = [to_dev(torch, x, dev) for x in inputs.rank_buffers(inputs.WL_AR_SMALL, p, n, dt)]
+            tdt = torch.float32 if dt == inputs.F32 else torch.int32
+            recv = [torch.empty(n, dtype=tdt, device=dev) for _ in range(p)]
+            f = coll.coll_allreduce(send, recv, op, defer=True)
+            med, p95, _ = stats_us(time_launches(torch, [f], 50, 10)[0])
+            rows.append(coll_entry(metrics, f"allreduce_small_{oname}", "allreduce", p, n, 4, med, "ring",
+                                   {"dtype": dname, "op": oname, "t_p95_us": round(p95, 2),
+                                    "workload": "AllReduce p=4, 2^20 per rank, back to back (warm)"}))
+
+    # --- 10,000 small AllReduces in one launch, p = 16 -----------------------
+    if want("batch"):
+        rows.append(batch_row(torch, coll, inputs, dev))
+
+    # --- copy ceiling ---------------------------------------------------------
+    if want("copy"):
+        nbytes = 1 << 30
+        a = torch.empty(nbytes // 4, dtype=torch.int32, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        med_t, _, _ = stats_us(time_launches(torch, [lambda: b.copy_(a)], iters, warmup)[0])
+        f = coll.coll_broadcast(a, [b], 0, defer=True)
+        med_c, _, _ = stats_us(time_launches(torch, [f], iters, warmup)[0])
+        rows.append({"name": "copy_ceiling", "bytes_read": nbytes, "bytes_written": nbytes,
+                     "torch_copy_GBps": round(2 * nbytes / (med_t * 1e-6) / 1e9, 1),
+                     "coll_copy_kernel_GBps": round(2 * nbytes / (med_c * 1e-6) / 1e9, 1),
+                     "note": "1 GiB device-to-device: torch copy_ and coll_broadcast with p=1"})
+        del a, b
+        torch.cuda.empty_cache()
+    return rows
+
+
+def batch_row(torch, coll, inputs, dev, iters=5, warmup=2):
+    p = 16
+    plan, out_elems = inputs.small_batch_plan(10000)
+    pf, pi = inputs.small_batch_pools(p)
+    dpf = [to_dev(torch, x, dev) for x in pf]
+    dpi = [to_dev(torch, x, dev) for x in pi]
+    outs = [torch.empty(out_elems, dtype=torch.int32, device=dev) for _ in range(p)]
+    base_f = [t.data_ptr() for t in dpf]
+    base_i = [t.data_ptr() for t in dpi]
+    base_o = [t.data_ptr() for t in outs]
+    calls, total_bytes = [], 0
+    for c in plan:
+        src = base_f if c.dtype == inputs.F32 else base_i
+        calls.append(([b + 4 * c.src_off for b in src], [b + 4 * c.dst_off for b in base_o], c.n, c.dtype, c.op))
+        total_bytes += 4 * c.n
+    f = coll.coll_allreduce_batch(calls, p, defer=True)
+    # wall time of whole calls (host validation + descriptor upload + kernel)
+    for _ in range(warmup):
+        f()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(iters):
+        f()
+    torch.cuda.synchronize()
+    wall_us = (time.perf_counter() - t0) / iters * 1e6
+    med, p95, _ = stats_us(time_launches(torch, [f], iters, 1)[0])
+    hbm = 2 * p * total_bytes
+    return {
+        "name": "allreduce_batch_10000", "p": p, "calls": len(plan), "dtype": "f32/i32", "op": "sum/min/max",
+        "payload_bytes": total_bytes,
+        "t_med_us": round(med, 1), "t_p95_us": round(p95, 1), "wall_us_per_batch": round(wall_us, 1),
+        "us_per_call": round(med / len(plan), 4),
+        "hbm_bytes": hbm, "hbm_GBps": round(hbm / (med * 1e-6) / 1e9, 1),
+        "pct_hbm_peak": round(100.0 * hbm / (med * 1e-6) / 1e9 / HBM_PEAK, 1),
+        "busbw_GBps": round(total_bytes / (med * 1e-6) / 1e9 * 2 * (p - 1) / p, 1),
+        "workload": "10,000 AllReduces, sizes log-uniform 4 KiB-1 MiB, one launch",
+    }
+
+
+# ----------------------------------------------------------------------------
+
+def main(argv=None) -> int:
+    args = parse_args(argv)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: all p logical ranks live in one device's HBM and "
+              "nothing here runs across GPUs; run it with --gpus 1.", file=sys.stderr)
+        return 2
+    import torch
+
+    import collective_communication_primitives_coll_amd as coll
+    from collective_communication_primitives_coll_amd import inputs, metrics
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    coll.lib()
+
+    wl = zero_workload(torch, coll, inputs, dev)
+    p, n, total = wl["p"], wl["n"], wl["total"]
+    rs, ag = wl["rs"], wl["ag"]
+    print(f"# zero_rs_ag: p={p} n_shard={n} bf16, warmup {args.warmup}, steps {args.steps}",
+          file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        rs()
+        ag()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record()
+        rs()
+        ev[i][1].record()
+        ag()
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_rs = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
+    t_ag = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
+    ms_per_step = wall * 1e3 / K
+
+    hbm_rs = metrics.hbm_bytes("reduce_scatter", p, n, 2)
+    hbm_ag = metrics.hbm_bytes("allgather", p, n, 2)
+    value = (hbm_rs + hbm_ag) / (ms_per_step * 1e-3) / 1e9
+    rs_med, rs_p95, rs_mean = stats_us(t_rs)
+    ag_med, ag_p95, ag_mean = stats_us(t_ag)
+    per_coll = {
+        "reduce_scatter": coll_entry(metrics, "reduce_scatter", "reduce_scatter", p, n, 2, rs_med, "ring",
+                                     {"t_p95_us": round(rs_p95, 2), "t_mean_us": round(rs_mean, 2)}),
+        "allgather": coll_entry(metrics, "allgather", "allgather", p, n, 2, ag_med, "ring",
+                                {"t_p95_us": round(ag_p95, 2), "t_mean_us": round(ag_mean, 2)}),
+    }
+    # dominant kernel: the longer of the two launches
+    if rs_mean >= ag_mean:
+        dom, dom_bytes, dom_us, kkey = "reduce_kernel<bf16,sum,p=8> (coll_reduce_scatter)", hbm_rs, rs_mean, "reduce_scatter"
+    else:
+        dom, dom_bytes, dom_us, kkey = "copy_kernel<2B> (coll_allgather)", hbm_ag, ag_mean, "allgather"
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK, 4), "traffic": read_traffic(kkey, dom_bytes),
+                "kernel": dom, "algorithmic_bytes_per_launch": dom_bytes, "mean_launch_us": round(dom_us, 2)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+
+    del wl, rs, ag
+    torch.cuda.empty_cache()
+    rows = []
+    if not args.no_collectives:
+        which = set(args.only.split(",")) if args.only else None
+        print("# per-collective table", file=sys.stderr, flush=True)
+        rows = extra_collectives(torch, coll, inputs, metrics, dev, which)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded NumPy PCG64, bf16 ~ N(0, 1e-3))",
+        "config": {
+            "workload": "zero_rs_ag: ReduceScatter(sum) then AllGather, p=8 logical ranks, "
+                        "2^26 bf16 elements per rank, fp32 accumulation, shard 2^23",
+            "p": p, "elements_per_rank": total, "storage": "bf16", "accumulate": "f32",
+            "hbm_bytes_per_step": hbm_rs + hbm_ag,
+            "pct_hbm_peak": round(100.0 * value / HBM_PEAK, 1),
+        },
+        "per_collective": per_coll,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "collectives": rows,
+        "source_hash": source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

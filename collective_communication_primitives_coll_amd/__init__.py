@@ -143,6 +143,31 @@ def _check(status: int, what: str) -> None:
         raise CollError(status, f"{what}: {msg}")
 
 
+class Prepared:
+    """A C-ABI call whose arguments were marshalled once.
+
+    Calling it launches the same collective again on the same buffers and
+    stream; it raises CollError on a non-OK status like the direct call.
+    """
+
+    def __init__(self, fname: str, args: tuple, what: str, keep: tuple):
+        self._f = getattr(lib(), fname)
+        self._args = args
+        self._what = what
+        self._keep = keep   # ctypes arrays the argument pointers refer to
+
+    def __call__(self) -> None:
+        _check(self._f(*self._args), self._what)
+
+
+def _run(fname: str, args: tuple, what: str, defer: bool, keep: tuple = ()):
+    """Call fname(*args) now, or with defer=True return it as a Prepared call."""
+    if defer:
+        return Prepared(fname, args, what, keep)
+    _check(getattr(lib(), fname)(*args), what)
+    return None
+
+
 def _check_sizes(xs: Sequence[Any], need: int, what: str) -> None:
     for x in xs:
         if hasattr(x, "numel") and x.numel() < need:
@@ -161,12 +186,12 @@ def _same_dtype(xs: Sequence[Any], dt: int) -> None:
 # ----------------------------------------------------------------------------
 
 def coll_allreduce(send, recv, op: int = COLL_SUM, n: int | None = None, dtype: int | None = None,
-                   stream=None) -> None:
-    coll_allreduce_algo(send, recv, COLL_ALGO_RING, op, n, dtype, stream)
+                   stream=None, defer: bool = False):
+    return coll_allreduce_algo(send, recv, COLL_ALGO_RING, op, n, dtype, stream, defer)
 
 
 def coll_allreduce_algo(send, recv, algo: int, op: int = COLL_SUM, n: int | None = None,
-                        dtype: int | None = None, stream=None) -> None:
+                        dtype: int | None = None, stream=None, defer: bool = False):
     p = len(send)
     if len(recv) != p:
         raise ValueError("send and recv must list the same ranks")
@@ -174,36 +199,38 @@ def coll_allreduce_algo(send, recv, algo: int, op: int = COLL_SUM, n: int | None
     n = _numel(send[0], n)
     _same_dtype([*send, *recv], dt)
     _check_sizes([*send, *recv], n, "allreduce")
-    s, _k1 = _ptr_array(send)
-    r, _k2 = _ptr_array(recv)
-    _check(lib().coll_allreduce_algo(s, r, p, n, dt, int(op), int(algo), _stream(stream)), "coll_allreduce")
+    s, k1 = _ptr_array(send)
+    r, k2 = _ptr_array(recv)
+    return _run("coll_allreduce_algo", (s, r, p, n, dt, int(op), int(algo), _stream(stream)),
+                "coll_allreduce", defer, (k1, k2))
 
 
 def coll_reduce(send, recv_root, root: int, op: int = COLL_SUM, n: int | None = None,
-                dtype: int | None = None, stream=None) -> None:
+                dtype: int | None = None, stream=None, defer: bool = False):
     p = len(send)
     dt = _dtype_of(send[0], dtype)
     n = _numel(send[0], n)
     _same_dtype([*send, recv_root], dt)
     _check_sizes([*send, recv_root], n, "reduce")
-    s, _k = _ptr_array(send)
-    _check(lib().coll_reduce(s, _addr(recv_root), p, n, dt, int(op), int(root), _stream(stream)),
-           "coll_reduce")
+    s, k = _ptr_array(send)
+    return _run("coll_reduce", (s, _addr(recv_root), p, n, dt, int(op), int(root), _stream(stream)),
+                "coll_reduce", defer, (k,))
 
 
 def coll_broadcast(send_root, recv, root: int, n: int | None = None, dtype: int | None = None,
-                   stream=None) -> None:
+                   stream=None, defer: bool = False):
     p = len(recv)
     dt = _dtype_of(send_root, dtype)
     n = _numel(send_root, n)
     _same_dtype([send_root, *recv], dt)
     _check_sizes([send_root, *recv], n, "broadcast")
-    r, _k = _ptr_array(recv)
-    _check(lib().coll_broadcast(_addr(send_root), r, p, n, dt, int(root), _stream(stream)), "coll_broadcast")
+    r, k = _ptr_array(recv)
+    return _run("coll_broadcast", (_addr(send_root), r, p, n, dt, int(root), _stream(stream)),
+                "coll_broadcast", defer, (k,))
 
 
 def coll_reduce_scatter(send, recv, op: int = COLL_SUM, n: int | None = None, dtype: int | None = None,
-                        stream=None) -> None:
+                        stream=None, defer: bool = False):
     """n = elements each rank receives; send[r] holds p*n."""
     p = len(send)
     dt = _dtype_of(send[0], dtype)
@@ -211,12 +238,14 @@ def coll_reduce_scatter(send, recv, op: int = COLL_SUM, n: int | None = None, dt
     _same_dtype([*send, *recv], dt)
     _check_sizes(send, p * n, "reduce_scatter send")
     _check_sizes(recv, n, "reduce_scatter recv")
-    s, _k1 = _ptr_array(send)
-    r, _k2 = _ptr_array(recv)
-    _check(lib().coll_reduce_scatter(s, r, p, n, dt, int(op), _stream(stream)), "coll_reduce_scatter")
+    s, k1 = _ptr_array(send)
+    r, k2 = _ptr_array(recv)
+    return _run("coll_reduce_scatter", (s, r, p, n, dt, int(op), _stream(stream)),
+                "coll_reduce_scatter", defer, (k1, k2))
 
 
-def coll_allgather(send, recv, n: int | None = None, dtype: int | None = None, stream=None) -> None:
+def coll_allgather(send, recv, n: int | None = None, dtype: int | None = None, stream=None,
+                   defer: bool = False):
     """n = elements each rank sends; recv[r] holds p*n."""
     p = len(send)
     dt = _dtype_of(send[0], dtype)
@@ -224,12 +253,13 @@ def coll_allgather(send, recv, n: int | None = None, dtype: int | None = None, s
     _same_dtype([*send, *recv], dt)
     _check_sizes(send, n, "allgather send")
     _check_sizes(recv, p * n, "allgather recv")
-    s, _k1 = _ptr_array(send)
-    r, _k2 = _ptr_array(recv)
-    _check(lib().coll_allgather(s, r, p, n, dt, _stream(stream)), "coll_allgather")
+    s, k1 = _ptr_array(send)
+    r, k2 = _ptr_array(recv)
+    return _run("coll_allgather", (s, r, p, n, dt, _stream(stream)), "coll_allgather", defer, (k1, k2))
 
 
-def coll_alltoall(send, recv, n_block: int | None = None, dtype: int | None = None, stream=None) -> None:
+def coll_alltoall(send, recv, n_block: int | None = None, dtype: int | None = None, stream=None,
+                  defer: bool = False):
     """send[i] and recv[j] hold p blocks of n_block elements."""
     p = len(send)
     dt = _dtype_of(send[0], dtype)
@@ -237,14 +267,15 @@ def coll_alltoall(send, recv, n_block: int | None = None, dtype: int | None = No
         n_block = _numel(send[0], None) // p
     _same_dtype([*send, *recv], dt)
     _check_sizes([*send, *recv], p * n_block, "alltoall")
-    s, _k1 = _ptr_array(send)
-    r, _k2 = _ptr_array(recv)
-    _check(lib().coll_alltoall(s, r, p, int(n_block), dt, _stream(stream)), "coll_alltoall")
+    s, k1 = _ptr_array(send)
+    r, k2 = _ptr_array(recv)
+    return _run("coll_alltoall", (s, r, p, int(n_block), dt, _stream(stream)), "coll_alltoall", defer,
+                (k1, k2))
 
 
 def coll_alltoallv(send, recv, counts_dev, send_cap: Sequence[int] | None = None,
                    recv_cap: Sequence[int] | None = None, status_dev=None, dtype: int | None = None,
-                   stream=None) -> None:
+                   stream=None, defer: bool = False):
     """counts_dev: device int64 [p, p] (row = source).  Capacities default to
     the tensors' sizes."""
     p = len(send)
@@ -258,16 +289,17 @@ def coll_alltoallv(send, recv, counts_dev, send_cap: Sequence[int] | None = None
         if counts_dev.dtype != torch.int64 or counts_dev.numel() < p * p:
             raise ValueError("counts must be a device int64 tensor with p*p entries")
     _same_dtype([*send, *recv], dt)
-    s, _k1 = _ptr_array(send)
-    r, _k2 = _ptr_array(recv)
+    s, k1 = _ptr_array(send)
+    r, k2 = _ptr_array(recv)
     sc = (ctypes.c_int64 * p)(*[int(v) for v in send_cap])
     rc = (ctypes.c_int64 * p)(*[int(v) for v in recv_cap])
     st = _addr(status_dev) if status_dev is not None else None
-    _check(lib().coll_alltoallv(s, r, p, _addr(counts_dev), sc, rc, st, dt, _stream(stream)),
-           "coll_alltoallv")
+    return _run("coll_alltoallv", (s, r, p, _addr(counts_dev), sc, rc, st, dt, _stream(stream)),
+                "coll_alltoallv", defer, (k1, k2, sc, rc))
 
 
-def coll_allreduce_batch(calls: Sequence[tuple], p: int, flags: int = 0, stream=None) -> None:
+def coll_allreduce_batch(calls: Sequence[tuple], p: int, flags: int = 0, stream=None,
+                         defer: bool = False):
     """calls: (send list, recv list, n, dtype, op) per AllReduce."""
     keep = []
     arr = (coll_call_t * len(calls))()
@@ -279,8 +311,8 @@ def coll_allreduce_batch(calls: Sequence[tuple], p: int, flags: int = 0, stream=
         keep.append((ks, kr))
         arr[k].send, arr[k].recv = s, r
         arr[k].n, arr[k].dtype, arr[k].op = int(n), int(dtype), int(op)
-    _check(lib().coll_allreduce_batch(arr, len(calls), int(p), int(flags), _stream(stream)),
-           "coll_allreduce_batch")
+    return _run("coll_allreduce_batch", (arr, len(calls), int(p), int(flags), _stream(stream)),
+                "coll_allreduce_batch", defer, (arr, keep))
 
 
 def coll_status_string(status: int) -> str:
