@@ -38,7 +38,11 @@ struct DevInfo {
 DevInfo g_dev[64];
 std::atomic<int> g_wg_per_cu{0};
 
-constexpr int kDefaultWgPerCu = 8;
+// Default workgroups (of 256 threads) per compute unit, per kernel family.
+// Reductions keep 16-32 loads in flight per lane and run best with one
+// workgroup per CU; copies with two.
+enum Family { kFamReduce = 0, kFamCopy = 1 };
+constexpr int kDefaultWgPerCu[2] = {1, 2};
 
 int current_device(int* dev) { return (int)hipGetDevice(dev); }
 
@@ -59,14 +63,14 @@ int device_cus(int dev, int* out) {
 }
 
 // Grid limit: workgroups per CU times CUs of the current device.
-int max_grid(int* out) {
+int max_grid(int* out, Family fam) {
   int dev = 0, cus = 0;
   int e = current_device(&dev);
   if (e) return e;
   e = device_cus(dev, &cus);
   if (e) return e;
   int w = g_wg_per_cu.load(std::memory_order_relaxed);
-  if (w <= 0) w = kDefaultWgPerCu;
+  if (w <= 0) w = kDefaultWgPerCu[fam];
   *out = cus * w;
   return 0;
 }
@@ -190,7 +194,7 @@ COLL_EXPORT coll_status_t coll_allreduce_algo(const void* const* send, void* con
   if (algo == COLL_ALGO_ONEPASS && !(p == 2 || p == 4 || p == 8 || p == 16)) return COLL_ERR_UNSUPPORTED;
   if (algo == COLL_ALGO_RING_LITERAL && dtype == COLL_BF16) return COLL_ERR_UNSUPPORTED;
   int grid;
-  int e = max_grid(&grid);
+  int e = max_grid(&grid, algo == COLL_ALGO_RING_LITERAL ? kFamCopy : kFamReduce);
   if (e) return hip_fail(e);
   const int smis = common_mis(send, p), dmis = common_mis((const void* const*)recv, p);
   if (algo == COLL_ALGO_RING_LITERAL) {
@@ -250,7 +254,7 @@ COLL_EXPORT coll_status_t coll_reduce(const void* const* send, void* recv_root, 
   });
   if (st != COLL_OK) return st;
   int grid;
-  int e = max_grid(&grid);
+  int e = max_grid(&grid, kFamReduce);
   if (e) return hip_fail(e);
   void* dst[1] = {recv_root};
   coll::RankPtrs P = make_ptrs(send, p, dst, 1);
@@ -281,7 +285,7 @@ COLL_EXPORT coll_status_t coll_broadcast(const void* send_root, void* const* rec
   });
   if (st != COLL_OK) return st;
   int grid;
-  int e = max_grid(&grid);
+  int e = max_grid(&grid, kFamCopy);
   if (e) return hip_fail(e);
   const void* src[1] = {send_root};
   coll::RankPtrs P = make_ptrs(src, 1, recv, p);
@@ -308,7 +312,7 @@ COLL_EXPORT coll_status_t coll_reduce_scatter(const void* const* send, void* con
   });
   if (st != COLL_OK) return st;
   int grid;
-  int e = max_grid(&grid);
+  int e = max_grid(&grid, kFamReduce);
   if (e) return hip_fail(e);
   coll::RankPtrs P = make_ptrs(send, p, recv, p);
   coll::ReduceGeom g{};
@@ -339,7 +343,7 @@ COLL_EXPORT coll_status_t coll_allgather(const void* const* send, void* const* r
   });
   if (st != COLL_OK) return st;
   int grid;
-  int e = max_grid(&grid);
+  int e = max_grid(&grid, kFamCopy);
   if (e) return hip_fail(e);
   coll::RankPtrs P = make_ptrs(send, p, recv, p);
   coll::CopyGeom g{n, p, coll::kCopyAllGather, common_mis(send, p), common_mis((const void* const*)recv, p)};
@@ -361,7 +365,7 @@ COLL_EXPORT coll_status_t coll_alltoall(const void* const* send, void* const* re
   coll_status_t st = check_alias(rs, [](const Range&, const Range&) { return false; });
   if (st != COLL_OK) return st;
   int grid;
-  int e = max_grid(&grid);
+  int e = max_grid(&grid, kFamCopy);
   if (e) return hip_fail(e);
   coll::RankPtrs P = make_ptrs(send, p, recv, p);
   coll::CopyGeom g{n_block, p, coll::kCopyAllToAll, common_mis(send, p),
@@ -402,7 +406,7 @@ COLL_EXPORT coll_status_t coll_alltoallv(const void* const* send, void* const* r
   const size_t lds = (size_t)3 * p * p * sizeof(int64_t) + 64;
   if (lds > (size_t)g_dev[dev].lds_per_block.load()) return COLL_ERR_UNSUPPORTED;
   int grid;
-  e = max_grid(&grid);
+  e = max_grid(&grid, kFamCopy);
   if (e) return hip_fail(e);
   coll::RankPtrs P = make_ptrs(send, p, recv, p);
   coll::A2avArgs a;
@@ -503,7 +507,7 @@ COLL_EXPORT coll_status_t coll_allreduce_batch(const coll_call_t* calls, int nca
     b.dtype = (uint32_t)c.dtype;
     b.op = (uint32_t)c.op;
     b.mis = c.n ? common_mis2(common_mis(c.send, p), common_mis((const void* const*)c.recv, p)) : -1;
-    const uint64_t te = (uint64_t)256 * (c.dtype == COLL_BF16 ? 8 : 4);
+    const uint64_t te = coll::batch_tile_elems_host(c.dtype, p);
     const uint64_t q = (c.n + p - 1) / p;
     b.tiles_per_chunk = c.n ? (uint32_t)std::max<uint64_t>(1, (q + te - 1) / te) : 0;
     if (c.n && (q + te - 1) / te > 0xffffffffull) return COLL_ERR_INVALID_ARG;
@@ -520,7 +524,7 @@ COLL_EXPORT coll_status_t coll_allreduce_batch(const coll_call_t* calls, int nca
   int e = current_device(&dev);
   if (e) return hip_fail(e);
   int grid;
-  e = max_grid(&grid);
+  e = max_grid(&grid, kFamReduce);
   if (e) return hip_fail(e);
 
   std::lock_guard<std::mutex> lock(g_batch.mu);

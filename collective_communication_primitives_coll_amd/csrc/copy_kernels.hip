@@ -13,123 +13,51 @@
 //              prefix sums of the count matrix ("Collective Communication：
 //              AllReduce、AllGather、ReduceScatter 与 All-to-All", ragged
 //              All-to-All).
-// A lane loads kCopyUnroll 16-byte vectors, then stores each to every
-// destination of the segment; the copy is type-blind apart from the
-// element width used for misaligned heads and tails.
-#include "device_common.h"
+// Fan-out copies (one source, p destinations) load through the cache and
+// store non-temporally; 1:1 copies are non-temporal both ways.
+#include "copy_tile.h"
 
 namespace coll {
 
-template <int B>
-struct Word;
-template <>
-struct Word<2> {
-  using T = uint16_t;
-};
-template <>
-struct Word<4> {
-  using T = uint32_t;
-};
-
-template <int B>
-constexpr uint64_t copy_tile_elems() {
-  return kCopyUnroll * kBlock * (16 / B);
-}
-
-// Copy one tile of a segment.  src and dst(k) point at the segment start.
-template <int B, bool DSTALL, typename GD>
-__device__ __forceinline__ void copy_tile(const typename Word<B>::T* src, const GD& gdst, int ndst,
-                                          const TileSpan& sp) {
+// AllGather / Broadcast with a compile-time rank count P (0: any).
+// Destination pointers of a segment are read once into registers.
+template <int B, int KIND, int P>
+__global__ __launch_bounds__(kBlock) void fanout_kernel(RankPtrs ptrs, CopyGeom g) {
   using W = typename Word<B>::T;
-  constexpr int V = 16 / B;
-  constexpr int U = (int)kCopyUnroll;
-  const uint64_t tid = threadIdx.x;
-  auto elems = [&](uint64_t from, uint64_t cnt) {
-    for (uint64_t i = tid; i < cnt; i += kBlock) {
-      const uint64_t e = from + i;
-      const W w = ld1(src + e);
-      if constexpr (DSTALL) {
-        for (int k = 0; k < ndst; ++k) st1(gdst(k) + e, w);
-      } else {
-        st1(gdst(0) + e, w);
-      }
-    }
-  };
-  if (!sp.vec) {
-    elems(sp.begin, sp.head);
-    return;
-  }
-  if (sp.nvec) {
-    const uint64_t v0 = sp.begin + sp.head;
-    u32x4 r[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint64_t vi = (uint64_t)u * kBlock + tid;
-      if (vi < sp.nvec) r[u] = ld16(src + v0 + vi * V);
-    }
-    if constexpr (DSTALL) {
-      for (int k = 0; k < ndst; ++k) {
-        W* d = gdst(k);
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const uint64_t vi = (uint64_t)u * kBlock + tid;
-          if (vi < sp.nvec) st16(d + v0 + vi * V, r[u]);
-        }
-      }
-    } else {
-      W* d = gdst(0);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const uint64_t vi = (uint64_t)u * kBlock + tid;
-        if (vi < sp.nvec) st16(d + v0 + vi * V, r[u]);
-      }
-    }
-  }
-  if (sp.head) elems(sp.begin, sp.head);
-  if (sp.tail) elems(sp.begin + sp.head + sp.nvec * V, sp.tail);
-}
-
-__device__ __forceinline__ int seg_mis(int src_mis, int dst_mis, uint64_t src_byte_off,
-                                       uint64_t dst_byte_off) {
-  if (src_mis < 0 || dst_mis < 0) return -1;
-  const int sm = (int)((src_mis + src_byte_off) & 15);
-  const int dm = (int)((dst_mis + dst_byte_off) & 15);
-  return sm == dm ? sm : -1;
-}
-
-template <int B, bool DSTALL>
-__global__ __launch_bounds__(kBlock) void copy_kernel(RankPtrs ptrs, CopyGeom g) {
-  using W = typename Word<B>::T;
-  constexpr uint64_t TE = copy_tile_elems<B>();
-  const int p = g.p;
-  const uint64_t grid = gridDim.x, wg = blockIdx.x;
-  const int nseg = g.kind == kCopyAllGather ? p : (g.kind == kCopyBroadcast ? 1 : p * p);
-  const uint64_t ntiles = ceil_div(g.n, TE);
+  const int p = P ? P : g.p;
+  const int nseg = KIND == kCopyAllGather ? p : 1;
   uint64_t base = 0;
-  for (int sgi = 0; sgi < nseg; ++sgi, base += ntiles) {
-    const W* src;
-    uint64_t src_off = 0, dst_off = 0;
-    int dj = 0;
-    if (g.kind == kCopyAllGather) {
-      src = (const W*)ptrs.src[sgi];
-      dst_off = (uint64_t)sgi * g.n;
-    } else if (g.kind == kCopyBroadcast) {
-      src = (const W*)ptrs.src[0];
+  for (int s = 0; s < nseg; ++s) {
+    const W* src = (const W*)ptrs.src[s];
+    const uint64_t dst_off = KIND == kCopyAllGather ? (uint64_t)s * g.n : 0;
+    const int mis = seg_mis(g.src_mis, g.dst_mis, 0, dst_off * B);
+    if constexpr (P > 0) {
+      W* dst[P];
+#pragma unroll
+      for (int k = 0; k < P; ++k) dst[k] = (W*)ptrs.dst[k] + dst_off;
+      auto gdst = [&](int d) -> W* { return dst[d]; };
+      base += copy_segment<B, false, P>(src, gdst, P, g.n, mis, base);
     } else {
-      const int i = sgi / p, j = sgi - (sgi / p) * p;
-      src_off = (uint64_t)j * g.n;
-      dst_off = (uint64_t)i * g.n;
-      src = (const W*)ptrs.src[i] + src_off;
-      dj = j;
+      auto gdst = [&](int d) -> W* { return (W*)ptrs.dst[d] + dst_off; };
+      base += copy_segment<B, false, 0>(src, gdst, p, g.n, mis, base);
     }
-    const int mis = seg_mis(g.src_mis, g.dst_mis, src_off * B, dst_off * B);
-    auto gdst = [&](int k) -> W* {
-      if constexpr (DSTALL) return (W*)ptrs.dst[k] + dst_off;
-      else return (W*)ptrs.dst[dj] + dst_off;
-    };
-    for (uint64_t t = first_tile(base, wg, grid); t < ntiles; t += grid) {
-      const TileSpan sp = tile_span<B, 16 / B>(g.n, TE, t, mis);
-      copy_tile<B, DSTALL>(src, gdst, p, sp);
+  }
+}
+
+// Equal-split All-to-All: p*p segments, one destination each.
+template <int B>
+__global__ __launch_bounds__(kBlock) void alltoall_kernel(RankPtrs ptrs, CopyGeom g) {
+  using W = typename Word<B>::T;
+  const int p = g.p;
+  uint64_t base = 0;
+  for (int i = 0; i < p; ++i) {
+    for (int j = 0; j < p; ++j) {
+      const uint64_t src_off = (uint64_t)j * g.n, dst_off = (uint64_t)i * g.n;
+      const W* src = (const W*)ptrs.src[i] + src_off;
+      W* dst = (W*)ptrs.dst[j] + dst_off;
+      const int mis = seg_mis(g.src_mis, g.dst_mis, src_off * B, dst_off * B);
+      auto gdst = [&](int) -> W* { return dst; };
+      base += copy_segment<B, true, 1>(src, gdst, 1, g.n, mis, base);
     }
   }
 }
@@ -145,7 +73,6 @@ __global__ __launch_bounds__(kBlock) void copy_kernel(RankPtrs ptrs, CopyGeom g)
 template <int B>
 __global__ __launch_bounds__(kBlock) void alltoallv_kernel(RankPtrs ptrs, A2avArgs a) {
   using W = typename Word<B>::T;
-  constexpr uint64_t TE = copy_tile_elems<B>();
   extern __shared__ int64_t lds[];
   __shared__ int bad;
   const int p = a.p;
@@ -187,41 +114,52 @@ __global__ __launch_bounds__(kBlock) void alltoallv_kernel(RankPtrs ptrs, A2avAr
   if (blockIdx.x == 0 && tid == 0 && a.status) *a.status = reject ? 1 : 0;
   if (reject) return;
 
-  const uint64_t grid = gridDim.x, wg = blockIdx.x;
   uint64_t base = 0;
   for (int sgi = 0; sgi < pp; ++sgi) {
     const int i = sgi / p, j = sgi - (sgi / p) * p;
     const uint64_t len = (uint64_t)cnt[sgi];
     if (len == 0) continue;
-    const uint64_t ntiles = ceil_div(len, TE);
     const uint64_t so = (uint64_t)soff[sgi];
     const uint64_t ro = (uint64_t)roff[sgi];
     const W* src = (const W*)ptrs.src[i] + so;
     W* dst = (W*)ptrs.dst[j] + ro;
     const int mis = seg_mis(a.src_mis, a.dst_mis, so * B, ro * B);
     auto gdst = [&](int) -> W* { return dst; };
-    for (uint64_t t = first_tile(base, wg, grid); t < ntiles; t += grid) {
-      const TileSpan sp = tile_span<B, 16 / B>(len, TE, t, mis);
-      copy_tile<B, false>(src, gdst, 1, sp);
-    }
-    base += ntiles;
+    base += copy_segment<B, true, 1>(src, gdst, 1, len, mis, base);
   }
 }
 
+// ---------------------------------------------------------------------------
+// Host-side launch
+// ---------------------------------------------------------------------------
 static int clamp_grid(uint64_t tiles, int max_grid) {
   if (tiles == 0) return 0;
   return (int)(tiles < (uint64_t)max_grid ? tiles : (uint64_t)max_grid);
 }
 
+template <int B, int KIND>
+static void launch_fanout(int p, int grid, const RankPtrs& ptrs, const CopyGeom& g, hipStream_t s) {
+  switch (p) {
+    case 2: hipLaunchKernelGGL((fanout_kernel<B, KIND, 2>), dim3(grid), dim3(kBlock), 0, s, ptrs, g); break;
+    case 4: hipLaunchKernelGGL((fanout_kernel<B, KIND, 4>), dim3(grid), dim3(kBlock), 0, s, ptrs, g); break;
+    case 8: hipLaunchKernelGGL((fanout_kernel<B, KIND, 8>), dim3(grid), dim3(kBlock), 0, s, ptrs, g); break;
+    case 16: hipLaunchKernelGGL((fanout_kernel<B, KIND, 16>), dim3(grid), dim3(kBlock), 0, s, ptrs, g); break;
+    default: hipLaunchKernelGGL((fanout_kernel<B, KIND, 0>), dim3(grid), dim3(kBlock), 0, s, ptrs, g); break;
+  }
+}
+
 template <int B>
 static int launch_copy_b(const RankPtrs& ptrs, const CopyGeom& g, int max_grid, hipStream_t s) {
   const uint64_t nseg = g.kind == kCopyAllGather ? g.p : (g.kind == kCopyBroadcast ? 1 : (uint64_t)g.p * g.p);
-  const int grid = clamp_grid(nseg * ((g.n + copy_tile_elems<B>() - 1) / copy_tile_elems<B>()), max_grid);
+  const uint64_t te = kCopyTV * (16 / B);
+  const int grid = clamp_grid(nseg * ((g.n + te - 1) / te + 1), max_grid);
   if (!grid) return 0;
   if (g.kind == kCopyAllToAll)
-    hipLaunchKernelGGL((copy_kernel<B, false>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
+    hipLaunchKernelGGL((alltoall_kernel<B>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
+  else if (g.kind == kCopyAllGather)
+    launch_fanout<B, kCopyAllGather>(g.p, grid, ptrs, g, s);
   else
-    hipLaunchKernelGGL((copy_kernel<B, true>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
+    launch_fanout<B, kCopyBroadcast>(g.p, grid, ptrs, g, s);
   return (int)hipGetLastError();
 }
 

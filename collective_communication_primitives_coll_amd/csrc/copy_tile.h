@@ -1,0 +1,98 @@
+// Tiles of a plain copy from one source to one or more destinations.
+//
+// A lane loads kCopyUnroll 16-byte vectors, then stores each to every
+// destination of the segment; the copy is type-blind apart from the
+// element width used for misaligned heads and tails.  Stores are
+// non-temporal; the caller picks the load policy.
+#pragma once
+
+#include "device_common.h"
+
+namespace coll {
+
+template <int B>
+struct Word;
+template <>
+struct Word<2> {
+  using T = uint16_t;
+};
+template <>
+struct Word<4> {
+  using T = uint32_t;
+};
+
+constexpr int kCopyU = (int)kCopyUnroll;
+constexpr uint64_t kCopyTV = (uint64_t)kCopyU * kBlock;  // vectors per copy tile
+
+// Copy tile: U vectors per lane from src (at the segment's first aligned
+// vector) to ND destinations (ND = 0: nd, known only at run time).
+// j0 = tile * kCopyTV + lane.
+template <bool NTL, bool FULL, int ND, typename GD>
+__device__ __forceinline__ void copy_vec_tile(const u32x4* src, const GD& gdst, int nd, uint64_t j0,
+                                              uint64_t nvec) {
+  u32x4 r[kCopyU];
+#pragma unroll
+  for (int u = 0; u < kCopyU; ++u) {
+    const uint64_t j = j0 + (uint64_t)u * kBlock;
+    if (FULL || j < nvec) r[u] = ld16<NTL>(src + j);
+  }
+  const int ndst = ND ? ND : nd;
+#pragma unroll
+  for (int d = 0; d < ndst; ++d) {
+    u32x4* dv = gdst(d);
+#pragma unroll
+    for (int u = 0; u < kCopyU; ++u) {
+      const uint64_t j = j0 + (uint64_t)u * kBlock;
+      if (FULL || j < nvec) st16<true>(dv + j, r[u]);
+    }
+  }
+}
+
+// Copy one segment of len elements: this workgroup's vector tiles and,
+// if it owns the segment, the element-wise head and tail.  gdst(d) gives
+// destination d's element pointer at the segment start.  Returns the
+// segment's tile count.
+template <int B, bool NTL, int ND, typename GD>
+__device__ __forceinline__ uint64_t copy_segment(const typename Word<B>::T* src, const GD& gdst, int nd,
+                                                 uint64_t len, int mis, uint64_t base) {
+  using W = typename Word<B>::T;
+  constexpr uint64_t V = 16 / B;
+  const uint64_t grid = gridDim.x, wg = blockIdx.x;
+  const int ndst = ND ? ND : nd;
+  auto elems = [&](uint64_t from, uint64_t cnt) {
+    for (uint64_t i = threadIdx.x; i < cnt; i += kBlock) {
+      const uint64_t e = from + i;
+      const W w = ld1<NTL>(src + e);
+#pragma unroll
+      for (int d = 0; d < ndst; ++d) st1<true>(gdst(d) + e, w);
+    }
+  };
+  const SegSpan sp = seg_span<B>(len, mis);
+  if (!sp.vec) {
+    constexpr uint64_t TE = (uint64_t)kBlock * 4;
+    const uint64_t nt = ceil_div(len, TE);
+    for (uint64_t t = first_tile(base, wg, grid); t < nt; t += grid) {
+      const uint64_t from = t * TE;
+      elems(from, (len - from) < TE ? (len - from) : TE);
+    }
+    return nt;
+  }
+  const uint64_t nt = ceil_div(sp.nvec, kCopyTV);
+  if (sp.nvec) {
+    const u32x4* vs = reinterpret_cast<const u32x4*>(src + sp.head);
+    auto vd = [&](int d) -> u32x4* { return reinterpret_cast<u32x4*>(gdst(d) + sp.head); };
+    const uint64_t nfull = sp.nvec / kCopyTV;
+    for (uint64_t t = first_tile(base, wg, grid); t < nt; t += grid) {
+      const uint64_t j0 = t * kCopyTV + threadIdx.x;
+      if (t < nfull) copy_vec_tile<NTL, true, ND>(vs, vd, nd, j0, sp.nvec);
+      else copy_vec_tile<NTL, false, ND>(vs, vd, nd, j0, sp.nvec);
+    }
+  }
+  if ((sp.head || sp.tail) && first_tile(base, wg, grid) == 0) {
+    if (sp.head) elems(0, sp.head);
+    if (sp.tail) elems(sp.head + sp.nvec * V, sp.tail);
+  }
+  return nt;
+}
+
+}  // namespace coll

@@ -1,10 +1,18 @@
 // Device-side building blocks shared by the collective kernels (gfx950).
 //
-// Data moves in 16-byte vectors (global_load/store_dwordx4) with the
-// non-temporal hint: every byte is touched once, so nothing is worth
-// keeping in L2 or the Infinity Cache.  Element ranges whose start is not
-// 16-byte aligned, or whose source and destination are misaligned
-// differently, fall back to element-wide accesses.
+// Data moves in 16-byte vectors (global_load/store_dwordx4).  Each kernel
+// picks the cache policy per direction from what the direction mix of the
+// collective sustains on MI355X HBM3E:
+//   * reductions (p loads per store) stream their loads non-temporally and
+//     store through the cache;
+//   * fan-out copies (one load per p stores: AllGather, Broadcast) load
+//     through the cache and store non-temporally;
+//   * AllReduce (p loads, p stores) and 1:1 copies are non-temporal both
+//     ways.
+// A segment is a run of elements that starts at one offset in every
+// source and at one offset in every destination.  Its 16-byte aligned
+// middle goes through vector tiles; the misaligned head and tail (fewer
+// than one vector each) go element by element.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -39,21 +47,27 @@ template <> struct Traits<kI32> {
 };
 
 // ---------------------------------------------------------------------------
-// Loads and stores
+// Loads and stores.  NT selects the non-temporal (streaming) hint.
 // ---------------------------------------------------------------------------
+template <bool NT>
 __device__ __forceinline__ u32x4 ld16(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  else return *reinterpret_cast<const u32x4*>(p);
 }
+template <bool NT>
 __device__ __forceinline__ void st16(void* p, u32x4 v) {
-  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+  if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+  else *reinterpret_cast<u32x4*>(p) = v;
 }
-template <typename S>
+template <bool NT, typename S>
 __device__ __forceinline__ S ld1(const S* p) {
-  return __builtin_nontemporal_load(p);
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
 }
-template <typename S>
+template <bool NT, typename S>
 __device__ __forceinline__ void st1(S* p, S v) {
-  __builtin_nontemporal_store(v, p);
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
 }
 
 // ---------------------------------------------------------------------------
@@ -133,52 +147,55 @@ __device__ __forceinline__ void combine_vec(typename Traits<DT>::A (&acc)[Traits
 }
 
 // ---------------------------------------------------------------------------
-// Tile geometry.  A segment is a run of `len` elements that starts at the
-// same element offset in every source (and at one offset in every
-// destination).  It is cut into tiles of kTileVec vectors' worth of
-// elements; within a tile the 16-byte aligned middle goes through vector
-// accesses and the misaligned head and tail element by element.
+// Segment geometry.
 // ---------------------------------------------------------------------------
-struct TileSpan {
-  uint64_t begin;  // first element of the tile (segment-relative)
-  uint64_t head;   // elements before the first aligned vector
-  uint64_t nvec;   // aligned vectors
-  uint64_t tail;   // elements after the last vector
-  bool vec;        // false: every element goes through the element path
+__device__ __forceinline__ uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
+
+// Split of a segment of `len` elements of B bytes whose start sits `mis`
+// bytes past a 16-byte boundary in every source and destination (mis < 0:
+// they disagree, so nothing can be vectorised).
+struct SegSpan {
+  uint64_t head;  // elements before the first aligned vector
+  uint64_t nvec;  // aligned 16-byte vectors
+  uint64_t tail;  // elements after the last vector
+  bool vec;
 };
 
-// mis: byte misalignment (0..15) of the segment start, common to all
-// sources and destinations, or -1 when they differ.
-template <int B, int V>
-__device__ __forceinline__ TileSpan tile_span(uint64_t len, uint64_t tile_elems, uint64_t t, int mis) {
-  TileSpan s;
-  s.begin = t * tile_elems;
-  uint64_t n = len - s.begin;
-  if (n > tile_elems) n = tile_elems;
+template <int B>
+__device__ __forceinline__ SegSpan seg_span(uint64_t len, int mis) {
+  constexpr uint64_t V = 16 / B;
+  SegSpan s;
   if (mis < 0 || mis % B != 0) {
     s.vec = false;
-    s.head = n;
+    s.head = len;
     s.nvec = 0;
     s.tail = 0;
     return s;
   }
   s.vec = true;
-  // tile_elems * B is a multiple of 16, so every tile of the segment shares
-  // the segment's misalignment.
   uint64_t h = (uint64_t)(((16 - mis) & 15) / B);
-  if (h > n) h = n;
+  if (h > len) h = len;
   s.head = h;
-  s.nvec = (n - h) / V;
-  s.tail = n - h - s.nvec * V;
+  s.nvec = (len - h) / V;
+  s.tail = len - h - s.nvec * V;
   return s;
 }
 
-__device__ __forceinline__ uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
+// Misalignment of a segment whose sources start src_byte_off bytes past
+// bases with common misalignment src_mis (and likewise for destinations).
+__device__ __forceinline__ int seg_mis(int src_mis, int dst_mis, uint64_t src_byte_off,
+                                       uint64_t dst_byte_off) {
+  if (src_mis < 0 || dst_mis < 0) return -1;
+  const int sm = (int)((src_mis + src_byte_off) & 15);
+  const int dm = (int)((dst_mis + dst_byte_off) & 15);
+  return sm == dm ? sm : -1;
+}
 
 // First tile index t >= 0 of a segment whose flat index base + t is
-// congruent to the workgroup id modulo the grid size.
+// congruent to the workgroup id modulo the grid size.  The workgroup for
+// which this is 0 also owns the segment's element-wise head and tail.
 __device__ __forceinline__ uint64_t first_tile(uint64_t base, uint64_t wg, uint64_t grid) {
-  uint64_t r = base % grid;
+  const uint64_t r = base % grid;
   return (wg + grid - r) % grid;
 }
 

@@ -100,6 +100,10 @@ int launch_ring_step(int dtype, int op, const RankPtrs& ptrs, const RingStepGeom
                      void* stream);
 int launch_batch(const BatchArgs& a, int grid, void* stream);
 
+// Elements of one batch tile for a dtype and rank count (the host cuts
+// each call's chunks into tiles of this size).
+uint64_t batch_tile_elems_host(int dtype, int p);
+
 // 16-byte vectors each lane of a copy kernel keeps in flight.
 constexpr uint64_t kCopyUnroll = 4;
 

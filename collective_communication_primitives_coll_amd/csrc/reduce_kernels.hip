@@ -8,72 +8,148 @@
 // mode picks where a segment's result goes:
 //   all    every rank's buffer at the segment offset (AllReduce: the
 //          reduce-scatter result of chunk c and its all-gather to every
-//          rank come out of one pass),
+//          rank come out of one pass; stores are non-temporal),
 //   fixed  the root buffer at the segment offset (Reduce),
 //   owner  rank c's buffer from its start (ReduceScatter, block c lands on
 //          rank c: "集合通信：原语、算法、NCCL 实现与拓扑映射", section 1.5).
+// The rotated source list of a segment is read from the kernel arguments
+// once per segment and kept in scalar registers.
 #include "reduce_tile.h"
 
 namespace coll {
 
-template <int DT, int OP, int P, bool TREE, bool DSTALL>
+__device__ __forceinline__ void chunk_range(const ReduceGeom& g, int c, uint64_t* lo, uint64_t* len) {
+  uint64_t a = (uint64_t)c * g.stride;
+  uint64_t b = a + g.stride;
+  if (a > g.total) a = g.total;
+  if (b > g.total) b = g.total;
+  *lo = a;
+  *len = b - a;
+}
+
+template <int DT, int OP, int P, bool TREE, int DMODE>
 __global__ __launch_bounds__(kBlock) void reduce_kernel(RankPtrs ptrs, ReduceGeom g) {
   using T = Traits<DT>;
   using S = typename T::S;
-  constexpr uint64_t TE = reduce_tile_elems<DT, P>();
-  const int p = P ? P : g.p;
-  const uint64_t grid = gridDim.x;
-  const uint64_t wg = blockIdx.x;
+  constexpr bool ALL = DMODE == kDstAll;
+  constexpr int ND = ALL ? P : 1;
   uint64_t base = 0;
-  for (int c = 0; c < p; ++c) {
-    uint64_t lo = (uint64_t)c * g.stride;
-    uint64_t hi = lo + g.stride;
-    if (lo > g.total) lo = g.total;
-    if (hi > g.total) hi = g.total;
-    const uint64_t len = hi - lo;
+  for (int c = 0; c < P; ++c) {
+    uint64_t lo, len;
+    chunk_range(g, c, &lo, &len);
     if (len == 0) continue;
-    const uint64_t ntiles = ceil_div(len, TE);
-    const uint64_t dst_off = (g.dst_mode == kDstOwner) ? 0 : lo;
-    int mis = -1;
-    if (g.src_mis >= 0 && g.dst_mis >= 0) {
-      const int sm = (int)((g.src_mis + lo * T::B) & 15);
-      const int dm = (int)((g.dst_mis + dst_off * T::B) & 15);
-      if (sm == dm) mis = sm;
+    const uint64_t doff = (DMODE == kDstOwner) ? 0 : lo;
+    const S* src[P];
+#pragma unroll
+    for (int k = 0; k < P; ++k) src[k] = (const S*)ptrs.src[TREE ? k : (c + 1 + k) % P] + lo;
+    S* dst[ND];
+    if constexpr (ALL) {
+#pragma unroll
+      for (int k = 0; k < P; ++k) dst[k] = (S*)ptrs.dst[k] + lo;
+    } else if constexpr (DMODE == kDstOwner) {
+      dst[0] = (S*)ptrs.dst[c];
+    } else {
+      dst[0] = (S*)ptrs.dst[0] + lo;
     }
-    S* const dfix = (g.dst_mode == kDstOwner) ? (S*)ptrs.dst[c] : (S*)ptrs.dst[0] + lo;
-    auto gsrc = [&](int k) -> const S* {
-      const int r = TREE ? k : (c + 1 + k) % p;
-      return (const S*)ptrs.src[r] + lo;
-    };
-    auto gdst = [&](int k) -> S* {
-      if constexpr (DSTALL) return (S*)ptrs.dst[k] + lo;
-      else return dfix;
-    };
-    for (uint64_t t = first_tile(base, wg, grid); t < ntiles; t += grid) {
-      const TileSpan sp = tile_span<T::B, T::V>(len, TE, t, mis);
-      reduce_tile<DT, OP, P, TREE, DSTALL>(gsrc, gdst, p, sp);
-    }
-    base += ntiles;
+    const int mis = seg_mis(g.src_mis, g.dst_mis, lo * T::B, doff * T::B);
+    base += reduce_segment<DT, OP, P, TREE, ND, ALL>(src, dst, len, mis, base);
   }
 }
 
-template <int DT, int OP, int P, bool TREE>
-static void launch_p(const RankPtrs& ptrs, const ReduceGeom& g, int grid, hipStream_t s) {
-  if (g.dst_mode == kDstAll)
-    hipLaunchKernelGGL((reduce_kernel<DT, OP, P, TREE, true>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
-  else
-    hipLaunchKernelGGL((reduce_kernel<DT, OP, P, TREE, false>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
+// Any rank count (the slow general path): one vector per lane per tile,
+// operands in groups of 8 loads, pointers read from the kernel arguments.
+template <int DT, int OP, int DMODE>
+__global__ __launch_bounds__(kBlock) void reduce_kernel_any(RankPtrs ptrs, ReduceGeom g) {
+  using T = Traits<DT>;
+  using S = typename T::S;
+  using A = typename T::A;
+  constexpr int V = T::V;
+  constexpr bool ALL = DMODE == kDstAll;
+  const int p = g.p;
+  const uint64_t grid = gridDim.x, wg = blockIdx.x;
+  uint64_t base = 0;
+  for (int c = 0; c < p; ++c) {
+    uint64_t lo, len;
+    chunk_range(g, c, &lo, &len);
+    if (len == 0) continue;
+    const uint64_t doff = (DMODE == kDstOwner) ? 0 : lo;
+    auto sp_src = [&](int k) -> const S* { return (const S*)ptrs.src[(c + 1 + k) % p] + lo; };
+    auto sp_dst = [&](int k) -> S* {
+      if constexpr (ALL) return (S*)ptrs.dst[k] + lo;
+      else if constexpr (DMODE == kDstOwner) return (S*)ptrs.dst[c];
+      else return (S*)ptrs.dst[0] + lo;
+    };
+    const int nd = ALL ? p : 1;
+    const SegSpan sp = seg_span<T::B>(len, seg_mis(g.src_mis, g.dst_mis, lo * T::B, doff * T::B));
+    auto elems = [&](uint64_t from, uint64_t cnt) {
+      for (uint64_t i = threadIdx.x; i < cnt; i += kBlock) {
+        const uint64_t e = from + i;
+        A acc = widen1<DT>(ld1<true>(sp_src(0) + e));
+        for (int k = 1; k < p; ++k) acc = combine<OP>(acc, widen1<DT>(ld1<true>(sp_src(k) + e)));
+        const auto out = narrow1<DT>(acc);
+        for (int d = 0; d < nd; ++d) st1<ALL>(sp_dst(d) + e, out);
+      }
+    };
+    if (!sp.vec) {
+      constexpr uint64_t TE = (uint64_t)kBlock * 4;
+      const uint64_t nt = ceil_div(len, TE);
+      for (uint64_t t = first_tile(base, wg, grid); t < nt; t += grid) {
+        const uint64_t from = t * TE;
+        elems(from, (len - from) < TE ? (len - from) : TE);
+      }
+      base += nt;
+      continue;
+    }
+    const uint64_t nt = ceil_div(sp.nvec, (uint64_t)kBlock);
+    for (uint64_t t = first_tile(base, wg, grid); t < nt; t += grid) {
+      const uint64_t j = t * kBlock + threadIdx.x;
+      if (j >= sp.nvec) continue;
+      const uint64_t e = sp.head + j * V;
+      A acc[V];
+      widen<DT>(ld16<true>(sp_src(0) + e), acc);
+      for (int k0 = 1; k0 < p; k0 += 8) {
+        u32x4 r[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (k0 + q < p) r[q] = ld16<true>(sp_src(k0 + q) + e);
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (k0 + q < p) {
+            A t2[V];
+            widen<DT>(r[q], t2);
+            combine_vec<OP, DT>(acc, t2);
+          }
+      }
+      const u32x4 out = narrow<DT>(acc);
+      for (int d = 0; d < nd; ++d) st16<ALL>(sp_dst(d) + e, out);
+    }
+    if ((sp.head || sp.tail) && first_tile(base, wg, grid) == 0) {
+      if (sp.head) elems(0, sp.head);
+      if (sp.tail) elems(sp.head + sp.nvec * V, sp.tail);
+    }
+    base += nt;
+  }
 }
 
-template <int DT, int P>
+// ---------------------------------------------------------------------------
+// Host-side launch
+// ---------------------------------------------------------------------------
+template <int DT, int P, bool ALL>
+static uint64_t tile_elems() {
+  return (uint64_t)ReduceUnroll<P, ALL>::value * kBlock * Traits<DT>::V;
+}
+
+// Upper bound on the tiles of all segments (vector tiles plus one for a
+// misaligned head), used only to size the grid.
+template <int DT, int P, bool ALL>
 static uint64_t count_tiles(const ReduceGeom& g) {
-  constexpr uint64_t TE = reduce_tile_elems<DT, P>();
+  const uint64_t te = P ? tile_elems<DT, P, ALL>() : (uint64_t)kBlock * Traits<DT>::V;
   uint64_t total = 0;
   for (int c = 0; c < g.p; ++c) {
     uint64_t lo = (uint64_t)c * g.stride, hi = lo + g.stride;
     if (lo > g.total) lo = g.total;
     if (hi > g.total) hi = g.total;
-    total += (hi - lo + TE - 1) / TE;
+    if (hi > lo) total += (hi - lo + te - 1) / te + 1;
   }
   return total;
 }
@@ -83,46 +159,56 @@ static int clamp_grid(uint64_t tiles, int max_grid) {
   return (int)(tiles < (uint64_t)max_grid ? tiles : (uint64_t)max_grid);
 }
 
+template <int DT, int OP, int P, bool TREE>
+static int launch_p(const RankPtrs& ptrs, const ReduceGeom& g, int max_grid, hipStream_t s) {
+  if (g.dst_mode == kDstAll) {
+    const int grid = clamp_grid(count_tiles<DT, P, true>(g), max_grid);
+    if (grid)
+      hipLaunchKernelGGL((reduce_kernel<DT, OP, P, TREE, kDstAll>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
+    return (int)hipGetLastError();
+  }
+  const int grid = clamp_grid(count_tiles<DT, P, false>(g), max_grid);
+  if (!grid) return 0;
+  if (g.dst_mode == kDstOwner)
+    hipLaunchKernelGGL((reduce_kernel<DT, OP, P, TREE, kDstOwner>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
+  else
+    hipLaunchKernelGGL((reduce_kernel<DT, OP, P, TREE, kDstFixed>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
+  return (int)hipGetLastError();
+}
+
 template <int DT, int OP>
-static int launch_dt_op(bool tree, const RankPtrs& ptrs, const ReduceGeom& g, int max_grid,
-                        hipStream_t s) {
-  int grid = 0;
-#define COLL_RING_CASE(PV)                                              \
-  case PV:                                                              \
-    grid = clamp_grid(count_tiles<DT, PV>(g), max_grid);                \
-    if (grid) launch_p<DT, OP, PV, false>(ptrs, g, grid, s);            \
-    break;
+static int launch_any(const RankPtrs& ptrs, const ReduceGeom& g, int max_grid, hipStream_t s) {
+  const int grid = clamp_grid(count_tiles<DT, 0, false>(g), max_grid);
+  if (!grid) return 0;
+  if (g.dst_mode == kDstAll)
+    hipLaunchKernelGGL((reduce_kernel_any<DT, OP, kDstAll>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
+  else if (g.dst_mode == kDstOwner)
+    hipLaunchKernelGGL((reduce_kernel_any<DT, OP, kDstOwner>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
+  else
+    hipLaunchKernelGGL((reduce_kernel_any<DT, OP, kDstFixed>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
+  return (int)hipGetLastError();
+}
+
+template <int DT, int OP>
+static int launch_dt_op(bool tree, const RankPtrs& ptrs, const ReduceGeom& g, int max_grid, hipStream_t s) {
   if constexpr ((DT == kF32 || DT == kBF16) && OP == kSum) {
     if (tree) {
       switch (g.p) {
-#define COLL_TREE_CASE(PV)                                              \
-  case PV:                                                              \
-    grid = clamp_grid(count_tiles<DT, PV>(g), max_grid);                \
-    if (grid) launch_p<DT, OP, PV, true>(ptrs, g, grid, s);             \
-    break;
-        COLL_TREE_CASE(2)
-        COLL_TREE_CASE(4)
-        COLL_TREE_CASE(8)
-        COLL_TREE_CASE(16)
-#undef COLL_TREE_CASE
-        default:
-          return (int)hipErrorInvalidValue;
+        case 2: return launch_p<DT, OP, 2, true>(ptrs, g, max_grid, s);
+        case 4: return launch_p<DT, OP, 4, true>(ptrs, g, max_grid, s);
+        case 8: return launch_p<DT, OP, 8, true>(ptrs, g, max_grid, s);
+        case 16: return launch_p<DT, OP, 16, true>(ptrs, g, max_grid, s);
+        default: return (int)hipErrorInvalidValue;
       }
-      return (int)hipGetLastError();
     }
   }
   switch (g.p) {
-    COLL_RING_CASE(2)
-    COLL_RING_CASE(4)
-    COLL_RING_CASE(8)
-    COLL_RING_CASE(16)
-    default:
-      grid = clamp_grid(count_tiles<DT, 0>(g), max_grid);
-      if (grid) launch_p<DT, OP, 0, false>(ptrs, g, grid, s);
-      break;
+    case 2: return launch_p<DT, OP, 2, false>(ptrs, g, max_grid, s);
+    case 4: return launch_p<DT, OP, 4, false>(ptrs, g, max_grid, s);
+    case 8: return launch_p<DT, OP, 8, false>(ptrs, g, max_grid, s);
+    case 16: return launch_p<DT, OP, 16, false>(ptrs, g, max_grid, s);
+    default: return launch_any<DT, OP>(ptrs, g, max_grid, s);
   }
-#undef COLL_RING_CASE
-  return (int)hipGetLastError();
 }
 
 template <int DT>

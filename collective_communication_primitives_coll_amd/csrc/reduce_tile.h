@@ -1,175 +1,164 @@
-// One tile of a p-way elementwise reduction.
+// Tiles of a p-way elementwise reduction.
 //
-// The k-th operand of the fold comes from gsrc(k) and the result goes to
-// gdst(0..ndst-1); both return element pointers already offset to the
-// segment start.  With the ring order the fold is a left fold in the
-// order gsrc(0), gsrc(1), ..., which the callers rotate so that chunk c is
-// folded x_{c+1}, x_{c+2}, ..., x_c: the ring all-reduce of
+// The operands of every element are folded left to right in the order the
+// caller lists the sources.  The callers list chunk c's sources as
+// x_{c+1}, x_{c+2}, ..., x_c: the ring all-reduce of
 // "集合通信：原语、算法、NCCL 实现与拓扑映射" (hpc/04, section 2.2) with the
-// partial kept in registers across its p-1 combine steps and the p
-// all-gather stores issued from the same registers.  TREE instead sums
-// the operands as a balanced pairwise tree (a one-pass reassociated sum).
+// partial held in registers across its p-1 combine steps, and for
+// AllReduce the p all-gather stores issued from the same registers.
+// TREE instead sums the operands as a balanced pairwise tree in rank order
+// (a one-pass reassociated sum).
 //
-// All p loads of a lane are issued before the first combine, so a lane
-// keeps p (x UNROLL) 16-byte requests in flight.
+// A lane handles U vectors of a tile.  It issues all P*U loads before the
+// first combine, source by source, so it keeps P*U 16-byte requests in
+// flight.
 #pragma once
 
 #include "device_common.h"
 
 namespace coll {
 
-template <int P>
+// Vectors per lane in a reduction tile.  Reductions that store once keep
+// 32 loads in flight per lane; AllReduce, which also stores p times,
+// keeps 16.
+template <int P, bool ALL>
 struct ReduceUnroll {
-  static constexpr int value = (P == 0 || P >= 8) ? 1 : 8 / P;
+  static constexpr int raw = P == 0 ? 1 : (ALL ? 16 / P : 32 / P);
+  static constexpr int value = raw < 1 ? 1 : (raw > 8 ? 8 : raw);
 };
 
-template <int DT, int OP, int P, bool TREE, bool DSTALL, typename GS, typename GD>
-__device__ __forceinline__ void reduce_elems(const GS& gsrc, const GD& gdst, int p, uint64_t from,
+// Fold of P operands already widened, in list order or as a tree.
+template <int DT, int OP, int P, bool TREE>
+__device__ __forceinline__ u32x4 fold_vectors(const u32x4 (&r)[P]) {
+  using A = typename Traits<DT>::A;
+  constexpr int V = Traits<DT>::V;
+  A acc[V];
+  if constexpr (TREE) {
+    A a[P][V];
+#pragma unroll
+    for (int k = 0; k < P; ++k) widen<DT>(r[k], a[k]);
+#pragma unroll
+    for (int st = 1; st < P; st *= 2)
+#pragma unroll
+      for (int k = 0; k + st < P; k += 2 * st) combine_vec<OP, DT>(a[k], a[k + st]);
+#pragma unroll
+    for (int x = 0; x < V; ++x) acc[x] = a[0][x];
+  } else {
+    widen<DT>(r[0], acc);
+#pragma unroll
+    for (int k = 1; k < P; ++k) {
+      A t[V];
+      widen<DT>(r[k], t);
+      combine_vec<OP, DT>(acc, t);
+    }
+  }
+  return narrow<DT>(acc);
+}
+
+// One vector tile.  src[k] and dst[d] point at the segment's first aligned
+// vector; j0 = tile * U * kBlock + lane is this lane's first vector index.
+// FULL: every vector of the tile lies inside the segment (nvec unused).
+template <int DT, int OP, int P, bool TREE, int ND, bool NTS, int U, bool FULL>
+__device__ __forceinline__ void reduce_vec_tile(const typename Traits<DT>::S* const (&src)[P],
+                                                typename Traits<DT>::S* const (&dst)[ND],
+                                                uint64_t j0, uint64_t nvec) {
+  constexpr int V = Traits<DT>::V;
+  u32x4 raw[U][P];
+#pragma unroll
+  for (int k = 0; k < P; ++k)
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint64_t j = j0 + (uint64_t)u * kBlock;
+      if (FULL || j < nvec) raw[u][k] = ld16<true>(src[k] + j * V);
+      else raw[u][k] = u32x4{0, 0, 0, 0};
+    }
+  u32x4 out[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) out[u] = fold_vectors<DT, OP, P, TREE>(raw[u]);
+#pragma unroll
+  for (int d = 0; d < ND; ++d)
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint64_t j = j0 + (uint64_t)u * kBlock;
+      if (FULL || j < nvec) st16<NTS>(dst[d] + j * V, out[u]);
+    }
+}
+
+// Element-wise path: cnt elements from element offset `from` of the
+// segment (src/dst at the segment start), one element per lane.
+template <int DT, int OP, int P, bool TREE, int ND, bool NTS>
+__device__ __forceinline__ void reduce_elems(const typename Traits<DT>::S* const (&src)[P],
+                                             typename Traits<DT>::S* const (&dst)[ND], uint64_t from,
                                              uint64_t cnt) {
-  using T = Traits<DT>;
-  using A = typename T::A;
-  const int np = P ? P : p;
+  using A = typename Traits<DT>::A;
   for (uint64_t i = threadIdx.x; i < cnt; i += kBlock) {
     const uint64_t e = from + i;
+    A a[P];
+#pragma unroll
+    for (int k = 0; k < P; ++k) a[k] = widen1<DT>(ld1<true>(src[k] + e));
     A acc;
     if constexpr (TREE) {
-      static_assert(P > 0, "tree order needs a compile-time rank count");
-      A a[P];
 #pragma unroll
-      for (int k = 0; k < P; ++k) a[k] = widen1<DT>(ld1(gsrc(k) + e));
+      for (int st = 1; st < P; st *= 2)
 #pragma unroll
-      for (int s = 1; s < P; s *= 2)
-#pragma unroll
-        for (int k = 0; k + s < P; k += 2 * s) a[k] = combine<OP>(a[k], a[k + s]);
+        for (int k = 0; k + st < P; k += 2 * st) a[k] = combine<OP>(a[k], a[k + st]);
       acc = a[0];
     } else {
-      acc = widen1<DT>(ld1(gsrc(0) + e));
-      if constexpr (P > 0) {
+      acc = a[0];
 #pragma unroll
-        for (int k = 1; k < P; ++k) acc = combine<OP>(acc, widen1<DT>(ld1(gsrc(k) + e)));
-      } else {
-        for (int k = 1; k < np; ++k) acc = combine<OP>(acc, widen1<DT>(ld1(gsrc(k) + e)));
-      }
+      for (int k = 1; k < P; ++k) acc = combine<OP>(acc, a[k]);
     }
     const auto out = narrow1<DT>(acc);
-    if constexpr (DSTALL) {
-      if constexpr (P > 0) {
 #pragma unroll
-        for (int k = 0; k < P; ++k) st1(gdst(k) + e, out);
-      } else {
-        for (int k = 0; k < np; ++k) st1(gdst(k) + e, out);
-      }
-    } else {
-      st1(gdst(0) + e, out);
-    }
+    for (int d = 0; d < ND; ++d) st1<NTS>(dst[d] + e, out);
   }
 }
 
-template <int DT, int OP, int P, bool TREE, bool DSTALL, int U, typename GS, typename GD>
-__device__ __forceinline__ void reduce_vectors(const GS& gsrc, const GD& gdst, int p, uint64_t v0,
-                                               uint64_t nvec) {
-  using T = Traits<DT>;
-  using S = typename T::S;
-  using A = typename T::A;
-  constexpr int V = T::V;
-  const uint64_t tid = threadIdx.x;
-  if constexpr (P > 0) {
-    const S* s[P];
-#pragma unroll
-    for (int k = 0; k < P; ++k) s[k] = gsrc(k);
-    u32x4 raw[U][P];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint64_t vi = (uint64_t)u * kBlock + tid;
-      if (vi < nvec) {
-        const uint64_t e = v0 + vi * V;
-#pragma unroll
-        for (int k = 0; k < P; ++k) raw[u][k] = ld16(s[k] + e);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint64_t vi = (uint64_t)u * kBlock + tid;
-      if (vi < nvec) {
-        const uint64_t e = v0 + vi * V;
-        A acc[V];
-        if constexpr (TREE) {
-          A a[P][V];
-#pragma unroll
-          for (int k = 0; k < P; ++k) widen<DT>(raw[u][k], a[k]);
-#pragma unroll
-          for (int st = 1; st < P; st *= 2)
-#pragma unroll
-            for (int k = 0; k + st < P; k += 2 * st) combine_vec<OP, DT>(a[k], a[k + st]);
-#pragma unroll
-          for (int x = 0; x < V; ++x) acc[x] = a[0][x];
-        } else {
-          widen<DT>(raw[u][0], acc);
-#pragma unroll
-          for (int k = 1; k < P; ++k) {
-            A t[V];
-            widen<DT>(raw[u][k], t);
-            combine_vec<OP, DT>(acc, t);
-          }
-        }
-        const u32x4 out = narrow<DT>(acc);
-        if constexpr (DSTALL) {
-#pragma unroll
-          for (int k = 0; k < P; ++k) st16(gdst(k) + e, out);
-        } else {
-          st16(gdst(0) + e, out);
-        }
-      }
-    }
-  } else {
-    // Rank count known only at run time: operands in groups of 8, each
-    // group's loads issued before its combines.
-    const uint64_t vi = tid;
-    if (vi < nvec) {
-      const uint64_t e = v0 + vi * V;
-      A acc[V];
-      widen<DT>(ld16(gsrc(0) + e), acc);
-      for (int k0 = 1; k0 < p; k0 += 8) {
-        u32x4 r[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (k0 + j < p) r[j] = ld16(gsrc(k0 + j) + e);
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (k0 + j < p) {
-            A t[V];
-            widen<DT>(r[j], t);
-            combine_vec<OP, DT>(acc, t);
-          }
-      }
-      const u32x4 out = narrow<DT>(acc);
-      if constexpr (DSTALL) {
-        for (int k = 0; k < p; ++k) st16(gdst(k) + e, out);
-      } else {
-        st16(gdst(0) + e, out);
-      }
-    }
-  }
-}
-
-// Tile elements for a reduction: U vectors per lane, one workgroup.
-template <int DT, int P>
-constexpr uint64_t reduce_tile_elems() {
-  return (uint64_t)ReduceUnroll<P>::value * kBlock * Traits<DT>::V;
-}
-
-template <int DT, int OP, int P, bool TREE, bool DSTALL, typename GS, typename GD>
-__device__ __forceinline__ void reduce_tile(const GS& gsrc, const GD& gdst, int p, const TileSpan& sp) {
-  constexpr int U = (P == 0) ? 1 : ReduceUnroll<P>::value;
+// A whole segment as seen by one workgroup: its share of the vector tiles
+// (flat tile indices congruent to the workgroup id modulo the grid,
+// counting from `base`) and, for the owning workgroup, the head and tail.
+// Returns the segment's tile count (the caller advances base by it).
+template <int DT, int OP, int P, bool TREE, int ND, bool NTS>
+__device__ __forceinline__ uint64_t reduce_segment(const typename Traits<DT>::S* const (&src)[P],
+                                                   typename Traits<DT>::S* const (&dst)[ND],
+                                                   uint64_t len, int mis, uint64_t base) {
+  using S = typename Traits<DT>::S;
   constexpr int V = Traits<DT>::V;
-  if (sp.vec) {
-    if (sp.nvec) reduce_vectors<DT, OP, P, TREE, DSTALL, U>(gsrc, gdst, p, sp.begin + sp.head, sp.nvec);
-    if (sp.head) reduce_elems<DT, OP, P, TREE, DSTALL>(gsrc, gdst, p, sp.begin, sp.head);
-    if (sp.tail)
-      reduce_elems<DT, OP, P, TREE, DSTALL>(gsrc, gdst, p, sp.begin + sp.head + sp.nvec * V, sp.tail);
-  } else {
-    reduce_elems<DT, OP, P, TREE, DSTALL>(gsrc, gdst, p, sp.begin, sp.head);
+  constexpr int U = ReduceUnroll<P, (ND > 1)>::value;
+  constexpr uint64_t TV = (uint64_t)U * kBlock;
+  const uint64_t grid = gridDim.x, wg = blockIdx.x;
+  const SegSpan sp = seg_span<Traits<DT>::B>(len, mis);
+  if (!sp.vec) {
+    // element path over tiles of kBlock * 4 elements
+    constexpr uint64_t TE = (uint64_t)kBlock * 4;
+    const uint64_t nt = ceil_div(len, TE);
+    for (uint64_t t = first_tile(base, wg, grid); t < nt; t += grid) {
+      const uint64_t from = t * TE;
+      const uint64_t cnt = (len - from) < TE ? (len - from) : TE;
+      reduce_elems<DT, OP, P, TREE, ND, NTS>(src, dst, from, cnt);
+    }
+    return nt;
   }
+  const uint64_t nt = ceil_div(sp.nvec, TV);
+  if (sp.nvec) {
+    const S* vs[P];
+    S* vd[ND];
+#pragma unroll
+    for (int k = 0; k < P; ++k) vs[k] = src[k] + sp.head;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) vd[d] = dst[d] + sp.head;
+    const uint64_t nfull = sp.nvec / TV;
+    for (uint64_t t = first_tile(base, wg, grid); t < nt; t += grid) {
+      const uint64_t j0 = t * TV + threadIdx.x;
+      if (t < nfull) reduce_vec_tile<DT, OP, P, TREE, ND, NTS, U, true>(vs, vd, j0, sp.nvec);
+      else reduce_vec_tile<DT, OP, P, TREE, ND, NTS, U, false>(vs, vd, j0, sp.nvec);
+    }
+  }
+  if ((sp.head || sp.tail) && first_tile(base, wg, grid) == 0) {
+    if (sp.head) reduce_elems<DT, OP, P, TREE, ND, NTS>(src, dst, 0, sp.head);
+    if (sp.tail) reduce_elems<DT, OP, P, TREE, ND, NTS>(src, dst, sp.head + sp.nvec * V, sp.tail);
+  }
+  return nt;
 }
 
 }  // namespace coll

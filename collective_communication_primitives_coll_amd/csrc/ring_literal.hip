@@ -15,7 +15,8 @@
 // ranks of a step run concurrently without races; steps are ordered by the
 // stream.  Combining in HBM costs (p-1)*3 + (p-1)*2 chunk passes per rank
 // instead of the fused kernel's single read and write.
-#include "device_common.h"
+#include "copy_tile.h"
+#include "reduce_tile.h"
 
 namespace coll {
 
@@ -23,13 +24,7 @@ template <int DT, int OP>
 __global__ __launch_bounds__(kBlock) void ring_step_kernel(RankPtrs ptrs, RingStepGeom g) {
   using T = Traits<DT>;
   using S = typename T::S;
-  using A = typename T::A;
-  constexpr int V = T::V;
-  constexpr int U = 2;
-  constexpr uint64_t TE = (uint64_t)U * kBlock * V;
   const int p = g.p;
-  const uint64_t grid = gridDim.x, wg = blockIdx.x;
-  const uint64_t tid = threadIdx.x;
   uint64_t base = 0;
   for (int x = 0; x < p; ++x) {
     const int nxt = (x + 1) % p;
@@ -39,55 +34,19 @@ __global__ __launch_bounds__(kBlock) void ring_step_kernel(RankPtrs ptrs, RingSt
     if (hi > g.n) hi = g.n;
     const uint64_t len = hi - lo;
     if (len == 0) continue;
-    const uint64_t ntiles = ceil_div(len, TE);
-    const S* a = (g.phase == 0 && g.step == 1) ? (const S*)ptrs.src[x] + lo : (const S*)ptrs.dst[x] + lo;
-    const S* b = (const S*)ptrs.src[nxt] + lo;
-    S* d = (S*)ptrs.dst[nxt] + lo;
     const int mis = g.mis < 0 ? -1 : (int)((g.mis + lo * T::B) & 15);
-    for (uint64_t t = first_tile(base, wg, grid); t < ntiles; t += grid) {
-      const TileSpan sp = tile_span<T::B, V>(len, TE, t, mis);
-      auto elems = [&](uint64_t from, uint64_t cnt) {
-        for (uint64_t i = tid; i < cnt; i += kBlock) {
-          const uint64_t e = from + i;
-          if (g.phase == 0)
-            st1(d + e, narrow1<DT>(combine<OP>(widen1<DT>(ld1(a + e)), widen1<DT>(ld1(b + e)))));
-          else
-            st1(d + e, ld1(a + e));
-        }
-      };
-      if (!sp.vec) {
-        elems(sp.begin, sp.head);
-        continue;
-      }
-      const uint64_t v0 = sp.begin + sp.head;
-      u32x4 ra[U], rb[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const uint64_t vi = (uint64_t)u * kBlock + tid;
-        if (vi < sp.nvec) {
-          ra[u] = ld16(a + v0 + vi * V);
-          if (g.phase == 0) rb[u] = ld16(b + v0 + vi * V);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const uint64_t vi = (uint64_t)u * kBlock + tid;
-        if (vi < sp.nvec) {
-          if (g.phase == 0) {
-            A acc[V], t2[V];
-            widen<DT>(ra[u], acc);
-            widen<DT>(rb[u], t2);
-            combine_vec<OP, DT>(acc, t2);
-            st16(d + v0 + vi * V, narrow<DT>(acc));
-          } else {
-            st16(d + v0 + vi * V, ra[u]);
-          }
-        }
-      }
-      if (sp.head) elems(sp.begin, sp.head);
-      if (sp.tail) elems(sp.begin + sp.head + sp.nvec * V, sp.tail);
+    const S* partial = (g.phase == 0 && g.step == 1) ? (const S*)ptrs.src[x] + lo : (const S*)ptrs.dst[x] + lo;
+    S* d = (S*)ptrs.dst[nxt] + lo;
+    if (g.phase == 0) {
+      // received partial on the left, the receiver's own input on the right
+      const S* src[2] = {partial, (const S*)ptrs.src[nxt] + lo};
+      S* dst[1] = {d};
+      base += reduce_segment<DT, OP, 2, false, 1, false>(src, dst, len, mis, base);
+    } else {
+      using W = typename Word<T::B>::T;
+      auto gdst = [&](int) -> W* { return (W*)d; };
+      base += copy_segment<T::B, true, 1>((const W*)partial, gdst, 1, len, mis, base);
     }
-    base += ntiles;
   }
 }
 
@@ -112,9 +71,9 @@ static int launch_dt(int op, const RankPtrs& ptrs, const RingStepGeom& g, int gr
 int launch_ring_step(int dtype, int op, const RankPtrs& ptrs, const RingStepGeom& g, int max_grid,
                      void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  const uint64_t te = 2ull * kBlock * (dtype == kBF16 ? 8 : 4);
-  uint64_t tiles = (uint64_t)g.p * ((g.q + te - 1) / te);
-  if (tiles == 0) return 0;
+  const uint64_t te = (uint64_t)ReduceUnroll<2, false>::value * kBlock * (dtype == kBF16 ? 8 : 4);
+  const uint64_t tiles = (uint64_t)g.p * ((g.q + te - 1) / te + 1);
+  if (g.q == 0) return 0;
   const int grid = (int)(tiles < (uint64_t)max_grid ? tiles : (uint64_t)max_grid);
   switch (dtype) {
     case kF32: return launch_dt<kF32>(op, ptrs, g, grid, s);
