@@ -20,7 +20,8 @@
 namespace coll {
 
 // AllGather / Broadcast with a compile-time rank count P (0: any).
-// Destination pointers of a segment are read once into registers.
+// Destination pointers of a segment are read once into registers.  With
+// one rank the fan-out is a 1:1 copy and loads non-temporally too.
 template <int B, int KIND, int P>
 __global__ __launch_bounds__(kBlock) void fanout_kernel(RankPtrs ptrs, CopyGeom g) {
   using W = typename Word<B>::T;
@@ -36,7 +37,7 @@ __global__ __launch_bounds__(kBlock) void fanout_kernel(RankPtrs ptrs, CopyGeom 
 #pragma unroll
       for (int k = 0; k < P; ++k) dst[k] = (W*)ptrs.dst[k] + dst_off;
       auto gdst = [&](int d) -> W* { return dst[d]; };
-      base += copy_segment<B, false, P>(src, gdst, P, g.n, mis, base);
+      base += copy_segment<B, P == 1, P>(src, gdst, P, g.n, mis, base);
     } else {
       auto gdst = [&](int d) -> W* { return (W*)ptrs.dst[d] + dst_off; };
       base += copy_segment<B, false, 0>(src, gdst, p, g.n, mis, base);
@@ -140,6 +141,7 @@ static int clamp_grid(uint64_t tiles, int max_grid) {
 template <int B, int KIND>
 static void launch_fanout(int p, int grid, const RankPtrs& ptrs, const CopyGeom& g, hipStream_t s) {
   switch (p) {
+    case 1: hipLaunchKernelGGL((fanout_kernel<B, KIND, 1>), dim3(grid), dim3(kBlock), 0, s, ptrs, g); break;
     case 2: hipLaunchKernelGGL((fanout_kernel<B, KIND, 2>), dim3(grid), dim3(kBlock), 0, s, ptrs, g); break;
     case 4: hipLaunchKernelGGL((fanout_kernel<B, KIND, 4>), dim3(grid), dim3(kBlock), 0, s, ptrs, g); break;
     case 8: hipLaunchKernelGGL((fanout_kernel<B, KIND, 8>), dim3(grid), dim3(kBlock), 0, s, ptrs, g); break;
