@@ -1,0 +1,182 @@
+"""Parity at the benchmark workloads' full sizes, in the launch configuration
+bench.py times (same entry points, default grids, same seeded inputs).
+
+The oracle cannot reduce gigabytes in seconds, so reductions are checked on
+sampled elements it computes one by one (random positions plus every tile
+and chunk boundary nearby), and copies are checked whole against the
+oracle's definitions.  Properties that hold at any size (every rank of an
+AllReduce holds the same bits; AllGather is the rank-order concatenation of
+what ReduceScatter produced) are checked on the device over every element.
+"""
+import numpy as np
+import pytest
+
+from gpu_util import BF16, F32, I32, assert_bf16_within_ulp, assert_bits_equal, assert_fp32_close, to_host
+from oracle import ref
+from collective_communication_primitives_coll_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    import collective_communication_primitives_coll_amd as c
+    torch.cuda.set_device(0)
+    c.lib()
+    return torch, c
+
+
+def dev(torch, a):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def sample_positions(n, seed, tile, extra=()):
+    """Random positions plus the neighbourhood of every tile boundary among
+    the first and last few tiles, and of the given extra boundaries."""
+    rng = np.random.default_rng(seed)
+    pos = set(rng.integers(0, n, 20000).tolist())
+    for b in list(range(0, min(n, 4 * tile) + 1, tile)) + list(range(max(0, n - 3 * tile), n + 1, tile)) + list(extra):
+        for d in (-2, -1, 0, 1, 2):
+            if 0 <= b + d < n:
+                pos.add(b + d)
+    pos.update({0, n - 1})
+    return np.array(sorted(pos), dtype=np.int64)
+
+
+def gather_host(torch, t, idx, dtype):
+    """t[idx] copied to the host (bit patterns for bf16)."""
+    sel = t[torch.from_numpy(idx).cuda()]
+    return to_host(sel, dtype)
+
+
+def test_zero_rs_ag_full_size(env):
+    """ReduceScatter (sum) then AllGather, p=8, 2^26 bf16 per rank ~ N(0, 1e-3)."""
+    torch, coll = env
+    p, total = 8, 1 << 26
+    n = total // p
+    hx = inputs.rank_buffers(inputs.WL_ZERO_RS_AG, p, total, inputs.BF16, dist="normal", sigma=1e-3)
+    send = [dev(torch, x) for x in hx]
+    shard = [torch.empty(n, dtype=torch.bfloat16, device="cuda") for _ in range(p)]
+    full = [torch.empty(total, dtype=torch.bfloat16, device="cuda") for _ in range(p)]
+    coll.coll_reduce_scatter(send, shard, coll.COLL_SUM)
+    coll.coll_allgather(shard, full)
+    torch.cuda.synchronize()
+    stacked = np.stack(hx)
+    tile = 4 * 256 * 8   # ReduceScatter tile of bf16 at p=8: 4 vectors per lane
+    for r in range(p):
+        j = sample_positions(n, 1000 + r, tile)
+        cols = stacked[:, r * n + j]
+        expect = ref.reduce_elements(cols, np.full(len(j), r), ref.SUM, ref.BF16)
+        got = gather_host(torch, shard[r], j, BF16)
+        assert_bits_equal(got, expect, f"RS full size, block {r}")
+    # AllGather: every rank holds the rank-order concatenation of the shards
+    for r in range(p):
+        for s in range(p):
+            assert torch.equal(full[r][s * n:(s + 1) * n].view(torch.int16), shard[s].view(torch.int16)), \
+                f"AG full size rank {r} block {s}"
+
+
+def test_dp_allreduce_full_size(env):
+    """AllReduce sum, p=8, 2^26 fp32 per rank ~ N(0,1): fused ring (bit-exact),
+    one-pass tree (1e-5 * sum|x|), literal 14-step ring (bit-exact)."""
+    torch, coll = env
+    p, n = 8, 1 << 26
+    hx = inputs.rank_buffers(inputs.WL_DP_RING_AR, p, n, inputs.F32, dist="normal")
+    send = [dev(torch, x) for x in hx]
+    recv = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(p)]
+    stacked = np.stack(hx)
+    q = -(-n // p)
+    j = sample_positions(n, 7, 2 * 256 * 4, extra=[c * q for c in range(p)])
+    cols = stacked[:, j]
+    expect = ref.reduce_elements(cols, ref.chunk_of(j, n, p), ref.SUM, ref.F32)
+    abs_sum = np.sum(np.abs(cols.astype(np.float64)), axis=0)
+    for algo in (coll.COLL_ALGO_RING, coll.COLL_ALGO_ONEPASS, coll.COLL_ALGO_RING_LITERAL):
+        for t in recv:
+            t.fill_(float("nan"))
+        coll.coll_allreduce_algo(send, recv, algo, coll.COLL_SUM)
+        torch.cuda.synchronize()
+        for r in range(1, p):
+            assert torch.equal(recv[r].view(torch.int32), recv[0].view(torch.int32)), f"algo {algo}: rank {r} differs"
+        got = gather_host(torch, recv[0], j, F32)
+        if algo == coll.COLL_ALGO_ONEPASS:
+            assert_fp32_close(got, expect, abs_sum, 1e-5, "one-pass full size")
+        else:
+            assert_bits_equal(got, expect, f"algo {algo} full size")
+
+
+def test_small_allreduce_full_size(env):
+    """AllReduce p=4, 2^20 per rank: fp32 sum, int32 min and max; whole arrays."""
+    torch, coll = env
+    p, n = 4, 1 << 20
+    for dt, op in ((inputs.F32, ref.SUM), (inputs.I32, ref.MIN), (inputs.I32, ref.MAX)):
+        hx = inputs.rank_buffers(inputs.WL_AR_SMALL, p, n, dt)
+        send = [dev(torch, x) for x in hx]
+        recv = [torch.empty_like(s) for s in send]
+        coll.coll_allreduce(send, recv, op)
+        torch.cuda.synchronize()
+        expect = ref.allreduce(hx, op, dt)
+        for r in range(p):
+            assert_bits_equal(to_host(recv[r], dt), expect[r], f"AR p=4 dt={dt} op={op} rank {r}")
+
+
+def test_moe_alltoall_full_size(env):
+    """All-to-All and Alltoallv, p=8, 4096 x 7168 bf16 per rank; whole arrays."""
+    torch, coll = env
+    p, tokens, hidden = 8, 4096, 7168
+    per = tokens * hidden
+    hx = inputs.rank_buffers(inputs.WL_MOE_A2A, p, per, inputs.BF16, dist="normal")
+    send = [dev(torch, x) for x in hx]
+    recv = [torch.empty(per, dtype=torch.bfloat16, device="cuda") for _ in range(p)]
+    coll.coll_alltoall(send, recv, per // p)
+    torch.cuda.synchronize()
+    expect = ref.alltoall(hx)
+    for jr in range(p):
+        assert_bits_equal(to_host(recv[jr], BF16), expect[jr], f"A2A full size dest {jr}")
+    del recv, expect
+    counts = inputs.moe_token_counts(p, tokens) * hidden
+    cols = counts.sum(axis=0)
+    recv = [torch.empty(int(c), dtype=torch.bfloat16, device="cuda") for c in cols]
+    cdev = torch.from_numpy(counts.reshape(-1).copy()).cuda()
+    status = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    coll.coll_alltoallv(send, recv, cdev, status_dev=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    expect = ref.alltoallv(hx, counts)
+    for jr in range(p):
+        assert_bits_equal(to_host(recv[jr], BF16), expect[jr], f"A2Av full size dest {jr}")
+
+
+def test_small_batch_full_plan(env):
+    """The 10,000-call batched AllReduce plan at p=16 in one launch; a seeded
+    sample of calls (plus the first and last) checked whole."""
+    torch, coll = env
+    p = 16
+    plan, out_elems = inputs.small_batch_plan(10000)
+    pf, pi = inputs.small_batch_pools(p)
+    dpf = [dev(torch, x) for x in pf]
+    dpi = [dev(torch, x) for x in pi]
+    outs = [torch.empty(out_elems, dtype=torch.int32, device="cuda") for _ in range(p)]
+    bf = [t.data_ptr() for t in dpf]
+    bi = [t.data_ptr() for t in dpi]
+    bo = [t.data_ptr() for t in outs]
+    calls = []
+    for c in plan:
+        src = bf if c.dtype == inputs.F32 else bi
+        calls.append(([b + 4 * c.src_off for b in src], [b + 4 * c.dst_off for b in bo], c.n, c.dtype, c.op))
+    coll.coll_allreduce_batch(calls, p)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    pick = sorted(set(rng.choice(len(plan), 150, replace=False).tolist()) | {0, len(plan) - 1})
+    for k in pick:
+        c = plan[k]
+        pool = pf if c.dtype == inputs.F32 else pi
+        xs = [pool[r][c.src_off:c.src_off + c.n] for r in range(p)]
+        expect = ref.allreduce(xs, c.op, c.dtype)
+        for r in (0, 7, 15):
+            got = outs[r][c.dst_off:c.dst_off + c.n].cpu().numpy()
+            if c.dtype == inputs.F32:
+                got = got.view(np.float32)
+            assert_bits_equal(got, expect[r], f"batch call {k} rank {r}")
