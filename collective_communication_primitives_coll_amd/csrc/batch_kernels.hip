@@ -8,100 +8,127 @@
 //
 // The host lays out, per call, p chunks of ceil(n/p) elements, each cut
 // into tiles_per_chunk tiles, and a prefix of tile counts over the calls.
-// Each workgroup takes one contiguous run of the flat tile range, finds
-// its first call by binary search and then steps forward through the
-// calls, so the descriptor lookups per tile are a single comparison.
-// Within a tile the work is exactly the single-call AllReduce's: ring
-// order, partial in registers, p stores; tile 0 of a chunk also does the
-// chunk's misaligned head and tail.
+// Each wave (64 lanes) is an independent worker that takes one contiguous
+// run of the flat tile range, finds its first call by binary search and
+// then walks forward call by call and chunk by chunk, so descriptors,
+// rotated pointers and chunk geometry are read once per chunk of its run.
+// Wave-sized tiles keep lanes busy on the many chunks of a few hundred
+// elements that small calls produce.
+// Within a tile the work is the single-call AllReduce's: ring order,
+// partial in registers, p stores; the wave that holds tile 0 of a chunk
+// also does the chunk's misaligned head and tail.
 #include "reduce_tile.h"
 
 namespace coll {
 
-// Elements of a batch tile: one vector tile of the AllReduce kernel.
+constexpr int kWave = 64;  // lanes of a wave: the batch's unit of work
+
+// Elements of a batch tile: one wave's share, U vectors per lane.
 template <int DT, int P>
 __host__ __device__ constexpr uint64_t batch_tile_elems() {
-  return (uint64_t)ReduceUnroll<P, true>::value * kBlock * Traits<DT>::V;
+  return (uint64_t)ReduceUnroll<P, true>::value * kWave * Traits<DT>::V;
 }
 
+// Tiles [from, to) of one call (tile indices local to the call), walked
+// chunk by chunk by one wave: a chunk's rotated pointers and geometry are
+// set up once for all of its tiles in the run.
 template <int DT, int OP, int P>
-__device__ __forceinline__ void batch_tile(const BatchCall& bc, const void* const* pt, uint64_t local) {
+__device__ __forceinline__ void batch_run(const BatchCall& bc, const void* const* pt, uint64_t from,
+                                          uint64_t to, int lane) {
   using T = Traits<DT>;
   using S = typename T::S;
   constexpr int U = ReduceUnroll<P, true>::value;
-  constexpr uint64_t TV = (uint64_t)U * kBlock;
+  constexpr uint64_t TV = (uint64_t)U * kWave;
   constexpr int V = T::V;
   const uint64_t tpc = bc.tiles_per_chunk;
-  const int c = (int)(local / tpc);
-  const uint64_t t = local - (uint64_t)c * tpc;
   const uint64_t q = (bc.n + P - 1) / P;
-  uint64_t lo = (uint64_t)c * q, hi = lo + q;
-  if (lo > bc.n) lo = bc.n;
-  if (hi > bc.n) hi = bc.n;
-  const uint64_t len = hi - lo;
-  if (len == 0) return;
-  const S* src[P];
-  S* dst[P];
+  int c = (int)(from / tpc);
+  uint64_t t = from - (uint64_t)c * tpc;
+  uint64_t left = to - from;
+  while (left) {
+    const uint64_t cnt = (tpc - t) < left ? (tpc - t) : left;
+    uint64_t lo = (uint64_t)c * q, hi = lo + q;
+    if (lo > bc.n) lo = bc.n;
+    if (hi > bc.n) hi = bc.n;
+    const uint64_t len = hi - lo;
+    if (len) {
+      const S* src[P];
+      S* dst[P];
 #pragma unroll
-  for (int k = 0; k < P; ++k) {
-    src[k] = (const S*)pt[(c + 1 + k) % P] + lo;
-    dst[k] = (S*)pt[P + k] + lo;
-  }
-  const int mis = bc.mis < 0 ? -1 : (int)((bc.mis + lo * T::B) & 15);
-  const SegSpan sp = seg_span<T::B>(len, mis);
-  if (!sp.vec) {
-    const uint64_t from = t * TV * V;
-    if (from < len) {
-      const uint64_t cnt = (len - from) < TV * V ? (len - from) : TV * V;
-      reduce_elems<DT, OP, P, false, P, true>(src, dst, from, cnt);
-    }
-    return;
-  }
-  if (t * TV < sp.nvec) {
-    const S* vs[P];
-    S* vd[P];
+      for (int k = 0; k < P; ++k) {
+        src[k] = (const S*)pt[(c + 1 + k) % P] + lo;
+        dst[k] = (S*)pt[P + k] + lo;
+      }
+      const int mis = bc.mis < 0 ? -1 : (int)((bc.mis + lo * T::B) & 15);
+      const SegSpan sp = seg_span<T::B>(len, mis);
+      if (!sp.vec) {
+        for (uint64_t i = t; i < t + cnt; ++i) {
+          const uint64_t e0 = i * TV * V;
+          if (e0 < len)
+            reduce_elems<DT, OP, P, false, P, true, kWave>(src, dst, e0,
+                                                          (len - e0) < TV * V ? (len - e0) : TV * V, lane);
+        }
+      } else {
+        const S* vs[P];
+        S* vd[P];
 #pragma unroll
-    for (int k = 0; k < P; ++k) {
-      vs[k] = src[k] + sp.head;
-      vd[k] = dst[k] + sp.head;
+        for (int k = 0; k < P; ++k) {
+          vs[k] = src[k] + sp.head;
+          vd[k] = dst[k] + sp.head;
+        }
+        const uint64_t nfull = sp.nvec / TV;
+        for (uint64_t i = t; i < t + cnt; ++i) {
+          const uint64_t j0 = i * TV + lane;
+          if (i < nfull) reduce_vec_tile<DT, OP, P, false, P, true, U, true, kWave>(vs, vd, j0, sp.nvec);
+          else if (i * TV < sp.nvec) reduce_vec_tile<DT, OP, P, false, P, true, U, false, kWave>(vs, vd, j0, sp.nvec);
+        }
+        if (t == 0) {
+          if (sp.head) reduce_elems<DT, OP, P, false, P, true, kWave>(src, dst, 0, sp.head, lane);
+          if (sp.tail)
+            reduce_elems<DT, OP, P, false, P, true, kWave>(src, dst, sp.head + sp.nvec * V, sp.tail, lane);
+        }
+      }
     }
-    reduce_vec_tile<DT, OP, P, false, P, true, U, false>(vs, vd, t * TV + threadIdx.x, sp.nvec);
-  }
-  if (t == 0) {
-    if (sp.head) reduce_elems<DT, OP, P, false, P, true>(src, dst, 0, sp.head);
-    if (sp.tail) reduce_elems<DT, OP, P, false, P, true>(src, dst, sp.head + sp.nvec * V, sp.tail);
+    left -= cnt;
+    ++c;
+    t = 0;
   }
 }
 
 // Any rank count: element path with pointers read from the table.
 template <int DT, int OP>
-__device__ __forceinline__ void batch_tile_any(const BatchCall& bc, const void* const* pt, int p, uint64_t local) {
+__device__ __forceinline__ void batch_run_any(const BatchCall& bc, const void* const* pt, int p, uint64_t from,
+                                              uint64_t to, int lane) {
   using T = Traits<DT>;
   using S = typename T::S;
   using A = typename T::A;
-  constexpr uint64_t TE = (uint64_t)kBlock * T::V;
+  constexpr uint64_t TE = (uint64_t)kWave * T::V;
   const uint64_t tpc = bc.tiles_per_chunk;
-  const int c = (int)(local / tpc);
-  const uint64_t t = local - (uint64_t)c * tpc;
   const uint64_t q = (bc.n + p - 1) / p;
-  uint64_t lo = (uint64_t)c * q, hi = lo + q;
-  if (lo > bc.n) lo = bc.n;
-  if (hi > bc.n) hi = bc.n;
-  const uint64_t len = hi - lo;
-  for (uint64_t e = t * TE + threadIdx.x; e < len && e < (t + 1) * TE; e += kBlock) {
-    A acc = widen1<DT>(ld1<true>((const S*)pt[(c + 1) % p] + lo + e));
-    for (int k = 1; k < p; ++k) acc = combine<OP>(acc, widen1<DT>(ld1<true>((const S*)pt[(c + 1 + k) % p] + lo + e)));
-    const S out = narrow1<DT>(acc);
-    for (int k = 0; k < p; ++k) st1<true>((S*)pt[p + k] + lo + e, out);
+  for (uint64_t local = from; local < to; ++local) {
+    const int c = (int)(local / tpc);
+    const uint64_t t = local - (uint64_t)c * tpc;
+    uint64_t lo = (uint64_t)c * q, hi = lo + q;
+    if (lo > bc.n) lo = bc.n;
+    if (hi > bc.n) hi = bc.n;
+    const uint64_t len = hi - lo;
+    for (uint64_t e = t * TE + lane; e < len && e < (t + 1) * TE; e += kWave) {
+      A acc = widen1<DT>(ld1<true>((const S*)pt[(c + 1) % p] + lo + e));
+      for (int k = 1; k < p; ++k)
+        acc = combine<OP>(acc, widen1<DT>(ld1<true>((const S*)pt[(c + 1 + k) % p] + lo + e)));
+      const S out = narrow1<DT>(acc);
+      for (int k = 0; k < p; ++k) st1<true>((S*)pt[p + k] + lo + e, out);
+    }
   }
 }
 
 template <int P>
-__device__ __forceinline__ void batch_dispatch(const BatchCall& bc, const void* const* pt, int p, uint64_t local) {
+__device__ __forceinline__ void batch_dispatch(const BatchCall& bc, const void* const* pt, int p, uint64_t from,
+                                               uint64_t to, int lane) {
 #define COLL_BATCH_CASE(DTV, OPV)                                          \
   case DTV * 3 + OPV:                                                      \
-    if constexpr (P > 0) batch_tile<DTV, OPV, P>(bc, pt, local);           \
-    else batch_tile_any<DTV, OPV>(bc, pt, p, local);                       \
+    if constexpr (P > 0) batch_run<DTV, OPV, P>(bc, pt, from, to, lane);   \
+    else batch_run_any<DTV, OPV>(bc, pt, p, from, to, lane);               \
     break;
   switch (bc.dtype * 3 + bc.op) {
     COLL_BATCH_CASE(kF32, kSum)
@@ -118,13 +145,19 @@ __device__ __forceinline__ void batch_dispatch(const BatchCall& bc, const void* 
 #undef COLL_BATCH_CASE
 }
 
+// Every wave is an independent worker: it takes one contiguous run of the
+// flat tile range, finds its first call by binary search and walks
+// forward call by call.
 template <int P>
-__global__ __launch_bounds__(kBlock) void batch_kernel(BatchArgs a) {
+COLL_STREAM_KERNEL void batch_kernel(BatchArgs a) {
   const int p = P ? P : a.p;
+  const int lane = (int)(threadIdx.x % kWave);
+  const uint64_t waves = (uint64_t)gridDim.x * (kBlock / kWave);
+  const uint64_t wid =
+      (uint64_t)blockIdx.x * (kBlock / kWave) + (uint64_t)__builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const uint64_t total = a.calls[a.ncalls].first_tile;
-  const uint64_t grid = gridDim.x;
-  const uint64_t per = (total + grid - 1) / grid;
-  uint64_t t = (uint64_t)blockIdx.x * per;
+  const uint64_t per = (total + waves - 1) / waves;
+  uint64_t t = wid * per;
   uint64_t end = t + per;
   if (end > total) end = total;
   if (t >= end) return;
@@ -135,15 +168,13 @@ __global__ __launch_bounds__(kBlock) void batch_kernel(BatchArgs a) {
     if (a.calls[mid].first_tile <= t) lo = mid;
     else hi = mid;
   }
-  int k = lo;
-  uint64_t next_first = a.calls[k + 1].first_tile;
-  for (; t < end; ++t) {
-    while (t >= next_first) {
-      ++k;
-      next_first = a.calls[k + 1].first_tile;
-    }
+  for (int k = lo; t < end; ++k) {
     const BatchCall bc = a.calls[k];
-    batch_dispatch<P>(bc, a.ptrs + (size_t)k * 2 * p, p, t - bc.first_tile);
+    const uint64_t next = a.calls[k + 1].first_tile;
+    const uint64_t stop = next < end ? next : end;
+    if (stop > t)
+      batch_dispatch<P>(bc, a.ptrs + (size_t)k * 2 * p, p, t - bc.first_tile, stop - bc.first_tile, lane);
+    t = stop > t ? stop : t;
   }
 }
 
@@ -154,7 +185,7 @@ uint64_t batch_tile_elems_host(int dtype, int p) {
     case 4: return bf ? batch_tile_elems<kBF16, 4>() : batch_tile_elems<kF32, 4>();
     case 8: return bf ? batch_tile_elems<kBF16, 8>() : batch_tile_elems<kF32, 8>();
     case 16: return bf ? batch_tile_elems<kBF16, 16>() : batch_tile_elems<kF32, 16>();
-    default: return (uint64_t)kBlock * (bf ? 8 : 4);
+    default: return (uint64_t)kWave * (bf ? 8 : 4);
   }
 }
 

@@ -23,7 +23,7 @@ namespace coll {
 // Destination pointers of a segment are read once into registers.  With
 // one rank the fan-out is a 1:1 copy and loads non-temporally too.
 template <int B, int KIND, int P>
-__global__ __launch_bounds__(kBlock) void fanout_kernel(RankPtrs ptrs, CopyGeom g) {
+COLL_STREAM_KERNEL void fanout_kernel(RankPtrs ptrs, CopyGeom g) {
   using W = typename Word<B>::T;
   const int p = P ? P : g.p;
   const int nseg = KIND == kCopyAllGather ? p : 1;
@@ -47,7 +47,7 @@ __global__ __launch_bounds__(kBlock) void fanout_kernel(RankPtrs ptrs, CopyGeom 
 
 // Equal-split All-to-All: p*p segments, one destination each.
 template <int B>
-__global__ __launch_bounds__(kBlock) void alltoall_kernel(RankPtrs ptrs, CopyGeom g) {
+COLL_STREAM_KERNEL void alltoall_kernel(RankPtrs ptrs, CopyGeom g) {
   using W = typename Word<B>::T;
   const int p = g.p;
   uint64_t base = 0;
@@ -72,7 +72,7 @@ __global__ __launch_bounds__(kBlock) void alltoall_kernel(RankPtrs ptrs, CopyGeo
 // is written.
 // ---------------------------------------------------------------------------
 template <int B>
-__global__ __launch_bounds__(kBlock) void alltoallv_kernel(RankPtrs ptrs, A2avArgs a) {
+COLL_STREAM_KERNEL void alltoallv_kernel(RankPtrs ptrs, A2avArgs a) {
   using W = typename Word<B>::T;
   extern __shared__ int64_t lds[];
   __shared__ int bad;

@@ -36,6 +36,7 @@ __device__ __forceinline__ void copy_vec_tile(const u32x4* src, const GD& gdst, 
     const uint64_t j = j0 + (uint64_t)u * kBlock;
     if (FULL || j < nvec) r[u] = ld16<NTL>(src + j);
   }
+  __builtin_amdgcn_sched_barrier(0);  // all loads of the tile before the first store
   const int ndst = ND ? ND : nd;
 #pragma unroll
   for (int d = 0; d < ndst; ++d) {

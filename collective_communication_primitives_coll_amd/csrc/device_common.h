@@ -26,6 +26,13 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBlock = 256;  // threads per workgroup (4 wave64s)
 
+// Launch attributes of the streaming kernels.  They run one or two
+// workgroups per CU and rely on many loads in flight per lane, so the
+// compiler is told to target at most two waves per SIMD: it may then keep
+// every operand of a tile in registers instead of serialising loads to
+// fit a high-occupancy register budget.
+#define COLL_STREAM_KERNEL __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 2)))
+
 template <int DT> struct Traits;
 template <> struct Traits<kF32> {
   using S = float;     // storage type

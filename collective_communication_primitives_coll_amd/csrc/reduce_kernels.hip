@@ -28,7 +28,7 @@ __device__ __forceinline__ void chunk_range(const ReduceGeom& g, int c, uint64_t
 }
 
 template <int DT, int OP, int P, bool TREE, int DMODE>
-__global__ __launch_bounds__(kBlock) void reduce_kernel(RankPtrs ptrs, ReduceGeom g) {
+COLL_STREAM_KERNEL void reduce_kernel(RankPtrs ptrs, ReduceGeom g) {
   using T = Traits<DT>;
   using S = typename T::S;
   constexpr bool ALL = DMODE == kDstAll;
@@ -59,7 +59,7 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(RankPtrs ptrs, ReduceGeo
 // Any rank count (the slow general path): one vector per lane per tile,
 // operands in groups of 8 loads, pointers read from the kernel arguments.
 template <int DT, int OP, int DMODE>
-__global__ __launch_bounds__(kBlock) void reduce_kernel_any(RankPtrs ptrs, ReduceGeom g) {
+COLL_STREAM_KERNEL void reduce_kernel_any(RankPtrs ptrs, ReduceGeom g) {
   using T = Traits<DT>;
   using S = typename T::S;
   using A = typename T::A;

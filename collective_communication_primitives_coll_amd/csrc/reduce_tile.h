@@ -55,10 +55,11 @@ __device__ __forceinline__ u32x4 fold_vectors(const u32x4 (&r)[P]) {
   return narrow<DT>(acc);
 }
 
-// One vector tile.  src[k] and dst[d] point at the segment's first aligned
-// vector; j0 = tile * U * kBlock + lane is this lane's first vector index.
+// One vector tile worked by LANES lanes (a workgroup or a single wave).
+// src[k] and dst[d] point at the segment's first aligned vector;
+// j0 = tile * U * LANES + lane is this lane's first vector index.
 // FULL: every vector of the tile lies inside the segment (nvec unused).
-template <int DT, int OP, int P, bool TREE, int ND, bool NTS, int U, bool FULL>
+template <int DT, int OP, int P, bool TREE, int ND, bool NTS, int U, bool FULL, int LANES = kBlock>
 __device__ __forceinline__ void reduce_vec_tile(const typename Traits<DT>::S* const (&src)[P],
                                                 typename Traits<DT>::S* const (&dst)[ND],
                                                 uint64_t j0, uint64_t nvec) {
@@ -68,7 +69,7 @@ __device__ __forceinline__ void reduce_vec_tile(const typename Traits<DT>::S* co
   for (int k = 0; k < P; ++k)
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const uint64_t j = j0 + (uint64_t)u * kBlock;
+      const uint64_t j = j0 + (uint64_t)u * LANES;
       if (FULL || j < nvec) raw[u][k] = ld16<true>(src[k] + j * V);
       else raw[u][k] = u32x4{0, 0, 0, 0};
     }
@@ -79,19 +80,21 @@ __device__ __forceinline__ void reduce_vec_tile(const typename Traits<DT>::S* co
   for (int d = 0; d < ND; ++d)
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const uint64_t j = j0 + (uint64_t)u * kBlock;
+      const uint64_t j = j0 + (uint64_t)u * LANES;
       if (FULL || j < nvec) st16<NTS>(dst[d] + j * V, out[u]);
     }
 }
 
 // Element-wise path: cnt elements from element offset `from` of the
-// segment (src/dst at the segment start), one element per lane.
-template <int DT, int OP, int P, bool TREE, int ND, bool NTS>
+// segment (src/dst at the segment start), one element per lane; `lane`
+// of LANES lanes.
+template <int DT, int OP, int P, bool TREE, int ND, bool NTS, int LANES = kBlock>
 __device__ __forceinline__ void reduce_elems(const typename Traits<DT>::S* const (&src)[P],
                                              typename Traits<DT>::S* const (&dst)[ND], uint64_t from,
-                                             uint64_t cnt) {
+                                             uint64_t cnt, int lane = -1) {
   using A = typename Traits<DT>::A;
-  for (uint64_t i = threadIdx.x; i < cnt; i += kBlock) {
+  const uint64_t l0 = lane < 0 ? threadIdx.x : (uint64_t)lane;
+  for (uint64_t i = l0; i < cnt; i += LANES) {
     const uint64_t e = from + i;
     A a[P];
 #pragma unroll

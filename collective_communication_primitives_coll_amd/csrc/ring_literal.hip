@@ -21,7 +21,7 @@
 namespace coll {
 
 template <int DT, int OP>
-__global__ __launch_bounds__(kBlock) void ring_step_kernel(RankPtrs ptrs, RingStepGeom g) {
+COLL_STREAM_KERNEL void ring_step_kernel(RankPtrs ptrs, RingStepGeom g) {
   using T = Traits<DT>;
   using S = typename T::S;
   const int p = g.p;
