@@ -356,6 +356,7 @@ def batch_row(torch, coll, inputs, dev, iters=5, warmup=2):
     wall_us = (time.perf_counter() - t0) / iters * 1e6
     med, p95, _ = stats_us(time_launches(torch, [f], iters, 1)[0])
     hbm = 2 * p * total_bytes
+    indiv = individual_calls(torch, coll, calls, p)
     return {
         "name": "allreduce_batch_10000", "p": p, "calls": len(plan), "dtype": "f32/i32", "op": "sum/min/max",
         "payload_bytes": total_bytes,
@@ -365,6 +366,51 @@ def batch_row(torch, coll, inputs, dev, iters=5, warmup=2):
         "pct_hbm_peak": round(100.0 * hbm / (med * 1e-6) / 1e9 / HBM_PEAK, 1),
         "busbw_GBps": round(total_bytes / (med * 1e-6) / 1e9 * 2 * (p - 1) / p, 1),
         "workload": "10,000 AllReduces, sizes log-uniform 4 KiB-1 MiB, one launch",
+        "individual_calls": indiv,
+    }
+
+
+def individual_calls(torch, coll, calls, p, sample=1000):
+    """The same AllReduces as separate coll_allreduce calls.
+
+    back_to_back: all calls enqueued without synchronisation (arguments
+    marshalled beforehand), wall time per call; this is the submission
+    rate of one host thread.  latency: a seeded sample of calls, each
+    followed by a stream synchronisation, end-to-end wall time per call
+    (host validation + launch + kernel + completion), with percentiles and
+    a least-squares fit t = alpha + bytes / beta (the alpha-beta model of
+    "集合通信：原语、算法、NCCL 实现与拓扑映射", section 2.1)."""
+    prepared = [coll.coll_allreduce(s, r, op, n=n, dtype=dt, defer=True) for s, r, n, dt, op in calls]
+    for f in prepared[:200]:
+        f()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for f in prepared:
+        f()
+    torch.cuda.synchronize()
+    b2b_us = (time.perf_counter() - t0) / len(prepared) * 1e6
+    rng = np.random.default_rng(11)
+    idx = rng.choice(len(prepared), min(sample, len(prepared)), replace=False)
+    lat, size = [], []
+    for k in idx:
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        prepared[k]()
+        torch.cuda.synchronize()
+        lat.append((time.perf_counter() - t1) * 1e6)
+        size.append(4 * calls[k][2])
+    lat, size = np.asarray(lat), np.asarray(size, dtype=np.float64)
+    A = np.stack([np.ones_like(size), size], axis=1)
+    (alpha, inv_beta), *_ = np.linalg.lstsq(A, lat, rcond=None)
+    return {
+        "back_to_back_us_per_call": round(b2b_us, 2),
+        "latency_sample": int(len(lat)),
+        "latency_p50_us": round(float(np.percentile(lat, 50)), 2),
+        "latency_p95_us": round(float(np.percentile(lat, 95)), 2),
+        "latency_p99_us": round(float(np.percentile(lat, 99)), 2),
+        "alpha_us": round(float(alpha), 2),
+        "beta_GBps_per_rank_payload": round(float(1e-3 / inv_beta), 1) if inv_beta > 0 else None,
+        "note": "alpha-beta fitted on end-to-end latency vs per-rank payload bytes",
     }
 
 

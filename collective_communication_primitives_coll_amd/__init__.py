@@ -19,7 +19,8 @@ from typing import Any, Sequence
 COLL_F32, COLL_BF16, COLL_I32 = 0, 1, 2
 COLL_SUM, COLL_MIN, COLL_MAX = 0, 1, 2
 COLL_OK, COLL_ERR_INVALID_ARG, COLL_ERR_UNSUPPORTED, COLL_ERR_ALIAS, COLL_ERR_HIP = 0, 1, 2, 3, 4
-COLL_ALGO_RING, COLL_ALGO_ONEPASS, COLL_ALGO_RING_LITERAL = 0, 1, 2
+COLL_ALGO_RING, COLL_ALGO_ONEPASS, COLL_ALGO_RING_LITERAL, COLL_ALGO_HALVING_DOUBLING = 0, 1, 2, 3
+COLL_ALGO_RECURSIVE_DOUBLING = COLL_ALGO_ONEPASS
 COLL_MAX_RANKS = 64
 COLL_BATCH_CHECK_ALIAS = 1
 

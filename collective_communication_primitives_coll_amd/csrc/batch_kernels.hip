@@ -65,7 +65,7 @@ __device__ __forceinline__ void batch_run(const BatchCall& bc, const void* const
         for (uint64_t i = t; i < t + cnt; ++i) {
           const uint64_t e0 = i * TV * V;
           if (e0 < len)
-            reduce_elems<DT, OP, P, false, P, true, kWave>(src, dst, e0,
+            reduce_elems<DT, OP, P, kOrdRing, P, true, kWave>(src, dst, e0,
                                                           (len - e0) < TV * V ? (len - e0) : TV * V, lane);
         }
       } else {
@@ -79,13 +79,13 @@ __device__ __forceinline__ void batch_run(const BatchCall& bc, const void* const
         const uint64_t nfull = sp.nvec / TV;
         for (uint64_t i = t; i < t + cnt; ++i) {
           const uint64_t j0 = i * TV + lane;
-          if (i < nfull) reduce_vec_tile<DT, OP, P, false, P, true, U, true, kWave>(vs, vd, j0, sp.nvec);
-          else if (i * TV < sp.nvec) reduce_vec_tile<DT, OP, P, false, P, true, U, false, kWave>(vs, vd, j0, sp.nvec);
+          if (i < nfull) reduce_vec_tile<DT, OP, P, kOrdRing, P, true, U, true, kWave>(vs, vd, j0, sp.nvec);
+          else if (i * TV < sp.nvec) reduce_vec_tile<DT, OP, P, kOrdRing, P, true, U, false, kWave>(vs, vd, j0, sp.nvec);
         }
         if (t == 0) {
-          if (sp.head) reduce_elems<DT, OP, P, false, P, true, kWave>(src, dst, 0, sp.head, lane);
+          if (sp.head) reduce_elems<DT, OP, P, kOrdRing, P, true, kWave>(src, dst, 0, sp.head, lane);
           if (sp.tail)
-            reduce_elems<DT, OP, P, false, P, true, kWave>(src, dst, sp.head + sp.nvec * V, sp.tail, lane);
+            reduce_elems<DT, OP, P, kOrdRing, P, true, kWave>(src, dst, sp.head + sp.nvec * V, sp.tail, lane);
         }
       }
     }

@@ -188,10 +188,11 @@ coll_status_t check_allreduce(const void* const* send, void* const* recv, int p,
 COLL_EXPORT coll_status_t coll_allreduce_algo(const void* const* send, void* const* recv, int p, size_t n,
                                               coll_dtype_t dtype, coll_op_t op, coll_algo_t algo,
                                               void* stream) {
-  if ((int)algo < COLL_ALGO_RING || (int)algo > COLL_ALGO_RING_LITERAL) return COLL_ERR_INVALID_ARG;
+  if ((int)algo < COLL_ALGO_RING || (int)algo > COLL_ALGO_HALVING_DOUBLING) return COLL_ERR_INVALID_ARG;
   coll_status_t st = check_allreduce(send, recv, p, n, dtype, op);
   if (st != COLL_OK || n == 0) return st;
-  if (algo == COLL_ALGO_ONEPASS && !(p == 2 || p == 4 || p == 8 || p == 16)) return COLL_ERR_UNSUPPORTED;
+  const bool tree_algo = algo == COLL_ALGO_RECURSIVE_DOUBLING || algo == COLL_ALGO_HALVING_DOUBLING;
+  if (tree_algo && !(p == 2 || p == 4 || p == 8 || p == 16)) return COLL_ERR_UNSUPPORTED;
   if (algo == COLL_ALGO_RING_LITERAL && dtype == COLL_BF16) return COLL_ERR_UNSUPPORTED;
   int grid;
   int e = max_grid(&grid, algo == COLL_ALGO_RING_LITERAL ? kFamCopy : kFamReduce);
@@ -227,8 +228,10 @@ COLL_EXPORT coll_status_t coll_allreduce_algo(const void* const* send, void* con
   g.dst_mode = coll::kDstAll;
   g.src_mis = smis;
   g.dst_mis = dmis;
-  const bool tree = algo == COLL_ALGO_ONEPASS && dtype != COLL_I32 && op == COLL_SUM;
-  return finish(coll::launch_reduce(dtype, op, tree ? 1 : 0, P, g, grid, stream));
+  const int order = algo == COLL_ALGO_RECURSIVE_DOUBLING ? coll::kOrdRD
+                    : algo == COLL_ALGO_HALVING_DOUBLING  ? coll::kOrdHD
+                                                          : coll::kOrdRing;
+  return finish(coll::launch_reduce(dtype, op, order, P, g, grid, stream));
 }
 
 COLL_EXPORT coll_status_t coll_allreduce(const void* const* send, void* const* recv, int p, size_t n,
@@ -265,7 +268,7 @@ COLL_EXPORT coll_status_t coll_reduce(const void* const* send, void* recv_root, 
   g.dst_mode = coll::kDstFixed;
   g.src_mis = common_mis(send, p);
   g.dst_mis = (int)((uintptr_t)recv_root & 15);
-  return finish(coll::launch_reduce(dtype, op, 0, P, g, grid, stream));
+  return finish(coll::launch_reduce(dtype, op, coll::kOrdRing, P, g, grid, stream));
 }
 
 COLL_EXPORT coll_status_t coll_broadcast(const void* send_root, void* const* recv, int p, size_t n,
@@ -322,7 +325,7 @@ COLL_EXPORT coll_status_t coll_reduce_scatter(const void* const* send, void* con
   g.dst_mode = coll::kDstOwner;
   g.src_mis = common_mis(send, p);
   g.dst_mis = common_mis((const void* const*)recv, p);
-  return finish(coll::launch_reduce(dtype, op, 0, P, g, grid, stream));
+  return finish(coll::launch_reduce(dtype, op, coll::kOrdRing, P, g, grid, stream));
 }
 
 COLL_EXPORT coll_status_t coll_allgather(const void* const* send, void* const* recv, int p, size_t n,

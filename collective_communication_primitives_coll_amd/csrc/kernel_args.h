@@ -12,6 +12,13 @@ namespace coll {
 constexpr int kMaxRanks = 64;
 
 enum DType : int { kF32 = 0, kBF16 = 1, kI32 = 2 };
+
+// Summation order of a reduction.
+enum Order : int {
+  kOrdRing = 0,  // left fold over the rotated ring order x_{c+1}, ..., x_c
+  kOrdRD = 1,    // balanced tree pairing ranks (0,1), (2,3), ... first (recursive doubling)
+  kOrdHD = 2     // balanced tree pairing ranks (k, k + p/2) first (halving-doubling)
+};
 enum Op : int { kSum = 0, kMin = 1, kMax = 2 };
 
 // Destination selection of the reduction kernels.
@@ -92,7 +99,7 @@ struct BatchArgs {
 // Launchers (return a hipError_t as int).
 // max_grid bounds the number of workgroups; launchers shrink it to the
 // number of tiles.  launch_alltoallv and launch_batch take the grid as is.
-int launch_reduce(int dtype, int op, int algo_tree, const RankPtrs& ptrs, const ReduceGeom& g,
+int launch_reduce(int dtype, int op, int order, const RankPtrs& ptrs, const ReduceGeom& g,
                   int max_grid, void* stream);
 int launch_copy(int elem_bytes, const RankPtrs& ptrs, const CopyGeom& g, int max_grid, void* stream);
 int launch_alltoallv(int elem_bytes, const RankPtrs& ptrs, const A2avArgs& a, int grid, void* stream);

@@ -27,7 +27,7 @@ __device__ __forceinline__ void chunk_range(const ReduceGeom& g, int c, uint64_t
   *len = b - a;
 }
 
-template <int DT, int OP, int P, bool TREE, int DMODE>
+template <int DT, int OP, int P, int ORD, int DMODE>
 COLL_STREAM_KERNEL void reduce_kernel(RankPtrs ptrs, ReduceGeom g) {
   using T = Traits<DT>;
   using S = typename T::S;
@@ -41,7 +41,7 @@ COLL_STREAM_KERNEL void reduce_kernel(RankPtrs ptrs, ReduceGeom g) {
     const uint64_t doff = (DMODE == kDstOwner) ? 0 : lo;
     const S* src[P];
 #pragma unroll
-    for (int k = 0; k < P; ++k) src[k] = (const S*)ptrs.src[TREE ? k : (c + 1 + k) % P] + lo;
+    for (int k = 0; k < P; ++k) src[k] = (const S*)ptrs.src[ORD != kOrdRing ? k : (c + 1 + k) % P] + lo;
     S* dst[ND];
     if constexpr (ALL) {
 #pragma unroll
@@ -52,7 +52,7 @@ COLL_STREAM_KERNEL void reduce_kernel(RankPtrs ptrs, ReduceGeom g) {
       dst[0] = (S*)ptrs.dst[0] + lo;
     }
     const int mis = seg_mis(g.src_mis, g.dst_mis, lo * T::B, doff * T::B);
-    base += reduce_segment<DT, OP, P, TREE, ND, ALL>(src, dst, len, mis, base);
+    base += reduce_segment<DT, OP, P, ORD, ND, ALL>(src, dst, len, mis, base);
   }
 }
 
@@ -159,20 +159,20 @@ static int clamp_grid(uint64_t tiles, int max_grid) {
   return (int)(tiles < (uint64_t)max_grid ? tiles : (uint64_t)max_grid);
 }
 
-template <int DT, int OP, int P, bool TREE>
+template <int DT, int OP, int P, int ORD>
 static int launch_p(const RankPtrs& ptrs, const ReduceGeom& g, int max_grid, hipStream_t s) {
   if (g.dst_mode == kDstAll) {
     const int grid = clamp_grid(count_tiles<DT, P, true>(g), max_grid);
     if (grid)
-      hipLaunchKernelGGL((reduce_kernel<DT, OP, P, TREE, kDstAll>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
+      hipLaunchKernelGGL((reduce_kernel<DT, OP, P, ORD, kDstAll>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
     return (int)hipGetLastError();
   }
   const int grid = clamp_grid(count_tiles<DT, P, false>(g), max_grid);
   if (!grid) return 0;
   if (g.dst_mode == kDstOwner)
-    hipLaunchKernelGGL((reduce_kernel<DT, OP, P, TREE, kDstOwner>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
+    hipLaunchKernelGGL((reduce_kernel<DT, OP, P, ORD, kDstOwner>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
   else
-    hipLaunchKernelGGL((reduce_kernel<DT, OP, P, TREE, kDstFixed>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
+    hipLaunchKernelGGL((reduce_kernel<DT, OP, P, ORD, kDstFixed>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
   return (int)hipGetLastError();
 }
 
@@ -189,47 +189,53 @@ static int launch_any(const RankPtrs& ptrs, const ReduceGeom& g, int max_grid, h
   return (int)hipGetLastError();
 }
 
+// Tree orders only change the result of floating-point sums; integer sums
+// and min/max give the same bits in any order, so they always run the
+// ring-order kernel.
+template <int DT, int OP, int ORD>
+static int launch_tree(const RankPtrs& ptrs, const ReduceGeom& g, int max_grid, hipStream_t s) {
+  switch (g.p) {
+    case 2: return launch_p<DT, OP, 2, ORD>(ptrs, g, max_grid, s);
+    case 4: return launch_p<DT, OP, 4, ORD>(ptrs, g, max_grid, s);
+    case 8: return launch_p<DT, OP, 8, ORD>(ptrs, g, max_grid, s);
+    case 16: return launch_p<DT, OP, 16, ORD>(ptrs, g, max_grid, s);
+    default: return (int)hipErrorInvalidValue;
+  }
+}
+
 template <int DT, int OP>
-static int launch_dt_op(bool tree, const RankPtrs& ptrs, const ReduceGeom& g, int max_grid, hipStream_t s) {
+static int launch_dt_op(int order, const RankPtrs& ptrs, const ReduceGeom& g, int max_grid, hipStream_t s) {
   if constexpr ((DT == kF32 || DT == kBF16) && OP == kSum) {
-    if (tree) {
-      switch (g.p) {
-        case 2: return launch_p<DT, OP, 2, true>(ptrs, g, max_grid, s);
-        case 4: return launch_p<DT, OP, 4, true>(ptrs, g, max_grid, s);
-        case 8: return launch_p<DT, OP, 8, true>(ptrs, g, max_grid, s);
-        case 16: return launch_p<DT, OP, 16, true>(ptrs, g, max_grid, s);
-        default: return (int)hipErrorInvalidValue;
-      }
-    }
+    if (order == kOrdRD) return launch_tree<DT, OP, kOrdRD>(ptrs, g, max_grid, s);
+    if (order == kOrdHD) return launch_tree<DT, OP, kOrdHD>(ptrs, g, max_grid, s);
   }
   switch (g.p) {
-    case 2: return launch_p<DT, OP, 2, false>(ptrs, g, max_grid, s);
-    case 4: return launch_p<DT, OP, 4, false>(ptrs, g, max_grid, s);
-    case 8: return launch_p<DT, OP, 8, false>(ptrs, g, max_grid, s);
-    case 16: return launch_p<DT, OP, 16, false>(ptrs, g, max_grid, s);
+    case 2: return launch_p<DT, OP, 2, kOrdRing>(ptrs, g, max_grid, s);
+    case 4: return launch_p<DT, OP, 4, kOrdRing>(ptrs, g, max_grid, s);
+    case 8: return launch_p<DT, OP, 8, kOrdRing>(ptrs, g, max_grid, s);
+    case 16: return launch_p<DT, OP, 16, kOrdRing>(ptrs, g, max_grid, s);
     default: return launch_any<DT, OP>(ptrs, g, max_grid, s);
   }
 }
 
 template <int DT>
-static int launch_dt(int op, bool tree, const RankPtrs& ptrs, const ReduceGeom& g, int max_grid,
+static int launch_dt(int op, int order, const RankPtrs& ptrs, const ReduceGeom& g, int max_grid,
                      hipStream_t s) {
   switch (op) {
-    case kSum: return launch_dt_op<DT, kSum>(tree, ptrs, g, max_grid, s);
-    case kMin: return launch_dt_op<DT, kMin>(tree, ptrs, g, max_grid, s);
-    case kMax: return launch_dt_op<DT, kMax>(tree, ptrs, g, max_grid, s);
+    case kSum: return launch_dt_op<DT, kSum>(order, ptrs, g, max_grid, s);
+    case kMin: return launch_dt_op<DT, kMin>(order, ptrs, g, max_grid, s);
+    case kMax: return launch_dt_op<DT, kMax>(order, ptrs, g, max_grid, s);
   }
   return (int)hipErrorInvalidValue;
 }
 
-int launch_reduce(int dtype, int op, int algo_tree, const RankPtrs& ptrs, const ReduceGeom& g,
+int launch_reduce(int dtype, int op, int order, const RankPtrs& ptrs, const ReduceGeom& g,
                   int max_grid, void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  const bool tree = algo_tree != 0;
   switch (dtype) {
-    case kF32: return launch_dt<kF32>(op, tree, ptrs, g, max_grid, s);
-    case kBF16: return launch_dt<kBF16>(op, tree, ptrs, g, max_grid, s);
-    case kI32: return launch_dt<kI32>(op, tree, ptrs, g, max_grid, s);
+    case kF32: return launch_dt<kF32>(op, order, ptrs, g, max_grid, s);
+    case kBF16: return launch_dt<kBF16>(op, order, ptrs, g, max_grid, s);
+    case kI32: return launch_dt<kI32>(op, order, ptrs, g, max_grid, s);
   }
   return (int)hipErrorInvalidValue;
 }

@@ -6,8 +6,11 @@
 // "集合通信：原语、算法、NCCL 实现与拓扑映射" (hpc/04, section 2.2) with the
 // partial held in registers across its p-1 combine steps, and for
 // AllReduce the p all-gather stores issued from the same registers.
-// TREE instead sums the operands as a balanced pairwise tree in rank order
-// (a one-pass reassociated sum).
+// The tree orders instead sum the operands, listed in rank order, as a
+// balanced pairwise tree: kOrdRD pairs neighbours first, as recursive
+// doubling does (section 2.3 there: exchange at distance 1, 2, 4, ...);
+// kOrdHD pairs ranks p/2 apart first, as the recursive-halving
+// reduce-scatter of halving-doubling does.
 //
 // A lane handles U vectors of a tile.  It issues all P*U loads before the
 // first combine, source by source, so it keeps P*U 16-byte requests in
@@ -27,13 +30,13 @@ struct ReduceUnroll {
   static constexpr int value = raw < 1 ? 1 : (raw > 8 ? 8 : raw);
 };
 
-// Fold of P operands already widened, in list order or as a tree.
-template <int DT, int OP, int P, bool TREE>
+// Fold of P operands, in list order or as one of the trees.
+template <int DT, int OP, int P, int ORD>
 __device__ __forceinline__ u32x4 fold_vectors(const u32x4 (&r)[P]) {
   using A = typename Traits<DT>::A;
   constexpr int V = Traits<DT>::V;
   A acc[V];
-  if constexpr (TREE) {
+  if constexpr (ORD == kOrdRD) {
     A a[P][V];
 #pragma unroll
     for (int k = 0; k < P; ++k) widen<DT>(r[k], a[k]);
@@ -41,6 +44,16 @@ __device__ __forceinline__ u32x4 fold_vectors(const u32x4 (&r)[P]) {
     for (int st = 1; st < P; st *= 2)
 #pragma unroll
       for (int k = 0; k + st < P; k += 2 * st) combine_vec<OP, DT>(a[k], a[k + st]);
+#pragma unroll
+    for (int x = 0; x < V; ++x) acc[x] = a[0][x];
+  } else if constexpr (ORD == kOrdHD) {
+    A a[P][V];
+#pragma unroll
+    for (int k = 0; k < P; ++k) widen<DT>(r[k], a[k]);
+#pragma unroll
+    for (int st = P / 2; st >= 1; st /= 2)
+#pragma unroll
+      for (int k = 0; k < st; ++k) combine_vec<OP, DT>(a[k], a[k + st]);
 #pragma unroll
     for (int x = 0; x < V; ++x) acc[x] = a[0][x];
   } else {
@@ -59,7 +72,7 @@ __device__ __forceinline__ u32x4 fold_vectors(const u32x4 (&r)[P]) {
 // src[k] and dst[d] point at the segment's first aligned vector;
 // j0 = tile * U * LANES + lane is this lane's first vector index.
 // FULL: every vector of the tile lies inside the segment (nvec unused).
-template <int DT, int OP, int P, bool TREE, int ND, bool NTS, int U, bool FULL, int LANES = kBlock>
+template <int DT, int OP, int P, int ORD, int ND, bool NTS, int U, bool FULL, int LANES = kBlock>
 __device__ __forceinline__ void reduce_vec_tile(const typename Traits<DT>::S* const (&src)[P],
                                                 typename Traits<DT>::S* const (&dst)[ND],
                                                 uint64_t j0, uint64_t nvec) {
@@ -75,7 +88,7 @@ __device__ __forceinline__ void reduce_vec_tile(const typename Traits<DT>::S* co
     }
   u32x4 out[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) out[u] = fold_vectors<DT, OP, P, TREE>(raw[u]);
+  for (int u = 0; u < U; ++u) out[u] = fold_vectors<DT, OP, P, ORD>(raw[u]);
 #pragma unroll
   for (int d = 0; d < ND; ++d)
 #pragma unroll
@@ -88,7 +101,7 @@ __device__ __forceinline__ void reduce_vec_tile(const typename Traits<DT>::S* co
 // Element-wise path: cnt elements from element offset `from` of the
 // segment (src/dst at the segment start), one element per lane; `lane`
 // of LANES lanes.
-template <int DT, int OP, int P, bool TREE, int ND, bool NTS, int LANES = kBlock>
+template <int DT, int OP, int P, int ORD, int ND, bool NTS, int LANES = kBlock>
 __device__ __forceinline__ void reduce_elems(const typename Traits<DT>::S* const (&src)[P],
                                              typename Traits<DT>::S* const (&dst)[ND], uint64_t from,
                                              uint64_t cnt, int lane = -1) {
@@ -100,11 +113,17 @@ __device__ __forceinline__ void reduce_elems(const typename Traits<DT>::S* const
 #pragma unroll
     for (int k = 0; k < P; ++k) a[k] = widen1<DT>(ld1<true>(src[k] + e));
     A acc;
-    if constexpr (TREE) {
+    if constexpr (ORD == kOrdRD) {
 #pragma unroll
       for (int st = 1; st < P; st *= 2)
 #pragma unroll
         for (int k = 0; k + st < P; k += 2 * st) a[k] = combine<OP>(a[k], a[k + st]);
+      acc = a[0];
+    } else if constexpr (ORD == kOrdHD) {
+#pragma unroll
+      for (int st = P / 2; st >= 1; st /= 2)
+#pragma unroll
+        for (int k = 0; k < st; ++k) a[k] = combine<OP>(a[k], a[k + st]);
       acc = a[0];
     } else {
       acc = a[0];
@@ -121,7 +140,7 @@ __device__ __forceinline__ void reduce_elems(const typename Traits<DT>::S* const
 // (flat tile indices congruent to the workgroup id modulo the grid,
 // counting from `base`) and, for the owning workgroup, the head and tail.
 // Returns the segment's tile count (the caller advances base by it).
-template <int DT, int OP, int P, bool TREE, int ND, bool NTS>
+template <int DT, int OP, int P, int ORD, int ND, bool NTS>
 __device__ __forceinline__ uint64_t reduce_segment(const typename Traits<DT>::S* const (&src)[P],
                                                    typename Traits<DT>::S* const (&dst)[ND],
                                                    uint64_t len, int mis, uint64_t base) {
@@ -138,7 +157,7 @@ __device__ __forceinline__ uint64_t reduce_segment(const typename Traits<DT>::S*
     for (uint64_t t = first_tile(base, wg, grid); t < nt; t += grid) {
       const uint64_t from = t * TE;
       const uint64_t cnt = (len - from) < TE ? (len - from) : TE;
-      reduce_elems<DT, OP, P, TREE, ND, NTS>(src, dst, from, cnt);
+      reduce_elems<DT, OP, P, ORD, ND, NTS>(src, dst, from, cnt);
     }
     return nt;
   }
@@ -153,13 +172,13 @@ __device__ __forceinline__ uint64_t reduce_segment(const typename Traits<DT>::S*
     const uint64_t nfull = sp.nvec / TV;
     for (uint64_t t = first_tile(base, wg, grid); t < nt; t += grid) {
       const uint64_t j0 = t * TV + threadIdx.x;
-      if (t < nfull) reduce_vec_tile<DT, OP, P, TREE, ND, NTS, U, true>(vs, vd, j0, sp.nvec);
-      else reduce_vec_tile<DT, OP, P, TREE, ND, NTS, U, false>(vs, vd, j0, sp.nvec);
+      if (t < nfull) reduce_vec_tile<DT, OP, P, ORD, ND, NTS, U, true>(vs, vd, j0, sp.nvec);
+      else reduce_vec_tile<DT, OP, P, ORD, ND, NTS, U, false>(vs, vd, j0, sp.nvec);
     }
   }
   if ((sp.head || sp.tail) && first_tile(base, wg, grid) == 0) {
-    if (sp.head) reduce_elems<DT, OP, P, TREE, ND, NTS>(src, dst, 0, sp.head);
-    if (sp.tail) reduce_elems<DT, OP, P, TREE, ND, NTS>(src, dst, sp.head + sp.nvec * V, sp.tail);
+    if (sp.head) reduce_elems<DT, OP, P, ORD, ND, NTS>(src, dst, 0, sp.head);
+    if (sp.tail) reduce_elems<DT, OP, P, ORD, ND, NTS>(src, dst, sp.head + sp.nvec * V, sp.tail);
   }
   return nt;
 }

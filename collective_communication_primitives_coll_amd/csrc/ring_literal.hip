@@ -41,7 +41,7 @@ COLL_STREAM_KERNEL void ring_step_kernel(RankPtrs ptrs, RingStepGeom g) {
       // received partial on the left, the receiver's own input on the right
       const S* src[2] = {partial, (const S*)ptrs.src[nxt] + lo};
       S* dst[1] = {d};
-      base += reduce_segment<DT, OP, 2, false, 1, false>(src, dst, len, mis, base);
+      base += reduce_segment<DT, OP, 2, kOrdRing, 1, false>(src, dst, len, mis, base);
     } else {
       using W = typename Word<T::B>::T;
       auto gdst = [&](int) -> W* { return (W*)d; };

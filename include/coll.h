@@ -66,22 +66,33 @@ typedef enum {
   COLL_ERR_HIP = 4           /* the HIP runtime reported an error; see coll_last_hip_error */
 } coll_status_t;
 
-/* AllReduce schedules ([A] 2.2 ring; 2.3 table of algorithms).
+/* AllReduce schedules ([A] 2.2 ring; 2.3 recursive doubling and
+ * halving-doubling).  On one device every schedule reads each input once
+ * and writes each output once; they differ in the floating-point
+ * summation order, which each reproduces exactly.
  * RING: each chunk c of q = ceil(n/p) elements is folded in the ring
  *   order x_{c+1}, x_{c+2}, ..., x_c (indices mod p) with the partial kept
  *   on chip across the p-1 combine steps, then stored to all p outputs in
  *   the same pass (reduce-scatter and all-gather fused).  Bit-exact with
  *   the ring all-reduce of [A] 2.2 read with chunk c ending on rank c.
- * ONEPASS: all p inputs read at once and summed as a balanced pairwise
- *   tree in rank order (another correct summation order, [B] numerics);
- *   fp32/bf16 sum only differs from RING in rounding.  p in {2,4,8,16}.
+ * ONEPASS (= RECURSIVE_DOUBLING): all p inputs summed as the balanced
+ *   tree that recursive doubling builds when rank r exchanges with
+ *   r XOR 2^k at step k = 0, 1, ... ([A] 2.3): (x0+x1), (x2+x3), ... first.
+ *   Every rank gets the same bits.  p in {2,4,8,16}.
  * RING_LITERAL: the 2(p-1) neighbour steps of [A] 2.2 run one step per
  *   kernel launch through HBM, partials stored in the receive buffers.
- *   Bit-exact with RING.  fp32 and int32 only. */
+ *   Bit-exact with RING.  fp32 and int32 only.
+ * HALVING_DOUBLING: the order of [A] 2.3's halving-doubling, read as a
+ *   recursive-halving reduce-scatter pairing ranks at distance p/2, p/4,
+ *   ..., 1 followed by a recursive-doubling all-gather:
+ *   (x0 + x_{p/2}), (x1 + x_{p/2+1}), ... first.  p in {2,4,8,16}.
+ * Integer sums and min/max give the same bits under every schedule. */
 typedef enum {
   COLL_ALGO_RING = 0,
   COLL_ALGO_ONEPASS = 1,
-  COLL_ALGO_RING_LITERAL = 2
+  COLL_ALGO_RECURSIVE_DOUBLING = 1,
+  COLL_ALGO_RING_LITERAL = 2,
+  COLL_ALGO_HALVING_DOUBLING = 3
 } coll_algo_t;
 
 #define COLL_MAX_RANKS 64

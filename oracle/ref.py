@@ -12,7 +12,8 @@ definitions on the pages it follows:
   notation p, [n], elementwise + in {sum, min, max} (chapter preamble);
   primitive table (section 0); Broadcast 1.1, AllGather 1.2, Reduce 1.3
   with its worked example, AllReduce 1.4, ReduceScatter 1.5, AllToAll 1.6,
-  the forward/backward duality table 1.7; ring all-reduce 2.2.
+  the forward/backward duality table 1.7; ring all-reduce 2.2;
+  recursive doubling and halving-doubling 2.3.
 * "Collective Communication：AllReduce、AllGather、ReduceScatter 与 All-to-All"
   (charlestar.github.io): ragged All-to-All (counts c_ij, prefix-sum
   offsets), B convention for volumes, numerics of reduction order.
@@ -36,6 +37,9 @@ Readings taken where the pages are silent or inconsistent:
 6. Alltoallv: recv counts are the columns of the send-count matrix; the
    receive buffer of rank j holds the blocks from sources 0..p-1 in source
    order, packed.
+7. Halving-doubling: the page gives message sizes per step, not partner
+   distances; the reduce-scatter phase pairs ranks at distance p/2, then
+   p/4, ..., 1 (see halving_doubling_simulated).
 """
 from __future__ import annotations
 
@@ -263,6 +267,115 @@ def ring_allreduce_simulated(xs: list[np.ndarray], op: int, dtype: int,
     if dtype == BF16:
         return [f32_to_bf16_rne(b) for b in buf]
     return buf
+
+
+# ----------------------------------------------------------------------------
+# Recursive doubling and halving-doubling (section 2.3 of the hpc/04 page)
+# ----------------------------------------------------------------------------
+
+def _is_pow2(p: int) -> bool:
+    return p >= 1 and (p & (p - 1)) == 0
+
+
+def recursive_doubling_simulated(xs: list[np.ndarray], op: int, dtype: int) -> list[np.ndarray]:
+    """log2(p) steps; at step k every rank exchanges its whole vector with
+    the peer at distance 2^k (rank XOR 2^k) and both keep the combination.
+
+    The lower rank's partial is the left operand.  Partials stay in fp32 for
+    bf16 and are narrowed once at the end.  p must be a power of two.
+    """
+    p = len(xs)
+    assert _is_pow2(p)
+    buf = [_widen(x, dtype).copy() for x in xs]
+    d = 1
+    while d < p:
+        snap = [b.copy() for b in buf]
+        for r in range(p):
+            lo, hi = min(r, r ^ d), max(r, r ^ d)
+            buf[r] = _combine(snap[lo], snap[hi], op)
+        d *= 2
+    if dtype == BF16:
+        return [f32_to_bf16_rne(b) for b in buf]
+    return buf
+
+
+def halving_doubling_simulated(xs: list[np.ndarray], op: int, dtype: int) -> list[np.ndarray]:
+    """Reduce-scatter by recursive halving, then all-gather by recursive
+    doubling.
+
+    Reading of the page (it gives the message sizes, not the partner
+    distances): the halving phase pairs ranks at distance p/2, p/4, ..., 1
+    (Rabenseifner's order).  At each step a rank splits the range it holds
+    in two, keeps the lower half if its distance bit is 0 and the upper
+    half otherwise, and combines its partial of the kept half with the
+    peer's partial of the same half (lower rank's partial on the left).
+    After log2(p) steps rank r holds block r of the result; the doubling
+    phase copies the blocks back to every rank (distances 1, 2, ..., p/2).
+    Blocks are q = ceil(n/p) elements; p must be a power of two.
+    """
+    p = len(xs)
+    assert _is_pow2(p)
+    n = len(xs[0])
+    q = chunk_len(n, p)
+    buf = [_widen(x, dtype).copy() for x in xs]
+    blk = [(0, p) for _ in range(p)]          # block range [b0, b1) each rank holds
+    d = p // 2
+    while d >= 1:
+        snap = [b.copy() for b in buf]
+        new_blk = []
+        for r in range(p):
+            b0, b1 = blk[r]
+            mid = (b0 + b1) // 2
+            keep = (b0, mid) if (r & d) == 0 else (mid, b1)
+            sl = slice(min(keep[0] * q, n), min(keep[1] * q, n))
+            lo, hi = min(r, r ^ d), max(r, r ^ d)
+            buf[r][sl] = _combine(snap[lo][sl], snap[hi][sl], op)
+            new_blk.append(keep)
+        blk = new_blk
+        d //= 2
+    assert all(blk[r] == (r, r + 1) for r in range(p))
+    d = 1
+    while d < p:
+        snap = [b.copy() for b in buf]
+        new_blk = []
+        for r in range(p):
+            (a0, a1), (c0, c1) = blk[r], blk[r ^ d]
+            sl = slice(min(c0 * q, n), min(c1 * q, n))
+            buf[r][sl] = snap[r ^ d][sl]
+            new_blk.append((min(a0, c0), max(a1, c1)))
+        blk = new_blk
+        d *= 2
+    if dtype == BF16:
+        return [f32_to_bf16_rne(b) for b in buf]
+    return buf
+
+
+def fold_tree(vals: list[np.ndarray], op: int, dtype: int, first_stride: str) -> np.ndarray:
+    """Balanced pairwise tree over ranks 0..p-1 (p a power of two).
+
+    first_stride "low": pairs (0,1), (2,3), ... first, then pairs of pairs
+    (the recursive-doubling order); "high": pairs (k, k + p/2) first, then
+    (k, k + p/4), ... (the halving-doubling order).  Operands are the
+    values of ranks in rank order (not rotated); narrowed once for bf16.
+    """
+    p = len(vals)
+    assert _is_pow2(p)
+    a = [_widen(v, dtype).copy() for v in vals]
+    if first_stride == "low":
+        s = 1
+        while s < p:
+            for k in range(0, p, 2 * s):
+                a[k] = _combine(a[k], a[k + s], op)
+            s *= 2
+    else:
+        s = p // 2
+        while s >= 1:
+            for k in range(s):
+                a[k] = _combine(a[k], a[k + s], op)
+            s //= 2
+    if dtype == BF16:
+        return f32_to_bf16_rne(a[0])
+    return a[0]
 
 
 # ----------------------------------------------------------------------------

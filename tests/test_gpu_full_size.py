@@ -80,8 +80,10 @@ def test_zero_rs_ag_full_size(env):
 
 
 def test_dp_allreduce_full_size(env):
-    """AllReduce sum, p=8, 2^26 fp32 per rank ~ N(0,1): fused ring (bit-exact),
-    one-pass tree (1e-5 * sum|x|), literal 14-step ring (bit-exact)."""
+    """AllReduce sum, p=8, 2^26 fp32 per rank ~ N(0,1): fused ring, recursive
+    doubling, halving-doubling and the literal 14-step ring, each bit-exact
+    against the oracle's order for that schedule; the recursive-doubling
+    result is also held to 1e-5 * sum|x| of the ring order."""
     torch, coll = env
     p, n = 8, 1 << 26
     hx = inputs.rank_buffers(inputs.WL_DP_RING_AR, p, n, inputs.F32, dist="normal")
@@ -93,7 +95,11 @@ def test_dp_allreduce_full_size(env):
     cols = stacked[:, j]
     expect = ref.reduce_elements(cols, ref.chunk_of(j, n, p), ref.SUM, ref.F32)
     abs_sum = np.sum(np.abs(cols.astype(np.float64)), axis=0)
-    for algo in (coll.COLL_ALGO_RING, coll.COLL_ALGO_ONEPASS, coll.COLL_ALGO_RING_LITERAL):
+    per_rank = [cols[r] for r in range(p)]
+    trees = {coll.COLL_ALGO_RECURSIVE_DOUBLING: ref.fold_tree(per_rank, ref.SUM, ref.F32, "low"),
+             coll.COLL_ALGO_HALVING_DOUBLING: ref.fold_tree(per_rank, ref.SUM, ref.F32, "high")}
+    for algo in (coll.COLL_ALGO_RING, coll.COLL_ALGO_RECURSIVE_DOUBLING, coll.COLL_ALGO_HALVING_DOUBLING,
+                 coll.COLL_ALGO_RING_LITERAL):
         for t in recv:
             t.fill_(float("nan"))
         coll.coll_allreduce_algo(send, recv, algo, coll.COLL_SUM)
@@ -101,10 +107,9 @@ def test_dp_allreduce_full_size(env):
         for r in range(1, p):
             assert torch.equal(recv[r].view(torch.int32), recv[0].view(torch.int32)), f"algo {algo}: rank {r} differs"
         got = gather_host(torch, recv[0], j, F32)
-        if algo == coll.COLL_ALGO_ONEPASS:
-            assert_fp32_close(got, expect, abs_sum, 1e-5, "one-pass full size")
-        else:
-            assert_bits_equal(got, expect, f"algo {algo} full size")
+        assert_bits_equal(got, trees.get(algo, expect), f"algo {algo} full size")
+        if algo == coll.COLL_ALGO_RECURSIVE_DOUBLING:
+            assert_fp32_close(got, expect, abs_sum, 1e-5, "recursive doubling vs ring order")
 
 
 def test_small_allreduce_full_size(env):

@@ -2,9 +2,9 @@
 
 Sizes span several tiles plus ragged tails; edge cases cover n = 0,
 n < p, p = 1, misaligned buffers, in-place forms and the error paths.
-Bit-exact where the summation order is fixed (ring order, integers,
-min/max, copies); the one-pass tree variant is held to 1e-5 * sum|x| for
-fp32 and 1 ulp for bf16.
+Bit-exact everywhere: every schedule's summation order is reproduced by
+the oracle (ring order, recursive doubling and halving-doubling trees),
+and integers, min/max and copies are order independent.
 """
 import numpy as np
 import pytest
@@ -144,33 +144,41 @@ def test_allreduce_ring_literal_in_place(coll):
 
 @pytest.mark.parametrize("p", [2, 4, 8, 16])
 @pytest.mark.parametrize("dtype", DTYPES)
-def test_allreduce_onepass(coll, p, dtype):
+@pytest.mark.parametrize("algo,sim", [("RECURSIVE_DOUBLING", "recursive_doubling_simulated"),
+                                      ("HALVING_DOUBLING", "halving_doubling_simulated")])
+def test_allreduce_doubling_schedules_bitexact(coll, p, dtype, algo, sim):
+    """The tree schedules against step-by-step simulations of recursive
+    doubling and halving-doubling, bit for bit, on every rank."""
     n = p * 3000 + 11
     hx = gen(p, n, dtype, 6)
     send = [to_dev(x, dtype) for x in hx]
     for op in OPS:
-        recv = [empty(n, dtype) for _ in range(p)]
-        coll.coll_allreduce_algo(send, recv, coll.COLL_ALGO_ONEPASS, op)
+        recv = [empty(n, dtype, fill=0x3C3C3C3C) for _ in range(p)]
+        coll.coll_allreduce_algo(send, recv, getattr(coll, "COLL_ALGO_" + algo), op)
         sync()
-        expect = ref.allreduce(hx, op, dtype)
-        got = [to_host(t, dtype) for t in recv]
+        expect = getattr(ref, sim)(hx, op, dtype)
         for r in range(p):
-            assert_bits_equal(got[r], got[0], "one-pass ranks agree")
-        if op != ref.SUM or dtype == I32:
-            assert_bits_equal(got[0], expect[0], "one-pass exact ops")
-        elif dtype == F32:
-            abs_sum = np.sum(np.abs(np.stack(hx).astype(np.float64)), axis=0)
-            assert_fp32_close(got[0], expect[0], abs_sum, 1e-5, "one-pass fp32")
-        else:
-            assert_bf16_within_ulp(got[0], expect[0], 1, "one-pass bf16")
+            assert_bits_equal(to_host(recv[r], dtype), expect[r], f"{algo} p={p} dt={dtype} op={op} r={r}")
+
+
+def test_doubling_schedules_misaligned_and_in_place(coll):
+    p, n = 8, 5003
+    hx = gen(p, n, F32, 60)
+    keep, send = zip(*[upload_offset(x, F32, 1) for x in hx])
+    coll.coll_allreduce_algo(list(send), list(send), coll.COLL_ALGO_HALVING_DOUBLING, coll.COLL_SUM)
+    sync()
+    expect = ref.halving_doubling_simulated(hx, ref.SUM, F32)
+    for r in range(p):
+        assert_bits_equal(to_host(send[r], F32), expect[r], f"HD in place misaligned r={r}")
 
 
 def test_onepass_unsupported_rank_count(coll):
     send = [empty(10, F32) for _ in range(3)]
     recv = [empty(10, F32) for _ in range(3)]
-    with pytest.raises(coll.CollError) as e:
-        coll.coll_allreduce_algo(send, recv, coll.COLL_ALGO_ONEPASS, coll.COLL_SUM)
-    assert e.value.status == coll.COLL_ERR_UNSUPPORTED
+    for algo in (coll.COLL_ALGO_ONEPASS, coll.COLL_ALGO_HALVING_DOUBLING):
+        with pytest.raises(coll.CollError) as e:
+            coll.coll_allreduce_algo(send, recv, algo, coll.COLL_SUM)
+        assert e.value.status == coll.COLL_ERR_UNSUPPORTED
     with pytest.raises(coll.CollError) as e:
         s = [empty(10, BF16) for _ in range(3)]
         r = [empty(10, BF16) for _ in range(3)]

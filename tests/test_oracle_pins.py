@@ -473,3 +473,101 @@ def test_input_recipes():
     assert all(c.src_off % 64 == 0 and c.dst_off % 64 == 0 for c in calls)
     assert [c.op for c in calls[:6]] == [0, 1, 2, 0, 1, 2]
     assert [c.dtype for c in calls[:6]] == [0, 0, 0, 2, 2, 2]
+
+
+# ----------------------------------------------------------------------------
+# Recursive doubling and halving-doubling (hpc/04 section 2.3)
+# ----------------------------------------------------------------------------
+
+def _py_tree(vals, first_stride, dtype):
+    """Pure-Python pairwise tree with struct-rounded fp32 adds."""
+    a = list(vals)
+    p = len(a)
+    if first_stride == "low":
+        s = 1
+        while s < p:
+            for k in range(0, p, 2 * s):
+                a[k] = _py_add_f32(a[k], a[k + s])
+            s *= 2
+    else:
+        s = p // 2
+        while s >= 1:
+            for k in range(s):
+                a[k] = _py_add_f32(a[k], a[k + s])
+            s //= 2
+    return _py_bf16_rne(a[0]) if dtype == ref.BF16 else a[0]
+
+
+@pytest.mark.parametrize("dtype", [ref.F32, ref.BF16])
+@pytest.mark.parametrize("p", [1, 2, 4, 8, 16])
+def test_doubling_schedules_simulated_equal_their_trees(dtype, p):
+    """The step-by-step simulations give, on every rank, the balanced tree of
+    their pairing order, checked element by element against a pure-Python
+    tree with struct-rounded fp32 additions."""
+    rng = np.random.default_rng(77 + p)
+    for n in (1, p - 1 if p > 1 else 1, 3 * p + 1, 37):
+        xs = [(rng.standard_normal(n) * 10.0 ** rng.integers(-2, 3)).astype(np.float32) for _ in range(p)]
+        if dtype == ref.BF16:
+            xs = [(x.view(np.uint32) >> 16).astype(np.uint16) for x in xs]
+        widened = [_to_float(x, dtype) for x in xs]
+        for sim, stride in ((ref.recursive_doubling_simulated, "low"), (ref.halving_doubling_simulated, "high")):
+            outs = sim(xs, ref.SUM, dtype)
+            tree = ref.fold_tree(xs, ref.SUM, dtype, stride)
+            for r in range(p):
+                assert np.array_equal(_bits(outs[r]), _bits(tree)), (sim.__name__, p, n, r)
+            got = _to_float(tree, dtype)
+            for i in range(n):
+                assert got[i] == _py_tree([float(w[i]) for w in widened], stride, dtype), (stride, p, n, i)
+
+
+@pytest.mark.parametrize("p", [2, 4, 8])
+def test_doubling_schedules_exact_on_integers(p):
+    """Brute-force style: integer data (exact in every order) gives the plain
+    sum, min and max on every rank, for int32 and for small fp32 integers."""
+    rng = np.random.default_rng(p)
+    for n in (1, 5, 2 * p + 3):
+        ints = [rng.integers(-50, 51, n) for _ in range(p)]
+        for dtype in (ref.I32, ref.F32):
+            xs = [_as_dtype(v, dtype) for v in ints]
+            for op, fn in ((ref.SUM, np.sum), (ref.MIN, np.min), (ref.MAX, np.max)):
+                expect = fn(np.stack(ints), axis=0)
+                for sim in (ref.recursive_doubling_simulated, ref.halving_doubling_simulated):
+                    for out in sim(xs, op, dtype):
+                        assert list(_to_float(out, dtype)) == list(expect.astype(np.float64))
+
+
+def test_halving_doubling_leaves_block_r_on_rank_r():
+    """After the halving phase rank r owns block r (the reduce-scatter
+    placement of section 1.5); the simulator asserts it internally, and the
+    all-gather phase then gives every rank the full vector."""
+    p, n = 8, 8 * 5
+    xs = [np.full(n, float(r + 1), dtype=np.float32) for r in range(p)]
+    outs = ref.halving_doubling_simulated(xs, ref.SUM, ref.F32)
+    for o in outs:
+        assert np.all(o == sum(range(1, p + 1)))
+
+
+def test_doubling_orders_differ_from_ring_and_each_other():
+    """Guard: at p = 8 the three orders give different bits on this data,
+    so a kernel using the wrong one fails its parity test."""
+    rng = np.random.default_rng(9)
+    xs = [rng.standard_normal(4096).astype(np.float32) for _ in range(8)]
+    ring = ref.allreduce(xs, ref.SUM, ref.F32)[0]
+    rd = ref.fold_tree(xs, ref.SUM, ref.F32, "low")
+    hd = ref.fold_tree(xs, ref.SUM, ref.F32, "high")
+    assert not np.array_equal(_bits(ring), _bits(rd))
+    assert not np.array_equal(_bits(ring), _bits(hd))
+    assert not np.array_equal(_bits(rd), _bits(hd))
+
+
+@pytest.mark.parametrize("stride", ["low", "high"])
+def test_tree_orders_within_summation_bound(stride):
+    """A balanced tree over p = 16 values has depth 4: |tree - fsum| <= gamma_4 sum|x|."""
+    p, n = 16, 1024
+    xs = inputs.rank_buffers(inputs.WL_TEST, p, n, ref.F32, dist="normal", extra=(43, p))
+    got = ref.fold_tree(xs, ref.SUM, ref.F32, stride).astype(np.float64)
+    u = 2.0 ** -24
+    gamma = 4 * u / (1 - 4 * u)
+    for i in range(0, n, 5):
+        vals = [float(x[i]) for x in xs]
+        assert abs(got[i] - math.fsum(vals)) <= gamma * sum(abs(v) for v in vals) + 1e-45
