@@ -17,10 +17,11 @@ the part of the network.  The JSON line reports
   the HBM traffic read from rocprofv3 FETCH_SIZE / WRITE_SIZE counters
   when a counter summary for the current kernel sources is on file;
 * cpu_baseline: the CPU oracle on a bounded slice of the same workload;
-* collectives: the other p = 8 collectives (AllReduce three ways,
-  All-to-All, Alltoallv), the small AllReduce at p = 4, the 10,000-call
-  batched AllReduce at p = 16 and the box's copy ceiling, each timed
-  with HIP events.
+* collectives: the other p = 8 collectives (AllReduce in four
+  schedules, All-to-All, Alltoallv, Gather, Scatter), the small
+  AllReduce at p = 4, the 10,000-call batched AllReduce at p = 16 (also
+  as individual calls, with latency percentiles and an alpha-beta fit)
+  and the box's copy ceiling, each timed with HIP events.
 
 Only one GPU is used; --gpus above 1 is refused.
 """
@@ -55,8 +56,8 @@ def parse_args(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-collectives", action="store_true", help="time only the main step")
     ap.add_argument("--only", default=None,
-                    help="comma list of extra collectives to time (ar_ring, ar_onepass, ar_literal, "
-                         "a2a, a2av, ar_small, batch, copy)")
+                    help="comma list of extra collectives to time (ar_ring, ar_onepass, ar_hd, "
+                         "ar_literal, a2a, a2av, gs, ar_small, batch, copy)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
     return ap.parse_args(argv)
 
@@ -233,14 +234,15 @@ def extra_collectives(torch, coll, inputs, metrics, dev, which, iters=10, warmup
     want = lambda k: which is None or k in which  # noqa: E731
 
     # --- DP gradient AllReduce, p = 8, 256 MiB fp32 per rank ~ N(0, 1) -------
-    if want("ar_ring") or want("ar_onepass") or want("ar_literal"):
+    if want("ar_ring") or want("ar_onepass") or want("ar_hd") or want("ar_literal"):
         p, n = 8, 1 << 26
         send = [to_dev(torch, x, dev) for x in inputs.rank_buffers(inputs.WL_DP_RING_AR, p, n, inputs.F32,
                                                                     dist="normal")]
         recv = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(p)]
         for key, algo, label, aname in (
                 ("ar_ring", coll.COLL_ALGO_RING, "allreduce_ring_fused", "ring"),
-                ("ar_onepass", coll.COLL_ALGO_ONEPASS, "allreduce_onepass_tree", "ring"),
+                ("ar_onepass", coll.COLL_ALGO_RECURSIVE_DOUBLING, "allreduce_recursive_doubling_order", "ring"),
+                ("ar_hd", coll.COLL_ALGO_HALVING_DOUBLING, "allreduce_halving_doubling_order", "ring"),
                 ("ar_literal", coll.COLL_ALGO_RING_LITERAL, "allreduce_ring_literal_14_steps",
                  "ring_literal")):
             if not want(key):
@@ -291,6 +293,22 @@ def extra_collectives(torch, coll, inputs, metrics, dev, which, iters=10, warmup
             })
             del recv, cdev
         del send
+        torch.cuda.empty_cache()
+
+    # --- Gather / Scatter, p = 8, 2^23 bf16 per rank (root buffer 128 MiB) ----
+    if want("gs"):
+        p, n = 8, 1 << 23
+        ranks = [torch.empty(n, dtype=torch.bfloat16, device=dev).normal_() for _ in range(p)]
+        root_buf = torch.empty(p * n, dtype=torch.bfloat16, device=dev)
+        fg = coll.coll_gather(ranks, root_buf, 0, defer=True)
+        fs = coll.coll_scatter(root_buf, ranks, 0, defer=True)
+        tg, ts = time_launches(torch, [fg, fs], iters, warmup)
+        for name, kind, ms in (("gather", "gather", tg), ("scatter", "scatter", ts)):
+            med, p95, _ = stats_us(ms)
+            rows.append(coll_entry(metrics, name, kind, p, n, 2, med, "ring",
+                                   {"dtype": "bf16", "t_p95_us": round(p95, 2), "root": 0,
+                                    "workload": "p=8, 2^23 bf16 per rank, 128 MiB root buffer"}))
+        del ranks, root_buf
         torch.cuda.empty_cache()
 
     # --- small AllReduce, p = 4, 2^20 per rank (Infinity-Cache resident) ------

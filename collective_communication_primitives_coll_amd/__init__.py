@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
         "coll_allgather": [pp, pp, i32, sz, i32, vp],
         "coll_alltoall": [pp, pp, i32, sz, i32, vp],
         "coll_alltoallv": [pp, pp, i32, vp, i64p, i64p, vp, i32, vp],
+        "coll_gather": [pp, vp, i32, sz, i32, i32, vp],
+        "coll_scatter": [vp, pp, i32, sz, i32, i32, vp],
         "coll_allreduce_batch": [ctypes.POINTER(coll_call_t), i32, i32, ctypes.c_uint, vp],
     }
     for name, args in sig.items():
@@ -272,6 +274,34 @@ def coll_alltoall(send, recv, n_block: int | None = None, dtype: int | None = No
     r, k2 = _ptr_array(recv)
     return _run("coll_alltoall", (s, r, p, int(n_block), dt, _stream(stream)), "coll_alltoall", defer,
                 (k1, k2))
+
+
+def coll_gather(send, recv_root, root: int, n: int | None = None, dtype: int | None = None, stream=None,
+                defer: bool = False):
+    """n = elements each rank sends; recv_root holds p*n."""
+    p = len(send)
+    dt = _dtype_of(send[0], dtype)
+    n = _numel(send[0], n)
+    _same_dtype([*send, recv_root], dt)
+    _check_sizes(send, n, "gather send")
+    _check_sizes([recv_root], p * n, "gather recv")
+    s, k = _ptr_array(send)
+    return _run("coll_gather", (s, _addr(recv_root), p, n, dt, int(root), _stream(stream)),
+                "coll_gather", defer, (k,))
+
+
+def coll_scatter(send_root, recv, root: int, n: int | None = None, dtype: int | None = None, stream=None,
+                 defer: bool = False):
+    """n = elements each rank receives; send_root holds p*n."""
+    p = len(recv)
+    dt = _dtype_of(send_root, dtype)
+    n = _numel(recv[0], n)
+    _same_dtype([send_root, *recv], dt)
+    _check_sizes([send_root], p * n, "scatter send")
+    _check_sizes(recv, n, "scatter recv")
+    r, k = _ptr_array(recv)
+    return _run("coll_scatter", (_addr(send_root), r, p, n, dt, int(root), _stream(stream)),
+                "coll_scatter", defer, (k,))
 
 
 def coll_alltoallv(send, recv, counts_dev, send_cap: Sequence[int] | None = None,

@@ -376,6 +376,59 @@ COLL_EXPORT coll_status_t coll_alltoall(const void* const* send, void* const* re
   return finish(coll::launch_copy((int)dsize(dtype), P, g, grid, stream));
 }
 
+COLL_EXPORT coll_status_t coll_gather(const void* const* send, void* recv_root, int p, size_t n,
+                                      coll_dtype_t dtype, int root, void* stream) {
+  if (p < 1 || p > kMaxRanks || !dtype_ok(dtype) || root < 0 || root >= p) return COLL_ERR_INVALID_ARG;
+  if (n == 0) return COLL_OK;
+  size_t bytes;
+  if (!mul_ok(n, dsize(dtype), (size_t)p, &bytes)) return COLL_ERR_INVALID_ARG;
+  if (!all_non_null(send, p) || !recv_root) return COLL_ERR_INVALID_ARG;
+  if (!elem_aligned(send, p, dsize(dtype)) || !elem_aligned1(recv_root, dsize(dtype))) return COLL_ERR_INVALID_ARG;
+  const size_t nb = n * dsize(dtype);
+  std::vector<Range> rs;
+  for (int r = 0; r < p; ++r) rs.push_back(rng(send[r], nb, false, r));
+  rs.push_back(rng(recv_root, nb * p, true, root));
+  coll_status_t st = check_alias(rs, [nb](const Range& o, const Range& x) {
+    // send[root] == recv_root + root*n elements (the root's own block)
+    return !x.out && x.rank == o.rank && x.b == o.b + (uintptr_t)o.rank * nb;
+  });
+  if (st != COLL_OK) return st;
+  int grid;
+  int e = max_grid(&grid, kFamCopy);
+  if (e) return hip_fail(e);
+  void* dst[1] = {recv_root};
+  coll::RankPtrs P = make_ptrs(send, p, dst, 1);
+  coll::CopyGeom g{n, p, coll::kCopyGather, common_mis(send, p), (int)((uintptr_t)recv_root & 15)};
+  return finish(coll::launch_copy((int)dsize(dtype), P, g, grid, stream));
+}
+
+COLL_EXPORT coll_status_t coll_scatter(const void* send_root, void* const* recv, int p, size_t n,
+                                       coll_dtype_t dtype, int root, void* stream) {
+  if (p < 1 || p > kMaxRanks || !dtype_ok(dtype) || root < 0 || root >= p) return COLL_ERR_INVALID_ARG;
+  if (n == 0) return COLL_OK;
+  size_t bytes;
+  if (!mul_ok(n, dsize(dtype), (size_t)p, &bytes)) return COLL_ERR_INVALID_ARG;
+  if (!send_root || !all_non_null(recv, p)) return COLL_ERR_INVALID_ARG;
+  if (!elem_aligned1(send_root, dsize(dtype)) || !elem_aligned(recv, p, dsize(dtype))) return COLL_ERR_INVALID_ARG;
+  const size_t nb = n * dsize(dtype);
+  std::vector<Range> rs;
+  rs.push_back(rng(send_root, nb * p, false, root));
+  for (int r = 0; r < p; ++r) rs.push_back(rng(recv[r], nb, true, r));
+  coll_status_t st = check_alias(rs, [nb](const Range& o, const Range& x) {
+    // recv[root] == send_root + root*n elements (the root's own block)
+    return !x.out && x.rank == o.rank && o.b == x.b + (uintptr_t)o.rank * nb;
+  });
+  if (st != COLL_OK) return st;
+  int grid;
+  int e = max_grid(&grid, kFamCopy);
+  if (e) return hip_fail(e);
+  const void* src[1] = {send_root};
+  coll::RankPtrs P = make_ptrs(src, 1, recv, p);
+  coll::CopyGeom g{n, p, coll::kCopyScatter, (int)((uintptr_t)send_root & 15),
+                   common_mis((const void* const*)recv, p)};
+  return finish(coll::launch_copy((int)dsize(dtype), P, g, grid, stream));
+}
+
 COLL_EXPORT coll_status_t coll_alltoallv(const void* const* send, void* const* recv, int p,
                                          const int64_t* counts_dev, const int64_t* send_cap,
                                          const int64_t* recv_cap, int32_t* status_dev, coll_dtype_t dtype,

@@ -1,7 +1,7 @@
-// Data re-placement without arithmetic: AllGather, Broadcast, All-to-All
-// and variable-split All-to-All.
+// Data re-placement without arithmetic: AllGather, Broadcast, All-to-All,
+// variable-split All-to-All, Gather and Scatter.
 //
-// All four are block copies between rank buffers; they differ only in how
+// All six are block copies between rank buffers; they differ only in how
 // a segment (source range -> destination range(s)) is derived:
 //   AllGather  segment s: send[s] -> recv[r] + s*n for every r, rank-order
 //              concatenation ("集合通信：原语、算法、NCCL 实现与拓扑映射",
@@ -9,6 +9,8 @@
 //   Broadcast  one segment: send_root -> recv[r] for every r (section 1.1);
 //   AllToAll   segment (i,j): send[i] + j*n -> recv[j] + i*n, the block
 //              transpose of section 1.6;
+//   Gather     segment s: send[s] -> recv_root + s*n;
+//   Scatter    segment r: send_root + r*n -> recv[r];
 //   Alltoallv  segment (i,j) of counts[i][j] elements, offsets from the
 //              prefix sums of the count matrix ("Collective Communication：
 //              AllReduce、AllGather、ReduceScatter 与 All-to-All", ragged
@@ -45,21 +47,40 @@ COLL_STREAM_KERNEL void fanout_kernel(RankPtrs ptrs, CopyGeom g) {
   }
 }
 
-// Equal-split All-to-All: p*p segments, one destination each.
-template <int B>
-COLL_STREAM_KERNEL void alltoall_kernel(RankPtrs ptrs, CopyGeom g) {
+// 1:1 block copies, one destination per segment:
+//   All-to-All  p*p segments (i, j): send[i] + j*n -> recv[j] + i*n;
+//   Gather      p segments s: send[s] -> recv_root + s*n (AllGather with one
+//               receiver, "详解分布式训练8大集合通信原语" section 4.3);
+//   Scatter     p segments r: send_root + r*n -> recv[r] (section 3.3).
+// The in-place forms copy the root's own block onto itself.
+template <int B, int KIND>
+COLL_STREAM_KERNEL void pair_copy_kernel(RankPtrs ptrs, CopyGeom g) {
   using W = typename Word<B>::T;
   const int p = g.p;
+  const int nseg = KIND == kCopyAllToAll ? p * p : p;
   uint64_t base = 0;
-  for (int i = 0; i < p; ++i) {
-    for (int j = 0; j < p; ++j) {
-      const uint64_t src_off = (uint64_t)j * g.n, dst_off = (uint64_t)i * g.n;
-      const W* src = (const W*)ptrs.src[i] + src_off;
-      W* dst = (W*)ptrs.dst[j] + dst_off;
-      const int mis = seg_mis(g.src_mis, g.dst_mis, src_off * B, dst_off * B);
-      auto gdst = [&](int) -> W* { return dst; };
-      base += copy_segment<B, true, 1>(src, gdst, 1, g.n, mis, base);
+  for (int sgi = 0; sgi < nseg; ++sgi) {
+    uint64_t src_off = 0, dst_off = 0;
+    const W* src;
+    W* dst;
+    if constexpr (KIND == kCopyAllToAll) {
+      const int i = sgi / p, j = sgi - (sgi / p) * p;
+      src_off = (uint64_t)j * g.n;
+      dst_off = (uint64_t)i * g.n;
+      src = (const W*)ptrs.src[i] + src_off;
+      dst = (W*)ptrs.dst[j] + dst_off;
+    } else if constexpr (KIND == kCopyGather) {
+      dst_off = (uint64_t)sgi * g.n;
+      src = (const W*)ptrs.src[sgi];
+      dst = (W*)ptrs.dst[0] + dst_off;
+    } else {
+      src_off = (uint64_t)sgi * g.n;
+      src = (const W*)ptrs.src[0] + src_off;
+      dst = (W*)ptrs.dst[sgi];
     }
+    const int mis = seg_mis(g.src_mis, g.dst_mis, src_off * B, dst_off * B);
+    auto gdst = [&](int) -> W* { return dst; };
+    base += copy_segment<B, true, 1>(src, gdst, 1, g.n, mis, base);
   }
 }
 
@@ -152,12 +173,16 @@ static void launch_fanout(int p, int grid, const RankPtrs& ptrs, const CopyGeom&
 
 template <int B>
 static int launch_copy_b(const RankPtrs& ptrs, const CopyGeom& g, int max_grid, hipStream_t s) {
-  const uint64_t nseg = g.kind == kCopyAllGather ? g.p : (g.kind == kCopyBroadcast ? 1 : (uint64_t)g.p * g.p);
+  const uint64_t nseg = g.kind == kCopyBroadcast ? 1 : (g.kind == kCopyAllToAll ? (uint64_t)g.p * g.p : g.p);
   const uint64_t te = kCopyTV * (16 / B);
   const int grid = clamp_grid(nseg * ((g.n + te - 1) / te + 1), max_grid);
   if (!grid) return 0;
   if (g.kind == kCopyAllToAll)
-    hipLaunchKernelGGL((alltoall_kernel<B>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
+    hipLaunchKernelGGL((pair_copy_kernel<B, kCopyAllToAll>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
+  else if (g.kind == kCopyGather)
+    hipLaunchKernelGGL((pair_copy_kernel<B, kCopyGather>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
+  else if (g.kind == kCopyScatter)
+    hipLaunchKernelGGL((pair_copy_kernel<B, kCopyScatter>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
   else if (g.kind == kCopyAllGather)
     launch_fanout<B, kCopyAllGather>(g.p, grid, ptrs, g, s);
   else

@@ -48,7 +48,9 @@ struct ReduceGeom {
 enum CopyKind : int {
   kCopyAllGather = 0,  // segment s: src[s] -> dst[r] + s*n, every r
   kCopyBroadcast = 1,  // one segment: src[0] -> dst[r], every r
-  kCopyAllToAll = 2    // segment (i,j): src[i] + j*n -> dst[j] + i*n
+  kCopyAllToAll = 2,   // segment (i,j): src[i] + j*n -> dst[j] + i*n
+  kCopyGather = 3,     // segment s: src[s] -> dst[0] + s*n (root buffer)
+  kCopyScatter = 4     // segment r: src[0] + r*n -> dst[r]
 };
 
 struct CopyGeom {

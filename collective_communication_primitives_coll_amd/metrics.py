@@ -27,6 +27,10 @@ def busbw_factor(coll: str, p: int) -> float:
         return (p - 1) / p
     if coll in ("broadcast", "reduce"):
         return 1.0
+    if coll in ("gather", "scatter"):
+        # not in the section 2.5 table: of the root's p*n elements, the
+        # root's own block never crosses a link, so (p-1)/p of B moves
+        return (p - 1) / p
     raise ValueError(coll)
 
 
@@ -36,11 +40,12 @@ def payload_bytes(coll: str, p: int, n: int, d: int) -> int:
     reduce_scatter: recv n per rank (B = p*n*d, the full tensor);
     allgather: send n per rank (B = p*n*d);
     alltoall: n = block elements (B_local = p*n*d);
+    gather/scatter: n = elements per rank (B = p*n*d, the root's buffer);
     alltoallv: n = elements each rank sends on average (B_local = n*d).
     """
     if coll in ("allreduce", "reduce", "broadcast", "alltoallv"):
         return n * d
-    if coll in ("reduce_scatter", "allgather", "alltoall"):
+    if coll in ("reduce_scatter", "allgather", "alltoall", "gather", "scatter"):
         return p * n * d
     raise ValueError(coll)
 
@@ -65,6 +70,8 @@ def hbm_bytes(coll: str, p: int, n: int, d: int, algo: str = "ring") -> int:
     if coll == "alltoall":
         return 2 * p * p * n * d
     if coll == "alltoallv":
+        return 2 * p * n * d
+    if coll in ("gather", "scatter"):
         return 2 * p * n * d
     raise ValueError(coll)
 

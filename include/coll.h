@@ -13,6 +13,8 @@
  *       All-to-All" (charlestar.github.io): ragged All-to-All; CUDA-stream
  *       semantics ("API return is not completion"); in-place offset rules;
  *       failure semantics (a collective is not a transaction).
+ *   [C] "详解分布式训练8大集合通信原语：从Send/Recv到All2All"
+ *       (bjdmk.com.cn): Scatter (section 3.3), Gather (section 4.3).
  *
  * Common contract
  * ---------------
@@ -138,6 +140,20 @@ coll_status_t coll_allgather(const void* const* send, void* const* recv, int p, 
  * transpose of the p x p block matrix.  No in-place form. */
 coll_status_t coll_alltoall(const void* const* send, void* const* recv, int p, size_t n_block,
                             coll_dtype_t dtype, void* stream);
+
+/* Gather ([C] section 4.3; [A] note after 1.6): AllGather whose result
+ * only the root keeps.  send[s] holds n elements, recv_root holds p*n;
+ * recv_root[s*n + j] = send[s][j] (rank-order concatenation).  root in
+ * [0, p).  In place: send[root] == recv_root + root*n elements. */
+coll_status_t coll_gather(const void* const* send, void* recv_root, int p, size_t n,
+                          coll_dtype_t dtype, int root, void* stream);
+
+/* Scatter ([C] section 3.3; [A] note after 1.6): the root's p*n elements
+ * cut into p blocks of n, block r to rank r: recv[r][j] =
+ * send_root[r*n + j].  root in [0, p).  In place: recv[root] ==
+ * send_root + root*n elements. */
+coll_status_t coll_scatter(const void* send_root, void* const* recv, int p, size_t n,
+                           coll_dtype_t dtype, int root, void* stream);
 
 /* Variable-split All-to-All ([B] Ragged All-to-All).
  * counts_dev: DEVICE array of p*p int64, row-major, counts[i*p + j] =

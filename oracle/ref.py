@@ -12,11 +12,14 @@ definitions on the pages it follows:
   notation p, [n], elementwise + in {sum, min, max} (chapter preamble);
   primitive table (section 0); Broadcast 1.1, AllGather 1.2, Reduce 1.3
   with its worked example, AllReduce 1.4, ReduceScatter 1.5, AllToAll 1.6,
-  the forward/backward duality table 1.7; ring all-reduce 2.2;
+  the forward/backward duality table 1.7 and the Gather/Scatter note
+  after 1.6; ring all-reduce 2.2;
   recursive doubling and halving-doubling 2.3.
 * "Collective Communication：AllReduce、AllGather、ReduceScatter 与 All-to-All"
   (charlestar.github.io): ragged All-to-All (counts c_ij, prefix-sum
   offsets), B convention for volumes, numerics of reduction order.
+* "详解分布式训练8大集合通信原语：从Send/Recv到All2All" (bjdmk.com.cn):
+  Scatter (section 3.3) and Gather (section 4.3).
 
 Readings taken where the pages are silent or inconsistent:
 
@@ -188,6 +191,24 @@ def allgather(xs: list[np.ndarray]) -> list[np.ndarray]:
     """Every rank receives [x_0 | x_1 | ... | x_{p-1}] in rank order (section 1.2)."""
     cat = np.concatenate(xs)
     return [cat.copy() for _ in xs]
+
+
+def gather(xs: list[np.ndarray], root: int) -> np.ndarray:
+    """Only the root receives [x_0 | x_1 | ... | x_{p-1}] in rank order:
+    AllGather with a single receiver ("详解分布式训练8大集合通信原语" page,
+    section 4.3; the hpc/04 page's note after section 1.6)."""
+    assert 0 <= root < len(xs)
+    return np.concatenate(xs)
+
+
+def scatter(x_root: np.ndarray, p: int, root: int) -> list[np.ndarray]:
+    """The root's [p*n] is cut into p blocks of n; rank r receives block r
+    (the same page, section 3.3: every rank gets one slice of the whole)."""
+    assert 0 <= root < p
+    total = len(x_root)
+    assert total % p == 0
+    n = total // p
+    return [np.array(x_root[r * n:(r + 1) * n], copy=True) for r in range(p)]
 
 
 def alltoall(xs: list[np.ndarray]) -> list[np.ndarray]:

@@ -63,6 +63,8 @@ def test_zero_elements_is_ok_without_pointers():
     assert L.coll_broadcast(None, None, 4, 0, 2, 0, None) == coll.COLL_OK
     assert L.coll_reduce(None, None, 4, 0, 2, 1, 3, None) == coll.COLL_OK
     assert L.coll_allreduce_batch(None, 0, 4, 0, None) == coll.COLL_OK
+    assert L.coll_gather(None, None, 4, 0, 0, 1, None) == coll.COLL_OK
+    assert L.coll_scatter(None, None, 4, 0, 0, 1, None) == coll.COLL_OK
 
 
 @host_only
@@ -97,6 +99,12 @@ def test_invalid_arguments_rejected():
     assert L.coll_alltoallv(s, r, 4, base + 0x40000004, caps, caps, None, 0, None) == INV  # counts misaligned
     assert L.coll_allreduce_batch(None, 3, 4, 0, None) == INV
     assert L.coll_allreduce_batch(None, 0, 4, 8, None) == INV        # unknown flag
+    assert L.coll_gather(s, base + 0x20000000, 4, n, 0, 4, None) == INV     # root out of range
+    assert L.coll_gather(s, None, 4, n, 0, 0, None) == INV                  # null root buffer
+    assert L.coll_gather(s, base + 0x20000002, 4, n, 0, 0, None) == INV     # misaligned root buffer
+    assert L.coll_scatter(base, r, 4, n, 0, -1, None) == INV
+    assert L.coll_scatter(None, r, 4, n, 0, 0, None) == INV
+    assert L.coll_scatter(base, r, 4, n, 5, 0, None) == INV                 # bad dtype
 
 
 @host_only
@@ -140,4 +148,17 @@ def test_illegal_aliasing_rejected():
     caps = (ctypes.c_int64 * 4)(n, n, n, n)
     r, _k11 = _arr(recv)
     assert L.coll_alltoallv(s, r, p, recv[1] + 64, caps, caps, None, 0, None) == AL
+    # Gather: send[1] inside the root buffer, but the root is 2
+    root_buf = base + 0x30000000
+    sg2, _k12 = _arr([send[0], root_buf + 1 * nb, send[2], send[3]])
+    assert L.coll_gather(sg2, root_buf, p, n, 0, 2, None) == AL
+    # Gather: the root's own block in place is accepted
+    sg3, _k13 = _arr([send[0], send[1], root_buf + 2 * nb, send[3]])
+    assert L.coll_gather(sg3, root_buf, p, n, 0, 2, None) != AL
+    # Scatter: two outputs overlap
+    r, _k14 = _arr([recv[0], recv[0] + 4, recv[2], recv[3]])
+    assert L.coll_scatter(root_buf, r, p, n, 0, 0, None) == AL
+    # Scatter: recv[0] inside the root buffer while the root is 1
+    r, _k15 = _arr([root_buf, recv[1], recv[2], recv[3]])
+    assert L.coll_scatter(root_buf, r, p, n, 0, 1, None) == AL
     assert nb > 0

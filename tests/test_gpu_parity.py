@@ -312,6 +312,65 @@ def test_misaligned_rs_ag(coll, dtype):
 
 
 # ----------------------------------------------------------------------------
+# Gather and Scatter
+# ----------------------------------------------------------------------------
+
+GS_SHAPES = [(1, 7), (2, 1), (3, 1001), (4, 4096), (5, 33), (8, 8192 + 3), (16, 2050)]
+
+
+@pytest.mark.parametrize("p,n", GS_SHAPES)
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_gather_every_root(coll, p, n, dtype):
+    hx = gen(p, n, dtype, 70)
+    send = [to_dev(x, dtype) for x in hx]
+    for root in sorted({0, p // 2, p - 1}):
+        out = empty(p * n + 3, dtype, fill=0x7777)
+        coll.coll_gather(send, out[:p * n], root)
+        sync()
+        got = to_host(out, dtype)
+        assert_bits_equal(got[:p * n], ref.gather(hx, root), f"gather p={p} n={n} root={root}")
+        assert np.all(got[p * n:].view(np.uint16 if dtype == BF16 else np.uint32) ==
+                      (0x7777 if dtype == BF16 else 0x7777)), "gather wrote past the end"
+
+
+@pytest.mark.parametrize("p,n", GS_SHAPES)
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_scatter_every_root(coll, p, n, dtype):
+    whole = gen(1, p * n, dtype, 71)[0]
+    src = to_dev(whole, dtype)
+    for root in sorted({0, p // 2, p - 1}):
+        recv = [empty(n, dtype, fill=3) for _ in range(p)]
+        coll.coll_scatter(src, recv, root)
+        sync()
+        expect = ref.scatter(whole, p, root)
+        for r in range(p):
+            assert_bits_equal(to_host(recv[r], dtype), expect[r], f"scatter p={p} n={n} root={root} r={r}")
+
+
+def test_gather_scatter_in_place_and_misaligned(coll):
+    p, n, root = 8, 3001, 5
+    hx = gen(p, n, F32, 72)
+    buf = empty(p * n, F32, fill=0)
+    buf[root * n:(root + 1) * n].copy_(to_dev(hx[root], F32))
+    send = [to_dev(x, F32) for x in hx]
+    send[root] = buf[root * n:(root + 1) * n]          # in place: the root's own block
+    coll.coll_gather(send, buf, root)
+    sync()
+    assert_bits_equal(to_host(buf, F32), ref.gather(hx, root), "gather in place")
+    recv = [empty(n, F32, fill=0) for _ in range(p)]
+    recv[root] = buf[root * n:(root + 1) * n]          # scatter in place
+    coll.coll_scatter(buf, recv, root)
+    sync()
+    for r in range(p):
+        assert_bits_equal(to_host(recv[r], F32), hx[r], f"scatter in place r={r}")
+    ks, msend = zip(*[upload_offset(x, BF16, 3) for x in gen(p, n, BF16, 73)])
+    kb, mbuf = upload_offset(np.zeros(p * n, dtype=np.uint16), BF16, 1)
+    coll.coll_gather(list(msend), mbuf, 0)
+    sync()
+    assert_bits_equal(to_host(mbuf, BF16), ref.gather(gen(p, n, BF16, 73), 0), "gather misaligned")
+
+
+# ----------------------------------------------------------------------------
 # All-to-All and Alltoallv
 # ----------------------------------------------------------------------------
 

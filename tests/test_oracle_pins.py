@@ -571,3 +571,56 @@ def test_tree_orders_within_summation_bound(stride):
     for i in range(0, n, 5):
         vals = [float(x[i]) for x in xs]
         assert abs(got[i] - math.fsum(vals)) <= gamma * sum(abs(v) for v in vals) + 1e-45
+
+
+# ----------------------------------------------------------------------------
+# Gather and Scatter (single-root forms of AllGather and Broadcast)
+# ----------------------------------------------------------------------------
+
+def test_gather_scatter_symbolic():
+    rows = read_golden("gather_scatter_symbolic.txt")
+    gin = {int(r[1]): r[2:] for r in rows if r[0] == "gather_in"}
+    gout = [r for r in rows if r[0] == "gather_out"][0]
+    p = len(gin)
+    root = int(gout[1])
+    # symbols -> integer codes so the oracle runs on arrays
+    sym = sorted({v for vs in gin.values() for v in vs})
+    code = {v: i for i, v in enumerate(sym)}
+    xs = [np.array([code[v] for v in gin[r]], dtype=np.int32) for r in range(p)]
+    got = ref.gather(xs, root)
+    assert [sym[i] for i in got] == gout[2:]
+    sin = [r for r in rows if r[0] == "scatter_in"][0]
+    sroot, svals = int(sin[1]), sin[2:]
+    scode = {v: i for i, v in enumerate(svals)}
+    outs = ref.scatter(np.array([scode[v] for v in svals], dtype=np.int32), p, sroot)
+    for r in rows:
+        if r[0] == "scatter_out":
+            assert [svals[i] for i in outs[int(r[1])]] == r[2:]
+
+
+def test_gather_is_allgather_at_root_and_scatter_inverts_it():
+    rng = np.random.default_rng(31)
+    for p in (1, 2, 5, 8):
+        n = int(rng.integers(1, 9))
+        xs = [rng.integers(-100, 100, n).astype(np.int32) for _ in range(p)]
+        for root in range(p):
+            g = ref.gather(xs, root)
+            assert np.array_equal(g, ref.allgather(xs)[root])
+            back = ref.scatter(g, p, root)
+            assert all(np.array_equal(a, b) for a, b in zip(back, xs))
+            whole = rng.integers(-100, 100, p * n).astype(np.int32)
+            assert np.array_equal(ref.gather(ref.scatter(whole, p, root), root), whole)
+
+
+def test_gather_scatter_adjoint():
+    """<Gather(x), y> = <x, Scatter(y)>: one copy map is the other's transpose
+    (the duality of the hpc/04 page's section 1.7 applied to the single-root
+    pair), exact in int64."""
+    rng = np.random.default_rng(32)
+    for p in (2, 3, 8):
+        n = 5
+        xs = [rng.integers(-1000, 1000, n).astype(np.int64) for _ in range(p)]
+        y = rng.integers(-1000, 1000, p * n).astype(np.int64)
+        lhs = int(np.dot(ref.gather(xs, 0), y))
+        rhs = sum(int(np.dot(x, s)) for x, s in zip(xs, ref.scatter(y, p, 0)))
+        assert lhs == rhs
