@@ -18,7 +18,8 @@ the part of the network.  The JSON line reports
   when a counter summary for the current kernel sources is on file;
 * cpu_baseline: the CPU oracle on a bounded slice of the same workload;
 * collectives: the other p = 8 collectives (AllReduce in four
-  schedules, All-to-All, Alltoallv, Gather, Scatter), the small
+  schedules, All-to-All, Alltoallv, the MoE pack -> exchange -> reverse
+  exchange -> combine path, Gather, Scatter), the small
   AllReduce at p = 4, the 10,000-call batched AllReduce at p = 16 (also
   as individual calls, with latency percentiles and an alpha-beta fit)
   and the box's copy ceiling, each timed with HIP events.
@@ -57,7 +58,7 @@ def parse_args(argv=None):
     ap.add_argument("--no-collectives", action="store_true", help="time only the main step")
     ap.add_argument("--only", default=None,
                     help="comma list of extra collectives to time (ar_ring, ar_onepass, ar_hd, "
-                         "ar_literal, a2a, a2av, gs, ar_small, batch, copy)")
+                         "ar_literal, a2a, a2av, moe, gs, ar_small, batch, copy)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
     return ap.parse_args(argv)
 
@@ -295,6 +296,10 @@ def extra_collectives(torch, coll, inputs, metrics, dev, which, iters=10, warmup
         del send
         torch.cuda.empty_cache()
 
+    # --- MoE dispatch and combine around the ragged exchange -----------------
+    if want("moe"):
+        rows.append(moe_row(torch, coll, inputs, dev, iters, warmup))
+
     # --- Gather / Scatter, p = 8, 2^23 bf16 per rank (root buffer 128 MiB) ----
     if want("gs"):
         p, n = 8, 1 << 23
@@ -345,6 +350,47 @@ def extra_collectives(torch, coll, inputs, metrics, dev, which, iters=10, warmup
         del a, b
         torch.cuda.empty_cache()
     return rows
+
+
+def moe_row(torch, coll, inputs, dev, iters, warmup):
+    """Pack -> dispatch Alltoallv -> reverse Alltoallv -> weighted combine
+    (in place on a residual), p = 8, 4096 tokens x 7168 bf16 per rank,
+    top-2 routing uniform over ranks; each stage timed on its own."""
+    p, T, H, k = 8, 4096, 7168, 2
+    A = T * k
+    d = 2
+    toks = [to_dev(torch, x, dev) for x in inputs.rank_buffers(inputs.WL_MOE_A2A, p, T * H, inputs.BF16,
+                                                               dist="normal")]
+    dest = [torch.from_numpy(r).to(dev) for r in inputs.moe_routes(p, T, k)]
+    wts = [torch.from_numpy(w).to(dev) for w in inputs.moe_weights(p, T, k)]
+    packed = [torch.empty(A * H, dtype=torch.bfloat16, device=dev) for _ in range(p)]
+    pos = [torch.empty(A, dtype=torch.int32, device=dev) for _ in range(p)]
+    counts = torch.empty(p * p, dtype=torch.int64, device=dev)
+    f_pack = coll.coll_moe_pack(toks, dest, packed, pos, counts, k, H, defer=True)
+    f_pack()
+    torch.cuda.synchronize()
+    cols = counts.cpu().numpy().reshape(p, p).sum(axis=0)
+    recv = [torch.empty(int(c), dtype=torch.bfloat16, device=dev) for c in cols]
+    back = [torch.empty(A * H, dtype=torch.bfloat16, device=dev) for _ in range(p)]
+    out = [torch.empty(T * H, dtype=torch.bfloat16, device=dev).normal_() for _ in range(p)]
+    f_disp = coll.coll_alltoallv(packed, recv, counts, defer=True)
+    f_rev = coll.coll_alltoallv_transposed(recv, back, counts, defer=True)
+    f_comb = coll.coll_moe_combine(back, pos, wts, out, k, H, residual=out, defer=True)
+    t = [stats_us(x)[0] for x in time_launches(torch, [f_pack, f_disp, f_rev, f_comb], iters, warmup)]
+    # algorithmic HBM bytes per stage (all ranks)
+    b_pack = p * (A * H * d * 2 + A * 4 * 2)          # gather A rows, write A rows, read dest, write pos
+    b_xchg = p * 2 * A * H * d                       # each exchange reads and writes every row once
+    b_comb = p * (A * H * d + 2 * T * H * d + A * 8)  # A rows + residual in, T rows out, pos + weights
+    stage = {}
+    for name, us, b in (("pack", t[0], b_pack), ("dispatch_alltoallv", t[1], b_xchg),
+                        ("reverse_alltoallv", t[2], b_xchg), ("combine", t[3], b_comb)):
+        stage[name] = {"t_med_us": round(us, 2), "hbm_bytes": b, "hbm_GBps": round(b / (us * 1e-6) / 1e9, 1)}
+    tot_us = sum(t)
+    tot_b = b_pack + 2 * b_xchg + b_comb
+    return {"name": "moe_dispatch_combine", "p": p, "tokens": T, "hidden": H, "top_k": k, "dtype": "bf16",
+            "t_med_us": round(tot_us, 2), "hbm_bytes": tot_b, "hbm_GBps": round(tot_b / (tot_us * 1e-6) / 1e9, 1),
+            "pct_hbm_peak": round(100.0 * tot_b / (tot_us * 1e-6) / 1e9 / HBM_PEAK, 1), "stages": stage,
+            "workload": "pack -> Alltoallv -> reverse Alltoallv -> weighted combine + residual"}
 
 
 def batch_row(torch, coll, inputs, dev, iters=5, warmup=2):

@@ -68,6 +68,9 @@ def lib() -> ctypes.CDLL:
         "coll_alltoall": [pp, pp, i32, sz, i32, vp],
         "coll_alltoallv": [pp, pp, i32, vp, i64p, i64p, vp, i32, vp],
         "coll_gather": [pp, vp, i32, sz, i32, i32, vp],
+        "coll_alltoallv_transposed": [pp, pp, i32, vp, i64p, i64p, vp, i32, vp],
+        "coll_moe_pack": [pp, pp, pp, pp, vp, vp, i32, sz, i32, sz, i32, vp],
+        "coll_moe_combine": [pp, pp, pp, pp, pp, i32, sz, i32, sz, i32, vp],
         "coll_scatter": [vp, pp, i32, sz, i32, i32, vp],
         "coll_allreduce_batch": [ctypes.POINTER(coll_call_t), i32, i32, ctypes.c_uint, vp],
     }
@@ -327,6 +330,75 @@ def coll_alltoallv(send, recv, counts_dev, send_cap: Sequence[int] | None = None
     st = _addr(status_dev) if status_dev is not None else None
     return _run("coll_alltoallv", (s, r, p, _addr(counts_dev), sc, rc, st, dt, _stream(stream)),
                 "coll_alltoallv", defer, (k1, k2, sc, rc))
+
+
+def coll_alltoallv_transposed(send, recv, counts_dev, send_cap: Sequence[int] | None = None,
+                              recv_cap: Sequence[int] | None = None, status_dev=None, dtype: int | None = None,
+                              stream=None, defer: bool = False):
+    """The reverse exchange of coll_alltoallv: counts_dev is the forward
+    [p, p] matrix; rank i sends counts[j][i] elements to rank j."""
+    p = len(send)
+    dt = _dtype_of(send[0], dtype)
+    if send_cap is None:
+        send_cap = [_numel(x, None) for x in send]
+    if recv_cap is None:
+        recv_cap = [_numel(x, None) for x in recv]
+    if hasattr(counts_dev, "dtype"):
+        import torch
+        if counts_dev.dtype != torch.int64 or counts_dev.numel() < p * p:
+            raise ValueError("counts must be a device int64 tensor with p*p entries")
+    _same_dtype([*send, *recv], dt)
+    s, k1 = _ptr_array(send)
+    r, k2 = _ptr_array(recv)
+    sc = (ctypes.c_int64 * p)(*[int(v) for v in send_cap])
+    rc = (ctypes.c_int64 * p)(*[int(v) for v in recv_cap])
+    st = _addr(status_dev) if status_dev is not None else None
+    return _run("coll_alltoallv_transposed", (s, r, p, _addr(counts_dev), sc, rc, st, dt, _stream(stream)),
+                "coll_alltoallv_transposed", defer, (k1, k2, sc, rc))
+
+
+def coll_moe_pack(tokens, dest, packed, pos, counts_dev, k: int, hidden: int, status_dev=None,
+                  tokens_per_rank: int | None = None, dtype: int | None = None, stream=None,
+                  defer: bool = False):
+    """Dispatch pack: per rank, tokens [T*hidden], dest int32 [T*k] ->
+    packed [T*k*hidden], pos int32 [T*k]; counts_dev int64 [p, p] (elements)."""
+    p = len(tokens)
+    dt = _dtype_of(tokens[0], dtype)
+    T = tokens_per_rank if tokens_per_rank is not None else _numel(tokens[0], None) // int(hidden)
+    _same_dtype([*tokens, *packed], dt)
+    _check_sizes(tokens, T * hidden, "moe_pack tokens")
+    _check_sizes(packed, T * k * hidden, "moe_pack packed")
+    _check_sizes([*dest, *pos], T * k, "moe_pack dest/pos")
+    a1, k1 = _ptr_array(tokens)
+    a2, k2 = _ptr_array(dest)
+    a3, k3 = _ptr_array(packed)
+    a4, k4 = _ptr_array(pos)
+    st = _addr(status_dev) if status_dev is not None else None
+    return _run("coll_moe_pack", (a1, a2, a3, a4, _addr(counts_dev), st, p, int(T), int(k), int(hidden), dt,
+                                  _stream(stream)), "coll_moe_pack", defer, (k1, k2, k3, k4))
+
+
+def coll_moe_combine(back, pos, weights, out, k: int, hidden: int, residual=None,
+                     tokens_per_rank: int | None = None, dtype: int | None = None, stream=None,
+                     defer: bool = False):
+    """Weighted combine: per rank out[t] = residual[t] + sum_s w[t*k+s] * back[pos[t*k+s]]."""
+    p = len(back)
+    dt = _dtype_of(back[0], dtype)
+    T = tokens_per_rank if tokens_per_rank is not None else _numel(out[0], None) // int(hidden)
+    _same_dtype([*back, *out, *(residual or [])], dt)
+    _check_sizes(back, T * k * hidden, "moe_combine back")
+    _check_sizes(out, T * hidden, "moe_combine out")
+    _check_sizes([*pos, *weights], T * k, "moe_combine pos/weights")
+    a1, k1 = _ptr_array(back)
+    a2, k2 = _ptr_array(pos)
+    a3, k3 = _ptr_array(weights)
+    a5, k5 = _ptr_array(out)
+    if residual is not None:
+        a4, k4 = _ptr_array(residual)
+    else:
+        a4, k4 = None, None
+    return _run("coll_moe_combine", (a1, a2, a3, a4, a5, p, int(T), int(k), int(hidden), dt, _stream(stream)),
+                "coll_moe_combine", defer, (k1, k2, k3, k4, k5))
 
 
 def coll_allreduce_batch(calls: Sequence[tuple], p: int, flags: int = 0, stream=None,

@@ -24,6 +24,7 @@ SOURCES = [
     "copy_kernels.hip",
     "ring_literal.hip",
     "batch_kernels.hip",
+    "moe_kernels.hip",
 ]
 
 ARCH = "gfx950"

@@ -40,9 +40,11 @@ std::atomic<int> g_wg_per_cu{0};
 
 // Default workgroups (of 256 threads) per compute unit, per kernel family.
 // Reductions keep 16-32 loads in flight per lane and run best with one
-// workgroup per CU; copies with two.
-enum Family { kFamReduce = 0, kFamCopy = 1 };
-constexpr int kDefaultWgPerCu[2] = {1, 2};
+// workgroup per CU; copies with two.  Row kernels (MoE pack and combine)
+// move one token row (a few KiB) per workgroup step and need more
+// workgroups to keep enough bytes in flight.
+enum Family { kFamReduce = 0, kFamCopy = 1, kFamRow = 2 };
+constexpr int kDefaultWgPerCu[3] = {1, 2, 8};
 
 int current_device(int* dev) { return (int)hipGetDevice(dev); }
 
@@ -429,10 +431,10 @@ COLL_EXPORT coll_status_t coll_scatter(const void* send_root, void* const* recv,
   return finish(coll::launch_copy((int)dsize(dtype), P, g, grid, stream));
 }
 
-COLL_EXPORT coll_status_t coll_alltoallv(const void* const* send, void* const* recv, int p,
-                                         const int64_t* counts_dev, const int64_t* send_cap,
-                                         const int64_t* recv_cap, int32_t* status_dev, coll_dtype_t dtype,
-                                         void* stream) {
+namespace {
+coll_status_t alltoallv_impl(const void* const* send, void* const* recv, int p, const int64_t* counts_dev,
+                             const int64_t* send_cap, const int64_t* recv_cap, int32_t* status_dev,
+                             coll_dtype_t dtype, int transposed, void* stream) {
   if (p < 1 || p > kMaxRanks || !dtype_ok(dtype)) return COLL_ERR_INVALID_ARG;
   if (!counts_dev || !send_cap || !recv_cap) return COLL_ERR_INVALID_ARG;
   if (!all_non_null(send, p) || !all_non_null(recv, p)) return COLL_ERR_INVALID_ARG;
@@ -476,7 +478,152 @@ COLL_EXPORT coll_status_t coll_alltoallv(const void* const* send, void* const* r
   a.p = p;
   a.src_mis = common_mis(send, p);
   a.dst_mis = common_mis((const void* const*)recv, p);
+  a.transposed = transposed;
   return finish(coll::launch_alltoallv((int)d, P, a, grid, stream));
+}
+}  // namespace
+
+COLL_EXPORT coll_status_t coll_alltoallv(const void* const* send, void* const* recv, int p,
+                                         const int64_t* counts_dev, const int64_t* send_cap,
+                                         const int64_t* recv_cap, int32_t* status_dev, coll_dtype_t dtype,
+                                         void* stream) {
+  return alltoallv_impl(send, recv, p, counts_dev, send_cap, recv_cap, status_dev, dtype, 0, stream);
+}
+
+COLL_EXPORT coll_status_t coll_alltoallv_transposed(const void* const* send, void* const* recv, int p,
+                                                    const int64_t* counts_dev, const int64_t* send_cap,
+                                                    const int64_t* recv_cap, int32_t* status_dev,
+                                                    coll_dtype_t dtype, void* stream) {
+  return alltoallv_impl(send, recv, p, counts_dev, send_cap, recv_cap, status_dev, dtype, 1, stream);
+}
+
+// ---------------------------------------------------------------------------
+// MoE dispatch pack and combine
+// ---------------------------------------------------------------------------
+COLL_EXPORT coll_status_t coll_moe_pack(const void* const* tokens, const int32_t* const* dest,
+                                        void* const* packed, int32_t* const* pos, int64_t* counts_dev,
+                                        int32_t* status_dev, int p, size_t tokens_per_rank, int k,
+                                        size_t hidden, coll_dtype_t dtype, void* stream) {
+  if (p < 1 || p > kMaxRanks || !dtype_ok(dtype) || k < 1 || k > coll::kMaxTopK || hidden == 0)
+    return COLL_ERR_INVALID_ARG;
+  if (!counts_dev || !elem_aligned1(counts_dev, sizeof(int64_t))) return COLL_ERR_INVALID_ARG;
+  if (status_dev && !elem_aligned1(status_dev, sizeof(int32_t))) return COLL_ERR_INVALID_ARG;
+  const size_t d = dsize(dtype);
+  size_t A, rowbytes, tb, pb;
+  if (!mul_ok(tokens_per_rank, (size_t)k, 1, &A) || A > 0x7fffffffull) return COLL_ERR_INVALID_ARG;
+  if (!mul_ok(hidden, d, 1, &rowbytes) || !mul_ok(tokens_per_rank, rowbytes, 1, &tb) ||
+      !mul_ok(A, rowbytes, (size_t)kMaxRanks, &pb))
+    return COLL_ERR_INVALID_ARG;
+  pb = A * rowbytes;
+  std::vector<Range> rs;
+  if (A > 0) {
+    if (!all_non_null(tokens, p) || !all_non_null(dest, p) || !all_non_null(packed, p) || !all_non_null(pos, p))
+      return COLL_ERR_INVALID_ARG;
+    if (!elem_aligned(tokens, p, d) || !elem_aligned(packed, p, d) || !elem_aligned(dest, p, 4) ||
+        !elem_aligned(pos, p, 4))
+      return COLL_ERR_INVALID_ARG;
+    for (int r = 0; r < p; ++r) {
+      rs.push_back(rng(tokens[r], tb, false, r));
+      rs.push_back(rng(dest[r], A * 4, false, r));
+      rs.push_back(rng(packed[r], pb, true, r));
+      rs.push_back(rng(pos[r], A * 4, true, r));
+    }
+  }
+  rs.push_back(rng(counts_dev, (size_t)p * p * sizeof(int64_t), true, -1));
+  if (status_dev) rs.push_back(rng(status_dev, (size_t)p * sizeof(int32_t), true, -1));
+  coll_status_t st = check_alias(rs, [](const Range&, const Range&) { return false; });
+  if (st != COLL_OK) return st;
+  coll::MoeIndexArgs ia;
+  std::memset(&ia, 0, sizeof(ia));
+  for (int r = 0; r < p && A > 0; ++r) {
+    ia.dest[r] = dest[r];
+    ia.pos[r] = pos[r];
+  }
+  ia.counts = counts_dev;
+  ia.status = status_dev;
+  ia.assignments = A;
+  ia.hidden = hidden;
+  ia.p = p;
+  int e = coll::launch_moe_index(ia, stream);
+  if (e) return hip_fail(e);
+  if (A == 0) return COLL_OK;
+  int grid;
+  e = max_grid(&grid, kFamRow);
+  if (e) return hip_fail(e);
+  coll::MoeRowArgs ra;
+  std::memset(&ra, 0, sizeof(ra));
+  for (int r = 0; r < p; ++r) {
+    ra.src[r] = tokens[r];
+    ra.dst[r] = packed[r];
+    ra.pos[r] = pos[r];
+  }
+  ra.tokens = tokens_per_rank;
+  ra.hidden = hidden;
+  ra.k = k;
+  ra.p = p;
+  ra.src_mis = common_mis(tokens, p);
+  ra.dst_mis = common_mis((const void* const*)packed, p);
+  return finish(coll::launch_moe_pack((int)d, ra, grid, stream));
+}
+
+// Range tag of residual buffers (kept apart from the back rows of the same rank).
+constexpr int kResidualTag = 4 * kMaxRanks;
+
+COLL_EXPORT coll_status_t coll_moe_combine(const void* const* back, const int32_t* const* pos,
+                                           const float* const* weights, const void* const* residual,
+                                           void* const* out, int p, size_t tokens_per_rank, int k,
+                                           size_t hidden, coll_dtype_t dtype, void* stream) {
+  if (p < 1 || p > kMaxRanks || !dtype_ok(dtype) || k < 1 || k > coll::kMaxTopK || hidden == 0)
+    return COLL_ERR_INVALID_ARG;
+  if (dtype == COLL_I32) return COLL_ERR_UNSUPPORTED;
+  const size_t d = dsize(dtype);
+  size_t A, rowbytes, tb, pb;
+  if (!mul_ok(tokens_per_rank, (size_t)k, 1, &A) || A > 0x7fffffffull) return COLL_ERR_INVALID_ARG;
+  if (!mul_ok(hidden, d, 1, &rowbytes) || !mul_ok(tokens_per_rank, rowbytes, 1, &tb) ||
+      !mul_ok(A, rowbytes, (size_t)kMaxRanks, &pb))
+    return COLL_ERR_INVALID_ARG;
+  pb = A * rowbytes;
+  if (A == 0) return COLL_OK;
+  if (!all_non_null(back, p) || !all_non_null(pos, p) || !all_non_null(weights, p) || !all_non_null(out, p))
+    return COLL_ERR_INVALID_ARG;
+  if (residual && !all_non_null(residual, p)) return COLL_ERR_INVALID_ARG;
+  if (!elem_aligned(back, p, d) || !elem_aligned(out, p, d) || !elem_aligned(pos, p, 4) ||
+      !elem_aligned(weights, p, 4) || (residual && !elem_aligned(residual, p, d)))
+    return COLL_ERR_INVALID_ARG;
+  std::vector<Range> rs;
+  for (int r = 0; r < p; ++r) {
+    rs.push_back(rng(back[r], pb, false, r));
+    rs.push_back(rng(pos[r], A * 4, false, r));
+    rs.push_back(rng(weights[r], A * 4, false, r));
+    if (residual) rs.push_back(rng(residual[r], tb, false, kResidualTag + r));
+    rs.push_back(rng(out[r], tb, true, r));
+  }
+  coll_status_t st = check_alias(rs, [](const Range& o, const Range& x) {
+    // in place: out[r] is exactly residual[r] (the residual add)
+    return !x.out && x.rank == kResidualTag + o.rank && x.b == o.b && x.e == o.e;
+  });
+  if (st != COLL_OK) return st;
+  int grid;
+  int e = max_grid(&grid, kFamRow);
+  if (e) return hip_fail(e);
+  coll::MoeRowArgs ra;
+  std::memset(&ra, 0, sizeof(ra));
+  for (int r = 0; r < p; ++r) {
+    ra.src[r] = back[r];
+    ra.dst[r] = out[r];
+    ra.pos[r] = pos[r];
+    ra.weights[r] = weights[r];
+    if (residual) ra.residual[r] = residual[r];
+  }
+  ra.tokens = tokens_per_rank;
+  ra.hidden = hidden;
+  ra.k = k;
+  ra.p = p;
+  ra.has_residual = residual ? 1 : 0;
+  ra.src_mis = common_mis(back, p);
+  ra.dst_mis = common_mis((const void* const*)out, p);
+  ra.res_mis = residual ? common_mis(residual, p) : 0;
+  return finish(coll::launch_moe_combine(dtype, ra, grid, stream));
 }
 
 // ---------------------------------------------------------------------------

@@ -104,7 +104,10 @@ COLL_STREAM_KERNEL void alltoallv_kernel(RankPtrs ptrs, A2avArgs a) {
   int64_t* roff = lds + 2 * pp;
   const int tid = threadIdx.x;
   if (tid == 0) bad = 0;
-  for (int i = tid; i < pp; i += kBlock) cnt[i] = a.counts[i];
+  for (int i = tid; i < pp; i += kBlock) {
+    const int src = i / p, dst = i - (i / p) * p;
+    cnt[i] = a.transposed ? a.counts[dst * p + src] : a.counts[i];
+  }
   __syncthreads();
   if (tid < p) {
     const int i = tid;

@@ -62,13 +62,43 @@ struct CopyGeom {
 };
 
 struct A2avArgs {
-  const int64_t* counts;         // device, p*p, row = source
+  const int64_t* counts;         // device, p*p, row = source (column = source if transposed)
   int32_t* status;               // device, optional
   int64_t send_cap[kMaxRanks];   // elements
   int64_t recv_cap[kMaxRanks];
   int p;
   int src_mis;
   int dst_mis;
+  int transposed;                // elements from i to j are counts[j*p + i]
+};
+
+// MoE dispatch pack and combine.
+constexpr int kMaxTopK = 8;
+
+struct MoeIndexArgs {
+  const int32_t* dest[kMaxRanks];  // per rank: destination rank of each assignment
+  int32_t* pos[kMaxRanks];         // per rank: packed row of each assignment
+  int64_t* counts;                 // [p][p] elements
+  int32_t* status;                 // optional
+  uint64_t assignments;            // T * k per rank
+  uint64_t hidden;
+  int p;
+};
+
+struct MoeRowArgs {
+  const void* src[kMaxRanks];      // pack: tokens; combine: returned rows
+  void* dst[kMaxRanks];            // pack: packed rows; combine: output tokens
+  const int32_t* pos[kMaxRanks];
+  const float* weights[kMaxRanks];  // combine only
+  const void* residual[kMaxRanks];  // combine only, optional
+  uint64_t tokens;                 // T per rank
+  uint64_t hidden;
+  int k;
+  int p;
+  int has_residual;
+  int src_mis;                     // common misalignment of the src bases, or -1
+  int dst_mis;
+  int res_mis;
 };
 
 // Literal ring: one neighbour step per launch.
@@ -112,6 +142,12 @@ int launch_batch(const BatchArgs& a, int grid, void* stream);
 // Elements of one batch tile for a dtype and rank count (the host cuts
 // each call's chunks into tiles of this size).
 uint64_t batch_tile_elems_host(int dtype, int p);
+
+// MoE: the index pass (one workgroup per rank), the payload pack and the
+// weighted combine.
+int launch_moe_index(const MoeIndexArgs& a, void* stream);
+int launch_moe_pack(int elem_bytes, const MoeRowArgs& a, int max_grid, void* stream);
+int launch_moe_combine(int dtype, const MoeRowArgs& a, int max_grid, void* stream);
 
 // 16-byte vectors each lane of a copy kernel keeps in flight.
 constexpr uint64_t kCopyUnroll = 4;

@@ -1,0 +1,320 @@
+// MoE dispatch pack and weighted combine around the ragged exchange.
+//
+// "Collective Communication：AllReduce、AllGather、ReduceScatter 与
+// All-to-All" lists the expert-parallel flow (Ragged All-to-All and Expert
+// Parallel sections): router output -> count assignments per destination
+// -> prefix-sum offsets -> pack/permute payload -> variable-split
+// All-to-All -> expert compute -> reverse variable-split All-to-All ->
+// unpermute and weighted combine.  The exchanges are the Alltoallv
+// kernels; this file holds the steps either side of them.
+//
+// Index pass (one 1024-thread workgroup per source rank): every wave owns
+// a contiguous run of the rank's assignments.  It counts destinations 64
+// assignments at a time, grouping equal destinations of a group with
+// ballots; the per-wave counts are turned into exclusive offsets (by
+// destination, then by wave); a second walk gives every assignment its
+// packed row, stable in assignment order.  Destinations outside [0, p)
+// reject the rank: its counts are 0 and every pos is -1.
+//
+// Payload pack and combine: one wave per row (a token's hidden vector),
+// rows spread over every wave of the grid, so a workgroup keeps four rows
+// in flight.
+#include "copy_tile.h"
+
+namespace coll {
+
+constexpr int kIdxThreads = 1024;
+constexpr int kIdxWaves = kIdxThreads / 64;
+
+__global__ __launch_bounds__(kIdxThreads) void moe_index_kernel(MoeIndexArgs a) {
+  __shared__ int wofs[kIdxWaves][kMaxRanks];  // per-wave counts, then offsets
+  __shared__ int total[kMaxRanks];
+  __shared__ int base[kMaxRanks];
+  __shared__ int bad;
+  const int rank = blockIdx.x;
+  const int p = a.p;
+  const uint64_t A = a.assignments;
+  const int32_t* dest = a.dest[rank];
+  int32_t* pos = a.pos[rank];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int x = tid; x < kIdxWaves * kMaxRanks; x += kIdxThreads) (&wofs[0][0])[x] = 0;
+  if (tid == 0) bad = 0;
+  __syncthreads();
+  const uint64_t per = ((A + kIdxWaves - 1) / kIdxWaves + 63) / 64 * 64;
+  uint64_t lo = (uint64_t)w * per, hi = lo + per;
+  if (lo > A) lo = A;
+  if (hi > A) hi = A;
+  // pass 1: per-wave destination counts
+  for (uint64_t b = lo; b < hi; b += 64) {
+    const uint64_t x = b + lane;
+    int d = -1;
+    if (x < hi) {
+      d = dest[x];
+      if (d < 0 || d >= p) {
+        bad = 1;
+        d = -1;
+      }
+    }
+    uint64_t rem = __ballot(d >= 0);
+    while (rem) {
+      const int leader = __ffsll((unsigned long long)rem) - 1;
+      const int dl = __shfl(d, leader);
+      const uint64_t m = __ballot(d == dl) & rem;
+      if (lane == leader) wofs[w][dl] += __popcll(m);
+      rem &= ~m;
+    }
+  }
+  __syncthreads();
+  if (tid < p) {
+    int t = 0;
+    for (int ww = 0; ww < kIdxWaves; ++ww) {
+      const int c = wofs[ww][tid];
+      wofs[ww][tid] = t;
+      t += c;
+    }
+    total[tid] = t;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int s = 0;
+    for (int d = 0; d < p; ++d) {
+      base[d] = s;
+      s += total[d];
+    }
+  }
+  __syncthreads();
+  const bool reject = bad != 0;
+  if (tid < p) {
+    a.counts[(uint64_t)rank * p + tid] = reject ? 0 : (int64_t)total[tid] * (int64_t)a.hidden;
+    for (int ww = 0; ww < kIdxWaves; ++ww) wofs[ww][tid] += base[tid];
+  }
+  if (tid == 0 && a.status) a.status[rank] = reject ? 1 : 0;
+  __syncthreads();
+  if (reject) {
+    for (uint64_t x = tid; x < A; x += kIdxThreads) pos[x] = -1;
+    return;
+  }
+  // pass 2: packed row of every assignment
+  for (uint64_t b = lo; b < hi; b += 64) {
+    const uint64_t x = b + lane;
+    const int d = x < hi ? dest[x] : -1;
+    uint64_t rem = __ballot(d >= 0);
+    while (rem) {
+      const int leader = __ffsll((unsigned long long)rem) - 1;
+      const int dl = __shfl(d, leader);
+      const uint64_t m = __ballot(d == dl) & rem;
+      if (d == dl) pos[x] = wofs[w][dl] + __popcll(m & below);
+      if (lane == leader) wofs[w][dl] += __popcll(m);
+      rem &= ~m;
+    }
+  }
+}
+
+constexpr int kWaveLanes = 64;
+constexpr int kRowBatch = 16;  // 16-byte vectors per lane issued together in a row copy
+
+// Global index of this wave (uniform across its lanes) and the wave count.
+__device__ __forceinline__ uint64_t wave_id() {
+  return (uint64_t)blockIdx.x * (kBlock / kWaveLanes) +
+         (uint64_t)__builtin_amdgcn_readfirstlane(threadIdx.x / kWaveLanes);
+}
+__device__ __forceinline__ uint64_t wave_count() { return (uint64_t)gridDim.x * (kBlock / kWaveLanes); }
+
+// Copy one row of len elements with one wave: every lane issues up to
+// kRowBatch vector loads before its first store.
+template <int B>
+__device__ __forceinline__ void copy_row_wave(const typename Word<B>::T* src, typename Word<B>::T* dst,
+                                              uint64_t len, int mis, int lane) {
+  const SegSpan sp = seg_span<B>(len, mis);
+  if (sp.vec && sp.nvec) {
+    const u32x4* vs = reinterpret_cast<const u32x4*>(src + sp.head);
+    u32x4* vd = reinterpret_cast<u32x4*>(dst + sp.head);
+    for (uint64_t j0 = 0; j0 < sp.nvec; j0 += (uint64_t)kRowBatch * kWaveLanes) {
+      u32x4 r[kRowBatch];
+#pragma unroll
+      for (int u = 0; u < kRowBatch; ++u) {
+        const uint64_t j = j0 + (uint64_t)u * kWaveLanes + lane;
+        if (j < sp.nvec) r[u] = ld16<false>(vs + j);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < kRowBatch; ++u) {
+        const uint64_t j = j0 + (uint64_t)u * kWaveLanes + lane;
+        if (j < sp.nvec) st16<true>(vd + j, r[u]);
+      }
+    }
+  }
+  const uint64_t head = sp.vec ? sp.head : len;
+  for (uint64_t e = lane; e < head; e += kWaveLanes) st1<true>(dst + e, ld1<false>(src + e));
+  if (sp.vec) {
+    const uint64_t t0 = sp.head + sp.nvec * (16 / B);
+    for (uint64_t e = t0 + lane; e < len; e += kWaveLanes) st1<true>(dst + e, ld1<false>(src + e));
+  }
+}
+
+// packed[rank][pos[a] * H ...] = tokens[rank][(a / k) * H ...], one row per
+// wave.  Token rows are read through the cache (a token with k > 1 slots
+// is read k times).
+template <int B>
+COLL_STREAM_KERNEL void moe_pack_kernel(MoeRowArgs a) {
+  using W = typename Word<B>::T;
+  const int lane = (int)(threadIdx.x % kWaveLanes);
+  const uint64_t A = a.tokens * (uint64_t)a.k;
+  const uint64_t rows = A * (uint64_t)a.p;
+  for (uint64_t r = wave_id(); r < rows; r += wave_count()) {
+    const int rank = (int)(r / A);
+    const uint64_t x = r - (uint64_t)rank * A;
+    const int32_t ps = a.pos[rank][x];
+    if (ps < 0 || (uint64_t)ps >= A) continue;
+    const uint64_t t = x / (uint64_t)a.k;
+    const uint64_t so = t * a.hidden, dof = (uint64_t)ps * a.hidden;
+    const int mis = seg_mis(a.src_mis, a.dst_mis, so * B, dof * B);
+    copy_row_wave<B>((const W*)a.src[rank] + so, (W*)a.dst[rank] + dof, a.hidden, mis, lane);
+  }
+}
+
+// out[rank][t] = residual[rank][t] (or +0) + sum_s w[t*k+s] * back[rank][pos[t*k+s]],
+// accumulated in fp32 in slot order with every product and sum rounded on
+// its own; slots whose pos lies outside [0, T*k) are skipped.  One token
+// row per wave, kCombBatch vectors per lane per step.
+constexpr int kCombBatch = 4;
+
+template <int DT>
+COLL_STREAM_KERNEL void moe_combine_kernel(MoeRowArgs a) {
+#pragma clang fp contract(off)
+  using T = Traits<DT>;
+  using S = typename T::S;
+  using A = typename T::A;
+  constexpr int V = T::V;
+  const int lane = (int)(threadIdx.x % kWaveLanes);
+  const uint64_t Aa = a.tokens * (uint64_t)a.k;
+  const uint64_t rows = a.tokens * (uint64_t)a.p;
+  const int k = a.k;
+  const uint64_t H = a.hidden;
+  for (uint64_t r = wave_id(); r < rows; r += wave_count()) {
+    const int rank = (int)(r / a.tokens);
+    const uint64_t t = r - (uint64_t)rank * a.tokens;
+    const S* yrow[kMaxTopK];
+    float wt[kMaxTopK];
+    bool ok[kMaxTopK];
+    int mis = a.dst_mis < 0 ? -1 : (int)((a.dst_mis + t * H * T::B) & 15);
+    if (a.has_residual) mis = seg_mis(mis, a.res_mis, 0, t * H * T::B);
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s) {
+      ok[s] = false;
+      wt[s] = 0.0f;
+      yrow[s] = nullptr;
+      if (s < k) {
+        const int32_t ps = a.pos[rank][t * k + s];
+        ok[s] = ps >= 0 && (uint64_t)ps < Aa;
+        if (ok[s]) {
+          wt[s] = a.weights[rank][t * k + s];
+          yrow[s] = (const S*)a.src[rank] + (uint64_t)ps * H;
+          mis = seg_mis(mis, a.src_mis, 0, (uint64_t)ps * H * T::B);
+        }
+      }
+    }
+    const S* res = a.has_residual ? (const S*)a.residual[rank] + t * H : nullptr;
+    S* out = (S*)a.dst[rank] + t * H;
+    auto elems = [&](uint64_t from, uint64_t cnt) {
+      for (uint64_t e = from + lane; e < from + cnt; e += kWaveLanes) {
+        A acc = res ? widen1<DT>(ld1<true>(res + e)) : A(0.0f);
+#pragma unroll
+        for (int s = 0; s < kMaxTopK; ++s)
+          if (ok[s]) {
+            const A prod = wt[s] * widen1<DT>(ld1<true>(yrow[s] + e));
+            acc = acc + prod;
+          }
+        st1<false>(out + e, narrow1<DT>(acc));
+      }
+    };
+    const SegSpan sp = seg_span<T::B>(H, mis);
+    if (!sp.vec) {
+      elems(0, H);
+      continue;
+    }
+    for (uint64_t j0 = 0; j0 < sp.nvec; j0 += (uint64_t)kCombBatch * kWaveLanes) {
+      // every load of the batch (residual and all slots) before any arithmetic
+      u32x4 rr[kCombBatch];
+      u32x4 y[kMaxTopK][kCombBatch];
+#pragma unroll
+      for (int u = 0; u < kCombBatch; ++u) {
+        const uint64_t j = j0 + (uint64_t)u * kWaveLanes + lane;
+        rr[u] = u32x4{0, 0, 0, 0};
+        if (res && j < sp.nvec) rr[u] = ld16<true>(res + sp.head + j * V);
+      }
+#pragma unroll
+      for (int s = 0; s < kMaxTopK; ++s)
+#pragma unroll
+        for (int u = 0; u < kCombBatch; ++u) {
+          const uint64_t j = j0 + (uint64_t)u * kWaveLanes + lane;
+          y[s][u] = u32x4{0, 0, 0, 0};
+          if (ok[s] && j < sp.nvec) y[s][u] = ld16<true>(yrow[s] + sp.head + j * V);
+        }
+#pragma unroll
+      for (int u = 0; u < kCombBatch; ++u) {
+        A acc[V];
+        if (res) {
+          widen<DT>(rr[u], acc);
+        } else {
+#pragma unroll
+          for (int x = 0; x < V; ++x) acc[x] = 0.0f;
+        }
+#pragma unroll
+        for (int s = 0; s < kMaxTopK; ++s) {
+          if (!ok[s]) continue;
+          A v[V];
+          widen<DT>(y[s][u], v);
+#pragma unroll
+          for (int x = 0; x < V; ++x) {
+            const A prod = wt[s] * v[x];
+            acc[x] = acc[x] + prod;
+          }
+        }
+        const uint64_t j = j0 + (uint64_t)u * kWaveLanes + lane;
+        if (j < sp.nvec) st16<false>(out + sp.head + j * V, narrow<DT>(acc));
+      }
+    }
+    if (sp.head) elems(0, sp.head);
+    if (sp.tail) elems(sp.head + sp.nvec * V, sp.tail);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launch
+// ---------------------------------------------------------------------------
+int launch_moe_index(const MoeIndexArgs& a, void* stream) {
+  hipLaunchKernelGGL(moe_index_kernel, dim3(a.p), dim3(kIdxThreads), 0, (hipStream_t)stream, a);
+  return (int)hipGetLastError();
+}
+
+int launch_moe_pack(int elem_bytes, const MoeRowArgs& a, int max_grid, void* stream) {
+  const uint64_t rows = a.tokens * (uint64_t)a.k * (uint64_t)a.p;
+  if (!rows) return 0;
+  const int grid = (int)(rows < (uint64_t)max_grid ? rows : (uint64_t)max_grid);
+  hipStream_t s = (hipStream_t)stream;
+  if (elem_bytes == 2)
+    hipLaunchKernelGGL((moe_pack_kernel<2>), dim3(grid), dim3(kBlock), 0, s, a);
+  else if (elem_bytes == 4)
+    hipLaunchKernelGGL((moe_pack_kernel<4>), dim3(grid), dim3(kBlock), 0, s, a);
+  else
+    return (int)hipErrorInvalidValue;
+  return (int)hipGetLastError();
+}
+
+int launch_moe_combine(int dtype, const MoeRowArgs& a, int max_grid, void* stream) {
+  const uint64_t rows = a.tokens * (uint64_t)a.p;
+  if (!rows) return 0;
+  const int grid = (int)(rows < (uint64_t)max_grid ? rows : (uint64_t)max_grid);
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == kF32)
+    hipLaunchKernelGGL((moe_combine_kernel<kF32>), dim3(grid), dim3(kBlock), 0, s, a);
+  else if (dtype == kBF16)
+    hipLaunchKernelGGL((moe_combine_kernel<kBF16>), dim3(grid), dim3(kBlock), 0, s, a);
+  else
+    return (int)hipErrorInvalidValue;
+  return (int)hipGetLastError();
+}
+
+}  // namespace coll

@@ -148,3 +148,18 @@ def small_batch_pools(p: int = 16, pool_bytes: int = 32 << 20) -> tuple[list[np.
     f = [uniform_f32(rng_for(WL_SMALL_BATCH, r, 1), ne) for r in range(p)]
     i = [uniform_i32(rng_for(WL_SMALL_BATCH, r, 2), ne) for r in range(p)]
     return f, i
+
+
+# ----------------------------------------------------------------------------
+# MoE routing: destination rank per assignment and combine weights
+# ----------------------------------------------------------------------------
+
+def moe_routes(p: int, tokens: int, k: int, workload: int = WL_MOE_A2A, extra: int = 0) -> list[np.ndarray]:
+    """Per rank, int32 [tokens*k]: destination rank of assignment t*k + s,
+    uniform over the p ranks (so per-pair token counts are multinomial)."""
+    return [rng_for(workload, r, 2000 + extra, k).integers(0, p, tokens * k).astype(np.int32) for r in range(p)]
+
+
+def moe_weights(p: int, tokens: int, k: int, workload: int = WL_MOE_A2A, extra: int = 0) -> list[np.ndarray]:
+    """Per rank, fp32 [tokens*k] combine weights uniform in [0, 1)."""
+    return [rng_for(workload, r, 3000 + extra, k).random(tokens * k, dtype=np.float32) for r in range(p)]

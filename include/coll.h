@@ -172,6 +172,51 @@ coll_status_t coll_alltoallv(const void* const* send, void* const* recv, int p,
                              const int64_t* recv_cap, int32_t* status_dev,
                              coll_dtype_t dtype, void* stream);
 
+/* The reverse of coll_alltoallv ([A] 1.7 duality table: All-to-All is
+ * its own dual with the splits swapped; [B] Ragged All-to-All: "reverse
+ * variable-split All-to-All").  counts_dev is the FORWARD matrix: the
+ * elements going from rank i to rank j now are counts_dev[j*p + i].
+ * Otherwise as coll_alltoallv (capacities, device-side checks, status). */
+coll_status_t coll_alltoallv_transposed(const void* const* send, void* const* recv, int p,
+                                        const int64_t* counts_dev, const int64_t* send_cap,
+                                        const int64_t* recv_cap, int32_t* status_dev,
+                                        coll_dtype_t dtype, void* stream);
+
+/* MoE dispatch pack ([B] Ragged All-to-All flow "count assignments per
+ * destination -> prefix-sum offsets -> pack/permute payload"; [B] Expert
+ * Parallel: the unit is the assignment, not the token).
+ * Per rank i: tokens[i] holds T rows of `hidden` elements; dest[i] (device
+ * int32, T*k) is the destination rank of assignment a = t*k + s.
+ * Assignments are ordered by destination rank, stable in a.  Outputs:
+ *   pos[i][a]      packed row of assignment a (device int32, T*k);
+ *   packed[i]      T*k rows: row pos[i][a] = token a / k;
+ *   counts_dev     [p][p] int64, counts[i][j] = hidden * (assignments of
+ *                  rank i to rank j): the forward matrix for
+ *                  coll_alltoallv, then coll_alltoallv_transposed;
+ *   status_dev     optional device int32[p]: 0, or 1 if rank i had a
+ *                  destination outside [0, p); such a rank gets counts 0,
+ *                  every pos -1 and no payload.
+ * k in [1, 8]; T = 0 writes zero counts.  No output may overlap another
+ * buffer. */
+coll_status_t coll_moe_pack(const void* const* tokens, const int32_t* const* dest, void* const* packed,
+                            int32_t* const* pos, int64_t* counts_dev, int32_t* status_dev, int p,
+                            size_t tokens_per_rank, int k, size_t hidden, coll_dtype_t dtype,
+                            void* stream);
+
+/* MoE weighted combine ([B] Expert Parallel: "weighted combine +
+ * residual", after the reverse exchange and the unpermute).  back[i] holds
+ * rank i's T*k returned rows in packed order; for every token t
+ *   out[i][t] = r + w[i][t*k] * back[i][pos[i][t*k]] + ... + w[i][t*k+k-1] * ...
+ * with r = residual[i][t] (residual may be NULL: r = +0), accumulated in
+ * fp32 in slot order, every product and sum rounded to fp32 on its own (no
+ * fused multiply-add), bf16 narrowed once.  weights: device fp32 (T*k).
+ * Slots whose pos is outside [0, T*k) are skipped.  fp32 and bf16 only
+ * (COLL_ERR_UNSUPPORTED for int32).  In place: out[i] == residual[i]. */
+coll_status_t coll_moe_combine(const void* const* back, const int32_t* const* pos,
+                               const float* const* weights, const void* const* residual,
+                               void* const* out, int p, size_t tokens_per_rank, int k, size_t hidden,
+                               coll_dtype_t dtype, void* stream);
+
 /* One AllReduce of a batch (host-side view). */
 typedef struct {
   const void* const* send;  /* host array of p device pointers */

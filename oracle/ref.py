@@ -43,6 +43,10 @@ Readings taken where the pages are silent or inconsistent:
 7. Halving-doubling: the page gives message sizes per step, not partner
    distances; the reduce-scatter phase pairs ranks at distance p/2, then
    p/4, ..., 1 (see halving_doubling_simulated).
+8. MoE pack/combine: the page lists the steps, not the formats.  Packing
+   orders assignments by destination rank, stable in assignment index;
+   the combine accumulates in fp32 in slot order with products and sums
+   rounded separately (see moe_pack, moe_combine).
 """
 from __future__ import annotations
 
@@ -241,6 +245,71 @@ def alltoallv(xs: list[np.ndarray], counts: np.ndarray) -> list[np.ndarray]:
 def alltoallv_recv_counts(counts: np.ndarray) -> np.ndarray:
     """Elements each destination receives: the column sums of the count matrix."""
     return np.asarray(counts, dtype=np.int64).sum(axis=0)
+
+
+# ----------------------------------------------------------------------------
+# MoE dispatch and combine around the ragged exchange ("Collective
+# Communication" page: Ragged All-to-All flow; Expert Parallel section)
+# ----------------------------------------------------------------------------
+
+def moe_pack(tokens: np.ndarray, dest: np.ndarray, k: int, hidden: int, p: int):
+    """One rank's dispatch pack.
+
+    tokens: [T*hidden] (row t = token t); dest[a] = destination rank of
+    assignment a = t*k + s (token t, slot s).  Assignments are ordered by
+    destination rank, stable in a (the page's "count assignments per
+    destination -> prefix-sum offsets -> pack/permute payload").
+
+    Returns (counts, pos, packed): counts[j] = hidden * (assignments to j),
+    in elements as the ragged exchange takes them; pos[a] = packed row of
+    assignment a; packed row pos[a] = token a // k.
+    """
+    dest = np.asarray(dest, dtype=np.int64)
+    A = len(dest)
+    assert np.all((dest >= 0) & (dest < p))
+    rows = np.zeros(p, dtype=np.int64)
+    for a in range(A):
+        rows[dest[a]] += 1
+    offset = np.zeros(p, dtype=np.int64)
+    for j in range(1, p):
+        offset[j] = offset[j - 1] + rows[j - 1]
+    cursor = offset.copy()
+    pos = np.zeros(A, dtype=np.int64)
+    for a in range(A):
+        pos[a] = cursor[dest[a]]
+        cursor[dest[a]] += 1
+    packed = np.zeros(A * hidden, dtype=np.asarray(tokens).dtype)
+    for a in range(A):
+        t = a // k
+        packed[pos[a] * hidden:(pos[a] + 1) * hidden] = tokens[t * hidden:(t + 1) * hidden]
+    return rows * hidden, pos, packed
+
+
+def moe_combine(back: np.ndarray, pos: np.ndarray, weights: np.ndarray, k: int, hidden: int, dtype: int,
+                residual: np.ndarray | None = None) -> np.ndarray:
+    """One rank's weighted combine after the reverse exchange.
+
+    back holds the rows returned in packed order; for token t,
+    out[t] = r[t] + w[t*k] * y_0 + w[t*k+1] * y_1 + ... with y_s = row
+    pos[t*k + s] of back and r the residual (or +0 without one): the page's
+    "weighted combine + residual".  Reading: fp32 accumulation in slot
+    order, each product and each sum rounded to fp32 separately (no fused
+    multiply-add), bf16 narrowed once at the end.
+    """
+    A = len(pos)
+    T = A // k
+    w = np.asarray(weights, dtype=np.float32)
+    rows = _widen(back, dtype).reshape(A, hidden)
+    if residual is not None:
+        acc = _widen(residual, dtype).reshape(T, hidden).copy()
+    else:
+        acc = np.zeros((T, hidden), dtype=np.float32)
+    for s in range(k):
+        a = np.arange(T) * k + s
+        prod = (w[a][:, None] * rows[pos[a]]).astype(np.float32)
+        acc = (acc + prod).astype(np.float32)
+    acc = acc.reshape(-1)
+    return f32_to_bf16_rne(acc) if dtype == BF16 else acc
 
 
 # ----------------------------------------------------------------------------

@@ -105,6 +105,15 @@ def test_invalid_arguments_rejected():
     assert L.coll_scatter(base, r, 4, n, 0, -1, None) == INV
     assert L.coll_scatter(None, r, 4, n, 0, 0, None) == INV
     assert L.coll_scatter(base, r, 4, n, 5, 0, None) == INV                 # bad dtype
+    cnt = base + 0x50000000
+    assert L.coll_moe_pack(s, s, r, r, cnt, None, 4, 10, 0, 16, 1, None) == INV   # k = 0
+    assert L.coll_moe_pack(s, s, r, r, cnt, None, 4, 10, 9, 16, 1, None) == INV   # k > 8
+    assert L.coll_moe_pack(s, s, r, r, cnt, None, 4, 10, 2, 0, 1, None) == INV    # hidden = 0
+    assert L.coll_moe_pack(s, s, r, r, None, None, 4, 10, 2, 16, 1, None) == INV  # no counts
+    assert L.coll_moe_pack(s, s, r, r, cnt + 4, None, 4, 10, 2, 16, 1, None) == INV  # counts misaligned
+    assert L.coll_moe_combine(s, s, s, None, r, 4, 10, 2, 16, 2, None) == coll.COLL_ERR_UNSUPPORTED  # int32
+    assert L.coll_moe_combine(s, s, s, None, None, 4, 10, 2, 16, 0, None) == INV  # no outputs
+    assert L.coll_alltoallv_transposed(s, r, 4, None, caps, caps, None, 0, None) == INV
 
 
 @host_only
@@ -161,4 +170,23 @@ def test_illegal_aliasing_rejected():
     # Scatter: recv[0] inside the root buffer while the root is 1
     r, _k15 = _arr([root_buf, recv[1], recv[2], recv[3]])
     assert L.coll_scatter(root_buf, r, p, n, 0, 1, None) == AL
+    # MoE combine: an output overlapping a returned-rows buffer is rejected
+    T, k, H = 8, 2, 16
+    back = [base + 0x60000000 + 0x100000 * i for i in range(p)]
+    outs = [base + 0x70000000 + 0x100000 * i for i in range(p)]
+    posb = [base + 0x78000000 + 0x100000 * i for i in range(p)]
+    wb = [base + 0x7c000000 + 0x100000 * i for i in range(p)]
+    b_, _k16 = _arr(back)
+    pz, _k17 = _arr(posb)
+    wz, _k18 = _arr(wb)
+    o_, _k19 = _arr([back[0]] + outs[1:])
+    assert L.coll_moe_combine(b_, pz, wz, None, o_, p, T, k, H, 0, None) == AL
+    # ... and out == residual (in place) is accepted by the alias check
+    o_, _k20 = _arr(outs)
+    assert L.coll_moe_combine(b_, pz, wz, o_, o_, p, T, k, H, 0, None) != AL
+    # MoE pack: pos overlapping packed is rejected
+    pk = [base + 0x40000000 + 0x1000000 * i for i in range(p)]
+    pk_, _k21 = _arr(pk)
+    ps_, _k22 = _arr([pk[0]] + [base + 0x48000000 + 0x10000 * i for i in range(1, p)])
+    assert L.coll_moe_pack(s, s, pk_, ps_, base + 0x4f000000, None, p, T, k, H, 0, None) == AL
     assert nb > 0

@@ -185,3 +185,42 @@ def test_small_batch_full_plan(env):
             if c.dtype == inputs.F32:
                 got = got.view(np.float32)
             assert_bits_equal(got, expect[r], f"batch call {k} rank {r}")
+
+
+def test_moe_round_trip_full_size(env):
+    """MoE dispatch and combine at p=8, 4096 tokens x 7168 bf16 per rank,
+    top-2 routing uniform over ranks: pack, dispatch exchange, reverse
+    exchange and weighted combine with residual, whole arrays against the
+    oracle at every stage."""
+    torch, coll = env
+    p, T, H, k = 8, 4096, 7168, 2
+    toks = inputs.rank_buffers(inputs.WL_MOE_A2A, p, T * H, inputs.BF16, dist="normal")
+    routes = inputs.moe_routes(p, T, k)
+    weights = inputs.moe_weights(p, T, k)
+    dtok = [dev(torch, x) for x in toks]
+    packed = [torch.empty(T * k * H, dtype=torch.bfloat16, device="cuda") for _ in range(p)]
+    pos = [torch.empty(T * k, dtype=torch.int32, device="cuda") for _ in range(p)]
+    counts = torch.empty(p * p, dtype=torch.int64, device="cuda")
+    coll.coll_moe_pack(dtok, [dev(torch, r) for r in routes], packed, pos, counts, k, H)
+    torch.cuda.synchronize()
+    C = counts.cpu().numpy().reshape(p, p)
+    packs = [ref.moe_pack(toks[i], routes[i], k, H, p) for i in range(p)]
+    assert np.array_equal(C, np.stack([pk[0] for pk in packs]))
+    for i in range(p):
+        assert pos[i].cpu().numpy().tolist() == packs[i][1].tolist()
+        assert_bits_equal(to_host(packed[i], BF16), packs[i][2], f"packed rank {i}")
+    cols = C.sum(axis=0)
+    recv = [torch.empty(int(c), dtype=torch.bfloat16, device="cuda") for c in cols]
+    coll.coll_alltoallv(packed, recv, counts)
+    back = [torch.empty(T * k * H, dtype=torch.bfloat16, device="cuda") for _ in range(p)]
+    coll.coll_alltoallv_transposed(recv, back, counts)
+    torch.cuda.synchronize()
+    for i in range(p):
+        assert torch.equal(back[i].view(torch.int16), packed[i].view(torch.int16)), f"round trip rank {i}"
+    residual = inputs.rank_buffers(inputs.WL_MOE_A2A, p, T * H, inputs.BF16, dist="normal", extra=(5,))
+    out = [dev(torch, r) for r in residual]
+    coll.coll_moe_combine(back, pos, [dev(torch, w) for w in weights], out, k, H, residual=out)
+    torch.cuda.synchronize()
+    for i in range(p):
+        expect = ref.moe_combine(packs[i][2], packs[i][1], weights[i], k, H, BF16, residual[i])
+        assert_bits_equal(to_host(out[i], BF16), expect, f"combine rank {i}")

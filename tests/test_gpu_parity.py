@@ -464,6 +464,158 @@ def test_alltoallv_equal_counts_match_alltoall(coll):
         assert torch.equal(r1[j].view(torch.int16), r2[j].view(torch.int16))
 
 
+@pytest.mark.parametrize("p", [1, 3, 8])
+def test_alltoallv_transposed(coll, p):
+    import torch
+    rng = np.random.default_rng(40 + p)
+    counts = _counts(p, rng, 900)
+    rows_t = counts.sum(axis=0)       # the reverse exchange sends column sums
+    cols_t = counts.sum(axis=1)
+    hx = [gen(1, int(rows_t[i]), BF16, 41 + i)[0] for i in range(p)]
+    send = [to_dev(x, BF16) if len(x) else empty(1, BF16) for x in hx]
+    recv = [empty(int(max(c, 1)), BF16, fill=0) for c in cols_t]
+    cdev = torch.from_numpy(counts.reshape(-1)).cuda()
+    status = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    coll.coll_alltoallv_transposed(send, recv, cdev, send_cap=[max(int(r), 1) for r in rows_t],
+                                   recv_cap=[int(max(c, 1)) for c in cols_t], status_dev=status)
+    sync()
+    assert int(status.item()) == 0
+    expect = ref.alltoallv(hx, counts.T)
+    for j in range(p):
+        assert_bits_equal(to_host(recv[j], BF16)[:int(cols_t[j])], expect[j], f"A2Av^T p={p} j={j}")
+
+
+# ----------------------------------------------------------------------------
+# MoE dispatch pack, round trip and weighted combine
+# ----------------------------------------------------------------------------
+
+def _moe_case(p, T, k, H, dtype, seed):
+    toks = gen(p, T * H, dtype, seed)
+    routes = inputs.moe_routes(p, T, k, inputs.WL_TEST, seed)
+    weights = inputs.moe_weights(p, T, k, inputs.WL_TEST, seed)
+    return toks, routes, weights
+
+
+def _i32dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+
+def _f32dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+@pytest.mark.parametrize("p,T,k,H", [(1, 5, 1, 8), (2, 1, 2, 7), (3, 100, 2, 64), (8, 513, 1, 96),
+                                     (8, 257, 8, 40), (16, 64, 3, 33)])
+@pytest.mark.parametrize("dtype", [BF16, F32])
+def test_moe_pack(coll, p, T, k, H, dtype):
+    import torch
+    toks, routes, _ = _moe_case(p, T, k, H, dtype, 50 + T)
+    dtok = [to_dev(x, dtype) for x in toks]
+    ddest = [_i32dev(r) for r in routes]
+    packed = [empty(T * k * H, dtype, fill=0x1111) for _ in range(p)]
+    pos = [torch.full((T * k,), -5, dtype=torch.int32, device="cuda") for _ in range(p)]
+    counts = torch.full((p * p,), -1, dtype=torch.int64, device="cuda")
+    status = torch.full((p,), -9, dtype=torch.int32, device="cuda")
+    coll.coll_moe_pack(dtok, ddest, packed, pos, counts, k, H, status_dev=status)
+    sync()
+    assert status.cpu().tolist() == [0] * p
+    c = counts.cpu().numpy().reshape(p, p)
+    for i in range(p):
+        ec, epos, epk = ref.moe_pack(toks[i], routes[i], k, H, p)
+        assert list(c[i]) == list(ec), f"counts rank {i}"
+        assert pos[i].cpu().numpy().tolist() == epos.tolist(), f"pos rank {i}"
+        assert_bits_equal(to_host(packed[i], dtype), epk, f"packed rank {i}")
+
+
+def test_moe_pack_rejects_bad_destination(coll):
+    import torch
+    p, T, k, H = 4, 33, 2, 16
+    toks, routes, _ = _moe_case(p, T, k, H, F32, 60)
+    routes[2] = routes[2].copy()
+    routes[2][17] = p            # out of range on rank 2 only
+    dtok = [to_dev(x, F32) for x in toks]
+    packed = [empty(T * k * H, F32, fill=0x2222) for _ in range(p)]
+    pos = [torch.zeros(T * k, dtype=torch.int32, device="cuda") for _ in range(p)]
+    counts = torch.zeros(p * p, dtype=torch.int64, device="cuda")
+    status = torch.full((p,), -9, dtype=torch.int32, device="cuda")
+    coll.coll_moe_pack(dtok, [_i32dev(r) for r in routes], packed, pos, counts, k, H, status_dev=status)
+    sync()
+    assert status.cpu().tolist() == [0, 0, 1, 0]
+    c = counts.cpu().numpy().reshape(p, p)
+    assert c[2].tolist() == [0] * p
+    assert pos[2].cpu().numpy().tolist() == [-1] * (T * k)
+    assert torch.equal(packed[2], empty(T * k * H, F32, fill=0x2222)), "payload written for a rejected rank"
+    ec, epos, epk = ref.moe_pack(toks[1], routes[1], k, H, p)
+    assert list(c[1]) == list(ec)
+    assert_bits_equal(to_host(packed[1], F32), epk, "other ranks packed normally")
+
+
+@pytest.mark.parametrize("p,T,k,H", [(2, 50, 1, 24), (4, 301, 2, 40), (8, 128, 8, 17)])
+@pytest.mark.parametrize("dtype", [BF16, F32])
+@pytest.mark.parametrize("with_residual", [False, True])
+def test_moe_round_trip_and_combine(coll, p, T, k, H, dtype, with_residual):
+    """pack -> alltoallv -> (expert compute left out) -> alltoallv_transposed
+    -> combine, every stage against the oracle; the residual case runs in
+    place (out == residual)."""
+    import torch
+    toks, routes, weights = _moe_case(p, T, k, H, dtype, 70 + T + k)
+    dtok = [to_dev(x, dtype) for x in toks]
+    packed = [empty(T * k * H, dtype) for _ in range(p)]
+    pos = [torch.empty(T * k, dtype=torch.int32, device="cuda") for _ in range(p)]
+    counts = torch.empty(p * p, dtype=torch.int64, device="cuda")
+    coll.coll_moe_pack(dtok, [_i32dev(r) for r in routes], packed, pos, counts, k, H)
+    sync()
+    C = counts.cpu().numpy().reshape(p, p)
+    packs = [ref.moe_pack(toks[i], routes[i], k, H, p) for i in range(p)]
+    assert np.array_equal(C, np.stack([pk[0] for pk in packs]))
+    cols = C.sum(axis=0)
+    recv = [empty(int(max(c, 1)), dtype, fill=0) for c in cols]
+    coll.coll_alltoallv(packed, recv, counts, recv_cap=[int(max(c, 1)) for c in cols])
+    back = [empty(T * k * H, dtype, fill=0) for _ in range(p)]
+    coll.coll_alltoallv_transposed(recv, back, counts, send_cap=[int(max(c, 1)) for c in cols])
+    sync()
+    exp_recv = ref.alltoallv([pk[2] for pk in packs], C)
+    for j in range(p):
+        assert_bits_equal(to_host(recv[j], dtype)[:int(cols[j])], exp_recv[j], f"dispatch dest {j}")
+    for i in range(p):
+        assert_bits_equal(to_host(back[i], dtype), packs[i][2], f"returned rows rank {i}")
+    residual = gen(p, T * H, dtype, 80) if with_residual else None
+    out = [to_dev(r, dtype) for r in residual] if with_residual else [empty(T * H, dtype) for _ in range(p)]
+    coll.coll_moe_combine(back, pos, [_f32dev(w) for w in weights], out, k, H,
+                          residual=out if with_residual else None)
+    sync()
+    for i in range(p):
+        expect = ref.moe_combine(packs[i][2], packs[i][1], weights[i], k, H, dtype,
+                                 residual[i] if with_residual else None)
+        assert_bits_equal(to_host(out[i], dtype), expect, f"combine rank {i}")
+
+
+def test_moe_misaligned_rows(coll):
+    """Row length whose bytes are not a multiple of 16 and buffers shifted by
+    one element: vector heads/tails per row and the element path."""
+    import torch
+    p, T, k, H = 3, 40, 2, 13
+    toks, routes, weights = _moe_case(p, T, k, H, BF16, 90)
+    kt, dtok = zip(*[upload_offset(x, BF16, 1) for x in toks])
+    kp, packed = zip(*[upload_offset(np.zeros(T * k * H, np.uint16), BF16, 3) for _ in range(p)])
+    pos = [torch.empty(T * k, dtype=torch.int32, device="cuda") for _ in range(p)]
+    counts = torch.empty(p * p, dtype=torch.int64, device="cuda")
+    coll.coll_moe_pack(list(dtok), [_i32dev(r) for r in routes], list(packed), pos, counts, k, H)
+    sync()
+    for i in range(p):
+        _, epos, epk = ref.moe_pack(toks[i], routes[i], k, H, p)
+        assert_bits_equal(to_host(packed[i], BF16), epk, f"misaligned pack rank {i}")
+    ko, out = zip(*[upload_offset(np.zeros(T * H, np.uint16), BF16, 5) for _ in range(p)])
+    coll.coll_moe_combine(list(packed), pos, [_f32dev(w) for w in weights], list(out), k, H)
+    sync()
+    for i in range(p):
+        _, epos, epk = ref.moe_pack(toks[i], routes[i], k, H, p)
+        expect = ref.moe_combine(epk, epos, weights[i], k, H, BF16)
+        assert_bits_equal(to_host(out[i], BF16), expect, f"misaligned combine rank {i}")
+
+
 # ----------------------------------------------------------------------------
 # Batched AllReduce
 # ----------------------------------------------------------------------------

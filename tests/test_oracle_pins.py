@@ -624,3 +624,72 @@ def test_gather_scatter_adjoint():
         lhs = int(np.dot(ref.gather(xs, 0), y))
         rhs = sum(int(np.dot(x, s)) for x, s in zip(xs, ref.scatter(y, p, 0)))
         assert lhs == rhs
+
+
+# ----------------------------------------------------------------------------
+# MoE dispatch pack and combine ("Collective Communication" page, Ragged
+# All-to-All flow and Expert Parallel section)
+# ----------------------------------------------------------------------------
+
+def _route(rng, p, T, k):
+    return rng.integers(0, p, T * k).astype(np.int32)
+
+
+@pytest.mark.parametrize("p,T,k", [(1, 3, 1), (2, 5, 2), (3, 7, 1), (4, 9, 3), (8, 16, 2)])
+def test_moe_pack_order_and_counts(p, T, k):
+    """The packed order is Python's sorted() by (destination, assignment);
+    counts are the destination histogram times the row length."""
+    rng = np.random.default_rng(p * 100 + T)
+    H = 3
+    tokens = rng.integers(-9, 10, T * H).astype(np.int32)
+    dest = _route(rng, p, T, k)
+    counts, pos, packed = ref.moe_pack(tokens, dest, k, H, p)
+    order = sorted(range(T * k), key=lambda a: (int(dest[a]), a))
+    assert [int(pos[a]) for a in order] == list(range(T * k))
+    assert list(counts) == [H * int((dest == j).sum()) for j in range(p)]
+    for row, a in enumerate(order):
+        t = a // k
+        assert list(packed[row * H:(row + 1) * H]) == list(tokens[t * H:(t + 1) * H])
+
+
+@pytest.mark.parametrize("dtype", [ref.F32, ref.BF16])
+def test_moe_round_trip_is_identity(dtype):
+    """pack -> ragged exchange -> reverse exchange (transposed counts) ->
+    combine with one slot of weight 1 returns every rank's tokens exactly;
+    two slots of weight 1/2 do too (halving and the sum are exact)."""
+    rng = np.random.default_rng(4)
+    p, T, H = 4, 11, 5
+    toks = [(rng.standard_normal(T * H)).astype(np.float32) for _ in range(p)]
+    if dtype == ref.BF16:
+        toks = [(t.view(np.uint32) >> 16).astype(np.uint16) for t in toks]
+    for k, w in ((1, [1.0]), (2, [0.5, 0.5])):
+        routes = [_route(rng, p, T, k) for _ in range(p)]
+        packs = [ref.moe_pack(toks[i], routes[i], k, H, p) for i in range(p)]
+        C = np.stack([pk[0] for pk in packs])
+        recv = ref.alltoallv([pk[2] for pk in packs], C)
+        back = ref.alltoallv(recv, C.T)
+        for i in range(p):
+            assert np.array_equal(back[i], packs[i][2])
+            weights = np.tile(np.array(w, dtype=np.float32), T)
+            out = ref.moe_combine(back[i], packs[i][1], weights, k, H, dtype)
+            assert np.array_equal(_bits(out), _bits(toks[i])), (k, i)
+
+
+def test_moe_combine_against_pure_python():
+    rng = np.random.default_rng(8)
+    T, k, H = 6, 3, 4
+    A = T * k
+    back = rng.standard_normal(A * H).astype(np.float32)
+    pos = rng.permutation(A)
+    w = rng.random(A).astype(np.float32)
+    res = rng.standard_normal(T * H).astype(np.float32)
+    for residual in (None, res):
+        got = ref.moe_combine(back, pos, w, k, H, ref.F32, residual)
+        for t in range(T):
+            for h in range(H):
+                acc = 0.0 if residual is None else float(residual[t * H + h])
+                for s_ in range(k):
+                    a = t * k + s_
+                    prod = struct.unpack("f", struct.pack("f", float(w[a]) * float(back[pos[a] * H + h])))[0]
+                    acc = _py_add_f32(acc, prod)
+                assert got[t * H + h] == np.float32(acc)
