@@ -63,14 +63,23 @@ def parse_args(argv=None):
     return ap.parse_args(argv)
 
 
-def source_hash() -> str:
-    """SHA-256 over the HIP/C++ sources: identifies the kernels a counter summary was taken on."""
+# Sources each timed kernel is built from (its launch code included).
+KERNEL_SOURCES = {
+    "reduce_scatter": ["coll_api.cpp", "kernel_args.h", "device_common.h", "reduce_tile.h", "reduce_kernels.hip"],
+    "allgather": ["coll_api.cpp", "kernel_args.h", "device_common.h", "copy_tile.h", "copy_kernels.hip"],
+}
+
+
+def source_hash(kernel: str | None = None) -> str:
+    """SHA-256 over the sources of one timed kernel (all HIP/C++ sources if
+    kernel is None): identifies the code a counter summary was taken on."""
+    names = KERNEL_SOURCES[kernel] if kernel else sorted(
+        n for n in os.listdir(CSRC) if n.endswith((".hip", ".h", ".cpp")))
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            h.update(name.encode())
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(f.read())
+    for name in names:
+        h.update(name.encode())
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 
@@ -140,14 +149,15 @@ def coll_entry(metrics, name, coll_kind, p, n, d, t_us, algo="ring", extra=None)
 def read_traffic(kernel_key: str, launches_bytes: int):
     """HBM bytes per launch of kernel_key from profiles/hbm_traffic_*.txt.
 
-    The file holds `source_hash:`, `copy_fetch_factor:`, `copy_write_factor:`
-    and per-kernel `kernel <key> fetch_kib <F> write_kib <W>` lines; the
-    factors scale the raw counters by what they read for a plain copy of
-    known size.  Returns None when no summary matches the current sources.
+    The file holds `source_hash_<key>:`, `copy_fetch_factor:`,
+    `copy_write_factor:` and per-kernel `kernel <key> fetch_kib <F>
+    write_kib <W>` lines; the factors scale the raw counters by what they
+    read for a plain copy of known size.  Returns None when no summary
+    matches the kernel's current sources.
     """
     if not os.path.isdir(PROFILES):
         return None
-    cur = source_hash()
+    cur = source_hash(kernel_key)
     for name in sorted(os.listdir(PROFILES)):
         if not (name.startswith("hbm_traffic_") and name.endswith(".txt")):
             continue
@@ -162,7 +172,7 @@ def read_traffic(kernel_key: str, launches_bytes: int):
                 m = re.match(r"^([a-z_]+):\s*(\S+)", line)
                 if m:
                     kv[m.group(1)] = m.group(2)
-        if kv.get("source_hash") != cur or kernel_key not in kern:
+        if kv.get("source_hash_" + kernel_key) != cur or kernel_key not in kern:
             continue
         ff = float(kv.get("copy_fetch_factor", "1"))
         wf = float(kv.get("copy_write_factor", "1"))
@@ -581,7 +591,7 @@ def main(argv=None) -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
         "collectives": rows,
-        "source_hash": source_hash(),
+        "source_hash": {k: source_hash(k) for k in KERNEL_SOURCES},
     }
     print(json.dumps(line), flush=True)
     return 0
