@@ -17,7 +17,7 @@ from typing import Any, Sequence
 
 # Enum values of coll.h
 COLL_F32, COLL_BF16, COLL_I32 = 0, 1, 2
-COLL_SUM, COLL_MIN, COLL_MAX = 0, 1, 2
+COLL_SUM, COLL_MIN, COLL_MAX, COLL_AVG = 0, 1, 2, 3
 COLL_OK, COLL_ERR_INVALID_ARG, COLL_ERR_UNSUPPORTED, COLL_ERR_ALIAS, COLL_ERR_HIP = 0, 1, 2, 3, 4
 COLL_ALGO_RING, COLL_ALGO_ONEPASS, COLL_ALGO_RING_LITERAL, COLL_ALGO_HALVING_DOUBLING = 0, 1, 2, 3
 COLL_ALGO_RECURSIVE_DOUBLING = COLL_ALGO_ONEPASS
@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
         "coll_alltoall": [pp, pp, i32, sz, i32, vp],
         "coll_alltoallv": [pp, pp, i32, vp, i64p, i64p, vp, i32, vp],
         "coll_gather": [pp, vp, i32, sz, i32, i32, vp],
+        "coll_allreduce_premul": [pp, pp, i32, sz, i32, ctypes.POINTER(ctypes.c_float), i32, vp],
+        "coll_reduce_scatter_premul": [pp, pp, i32, sz, i32, ctypes.POINTER(ctypes.c_float), vp],
         "coll_alltoallv_transposed": [pp, pp, i32, vp, i64p, i64p, vp, i32, vp],
         "coll_moe_pack": [pp, pp, pp, pp, vp, vp, i32, sz, i32, sz, i32, vp],
         "coll_moe_combine": [pp, pp, pp, pp, pp, i32, sz, i32, sz, i32, vp],
@@ -209,6 +211,41 @@ def coll_allreduce_algo(send, recv, algo: int, op: int = COLL_SUM, n: int | None
     r, k2 = _ptr_array(recv)
     return _run("coll_allreduce_algo", (s, r, p, n, dt, int(op), int(algo), _stream(stream)),
                 "coll_allreduce", defer, (k1, k2))
+
+
+def coll_allreduce_premul(send, recv, scale: Sequence[float], algo: int = COLL_ALGO_RING, n: int | None = None,
+                          dtype: int | None = None, stream=None, defer: bool = False):
+    """recv[r] = sum_k scale[k] * send[k] (fp32 products rounded on their own)."""
+    p = len(send)
+    if len(recv) != p or len(scale) != p:
+        raise ValueError("send, recv and scale must list the same ranks")
+    dt = _dtype_of(send[0], dtype)
+    n = _numel(send[0], n)
+    _same_dtype([*send, *recv], dt)
+    _check_sizes([*send, *recv], n, "allreduce_premul")
+    s, k1 = _ptr_array(send)
+    r, k2 = _ptr_array(recv)
+    sc = (ctypes.c_float * p)(*[float(v) for v in scale])
+    return _run("coll_allreduce_premul", (s, r, p, n, dt, sc, int(algo), _stream(stream)),
+                "coll_allreduce_premul", defer, (k1, k2, sc))
+
+
+def coll_reduce_scatter_premul(send, recv, scale: Sequence[float], n: int | None = None, dtype: int | None = None,
+                               stream=None, defer: bool = False):
+    """ReduceScatter of sum_k scale[k] * send[k]; n = elements each rank receives."""
+    p = len(send)
+    if len(scale) != p:
+        raise ValueError("one scale per rank")
+    dt = _dtype_of(send[0], dtype)
+    n = _numel(recv[0], n)
+    _same_dtype([*send, *recv], dt)
+    _check_sizes(send, p * n, "reduce_scatter_premul send")
+    _check_sizes(recv, n, "reduce_scatter_premul recv")
+    s, k1 = _ptr_array(send)
+    r, k2 = _ptr_array(recv)
+    sc = (ctypes.c_float * p)(*[float(v) for v in scale])
+    return _run("coll_reduce_scatter_premul", (s, r, p, n, dt, sc, _stream(stream)),
+                "coll_reduce_scatter_premul", defer, (k1, k2, sc))
 
 
 def coll_reduce(send, recv_root, root: int, op: int = COLL_SUM, n: int | None = None,

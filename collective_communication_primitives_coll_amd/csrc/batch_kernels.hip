@@ -42,6 +42,7 @@ __device__ __forceinline__ void batch_run(const BatchCall& bc, const void* const
   constexpr int V = T::V;
   const uint64_t tpc = bc.tiles_per_chunk;
   const uint64_t q = (bc.n + P - 1) / P;
+  const Scales<P> sc{};  // unused: the batch has no pre-multiplied sums
   int c = (int)(from / tpc);
   uint64_t t = from - (uint64_t)c * tpc;
   uint64_t left = to - from;
@@ -66,7 +67,8 @@ __device__ __forceinline__ void batch_run(const BatchCall& bc, const void* const
           const uint64_t e0 = i * TV * V;
           if (e0 < len)
             reduce_elems<DT, OP, P, kOrdRing, P, true, kWave>(src, dst, e0,
-                                                          (len - e0) < TV * V ? (len - e0) : TV * V, lane);
+                                                          (len - e0) < TV * V ? (len - e0) : TV * V, sc, P,
+                                                          lane);
         }
       } else {
         const S* vs[P];
@@ -79,13 +81,16 @@ __device__ __forceinline__ void batch_run(const BatchCall& bc, const void* const
         const uint64_t nfull = sp.nvec / TV;
         for (uint64_t i = t; i < t + cnt; ++i) {
           const uint64_t j0 = i * TV + lane;
-          if (i < nfull) reduce_vec_tile<DT, OP, P, kOrdRing, P, true, U, true, kWave>(vs, vd, j0, sp.nvec);
-          else if (i * TV < sp.nvec) reduce_vec_tile<DT, OP, P, kOrdRing, P, true, U, false, kWave>(vs, vd, j0, sp.nvec);
+          if (i < nfull)
+            reduce_vec_tile<DT, OP, P, kOrdRing, P, true, U, true, kWave>(vs, vd, j0, sp.nvec, sc, P);
+          else if (i * TV < sp.nvec)
+            reduce_vec_tile<DT, OP, P, kOrdRing, P, true, U, false, kWave>(vs, vd, j0, sp.nvec, sc, P);
         }
         if (t == 0) {
-          if (sp.head) reduce_elems<DT, OP, P, kOrdRing, P, true, kWave>(src, dst, 0, sp.head, lane);
+          if (sp.head) reduce_elems<DT, OP, P, kOrdRing, P, true, kWave>(src, dst, 0, sp.head, sc, P, lane);
           if (sp.tail)
-            reduce_elems<DT, OP, P, kOrdRing, P, true, kWave>(src, dst, sp.head + sp.nvec * V, sp.tail, lane);
+            reduce_elems<DT, OP, P, kOrdRing, P, true, kWave>(src, dst, sp.head + sp.nvec * V, sp.tail, sc, P,
+                                                              lane);
         }
       }
     }
@@ -116,7 +121,7 @@ __device__ __forceinline__ void batch_run_any(const BatchCall& bc, const void* c
       A acc = widen1<DT>(ld1<true>((const S*)pt[(c + 1) % p] + lo + e));
       for (int k = 1; k < p; ++k)
         acc = combine<OP>(acc, widen1<DT>(ld1<true>((const S*)pt[(c + 1 + k) % p] + lo + e)));
-      const S out = narrow1<DT>(acc);
+      const S out = narrow1<DT>(finish<OP>(acc, p));
       for (int k = 0; k < p; ++k) st1<true>((S*)pt[p + k] + lo + e, out);
     }
   }
@@ -126,20 +131,23 @@ template <int P>
 __device__ __forceinline__ void batch_dispatch(const BatchCall& bc, const void* const* pt, int p, uint64_t from,
                                                uint64_t to, int lane) {
 #define COLL_BATCH_CASE(DTV, OPV)                                          \
-  case DTV * 3 + OPV:                                                      \
+  case DTV * 4 + OPV:                                                      \
     if constexpr (P > 0) batch_run<DTV, OPV, P>(bc, pt, from, to, lane);   \
     else batch_run_any<DTV, OPV>(bc, pt, p, from, to, lane);               \
     break;
-  switch (bc.dtype * 3 + bc.op) {
+  switch (bc.dtype * 4 + bc.op) {
     COLL_BATCH_CASE(kF32, kSum)
     COLL_BATCH_CASE(kF32, kMin)
     COLL_BATCH_CASE(kF32, kMax)
+    COLL_BATCH_CASE(kF32, kAvg)
     COLL_BATCH_CASE(kBF16, kSum)
     COLL_BATCH_CASE(kBF16, kMin)
     COLL_BATCH_CASE(kBF16, kMax)
+    COLL_BATCH_CASE(kBF16, kAvg)
     COLL_BATCH_CASE(kI32, kSum)
     COLL_BATCH_CASE(kI32, kMin)
     COLL_BATCH_CASE(kI32, kMax)
+    COLL_BATCH_CASE(kI32, kAvg)
     default: break;
   }
 #undef COLL_BATCH_CASE

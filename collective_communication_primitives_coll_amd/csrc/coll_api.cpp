@@ -81,7 +81,7 @@ int max_grid(int* out, Family fam) {
 // Argument checks
 // ---------------------------------------------------------------------------
 bool dtype_ok(int d) { return d == COLL_F32 || d == COLL_BF16 || d == COLL_I32; }
-bool op_ok(int o) { return o == COLL_SUM || o == COLL_MIN || o == COLL_MAX; }
+bool op_ok(int o) { return o == COLL_SUM || o == COLL_MIN || o == COLL_MAX || o == COLL_AVG; }
 size_t dsize(int d) { return d == COLL_BF16 ? 2 : 4; }
 
 // bytes = a * b * c without overflow, and below 2^62 so that every derived
@@ -241,6 +241,35 @@ COLL_EXPORT coll_status_t coll_allreduce(const void* const* send, void* const* r
   return coll_allreduce_algo(send, recv, p, n, dtype, op, COLL_ALGO_RING, stream);
 }
 
+COLL_EXPORT coll_status_t coll_allreduce_premul(const void* const* send, void* const* recv, int p, size_t n,
+                                                coll_dtype_t dtype, const float* scale, coll_algo_t algo,
+                                                void* stream) {
+  if ((int)algo < COLL_ALGO_RING || (int)algo > COLL_ALGO_HALVING_DOUBLING) return COLL_ERR_INVALID_ARG;
+  coll_status_t st = check_allreduce(send, recv, p, n, dtype, COLL_SUM);
+  if (st != COLL_OK) return st;
+  if (!scale) return COLL_ERR_INVALID_ARG;
+  if (n == 0) return COLL_OK;
+  if (dtype == COLL_I32 || algo == COLL_ALGO_RING_LITERAL) return COLL_ERR_UNSUPPORTED;
+  const bool tree_algo = algo == COLL_ALGO_RECURSIVE_DOUBLING || algo == COLL_ALGO_HALVING_DOUBLING;
+  if (tree_algo && !(p == 2 || p == 4 || p == 8 || p == 16)) return COLL_ERR_UNSUPPORTED;
+  int grid;
+  int e = max_grid(&grid, kFamReduce);
+  if (e) return hip_fail(e);
+  coll::RankPtrs P = make_ptrs(send, p, recv, p);
+  coll::ReduceGeom g{};
+  g.stride = (n + p - 1) / p;
+  g.total = n;
+  g.p = p;
+  g.dst_mode = coll::kDstAll;
+  g.src_mis = common_mis(send, p);
+  g.dst_mis = common_mis((const void* const*)recv, p);
+  for (int r = 0; r < p; ++r) g.scale[r] = scale[r];
+  const int order = algo == COLL_ALGO_RECURSIVE_DOUBLING ? coll::kOrdRD
+                    : algo == COLL_ALGO_HALVING_DOUBLING  ? coll::kOrdHD
+                                                          : coll::kOrdRing;
+  return finish(coll::launch_reduce(dtype, coll::kPreMul, order, P, g, grid, stream));
+}
+
 COLL_EXPORT coll_status_t coll_reduce(const void* const* send, void* recv_root, int p, size_t n,
                                       coll_dtype_t dtype, coll_op_t op, int root, void* stream) {
   if (p < 1 || p > kMaxRanks || !dtype_ok(dtype) || !op_ok(op) || root < 0 || root >= p)
@@ -299,9 +328,10 @@ COLL_EXPORT coll_status_t coll_broadcast(const void* send_root, void* const* rec
   return finish(coll::launch_copy((int)dsize(dtype), P, g, grid, stream));
 }
 
-COLL_EXPORT coll_status_t coll_reduce_scatter(const void* const* send, void* const* recv, int p, size_t n,
-                                              coll_dtype_t dtype, coll_op_t op, void* stream) {
-  if (p < 1 || p > kMaxRanks || !dtype_ok(dtype) || !op_ok(op)) return COLL_ERR_INVALID_ARG;
+namespace {
+coll_status_t reduce_scatter_impl(const void* const* send, void* const* recv, int p, size_t n, coll_dtype_t dtype,
+                                  int op, const float* scale, void* stream) {
+  if (p < 1 || p > kMaxRanks || !dtype_ok(dtype) || !(op_ok(op) || op == coll::kPreMul)) return COLL_ERR_INVALID_ARG;
   if (n == 0) return COLL_OK;
   size_t bytes;
   if (!mul_ok(n, dsize(dtype), (size_t)p * p, &bytes)) return COLL_ERR_INVALID_ARG;
@@ -327,7 +357,24 @@ COLL_EXPORT coll_status_t coll_reduce_scatter(const void* const* send, void* con
   g.dst_mode = coll::kDstOwner;
   g.src_mis = common_mis(send, p);
   g.dst_mis = common_mis((const void* const*)recv, p);
+  if (scale)
+    for (int r = 0; r < p; ++r) g.scale[r] = scale[r];
   return finish(coll::launch_reduce(dtype, op, coll::kOrdRing, P, g, grid, stream));
+}
+}  // namespace
+
+COLL_EXPORT coll_status_t coll_reduce_scatter(const void* const* send, void* const* recv, int p, size_t n,
+                                              coll_dtype_t dtype, coll_op_t op, void* stream) {
+  if (!op_ok(op)) return COLL_ERR_INVALID_ARG;
+  return reduce_scatter_impl(send, recv, p, n, dtype, op, nullptr, stream);
+}
+
+COLL_EXPORT coll_status_t coll_reduce_scatter_premul(const void* const* send, void* const* recv, int p,
+                                                     size_t n, coll_dtype_t dtype, const float* scale,
+                                                     void* stream) {
+  if (p < 1 || p > kMaxRanks || !dtype_ok(dtype) || !scale) return COLL_ERR_INVALID_ARG;
+  if (dtype == COLL_I32) return COLL_ERR_UNSUPPORTED;
+  return reduce_scatter_impl(send, recv, p, n, dtype, coll::kPreMul, scale, stream);
 }
 
 COLL_EXPORT coll_status_t coll_allgather(const void* const* send, void* const* recv, int p, size_t n,

@@ -137,11 +137,11 @@ __device__ __forceinline__ typename Traits<DT>::S narrow1(typename Traits<DT>::A
 
 // ---------------------------------------------------------------------------
 // The elementwise operation.  acc is the running partial, v the next
-// rank's value; min/max keep acc on ties.
+// rank's value; min/max keep acc on ties; avg and pre-multiplied sums add.
 // ---------------------------------------------------------------------------
 template <int OP, typename A>
 __device__ __forceinline__ A combine(A acc, A v) {
-  if constexpr (OP == kSum) return acc + v;
+  if constexpr (OP == kSum || OP == kAvg || OP == kPreMul) return acc + v;
   else if constexpr (OP == kMin) return (v < acc) ? v : acc;
   else return (v > acc) ? v : acc;
 }

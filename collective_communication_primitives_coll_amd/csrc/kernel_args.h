@@ -19,7 +19,9 @@ enum Order : int {
   kOrdRD = 1,    // balanced tree pairing ranks (0,1), (2,3), ... first (recursive doubling)
   kOrdHD = 2     // balanced tree pairing ranks (k, k + p/2) first (halving-doubling)
 };
-enum Op : int { kSum = 0, kMin = 1, kMax = 2 };
+// Reductions.  kAvg: the sum, then divided by the rank count; kPreMul:
+// every operand times its rank's scale, then the sum.
+enum Op : int { kSum = 0, kMin = 1, kMax = 2, kAvg = 3, kPreMul = 4 };
 
 // Destination selection of the reduction kernels.
 enum DstMode : int {
@@ -42,6 +44,7 @@ struct ReduceGeom {
   int dst_mode;
   int src_mis;  // common byte misalignment of the source bases, or -1
   int dst_mis;  // common byte misalignment of the destination bases, or -1
+  float scale[kMaxRanks];  // kPreMul: scale of rank r's operand
 };
 
 // Copy kinds.
@@ -107,7 +110,7 @@ struct RingStepGeom {
   uint64_t q;    // chunk length ceil(n/p)
   int p;
   int phase;     // 0 reduce-scatter, 1 all-gather
-  int step;      // 1..p-1
+  int step;      // 1..p-1 (kAvg divides by p in the last reduce-scatter step)
   int mis;       // common misalignment of all send and recv bases, or -1
 };
 

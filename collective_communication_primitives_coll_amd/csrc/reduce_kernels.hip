@@ -51,8 +51,11 @@ COLL_STREAM_KERNEL void reduce_kernel(RankPtrs ptrs, ReduceGeom g) {
     } else {
       dst[0] = (S*)ptrs.dst[0] + lo;
     }
+    Scales<P> sc;
+#pragma unroll
+    for (int k = 0; k < P; ++k) sc.s[k] = OP == kPreMul ? g.scale[ORD != kOrdRing ? k : (c + 1 + k) % P] : 1.0f;
     const int mis = seg_mis(g.src_mis, g.dst_mis, lo * T::B, doff * T::B);
-    base += reduce_segment<DT, OP, P, ORD, ND, ALL>(src, dst, len, mis, base);
+    base += reduce_segment<DT, OP, P, ORD, ND, ALL>(src, dst, len, mis, base, sc, P);
   }
 }
 
@@ -60,6 +63,7 @@ COLL_STREAM_KERNEL void reduce_kernel(RankPtrs ptrs, ReduceGeom g) {
 // operands in groups of 8 loads, pointers read from the kernel arguments.
 template <int DT, int OP, int DMODE>
 COLL_STREAM_KERNEL void reduce_kernel_any(RankPtrs ptrs, ReduceGeom g) {
+#pragma clang fp contract(off)
   using T = Traits<DT>;
   using S = typename T::S;
   using A = typename T::A;
@@ -81,12 +85,19 @@ COLL_STREAM_KERNEL void reduce_kernel_any(RankPtrs ptrs, ReduceGeom g) {
     };
     const int nd = ALL ? p : 1;
     const SegSpan sp = seg_span<T::B>(len, seg_mis(g.src_mis, g.dst_mis, lo * T::B, doff * T::B));
+    auto scale_of = [&](int k) -> float { return g.scale[(c + 1 + k) % p]; };
     auto elems = [&](uint64_t from, uint64_t cnt) {
+#pragma clang fp contract(off)
       for (uint64_t i = threadIdx.x; i < cnt; i += kBlock) {
         const uint64_t e = from + i;
         A acc = widen1<DT>(ld1<true>(sp_src(0) + e));
-        for (int k = 1; k < p; ++k) acc = combine<OP>(acc, widen1<DT>(ld1<true>(sp_src(k) + e)));
-        const auto out = narrow1<DT>(acc);
+        if constexpr (OP == kPreMul) acc = scale_of(0) * acc;
+        for (int k = 1; k < p; ++k) {
+          A v = widen1<DT>(ld1<true>(sp_src(k) + e));
+          if constexpr (OP == kPreMul) v = scale_of(k) * v;
+          acc = combine<OP>(acc, v);
+        }
+        const auto out = narrow1<DT>(finish<OP>(acc, p));
         for (int d = 0; d < nd; ++d) st1<ALL>(sp_dst(d) + e, out);
       }
     };
@@ -107,6 +118,10 @@ COLL_STREAM_KERNEL void reduce_kernel_any(RankPtrs ptrs, ReduceGeom g) {
       const uint64_t e = sp.head + j * V;
       A acc[V];
       widen<DT>(ld16<true>(sp_src(0) + e), acc);
+      if constexpr (OP == kPreMul) {
+#pragma unroll
+        for (int x = 0; x < V; ++x) acc[x] = scale_of(0) * acc[x];
+      }
       for (int k0 = 1; k0 < p; k0 += 8) {
         u32x4 r[8];
 #pragma unroll
@@ -117,9 +132,15 @@ COLL_STREAM_KERNEL void reduce_kernel_any(RankPtrs ptrs, ReduceGeom g) {
           if (k0 + q < p) {
             A t2[V];
             widen<DT>(r[q], t2);
+            if constexpr (OP == kPreMul) {
+#pragma unroll
+              for (int x = 0; x < V; ++x) t2[x] = scale_of(k0 + q) * t2[x];
+            }
             combine_vec<OP, DT>(acc, t2);
           }
       }
+#pragma unroll
+      for (int x = 0; x < V; ++x) acc[x] = finish<OP>(acc[x], p);
       const u32x4 out = narrow<DT>(acc);
       for (int d = 0; d < nd; ++d) st16<ALL>(sp_dst(d) + e, out);
     }
@@ -189,9 +210,9 @@ static int launch_any(const RankPtrs& ptrs, const ReduceGeom& g, int max_grid, h
   return (int)hipGetLastError();
 }
 
-// Tree orders only change the result of floating-point sums; integer sums
-// and min/max give the same bits in any order, so they always run the
-// ring-order kernel.
+// Tree orders only change the result of floating-point sums (plain,
+// averaged or pre-multiplied); integer sums and min/max give the same bits
+// in any order, so they always run the ring-order kernel.
 template <int DT, int OP, int ORD>
 static int launch_tree(const RankPtrs& ptrs, const ReduceGeom& g, int max_grid, hipStream_t s) {
   switch (g.p) {
@@ -205,7 +226,7 @@ static int launch_tree(const RankPtrs& ptrs, const ReduceGeom& g, int max_grid, 
 
 template <int DT, int OP>
 static int launch_dt_op(int order, const RankPtrs& ptrs, const ReduceGeom& g, int max_grid, hipStream_t s) {
-  if constexpr ((DT == kF32 || DT == kBF16) && OP == kSum) {
+  if constexpr ((DT == kF32 || DT == kBF16) && (OP == kSum || OP == kAvg || OP == kPreMul)) {
     if (order == kOrdRD) return launch_tree<DT, OP, kOrdRD>(ptrs, g, max_grid, s);
     if (order == kOrdHD) return launch_tree<DT, OP, kOrdHD>(ptrs, g, max_grid, s);
   }
@@ -225,6 +246,10 @@ static int launch_dt(int op, int order, const RankPtrs& ptrs, const ReduceGeom& 
     case kSum: return launch_dt_op<DT, kSum>(order, ptrs, g, max_grid, s);
     case kMin: return launch_dt_op<DT, kMin>(order, ptrs, g, max_grid, s);
     case kMax: return launch_dt_op<DT, kMax>(order, ptrs, g, max_grid, s);
+    case kAvg: return launch_dt_op<DT, kAvg>(order, ptrs, g, max_grid, s);
+    case kPreMul:
+      if constexpr (DT != kI32) return launch_dt_op<DT, kPreMul>(order, ptrs, g, max_grid, s);
+      break;
   }
   return (int)hipErrorInvalidValue;
 }

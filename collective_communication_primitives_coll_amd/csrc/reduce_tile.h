@@ -30,16 +30,45 @@ struct ReduceUnroll {
   static constexpr int value = raw < 1 ? 1 : (raw > 8 ? 8 : raw);
 };
 
+// Per-operand scales of a pre-multiplied sum, in the order the operands
+// are listed.
+template <int P>
+struct Scales {
+  float s[P];
+};
+
+// Operand k widened (and scaled by its rank's factor for kPreMul, the
+// product rounded to fp32 on its own).
+template <int DT, int OP, int P>
+__device__ __forceinline__ void operand(u32x4 r, const Scales<P>& sc, int k,
+                                        typename Traits<DT>::A (&a)[Traits<DT>::V]) {
+#pragma clang fp contract(off)
+  widen<DT>(r, a);
+  if constexpr (OP == kPreMul) {
+#pragma unroll
+    for (int x = 0; x < Traits<DT>::V; ++x) a[x] = sc.s[k] * a[x];
+  }
+}
+
+// After the fold: kAvg divides by the rank count p (one IEEE division for
+// floats, C division for int32).
+template <int OP, typename A>
+__device__ __forceinline__ A finish(A acc, int p) {
+  if constexpr (OP == kAvg) return acc / (A)p;
+  else return acc;
+}
+
 // Fold of P operands, in list order or as one of the trees.
 template <int DT, int OP, int P, int ORD>
-__device__ __forceinline__ u32x4 fold_vectors(const u32x4 (&r)[P]) {
+__device__ __forceinline__ u32x4 fold_vectors(const u32x4 (&r)[P], const Scales<P>& sc, int avg_p) {
+#pragma clang fp contract(off)
   using A = typename Traits<DT>::A;
   constexpr int V = Traits<DT>::V;
   A acc[V];
   if constexpr (ORD == kOrdRD) {
     A a[P][V];
 #pragma unroll
-    for (int k = 0; k < P; ++k) widen<DT>(r[k], a[k]);
+    for (int k = 0; k < P; ++k) operand<DT, OP, P>(r[k], sc, k, a[k]);
 #pragma unroll
     for (int st = 1; st < P; st *= 2)
 #pragma unroll
@@ -49,7 +78,7 @@ __device__ __forceinline__ u32x4 fold_vectors(const u32x4 (&r)[P]) {
   } else if constexpr (ORD == kOrdHD) {
     A a[P][V];
 #pragma unroll
-    for (int k = 0; k < P; ++k) widen<DT>(r[k], a[k]);
+    for (int k = 0; k < P; ++k) operand<DT, OP, P>(r[k], sc, k, a[k]);
 #pragma unroll
     for (int st = P / 2; st >= 1; st /= 2)
 #pragma unroll
@@ -57,14 +86,16 @@ __device__ __forceinline__ u32x4 fold_vectors(const u32x4 (&r)[P]) {
 #pragma unroll
     for (int x = 0; x < V; ++x) acc[x] = a[0][x];
   } else {
-    widen<DT>(r[0], acc);
+    operand<DT, OP, P>(r[0], sc, 0, acc);
 #pragma unroll
     for (int k = 1; k < P; ++k) {
       A t[V];
-      widen<DT>(r[k], t);
+      operand<DT, OP, P>(r[k], sc, k, t);
       combine_vec<OP, DT>(acc, t);
     }
   }
+#pragma unroll
+  for (int x = 0; x < V; ++x) acc[x] = finish<OP>(acc[x], avg_p);
   return narrow<DT>(acc);
 }
 
@@ -75,7 +106,8 @@ __device__ __forceinline__ u32x4 fold_vectors(const u32x4 (&r)[P]) {
 template <int DT, int OP, int P, int ORD, int ND, bool NTS, int U, bool FULL, int LANES = kBlock>
 __device__ __forceinline__ void reduce_vec_tile(const typename Traits<DT>::S* const (&src)[P],
                                                 typename Traits<DT>::S* const (&dst)[ND],
-                                                uint64_t j0, uint64_t nvec) {
+                                                uint64_t j0, uint64_t nvec, const Scales<P>& sc,
+                                                int avg_p) {
   constexpr int V = Traits<DT>::V;
   u32x4 raw[U][P];
 #pragma unroll
@@ -88,7 +120,7 @@ __device__ __forceinline__ void reduce_vec_tile(const typename Traits<DT>::S* co
     }
   u32x4 out[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) out[u] = fold_vectors<DT, OP, P, ORD>(raw[u]);
+  for (int u = 0; u < U; ++u) out[u] = fold_vectors<DT, OP, P, ORD>(raw[u], sc, avg_p);
 #pragma unroll
   for (int d = 0; d < ND; ++d)
 #pragma unroll
@@ -104,14 +136,18 @@ __device__ __forceinline__ void reduce_vec_tile(const typename Traits<DT>::S* co
 template <int DT, int OP, int P, int ORD, int ND, bool NTS, int LANES = kBlock>
 __device__ __forceinline__ void reduce_elems(const typename Traits<DT>::S* const (&src)[P],
                                              typename Traits<DT>::S* const (&dst)[ND], uint64_t from,
-                                             uint64_t cnt, int lane = -1) {
+                                             uint64_t cnt, const Scales<P>& sc, int avg_p, int lane = -1) {
+#pragma clang fp contract(off)
   using A = typename Traits<DT>::A;
   const uint64_t l0 = lane < 0 ? threadIdx.x : (uint64_t)lane;
   for (uint64_t i = l0; i < cnt; i += LANES) {
     const uint64_t e = from + i;
     A a[P];
 #pragma unroll
-    for (int k = 0; k < P; ++k) a[k] = widen1<DT>(ld1<true>(src[k] + e));
+    for (int k = 0; k < P; ++k) {
+      a[k] = widen1<DT>(ld1<true>(src[k] + e));
+      if constexpr (OP == kPreMul) a[k] = sc.s[k] * a[k];
+    }
     A acc;
     if constexpr (ORD == kOrdRD) {
 #pragma unroll
@@ -130,7 +166,7 @@ __device__ __forceinline__ void reduce_elems(const typename Traits<DT>::S* const
 #pragma unroll
       for (int k = 1; k < P; ++k) acc = combine<OP>(acc, a[k]);
     }
-    const auto out = narrow1<DT>(acc);
+    const auto out = narrow1<DT>(finish<OP>(acc, avg_p));
 #pragma unroll
     for (int d = 0; d < ND; ++d) st1<NTS>(dst[d] + e, out);
   }
@@ -143,7 +179,8 @@ __device__ __forceinline__ void reduce_elems(const typename Traits<DT>::S* const
 template <int DT, int OP, int P, int ORD, int ND, bool NTS>
 __device__ __forceinline__ uint64_t reduce_segment(const typename Traits<DT>::S* const (&src)[P],
                                                    typename Traits<DT>::S* const (&dst)[ND],
-                                                   uint64_t len, int mis, uint64_t base) {
+                                                   uint64_t len, int mis, uint64_t base, const Scales<P>& sc,
+                                                   int avg_p) {
   using S = typename Traits<DT>::S;
   constexpr int V = Traits<DT>::V;
   constexpr int U = ReduceUnroll<P, (ND > 1)>::value;
@@ -157,7 +194,7 @@ __device__ __forceinline__ uint64_t reduce_segment(const typename Traits<DT>::S*
     for (uint64_t t = first_tile(base, wg, grid); t < nt; t += grid) {
       const uint64_t from = t * TE;
       const uint64_t cnt = (len - from) < TE ? (len - from) : TE;
-      reduce_elems<DT, OP, P, ORD, ND, NTS>(src, dst, from, cnt);
+      reduce_elems<DT, OP, P, ORD, ND, NTS>(src, dst, from, cnt, sc, avg_p);
     }
     return nt;
   }
@@ -172,13 +209,13 @@ __device__ __forceinline__ uint64_t reduce_segment(const typename Traits<DT>::S*
     const uint64_t nfull = sp.nvec / TV;
     for (uint64_t t = first_tile(base, wg, grid); t < nt; t += grid) {
       const uint64_t j0 = t * TV + threadIdx.x;
-      if (t < nfull) reduce_vec_tile<DT, OP, P, ORD, ND, NTS, U, true>(vs, vd, j0, sp.nvec);
-      else reduce_vec_tile<DT, OP, P, ORD, ND, NTS, U, false>(vs, vd, j0, sp.nvec);
+      if (t < nfull) reduce_vec_tile<DT, OP, P, ORD, ND, NTS, U, true>(vs, vd, j0, sp.nvec, sc, avg_p);
+      else reduce_vec_tile<DT, OP, P, ORD, ND, NTS, U, false>(vs, vd, j0, sp.nvec, sc, avg_p);
     }
   }
   if ((sp.head || sp.tail) && first_tile(base, wg, grid) == 0) {
-    if (sp.head) reduce_elems<DT, OP, P, ORD, ND, NTS>(src, dst, 0, sp.head);
-    if (sp.tail) reduce_elems<DT, OP, P, ORD, ND, NTS>(src, dst, sp.head + sp.nvec * V, sp.tail);
+    if (sp.head) reduce_elems<DT, OP, P, ORD, ND, NTS>(src, dst, 0, sp.head, sc, avg_p);
+    if (sp.tail) reduce_elems<DT, OP, P, ORD, ND, NTS>(src, dst, sp.head + sp.nvec * V, sp.tail, sc, avg_p);
   }
   return nt;
 }

@@ -38,10 +38,15 @@ COLL_STREAM_KERNEL void ring_step_kernel(RankPtrs ptrs, RingStepGeom g) {
     const S* partial = (g.phase == 0 && g.step == 1) ? (const S*)ptrs.src[x] + lo : (const S*)ptrs.dst[x] + lo;
     S* d = (S*)ptrs.dst[nxt] + lo;
     if (g.phase == 0) {
-      // received partial on the left, the receiver's own input on the right
+      // received partial on the left, the receiver's own input on the right;
+      // an average is a sum until the last step, which divides by p
       const S* src[2] = {partial, (const S*)ptrs.src[nxt] + lo};
       S* dst[1] = {d};
-      base += reduce_segment<DT, OP, 2, kOrdRing, 1, false>(src, dst, len, mis, base);
+      const Scales<2> sc{};
+      if (OP == kAvg && g.step == p - 1)
+        base += reduce_segment<DT, kAvg, 2, kOrdRing, 1, false>(src, dst, len, mis, base, sc, p);
+      else
+        base += reduce_segment<DT, OP == kAvg ? kSum : OP, 2, kOrdRing, 1, false>(src, dst, len, mis, base, sc, p);
     } else {
       using W = typename Word<T::B>::T;
       auto gdst = [&](int) -> W* { return (W*)d; };
@@ -61,6 +66,9 @@ static int launch_dt(int op, const RankPtrs& ptrs, const RingStepGeom& g, int gr
       break;
     case kMax:
       hipLaunchKernelGGL((ring_step_kernel<DT, kMax>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
+      break;
+    case kAvg:
+      hipLaunchKernelGGL((ring_step_kernel<DT, kAvg>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
       break;
     default:
       return (int)hipErrorInvalidValue;

@@ -57,8 +57,12 @@ extern "C" {
  * round-to-nearest-even. */
 typedef enum { COLL_F32 = 0, COLL_BF16 = 1, COLL_I32 = 2 } coll_dtype_t;
 
-/* Elementwise reduction ([A] preamble: + is sum, min or max). */
-typedef enum { COLL_SUM = 0, COLL_MIN = 1, COLL_MAX = 2 } coll_op_t;
+/* Elementwise reduction ([A] preamble: + is sum, min or max).
+ * COLL_AVG: the sum in the schedule's order, then divided by p ([A] 1.4:
+ * older NCCL had no average, callers summed and divided by the world
+ * size): one IEEE fp32 division (bf16 narrowed after it), and for int32 C
+ * division of the wrapped sum, truncating toward zero. */
+typedef enum { COLL_SUM = 0, COLL_MIN = 1, COLL_MAX = 2, COLL_AVG = 3 } coll_op_t;
 
 typedef enum {
   COLL_OK = 0,
@@ -111,6 +115,17 @@ coll_status_t coll_allreduce_algo(const void* const* send, void* const* recv, in
                                   coll_dtype_t dtype, coll_op_t op, coll_algo_t algo,
                                   void* stream);
 
+/* Pre-multiplied AllReduce ([B] numerics: NCCL's PreMulSum, the one
+ * constrained custom reduction): recv[r][i] = sum_k scale[k] * send[k][i],
+ * each operand multiplied by its rank's scale in fp32 and rounded on its
+ * own, then summed in the order of `algo` (RING, RECURSIVE_DOUBLING or
+ * HALVING_DOUBLING).  scale: HOST array of p floats.  fp32 and bf16 only
+ * (COLL_ERR_UNSUPPORTED for int32 and RING_LITERAL).  In place as
+ * coll_allreduce.  scale = 1/p for every rank is the average of DDP. */
+coll_status_t coll_allreduce_premul(const void* const* send, void* const* recv, int p, size_t n,
+                                    coll_dtype_t dtype, const float* scale, coll_algo_t algo,
+                                    void* stream);
+
 /* Reduce ([A] 1.3 with its worked example): recv_root[i] = (+)_r send[r][i];
  * only the root's buffer is written.  Same summation order as
  * coll_allreduce, so Reduce then Broadcast equals AllReduce bit for bit.
@@ -128,6 +143,12 @@ coll_status_t coll_broadcast(const void* send_root, void* const* recv, int p, si
  * x_{r+1}, ..., x_r.  In place: recv[r] == send[r] + r*n elements. */
 coll_status_t coll_reduce_scatter(const void* const* send, void* const* recv, int p, size_t n,
                                   coll_dtype_t dtype, coll_op_t op, void* stream);
+
+/* Pre-multiplied ReduceScatter: as coll_reduce_scatter with op sum, each
+ * rank's operand first multiplied by scale[rank] (HOST array of p floats),
+ * products rounded to fp32 on their own.  fp32 and bf16 only. */
+coll_status_t coll_reduce_scatter_premul(const void* const* send, void* const* recv, int p, size_t n,
+                                         coll_dtype_t dtype, const float* scale, void* stream);
 
 /* AllGather ([A] 1.2): send[s] holds n elements, recv[r] holds p*n;
  * recv[r][s*n + j] = send[s][j] (rank-order concatenation).

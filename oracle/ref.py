@@ -34,7 +34,10 @@ Readings taken where the pages are silent or inconsistent:
 3. bf16: widen exactly to fp32, fold in fp32 (IEEE add, round to nearest
    even), narrow once with round-to-nearest-even.
 4. min/max: compare-select, acc = v if v < acc (min) / v > acc (max), in
-   fp32 for bf16.  int32 sum wraps modulo 2^32.
+   fp32 for bf16.  int32 sum wraps modulo 2^32.  AVG: the schedule's sum,
+   then one IEEE fp32 division by p (int32: C division, truncating toward
+   zero).  PreMulSum: each operand times its rank's fp32 scale, every
+   product rounded on its own, then the sum.
 5. Reduce uses the AllReduce chunking, so Reduce then Broadcast equals
    AllReduce bit for bit.
 6. Alltoallv: recv counts are the columns of the send-count matrix; the
@@ -52,7 +55,7 @@ from __future__ import annotations
 
 import numpy as np
 
-SUM, MIN, MAX = 0, 1, 2
+SUM, MIN, MAX, AVG = 0, 1, 2, 3
 F32, BF16, I32 = 0, 1, 2
 
 
@@ -105,7 +108,7 @@ def _widen(v: np.ndarray, dtype: int) -> np.ndarray:
 
 
 def _combine(acc: np.ndarray, v: np.ndarray, op: int) -> np.ndarray:
-    if op == SUM:
+    if op in (SUM, AVG):
         with np.errstate(over="ignore"):
             return acc + v          # fp32 IEEE add (RNE) / int32 add mod 2^32
     if op == MIN:
@@ -115,29 +118,55 @@ def _combine(acc: np.ndarray, v: np.ndarray, op: int) -> np.ndarray:
     raise ValueError(op)
 
 
-def fold(vals_in_order: list[np.ndarray], op: int, dtype: int) -> np.ndarray:
-    """acc = v0; acc = acc (+) v1; ...; then narrow once for bf16."""
-    acc = _widen(vals_in_order[0], dtype).copy()
-    for v in vals_in_order[1:]:
-        acc = _combine(acc, _widen(v, dtype), op)
+def _finish(acc: np.ndarray, op: int, dtype: int, p: int) -> np.ndarray:
+    """After the fold: AVG divides the sum by p (one IEEE fp32 division;
+    int32: C division of the wrapped sum, truncating toward zero), then
+    bf16 is narrowed once."""
+    if op == AVG:
+        if dtype == I32:
+            a = np.asarray(acc).astype(np.int64)
+            acc = (np.sign(a) * (np.abs(a) // p)).astype(np.int32)
+        else:
+            acc = (np.asarray(acc, dtype=np.float32) / np.float32(p)).astype(np.float32)
     if dtype == BF16:
         return f32_to_bf16_rne(acc)
     return acc
 
 
-def reduce_elements(cols: np.ndarray, chunk: np.ndarray, op: int, dtype: int) -> np.ndarray:
+def fold(vals_in_order: list[np.ndarray], op: int, dtype: int, scales=None) -> np.ndarray:
+    """acc = v0; acc = acc (+) v1; ...; then _finish.
+
+    With scales (PreMulSum, sum only) operand k is first multiplied by
+    scales[k] in fp32, each product rounded on its own."""
+    def operand(k):
+        w = _widen(vals_in_order[k], dtype)
+        if scales is not None:
+            w = (np.float32(scales[k]) * w.astype(np.float32)).astype(np.float32)
+        return w
+    acc = operand(0).copy()
+    for k in range(1, len(vals_in_order)):
+        acc = _combine(acc, operand(k), op)
+    return _finish(acc, op, dtype, len(vals_in_order))
+
+
+def reduce_elements(cols: np.ndarray, chunk: np.ndarray, op: int, dtype: int, scales=None) -> np.ndarray:
     """Reduce selected elements.
 
     cols[r, e] is rank r's value of element e; chunk[e] is the chunk that
     element belongs to.  Element e is folded in ring_order(chunk[e], p).
-    Used both for whole buffers and for sampled elements of large ones.
+    scales[r] (PreMulSum) multiplies rank r's operand.  Used both for whole
+    buffers and for sampled elements of large ones.
     """
     cols = np.asarray(cols)
     p, m = cols.shape
     chunk = np.asarray(chunk, dtype=np.int64)
     e = np.arange(m)
-    ordered = [cols[(chunk + k) % p, e] for k in range(1, p + 1)]
-    return fold(ordered, op, dtype)
+    ranks = [(chunk + k) % p for k in range(1, p + 1)]
+    ordered = [cols[r, e] for r in ranks]
+    if scales is None:
+        return fold(ordered, op, dtype)
+    sc = np.asarray(scales, dtype=np.float32)
+    return fold(ordered, op, dtype, scales=[sc[r] for r in ranks])
 
 
 def chunk_len(n: int, p: int) -> int:
@@ -154,13 +183,18 @@ def chunk_of(idx: np.ndarray, n: int, p: int) -> np.ndarray:
 # The primitives (section 0 primitive table of the hpc/04 page)
 # ----------------------------------------------------------------------------
 
-def allreduce(xs: list[np.ndarray], op: int, dtype: int) -> list[np.ndarray]:
-    """out_r[i] = (+)_{r'} x_{r'}[i] on every rank r (section 1.4)."""
+def allreduce(xs: list[np.ndarray], op: int, dtype: int, scales=None) -> list[np.ndarray]:
+    """out_r[i] = (+)_{r'} x_{r'}[i] on every rank r (section 1.4).
+
+    op AVG: the sum divided by p, the average that the page notes older
+    NCCL lacked (section 1.4, sum then divide by the world size).
+    scales: PreMulSum, out = sum_r scales[r] * x_r ("Collective
+    Communication" page: NCCL's constrained custom reduction)."""
     p = len(xs)
     n = len(xs[0])
     if n == 0:
         return [xs[0][:0].copy() for _ in range(p)]
-    res = reduce_elements(np.stack(xs), chunk_of(np.arange(n), n, p), op, dtype)
+    res = reduce_elements(np.stack(xs), chunk_of(np.arange(n), n, p), op, dtype, scales)
     return [res.copy() for _ in range(p)]
 
 
@@ -175,10 +209,10 @@ def broadcast(x_root: np.ndarray, p: int) -> list[np.ndarray]:
     return [np.array(x_root, copy=True) for _ in range(p)]
 
 
-def reduce_scatter(xs: list[np.ndarray], op: int, dtype: int) -> list[np.ndarray]:
+def reduce_scatter(xs: list[np.ndarray], op: int, dtype: int, scales=None) -> list[np.ndarray]:
     """Each rank holds [p*n]; rank r keeps block r of the reduction (section 1.5).
 
-    Block r is reduced in ring_order(r, p).
+    Block r is reduced in ring_order(r, p); scales as in allreduce.
     """
     p = len(xs)
     total = len(xs[0])
@@ -186,8 +220,10 @@ def reduce_scatter(xs: list[np.ndarray], op: int, dtype: int) -> list[np.ndarray
     n = total // p
     out = []
     for r in range(p):
-        blk = [xs[k][r * n:(r + 1) * n] for k in ring_order(r, p)]
-        out.append(fold(blk, op, dtype) if n > 0 else xs[0][:0].copy())
+        order = ring_order(r, p)
+        blk = [xs[k][r * n:(r + 1) * n] for k in order]
+        sc = None if scales is None else [scales[k] for k in order]
+        out.append(fold(blk, op, dtype, sc) if n > 0 else xs[0][:0].copy())
     return out
 
 
@@ -354,9 +390,7 @@ def ring_allreduce_simulated(xs: list[np.ndarray], op: int, dtype: int,
             c = (x + 1 - t) % p
             dst = (x + 1) % p
             buf[dst][sl(c)] = snap[x][sl(c)]
-    if dtype == BF16:
-        return [f32_to_bf16_rne(b) for b in buf]
-    return buf
+    return [_finish(b, op, dtype, p) for b in buf]
 
 
 # ----------------------------------------------------------------------------
@@ -384,9 +418,7 @@ def recursive_doubling_simulated(xs: list[np.ndarray], op: int, dtype: int) -> l
             lo, hi = min(r, r ^ d), max(r, r ^ d)
             buf[r] = _combine(snap[lo], snap[hi], op)
         d *= 2
-    if dtype == BF16:
-        return [f32_to_bf16_rne(b) for b in buf]
-    return buf
+    return [_finish(b, op, dtype, p) for b in buf]
 
 
 def halving_doubling_simulated(xs: list[np.ndarray], op: int, dtype: int) -> list[np.ndarray]:
@@ -435,9 +467,7 @@ def halving_doubling_simulated(xs: list[np.ndarray], op: int, dtype: int) -> lis
             new_blk.append((min(a0, c0), max(a1, c1)))
         blk = new_blk
         d *= 2
-    if dtype == BF16:
-        return [f32_to_bf16_rne(b) for b in buf]
-    return buf
+    return [_finish(b, op, dtype, p) for b in buf]
 
 
 def fold_tree(vals: list[np.ndarray], op: int, dtype: int, first_stride: str) -> np.ndarray:
@@ -463,9 +493,7 @@ def fold_tree(vals: list[np.ndarray], op: int, dtype: int, first_stride: str) ->
             for k in range(s):
                 a[k] = _combine(a[k], a[k + s], op)
             s //= 2
-    if dtype == BF16:
-        return f32_to_bf16_rne(a[0])
-    return a[0]
+    return _finish(a[0], op, dtype, p)
 
 
 # ----------------------------------------------------------------------------

@@ -78,7 +78,14 @@ def test_invalid_arguments_rejected():
     assert L.coll_allreduce(s, r, 0, n, 0, 0, None) == INV            # p = 0
     assert L.coll_allreduce(s, r, 65, n, 0, 0, None) == INV           # p > 64
     assert L.coll_allreduce(s, r, 4, n, 3, 0, None) == INV            # bad dtype
-    assert L.coll_allreduce(s, r, 4, n, 0, 3, None) == INV            # bad op
+    assert L.coll_allreduce(s, r, 4, n, 0, 4, None) == INV            # bad op (4 is internal)
+    assert L.coll_allreduce(s, r, 4, n, 0, -1, None) == INV           # bad op
+    assert L.coll_allreduce_premul(s, r, 4, n, 0, None, 0, None) == INV   # no scales
+    assert L.coll_reduce_scatter_premul(s, r, 4, n, 0, None, None) == INV
+    one = (ctypes.c_float * 4)(1, 1, 1, 1)
+    assert L.coll_allreduce_premul(s, r, 4, n, 2, one, 0, None) == coll.COLL_ERR_UNSUPPORTED  # int32
+    assert L.coll_allreduce_premul(s, r, 4, n, 0, one, 2, None) == coll.COLL_ERR_UNSUPPORTED  # literal ring
+    assert L.coll_reduce_scatter_premul(s, r, 4, n, 2, one, None) == coll.COLL_ERR_UNSUPPORTED
     assert L.coll_allreduce_algo(s, r, 4, n, 0, 0, 7, None) == INV    # bad algo
     assert L.coll_allreduce(None, r, 4, n, 0, 0, None) == INV         # null array
     assert L.coll_allreduce(s, r, 4, 1 << 61, 0, 0, None) == INV      # size overflow

@@ -187,6 +187,112 @@ def test_onepass_unsupported_rank_count(coll):
 
 
 # ----------------------------------------------------------------------------
+# AVG and PreMulSum
+# ----------------------------------------------------------------------------
+
+SCHEDULES = [("RING", None), ("RECURSIVE_DOUBLING", "recursive_doubling_simulated"),
+             ("HALVING_DOUBLING", "halving_doubling_simulated"), ("RING_LITERAL", "ring_allreduce_simulated")]
+
+
+@pytest.mark.parametrize("p,n", [(1, 50), (2, 4097), (3, 1001), (5, 777), (8, 8 * 1024 + 17), (16, 16 * 257), (33, 999)])
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_allreduce_avg_every_schedule(coll, p, n, dtype):
+    hx = gen(p, n, dtype, 90)
+    send = [to_dev(x, dtype) for x in hx]
+    pow2 = p in (2, 4, 8, 16)
+    for algo, sim in SCHEDULES:
+        if algo in ("RECURSIVE_DOUBLING", "HALVING_DOUBLING") and not pow2:
+            continue
+        if algo == "RING_LITERAL" and dtype == BF16:
+            continue
+        recv = [empty(n, dtype, fill=0x4B4B4B4B) for _ in range(p)]
+        coll.coll_allreduce_algo(send, recv, getattr(coll, "COLL_ALGO_" + algo), coll.COLL_AVG)
+        sync()
+        expect = ref.allreduce(hx, ref.AVG, dtype) if sim is None else getattr(ref, sim)(hx, ref.AVG, dtype)
+        for r in range(p):
+            assert_bits_equal(to_host(recv[r], dtype), expect[r], f"AVG {algo} p={p} n={n} dt={dtype} r={r}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_reduce_scatter_and_reduce_avg(coll, dtype):
+    p, n = 8, 3001
+    hx = gen(p, p * n, dtype, 91)
+    send = [to_dev(x, dtype) for x in hx]
+    recv = [empty(n, dtype) for _ in range(p)]
+    coll.coll_reduce_scatter(send, recv, coll.COLL_AVG)
+    root = empty(p * n, dtype)
+    coll.coll_reduce(send, root, 5, coll.COLL_AVG)
+    sync()
+    expect = ref.reduce_scatter(hx, ref.AVG, dtype)
+    for r in range(p):
+        assert_bits_equal(to_host(recv[r], dtype), expect[r], f"RS avg r={r}")
+    assert_bits_equal(to_host(root, dtype), ref.reduce(hx, ref.AVG, dtype, 5), "Reduce avg")
+
+
+def _prescaled(hx, scales, dtype):
+    """PreMulSum operands: every rank's values times its scale, in fp32."""
+    return [(np.float32(sc) * ref.bf16_to_f32(x) if dtype == BF16 else np.float32(sc) * x).astype(np.float32)
+            for x, sc in zip(hx, scales)]
+
+
+@pytest.mark.parametrize("p", [1, 2, 3, 4, 8, 16, 20])
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_allreduce_premul_every_schedule(coll, p, dtype):
+    n = p * 1500 + 7
+    hx = gen(p, n, dtype, 92)
+    send = [to_dev(x, dtype) for x in hx]
+    rng = np.random.default_rng(p)
+    scales = (rng.random(p) * 2 - 0.5).astype(np.float32)
+    for algo, sim in SCHEDULES[:3]:
+        if algo != "RING" and p not in (2, 4, 8, 16):
+            continue
+        recv = [empty(n, dtype, fill=0) for _ in range(p)]
+        coll.coll_allreduce_premul(send, recv, scales, getattr(coll, "COLL_ALGO_" + algo))
+        sync()
+        if sim is None:
+            expect = ref.allreduce(hx, ref.SUM, dtype, scales=scales)
+        else:
+            tree = getattr(ref, sim)(_prescaled(hx, scales, dtype), ref.SUM, F32)
+            expect = [ref.f32_to_bf16_rne(t) if dtype == BF16 else t for t in tree]
+        for r in range(p):
+            assert_bits_equal(to_host(recv[r], dtype), expect[r], f"premul {algo} p={p} dt={dtype} r={r}")
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_reduce_scatter_premul_and_in_place(coll, dtype):
+    p, n = 8, 4099
+    hx = gen(p, p * n, dtype, 93)
+    scales = np.full(p, 1.0 / p, dtype=np.float32)
+    send = [to_dev(x, dtype) for x in hx]
+    recv = [send[r][r * n:(r + 1) * n] for r in range(p)]
+    coll.coll_reduce_scatter_premul(send, recv, scales)
+    sync()
+    expect = ref.reduce_scatter(hx, ref.SUM, dtype, scales=scales)
+    avg = ref.reduce_scatter(hx, ref.AVG, dtype)
+    for r in range(p):
+        assert_bits_equal(to_host(recv[r], dtype), expect[r], f"RS premul r={r}")
+        assert_bits_equal(expect[r], avg[r], "scale 1/p equals AVG at p=8")
+
+
+def test_batch_with_avg_calls(coll):
+    p, rng = 8, np.random.default_rng(94)
+    calls, host = [], []
+    for k in range(40):
+        n = int(rng.choice([1, 7, 100, 4097, 9000]))
+        dtype = (F32, I32, BF16)[k % 3]
+        op = int(rng.integers(0, 4))
+        hx = gen(p, n, dtype, 300 + k)
+        calls.append(([to_dev(x, dtype) for x in hx], [empty(n, dtype) for _ in range(p)], n, dtype, op))
+        host.append((hx, op, dtype))
+    coll.coll_allreduce_batch(calls, p)
+    sync()
+    for k, ((_, recv, n, dtype, op), (hx, _, _)) in enumerate(zip(calls, host)):
+        expect = ref.allreduce(hx, op, dtype)
+        for r in (0, p - 1):
+            assert_bits_equal(to_host(recv[r], dtype), expect[r], f"batch call {k} op {op}")
+
+
+# ----------------------------------------------------------------------------
 # Reduce and Broadcast
 # ----------------------------------------------------------------------------
 

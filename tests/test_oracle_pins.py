@@ -693,3 +693,99 @@ def test_moe_combine_against_pure_python():
                     prod = struct.unpack("f", struct.pack("f", float(w[a]) * float(back[pos[a] * H + h])))[0]
                     acc = _py_add_f32(acc, prod)
                 assert got[t * H + h] == np.float32(acc)
+
+
+# ----------------------------------------------------------------------------
+# AVG and PreMulSum (hpc/04 section 1.4 note; "Collective Communication"
+# numerics section on NCCL's constrained custom reduction)
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_avg_on_worked_example(dtype):
+    """The worked example's sum [10 14] over p = 4 ranks: the average is
+    [2.5 3.5]; int32 truncates toward zero to [2 3]; bf16 holds 2.5 and 3.5
+    exactly."""
+    xs, _ = _worked_example()
+    arrs = [_as_dtype(x, dtype) for x in xs]
+    expect = [2, 3] if dtype == ref.I32 else [2.5, 3.5]
+    for out in ref.allreduce(arrs, ref.AVG, dtype):
+        assert list(_to_float(out, dtype)) == expect
+
+
+@pytest.mark.parametrize("p", [1, 2, 3, 4])
+def test_avg_int32_bruteforce_truncates(p):
+    """Every int32 input in {-3..3}^p: AVG is the sum divided by p,
+    truncated toward zero (C division), for one element."""
+    for vals in itertools.product(range(-3, 4), repeat=p):
+        xs = [np.array([v], dtype=np.int32) for v in vals]
+        got = int(ref.allreduce(xs, ref.AVG, ref.I32)[0][0])
+        s_ = sum(vals)
+        assert got == int(s_ / p) == (abs(s_) // p) * (1 if s_ >= 0 else -1)
+
+
+@pytest.mark.parametrize("dtype", [ref.F32, ref.BF16])
+def test_avg_is_rounded_sum_over_p(dtype):
+    """fp32 AVG = fl(fl_sum / p) with one IEEE division; checked against
+    Python's float division of the pure-Python ring-order sum, including a
+    p that is not a power of two."""
+    rng = np.random.default_rng(21)
+    for p in (3, 5, 8):
+        xs = [rng.standard_normal(64).astype(np.float32) for _ in range(p)]
+        if dtype == ref.BF16:
+            xs = [(x.view(np.uint32) >> 16).astype(np.uint16) for x in xs]
+        n = 64
+        q = -(-n // p)
+        got = _to_float(ref.allreduce(xs, ref.AVG, dtype)[0], dtype)
+        widened = [_to_float(x, dtype) for x in xs]
+        for i in range(n):
+            ssum = _py_ring_fold([float(w[i]) for w in widened], i // q, ref.F32)
+            # the double quotient rounded to fp32; differs from one rounding only
+            # if the double lands exactly on an fp32 tie (probability ~2^-28)
+            quo = struct.unpack("f", struct.pack("f", ssum / p))[0]
+            expect = _py_bf16_rne(quo) if dtype == ref.BF16 else quo
+            assert got[i] == expect, (p, i)
+
+
+@pytest.mark.parametrize("dtype", [ref.F32, ref.BF16])
+def test_premulsum_special_cases(dtype):
+    """Scales of 1 give the plain sum bit for bit; scales of 1/p with p a
+    power of two give AVG bit for bit (scaling by a power of two commutes
+    with rounding); integer scales on small integers give the exact sum."""
+    rng = np.random.default_rng(22)
+    p, n = 8, 300
+    xs = [rng.standard_normal(n).astype(np.float32) for _ in range(p)]
+    if dtype == ref.BF16:
+        xs = [(x.view(np.uint32) >> 16).astype(np.uint16) for x in xs]
+    ones = np.ones(p, dtype=np.float32)
+    assert np.array_equal(_bits(ref.allreduce(xs, ref.SUM, dtype, scales=ones)[0]),
+                          _bits(ref.allreduce(xs, ref.SUM, dtype)[0]))
+    inv = np.full(p, 1.0 / p, dtype=np.float32)
+    assert np.array_equal(_bits(ref.allreduce(xs, ref.SUM, dtype, scales=inv)[0]),
+                          _bits(ref.allreduce(xs, ref.AVG, dtype)[0]))
+    ints = [rng.integers(-20, 21, n) for _ in range(p)]
+    sc = rng.integers(-3, 4, p).astype(np.float32)
+    got = _to_float(ref.allreduce([_as_dtype(v, dtype) for v in ints], ref.SUM, dtype, scales=sc)[0], dtype)
+    assert list(got) == list(sum(float(sc[r]) * ints[r].astype(np.float64) for r in range(p)))
+
+
+def test_premulsum_reduce_scatter_matches_allreduce_blocks():
+    rng = np.random.default_rng(23)
+    p, n = 4, 50
+    xs = [rng.standard_normal(p * n).astype(np.float32) for _ in range(p)]
+    sc = rng.random(p).astype(np.float32) + 0.5
+    rs = ref.reduce_scatter(xs, ref.SUM, ref.F32, scales=sc)
+    ar = ref.allreduce(xs, ref.SUM, ref.F32, scales=sc)[0]
+    for r in range(p):
+        assert np.array_equal(_bits(rs[r]), _bits(ar[r * n:(r + 1) * n]))
+
+
+@pytest.mark.parametrize("sim", ["recursive_doubling_simulated", "halving_doubling_simulated",
+                                 "ring_allreduce_simulated"])
+def test_avg_under_every_schedule_is_sum_divided(sim):
+    rng = np.random.default_rng(24)
+    p, n = 8, 40
+    xs = [rng.standard_normal(n).astype(np.float32) for _ in range(p)]
+    s_ = getattr(ref, sim)(xs, ref.SUM, ref.F32)
+    a_ = getattr(ref, sim)(xs, ref.AVG, ref.F32)
+    for r in range(p):
+        assert np.array_equal(_bits(a_[r]), _bits((s_[r] / np.float32(p)).astype(np.float32)))
