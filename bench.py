@@ -58,7 +58,7 @@ def parse_args(argv=None):
     ap.add_argument("--no-collectives", action="store_true", help="time only the main step")
     ap.add_argument("--only", default=None,
                     help="comma list of extra collectives to time (ar_ring, ar_onepass, ar_hd, "
-                         "ar_literal, a2a, a2av, moe, gs, ar_small, batch, copy)")
+                         "ar_literal, ar_avg, ar_premul, a2a, a2av, moe, gs, ar_small, batch, copy)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
     return ap.parse_args(argv)
 
@@ -245,7 +245,7 @@ def extra_collectives(torch, coll, inputs, metrics, dev, which, iters=10, warmup
     want = lambda k: which is None or k in which  # noqa: E731
 
     # --- DP gradient AllReduce, p = 8, 256 MiB fp32 per rank ~ N(0, 1) -------
-    if want("ar_ring") or want("ar_onepass") or want("ar_hd") or want("ar_literal"):
+    if any(want(k) for k in ("ar_ring", "ar_onepass", "ar_hd", "ar_literal", "ar_avg", "ar_premul")):
         p, n = 8, 1 << 26
         send = [to_dev(torch, x, dev) for x in inputs.rank_buffers(inputs.WL_DP_RING_AR, p, n, inputs.F32,
                                                                     dist="normal")]
@@ -262,6 +262,21 @@ def extra_collectives(torch, coll, inputs, metrics, dev, which, iters=10, warmup
             med, p95, _ = stats_us(time_launches(torch, [f], iters, warmup)[0])
             rows.append(coll_entry(metrics, label, "allreduce", p, n, 4, med, aname,
                                    {"dtype": "f32", "op": "sum", "t_p95_us": round(p95, 2),
+                                    "workload": "DP gradient AllReduce, 256 MiB fp32 per rank"}))
+        # Scaled variants on the same buffers: AVG (sum then one division by
+        # p) and PreMulSum with per-rank weights w_r = 1/p.
+        if want("ar_avg"):
+            f = coll.coll_allreduce_algo(send, recv, coll.COLL_ALGO_RING, coll.COLL_AVG, defer=True)
+            med, p95, _ = stats_us(time_launches(torch, [f], iters, warmup)[0])
+            rows.append(coll_entry(metrics, "allreduce_avg_ring", "allreduce", p, n, 4, med, "ring",
+                                   {"dtype": "f32", "op": "avg", "t_p95_us": round(p95, 2),
+                                    "workload": "DP gradient AllReduce, 256 MiB fp32 per rank"}))
+        if want("ar_premul"):
+            scales = np.full(p, 1.0 / p, dtype=np.float32)
+            f = coll.coll_allreduce_premul(send, recv, scales, coll.COLL_ALGO_RING, defer=True)
+            med, p95, _ = stats_us(time_launches(torch, [f], iters, warmup)[0])
+            rows.append(coll_entry(metrics, "allreduce_premulsum_ring", "allreduce", p, n, 4, med, "ring",
+                                   {"dtype": "f32", "op": "premulsum", "t_p95_us": round(p95, 2),
                                     "workload": "DP gradient AllReduce, 256 MiB fp32 per rank"}))
         del send, recv
         torch.cuda.empty_cache()

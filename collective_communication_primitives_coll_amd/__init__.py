@@ -24,7 +24,8 @@ COLL_ALGO_RECURSIVE_DOUBLING = COLL_ALGO_ONEPASS
 COLL_MAX_RANKS = 64
 COLL_BATCH_CHECK_ALIAS = 1
 
-ELEM_BYTES = {COLL_F32: 4, COLL_BF16: 2, COLL_I32: 4}
+COLL_U8 = 3
+ELEM_BYTES = {COLL_F32: 4, COLL_BF16: 2, COLL_I32: 4, COLL_U8: 1}
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcoll.so")
 
@@ -75,6 +76,8 @@ def lib() -> ctypes.CDLL:
         "coll_moe_combine": [pp, pp, pp, pp, pp, i32, sz, i32, sz, i32, vp],
         "coll_scatter": [vp, pp, i32, sz, i32, i32, vp],
         "coll_allreduce_batch": [ctypes.POINTER(coll_call_t), i32, i32, ctypes.c_uint, vp],
+        "coll_moe_pack_fp8": [pp, pp, pp, pp, vp, vp, vp, i32, sz, i32, sz, sz, vp],
+        "coll_moe_dequant_fp8": [pp, pp, i32, vp, i64p, vp, sz, sz, vp],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -86,6 +89,8 @@ def lib() -> ctypes.CDLL:
     L.coll_last_hip_error.restype = ctypes.c_int
     L.coll_version.argtypes = []
     L.coll_version.restype = ctypes.c_int
+    L.coll_moe_fp8_row_bytes.argtypes = [sz, sz]
+    L.coll_moe_fp8_row_bytes.restype = sz
     L.coll_finalize.argtypes = []
     L.coll_finalize.restype = None
     L.coll_set_grid_limit.argtypes = [ctypes.c_int]
@@ -119,9 +124,10 @@ def _dtype_of(x: Any, dtype: int | None) -> int:
     if dtype is not None:
         return int(dtype)
     import torch
-    m = {torch.float32: COLL_F32, torch.bfloat16: COLL_BF16, torch.int32: COLL_I32}
+    m = {torch.float32: COLL_F32, torch.bfloat16: COLL_BF16, torch.int32: COLL_I32, torch.uint8: COLL_U8}
     if not hasattr(x, "dtype") or x.dtype not in m:
-        raise ValueError("dtype must be given for raw addresses, or tensors must be float32/bfloat16/int32")
+        raise ValueError("dtype must be given for raw addresses, or tensors must be "
+                         "float32/bfloat16/int32/uint8")
     return m[x.dtype]
 
 
@@ -413,6 +419,53 @@ def coll_moe_pack(tokens, dest, packed, pos, counts_dev, k: int, hidden: int, st
     st = _addr(status_dev) if status_dev is not None else None
     return _run("coll_moe_pack", (a1, a2, a3, a4, _addr(counts_dev), st, p, int(T), int(k), int(hidden), dt,
                                   _stream(stream)), "coll_moe_pack", defer, (k1, k2, k3, k4))
+
+
+def coll_moe_fp8_row_bytes(hidden: int, group: int) -> int:
+    """Bytes of one packed FP8 row (codes, scales, padding); 0 if the shape
+    is not accepted."""
+    return int(lib().coll_moe_fp8_row_bytes(int(hidden), int(group)))
+
+
+def coll_moe_pack_fp8(tokens, dest, packed, pos, counts_dev, k: int, hidden: int, group: int,
+                      counts_hidden_dev=None, status_dev=None, tokens_per_rank: int | None = None,
+                      stream=None, defer: bool = False):
+    """Quantizing dispatch pack: per rank, bf16 tokens [T*hidden], dest int32
+    [T*k] -> packed uint8 [T*k*row_bytes], pos int32 [T*k]; counts_dev int64
+    [p, p] in bytes; counts_hidden_dev (optional) int64 [p, p] in rows*hidden."""
+    p = len(tokens)
+    T = tokens_per_rank if tokens_per_rank is not None else _numel(tokens[0], None) // int(hidden)
+    R = coll_moe_fp8_row_bytes(hidden, group)
+    if R:
+        _check_sizes(packed, T * k * R, "moe_pack_fp8 packed")
+    _check_sizes(tokens, T * hidden, "moe_pack_fp8 tokens")
+    _check_sizes([*dest, *pos], T * k, "moe_pack_fp8 dest/pos")
+    a1, k1 = _ptr_array(tokens)
+    a2, k2 = _ptr_array(dest)
+    a3, k3 = _ptr_array(packed)
+    a4, k4 = _ptr_array(pos)
+    st = _addr(status_dev) if status_dev is not None else None
+    ch = _addr(counts_hidden_dev) if counts_hidden_dev is not None else None
+    return _run("coll_moe_pack_fp8", (a1, a2, a3, a4, _addr(counts_dev), ch, st, p, int(T), int(k), int(hidden),
+                                      int(group), _stream(stream)), "coll_moe_pack_fp8", defer, (k1, k2, k3, k4))
+
+
+def coll_moe_dequant_fp8(recv, out, counts_dev, rows_cap: Sequence[int], hidden: int, group: int,
+                         status_dev=None, stream=None, defer: bool = False):
+    """bf16 rows of the FP8 rows each rank received (byte counts [p, p] on
+    the device, as written by coll_moe_pack_fp8)."""
+    p = len(recv)
+    R = coll_moe_fp8_row_bytes(hidden, group)
+    for r in range(p):
+        if R:
+            _check_sizes([recv[r]], int(rows_cap[r]) * R, "moe_dequant_fp8 recv")
+        _check_sizes([out[r]], int(rows_cap[r]) * hidden, "moe_dequant_fp8 out")
+    a1, k1 = _ptr_array(recv)
+    a2, k2 = _ptr_array(out)
+    cap = (ctypes.c_int64 * p)(*[int(c) for c in rows_cap])
+    st = _addr(status_dev) if status_dev is not None else None
+    return _run("coll_moe_dequant_fp8", (a1, a2, p, _addr(counts_dev), cap, st, int(hidden), int(group),
+                                         _stream(stream)), "coll_moe_dequant_fp8", defer, (k1, k2, cap))
 
 
 def coll_moe_combine(back, pos, weights, out, k: int, hidden: int, residual=None,

@@ -25,6 +25,7 @@ SOURCES = [
     "ring_literal.hip",
     "batch_kernels.hip",
     "moe_kernels.hip",
+    "fp8_kernels.hip",
 ]
 
 ARCH = "gfx950"

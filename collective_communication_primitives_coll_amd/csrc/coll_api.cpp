@@ -80,9 +80,11 @@ int max_grid(int* out, Family fam) {
 // ---------------------------------------------------------------------------
 // Argument checks
 // ---------------------------------------------------------------------------
-bool dtype_ok(int d) { return d == COLL_F32 || d == COLL_BF16 || d == COLL_I32; }
+// Types with arithmetic (reductions, combine) and all types (data movement).
+bool arith_dtype_ok(int d) { return d == COLL_F32 || d == COLL_BF16 || d == COLL_I32; }
+bool dtype_ok(int d) { return arith_dtype_ok(d) || d == COLL_U8; }
 bool op_ok(int o) { return o == COLL_SUM || o == COLL_MIN || o == COLL_MAX || o == COLL_AVG; }
-size_t dsize(int d) { return d == COLL_BF16 ? 2 : 4; }
+size_t dsize(int d) { return d == COLL_BF16 ? 2 : d == COLL_U8 ? 1 : 4; }
 
 // bytes = a * b * c without overflow, and below 2^62 so that every derived
 // offset stays representable.
@@ -165,7 +167,7 @@ coll_status_t finish(int err) { return err ? hip_fail(err) : COLL_OK; }
 // AllReduce validation shared by the single and the batched entry points.
 coll_status_t check_allreduce(const void* const* send, void* const* recv, int p, size_t n, int dtype,
                               int op) {
-  if (p < 1 || p > kMaxRanks || !dtype_ok(dtype) || !op_ok(op)) return COLL_ERR_INVALID_ARG;
+  if (p < 1 || p > kMaxRanks || !arith_dtype_ok(dtype) || !op_ok(op)) return COLL_ERR_INVALID_ARG;
   if (n == 0) return COLL_OK;
   size_t bytes;
   if (!mul_ok(n, dsize(dtype), (size_t)p, &bytes)) return COLL_ERR_INVALID_ARG;
@@ -272,7 +274,7 @@ COLL_EXPORT coll_status_t coll_allreduce_premul(const void* const* send, void* c
 
 COLL_EXPORT coll_status_t coll_reduce(const void* const* send, void* recv_root, int p, size_t n,
                                       coll_dtype_t dtype, coll_op_t op, int root, void* stream) {
-  if (p < 1 || p > kMaxRanks || !dtype_ok(dtype) || !op_ok(op) || root < 0 || root >= p)
+  if (p < 1 || p > kMaxRanks || !arith_dtype_ok(dtype) || !op_ok(op) || root < 0 || root >= p)
     return COLL_ERR_INVALID_ARG;
   if (n == 0) return COLL_OK;
   size_t bytes;
@@ -331,7 +333,7 @@ COLL_EXPORT coll_status_t coll_broadcast(const void* send_root, void* const* rec
 namespace {
 coll_status_t reduce_scatter_impl(const void* const* send, void* const* recv, int p, size_t n, coll_dtype_t dtype,
                                   int op, const float* scale, void* stream) {
-  if (p < 1 || p > kMaxRanks || !dtype_ok(dtype) || !(op_ok(op) || op == coll::kPreMul)) return COLL_ERR_INVALID_ARG;
+  if (p < 1 || p > kMaxRanks || !arith_dtype_ok(dtype) || !(op_ok(op) || op == coll::kPreMul)) return COLL_ERR_INVALID_ARG;
   if (n == 0) return COLL_OK;
   size_t bytes;
   if (!mul_ok(n, dsize(dtype), (size_t)p * p, &bytes)) return COLL_ERR_INVALID_ARG;
@@ -372,7 +374,7 @@ COLL_EXPORT coll_status_t coll_reduce_scatter(const void* const* send, void* con
 COLL_EXPORT coll_status_t coll_reduce_scatter_premul(const void* const* send, void* const* recv, int p,
                                                      size_t n, coll_dtype_t dtype, const float* scale,
                                                      void* stream) {
-  if (p < 1 || p > kMaxRanks || !dtype_ok(dtype) || !scale) return COLL_ERR_INVALID_ARG;
+  if (p < 1 || p > kMaxRanks || !arith_dtype_ok(dtype) || !scale) return COLL_ERR_INVALID_ARG;
   if (dtype == COLL_I32) return COLL_ERR_UNSUPPORTED;
   return reduce_scatter_impl(send, recv, p, n, dtype, coll::kPreMul, scale, stream);
 }
@@ -620,7 +622,7 @@ COLL_EXPORT coll_status_t coll_moe_combine(const void* const* back, const int32_
                                            const float* const* weights, const void* const* residual,
                                            void* const* out, int p, size_t tokens_per_rank, int k,
                                            size_t hidden, coll_dtype_t dtype, void* stream) {
-  if (p < 1 || p > kMaxRanks || !dtype_ok(dtype) || k < 1 || k > coll::kMaxTopK || hidden == 0)
+  if (p < 1 || p > kMaxRanks || !arith_dtype_ok(dtype) || k < 1 || k > coll::kMaxTopK || hidden == 0)
     return COLL_ERR_INVALID_ARG;
   if (dtype == COLL_I32) return COLL_ERR_UNSUPPORTED;
   const size_t d = dsize(dtype);
@@ -671,6 +673,145 @@ COLL_EXPORT coll_status_t coll_moe_combine(const void* const* back, const int32_
   ra.dst_mis = common_mis((const void* const*)out, p);
   ra.res_mis = residual ? common_mis(residual, p) : 0;
   return finish(coll::launch_moe_combine(dtype, ra, grid, stream));
+}
+
+// ---------------------------------------------------------------------------
+// FP8 e4m3 dispatch
+// ---------------------------------------------------------------------------
+namespace {
+// 0: accepted; otherwise the status to return.
+coll_status_t fp8_shape(size_t hidden, size_t group) {
+  if (hidden == 0 || group == 0 || hidden % group) return COLL_ERR_INVALID_ARG;
+  if (hidden > coll::kFp8MaxHidden || group < 16) return COLL_ERR_UNSUPPORTED;
+  if (group <= 1024 ? (group & (group - 1)) != 0 : group % 1024 != 0) return COLL_ERR_UNSUPPORTED;
+  return COLL_OK;
+}
+size_t fp8_row_bytes(size_t hidden, size_t group) { return hidden + 16 * ((4 * (hidden / group) + 15) / 16); }
+bool aligned16(const void* const* arr, int p) {
+  for (int r = 0; r < p; ++r)
+    if ((uintptr_t)arr[r] & 15) return false;
+  return true;
+}
+}  // namespace
+
+COLL_EXPORT size_t coll_moe_fp8_row_bytes(size_t hidden, size_t group) {
+  return fp8_shape(hidden, group) == COLL_OK ? fp8_row_bytes(hidden, group) : 0;
+}
+
+COLL_EXPORT coll_status_t coll_moe_pack_fp8(const void* const* tokens, const int32_t* const* dest,
+                                            void* const* packed, int32_t* const* pos, int64_t* counts_dev,
+                                            int64_t* counts_hidden_dev, int32_t* status_dev, int p,
+                                            size_t tokens_per_rank, int k, size_t hidden, size_t group,
+                                            void* stream) {
+  if (p < 1 || p > kMaxRanks || k < 1 || k > coll::kMaxTopK) return COLL_ERR_INVALID_ARG;
+  coll_status_t st = fp8_shape(hidden, group);
+  if (st != COLL_OK) return st;
+  if (!counts_dev || !elem_aligned1(counts_dev, sizeof(int64_t))) return COLL_ERR_INVALID_ARG;
+  if (counts_hidden_dev && !elem_aligned1(counts_hidden_dev, sizeof(int64_t))) return COLL_ERR_INVALID_ARG;
+  if (status_dev && !elem_aligned1(status_dev, sizeof(int32_t))) return COLL_ERR_INVALID_ARG;
+  const size_t R = fp8_row_bytes(hidden, group);
+  size_t A, tb, pb;
+  if (!mul_ok(tokens_per_rank, (size_t)k, 1, &A) || A > 0x7fffffffull) return COLL_ERR_INVALID_ARG;
+  if (!mul_ok(tokens_per_rank, hidden * 2, 1, &tb) || !mul_ok(A, R, (size_t)kMaxRanks, &pb))
+    return COLL_ERR_INVALID_ARG;
+  pb = A * R;
+  std::vector<Range> rs;
+  if (A > 0) {
+    if (!all_non_null(tokens, p) || !all_non_null(dest, p) || !all_non_null(packed, p) || !all_non_null(pos, p))
+      return COLL_ERR_INVALID_ARG;
+    if (!aligned16(tokens, p) || !aligned16((const void* const*)packed, p) || !elem_aligned(dest, p, 4) ||
+        !elem_aligned(pos, p, 4))
+      return COLL_ERR_INVALID_ARG;
+    for (int r = 0; r < p; ++r) {
+      rs.push_back(rng(tokens[r], tb, false, r));
+      rs.push_back(rng(dest[r], A * 4, false, r));
+      rs.push_back(rng(packed[r], pb, true, r));
+      rs.push_back(rng(pos[r], A * 4, true, r));
+    }
+  }
+  rs.push_back(rng(counts_dev, (size_t)p * p * sizeof(int64_t), true, -1));
+  if (counts_hidden_dev) rs.push_back(rng(counts_hidden_dev, (size_t)p * p * sizeof(int64_t), true, -1));
+  if (status_dev) rs.push_back(rng(status_dev, (size_t)p * sizeof(int32_t), true, -1));
+  st = check_alias(rs, [](const Range&, const Range&) { return false; });
+  if (st != COLL_OK) return st;
+  coll::MoeIndexArgs ia;
+  std::memset(&ia, 0, sizeof(ia));
+  for (int r = 0; r < p && A > 0; ++r) {
+    ia.dest[r] = dest[r];
+    ia.pos[r] = pos[r];
+  }
+  ia.counts = counts_dev;
+  ia.counts2 = counts_hidden_dev;
+  ia.status = status_dev;
+  ia.assignments = A;
+  ia.hidden = R;  // counts in bytes
+  ia.hidden2 = hidden;
+  ia.p = p;
+  int e = coll::launch_moe_index(ia, stream);
+  if (e) return hip_fail(e);
+  if (A == 0) return COLL_OK;
+  int grid;
+  e = max_grid(&grid, kFamRow);
+  if (e) return hip_fail(e);
+  coll::Fp8Args fa;
+  std::memset(&fa, 0, sizeof(fa));
+  for (int r = 0; r < p; ++r) {
+    fa.src[r] = tokens[r];
+    fa.dst[r] = packed[r];
+    fa.pos[r] = pos[r];
+  }
+  fa.tokens = tokens_per_rank;
+  fa.hidden = hidden;
+  fa.group = group;
+  fa.row_bytes = R;
+  fa.k = k;
+  fa.p = p;
+  return finish(coll::launch_moe_pack_fp8(fa, grid, stream));
+}
+
+COLL_EXPORT coll_status_t coll_moe_dequant_fp8(const void* const* recv, void* const* out, int p,
+                                               const int64_t* counts_dev, const int64_t* rows_cap,
+                                               int32_t* status_dev, size_t hidden, size_t group, void* stream) {
+  if (p < 1 || p > kMaxRanks || !rows_cap) return COLL_ERR_INVALID_ARG;
+  coll_status_t st = fp8_shape(hidden, group);
+  if (st != COLL_OK) return st;
+  if (!counts_dev || !elem_aligned1(counts_dev, sizeof(int64_t))) return COLL_ERR_INVALID_ARG;
+  if (status_dev && !elem_aligned1(status_dev, sizeof(int32_t))) return COLL_ERR_INVALID_ARG;
+  if (!all_non_null(recv, p) || !all_non_null(out, p)) return COLL_ERR_INVALID_ARG;
+  if (!aligned16(recv, p) || !aligned16((const void* const*)out, p)) return COLL_ERR_INVALID_ARG;
+  const size_t R = fp8_row_bytes(hidden, group);
+  std::vector<Range> rs;
+  for (int r = 0; r < p; ++r) {
+    size_t b;
+    if (rows_cap[r] < 0) return COLL_ERR_INVALID_ARG;
+    // p counts of at most a capacity each must sum without int64 overflow
+    // on the device
+    if (!mul_ok((size_t)rows_cap[r], R, kMaxRanks, &b) || !mul_ok((size_t)rows_cap[r], hidden * 2, 1, &b))
+      return COLL_ERR_INVALID_ARG;
+    rs.push_back(rng(recv[r], (size_t)rows_cap[r] * R, false, r));
+    rs.push_back(rng(out[r], (size_t)rows_cap[r] * hidden * 2, true, r));
+  }
+  rs.push_back(rng(counts_dev, (size_t)p * p * sizeof(int64_t), false, -1));
+  if (status_dev) rs.push_back(rng(status_dev, sizeof(int32_t), true, -1));
+  st = check_alias(rs, [](const Range&, const Range&) { return false; });
+  if (st != COLL_OK) return st;
+  int grid;
+  int e = max_grid(&grid, kFamRow);
+  if (e) return hip_fail(e);
+  coll::Fp8Args fa;
+  std::memset(&fa, 0, sizeof(fa));
+  for (int r = 0; r < p; ++r) {
+    fa.src[r] = recv[r];
+    fa.dst[r] = out[r];
+    fa.rows_cap[r] = rows_cap[r];
+  }
+  fa.counts = counts_dev;
+  fa.status = status_dev;
+  fa.hidden = hidden;
+  fa.group = group;
+  fa.row_bytes = R;
+  fa.p = p;
+  return finish(coll::launch_moe_dequant_fp8(fa, grid, stream));
 }
 
 // ---------------------------------------------------------------------------

@@ -195,6 +195,7 @@ static int launch_copy_b(const RankPtrs& ptrs, const CopyGeom& g, int max_grid, 
 
 int launch_copy(int elem_bytes, const RankPtrs& ptrs, const CopyGeom& g, int max_grid, void* stream) {
   hipStream_t s = (hipStream_t)stream;
+  if (elem_bytes == 1) return launch_copy_b<1>(ptrs, g, max_grid, s);
   if (elem_bytes == 2) return launch_copy_b<2>(ptrs, g, max_grid, s);
   if (elem_bytes == 4) return launch_copy_b<4>(ptrs, g, max_grid, s);
   return (int)hipErrorInvalidValue;
@@ -203,7 +204,9 @@ int launch_copy(int elem_bytes, const RankPtrs& ptrs, const CopyGeom& g, int max
 int launch_alltoallv(int elem_bytes, const RankPtrs& ptrs, const A2avArgs& a, int grid, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   const size_t shm = (size_t)3 * a.p * a.p * sizeof(int64_t);
-  if (elem_bytes == 2)
+  if (elem_bytes == 1)
+    hipLaunchKernelGGL((alltoallv_kernel<1>), dim3(grid), dim3(kBlock), shm, s, ptrs, a);
+  else if (elem_bytes == 2)
     hipLaunchKernelGGL((alltoallv_kernel<2>), dim3(grid), dim3(kBlock), shm, s, ptrs, a);
   else if (elem_bytes == 4)
     hipLaunchKernelGGL((alltoallv_kernel<4>), dim3(grid), dim3(kBlock), shm, s, ptrs, a);

@@ -13,6 +13,10 @@ namespace coll {
 template <int B>
 struct Word;
 template <>
+struct Word<1> {
+  using T = uint8_t;
+};
+template <>
 struct Word<2> {
   using T = uint16_t;
 };

@@ -81,10 +81,12 @@ constexpr int kMaxTopK = 8;
 struct MoeIndexArgs {
   const int32_t* dest[kMaxRanks];  // per rank: destination rank of each assignment
   int32_t* pos[kMaxRanks];         // per rank: packed row of each assignment
-  int64_t* counts;                 // [p][p] elements
+  int64_t* counts;                 // [p][p]: rows * hidden
+  int64_t* counts2;                // optional [p][p]: rows * hidden2
   int32_t* status;                 // optional
   uint64_t assignments;            // T * k per rank
   uint64_t hidden;
+  uint64_t hidden2;
   int p;
 };
 
@@ -102,6 +104,25 @@ struct MoeRowArgs {
   int src_mis;                     // common misalignment of the src bases, or -1
   int dst_mis;
   int res_mis;
+};
+
+// Quantized dispatch: FP8 e4m3 rows with one fp32 scale per group of
+// `group` elements.  Row layout: hidden code bytes, hidden/group scales,
+// zero bytes up to row_bytes (a multiple of 16).
+constexpr uint64_t kFp8MaxHidden = 16384;  // 16 units of 16 elements per lane
+struct Fp8Args {
+  const void* src[kMaxRanks];      // pack: bf16 tokens; dequant: received rows
+  void* dst[kMaxRanks];            // pack: packed rows; dequant: bf16 rows
+  const int32_t* pos[kMaxRanks];   // pack: packed row of each assignment
+  int64_t rows_cap[kMaxRanks];     // dequant: rows each output holds
+  const int64_t* counts;           // dequant: [p][p] bytes, row = source
+  int32_t* status;                 // dequant: optional
+  uint64_t tokens;                 // pack: T per rank
+  uint64_t hidden;
+  uint64_t group;
+  uint64_t row_bytes;
+  int k;
+  int p;
 };
 
 // Literal ring: one neighbour step per launch.
@@ -151,6 +172,11 @@ uint64_t batch_tile_elems_host(int dtype, int p);
 int launch_moe_index(const MoeIndexArgs& a, void* stream);
 int launch_moe_pack(int elem_bytes, const MoeRowArgs& a, int max_grid, void* stream);
 int launch_moe_combine(int dtype, const MoeRowArgs& a, int max_grid, void* stream);
+
+// FP8 dispatch: quantizing pack (after launch_moe_index with counts in
+// bytes) and the bf16 dequantization of received rows.
+int launch_moe_pack_fp8(const Fp8Args& a, int max_grid, void* stream);
+int launch_moe_dequant_fp8(const Fp8Args& a, int max_grid, void* stream);
 
 // 16-byte vectors each lane of a copy kernel keeps in flight.
 constexpr uint64_t kCopyUnroll = 4;

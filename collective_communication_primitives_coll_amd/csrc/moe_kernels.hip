@@ -87,6 +87,7 @@ __global__ __launch_bounds__(kIdxThreads) void moe_index_kernel(MoeIndexArgs a) 
   const bool reject = bad != 0;
   if (tid < p) {
     a.counts[(uint64_t)rank * p + tid] = reject ? 0 : (int64_t)total[tid] * (int64_t)a.hidden;
+    if (a.counts2) a.counts2[(uint64_t)rank * p + tid] = reject ? 0 : (int64_t)total[tid] * (int64_t)a.hidden2;
     for (int ww = 0; ww < kIdxWaves; ++ww) wofs[ww][tid] += base[tid];
   }
   if (tid == 0 && a.status) a.status[rank] = reject ? 1 : 0;
@@ -294,7 +295,9 @@ int launch_moe_pack(int elem_bytes, const MoeRowArgs& a, int max_grid, void* str
   if (!rows) return 0;
   const int grid = (int)(rows < (uint64_t)max_grid ? rows : (uint64_t)max_grid);
   hipStream_t s = (hipStream_t)stream;
-  if (elem_bytes == 2)
+  if (elem_bytes == 1)
+    hipLaunchKernelGGL((moe_pack_kernel<1>), dim3(grid), dim3(kBlock), 0, s, a);
+  else if (elem_bytes == 2)
     hipLaunchKernelGGL((moe_pack_kernel<2>), dim3(grid), dim3(kBlock), 0, s, a);
   else if (elem_bytes == 4)
     hipLaunchKernelGGL((moe_pack_kernel<4>), dim3(grid), dim3(kBlock), 0, s, a);

@@ -54,8 +54,11 @@ extern "C" {
 #endif
 
 /* Element types.  bf16 is reduced in fp32 and narrowed once with
- * round-to-nearest-even. */
-typedef enum { COLL_F32 = 0, COLL_BF16 = 1, COLL_I32 = 2 } coll_dtype_t;
+ * round-to-nearest-even.  COLL_U8 is raw bytes (e.g. FP8 payloads): the
+ * data-movement calls (Broadcast, AllGather, Gather, Scatter, All-to-All,
+ * Alltoallv, coll_moe_pack) accept it; the reductions and the combine
+ * return COLL_ERR_INVALID_ARG for it. */
+typedef enum { COLL_F32 = 0, COLL_BF16 = 1, COLL_I32 = 2, COLL_U8 = 3 } coll_dtype_t;
 
 /* Elementwise reduction ([A] preamble: + is sum, min or max).
  * COLL_AVG: the sum in the schedule's order, then divided by p ([A] 1.4:
@@ -237,6 +240,53 @@ coll_status_t coll_moe_combine(const void* const* back, const int32_t* const* po
                                const float* const* weights, const void* const* residual,
                                void* const* out, int p, size_t tokens_per_rank, int k, size_t hidden,
                                coll_dtype_t dtype, void* stream);
+
+/* FP8 e4m3 dispatch ([A] 4.3 quantized communication: the dispatch
+ * payload travels as FP8 e4m3, the combine stays bf16, halving the
+ * dispatch bytes).  Format: OCP E4M3 (sign, 4 exponent bits with bias 7,
+ * 3 mantissa bits, subnormals m * 2^-9, no infinities, S.1111.111 NaN,
+ * largest finite 448).  Each token row of `hidden` bf16 values is cut into
+ * groups of `group` consecutive elements; per group, in fp32 with every
+ * operation rounded to nearest even:
+ *   amax  = max(max |x|, 2^-110),  inv = 448 / amax,  scale = amax / 448,
+ *   code  = e4m3(x * inv), round to nearest even, saturating at +-448.
+ * Packed row (coll_moe_fp8_row_bytes(hidden, group) bytes, a multiple of
+ * 16): the hidden codes, then the hidden/group fp32 scales, then zero
+ * bytes.  Shapes: group divides hidden; group is a power of two in
+ * [16, 1024] or a multiple of 1024; hidden <= 16384 (else
+ * COLL_ERR_UNSUPPORTED).  Non-finite inputs give unspecified codes. */
+
+/* Bytes of one packed FP8 row, or 0 if (hidden, group) is not accepted. */
+size_t coll_moe_fp8_row_bytes(size_t hidden, size_t group);
+
+/* Quantizing dispatch pack: coll_moe_pack for bf16 tokens, writing FP8
+ * rows.  tokens[i]: T rows of `hidden` bf16; dest, pos, status_dev as
+ * coll_moe_pack; packed[i]: T*k rows of row_bytes bytes, row pos[i][a]
+ * the encoded token a / k; counts_dev [p][p] int64 in BYTES (rows *
+ * row_bytes), the forward matrix for coll_alltoallv with COLL_U8;
+ * counts_hidden_dev (optional, may be NULL) the same matrix in rows *
+ * hidden, the forward matrix of the bf16 reverse exchange
+ * (coll_alltoallv_transposed of the experts' bf16 rows).  tokens and
+ * packed must be 16-byte aligned.  No output may overlap another buffer. */
+coll_status_t coll_moe_pack_fp8(const void* const* tokens, const int32_t* const* dest,
+                                void* const* packed, int32_t* const* pos, int64_t* counts_dev,
+                                int64_t* counts_hidden_dev, int32_t* status_dev, int p,
+                                size_t tokens_per_rank, int k, size_t hidden, size_t group,
+                                void* stream);
+
+/* Dequantization of received FP8 rows for a bf16 consumer:
+ * y = bf16(decode(code) * scale), the product rounded to fp32 first.
+ * Rank j received sum_i counts_dev[i*p + j] bytes (the forward matrix of
+ * coll_moe_pack_fp8, after coll_alltoallv): recv[j] holds those rows in
+ * arrival order, out[j] gets the same number of bf16 rows of `hidden`.
+ * rows_cap: host int64[p], rows that recv[j] and out[j] hold.  Checked on
+ * the device: every count a non-negative multiple of row_bytes and each
+ * rank's total within rows_cap; otherwise nothing is written and
+ * *status_dev (optional device int32) is 1, else 0.  recv and out must be
+ * 16-byte aligned and may not overlap. */
+coll_status_t coll_moe_dequant_fp8(const void* const* recv, void* const* out, int p,
+                                   const int64_t* counts_dev, const int64_t* rows_cap,
+                                   int32_t* status_dev, size_t hidden, size_t group, void* stream);
 
 /* One AllReduce of a batch (host-side view). */
 typedef struct {

@@ -63,32 +63,24 @@ def e4m3_encode(values: np.ndarray) -> np.ndarray:
     v = np.asarray(values, dtype=np.float32).astype(np.float64)
     neg = np.signbit(v)
     a = np.abs(v)
-    out = np.zeros(v.shape, dtype=np.uint8)
-    for idx in np.ndindex(v.shape):
-        x = a[idx]
-        if np.isnan(x):
-            code = 0x7F
-        elif x >= E4M3_MAX:
-            code = 0x7E
-        else:
-            # the spacing of e4m3 values around x
-            if x < _MIN_NORMAL:
-                quantum = _SUB_QUANTUM
-            else:
-                _, ex = np.frexp(x)          # x = f * 2^ex, f in [0.5, 1)
-                quantum = 2.0 ** (int(ex) - 1 - 3)
-            q = np.rint(x / quantum) * quantum   # exact in fp64; rint ties to even
-            if q == 0.0:
-                code = 0
-            elif q < _MIN_NORMAL:
-                code = int(q / _SUB_QUANTUM)
-            else:
-                _, ex = np.frexp(q)
-                e = int(ex) - 1
-                m = int((q / 2.0 ** e - 1.0) * 8.0)
-                code = ((e + 7) << 3) | m
-        out[idx] = code | (0x80 if neg[idx] else 0)
-    return out
+    nan = np.isnan(a)
+    a = np.where(nan, 0.0, np.minimum(a, E4M3_MAX))      # saturation
+    # spacing of the e4m3 values around a: 2^(e-3) for a in [2^e, 2^(e+1)),
+    # and the subnormal quantum 2^-9 below the smallest normal 2^-6
+    _, ex = np.frexp(a)                                   # a = f * 2^ex, f in [0.5, 1)
+    e = np.maximum(ex.astype(np.int64) - 1, -6)
+    quantum = np.exp2(e - 3.0)
+    q = np.rint(a / quantum) * quantum                    # exact in fp64; rint ties to even
+    # code of the representable value q
+    _, qx = np.frexp(q)
+    qe = qx.astype(np.int64) - 1
+    normal = q >= _MIN_NORMAL
+    qe_n = np.where(normal, qe, 0)
+    mant = np.where(normal, (q / np.exp2(qe_n) - 1.0) * 8.0, q / _SUB_QUANTUM)
+    field = np.where(normal, qe_n + 7, 0)
+    code = (field << 3) | np.rint(mant).astype(np.int64)
+    code = np.where(nan, 0x7F, code)
+    return (code | np.where(neg, 0x80, 0)).astype(np.uint8)
 
 
 # ----------------------------------------------------------------------------

@@ -77,7 +77,10 @@ def test_invalid_arguments_rejected():
     n = 1000
     assert L.coll_allreduce(s, r, 0, n, 0, 0, None) == INV            # p = 0
     assert L.coll_allreduce(s, r, 65, n, 0, 0, None) == INV           # p > 64
-    assert L.coll_allreduce(s, r, 4, n, 3, 0, None) == INV            # bad dtype
+    assert L.coll_allreduce(s, r, 4, n, 3, 0, None) == INV            # bytes: no arithmetic
+    assert L.coll_allreduce(s, r, 4, n, 4, 0, None) == INV            # bad dtype
+    assert L.coll_reduce_scatter(s, r, 4, n, 3, 0, None) == INV
+    assert L.coll_reduce(s, base + 0x20000000, 4, n, 3, 0, 0, None) == INV
     assert L.coll_allreduce(s, r, 4, n, 0, 4, None) == INV            # bad op (4 is internal)
     assert L.coll_allreduce(s, r, 4, n, 0, -1, None) == INV           # bad op
     assert L.coll_allreduce_premul(s, r, 4, n, 0, None, 0, None) == INV   # no scales
@@ -121,6 +124,48 @@ def test_invalid_arguments_rejected():
     assert L.coll_moe_combine(s, s, s, None, r, 4, 10, 2, 16, 2, None) == coll.COLL_ERR_UNSUPPORTED  # int32
     assert L.coll_moe_combine(s, s, s, None, None, 4, 10, 2, 16, 0, None) == INV  # no outputs
     assert L.coll_alltoallv_transposed(s, r, 4, None, caps, caps, None, 0, None) == INV
+    assert L.coll_moe_combine(s, s, s, None, r, 4, 10, 2, 16, 3, None) == INV    # bytes: no arithmetic
+
+
+def test_fp8_row_bytes():
+    rb = coll.coll_moe_fp8_row_bytes
+    assert rb(7168, 128) == 7168 + 56 * 4
+    assert rb(7168, 7168) == 7168 + 16          # one scale, padded to 16 bytes
+    assert rb(16384, 16384) == 16384 + 16
+    assert rb(96, 16) == 96 + 32
+    assert rb(2048, 2048) == 2048 + 16 and rb(6144, 3072) == 6144 + 16
+    for hidden, group in [(100, 16), (7168, 48), (7168, 0), (0, 16), (32768, 1024), (96, 8), (3072, 1536)]:
+        assert rb(hidden, group) == 0, (hidden, group)
+
+
+@host_only
+def test_fp8_invalid_arguments_rejected():
+    L = coll.lib()
+    INV, UNS = coll.COLL_ERR_INVALID_ARG, coll.COLL_ERR_UNSUPPORTED
+    base = 0x7F0000000000
+    tok, _k1 = _arr([base + 0x1000000 * r for r in range(4)])
+    dst, _k2 = _arr([base + 0x10000000 + 0x1000000 * r for r in range(4)])
+    pk, _k3 = _arr([base + 0x20000000 + 0x1000000 * r for r in range(4)])
+    ps, _k4 = _arr([base + 0x30000000 + 0x1000000 * r for r in range(4)])
+    cnt = base + 0x40000000
+    T, k, H = 10, 2, 256
+    assert L.coll_moe_pack_fp8(tok, dst, pk, ps, cnt, None, None, 4, T, k, 192, 48, None) == UNS  # group shape
+    assert L.coll_moe_pack_fp8(tok, dst, pk, ps, cnt, None, None, 4, T, k, 100, 16, None) == INV  # group does not divide
+    assert L.coll_moe_pack_fp8(tok, dst, pk, ps, cnt, None, None, 4, T, k, 32768, 1024, None) == UNS  # hidden too large
+    assert L.coll_moe_pack_fp8(tok, dst, pk, ps, cnt, None, None, 4, T, 0, H, 128, None) == INV   # k = 0
+    assert L.coll_moe_pack_fp8(tok, dst, pk, ps, None, None, None, 4, T, k, H, 128, None) == INV  # no counts
+    bad, _k5 = _arr([base + 8, base + 0x1000000, base + 0x2000000, base + 0x3000000])
+    assert L.coll_moe_pack_fp8(bad, dst, pk, ps, cnt, None, None, 4, T, k, H, 128, None) == INV  # tokens not 16-aligned
+    assert L.coll_moe_pack_fp8(tok, dst, bad, ps, cnt, None, None, 4, T, k, H, 128, None) == INV  # packed not 16-aligned
+    assert L.coll_moe_pack_fp8(tok, dst, tok, ps, cnt, None, None, 4, T, k, H, 128, None) == coll.COLL_ERR_ALIAS
+    caps = (ctypes.c_int64 * 4)(10, 10, 10, 10)
+    neg = (ctypes.c_int64 * 4)(10, -1, 10, 10)
+    assert L.coll_moe_dequant_fp8(pk, tok, 4, cnt, None, None, H, 128, None) == INV        # no capacities
+    assert L.coll_moe_dequant_fp8(pk, tok, 4, cnt, neg, None, H, 128, None) == INV
+    assert L.coll_moe_dequant_fp8(pk, tok, 4, None, caps, None, H, 128, None) == INV       # no counts
+    assert L.coll_moe_dequant_fp8(bad, tok, 4, cnt, caps, None, H, 128, None) == INV       # recv not 16-aligned
+    assert L.coll_moe_dequant_fp8(pk, tok, 4, cnt, caps, None, 192, 48, None) == UNS
+    assert L.coll_moe_dequant_fp8(pk, pk, 4, cnt, caps, None, H, 128, None) == coll.COLL_ERR_ALIAS
 
 
 @host_only

@@ -723,6 +723,164 @@ def test_moe_misaligned_rows(coll):
 
 
 # ----------------------------------------------------------------------------
+# FP8 e4m3 dispatch: quantizing pack, byte exchange, dequantization
+# ----------------------------------------------------------------------------
+
+def _u8(n, fill=0):
+    import torch
+    return torch.full((max(int(n), 1),), fill, dtype=torch.uint8, device="cuda")
+
+
+FP8_SHAPES = [  # p, T, k, hidden, group
+    (1, 3, 1, 16, 16), (2, 5, 2, 48, 16), (3, 100, 2, 256, 128), (4, 33, 3, 7168, 128),
+    (2, 9, 2, 7168, 7168), (8, 64, 2, 4096, 2048), (3, 7, 8, 1024, 1024), (2, 6, 1, 16384, 128),
+    (2, 4, 2, 16384, 16384), (16, 20, 2, 2048, 64), (5, 50, 4, 960, 32)]
+
+
+@pytest.mark.parametrize("p,T,k,H,G", FP8_SHAPES)
+def test_moe_pack_fp8(coll, p, T, k, H, G):
+    import torch
+    from oracle import fp8
+    R = coll.coll_moe_fp8_row_bytes(H, G)
+    assert R == fp8.row_bytes(H, G)
+    toks, routes, _ = _moe_case(p, T, k, H, BF16, 300 + T + H)
+    dtok = [to_dev(x, BF16) for x in toks]
+    packed = [_u8(T * k * R, 0xA5) for _ in range(p)]
+    pos = [torch.full((T * k,), -5, dtype=torch.int32, device="cuda") for _ in range(p)]
+    counts = torch.full((p * p,), -1, dtype=torch.int64, device="cuda")
+    counts_h = torch.full((p * p,), -1, dtype=torch.int64, device="cuda")
+    status = torch.full((p,), -9, dtype=torch.int32, device="cuda")
+    coll.coll_moe_pack_fp8(dtok, [_i32dev(r) for r in routes], packed, pos, counts, k, H, G,
+                           counts_hidden_dev=counts_h, status_dev=status)
+    sync()
+    assert status.cpu().tolist() == [0] * p
+    c = counts.cpu().numpy().reshape(p, p)
+    ch = counts_h.cpu().numpy().reshape(p, p)
+    for i in range(p):
+        ec, epos, epk = fp8.moe_pack_fp8(toks[i], routes[i], k, H, G, p)
+        assert list(c[i]) == list(ec), f"byte counts rank {i}"
+        assert list(ch[i]) == list(ec // R * H), f"hidden counts rank {i}"
+        assert pos[i].cpu().numpy().tolist() == epos.tolist(), f"pos rank {i}"
+        assert_bits_equal(packed[i].cpu().numpy(), epk, f"fp8 rows rank {i} (H={H}, G={G})")
+
+
+def test_moe_pack_fp8_rejects_bad_destination(coll):
+    import torch
+    from oracle import fp8
+    p, T, k, H, G = 4, 21, 2, 256, 128
+    R = fp8.row_bytes(H, G)
+    toks, routes, _ = _moe_case(p, T, k, H, BF16, 310)
+    routes[3] = routes[3].copy()
+    routes[3][5] = -1
+    packed = [_u8(T * k * R, 0x3C) for _ in range(p)]
+    pos = [torch.zeros(T * k, dtype=torch.int32, device="cuda") for _ in range(p)]
+    counts = torch.zeros(p * p, dtype=torch.int64, device="cuda")
+    status = torch.full((p,), -9, dtype=torch.int32, device="cuda")
+    coll.coll_moe_pack_fp8([to_dev(x, BF16) for x in toks], [_i32dev(r) for r in routes], packed, pos,
+                           counts, k, H, G, status_dev=status)
+    sync()
+    assert status.cpu().tolist() == [0, 0, 0, 1]
+    assert counts.cpu().numpy().reshape(p, p)[3].tolist() == [0] * p
+    assert pos[3].cpu().numpy().tolist() == [-1] * (T * k)
+    assert bool((packed[3] == 0x3C).all()), "payload written for a rejected rank"
+    _, _, epk = fp8.moe_pack_fp8(toks[0], routes[0], k, H, G, p)
+    assert_bits_equal(packed[0].cpu().numpy(), epk, "other ranks packed normally")
+
+
+@pytest.mark.parametrize("p,T,k,H,G", [(2, 40, 1, 128, 16), (4, 150, 2, 1024, 128), (8, 64, 8, 2048, 2048)])
+@pytest.mark.parametrize("with_residual", [False, True])
+def test_moe_fp8_round_trip_and_combine(coll, p, T, k, H, G, with_residual):
+    """FP8 pack -> alltoallv (bytes) -> dequant (the experts' bf16 input;
+    the expert itself is the identity) -> bf16 alltoallv_transposed ->
+    combine, every stage against the oracle."""
+    import torch
+    from oracle import fp8
+    R = fp8.row_bytes(H, G)
+    toks, routes, weights = _moe_case(p, T, k, H, BF16, 320 + T + k)
+    packed = [_u8(T * k * R) for _ in range(p)]
+    pos = [torch.empty(T * k, dtype=torch.int32, device="cuda") for _ in range(p)]
+    counts = torch.empty(p * p, dtype=torch.int64, device="cuda")
+    counts_h = torch.empty(p * p, dtype=torch.int64, device="cuda")
+    coll.coll_moe_pack_fp8([to_dev(x, BF16) for x in toks], [_i32dev(r) for r in routes], packed, pos,
+                           counts, k, H, G, counts_hidden_dev=counts_h)
+    sync()
+    packs = [fp8.moe_pack_fp8(toks[i], routes[i], k, H, G, p) for i in range(p)]
+    C = np.stack([pk[0] for pk in packs])
+    assert np.array_equal(counts.cpu().numpy().reshape(p, p), C)
+    rows = C.sum(axis=0) // R
+    recv = [_u8(max(r, 1) * R, 0x77) for r in rows]
+    coll.coll_alltoallv(packed, recv, counts, recv_cap=[int(max(r, 1) * R) for r in rows])
+    ex_in = [empty(int(max(r, 1)) * H, BF16, fill=0) for r in rows]
+    status = torch.full((1,), -9, dtype=torch.int32, device="cuda")
+    coll.coll_moe_dequant_fp8(recv, ex_in, counts, [int(max(r, 1)) for r in rows], H, G, status_dev=status)
+    sync()
+    assert int(status.item()) == 0
+    exp_recv = ref.alltoallv([pk[2] for pk in packs], C)
+    for j in range(p):
+        assert_bits_equal(recv[j].cpu().numpy()[:int(rows[j]) * R], exp_recv[j], f"fp8 dispatch dest {j}")
+        assert_bits_equal(to_host(ex_in[j], BF16)[:int(rows[j]) * H], fp8.dequantize_rows(exp_recv[j], H, G),
+                          f"dequant dest {j}")
+    back = [empty(T * k * H, BF16, fill=0) for _ in range(p)]
+    coll.coll_alltoallv_transposed(ex_in, back, counts_h, send_cap=[int(max(r, 1)) * H for r in rows])
+    residual = gen(p, T * H, BF16, 330) if with_residual else None
+    out = [to_dev(r, BF16) for r in residual] if with_residual else [empty(T * H, BF16) for _ in range(p)]
+    coll.coll_moe_combine(back, pos, [_f32dev(w) for w in weights], out, k, H,
+                          residual=out if with_residual else None)
+    sync()
+    for i in range(p):
+        deq = fp8.dequantize_rows(packs[i][2], H, G)
+        assert_bits_equal(to_host(back[i], BF16), deq, f"returned rows rank {i}")
+        expect = ref.moe_combine(deq, packs[i][1], weights[i], k, H, BF16,
+                                 residual[i] if with_residual else None)
+        assert_bits_equal(to_host(out[i], BF16), expect, f"fp8 combine rank {i}")
+
+
+def test_moe_dequant_fp8_rejects_bad_counts(coll):
+    import torch
+    from oracle import fp8
+    p, H, G = 3, 256, 64
+    R = fp8.row_bytes(H, G)
+    recv = [_u8(4 * R, 0) for _ in range(p)]
+    out = [empty(4 * H, BF16, fill=0x1234) for _ in range(p)]
+    status = torch.full((1,), -9, dtype=torch.int32, device="cuda")
+    good = np.array([[R, 0, R], [0, 2 * R, R], [R, R, 0]], dtype=np.int64)
+    for bad in (good + np.array([[0, 0, 0], [0, 1, 0], [0, 0, 0]]),        # not a whole row
+                good * np.array([[1, 1, 1], [1, 1, 4], [1, 1, 1]]),        # rank 2 over capacity
+                good * np.array([[1, 1, 1], [1, 1, -1], [1, 1, 1]])):      # negative
+        dc = torch.from_numpy(bad.reshape(-1).copy()).cuda()
+        coll.coll_moe_dequant_fp8(recv, out, dc, [4, 4, 4], H, G, status_dev=status)
+        sync()
+        assert int(status.item()) == 1
+        for o in out:
+            assert torch.equal(o, empty(4 * H, BF16, fill=0x1234)), "output written despite bad counts"
+    dc = torch.from_numpy(good.reshape(-1).copy()).cuda()
+    coll.coll_moe_dequant_fp8(recv, out, dc, [4, 4, 4], H, G, status_dev=status)
+    sync()
+    assert int(status.item()) == 0
+
+
+def test_u8_copy_collectives(coll):
+    """Byte payloads through the data-movement calls, including the
+    element-wise path (bases that disagree modulo 16)."""
+    import torch
+    p, n = 5, 1000 + 3
+    hx = [np.random.default_rng(400 + r).integers(0, 256, p * n).astype(np.uint8) for r in range(p)]
+    send = [torch.from_numpy(x).cuda() for x in hx]
+    recv = [_u8(p * n) for _ in range(p)]
+    coll.coll_alltoall(send, recv, n)
+    sync()
+    for j, e in enumerate(ref.alltoall(hx)):
+        assert_bits_equal(recv[j].cpu().numpy(), e, f"u8 alltoall {j}")
+    big = [_u8(p * n + 16) for _ in range(p)]
+    shifted = [b[1 + (r % 3):1 + (r % 3) + p * n] for r, b in enumerate(big)]
+    coll.coll_allgather([s[:n] for s in send], shifted, n)
+    sync()
+    exp = ref.allgather([x[:n] for x in hx])
+    for j in range(p):
+        assert_bits_equal(shifted[j].cpu().numpy(), exp[j], f"u8 allgather misaligned {j}")
+
+
+# ----------------------------------------------------------------------------
 # Batched AllReduce
 # ----------------------------------------------------------------------------
 
