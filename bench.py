@@ -58,7 +58,7 @@ def parse_args(argv=None):
     ap.add_argument("--no-collectives", action="store_true", help="time only the main step")
     ap.add_argument("--only", default=None,
                     help="comma list of extra collectives to time (ar_ring, ar_onepass, ar_hd, "
-                         "ar_literal, ar_avg, ar_premul, a2a, a2av, moe, gs, ar_small, batch, copy)")
+                         "ar_literal, ar_avg, ar_premul, a2a, a2av, moe, moe_fp8, gs, ar_small, batch, copy)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
     return ap.parse_args(argv)
 
@@ -324,6 +324,10 @@ def extra_collectives(torch, coll, inputs, metrics, dev, which, iters=10, warmup
     # --- MoE dispatch and combine around the ragged exchange -----------------
     if want("moe"):
         rows.append(moe_row(torch, coll, inputs, dev, iters, warmup))
+        torch.cuda.empty_cache()
+    if want("moe_fp8"):
+        rows.append(moe_fp8_row(torch, coll, inputs, dev, iters, warmup))
+        torch.cuda.empty_cache()
 
     # --- Gather / Scatter, p = 8, 2^23 bf16 per rank (root buffer 128 MiB) ----
     if want("gs"):
@@ -416,6 +420,56 @@ def moe_row(torch, coll, inputs, dev, iters, warmup):
             "t_med_us": round(tot_us, 2), "hbm_bytes": tot_b, "hbm_GBps": round(tot_b / (tot_us * 1e-6) / 1e9, 1),
             "pct_hbm_peak": round(100.0 * tot_b / (tot_us * 1e-6) / 1e9 / HBM_PEAK, 1), "stages": stage,
             "workload": "pack -> Alltoallv -> reverse Alltoallv -> weighted combine + residual"}
+
+
+def moe_fp8_row(torch, coll, inputs, dev, iters, warmup):
+    """The same MoE layer with the dispatch in FP8 e4m3 (one fp32 scale per
+    128 elements): quantizing pack -> byte Alltoallv -> dequant (the experts'
+    bf16 input) -> bf16 reverse Alltoallv -> weighted combine + residual."""
+    p, T, H, k, G = 8, 4096, 7168, 2, 128
+    A = T * k
+    R = coll.coll_moe_fp8_row_bytes(H, G)
+    toks = [to_dev(torch, x, dev) for x in inputs.rank_buffers(inputs.WL_MOE_A2A, p, T * H, inputs.BF16,
+                                                               dist="normal")]
+    dest = [torch.from_numpy(r).to(dev) for r in inputs.moe_routes(p, T, k)]
+    wts = [torch.from_numpy(w).to(dev) for w in inputs.moe_weights(p, T, k)]
+    packed = [torch.empty(A * R, dtype=torch.uint8, device=dev) for _ in range(p)]
+    pos = [torch.empty(A, dtype=torch.int32, device=dev) for _ in range(p)]
+    counts = torch.empty(p * p, dtype=torch.int64, device=dev)
+    counts_h = torch.empty(p * p, dtype=torch.int64, device=dev)
+    f_pack = coll.coll_moe_pack_fp8(toks, dest, packed, pos, counts, k, H, G, counts_hidden_dev=counts_h,
+                                    defer=True)
+    f_pack()
+    torch.cuda.synchronize()
+    rows = counts.cpu().numpy().reshape(p, p).sum(axis=0) // R
+    recv = [torch.empty(int(r) * R, dtype=torch.uint8, device=dev) for r in rows]
+    ex_in = [torch.empty(int(r) * H, dtype=torch.bfloat16, device=dev) for r in rows]
+    back = [torch.empty(A * H, dtype=torch.bfloat16, device=dev) for _ in range(p)]
+    out = [torch.empty(T * H, dtype=torch.bfloat16, device=dev).normal_() for _ in range(p)]
+    f_disp = coll.coll_alltoallv(packed, recv, counts, defer=True)
+    f_deq = coll.coll_moe_dequant_fp8(recv, ex_in, counts, [int(r) for r in rows], H, G, defer=True)
+    f_rev = coll.coll_alltoallv_transposed(ex_in, back, counts_h, defer=True)
+    f_comb = coll.coll_moe_combine(back, pos, wts, out, k, H, residual=out, defer=True)
+    t = [stats_us(x)[0] for x in time_launches(torch, [f_pack, f_disp, f_deq, f_rev, f_comb], iters, warmup)]
+    b_pack = p * (T * H * 2 + A * R + A * 4 * 2)      # tokens once, A fp8 rows out, dest, pos
+    b_disp = p * 2 * A * R
+    b_deq = p * (A * R + A * H * 2)
+    b_rev = p * 2 * A * H * 2
+    b_comb = p * (A * H * 2 + 2 * T * H * 2 + A * 8)
+    stage = {}
+    for name, us, b in (("pack_fp8", t[0], b_pack), ("dispatch_alltoallv_fp8", t[1], b_disp),
+                        ("dequant_fp8", t[2], b_deq), ("reverse_alltoallv_bf16", t[3], b_rev),
+                        ("combine", t[4], b_comb)):
+        stage[name] = {"t_med_us": round(us, 2), "hbm_bytes": b, "hbm_GBps": round(b / (us * 1e-6) / 1e9, 1)}
+    tot_us = sum(t)
+    tot_b = b_pack + b_disp + b_deq + b_rev + b_comb
+    return {"name": "moe_fp8_dispatch_bf16_combine", "p": p, "tokens": T, "hidden": H, "top_k": k, "group": G,
+            "row_bytes": R, "dtype": "fp8e4m3/bf16", "t_med_us": round(tot_us, 2),
+            "dispatch_path_us": round(t[0] + t[1], 2),
+            "dispatch_bytes_per_row_vs_bf16": round(R / (H * 2), 4),
+            "hbm_bytes": tot_b, "hbm_GBps": round(tot_b / (tot_us * 1e-6) / 1e9, 1),
+            "pct_hbm_peak": round(100.0 * tot_b / (tot_us * 1e-6) / 1e9 / HBM_PEAK, 1), "stages": stage,
+            "workload": "FP8 pack -> byte Alltoallv -> dequant -> bf16 reverse Alltoallv -> combine + residual"}
 
 
 def batch_row(torch, coll, inputs, dev, iters=5, warmup=2):

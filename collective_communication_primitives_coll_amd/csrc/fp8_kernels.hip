@@ -14,9 +14,11 @@
 // 448/amax and encoded, and the codes, scales and padding are written to
 // the packed row of every slot (assignment) of the token.
 //
-// Encoding rescales |y| by a power of two so that its e4m3 neighbours
-// become consecutive integers, rounds to even there, and assembles the
-// code; one formula serves the normal and the subnormal range.
+// Encoding and decoding use the gfx950 FP8 conversion instructions, which
+// implement OCP E4M3 with round to nearest even; magnitudes are clamped to
+// 448 before encoding (the format's saturating reading).  Their results
+// were compared with the format's definition for every fp32 bit pattern
+// up to infinity (encode) and every code (decode).
 //
 // Dequant: one wave per received row; codes decode exactly to fp32, are
 // multiplied by the group scale and narrowed to bf16 (round to nearest
@@ -28,36 +30,24 @@ namespace coll {
 namespace {
 
 constexpr int kLanes = 64;
-constexpr int kDeqBatch = 4;  // units per lane loaded together in the dequant
 
 __device__ __forceinline__ uint64_t fp8_wave_id() {
   return (uint64_t)blockIdx.x * (kBlock / kLanes) + (uint64_t)__builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
 }
 __device__ __forceinline__ uint64_t fp8_wave_count() { return (uint64_t)gridDim.x * (kBlock / kLanes); }
 
-// e4m3 code of an fp32 value: nearest, ties to even, saturating at +-448.
-// With E = max(exponent of |y|, -6), the e4m3 neighbours of |y| are the
-// multiples of 2^(E-3), so m = rint(|y| * 2^(3-E)) is the rounded
-// significand: 8..16 in the normal range (16 carries into the next
-// binade) and 0..8 for |y| < 2^-6 (the subnormals, 8 being 2^-6).  Then
-// code = ((E + 7) << 3) + m - 8 covers both ranges.  Clamping |y| to 448
-// first gives the saturation.
-__device__ __forceinline__ uint32_t e4m3_code(float y) {
-  const uint32_t u = __float_as_uint(y);
-  const uint32_t a = min(u & 0x7fffffffu, 0x43e00000u);  // |y| clamped to 448
-  const uint32_t eb = max(a >> 23, 121u);                // biased exponent, at least 127 - 6
-  const float m = __builtin_rintf(__builtin_ldexpf(__uint_as_float(a), 130 - (int)eb));
-  uint32_t c = ((eb - 120u) << 3) + (uint32_t)m - 8u;
-  if ((u & 0x7fffffffu) > 0x7f800000u) c = 0x7fu;        // NaN
-  return c | ((u >> 24) & 0x80u);
-}
-
-// Exact fp32 value of an e4m3 code.
-__device__ __forceinline__ float e4m3_value(uint32_t c) {
-  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
-  if (e == 15u && m == 7u) v = __uint_as_float(0x7fc00000u);
-  return (c & 0x80u) ? -v : v;
+// Four e4m3 codes (bytes 0..3) of four fp32 values: round to nearest
+// even through the gfx950 conversion instruction (v_cvt_pk_fp8_f32, OCP
+// E4M3), after clamping to +-448 so that larger magnitudes saturate
+// instead of becoming NaN.
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
+  a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+  b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+  c = __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f);
+  d = __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
 }
 
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
@@ -82,108 +72,192 @@ __device__ __forceinline__ u32x4 unit_codes(const u32x4& x0, const u32x4& x1, fl
   for (int q = 0; q < 4; ++q) {
     const u32x4& x = q < 2 ? x0 : x1;
     const uint32_t w0 = x[2 * (q & 1)], w1 = x[2 * (q & 1) + 1];
-    out[q] = e4m3_code(bf16_lo(w0) * inv) | (e4m3_code(bf16_hi(w0) * inv) << 8) |
-             (e4m3_code(bf16_lo(w1) * inv) << 16) | (e4m3_code(bf16_hi(w1) * inv) << 24);
+    out[q] = e4m3_pack4(bf16_lo(w0) * inv, bf16_hi(w0) * inv, bf16_lo(w1) * inv, bf16_hi(w1) * inv);
   }
   return out;
 }
 
 }  // namespace
 
-// UMAX: units (16 elements) per lane the row needs, rounded up to a power
-// of two; hidden <= 64 * 16 * UMAX.
-template <int UMAX>
-COLL_STREAM_KERNEL void moe_pack_fp8_kernel(Fp8Args a) {
+// Shared by both pack kernels: the token rows of wave-strided (rank, t),
+// skipping tokens with no valid slot (a rejected rank has none).
+struct PackRow {
+  const int32_t* pp;  // pos of the token's k slots
+  const u32x4* src;   // the token row, two vectors per unit
+  int rank;
+};
+
+__device__ __forceinline__ bool pack_row(const Fp8Args& a, uint64_t r, PackRow& out) {
+  const int rank = (int)(r / a.tokens);
+  const uint64_t t = r - (uint64_t)rank * a.tokens;
+  const uint64_t A = a.tokens * (uint64_t)a.k;
+  const int32_t* pp = a.pos[rank] + t * (uint64_t)a.k;
+  bool any = false;
+  for (int s = 0; s < a.k; ++s) {
+    const int32_t ps = pp[s];
+    any |= ps >= 0 && (uint64_t)ps < A;
+  }
+  out.pp = pp;
+  out.src = reinterpret_cast<const u32x4*>((const uint16_t*)a.src[rank] + t * a.hidden);
+  out.rank = rank;
+  return any;
+}
+
+// Groups of at most 1024 elements (g16 <= 64 units): every group lies in
+// one unit column (64 adjacent units), so a row streams through in
+// batches of CB columns and any hidden size works.
+constexpr int kPackCols = 8;
+
+template <int CB>
+COLL_STREAM_KERNEL void moe_pack_fp8_cols_kernel(Fp8Args a) {
 #pragma clang fp contract(off)
   const int lane = (int)(threadIdx.x % kLanes);
   const uint64_t H = a.hidden, R = a.row_bytes;
   const int k = a.k;
   const uint64_t A = a.tokens * (uint64_t)k;
-  const uint32_t nunits = (uint32_t)(H / 16);             // <= 1024
-  const uint32_t g16 = (uint32_t)(a.group / 16);          // units per group
-  const uint32_t gu = g16 > kLanes ? g16 / kLanes : 1u;   // unit columns per group (large groups)
+  const uint32_t nunits = (uint32_t)(H / 16);
+  const uint32_t ncols = (nunits + kLanes - 1) / kLanes;
+  const uint32_t g16 = (uint32_t)(a.group / 16);          // a power of two <= 64
+  const uint32_t gsh = 31u - (uint32_t)__builtin_clz(g16);
   const uint32_t ngroups = (uint32_t)(H / a.group);
-  const uint32_t npad = (uint32_t)((R - H) / 4) - ngroups;  // zero scale slots
+  const uint32_t npad = (uint32_t)((R - H) / 4) - ngroups;
   const uint64_t rows = a.tokens * (uint64_t)a.p;
   for (uint64_t r = fp8_wave_id(); r < rows; r += fp8_wave_count()) {
-    const int rank = (int)(r / a.tokens);
-    const uint64_t t = r - (uint64_t)rank * a.tokens;
-    const int32_t* pp = a.pos[rank] + t * (uint64_t)k;
-    bool any = false;
-    for (int s = 0; s < k; ++s) {
-      const int32_t ps = pp[s];
-      any |= ps >= 0 && (uint64_t)ps < A;
+    PackRow pr;
+    if (!pack_row(a, r, pr)) continue;
+    for (uint32_t c0 = 0; c0 < ncols; c0 += CB) {
+      u32x4 x[CB][2];
+      uint32_t mb[CB];
+#pragma unroll
+      for (int u = 0; u < CB; ++u) {
+        const uint32_t j = (c0 + u) * kLanes + lane;
+        if (j < nunits) {
+          x[u][0] = ld16<true>(pr.src + 2 * j);
+          x[u][1] = ld16<true>(pr.src + 2 * j + 1);
+        } else {
+          x[u][0] = u32x4{0, 0, 0, 0};
+          x[u][1] = u32x4{0, 0, 0, 0};
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < CB; ++u) {
+        mb[u] = unit_amax_bits(x[u][0], x[u][1]);
+        for (uint32_t off = 1; off < g16; off <<= 1) mb[u] = max(mb[u], (uint32_t)__shfl_xor((int)mb[u], (int)off));
+      }
+      float sc[CB];
+#pragma unroll
+      for (int u = 0; u < CB; ++u) {
+        const float amax = fmaxf(__uint_as_float(mb[u] << 16), 0x1p-110f);
+        x[u][0] = unit_codes(x[u][0], x[u][1], 448.0f / amax);
+        sc[u] = amax / 448.0f;
+      }
+      for (int s = 0; s < k; ++s) {
+        const int32_t ps = pr.pp[s];
+        if (ps < 0 || (uint64_t)ps >= A) continue;
+        uint8_t* row = (uint8_t*)a.dst[pr.rank] + (uint64_t)ps * R;
+        u32x4* vc = reinterpret_cast<u32x4*>(row);
+        float* scales = reinterpret_cast<float*>(row + H);
+#pragma unroll
+        for (int u = 0; u < CB; ++u) {
+          const uint32_t j = (c0 + u) * kLanes + lane;
+          if (j < nunits) {
+            st16<true>(vc + j, x[u][0]);
+            if ((j & (g16 - 1)) == 0) scales[j >> gsh] = sc[u];
+          }
+        }
+      }
     }
-    if (!any) continue;
-    const u32x4* src = reinterpret_cast<const u32x4*>((const uint16_t*)a.src[rank] + t * H);
+    if ((uint32_t)lane < npad) {
+      for (int s = 0; s < k; ++s) {
+        const int32_t ps = pr.pp[s];
+        if (ps < 0 || (uint64_t)ps >= A) continue;
+        reinterpret_cast<float*>((uint8_t*)a.dst[pr.rank] + (uint64_t)ps * R + H)[ngroups + lane] = 0.0f;
+      }
+    }
+  }
+}
+
+// Groups spanning whole unit columns (group a multiple of 1024): the row
+// is held in registers, UMAX units per lane (a power of two, hidden <=
+// 64 * 16 * UMAX), and a group's amax is reduced over the wave and over
+// its gu columns before any code is written.
+template <int UMAX>
+COLL_STREAM_KERNEL void moe_pack_fp8_rows_kernel(Fp8Args a) {
+#pragma clang fp contract(off)
+  const int lane = (int)(threadIdx.x % kLanes);
+  const uint64_t H = a.hidden, R = a.row_bytes;
+  const int k = a.k;
+  const uint64_t A = a.tokens * (uint64_t)k;
+  const uint32_t nunits = (uint32_t)(H / 16);
+  const uint32_t g16 = (uint32_t)(a.group / 16);
+  const uint32_t gu = g16 / kLanes;                       // unit columns per group
+  const uint32_t ngroups = (uint32_t)(H / a.group);
+  const uint32_t npad = (uint32_t)((R - H) / 4) - ngroups;
+  const uint64_t rows = a.tokens * (uint64_t)a.p;
+  for (uint64_t r = fp8_wave_id(); r < rows; r += fp8_wave_count()) {
+    PackRow pr;
+    if (!pack_row(a, r, pr)) continue;
     u32x4 x[UMAX][2];
 #pragma unroll
     for (int u = 0; u < UMAX; ++u) {
       const uint32_t j = (uint32_t)(u * kLanes + lane);
       if (j < nunits) {
-        x[u][0] = ld16<true>(src + 2 * j);
-        x[u][1] = ld16<true>(src + 2 * j + 1);
+        x[u][0] = ld16<true>(pr.src + 2 * j);
+        x[u][1] = ld16<true>(pr.src + 2 * j + 1);
       } else {
         x[u][0] = u32x4{0, 0, 0, 0};
         x[u][1] = u32x4{0, 0, 0, 0};
       }
     }
-    uint32_t mb[UMAX];  // group amax as a bf16 magnitude pattern
-#pragma unroll
-    for (int u = 0; u < UMAX; ++u) mb[u] = unit_amax_bits(x[u][0], x[u][1]);
-    if (g16 <= (uint32_t)kLanes) {
-      // a group is g16 adjacent lanes of one unit column
-#pragma unroll
-      for (int u = 0; u < UMAX; ++u)
-        for (uint32_t off = 1; off < g16; off <<= 1) mb[u] = max(mb[u], (uint32_t)__shfl_xor((int)mb[u], (int)off));
-    } else {
-      // a group is gu whole unit columns
-#pragma unroll
-      for (int u = 0; u < UMAX; ++u)
-#pragma unroll
-        for (int off = 1; off < kLanes; off <<= 1) mb[u] = max(mb[u], (uint32_t)__shfl_xor((int)mb[u], off));
-      uint32_t gm[UMAX];
-#pragma unroll
-      for (int u = 0; u < UMAX; ++u) {
-        const uint32_t gi = (uint32_t)u / gu;
-        uint32_t m = 0;
-#pragma unroll
-        for (int v = 0; v < UMAX; ++v)
-          if ((uint32_t)v / gu == gi) m = max(m, mb[v]);
-        gm[u] = m;
-      }
-#pragma unroll
-      for (int u = 0; u < UMAX; ++u) mb[u] = gm[u];
-    }
-    // quantize in place: x[u][0] becomes the unit's 16 codes, am[u] its scale
-    float am[UMAX];
+    uint32_t mb[UMAX];
 #pragma unroll
     for (int u = 0; u < UMAX; ++u) {
-      const float amax = fmaxf(__uint_as_float(mb[u] << 16), 0x1p-110f);
+      mb[u] = unit_amax_bits(x[u][0], x[u][1]);
+#pragma unroll
+      for (int off = 1; off < kLanes; off <<= 1) mb[u] = max(mb[u], (uint32_t)__shfl_xor((int)mb[u], off));
+    }
+    uint32_t gm[UMAX];  // amax of the unit's group (all its columns)
+#pragma unroll
+    for (int u = 0; u < UMAX; ++u) {
+      const uint32_t gi = (uint32_t)u / gu;
+      uint32_t m = 0;
+#pragma unroll
+      for (int v = 0; v < UMAX; ++v)
+        if ((uint32_t)v / gu == gi) m = max(m, mb[v]);
+      gm[u] = m;
+    }
+    float sc[UMAX];
+#pragma unroll
+    for (int u = 0; u < UMAX; ++u) {
+      const float amax = fmaxf(__uint_as_float(gm[u] << 16), 0x1p-110f);
+      sc[u] = amax / 448.0f;
       x[u][0] = unit_codes(x[u][0], x[u][1], 448.0f / amax);
-      am[u] = amax / 448.0f;
     }
     for (int s = 0; s < k; ++s) {
-      const int32_t ps = pp[s];
+      const int32_t ps = pr.pp[s];
       if (ps < 0 || (uint64_t)ps >= A) continue;
-      uint8_t* row = (uint8_t*)a.dst[rank] + (uint64_t)ps * R;
+      uint8_t* row = (uint8_t*)a.dst[pr.rank] + (uint64_t)ps * R;
       u32x4* vc = reinterpret_cast<u32x4*>(row);
-      float* sc = reinterpret_cast<float*>(row + H);
+      float* scales = reinterpret_cast<float*>(row + H);
 #pragma unroll
       for (int u = 0; u < UMAX; ++u) {
         const uint32_t j = (uint32_t)(u * kLanes + lane);
         if (j < nunits) {
           st16<true>(vc + j, x[u][0]);
-          const bool lead = g16 <= (uint32_t)kLanes ? (j % g16) == 0 : (lane == 0 && (uint32_t)u % gu == 0);
-          if (lead) sc[j / g16] = am[u];
+          if (lane == 0 && (uint32_t)u % gu == 0) scales[(uint32_t)u / gu] = sc[u];
         }
       }
-      if ((uint32_t)lane < npad) sc[ngroups + lane] = 0.0f;
+      if ((uint32_t)lane < npad) scales[ngroups + lane] = 0.0f;
     }
   }
 }
 
 // out[rank] rows = dequantized received rows, in the order they arrived.
+// Each lane takes units of 16 codes (one 16-byte load, two 16-byte bf16
+// stores), DB units per lane loaded together.
+constexpr int kDeqUnits = 8;
+
+template <int DB>
 COLL_STREAM_KERNEL void moe_dequant_fp8_kernel(Fp8Args a) {
 #pragma clang fp contract(off)
   __shared__ int64_t start[kMaxRanks + 1];
@@ -216,8 +290,13 @@ COLL_STREAM_KERNEL void moe_dequant_fp8_kernel(Fp8Args a) {
   if (blockIdx.x == 0 && tid == 0 && a.status) *a.status = reject ? 1 : 0;
   if (reject) return;
   const int lane = tid % kLanes;
-  const uint64_t nunits = H / 16;
-  const uint64_t g16 = a.group / 16;
+  const uint32_t nunits = (uint32_t)(H / 16);
+  // scale of unit j: j >> gsh for groups inside a unit column (a power of
+  // two <= 64 units), else column / gu, the same for the whole wave
+  const uint32_t g16 = (uint32_t)(a.group / 16);
+  const bool in_col = g16 <= (uint32_t)kLanes;
+  const uint32_t gsh = in_col ? 31u - (uint32_t)__builtin_clz(g16) : 0u;
+  const uint32_t gu = in_col ? 1u : g16 / kLanes;
   const uint64_t total = (uint64_t)start[p];
   for (uint64_t g = fp8_wave_id(); g < total; g += fp8_wave_count()) {
     int rk = 0;
@@ -227,30 +306,30 @@ COLL_STREAM_KERNEL void moe_dequant_fp8_kernel(Fp8Args a) {
     const u32x4* vc = reinterpret_cast<const u32x4*>(src);
     const float* sc = reinterpret_cast<const float*>(src + H);
     u32x4* dst = reinterpret_cast<u32x4*>((uint16_t*)a.dst[rk] + row * H);
-    for (uint64_t j0 = 0; j0 < nunits; j0 += (uint64_t)kDeqBatch * kLanes) {
-      u32x4 c[kDeqBatch];
-      float s[kDeqBatch];
+    for (uint32_t j0 = 0; j0 < nunits; j0 += DB * kLanes) {
+      u32x4 c[DB];
+      float s[DB];
 #pragma unroll
-      for (int b = 0; b < kDeqBatch; ++b) {
-        const uint64_t j = j0 + (uint64_t)b * kLanes + lane;
+      for (int b = 0; b < DB; ++b) {
+        const uint32_t j = j0 + b * kLanes + lane;
         if (j < nunits) {
           c[b] = ld16<true>(vc + j);
-          s[b] = sc[j / g16];
+          s[b] = sc[in_col ? (j >> gsh) : (j0 / kLanes + b) / gu];
         }
       }
 #pragma unroll
-      for (int b = 0; b < kDeqBatch; ++b) {
-        const uint64_t j = j0 + (uint64_t)b * kLanes + lane;
+      for (int b = 0; b < DB; ++b) {
+        const uint32_t j = j0 + b * kLanes + lane;
         if (j >= nunits) continue;
         u32x4 y0, y1;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const uint32_t w = c[b][q];
-          const uint32_t lo = bf16_pack(e4m3_value(w & 0xffu) * s[b], e4m3_value((w >> 8) & 0xffu) * s[b]);
-          const uint32_t hi = bf16_pack(e4m3_value((w >> 16) & 0xffu) * s[b], e4m3_value(w >> 24) * s[b]);
+          // exact fp32 values of codes 0,1 and 2,3 of the word (v_cvt_pk_f32_fp8)
+          const auto v01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[b][q], false);
+          const auto v23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[b][q], true);
           u32x4& y = q < 2 ? y0 : y1;
-          y[2 * (q & 1)] = lo;
-          y[2 * (q & 1) + 1] = hi;
+          y[2 * (q & 1)] = bf16_pack(v01[0] * s[b], v01[1] * s[b]);
+          y[2 * (q & 1) + 1] = bf16_pack(v23[0] * s[b], v23[1] * s[b]);
         }
         st16<true>(dst + 2 * j, y0);
         st16<true>(dst + 2 * j + 1, y1);
@@ -265,19 +344,23 @@ int launch_moe_pack_fp8(const Fp8Args& a, int max_grid, void* stream) {
   const uint64_t wg_needed = (rows + (kBlock / kLanes) - 1) / (kBlock / kLanes);
   const int grid = (int)(wg_needed < (uint64_t)max_grid ? wg_needed : (uint64_t)max_grid);
   if (grid == 0) return 0;
+  if (a.group <= 1024) {
+    hipLaunchKernelGGL((moe_pack_fp8_cols_kernel<kPackCols>), dim3(grid), dim3(kBlock), 0, s, a);
+    return (int)hipGetLastError();
+  }
   const uint64_t per_lane = (a.hidden / 16 + kLanes - 1) / kLanes;
-  if (per_lane <= 1) hipLaunchKernelGGL((moe_pack_fp8_kernel<1>), dim3(grid), dim3(kBlock), 0, s, a);
-  else if (per_lane <= 2) hipLaunchKernelGGL((moe_pack_fp8_kernel<2>), dim3(grid), dim3(kBlock), 0, s, a);
-  else if (per_lane <= 4) hipLaunchKernelGGL((moe_pack_fp8_kernel<4>), dim3(grid), dim3(kBlock), 0, s, a);
-  else if (per_lane <= 8) hipLaunchKernelGGL((moe_pack_fp8_kernel<8>), dim3(grid), dim3(kBlock), 0, s, a);
-  else if (per_lane <= 16) hipLaunchKernelGGL((moe_pack_fp8_kernel<16>), dim3(grid), dim3(kBlock), 0, s, a);
+  if (per_lane <= 1) hipLaunchKernelGGL((moe_pack_fp8_rows_kernel<1>), dim3(grid), dim3(kBlock), 0, s, a);
+  else if (per_lane <= 2) hipLaunchKernelGGL((moe_pack_fp8_rows_kernel<2>), dim3(grid), dim3(kBlock), 0, s, a);
+  else if (per_lane <= 4) hipLaunchKernelGGL((moe_pack_fp8_rows_kernel<4>), dim3(grid), dim3(kBlock), 0, s, a);
+  else if (per_lane <= 8) hipLaunchKernelGGL((moe_pack_fp8_rows_kernel<8>), dim3(grid), dim3(kBlock), 0, s, a);
+  else if (per_lane <= 16) hipLaunchKernelGGL((moe_pack_fp8_rows_kernel<16>), dim3(grid), dim3(kBlock), 0, s, a);
   else return (int)hipErrorInvalidValue;
   return (int)hipGetLastError();
 }
 
 int launch_moe_dequant_fp8(const Fp8Args& a, int max_grid, void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  hipLaunchKernelGGL(moe_dequant_fp8_kernel, dim3(max_grid), dim3(kBlock), 0, s, a);
+  hipLaunchKernelGGL((moe_dequant_fp8_kernel<kDeqUnits>), dim3(max_grid), dim3(kBlock), 0, s, a);
   return (int)hipGetLastError();
 }
 

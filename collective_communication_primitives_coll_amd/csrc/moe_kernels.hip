@@ -25,6 +25,7 @@ namespace coll {
 
 constexpr int kIdxThreads = 1024;
 constexpr int kIdxWaves = kIdxThreads / 64;
+constexpr int kIdxBatch = 8;  // groups of 64 assignments whose destinations a wave loads together
 
 __global__ __launch_bounds__(kIdxThreads) void moe_index_kernel(MoeIndexArgs a) {
   __shared__ int wofs[kIdxWaves][kMaxRanks];  // per-wave counts, then offsets
@@ -45,24 +46,29 @@ __global__ __launch_bounds__(kIdxThreads) void moe_index_kernel(MoeIndexArgs a) 
   uint64_t lo = (uint64_t)w * per, hi = lo + per;
   if (lo > A) lo = A;
   if (hi > A) hi = A;
-  // pass 1: per-wave destination counts
-  for (uint64_t b = lo; b < hi; b += 64) {
-    const uint64_t x = b + lane;
-    int d = -1;
-    if (x < hi) {
-      d = dest[x];
-      if (d < 0 || d >= p) {
+  // pass 1: per-wave destination counts (kIdxBatch groups of 64 loaded together)
+  for (uint64_t b0 = lo; b0 < hi; b0 += 64 * kIdxBatch) {
+    int dv[kIdxBatch];
+#pragma unroll
+    for (int i = 0; i < kIdxBatch; ++i) {
+      const uint64_t x = b0 + (uint64_t)i * 64 + lane;
+      dv[i] = x < hi ? dest[x] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < kIdxBatch; ++i) {
+      int d = dv[i];
+      if (b0 + (uint64_t)i * 64 + lane < hi && (d < 0 || d >= p)) {
         bad = 1;
         d = -1;
       }
-    }
-    uint64_t rem = __ballot(d >= 0);
-    while (rem) {
-      const int leader = __ffsll((unsigned long long)rem) - 1;
-      const int dl = __shfl(d, leader);
-      const uint64_t m = __ballot(d == dl) & rem;
-      if (lane == leader) wofs[w][dl] += __popcll(m);
-      rem &= ~m;
+      uint64_t rem = __ballot(d >= 0);
+      while (rem) {
+        const int leader = __ffsll((unsigned long long)rem) - 1;
+        const int dl = __shfl(d, leader);
+        const uint64_t m = __ballot(d == dl) & rem;
+        if (lane == leader) wofs[w][dl] += __popcll(m);
+        rem &= ~m;
+      }
     }
   }
   __syncthreads();
@@ -97,17 +103,28 @@ __global__ __launch_bounds__(kIdxThreads) void moe_index_kernel(MoeIndexArgs a) 
     return;
   }
   // pass 2: packed row of every assignment
-  for (uint64_t b = lo; b < hi; b += 64) {
-    const uint64_t x = b + lane;
-    const int d = x < hi ? dest[x] : -1;
-    uint64_t rem = __ballot(d >= 0);
-    while (rem) {
-      const int leader = __ffsll((unsigned long long)rem) - 1;
-      const int dl = __shfl(d, leader);
-      const uint64_t m = __ballot(d == dl) & rem;
-      if (d == dl) pos[x] = wofs[w][dl] + __popcll(m & below);
-      if (lane == leader) wofs[w][dl] += __popcll(m);
-      rem &= ~m;
+  for (uint64_t b0 = lo; b0 < hi; b0 += 64 * kIdxBatch) {
+    int dv[kIdxBatch];
+#pragma unroll
+    for (int i = 0; i < kIdxBatch; ++i) {
+      const uint64_t x = b0 + (uint64_t)i * 64 + lane;
+      dv[i] = x < hi ? dest[x] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < kIdxBatch; ++i) {
+      const uint64_t x = b0 + (uint64_t)i * 64 + lane;
+      const int d = dv[i];
+      int mine = 0;
+      uint64_t rem = __ballot(d >= 0);
+      while (rem) {
+        const int leader = __ffsll((unsigned long long)rem) - 1;
+        const int dl = __shfl(d, leader);
+        const uint64_t m = __ballot(d == dl) & rem;
+        if (d == dl) mine = wofs[w][dl] + __popcll(m & below);
+        if (lane == leader) wofs[w][dl] += __popcll(m);
+        rem &= ~m;
+      }
+      if (d >= 0) pos[x] = mine;
     }
   }
 }

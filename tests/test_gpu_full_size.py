@@ -224,3 +224,64 @@ def test_moe_round_trip_full_size(env):
     for i in range(p):
         expect = ref.moe_combine(packs[i][2], packs[i][1], weights[i], k, H, BF16, residual[i])
         assert_bits_equal(to_host(out[i], BF16), expect, f"combine rank {i}")
+
+
+def test_moe_fp8_round_trip_full_size(env):
+    """The FP8 dispatch at p=8, 4096 tokens x 7168 bf16 per rank, top-2,
+    one scale per 128 elements: routing, counts and pos whole; packed rows,
+    dequantized rows, returned rows and combined tokens on a seeded sample
+    of assignments (the oracle encodes row by row)."""
+    from oracle import fp8
+    torch, coll = env
+    p, T, H, k, G = 8, 4096, 7168, 2, 128
+    A = T * k
+    R = fp8.row_bytes(H, G)
+    toks = inputs.rank_buffers(inputs.WL_MOE_A2A, p, T * H, inputs.BF16, dist="normal")
+    routes = inputs.moe_routes(p, T, k)
+    weights = inputs.moe_weights(p, T, k)
+    packed = [torch.empty(A * R, dtype=torch.uint8, device="cuda") for _ in range(p)]
+    pos = [torch.empty(A, dtype=torch.int32, device="cuda") for _ in range(p)]
+    counts = torch.empty(p * p, dtype=torch.int64, device="cuda")
+    counts_h = torch.empty(p * p, dtype=torch.int64, device="cuda")
+    coll.coll_moe_pack_fp8([dev(torch, x) for x in toks], [dev(torch, r) for r in routes], packed, pos, counts,
+                           k, H, G, counts_hidden_dev=counts_h)
+    torch.cuda.synchronize()
+    C = counts.cpu().numpy().reshape(p, p)
+    rng = np.random.default_rng(17)
+    poss = []
+    for i in range(p):
+        rows_per_dest, epos, _ = ref.moe_pack(np.arange(T), routes[i], k, 1, p)
+        assert list(C[i]) == list(rows_per_dest * R), f"byte counts rank {i}"
+        got_pos = pos[i].cpu().numpy()
+        assert np.array_equal(got_pos, epos), f"pos rank {i}"
+        poss.append(got_pos)
+        for a in rng.choice(A, 48, replace=False).tolist() + [0, A - 1]:
+            row = packed[i][int(got_pos[a]) * R:(int(got_pos[a]) + 1) * R].cpu().numpy()
+            x = ref.bf16_to_f32(toks[i][(a // k) * H:(a // k + 1) * H])
+            assert_bits_equal(row, fp8.encode_row(x, G), f"fp8 row rank {i} assignment {a}")
+    assert np.array_equal(counts_h.cpu().numpy().reshape(p, p), C // R * H)
+    rows = C.sum(axis=0) // R
+    recv = [torch.empty(int(r) * R, dtype=torch.uint8, device="cuda") for r in rows]
+    ex_in = [torch.empty(int(r) * H, dtype=torch.bfloat16, device="cuda") for r in rows]
+    back = [torch.empty(A * H, dtype=torch.bfloat16, device="cuda") for _ in range(p)]
+    status = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    coll.coll_alltoallv(packed, recv, counts)
+    coll.coll_moe_dequant_fp8(recv, ex_in, counts, [int(r) for r in rows], H, G, status_dev=status)
+    coll.coll_alltoallv_transposed(ex_in, back, counts_h)
+    residual = inputs.rank_buffers(inputs.WL_MOE_A2A, p, T * H, inputs.BF16, dist="normal", extra=(9,))
+    out = [dev(torch, r) for r in residual]
+    coll.coll_moe_combine(back, pos, [dev(torch, w) for w in weights], out, k, H, residual=out)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    for i in range(p):
+        bk = to_host(back[i], BF16).reshape(A, H)
+        ot = to_host(out[i], BF16).reshape(T, H)
+        for t in rng.choice(T, 24, replace=False).tolist() + [0, T - 1]:
+            x = ref.bf16_to_f32(toks[i][t * H:(t + 1) * H])
+            deq = fp8.dequantize_rows(fp8.encode_row(x, G), H, G)
+            for s in range(k):
+                assert_bits_equal(bk[poss[i][t * k + s]], deq, f"returned row rank {i} token {t} slot {s}")
+            back_t = np.concatenate([deq] * k)
+            expect = ref.moe_combine(back_t, np.arange(k), weights[i][t * k:(t + 1) * k], k, H, BF16,
+                                     residual[i][t * H:(t + 1) * H])
+            assert_bits_equal(ot[t], expect, f"combined token rank {i} token {t}")

@@ -764,6 +764,50 @@ def test_moe_pack_fp8(coll, p, T, k, H, G):
         assert_bits_equal(packed[i].cpu().numpy(), epk, f"fp8 rows rank {i} (H={H}, G={G})")
 
 
+def _e4m3_grid_row():
+    """A 1024-element row with amax exactly 448 (so its group factor is 1):
+    every finite e4m3 magnitude, every midpoint between neighbours, one bf16
+    step either side of each midpoint, each with both signs, and -0."""
+    vals = [m * 2.0 ** -9 for m in range(8)]
+    vals += [(1 + m / 8) * 2.0 ** (e - 7) for e in range(1, 16) for m in range(8) if (e, m) != (15, 7)]
+    vals = np.array(sorted(vals))                       # 0 .. 448
+    mids = (vals[:-1] + vals[1:]) / 2
+    step = np.exp2(np.floor(np.log2(mids)) - 7)         # one bf16 ulp at the midpoint
+    pos = np.concatenate([vals, mids, mids - step, mids + step])
+    row = np.concatenate([pos, -pos, [-0.0]])
+    row = np.concatenate([row, np.resize(pos[::-1], 1024 - len(row))]).astype(np.float32)
+    bits = ref.f32_to_bf16_rne(row)
+    assert np.array_equal(ref.bf16_to_f32(bits), row), "grid values must be bf16-exact"
+    return bits
+
+
+def test_moe_fp8_every_code_and_midpoint(coll):
+    """Through the pack kernel: every e4m3 code, every rounding tie and its
+    neighbours (factor 1 and factor 2^20), then every code through the
+    dequant kernel; bit-exact against the oracle."""
+    import torch
+    from oracle import fp8
+    H = G = 1024
+    R = fp8.row_bytes(H, G)
+    row = _e4m3_grid_row()
+    tiny = ref.f32_to_bf16_rne((ref.bf16_to_f32(row) * np.float32(2.0 ** -20)).astype(np.float32))
+    toks = np.concatenate([row, row[::-1].copy(), tiny])
+    T, k, p = 3, 2, 1
+    routes = np.zeros(T * k, dtype=np.int32)
+    packed = _u8(T * k * R)
+    pos = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    counts = torch.empty(1, dtype=torch.int64, device="cuda")
+    coll.coll_moe_pack_fp8([to_dev(toks, BF16)], [_i32dev(routes)], [packed], [pos], counts, k, H, G)
+    out = empty(T * k * H, BF16)
+    coll.coll_moe_dequant_fp8([packed], [out], counts, [T * k], H, G)
+    sync()
+    ec, epos, epk = fp8.moe_pack_fp8(toks, routes, k, H, G, p)
+    got = packed.cpu().numpy()
+    assert len(set(got[:H].tolist())) == 254, "every non-NaN code appears in the grid row"
+    assert_bits_equal(got, epk, "fp8 codes of the grid rows")
+    assert_bits_equal(to_host(out, BF16), fp8.dequantize_rows(epk, H, G), "dequantized grid rows")
+
+
 def test_moe_pack_fp8_rejects_bad_destination(coll):
     import torch
     from oracle import fp8
