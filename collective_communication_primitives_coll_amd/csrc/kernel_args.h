@@ -109,7 +109,7 @@ struct MoeRowArgs {
 // Quantized dispatch: FP8 e4m3 rows with one fp32 scale per group of
 // `group` elements.  Row layout: hidden code bytes, hidden/group scales,
 // zero bytes up to row_bytes (a multiple of 16).
-constexpr uint64_t kFp8MaxHidden = 16384;  // 16 units of 16 elements per lane
+constexpr uint64_t kFp8MaxHidden = 16384;  // row-wide groups: 16 units of 16 elements per lane
 struct Fp8Args {
   const void* src[kMaxRanks];      // pack: bf16 tokens; dequant: received rows
   void* dst[kMaxRanks];            // pack: packed rows; dequant: bf16 rows

@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kIdxThreads) void moe_index_kernel(MoeIndexArgs a) 
       uint64_t rem = __ballot(d >= 0);
       while (rem) {
         const int leader = __ffsll((unsigned long long)rem) - 1;
-        const int dl = __shfl(d, leader);
+        const int dl = __builtin_amdgcn_readlane(d, leader);
         const uint64_t m = __ballot(d == dl) & rem;
         if (lane == leader) wofs[w][dl] += __popcll(m);
         rem &= ~m;
@@ -118,7 +118,7 @@ __global__ __launch_bounds__(kIdxThreads) void moe_index_kernel(MoeIndexArgs a) 
       uint64_t rem = __ballot(d >= 0);
       while (rem) {
         const int leader = __ffsll((unsigned long long)rem) - 1;
-        const int dl = __shfl(d, leader);
+        const int dl = __builtin_amdgcn_readlane(d, leader);
         const uint64_t m = __ballot(d == dl) & rem;
         if (d == dl) mine = wofs[w][dl] + __popcll(m & below);
         if (lane == leader) wofs[w][dl] += __popcll(m);

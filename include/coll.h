@@ -253,8 +253,9 @@ coll_status_t coll_moe_combine(const void* const* back, const int32_t* const* po
  * Packed row (coll_moe_fp8_row_bytes(hidden, group) bytes, a multiple of
  * 16): the hidden codes, then the hidden/group fp32 scales, then zero
  * bytes.  Shapes: group divides hidden; group is a power of two in
- * [16, 1024] or a multiple of 1024; hidden <= 16384 (else
- * COLL_ERR_UNSUPPORTED).  Non-finite inputs give unspecified codes. */
+ * [16, 1024] or a multiple of 1024; hidden < 2^31, and hidden <= 16384
+ * when group > 1024 (else COLL_ERR_UNSUPPORTED).  Non-finite inputs give
+ * unspecified codes. */
 
 /* Bytes of one packed FP8 row, or 0 if (hidden, group) is not accepted. */
 size_t coll_moe_fp8_row_bytes(size_t hidden, size_t group);

@@ -65,6 +65,9 @@ def test_zero_elements_is_ok_without_pointers():
     assert L.coll_allreduce_batch(None, 0, 4, 0, None) == coll.COLL_OK
     assert L.coll_gather(None, None, 4, 0, 0, 1, None) == coll.COLL_OK
     assert L.coll_scatter(None, None, 4, 0, 0, 1, None) == coll.COLL_OK
+    assert L.coll_allreduce_premul(None, None, 4, 0, 0, None, 0, None) == coll.COLL_OK
+    assert L.coll_reduce_scatter_premul(None, None, 4, 0, 1, None, None) == coll.COLL_OK
+    assert L.coll_alltoall(None, None, 4, 0, 3, None) == coll.COLL_OK       # bytes
 
 
 @host_only
@@ -134,7 +137,9 @@ def test_fp8_row_bytes():
     assert rb(16384, 16384) == 16384 + 16
     assert rb(96, 16) == 96 + 32
     assert rb(2048, 2048) == 2048 + 16 and rb(6144, 3072) == 6144 + 16
-    for hidden, group in [(100, 16), (7168, 48), (7168, 0), (0, 16), (32768, 1024), (96, 8), (3072, 1536)]:
+    assert rb(32768, 1024) == 32768 + 128       # column-local groups: any hidden size
+    for hidden, group in [(100, 16), (7168, 48), (7168, 0), (0, 16), (32768, 2048), (96, 8), (3072, 1536),
+                          (1 << 31, 1024)]:
         assert rb(hidden, group) == 0, (hidden, group)
 
 
@@ -151,7 +156,7 @@ def test_fp8_invalid_arguments_rejected():
     T, k, H = 10, 2, 256
     assert L.coll_moe_pack_fp8(tok, dst, pk, ps, cnt, None, None, 4, T, k, 192, 48, None) == UNS  # group shape
     assert L.coll_moe_pack_fp8(tok, dst, pk, ps, cnt, None, None, 4, T, k, 100, 16, None) == INV  # group does not divide
-    assert L.coll_moe_pack_fp8(tok, dst, pk, ps, cnt, None, None, 4, T, k, 32768, 1024, None) == UNS  # hidden too large
+    assert L.coll_moe_pack_fp8(tok, dst, pk, ps, cnt, None, None, 4, T, k, 32768, 2048, None) == UNS  # row too wide
     assert L.coll_moe_pack_fp8(tok, dst, pk, ps, cnt, None, None, 4, T, 0, H, 128, None) == INV   # k = 0
     assert L.coll_moe_pack_fp8(tok, dst, pk, ps, None, None, None, 4, T, k, H, 128, None) == INV  # no counts
     bad, _k5 = _arr([base + 8, base + 0x1000000, base + 0x2000000, base + 0x3000000])
