@@ -254,8 +254,8 @@ COLL_STREAM_KERNEL void moe_pack_fp8_rows_kernel(Fp8Args a) {
 
 // out[rank] rows = dequantized received rows, in the order they arrived.
 // Each lane takes units of 16 codes (one 16-byte load, two 16-byte bf16
-// stores), DB units per lane loaded together.
-constexpr int kDeqUnits = 8;
+// stores), DB units per lane per step.
+constexpr int kDeqUnits = 4;
 
 template <int DB>
 COLL_STREAM_KERNEL void moe_dequant_fp8_kernel(Fp8Args a) {
@@ -298,43 +298,82 @@ COLL_STREAM_KERNEL void moe_dequant_fp8_kernel(Fp8Args a) {
   const uint32_t gsh = in_col ? 31u - (uint32_t)__builtin_clz(g16) : 0u;
   const uint32_t gu = in_col ? 1u : g16 / kLanes;
   const uint64_t total = (uint64_t)start[p];
-  for (uint64_t g = fp8_wave_id(); g < total; g += fp8_wave_count()) {
+  // A wave walks its (row, batch) steps with the next step's loads issued
+  // before the current step's stores: loads and stores share one counter
+  // on gfx9, so loads issued after a store would wait for it.
+  auto row_of = [&](uint64_t g, const u32x4*& vc, const float*& sc, u32x4*& dst) {
     int rk = 0;
     while ((uint64_t)start[rk + 1] <= g) ++rk;
     const uint64_t row = g - (uint64_t)start[rk];
     const uint8_t* src = (const uint8_t*)a.src[rk] + row * R;
-    const u32x4* vc = reinterpret_cast<const u32x4*>(src);
-    const float* sc = reinterpret_cast<const float*>(src + H);
-    u32x4* dst = reinterpret_cast<u32x4*>((uint16_t*)a.dst[rk] + row * H);
-    for (uint32_t j0 = 0; j0 < nunits; j0 += DB * kLanes) {
-      u32x4 c[DB];
-      float s[DB];
+    vc = reinterpret_cast<const u32x4*>(src);
+    sc = reinterpret_cast<const float*>(src + H);
+    dst = reinterpret_cast<u32x4*>((uint16_t*)a.dst[rk] + row * H);
+  };
+  auto load = [&](const u32x4* vc, const float* sc, uint32_t j0, u32x4 (&c)[DB], float (&s)[DB]) {
 #pragma unroll
-      for (int b = 0; b < DB; ++b) {
-        const uint32_t j = j0 + b * kLanes + lane;
-        if (j < nunits) {
-          c[b] = ld16<true>(vc + j);
-          s[b] = sc[in_col ? (j >> gsh) : (j0 / kLanes + b) / gu];
-        }
-      }
-#pragma unroll
-      for (int b = 0; b < DB; ++b) {
-        const uint32_t j = j0 + b * kLanes + lane;
-        if (j >= nunits) continue;
-        u32x4 y0, y1;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          // exact fp32 values of codes 0,1 and 2,3 of the word (v_cvt_pk_f32_fp8)
-          const auto v01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[b][q], false);
-          const auto v23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[b][q], true);
-          u32x4& y = q < 2 ? y0 : y1;
-          y[2 * (q & 1)] = bf16_pack(v01[0] * s[b], v01[1] * s[b]);
-          y[2 * (q & 1) + 1] = bf16_pack(v23[0] * s[b], v23[1] * s[b]);
-        }
-        st16<true>(dst + 2 * j, y0);
-        st16<true>(dst + 2 * j + 1, y1);
+    for (int b = 0; b < DB; ++b) {
+      const uint32_t j = j0 + b * kLanes + lane;
+      if (j < nunits) {
+        c[b] = ld16<true>(vc + j);
+        s[b] = sc[in_col ? (j >> gsh) : (j0 / kLanes + b) / gu];
       }
     }
+  };
+  const uint64_t waves = fp8_wave_count();
+  uint64_t g = fp8_wave_id();
+  if (g >= total) return;
+  uint32_t j0 = 0;
+  const u32x4* vc;
+  const float* sc;
+  u32x4* dst;
+  row_of(g, vc, sc, dst);
+  u32x4 c[DB];
+  float s[DB];
+  load(vc, sc, j0, c, s);
+  while (true) {
+    uint64_t gn = g;
+    uint32_t jn = j0 + DB * kLanes;
+    if (jn >= nunits) {
+      jn = 0;
+      gn = g + waves;
+    }
+    const bool more = gn < total;
+    const u32x4* vcn = vc;
+    const float* scn = sc;
+    u32x4* dstn = dst;
+    if (more && gn != g) row_of(gn, vcn, scn, dstn);
+    u32x4 cn[DB];
+    float sn[DB];
+    if (more) load(vcn, scn, jn, cn, sn);
+#pragma unroll
+    for (int b = 0; b < DB; ++b) {
+      const uint32_t j = j0 + b * kLanes + lane;
+      if (j >= nunits) continue;
+      u32x4 y0, y1;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        // exact fp32 values of codes 0,1 and 2,3 of the word (v_cvt_pk_f32_fp8)
+        const auto v01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[b][q], false);
+        const auto v23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[b][q], true);
+        u32x4& y = q < 2 ? y0 : y1;
+        y[2 * (q & 1)] = bf16_pack(v01[0] * s[b], v01[1] * s[b]);
+        y[2 * (q & 1) + 1] = bf16_pack(v23[0] * s[b], v23[1] * s[b]);
+      }
+      st16<true>(dst + 2 * j, y0);
+      st16<true>(dst + 2 * j + 1, y1);
+    }
+    if (!more) break;
+#pragma unroll
+    for (int b = 0; b < DB; ++b) {
+      c[b] = cn[b];
+      s[b] = sn[b];
+    }
+    g = gn;
+    j0 = jn;
+    vc = vcn;
+    sc = scn;
+    dst = dstn;
   }
 }
 
