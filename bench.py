@@ -58,7 +58,7 @@ def parse_args(argv=None):
     ap.add_argument("--no-collectives", action="store_true", help="time only the main step")
     ap.add_argument("--only", default=None,
                     help="comma list of extra collectives to time (ar_ring, ar_onepass, ar_hd, "
-                         "ar_literal, ar_avg, ar_premul, a2a, a2av, moe, moe_fp8, gs, ar_small, batch, copy)")
+                         "ar_literal, ar_avg, ar_premul, a2a, a2av, moe, moe_fp8, gs, ar_small, batch, copy, ce)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
     return ap.parse_args(argv)
 
@@ -377,6 +377,49 @@ def extra_collectives(torch, coll, inputs, metrics, dev, which, iters=10, warmup
                      "coll_copy_kernel_GBps": round(2 * nbytes / (med_c * 1e-6) / 1e9, 1),
                      "note": "1 GiB device-to-device: torch copy_ and coll_broadcast with p=1"})
         del a, b
+        torch.cuda.empty_cache()
+
+    # --- copy-engine baseline: AllGather and All-to-All as p^2 D2D copies -------
+    # The collective built from device-to-device hipMemcpyAsync calls (torch
+    # copy_ on slices), one per (source, destination) block, against the
+    # library's single launch on the same buffers.
+    if want("ce"):
+        p = 8
+        n = 1 << 23
+        shard = [torch.empty(n, dtype=torch.bfloat16, device=dev).normal_() for _ in range(p)]
+        full = [torch.empty(p * n, dtype=torch.bfloat16, device=dev) for _ in range(p)]
+
+        def ag_memcpy():
+            for r in range(p):
+                for s_ in range(p):
+                    full[r][s_ * n:(s_ + 1) * n].copy_(shard[s_])
+        f = coll.coll_allgather(shard, full, defer=True)
+        t_ce, t_k = [stats_us(x)[0] for x in time_launches(torch, [ag_memcpy, f], iters, warmup)]
+        b_ag = 2 * p * p * n * 2
+        rows.append({"name": "allgather_vs_copy_engine", "p": p, "elem_bytes": 2, "hbm_bytes": b_ag,
+                     "memcpy_64_calls_us": round(t_ce, 2), "coll_allgather_us": round(t_k, 2),
+                     "memcpy_GBps": round(b_ag / (t_ce * 1e-6) / 1e9, 1),
+                     "coll_GBps": round(b_ag / (t_k * 1e-6) / 1e9, 1), "speedup": round(t_ce / t_k, 2),
+                     "workload": "AllGather p=8, 16 MiB bf16 shards: 64 device-to-device copies vs one launch"})
+        del shard, full
+        per = 4096 * 7168
+        blk = per // p
+        send = [torch.empty(per, dtype=torch.bfloat16, device=dev).normal_() for _ in range(p)]
+        recv = [torch.empty(per, dtype=torch.bfloat16, device=dev) for _ in range(p)]
+
+        def a2a_memcpy():
+            for i in range(p):
+                for j in range(p):
+                    recv[j][i * blk:(i + 1) * blk].copy_(send[i][j * blk:(j + 1) * blk])
+        f = coll.coll_alltoall(send, recv, blk, defer=True)
+        t_ce, t_k = [stats_us(x)[0] for x in time_launches(torch, [a2a_memcpy, f], iters, warmup)]
+        b_a2a = 2 * p * per * 2
+        rows.append({"name": "alltoall_vs_copy_engine", "p": p, "elem_bytes": 2, "hbm_bytes": b_a2a,
+                     "memcpy_64_calls_us": round(t_ce, 2), "coll_alltoall_us": round(t_k, 2),
+                     "memcpy_GBps": round(b_a2a / (t_ce * 1e-6) / 1e9, 1),
+                     "coll_GBps": round(b_a2a / (t_k * 1e-6) / 1e9, 1), "speedup": round(t_ce / t_k, 2),
+                     "workload": "All-to-All p=8, 4096x7168 bf16 per rank: 64 device-to-device copies vs one launch"})
+        del send, recv
         torch.cuda.empty_cache()
     return rows
 

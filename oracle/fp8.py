@@ -147,3 +147,18 @@ def moe_pack_fp8(tokens_bf16: np.ndarray, dest: np.ndarray, k: int, hidden: int,
     for a in range(A):
         packed[pos[a] * R:(pos[a] + 1) * R] = enc[a // k]
     return rows_per_dest * R, pos, packed
+
+
+def moe_dispatch_direct_fp8(tokens_bf16: list[np.ndarray], dests: list[np.ndarray], k: int, hidden: int,
+                            group: int):
+    """The direct dispatch (ref.moe_dispatch_direct) of encoded rows: recv[j]
+    holds row_bytes-byte rows; counts are in bytes."""
+    R = row_bytes(hidden, group)
+    enc = []
+    for tok in tokens_bf16:
+        x = ref.bf16_to_f32(np.asarray(tok, dtype=np.uint16)).reshape(-1, hidden)
+        enc.append(np.concatenate([encode_row(x[t], group) for t in range(len(x))]) if len(x) else
+                   np.zeros(0, dtype=np.uint8))
+    counts, slots, recv = ref.moe_dispatch_direct(enc, dests, k, R)
+    return counts, slots, recv
+

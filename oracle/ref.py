@@ -49,7 +49,9 @@ Readings taken where the pages are silent or inconsistent:
 8. MoE pack/combine: the page lists the steps, not the formats.  Packing
    orders assignments by destination rank, stable in assignment index;
    the combine accumulates in fp32 in slot order with products and sums
-   rounded separately (see moe_pack, moe_combine).
+   rounded separately (see moe_pack, moe_combine).  The direct dispatch
+   and combine (moe_dispatch_direct, moe_combine_direct) give the same
+   receive layout and outputs without the staging copies.
 """
 from __future__ import annotations
 
@@ -346,6 +348,48 @@ def moe_combine(back: np.ndarray, pos: np.ndarray, weights: np.ndarray, k: int, 
         acc = (acc + prod).astype(np.float32)
     acc = acc.reshape(-1)
     return f32_to_bf16_rne(acc) if dtype == BF16 else acc
+
+
+def moe_dispatch_direct(tokens: list[np.ndarray], dests: list[np.ndarray], k: int, hidden: int):
+    """Dispatch without a staging copy: every assignment's token row lands
+    directly in its destination's receive buffer.
+
+    recv[j] holds, for source ranks i = 0, 1, ..., p-1 in turn, the rows of
+    rank i's assignments to j in assignment order: the same receive layout
+    as pack followed by the ragged exchange (the "Collective Communication"
+    page's flow, with the pack and the exchange writing one buffer; the
+    load/store peer access of the hpc/04 page, section 3.9).  slot[i][a] is
+    the row of assignment a inside recv[dest[i][a]].  counts[i][j] =
+    hidden * (assignments of rank i to rank j), as moe_pack."""
+    p = len(tokens)
+    recv_rows = [[] for _ in range(p)]
+    slots = []
+    counts = np.zeros((p, p), dtype=np.int64)
+    for i in range(p):
+        d = np.asarray(dests[i], dtype=np.int64)
+        slot = np.zeros(len(d), dtype=np.int64)
+        for j in range(p):
+            for a in range(len(d)):
+                if d[a] == j:
+                    slot[a] = len(recv_rows[j])
+                    t = a // k
+                    recv_rows[j].append(np.asarray(tokens[i])[t * hidden:(t + 1) * hidden])
+                    counts[i, j] += hidden
+        slots.append(slot)
+    dt = np.asarray(tokens[0]).dtype
+    recv = [np.concatenate(r) if r else np.zeros(0, dtype=dt) for r in recv_rows]
+    return counts, slots, recv
+
+
+def moe_combine_direct(ys: list[np.ndarray], dest: np.ndarray, slot: np.ndarray, weights: np.ndarray, k: int,
+                       hidden: int, dtype: int, residual: np.ndarray | None = None) -> np.ndarray:
+    """One rank's weighted combine reading every expert output where it
+    lies: y_s = row slot[t*k+s] of ys[dest[t*k+s]].  Same arithmetic as
+    moe_combine (fp32, slot order, products and sums rounded separately)."""
+    A = len(dest)
+    rows = [np.asarray(ys[int(dest[a])])[int(slot[a]) * hidden:(int(slot[a]) + 1) * hidden] for a in range(A)]
+    back = np.concatenate(rows) if rows else np.zeros(0, dtype=np.asarray(ys[0]).dtype)
+    return moe_combine(back, np.arange(A), weights, k, hidden, dtype, residual)
 
 
 # ----------------------------------------------------------------------------

@@ -789,3 +789,68 @@ def test_avg_under_every_schedule_is_sum_divided(sim):
     a_ = getattr(ref, sim)(xs, ref.AVG, ref.F32)
     for r in range(p):
         assert np.array_equal(_bits(a_[r]), _bits((s_[r] / np.float32(p)).astype(np.float32)))
+
+
+# ----------------------------------------------------------------------------
+# Direct MoE dispatch and combine: equal to pack -> exchange -> reverse ->
+# combine, bit for bit
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("p,T,k,H", [(1, 5, 1, 3), (3, 17, 2, 4), (4, 30, 3, 2), (8, 25, 2, 5)])
+def test_direct_dispatch_equals_pack_then_exchange(p, T, k, H):
+    rng = np.random.default_rng(60 + p * T)
+    toks = [rng.integers(-50, 50, T * H).astype(np.int32) for _ in range(p)]
+    dests = [rng.integers(0, p, T * k).astype(np.int64) for _ in range(p)]
+    counts, slots, recv = ref.moe_dispatch_direct(toks, dests, k, H)
+    packs = [ref.moe_pack(toks[i], dests[i], k, H, p) for i in range(p)]
+    C = np.stack([pk[0] for pk in packs])
+    assert np.array_equal(counts, C)
+    via_exchange = ref.alltoallv([pk[2] for pk in packs], C)
+    for j in range(p):
+        assert np.array_equal(recv[j], via_exchange[j])
+    rows = C // H
+    for i in range(p):
+        soff = np.concatenate([[0], np.cumsum(rows[i])[:-1]])
+        for a in range(T * k):
+            j = int(dests[i][a])
+            t = a // k
+            # the slot's row is the token, and it is where the exchange put the packed row
+            assert np.array_equal(recv[j][slots[i][a] * H:(slots[i][a] + 1) * H], toks[i][t * H:(t + 1) * H])
+            assert slots[i][a] == rows[:i, j].sum() + (packs[i][1][a] - soff[j])
+
+
+@pytest.mark.parametrize("with_residual", [False, True])
+def test_direct_combine_equals_reverse_then_combine(with_residual):
+    p, T, k, H = 4, 23, 2, 6
+    rng = np.random.default_rng(71)
+    toks = [ref.f32_to_bf16_rne(rng.standard_normal(T * H).astype(np.float32)) for _ in range(p)]
+    dests = [rng.integers(0, p, T * k).astype(np.int64) for _ in range(p)]
+    w = [rng.random(T * k).astype(np.float32) for _ in range(p)]
+    res = [ref.f32_to_bf16_rne(rng.standard_normal(T * H).astype(np.float32)) for _ in range(p)]
+    counts, slots, recv = ref.moe_dispatch_direct(toks, dests, k, H)
+    # experts: any per-row map; use a row-dependent scaling
+    ys = [ref.f32_to_bf16_rne((ref.bf16_to_f32(r).reshape(-1, H) *
+                               (1 + np.arange(len(r) // H, dtype=np.float32))[:, None] / 7).reshape(-1))
+          for r in recv]
+    packs = [ref.moe_pack(toks[i], dests[i], k, H, p) for i in range(p)]
+    C = np.stack([pk[0] for pk in packs])
+    back = ref.alltoallv(ys, C.T.copy())          # reverse exchange: the transposed matrix
+    for i in range(p):
+        a = ref.moe_combine_direct(ys, dests[i], slots[i], w[i], k, H, ref.BF16, res[i] if with_residual else None)
+        b = ref.moe_combine(back[i], packs[i][1], w[i], k, H, ref.BF16, res[i] if with_residual else None)
+        assert np.array_equal(a, b)
+
+
+def test_direct_fp8_dispatch_equals_pack_then_exchange():
+    from oracle import fp8
+    p, T, k, H, G = 3, 11, 2, 64, 32
+    rng = np.random.default_rng(72)
+    toks = [ref.f32_to_bf16_rne(rng.standard_normal(T * H).astype(np.float32)) for _ in range(p)]
+    dests = [rng.integers(0, p, T * k).astype(np.int64) for _ in range(p)]
+    counts, slots, recv = fp8.moe_dispatch_direct_fp8(toks, dests, k, H, G)
+    packs = [fp8.moe_pack_fp8(toks[i], dests[i], k, H, G, p) for i in range(p)]
+    C = np.stack([pk[0] for pk in packs])
+    assert np.array_equal(counts, C)
+    via = ref.alltoallv([pk[2] for pk in packs], C)
+    for j in range(p):
+        assert np.array_equal(recv[j], via[j])
