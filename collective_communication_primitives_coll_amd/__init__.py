@@ -78,6 +78,9 @@ def lib() -> ctypes.CDLL:
         "coll_allreduce_batch": [ctypes.POINTER(coll_call_t), i32, i32, ctypes.c_uint, vp],
         "coll_moe_pack_fp8": [pp, pp, pp, pp, vp, vp, vp, i32, sz, i32, sz, sz, vp],
         "coll_moe_dequant_fp8": [pp, pp, i32, vp, i64p, vp, sz, sz, vp],
+        "coll_moe_dispatch": [pp, pp, pp, pp, vp, vp, i32, sz, i32, sz, i64p, i32, vp],
+        "coll_moe_dispatch_fp8": [pp, pp, pp, pp, vp, vp, vp, i32, sz, i32, sz, sz, i64p, vp],
+        "coll_moe_combine_direct": [pp, pp, pp, pp, pp, i32, sz, i32, sz, i64p, i32, vp],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -466,6 +469,89 @@ def coll_moe_dequant_fp8(recv, out, counts_dev, rows_cap: Sequence[int], hidden:
     st = _addr(status_dev) if status_dev is not None else None
     return _run("coll_moe_dequant_fp8", (a1, a2, p, _addr(counts_dev), cap, st, int(hidden), int(group),
                                          _stream(stream)), "coll_moe_dequant_fp8", defer, (k1, k2, cap))
+
+
+def coll_moe_dispatch(tokens, dest, recv, loc, counts_dev, k: int, hidden: int, recv_cap: Sequence[int] | None = None,
+                      status_dev=None, tokens_per_rank: int | None = None, dtype: int | None = None, stream=None,
+                      defer: bool = False):
+    """Direct dispatch: per rank, tokens [T*hidden], dest int32 [T*k] ->
+    recv[j] (rows received by rank j, capacity recv_cap[j] rows, default the
+    tensor's size), loc int64 [T*k] ((dest << 32) | row, or -1); counts_dev
+    int64 [p, p] in elements; status_dev optional int32 [p + 1]."""
+    p = len(tokens)
+    dt = _dtype_of(tokens[0], dtype)
+    T = tokens_per_rank if tokens_per_rank is not None else _numel(tokens[0], None) // int(hidden)
+    _same_dtype([*tokens, *recv], dt)
+    if recv_cap is None:
+        recv_cap = [_numel(x, None) // int(hidden) for x in recv]
+    for r in range(p):
+        _check_sizes([recv[r]], int(recv_cap[r]) * hidden, "moe_dispatch recv")
+    _check_sizes(tokens, T * hidden, "moe_dispatch tokens")
+    _check_sizes([*dest, *loc], T * k, "moe_dispatch dest/loc")
+    a1, k1 = _ptr_array(tokens)
+    a2, k2 = _ptr_array(dest)
+    a3, k3 = _ptr_array(recv)
+    a4, k4 = _ptr_array(loc)
+    cap = (ctypes.c_int64 * p)(*[int(c) for c in recv_cap])
+    st = _addr(status_dev) if status_dev is not None else None
+    return _run("coll_moe_dispatch", (a1, a2, a3, a4, _addr(counts_dev), st, p, int(T), int(k), int(hidden), cap, dt,
+                                      _stream(stream)), "coll_moe_dispatch", defer, (k1, k2, k3, k4, cap))
+
+
+def coll_moe_dispatch_fp8(tokens, dest, recv, loc, counts_dev, k: int, hidden: int, group: int,
+                          recv_cap: Sequence[int] | None = None, counts_hidden_dev=None, status_dev=None,
+                          tokens_per_rank: int | None = None, stream=None, defer: bool = False):
+    """Direct FP8 dispatch: bf16 tokens -> encoded rows written straight into
+    recv[j] (uint8, capacity recv_cap[j] rows of row_bytes); counts in bytes."""
+    p = len(tokens)
+    T = tokens_per_rank if tokens_per_rank is not None else _numel(tokens[0], None) // int(hidden)
+    R = coll_moe_fp8_row_bytes(hidden, group)
+    if recv_cap is None:
+        recv_cap = [(_numel(x, None) // R) if R else 0 for x in recv]
+    for r in range(p):
+        if R:
+            _check_sizes([recv[r]], int(recv_cap[r]) * R, "moe_dispatch_fp8 recv")
+    _check_sizes(tokens, T * hidden, "moe_dispatch_fp8 tokens")
+    _check_sizes([*dest, *loc], T * k, "moe_dispatch_fp8 dest/loc")
+    a1, k1 = _ptr_array(tokens)
+    a2, k2 = _ptr_array(dest)
+    a3, k3 = _ptr_array(recv)
+    a4, k4 = _ptr_array(loc)
+    cap = (ctypes.c_int64 * p)(*[int(c) for c in recv_cap])
+    ch = _addr(counts_hidden_dev) if counts_hidden_dev is not None else None
+    st = _addr(status_dev) if status_dev is not None else None
+    return _run("coll_moe_dispatch_fp8", (a1, a2, a3, a4, _addr(counts_dev), ch, st, p, int(T), int(k), int(hidden),
+                                          int(group), cap, _stream(stream)), "coll_moe_dispatch_fp8", defer,
+                (k1, k2, k3, k4, cap))
+
+
+def coll_moe_combine_direct(y, loc, weights, out, k: int, hidden: int, y_rows: Sequence[int] | None = None,
+                            residual=None, tokens_per_rank: int | None = None, dtype: int | None = None,
+                            stream=None, defer: bool = False):
+    """Combine reading expert outputs in place: y[j] rows (y_rows[j], default
+    the tensor's size) addressed by loc from coll_moe_dispatch(_fp8)."""
+    p = len(out)
+    dt = _dtype_of(out[0], dtype)
+    T = tokens_per_rank if tokens_per_rank is not None else _numel(out[0], None) // int(hidden)
+    _same_dtype([*y, *out, *(residual or [])], dt)
+    if y_rows is None:
+        y_rows = [_numel(x, None) // int(hidden) for x in y]
+    for j in range(len(y)):
+        _check_sizes([y[j]], int(y_rows[j]) * hidden, "moe_combine_direct y")
+    _check_sizes(out, T * hidden, "moe_combine_direct out")
+    _check_sizes([*loc, *weights], T * k, "moe_combine_direct loc/weights")
+    a1, k1 = _ptr_array(y)
+    a2, k2 = _ptr_array(loc)
+    a3, k3 = _ptr_array(weights)
+    a5, k5 = _ptr_array(out)
+    if residual is not None:
+        a4, k4 = _ptr_array(residual)
+    else:
+        a4, k4 = None, None
+    rows = (ctypes.c_int64 * p)(*[int(c) for c in y_rows])
+    return _run("coll_moe_combine_direct", (a1, a2, a3, a4, a5, p, int(T), int(k), int(hidden), rows, dt,
+                                            _stream(stream)), "coll_moe_combine_direct", defer,
+                (k1, k2, k3, k4, k5, rows))
 
 
 def coll_moe_combine(back, pos, weights, out, k: int, hidden: int, residual=None,

@@ -820,6 +820,216 @@ COLL_EXPORT coll_status_t coll_moe_dequant_fp8(const void* const* recv, void* co
 }
 
 // ---------------------------------------------------------------------------
+// Direct MoE dispatch and combine
+// ---------------------------------------------------------------------------
+namespace {
+// Dynamic LDS of the direct dispatch kernels: two p x p int32 placement tables.
+size_t direct_lds_bytes(int p) { return (size_t)2 * p * p * sizeof(int32_t); }
+
+// Shared validation of the direct dispatches.  elem: payload bytes per
+// token element (tokens); row_bytes: bytes per delivered row (recv).
+coll_status_t check_direct(const void* const* tokens, const int32_t* const* dest, void* const* recv,
+                           int64_t* const* loc, int64_t* counts_dev, int64_t* counts2_dev, int32_t* status_dev,
+                           int p, size_t T, int k, size_t hidden, const int64_t* recv_cap, size_t elem,
+                           size_t row_bytes, size_t align, size_t* A_out) {
+  if (p < 1 || p > kMaxRanks || k < 1 || k > coll::kMaxTopK || hidden == 0 || !recv_cap)
+    return COLL_ERR_INVALID_ARG;
+  if (!counts_dev || !elem_aligned1(counts_dev, sizeof(int64_t))) return COLL_ERR_INVALID_ARG;
+  if (counts2_dev && !elem_aligned1(counts2_dev, sizeof(int64_t))) return COLL_ERR_INVALID_ARG;
+  if (status_dev && !elem_aligned1(status_dev, sizeof(int32_t))) return COLL_ERR_INVALID_ARG;
+  size_t A, tb, b;
+  if (!mul_ok(T, (size_t)k, 1, &A) || A > 0x7fffffffull) return COLL_ERR_INVALID_ARG;
+  if (!mul_ok(hidden, elem, 1, &b) || !mul_ok(T, hidden * elem, 1, &tb) || !mul_ok(A, row_bytes, kMaxRanks, &b))
+    return COLL_ERR_INVALID_ARG;
+  for (int r = 0; r < p; ++r)
+    if (recv_cap[r] < 0 || recv_cap[r] > 0x7fffffffll || !mul_ok((size_t)recv_cap[r], row_bytes, kMaxRanks, &b))
+      return COLL_ERR_INVALID_ARG;
+  std::vector<Range> rs;
+  if (A > 0) {
+    if (!all_non_null(tokens, p) || !all_non_null(dest, p) || !all_non_null(recv, p) || !all_non_null(loc, p))
+      return COLL_ERR_INVALID_ARG;
+    if (!elem_aligned(tokens, p, align) || !elem_aligned(recv, p, align) || !elem_aligned(dest, p, 4) ||
+        !elem_aligned(loc, p, 8))
+      return COLL_ERR_INVALID_ARG;
+    for (int r = 0; r < p; ++r) {
+      rs.push_back(rng(tokens[r], tb, false, r));
+      rs.push_back(rng(dest[r], A * 4, false, r));
+      rs.push_back(rng(loc[r], A * 8, true, r));
+      rs.push_back(rng(recv[r], (size_t)recv_cap[r] * row_bytes, true, r));
+    }
+  }
+  rs.push_back(rng(counts_dev, (size_t)p * p * sizeof(int64_t), true, -1));
+  if (counts2_dev) rs.push_back(rng(counts2_dev, (size_t)p * p * sizeof(int64_t), true, -1));
+  if (status_dev) rs.push_back(rng(status_dev, (size_t)(p + 1) * sizeof(int32_t), true, -1));
+  coll_status_t st = check_alias(rs, [](const Range&, const Range&) { return false; });
+  if (st != COLL_OK) return st;
+  *A_out = A;
+  return COLL_OK;
+}
+
+// Index pass writing each assignment's packed row into the low word of its
+// location (the dispatch kernels turn it into the location).
+int launch_direct_index(const int32_t* const* dest, int64_t* const* loc, int64_t* counts, int64_t* counts2,
+                        int32_t* status, int p, size_t A, size_t unit, size_t unit2, void* stream) {
+  coll::MoeIndexArgs ia;
+  std::memset(&ia, 0, sizeof(ia));
+  for (int r = 0; r < p && A > 0; ++r) {
+    ia.dest[r] = dest[r];
+    ia.pos[r] = reinterpret_cast<int32_t*>(loc[r]);
+  }
+  ia.counts = counts;
+  ia.counts2 = counts2;
+  ia.status = status;
+  ia.assignments = A;
+  ia.hidden = unit;
+  ia.hidden2 = unit2;
+  ia.p = p;
+  ia.pos_shift = 1;
+  return coll::launch_moe_index(ia, stream);
+}
+
+coll::MoeDirectArgs direct_args(const void* const* tokens, const int32_t* const* dest, void* const* recv,
+                                int64_t* const* loc, const int64_t* counts, int32_t* status, int p, size_t T,
+                                int k, size_t hidden, const int64_t* recv_cap, size_t unit) {
+  coll::MoeDirectArgs a;
+  std::memset(&a, 0, sizeof(a));
+  for (int r = 0; r < p; ++r) {
+    a.src[r] = tokens[r];
+    a.dst[r] = recv[r];
+    a.loc[r] = loc[r];
+    a.dest[r] = dest[r];
+    a.cap[r] = recv_cap[r];
+  }
+  a.counts = counts;
+  a.status = status;
+  a.tokens = T;
+  a.hidden = hidden;
+  a.count_unit = unit;
+  a.k = k;
+  a.p = p;
+  a.src_mis = common_mis(tokens, p);
+  a.dst_mis = common_mis((const void* const*)recv, p);
+  return a;
+}
+}  // namespace
+
+COLL_EXPORT coll_status_t coll_moe_dispatch(const void* const* tokens, const int32_t* const* dest,
+                                            void* const* recv, int64_t* const* loc, int64_t* counts_dev,
+                                            int32_t* status_dev, int p, size_t tokens_per_rank, int k,
+                                            size_t hidden, const int64_t* recv_cap, coll_dtype_t dtype,
+                                            void* stream) {
+  if (!dtype_ok(dtype)) return COLL_ERR_INVALID_ARG;
+  const size_t d = dsize(dtype);
+  size_t A = 0;
+  coll_status_t st = check_direct(tokens, dest, recv, loc, counts_dev, nullptr, status_dev, p, tokens_per_rank, k,
+                                  hidden, recv_cap, d, hidden * d, d, &A);
+  if (st != COLL_OK) return st;
+  int e = launch_direct_index(dest, loc, counts_dev, nullptr, status_dev, p, A, hidden, 0, stream);
+  if (e) return hip_fail(e);
+  if (A == 0) return COLL_OK;
+  int dev = 0, cus = 0;
+  e = current_device(&dev);
+  if (!e) e = device_cus(dev, &cus);
+  if (e) return hip_fail(e);
+  if (direct_lds_bytes(p) > (size_t)g_dev[dev].lds_per_block.load()) return COLL_ERR_UNSUPPORTED;
+  int grid;
+  e = max_grid(&grid, kFamRow);
+  if (e) return hip_fail(e);
+  const coll::MoeDirectArgs a =
+      direct_args(tokens, dest, recv, loc, counts_dev, status_dev, p, tokens_per_rank, k, hidden, recv_cap, hidden);
+  return finish(coll::launch_moe_dispatch((int)d, a, grid, stream));
+}
+
+COLL_EXPORT coll_status_t coll_moe_dispatch_fp8(const void* const* tokens, const int32_t* const* dest,
+                                                void* const* recv, int64_t* const* loc, int64_t* counts_dev,
+                                                int64_t* counts_hidden_dev, int32_t* status_dev, int p,
+                                                size_t tokens_per_rank, int k, size_t hidden, size_t group,
+                                                const int64_t* recv_cap, void* stream) {
+  coll_status_t st = fp8_shape(hidden, group);
+  if (st != COLL_OK) return st;
+  const size_t R = fp8_row_bytes(hidden, group);
+  size_t A = 0;
+  st = check_direct(tokens, dest, recv, loc, counts_dev, counts_hidden_dev, status_dev, p, tokens_per_rank, k,
+                    hidden, recv_cap, 2, R, 16, &A);
+  if (st != COLL_OK) return st;
+  int e = launch_direct_index(dest, loc, counts_dev, counts_hidden_dev, status_dev, p, A, R, hidden, stream);
+  if (e) return hip_fail(e);
+  if (A == 0) return COLL_OK;
+  int dev = 0, cus = 0;
+  e = current_device(&dev);
+  if (!e) e = device_cus(dev, &cus);
+  if (e) return hip_fail(e);
+  if (direct_lds_bytes(p) > (size_t)g_dev[dev].lds_per_block.load()) return COLL_ERR_UNSUPPORTED;
+  int grid;
+  e = max_grid(&grid, kFamFp8);
+  if (e) return hip_fail(e);
+  coll::MoeDirectArgs a =
+      direct_args(tokens, dest, recv, loc, counts_dev, status_dev, p, tokens_per_rank, k, hidden, recv_cap, R);
+  a.group = group;
+  a.row_bytes = R;
+  return finish(coll::launch_moe_dispatch_fp8(a, grid, stream));
+}
+
+COLL_EXPORT coll_status_t coll_moe_combine_direct(const void* const* y, const int64_t* const* loc,
+                                                  const float* const* weights, const void* const* residual,
+                                                  void* const* out, int p, size_t tokens_per_rank, int k,
+                                                  size_t hidden, const int64_t* y_rows, coll_dtype_t dtype,
+                                                  void* stream) {
+  if (p < 1 || p > kMaxRanks || !arith_dtype_ok(dtype) || k < 1 || k > coll::kMaxTopK || hidden == 0 || !y_rows)
+    return COLL_ERR_INVALID_ARG;
+  if (dtype == COLL_I32) return COLL_ERR_UNSUPPORTED;
+  const size_t d = dsize(dtype);
+  size_t A, tb, b;
+  if (!mul_ok(tokens_per_rank, (size_t)k, 1, &A) || A > 0x7fffffffull) return COLL_ERR_INVALID_ARG;
+  if (!mul_ok(hidden, d, 1, &b) || !mul_ok(tokens_per_rank, hidden * d, 1, &tb)) return COLL_ERR_INVALID_ARG;
+  for (int r = 0; r < p; ++r)
+    if (y_rows[r] < 0 || y_rows[r] > 0x7fffffffll || !mul_ok((size_t)y_rows[r], hidden * d, 1, &b))
+      return COLL_ERR_INVALID_ARG;
+  if (A == 0) return COLL_OK;
+  if (!all_non_null(y, p) || !all_non_null(loc, p) || !all_non_null(weights, p) || !all_non_null(out, p))
+    return COLL_ERR_INVALID_ARG;
+  if (residual && !all_non_null(residual, p)) return COLL_ERR_INVALID_ARG;
+  if (!elem_aligned(y, p, d) || !elem_aligned(out, p, d) || !elem_aligned(loc, p, 8) ||
+      !elem_aligned(weights, p, 4) || (residual && !elem_aligned(residual, p, d)))
+    return COLL_ERR_INVALID_ARG;
+  std::vector<Range> rs;
+  for (int r = 0; r < p; ++r) {
+    rs.push_back(rng(y[r], (size_t)y_rows[r] * hidden * d, false, r));
+    rs.push_back(rng(loc[r], A * 8, false, r));
+    rs.push_back(rng(weights[r], A * 4, false, r));
+    if (residual) rs.push_back(rng(residual[r], tb, false, kResidualTag + r));
+    rs.push_back(rng(out[r], tb, true, r));
+  }
+  coll_status_t st = check_alias(rs, [](const Range& o, const Range& x) {
+    // in place: out[r] is exactly residual[r] (the residual add)
+    return !x.out && x.rank == kResidualTag + o.rank && x.b == o.b && x.e == o.e;
+  });
+  if (st != COLL_OK) return st;
+  int grid;
+  int e = max_grid(&grid, kFamRow);
+  if (e) return hip_fail(e);
+  coll::MoeRowArgs ra;
+  std::memset(&ra, 0, sizeof(ra));
+  for (int r = 0; r < p; ++r) {
+    ra.src[r] = y[r];
+    ra.dst[r] = out[r];
+    ra.pos[r] = reinterpret_cast<const int32_t*>(loc[r]);
+    ra.weights[r] = weights[r];
+    if (residual) ra.residual[r] = residual[r];
+    ra.cap[r] = (int32_t)y_rows[r];
+  }
+  ra.tokens = tokens_per_rank;
+  ra.hidden = hidden;
+  ra.k = k;
+  ra.p = p;
+  ra.has_residual = residual ? 1 : 0;
+  ra.src_mis = common_mis(y, p);
+  ra.dst_mis = common_mis((const void* const*)out, p);
+  ra.res_mis = residual ? common_mis(residual, p) : 0;
+  return finish(coll::launch_moe_combine_direct(dtype, ra, grid, stream));
+}
+
+// ---------------------------------------------------------------------------
 // Batched AllReduce
 // ---------------------------------------------------------------------------
 namespace {

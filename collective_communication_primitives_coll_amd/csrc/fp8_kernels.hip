@@ -24,6 +24,7 @@
 // multiplied by the group scale and narrowed to bf16 (round to nearest
 // even).  Rows per rank come from the byte counts on the device.
 #include "device_common.h"
+#include "moe_direct.h"
 
 namespace coll {
 
@@ -79,27 +80,68 @@ __device__ __forceinline__ u32x4 unit_codes(const u32x4& x0, const u32x4& x1, fl
 
 }  // namespace
 
-// Shared by both pack kernels: the token rows of wave-strided (rank, t),
-// skipping tokens with no valid slot (a rejected rank has none).
-struct PackRow {
-  const int32_t* pp;  // pos of the token's k slots
-  const u32x4* src;   // the token row, two vectors per unit
-  int rank;
+// Where the encoded slot rows of a token go.  Rows<Fp8Args>: the rank's
+// packed buffer, row = pos (coll_moe_pack_fp8).  Rows<MoeDirectArgs>: the
+// destination's receive buffer at the placement-table row, with the
+// location written back once the token is done (coll_moe_dispatch_fp8).
+template <class Args> struct Rows;
+
+template <> struct Rows<Fp8Args> {
+  const Fp8Args& a;
+  __device__ uint8_t* slot_row(int rank, uint64_t x, int64_t& loc) const {
+    loc = -1;
+    const int32_t ps = a.pos[rank][x];
+    if (ps < 0 || (uint64_t)ps >= a.tokens * (uint64_t)a.k) return nullptr;
+    return (uint8_t*)a.dst[rank] + (uint64_t)ps * a.row_bytes;
+  }
+  __device__ void finish(int, uint64_t, const int64_t (&)[kMaxTopK], int) const {}
 };
 
-__device__ __forceinline__ bool pack_row(const Fp8Args& a, uint64_t r, PackRow& out) {
-  const int rank = (int)(r / a.tokens);
-  const uint64_t t = r - (uint64_t)rank * a.tokens;
-  const uint64_t A = a.tokens * (uint64_t)a.k;
-  const int32_t* pp = a.pos[rank] + t * (uint64_t)a.k;
-  bool any = false;
-  for (int s = 0; s < a.k; ++s) {
-    const int32_t ps = pp[s];
-    any |= ps >= 0 && (uint64_t)ps < A;
+template <> struct Rows<MoeDirectArgs> {
+  const MoeDirectArgs& a;
+  const int32_t* soff;
+  const int32_t* roff;
+  bool reject;
+  __device__ uint8_t* slot_row(int rank, uint64_t x, int64_t& loc) const {
+    loc = -1;
+    if (reject) return nullptr;
+    // every lane reads the same words: keep them in scalar registers
+    const int32_t ps = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)(uint64_t)a.loc[rank][x]);
+    if (ps < 0 || (uint64_t)ps >= a.tokens * (uint64_t)a.k) return nullptr;
+    const int j = __builtin_amdgcn_readfirstlane(a.dest[rank][x]);
+    if (j < 0 || j >= a.p) return nullptr;
+    const int64_t row = (int64_t)roff[rank * a.p + j] + (ps - soff[rank * a.p + j]);
+    loc = direct_loc(j, row);
+    return (uint8_t*)a.dst[j] + (uint64_t)row * a.row_bytes;
   }
-  out.pp = pp;
-  out.src = reinterpret_cast<const u32x4*>((const uint16_t*)a.src[rank] + t * a.hidden);
-  out.rank = rank;
+  // after every read of the token's locations
+  __device__ void finish(int rank, uint64_t x0, const int64_t (&loc)[kMaxTopK], int lane) const {
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s)
+      if (s < a.k && lane == 0) a.loc[rank][x0 + s] = loc[s];
+  }
+};
+
+__device__ __forceinline__ Rows<Fp8Args> make_rows(const Fp8Args& a, int32_t*, int*) { return Rows<Fp8Args>{a}; }
+__device__ __forceinline__ Rows<MoeDirectArgs> make_rows(const MoeDirectArgs& a, int32_t* tabs, int* flag) {
+  const bool reject = direct_tables(a, tabs, tabs + a.p * a.p, flag);
+  return Rows<MoeDirectArgs>{a, tabs, tabs + a.p * a.p, reject};
+}
+
+// The destination rows of token t's k slots (nullptr: not delivered).
+template <class Args>
+__device__ __forceinline__ bool slot_rows(const Rows<Args>& tgt, const Args& a, int rank, uint64_t t,
+                                          uint8_t* (&row)[kMaxTopK], int64_t (&loc)[kMaxTopK]) {
+  bool any = false;
+#pragma unroll
+  for (int s = 0; s < kMaxTopK; ++s) {
+    row[s] = nullptr;
+    loc[s] = -1;
+    if (s < a.k) {
+      row[s] = tgt.slot_row(rank, t * (uint64_t)a.k + s, loc[s]);
+      any |= row[s] != nullptr;
+    }
+  }
   return any;
 }
 
@@ -108,72 +150,76 @@ __device__ __forceinline__ bool pack_row(const Fp8Args& a, uint64_t r, PackRow& 
 // batches of CB columns and any hidden size works.
 constexpr int kPackCols = 8;
 
-template <int CB>
-COLL_STREAM_KERNEL void moe_pack_fp8_cols_kernel(Fp8Args a) {
+template <int CB, class Args>
+COLL_STREAM_KERNEL void moe_pack_fp8_cols_kernel(Args a) {
 #pragma clang fp contract(off)
+  extern __shared__ int32_t tabs[];  // direct dispatch: placement tables
+  __shared__ int flag;
+  const Rows<Args> tgt = make_rows(a, tabs, &flag);
   const int lane = (int)(threadIdx.x % kLanes);
-  const uint64_t H = a.hidden, R = a.row_bytes;
-  const int k = a.k;
-  const uint64_t A = a.tokens * (uint64_t)k;
+  const uint64_t H = a.hidden;
   const uint32_t nunits = (uint32_t)(H / 16);
   const uint32_t ncols = (nunits + kLanes - 1) / kLanes;
   const uint32_t g16 = (uint32_t)(a.group / 16);          // a power of two <= 64
   const uint32_t gsh = 31u - (uint32_t)__builtin_clz(g16);
   const uint32_t ngroups = (uint32_t)(H / a.group);
-  const uint32_t npad = (uint32_t)((R - H) / 4) - ngroups;
+  const uint32_t npad = (uint32_t)((a.row_bytes - H) / 4) - ngroups;
   const uint64_t rows = a.tokens * (uint64_t)a.p;
   for (uint64_t r = fp8_wave_id(); r < rows; r += fp8_wave_count()) {
-    PackRow pr;
-    if (!pack_row(a, r, pr)) continue;
-    for (uint32_t c0 = 0; c0 < ncols; c0 += CB) {
-      u32x4 x[CB][2];
-      uint32_t mb[CB];
-#pragma unroll
-      for (int u = 0; u < CB; ++u) {
-        const uint32_t j = (c0 + u) * kLanes + lane;
-        if (j < nunits) {
-          x[u][0] = ld16<true>(pr.src + 2 * j);
-          x[u][1] = ld16<true>(pr.src + 2 * j + 1);
-        } else {
-          x[u][0] = u32x4{0, 0, 0, 0};
-          x[u][1] = u32x4{0, 0, 0, 0};
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < CB; ++u) {
-        mb[u] = unit_amax_bits(x[u][0], x[u][1]);
-        for (uint32_t off = 1; off < g16; off <<= 1) mb[u] = max(mb[u], (uint32_t)__shfl_xor((int)mb[u], (int)off));
-      }
-      float sc[CB];
-#pragma unroll
-      for (int u = 0; u < CB; ++u) {
-        const float amax = fmaxf(__uint_as_float(mb[u] << 16), 0x1p-110f);
-        x[u][0] = unit_codes(x[u][0], x[u][1], 448.0f / amax);
-        sc[u] = amax / 448.0f;
-      }
-      for (int s = 0; s < k; ++s) {
-        const int32_t ps = pr.pp[s];
-        if (ps < 0 || (uint64_t)ps >= A) continue;
-        uint8_t* row = (uint8_t*)a.dst[pr.rank] + (uint64_t)ps * R;
-        u32x4* vc = reinterpret_cast<u32x4*>(row);
-        float* scales = reinterpret_cast<float*>(row + H);
+    const int rank = (int)(r / a.tokens);
+    const uint64_t t = r - (uint64_t)rank * a.tokens;
+    uint8_t* drow[kMaxTopK];
+    int64_t loc[kMaxTopK];
+    if (slot_rows(tgt, a, rank, t, drow, loc)) {
+      const u32x4* src = reinterpret_cast<const u32x4*>((const uint16_t*)a.src[rank] + t * H);
+      for (uint32_t c0 = 0; c0 < ncols; c0 += CB) {
+        u32x4 x[CB][2];
+        uint32_t mb[CB];
 #pragma unroll
         for (int u = 0; u < CB; ++u) {
           const uint32_t j = (c0 + u) * kLanes + lane;
           if (j < nunits) {
-            st16<true>(vc + j, x[u][0]);
-            if ((j & (g16 - 1)) == 0) scales[j >> gsh] = sc[u];
+            x[u][0] = ld16<true>(src + 2 * j);
+            x[u][1] = ld16<true>(src + 2 * j + 1);
+          } else {
+            x[u][0] = u32x4{0, 0, 0, 0};
+            x[u][1] = u32x4{0, 0, 0, 0};
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < CB; ++u) {
+          mb[u] = unit_amax_bits(x[u][0], x[u][1]);
+          for (uint32_t off = 1; off < g16; off <<= 1) mb[u] = max(mb[u], (uint32_t)__shfl_xor((int)mb[u], (int)off));
+        }
+        float sc[CB];
+#pragma unroll
+        for (int u = 0; u < CB; ++u) {
+          const float amax = fmaxf(__uint_as_float(mb[u] << 16), 0x1p-110f);
+          x[u][0] = unit_codes(x[u][0], x[u][1], 448.0f / amax);
+          sc[u] = amax / 448.0f;
+        }
+#pragma unroll
+        for (int s = 0; s < kMaxTopK; ++s) {
+          if (!drow[s]) continue;
+          u32x4* vc = reinterpret_cast<u32x4*>(drow[s]);
+          float* scales = reinterpret_cast<float*>(drow[s] + H);
+#pragma unroll
+          for (int u = 0; u < CB; ++u) {
+            const uint32_t j = (c0 + u) * kLanes + lane;
+            if (j < nunits) {
+              st16<true>(vc + j, x[u][0]);
+              if ((j & (g16 - 1)) == 0) scales[j >> gsh] = sc[u];
+            }
           }
         }
       }
-    }
-    if ((uint32_t)lane < npad) {
-      for (int s = 0; s < k; ++s) {
-        const int32_t ps = pr.pp[s];
-        if (ps < 0 || (uint64_t)ps >= A) continue;
-        reinterpret_cast<float*>((uint8_t*)a.dst[pr.rank] + (uint64_t)ps * R + H)[ngroups + lane] = 0.0f;
+      if ((uint32_t)lane < npad) {
+#pragma unroll
+        for (int s = 0; s < kMaxTopK; ++s)
+          if (drow[s]) reinterpret_cast<float*>(drow[s] + H)[ngroups + lane] = 0.0f;
       }
     }
+    tgt.finish(rank, t * (uint64_t)a.k, loc, lane);
   }
 }
 
@@ -181,74 +227,80 @@ COLL_STREAM_KERNEL void moe_pack_fp8_cols_kernel(Fp8Args a) {
 // is held in registers, UMAX units per lane (a power of two, hidden <=
 // 64 * 16 * UMAX), and a group's amax is reduced over the wave and over
 // its gu columns before any code is written.
-template <int UMAX>
-COLL_STREAM_KERNEL void moe_pack_fp8_rows_kernel(Fp8Args a) {
+template <int UMAX, class Args>
+COLL_STREAM_KERNEL void moe_pack_fp8_rows_kernel(Args a) {
 #pragma clang fp contract(off)
+  extern __shared__ int32_t tabs[];
+  __shared__ int flag;
+  const Rows<Args> tgt = make_rows(a, tabs, &flag);
   const int lane = (int)(threadIdx.x % kLanes);
-  const uint64_t H = a.hidden, R = a.row_bytes;
-  const int k = a.k;
-  const uint64_t A = a.tokens * (uint64_t)k;
+  const uint64_t H = a.hidden;
   const uint32_t nunits = (uint32_t)(H / 16);
   const uint32_t g16 = (uint32_t)(a.group / 16);
   const uint32_t gu = g16 / kLanes;                       // unit columns per group
   const uint32_t ngroups = (uint32_t)(H / a.group);
-  const uint32_t npad = (uint32_t)((R - H) / 4) - ngroups;
+  const uint32_t npad = (uint32_t)((a.row_bytes - H) / 4) - ngroups;
   const uint64_t rows = a.tokens * (uint64_t)a.p;
   for (uint64_t r = fp8_wave_id(); r < rows; r += fp8_wave_count()) {
-    PackRow pr;
-    if (!pack_row(a, r, pr)) continue;
-    u32x4 x[UMAX][2];
-#pragma unroll
-    for (int u = 0; u < UMAX; ++u) {
-      const uint32_t j = (uint32_t)(u * kLanes + lane);
-      if (j < nunits) {
-        x[u][0] = ld16<true>(pr.src + 2 * j);
-        x[u][1] = ld16<true>(pr.src + 2 * j + 1);
-      } else {
-        x[u][0] = u32x4{0, 0, 0, 0};
-        x[u][1] = u32x4{0, 0, 0, 0};
-      }
-    }
-    uint32_t mb[UMAX];
-#pragma unroll
-    for (int u = 0; u < UMAX; ++u) {
-      mb[u] = unit_amax_bits(x[u][0], x[u][1]);
-#pragma unroll
-      for (int off = 1; off < kLanes; off <<= 1) mb[u] = max(mb[u], (uint32_t)__shfl_xor((int)mb[u], off));
-    }
-    uint32_t gm[UMAX];  // amax of the unit's group (all its columns)
-#pragma unroll
-    for (int u = 0; u < UMAX; ++u) {
-      const uint32_t gi = (uint32_t)u / gu;
-      uint32_t m = 0;
-#pragma unroll
-      for (int v = 0; v < UMAX; ++v)
-        if ((uint32_t)v / gu == gi) m = max(m, mb[v]);
-      gm[u] = m;
-    }
-    float sc[UMAX];
-#pragma unroll
-    for (int u = 0; u < UMAX; ++u) {
-      const float amax = fmaxf(__uint_as_float(gm[u] << 16), 0x1p-110f);
-      sc[u] = amax / 448.0f;
-      x[u][0] = unit_codes(x[u][0], x[u][1], 448.0f / amax);
-    }
-    for (int s = 0; s < k; ++s) {
-      const int32_t ps = pr.pp[s];
-      if (ps < 0 || (uint64_t)ps >= A) continue;
-      uint8_t* row = (uint8_t*)a.dst[pr.rank] + (uint64_t)ps * R;
-      u32x4* vc = reinterpret_cast<u32x4*>(row);
-      float* scales = reinterpret_cast<float*>(row + H);
+    const int rank = (int)(r / a.tokens);
+    const uint64_t t = r - (uint64_t)rank * a.tokens;
+    uint8_t* drow[kMaxTopK];
+    int64_t loc[kMaxTopK];
+    if (slot_rows(tgt, a, rank, t, drow, loc)) {
+      const u32x4* src = reinterpret_cast<const u32x4*>((const uint16_t*)a.src[rank] + t * H);
+      u32x4 x[UMAX][2];
 #pragma unroll
       for (int u = 0; u < UMAX; ++u) {
         const uint32_t j = (uint32_t)(u * kLanes + lane);
         if (j < nunits) {
-          st16<true>(vc + j, x[u][0]);
-          if (lane == 0 && (uint32_t)u % gu == 0) scales[(uint32_t)u / gu] = sc[u];
+          x[u][0] = ld16<true>(src + 2 * j);
+          x[u][1] = ld16<true>(src + 2 * j + 1);
+        } else {
+          x[u][0] = u32x4{0, 0, 0, 0};
+          x[u][1] = u32x4{0, 0, 0, 0};
         }
       }
-      if ((uint32_t)lane < npad) scales[ngroups + lane] = 0.0f;
+      uint32_t mb[UMAX];
+#pragma unroll
+      for (int u = 0; u < UMAX; ++u) {
+        mb[u] = unit_amax_bits(x[u][0], x[u][1]);
+#pragma unroll
+        for (int off = 1; off < kLanes; off <<= 1) mb[u] = max(mb[u], (uint32_t)__shfl_xor((int)mb[u], off));
+      }
+      uint32_t gm[UMAX];  // amax of the unit's group (all its columns)
+#pragma unroll
+      for (int u = 0; u < UMAX; ++u) {
+        const uint32_t gi = (uint32_t)u / gu;
+        uint32_t m = 0;
+#pragma unroll
+        for (int v = 0; v < UMAX; ++v)
+          if ((uint32_t)v / gu == gi) m = max(m, mb[v]);
+        gm[u] = m;
+      }
+      float sc[UMAX];
+#pragma unroll
+      for (int u = 0; u < UMAX; ++u) {
+        const float amax = fmaxf(__uint_as_float(gm[u] << 16), 0x1p-110f);
+        sc[u] = amax / 448.0f;
+        x[u][0] = unit_codes(x[u][0], x[u][1], 448.0f / amax);
+      }
+#pragma unroll
+      for (int s = 0; s < kMaxTopK; ++s) {
+        if (!drow[s]) continue;
+        u32x4* vc = reinterpret_cast<u32x4*>(drow[s]);
+        float* scales = reinterpret_cast<float*>(drow[s] + H);
+#pragma unroll
+        for (int u = 0; u < UMAX; ++u) {
+          const uint32_t j = (uint32_t)(u * kLanes + lane);
+          if (j < nunits) {
+            st16<true>(vc + j, x[u][0]);
+            if (lane == 0 && (uint32_t)u % gu == 0) scales[(uint32_t)u / gu] = sc[u];
+          }
+        }
+        if ((uint32_t)lane < npad) scales[ngroups + lane] = 0.0f;
+      }
     }
+    tgt.finish(rank, t * (uint64_t)a.k, loc, lane);
   }
 }
 
@@ -377,24 +429,32 @@ COLL_STREAM_KERNEL void moe_dequant_fp8_kernel(Fp8Args a) {
   }
 }
 
-int launch_moe_pack_fp8(const Fp8Args& a, int max_grid, void* stream) {
-  hipStream_t s = (hipStream_t)stream;
+template <class Args>
+static int launch_pack_fp8_t(const Args& a, int max_grid, size_t shm, hipStream_t s) {
   const uint64_t rows = a.tokens * (uint64_t)a.p;
   const uint64_t wg_needed = (rows + (kBlock / kLanes) - 1) / (kBlock / kLanes);
   const int grid = (int)(wg_needed < (uint64_t)max_grid ? wg_needed : (uint64_t)max_grid);
   if (grid == 0) return 0;
   if (a.group <= 1024) {
-    hipLaunchKernelGGL((moe_pack_fp8_cols_kernel<kPackCols>), dim3(grid), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((moe_pack_fp8_cols_kernel<kPackCols, Args>), dim3(grid), dim3(kBlock), shm, s, a);
     return (int)hipGetLastError();
   }
   const uint64_t per_lane = (a.hidden / 16 + kLanes - 1) / kLanes;
-  if (per_lane <= 1) hipLaunchKernelGGL((moe_pack_fp8_rows_kernel<1>), dim3(grid), dim3(kBlock), 0, s, a);
-  else if (per_lane <= 2) hipLaunchKernelGGL((moe_pack_fp8_rows_kernel<2>), dim3(grid), dim3(kBlock), 0, s, a);
-  else if (per_lane <= 4) hipLaunchKernelGGL((moe_pack_fp8_rows_kernel<4>), dim3(grid), dim3(kBlock), 0, s, a);
-  else if (per_lane <= 8) hipLaunchKernelGGL((moe_pack_fp8_rows_kernel<8>), dim3(grid), dim3(kBlock), 0, s, a);
-  else if (per_lane <= 16) hipLaunchKernelGGL((moe_pack_fp8_rows_kernel<16>), dim3(grid), dim3(kBlock), 0, s, a);
+  if (per_lane <= 1) hipLaunchKernelGGL((moe_pack_fp8_rows_kernel<1, Args>), dim3(grid), dim3(kBlock), shm, s, a);
+  else if (per_lane <= 2) hipLaunchKernelGGL((moe_pack_fp8_rows_kernel<2, Args>), dim3(grid), dim3(kBlock), shm, s, a);
+  else if (per_lane <= 4) hipLaunchKernelGGL((moe_pack_fp8_rows_kernel<4, Args>), dim3(grid), dim3(kBlock), shm, s, a);
+  else if (per_lane <= 8) hipLaunchKernelGGL((moe_pack_fp8_rows_kernel<8, Args>), dim3(grid), dim3(kBlock), shm, s, a);
+  else if (per_lane <= 16) hipLaunchKernelGGL((moe_pack_fp8_rows_kernel<16, Args>), dim3(grid), dim3(kBlock), shm, s, a);
   else return (int)hipErrorInvalidValue;
   return (int)hipGetLastError();
+}
+
+int launch_moe_pack_fp8(const Fp8Args& a, int max_grid, void* stream) {
+  return launch_pack_fp8_t(a, max_grid, 0, (hipStream_t)stream);
+}
+
+int launch_moe_dispatch_fp8(const MoeDirectArgs& a, int max_grid, void* stream) {
+  return launch_pack_fp8_t(a, max_grid, direct_tables_bytes(a.p), (hipStream_t)stream);
 }
 
 int launch_moe_dequant_fp8(const Fp8Args& a, int max_grid, void* stream) {

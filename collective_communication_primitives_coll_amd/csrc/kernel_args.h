@@ -80,7 +80,7 @@ constexpr int kMaxTopK = 8;
 
 struct MoeIndexArgs {
   const int32_t* dest[kMaxRanks];  // per rank: destination rank of each assignment
-  int32_t* pos[kMaxRanks];         // per rank: packed row of each assignment
+  int32_t* pos[kMaxRanks];         // per rank: packed row of each assignment, at pos[x << pos_shift]
   int64_t* counts;                 // [p][p]: rows * hidden
   int64_t* counts2;                // optional [p][p]: rows * hidden2
   int32_t* status;                 // optional
@@ -88,6 +88,7 @@ struct MoeIndexArgs {
   uint64_t hidden;
   uint64_t hidden2;
   int p;
+  int pos_shift;                   // 1: pos goes to the low words of an int64 array
 };
 
 struct MoeRowArgs {
@@ -104,6 +105,30 @@ struct MoeRowArgs {
   int src_mis;                     // common misalignment of the src bases, or -1
   int dst_mis;
   int res_mis;
+  int32_t cap[kMaxRanks];          // direct combine: rows each src[j] holds
+};
+
+// Direct dispatch: token rows written straight into the destinations'
+// receive buffers.  loc[i][a] holds the packed row (low word, from the
+// index pass) on entry and (dest << 32) | row inside recv[dest] on exit,
+// or -1 for an assignment that is not delivered.
+struct MoeDirectArgs {
+  const void* src[kMaxRanks];      // tokens
+  void* dst[kMaxRanks];            // receive buffers
+  int64_t* loc[kMaxRanks];
+  const int32_t* dest[kMaxRanks];
+  int64_t cap[kMaxRanks];          // rows each receive buffer holds
+  const int64_t* counts;           // [p][p]: rows * count_unit
+  int32_t* status;                 // optional [p + 1]; entry p: 1 if a receive buffer is too small
+  uint64_t tokens;                 // T per rank
+  uint64_t hidden;                 // elements per token
+  uint64_t count_unit;             // counts per row
+  uint64_t group;                  // FP8 only
+  uint64_t row_bytes;              // FP8 only
+  int k;
+  int p;
+  int src_mis;
+  int dst_mis;
 };
 
 // Quantized dispatch: FP8 e4m3 rows with one fp32 scale per group of
@@ -177,6 +202,12 @@ int launch_moe_combine(int dtype, const MoeRowArgs& a, int max_grid, void* strea
 // bytes) and the bf16 dequantization of received rows.
 int launch_moe_pack_fp8(const Fp8Args& a, int max_grid, void* stream);
 int launch_moe_dequant_fp8(const Fp8Args& a, int max_grid, void* stream);
+
+// Direct dispatch (after launch_moe_index with pos_shift 1) and the
+// combine reading expert outputs through the locations.
+int launch_moe_dispatch(int elem_bytes, const MoeDirectArgs& a, int max_grid, void* stream);
+int launch_moe_dispatch_fp8(const MoeDirectArgs& a, int max_grid, void* stream);
+int launch_moe_combine_direct(int dtype, const MoeRowArgs& a, int max_grid, void* stream);
 
 // 16-byte vectors each lane of a copy kernel keeps in flight.
 constexpr uint64_t kCopyUnroll = 4;

@@ -20,6 +20,7 @@
 // rows spread over every wave of the grid, so a workgroup keeps four rows
 // in flight.
 #include "copy_tile.h"
+#include "moe_direct.h"
 
 namespace coll {
 
@@ -99,7 +100,7 @@ __global__ __launch_bounds__(kIdxThreads) void moe_index_kernel(MoeIndexArgs a) 
   if (tid == 0 && a.status) a.status[rank] = reject ? 1 : 0;
   __syncthreads();
   if (reject) {
-    for (uint64_t x = tid; x < A; x += kIdxThreads) pos[x] = -1;
+    for (uint64_t x = tid; x < A; x += kIdxThreads) pos[x << a.pos_shift] = -1;
     return;
   }
   // pass 2: packed row of every assignment
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(kIdxThreads) void moe_index_kernel(MoeIndexArgs a) 
         if (lane == leader) wofs[w][dl] += __popcll(m);
         rem &= ~m;
       }
-      if (d >= 0) pos[x] = mine;
+      if (d >= 0) pos[x << a.pos_shift] = mine;
     }
   }
 }
@@ -192,13 +193,55 @@ COLL_STREAM_KERNEL void moe_pack_kernel(MoeRowArgs a) {
   }
 }
 
+// Direct dispatch: assignment x of rank i (token x / k) is copied straight
+// to row roff[i][j] + ps - soff[i][j] of recv[j], j = dest[i][x], ps its
+// packed row from the index pass; loc[i][x] becomes (j << 32) | row.  One
+// row per wave, as the pack.  Nothing is delivered (every loc -1) when a
+// receive buffer is too small; a rejected rank's assignments stay -1.
+template <int B>
+COLL_STREAM_KERNEL void moe_dispatch_kernel(MoeDirectArgs a) {
+  using W = typename Word<B>::T;
+  extern __shared__ int32_t tabs[];
+  __shared__ int flag;
+  const int p = a.p;
+  int32_t* soff = tabs;
+  int32_t* roff = tabs + p * p;
+  const bool reject = direct_tables(a, soff, roff, &flag);
+  const int lane = (int)(threadIdx.x % kWaveLanes);
+  const uint64_t A = a.tokens * (uint64_t)a.k;
+  const uint64_t rows = A * (uint64_t)p;
+  const uint64_t H = a.hidden;
+  for (uint64_t r = wave_id(); r < rows; r += wave_count()) {
+    const int rank = (int)(r / A);
+    const uint64_t x = r - (uint64_t)rank * A;
+    int64_t* lp = a.loc[rank] + x;
+    // every lane reads the same words: keep them in scalar registers
+    const int32_t ps = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)(uint64_t)*lp);  // packed row (low word)
+    int64_t out = -1;
+    if (!reject && ps >= 0 && (uint64_t)ps < A) {
+      const int j = __builtin_amdgcn_readfirstlane(a.dest[rank][x]);
+      if (j >= 0 && j < p) {
+        const int64_t row = (int64_t)roff[rank * p + j] + (ps - soff[rank * p + j]);
+        const uint64_t t = x / (uint64_t)a.k;
+        const int mis = seg_mis(a.src_mis, a.dst_mis, t * H * B, (uint64_t)row * H * B);
+        copy_row_wave<B>((const W*)a.src[rank] + t * H, (W*)a.dst[j] + (uint64_t)row * H, H, mis, lane);
+        out = direct_loc(j, row);
+      }
+    }
+    if (lane == 0) *lp = out;
+  }
+}
+
 // out[rank][t] = residual[rank][t] (or +0) + sum_s w[t*k+s] * back[rank][pos[t*k+s]],
 // accumulated in fp32 in slot order with every product and sum rounded on
 // its own; slots whose pos lies outside [0, T*k) are skipped.  One token
 // row per wave, kCombBatch vectors per lane per step.
 constexpr int kCombBatch = 4;
 
-template <int DT>
+// DIRECT: pos[rank] is an int64 location array from the direct dispatch;
+// slot s reads row (loc & 0xffffffff) of src[loc >> 32] (skipped when the
+// location is -1 or outside the rank count or the row capacity cap[j]).
+template <int DT, bool DIRECT>
 COLL_STREAM_KERNEL void moe_combine_kernel(MoeRowArgs a) {
 #pragma clang fp contract(off)
   using T = Traits<DT>;
@@ -224,12 +267,24 @@ COLL_STREAM_KERNEL void moe_combine_kernel(MoeRowArgs a) {
       wt[s] = 0.0f;
       yrow[s] = nullptr;
       if (s < k) {
-        const int32_t ps = a.pos[rank][t * k + s];
-        ok[s] = ps >= 0 && (uint64_t)ps < Aa;
+        int j = rank;
+        int64_t row;
+        if constexpr (DIRECT) {
+          // the same location in every lane: read it into scalar registers
+          const uint64_t lw = reinterpret_cast<const uint64_t*>(a.pos[rank])[t * k + s];
+          const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)lw);
+          const int32_t hi = __builtin_amdgcn_readfirstlane((int32_t)(lw >> 32));
+          j = hi;
+          row = lo;
+          ok[s] = hi >= 0 && hi < a.p && row < a.cap[hi];
+        } else {
+          row = a.pos[rank][t * k + s];
+          ok[s] = row >= 0 && (uint64_t)row < Aa;
+        }
         if (ok[s]) {
           wt[s] = a.weights[rank][t * k + s];
-          yrow[s] = (const S*)a.src[rank] + (uint64_t)ps * H;
-          mis = seg_mis(mis, a.src_mis, 0, (uint64_t)ps * H * T::B);
+          yrow[s] = (const S*)a.src[j] + (uint64_t)row * H;
+          mis = seg_mis(mis, a.src_mis, 0, (uint64_t)row * H * T::B);
         }
       }
     }
@@ -329,9 +384,40 @@ int launch_moe_combine(int dtype, const MoeRowArgs& a, int max_grid, void* strea
   const int grid = (int)(rows < (uint64_t)max_grid ? rows : (uint64_t)max_grid);
   hipStream_t s = (hipStream_t)stream;
   if (dtype == kF32)
-    hipLaunchKernelGGL((moe_combine_kernel<kF32>), dim3(grid), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((moe_combine_kernel<kF32, false>), dim3(grid), dim3(kBlock), 0, s, a);
   else if (dtype == kBF16)
-    hipLaunchKernelGGL((moe_combine_kernel<kBF16>), dim3(grid), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((moe_combine_kernel<kBF16, false>), dim3(grid), dim3(kBlock), 0, s, a);
+  else
+    return (int)hipErrorInvalidValue;
+  return (int)hipGetLastError();
+}
+
+int launch_moe_combine_direct(int dtype, const MoeRowArgs& a, int max_grid, void* stream) {
+  const uint64_t rows = a.tokens * (uint64_t)a.p;
+  if (!rows) return 0;
+  const int grid = (int)(rows < (uint64_t)max_grid ? rows : (uint64_t)max_grid);
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == kF32)
+    hipLaunchKernelGGL((moe_combine_kernel<kF32, true>), dim3(grid), dim3(kBlock), 0, s, a);
+  else if (dtype == kBF16)
+    hipLaunchKernelGGL((moe_combine_kernel<kBF16, true>), dim3(grid), dim3(kBlock), 0, s, a);
+  else
+    return (int)hipErrorInvalidValue;
+  return (int)hipGetLastError();
+}
+
+int launch_moe_dispatch(int elem_bytes, const MoeDirectArgs& a, int max_grid, void* stream) {
+  const uint64_t rows = a.tokens * (uint64_t)a.k * (uint64_t)a.p;
+  if (!rows) return 0;
+  const int grid = (int)(rows < (uint64_t)max_grid ? rows : (uint64_t)max_grid);
+  const size_t shm = direct_tables_bytes(a.p);
+  hipStream_t s = (hipStream_t)stream;
+  if (elem_bytes == 1)
+    hipLaunchKernelGGL((moe_dispatch_kernel<1>), dim3(grid), dim3(kBlock), shm, s, a);
+  else if (elem_bytes == 2)
+    hipLaunchKernelGGL((moe_dispatch_kernel<2>), dim3(grid), dim3(kBlock), shm, s, a);
+  else if (elem_bytes == 4)
+    hipLaunchKernelGGL((moe_dispatch_kernel<4>), dim3(grid), dim3(kBlock), shm, s, a);
   else
     return (int)hipErrorInvalidValue;
   return (int)hipGetLastError();

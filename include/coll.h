@@ -289,7 +289,57 @@ coll_status_t coll_moe_dequant_fp8(const void* const* recv, void* const* out, in
                                    const int64_t* counts_dev, const int64_t* rows_cap,
                                    int32_t* status_dev, size_t hidden, size_t group, void* stream);
 
-/* One AllReduce of a batch (host-side view). */
+/* Direct MoE dispatch ([B] Ragged All-to-All flow and Expert Parallel;
+ * [A] 3.9: kernels that load and store peers' buffers directly): the pack
+ * and the dispatch exchange in one pass, with no staging buffer.  Every
+ * assignment's token row is written straight into its destination's
+ * receive buffer, in the layout coll_moe_pack followed by coll_alltoallv
+ * produces (source ranks in order, each source's rows in assignment
+ * order).
+ *   recv[j]      the rows rank j receives; recv_cap: HOST int64[p], rows
+ *                each recv[j] holds (at most 2^31 - 1);
+ *   loc[i][a]    device int64 (T*k): (dest << 32) | row inside recv[dest],
+ *                or -1 when assignment a is not delivered; the handle
+ *                coll_moe_combine_direct reads;
+ *   counts_dev   [p][p] int64 = hidden * rows, as coll_moe_pack;
+ *   status_dev   optional device int32[p + 1]: entries 0..p-1 as
+ *                coll_moe_pack (1: the rank had a destination outside
+ *                [0, p) and its locations are -1); entry p is 1 when some
+ *                rank would receive more rows than its capacity, and then
+ *                no payload is written and every location is -1.
+ * Any dtype (COLL_U8 included); tokens and recv aligned to the element
+ * size; k in [1, 8].  No output may overlap another buffer. */
+coll_status_t coll_moe_dispatch(const void* const* tokens, const int32_t* const* dest, void* const* recv,
+                                int64_t* const* loc, int64_t* counts_dev, int32_t* status_dev, int p,
+                                size_t tokens_per_rank, int k, size_t hidden, const int64_t* recv_cap,
+                                coll_dtype_t dtype, void* stream);
+
+/* Direct FP8 dispatch: coll_moe_dispatch with the encoded rows of
+ * coll_moe_pack_fp8 (bf16 tokens; rows of coll_moe_fp8_row_bytes bytes,
+ * recv_cap counted in those rows); counts_dev in bytes, counts_hidden_dev
+ * (optional) in rows * hidden.  tokens and recv 16-byte aligned. */
+coll_status_t coll_moe_dispatch_fp8(const void* const* tokens, const int32_t* const* dest, void* const* recv,
+                                    int64_t* const* loc, int64_t* counts_dev, int64_t* counts_hidden_dev,
+                                    int32_t* status_dev, int p, size_t tokens_per_rank, int k, size_t hidden,
+                                    size_t group, const int64_t* recv_cap, void* stream);
+
+/* Combine reading the experts' outputs where they lie, in place of
+ * coll_alltoallv_transposed followed by coll_moe_combine: y[j] holds
+ * y_rows[j] (HOST int64, at most 2^31 - 1) output rows of `hidden`
+ * elements in rank j's receive order; loc comes from coll_moe_dispatch or
+ * coll_moe_dispatch_fp8.  For every token t of rank i
+ *   out[i][t] = r + sum_s w[i][t*k+s] * y[loc >> 32][loc & 0xffffffff]
+ * with loc = loc[i][t*k+s] and the arithmetic of coll_moe_combine (fp32,
+ * slot order, each product and sum rounded, bf16 narrowed once).
+ * Locations that are -1, name a rank >= p or a row >= y_rows are skipped.
+ * fp32 and bf16 (COLL_ERR_UNSUPPORTED for int32).  In place: out[i] ==
+ * residual[i]. */
+coll_status_t coll_moe_combine_direct(const void* const* y, const int64_t* const* loc,
+                                      const float* const* weights, const void* const* residual,
+                                      void* const* out, int p, size_t tokens_per_rank, int k, size_t hidden,
+                                      const int64_t* y_rows, coll_dtype_t dtype, void* stream);
+
+/* One AllReduce of a batch (host-side view). *//* One AllReduce of a batch (host-side view). */
 typedef struct {
   const void* const* send;  /* host array of p device pointers */
   void* const* recv;        /* host array of p device pointers */

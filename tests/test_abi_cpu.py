@@ -247,3 +247,44 @@ def test_illegal_aliasing_rejected():
     ps_, _k22 = _arr([pk[0]] + [base + 0x48000000 + 0x10000 * i for i in range(1, p)])
     assert L.coll_moe_pack(s, s, pk_, ps_, base + 0x4f000000, None, p, T, k, H, 0, None) == AL
     assert nb > 0
+
+
+@host_only
+def test_direct_moe_invalid_arguments_rejected():
+    L = coll.lib()
+    INV, UNS, AL = coll.COLL_ERR_INVALID_ARG, coll.COLL_ERR_UNSUPPORTED, coll.COLL_ERR_ALIAS
+    base = 0x7F0000000000
+    tok, _k1 = _arr([base + 0x1000000 * r for r in range(4)])
+    dst, _k2 = _arr([base + 0x10000000 + 0x1000000 * r for r in range(4)])
+    rcv, _k3 = _arr([base + 0x20000000 + 0x1000000 * r for r in range(4)])
+    loc, _k4 = _arr([base + 0x30000000 + 0x1000000 * r for r in range(4)])
+    cnt = base + 0x40000000
+    T, k, H = 10, 2, 256
+    caps = (ctypes.c_int64 * 4)(20, 20, 20, 20)
+    neg = (ctypes.c_int64 * 4)(20, -1, 20, 20)
+    big = (ctypes.c_int64 * 4)(20, 1 << 31, 20, 20)
+    assert L.coll_moe_dispatch(tok, dst, rcv, loc, cnt, None, 4, T, 0, H, caps, 1, None) == INV     # k = 0
+    assert L.coll_moe_dispatch(tok, dst, rcv, loc, cnt, None, 4, T, k, 0, caps, 1, None) == INV     # hidden 0
+    assert L.coll_moe_dispatch(tok, dst, rcv, loc, cnt, None, 4, T, k, H, None, 1, None) == INV     # no caps
+    assert L.coll_moe_dispatch(tok, dst, rcv, loc, cnt, None, 4, T, k, H, neg, 1, None) == INV
+    assert L.coll_moe_dispatch(tok, dst, rcv, loc, cnt, None, 4, T, k, H, big, 1, None) == INV     # > 2^31 - 1 rows
+    assert L.coll_moe_dispatch(tok, dst, rcv, loc, None, None, 4, T, k, H, caps, 1, None) == INV    # no counts
+    assert L.coll_moe_dispatch(tok, dst, rcv, loc, cnt, None, 4, T, k, H, caps, 9, None) == INV     # bad dtype
+    odd, _k5 = _arr([base + 0x30000004, base + 0x31000000, base + 0x32000000, base + 0x33000000])
+    assert L.coll_moe_dispatch(tok, dst, rcv, odd, cnt, None, 4, T, k, H, caps, 1, None) == INV     # loc not 8-aligned
+    assert L.coll_moe_dispatch(tok, dst, tok, loc, cnt, None, 4, T, k, H, caps, 1, None) == AL      # recv = tokens
+    assert L.coll_moe_dispatch(tok, dst, rcv, loc, cnt, loc[0], 4, T, k, H, caps, 1, None) == AL    # status in loc
+    assert L.coll_moe_dispatch_fp8(tok, dst, rcv, loc, cnt, None, None, 4, T, k, 192, 48, caps, None) == UNS
+    assert L.coll_moe_dispatch_fp8(tok, dst, rcv, loc, cnt, None, None, 4, T, k, 100, 16, caps, None) == INV
+    mis, _k6 = _arr([base + 0x20000008, base + 0x21000000, base + 0x22000000, base + 0x23000000])
+    assert L.coll_moe_dispatch_fp8(tok, dst, mis, loc, cnt, None, None, 4, T, k, H, 128, caps, None) == INV
+    assert L.coll_moe_dispatch_fp8(tok, dst, rcv, loc, cnt, cnt, None, 4, T, k, H, 128, caps, None) == AL
+    w, _k7 = _arr([base + 0x50000000 + 0x1000000 * r for r in range(4)])
+    out, _k8 = _arr([base + 0x60000000 + 0x1000000 * r for r in range(4)])
+    assert L.coll_moe_combine_direct(rcv, loc, w, None, out, 4, T, k, H, None, 1, None) == INV     # no y_rows
+    assert L.coll_moe_combine_direct(rcv, loc, w, None, out, 4, T, k, H, neg, 1, None) == INV
+    assert L.coll_moe_combine_direct(rcv, loc, w, None, out, 4, T, k, H, caps, 2, None) == UNS     # int32
+    assert L.coll_moe_combine_direct(rcv, loc, w, None, out, 4, T, k, H, caps, 3, None) == INV     # bytes
+    assert L.coll_moe_combine_direct(rcv, odd, w, None, out, 4, T, k, H, caps, 1, None) == INV
+    assert L.coll_moe_combine_direct(rcv, loc, w, None, rcv, 4, T, k, H, caps, 1, None) == AL      # out = y
+    assert L.coll_moe_combine_direct(rcv, loc, w, None, out, 4, 0, k, H, caps, 1, None) == coll.COLL_OK  # T = 0

@@ -926,6 +926,182 @@ def test_u8_copy_collectives(coll):
 
 
 # ----------------------------------------------------------------------------
+# Direct MoE dispatch and combine (no staging copies)
+# ----------------------------------------------------------------------------
+
+def _i64dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int64)).cuda()
+
+
+def _expected_locs(dests, slots):
+    return [(np.asarray(d, dtype=np.int64) << 32) | np.asarray(sl, dtype=np.int64) for d, sl in zip(dests, slots)]
+
+
+@pytest.mark.parametrize("p,T,k,H", [(1, 5, 1, 8), (2, 1, 2, 7), (3, 100, 2, 64), (8, 257, 2, 96),
+                                     (8, 60, 8, 40), (16, 33, 3, 33), (64, 4, 2, 16)])
+@pytest.mark.parametrize("dtype", [BF16, F32])
+def test_moe_dispatch_direct(coll, p, T, k, H, dtype):
+    import torch
+    toks, routes, _ = _moe_case(p, T, k, H, dtype, 400 + T + H)
+    counts, slots, recv = ref.moe_dispatch_direct(toks, routes, k, H)
+    rows = counts.sum(axis=0) // H
+    cap = [int(r) + 3 for r in rows]
+    drecv = [empty(c * H, dtype, fill=0x5A5A5A5A) for c in cap]
+    loc = [torch.full((T * k,), 77, dtype=torch.int64, device="cuda") for _ in range(p)]
+    cdev = torch.full((p * p,), -1, dtype=torch.int64, device="cuda")
+    status = torch.full((p + 1,), -9, dtype=torch.int32, device="cuda")
+    coll.coll_moe_dispatch([to_dev(x, dtype) for x in toks], [_i32dev(r) for r in routes], drecv, loc, cdev, k, H,
+                           recv_cap=cap, status_dev=status)
+    sync()
+    assert status.cpu().tolist() == [0] * (p + 1)
+    assert np.array_equal(cdev.cpu().numpy().reshape(p, p), counts)
+    for j in range(p):
+        got = to_host(drecv[j], dtype)
+        assert_bits_equal(got[:int(rows[j]) * H], recv[j], f"direct recv {j}")
+        assert_bits_equal(got[int(rows[j]) * H:], to_host(empty((cap[j] - int(rows[j])) * H, dtype, fill=0x5A5A5A5A),
+                                                          dtype), f"recv {j} beyond the rows untouched")
+    for i, e in enumerate(_expected_locs(routes, slots)):
+        assert np.array_equal(loc[i].cpu().numpy(), e), f"locations rank {i}"
+
+
+def test_moe_dispatch_direct_rejections(coll):
+    import torch
+    p, T, k, H = 4, 40, 2, 24
+    toks, routes, _ = _moe_case(p, T, k, H, BF16, 410)
+    routes[1] = routes[1].copy()
+    routes[1][7] = 9                                    # rank 1 rejected
+    kept = [r if i != 1 else np.zeros(0, np.int32) for i, r in enumerate(routes)]
+    counts, slots, recv = ref.moe_dispatch_direct(toks, kept, k, H)
+    rows = counts.sum(axis=0) // H
+    cap = [int(r) for r in rows]
+    drecv = [empty(max(c, 1) * H, BF16, fill=0) for c in cap]
+    loc = [torch.zeros(T * k, dtype=torch.int64, device="cuda") for _ in range(p)]
+    cdev = torch.empty(p * p, dtype=torch.int64, device="cuda")
+    status = torch.full((p + 1,), -9, dtype=torch.int32, device="cuda")
+    dt = [to_dev(x, BF16) for x in toks]
+    dd = [_i32dev(r) for r in routes]
+    coll.coll_moe_dispatch(dt, dd, drecv, loc, cdev, k, H, recv_cap=cap, status_dev=status)
+    sync()
+    assert status.cpu().tolist() == [0, 1, 0, 0, 0]
+    assert loc[1].cpu().numpy().tolist() == [-1] * (T * k)
+    for j in range(p):
+        assert_bits_equal(to_host(drecv[j], BF16)[:cap[j] * H], recv[j], f"recv {j} without the rejected rank")
+    exp = _expected_locs(kept, slots)
+    for i in (0, 2, 3):
+        assert np.array_equal(loc[i].cpu().numpy(), exp[i])
+    # one receive buffer one row short: nothing delivered, every location -1
+    small = list(cap)
+    small[2] -= 1
+    drecv2 = [empty(max(c, 1) * H, BF16, fill=0x1357) for c in small]
+    coll.coll_moe_dispatch(dt, dd, drecv2, loc, cdev, k, H, recv_cap=small, status_dev=status)
+    sync()
+    assert status.cpu().tolist() == [0, 1, 0, 0, 1]
+    for i in range(p):
+        assert loc[i].cpu().numpy().tolist() == [-1] * (T * k)
+    for j in range(p):
+        assert torch.equal(drecv2[j], empty(max(small[j], 1) * H, BF16, fill=0x1357)), "payload written"
+
+
+def test_moe_dispatch_direct_misaligned(coll):
+    """Rows whose byte length is not a multiple of 16 and token / receive
+    buffers shifted by one and three elements: vector heads and tails per
+    row and the element path."""
+    import torch
+    p, T, k, H = 3, 30, 2, 13
+    toks, routes, _ = _moe_case(p, T, k, H, BF16, 420)
+    counts, slots, recv = ref.moe_dispatch_direct(toks, routes, k, H)
+    rows = counts.sum(axis=0) // H
+    kt, dtok = zip(*[upload_offset(x, BF16, 1) for x in toks])
+    kr, drecv = zip(*[upload_offset(np.zeros(int(r) * H, np.uint16), BF16, 3) for r in rows])
+    loc = [torch.empty(T * k, dtype=torch.int64, device="cuda") for _ in range(p)]
+    cdev = torch.empty(p * p, dtype=torch.int64, device="cuda")
+    coll.coll_moe_dispatch(list(dtok), [_i32dev(r) for r in routes], list(drecv), loc, cdev, k, H,
+                           recv_cap=[int(r) for r in rows])
+    sync()
+    for j in range(p):
+        assert_bits_equal(to_host(drecv[j], BF16), recv[j], f"misaligned direct recv {j}")
+
+
+@pytest.mark.parametrize("p,T,k,H", [(2, 50, 1, 24), (4, 301, 2, 40), (8, 128, 8, 17), (8, 64, 2, 7168)])
+@pytest.mark.parametrize("dtype", [BF16, F32])
+@pytest.mark.parametrize("with_residual", [False, True])
+def test_moe_combine_direct(coll, p, T, k, H, dtype, with_residual):
+    """The combine reading expert outputs in place; the expert outputs and
+    the locations are the oracle's (the dispatch test checks that the GPU's
+    locations equal them).  Includes a location naming a row past y_rows
+    and a -1, both skipped."""
+    import torch
+    toks, routes, weights = _moe_case(p, T, k, H, dtype, 430 + T + k)
+    counts, slots, recv = ref.moe_dispatch_direct(toks, routes, k, H)
+    ys = [gen(1, len(r), dtype, 440 + j)[0] for j, r in enumerate(recv)]          # any expert output
+    locs = _expected_locs(routes, slots)
+    y_rows = [len(y) // H for y in ys]
+    locs[0] = locs[0].copy()
+    locs[0][0] = -1
+    j1 = int(locs[0][1] >> 32)
+    locs[0][1] = (j1 << 32) | (y_rows[j1] + 5)     # past the rows of y[j1]
+    residual = gen(p, T * H, dtype, 450) if with_residual else None
+    out = [to_dev(r, dtype) for r in residual] if with_residual else [empty(T * H, dtype) for _ in range(p)]
+    coll.coll_moe_combine_direct([to_dev(y, dtype) if len(y) else empty(H, dtype) for y in ys],
+                                 [_i64dev(l_) for l_ in locs], [_f32dev(w) for w in weights], out, k, H,
+                                 y_rows=y_rows, residual=out if with_residual else None)
+    sync()
+    for i in range(p):
+        res_i = residual[i] if with_residual else None
+        if i == 0:   # assignments 0 and 1 are skipped
+            exp = _combine_skipping(ys, routes[0], slots[0], weights[0], k, H, dtype, res_i, skip={0, 1})
+        else:
+            exp = ref.moe_combine_direct(ys, routes[i], slots[i], weights[i], k, H, dtype, res_i)
+        assert_bits_equal(to_host(out[i], dtype), exp, f"direct combine rank {i}")
+
+
+def _combine_skipping(ys, dest, slot, weights, k, H, dtype, residual, skip):
+    """The oracle's combine with the given assignments left out."""
+    T = len(dest) // k
+    acc = (ref.bf16_to_f32(residual) if dtype == BF16 else np.asarray(residual, np.float32)).reshape(T, H).copy() \
+        if residual is not None else np.zeros((T, H), np.float32)
+    w = np.asarray(weights, np.float32)
+    for s_ in range(k):
+        for t in range(T):
+            a = t * k + s_
+            if a in skip:
+                continue
+            y = np.asarray(ys[int(dest[a])])[int(slot[a]) * H:(int(slot[a]) + 1) * H]
+            yv = ref.bf16_to_f32(y) if dtype == BF16 else np.asarray(y, np.float32)
+            acc[t] = (acc[t] + (w[a] * yv).astype(np.float32)).astype(np.float32)
+    acc = acc.reshape(-1)
+    return ref.f32_to_bf16_rne(acc) if dtype == BF16 else acc
+
+
+@pytest.mark.parametrize("p,T,k,H,G", [(2, 9, 2, 256, 128), (4, 33, 3, 7168, 128), (3, 7, 8, 1024, 1024),
+                                       (2, 5, 2, 4096, 2048), (8, 20, 2, 2048, 64)])
+def test_moe_dispatch_fp8_direct(coll, p, T, k, H, G):
+    import torch
+    from oracle import fp8
+    R = fp8.row_bytes(H, G)
+    toks, routes, _ = _moe_case(p, T, k, H, BF16, 460 + T + H)
+    counts, slots, recv = fp8.moe_dispatch_direct_fp8(toks, routes, k, H, G)
+    rows = counts.sum(axis=0) // R
+    drecv = [_u8(max(int(r), 1) * R, 0xA5) for r in rows]
+    loc = [torch.empty(T * k, dtype=torch.int64, device="cuda") for _ in range(p)]
+    cdev = torch.empty(p * p, dtype=torch.int64, device="cuda")
+    ch = torch.empty(p * p, dtype=torch.int64, device="cuda")
+    status = torch.full((p + 1,), -9, dtype=torch.int32, device="cuda")
+    coll.coll_moe_dispatch_fp8([to_dev(x, BF16) for x in toks], [_i32dev(r) for r in routes], drecv, loc, cdev, k, H,
+                               G, recv_cap=[max(int(r), 1) for r in rows], counts_hidden_dev=ch, status_dev=status)
+    sync()
+    assert status.cpu().tolist() == [0] * (p + 1)
+    C = cdev.cpu().numpy().reshape(p, p)
+    assert np.array_equal(C, counts)
+    assert np.array_equal(ch.cpu().numpy().reshape(p, p), counts // R * H)
+    for j in range(p):
+        assert_bits_equal(drecv[j].cpu().numpy()[:int(rows[j]) * R], recv[j], f"direct fp8 recv {j}")
+    for i, e in enumerate(_expected_locs(routes, slots)):
+        assert np.array_equal(loc[i].cpu().numpy(), e), f"fp8 locations rank {i}"
+
+
+# ----------------------------------------------------------------------------
 # Batched AllReduce
 # ----------------------------------------------------------------------------
 
