@@ -58,7 +58,8 @@ def parse_args(argv=None):
     ap.add_argument("--no-collectives", action="store_true", help="time only the main step")
     ap.add_argument("--only", default=None,
                     help="comma list of extra collectives to time (ar_ring, ar_onepass, ar_hd, "
-                         "ar_literal, ar_avg, ar_premul, a2a, a2av, moe, moe_fp8, gs, ar_small, batch, copy, ce)")
+                         "ar_literal, ar_avg, ar_premul, a2a, a2av, moe, moe_fp8, moe_direct, moe_fp8_direct, gs, ar_small, "
+                         "batch, copy, ce)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
     return ap.parse_args(argv)
 
@@ -328,6 +329,12 @@ def extra_collectives(torch, coll, inputs, metrics, dev, which, iters=10, warmup
     if want("moe_fp8"):
         rows.append(moe_fp8_row(torch, coll, inputs, dev, iters, warmup))
         torch.cuda.empty_cache()
+    if want("moe_direct"):
+        rows.append(moe_direct_row(torch, coll, inputs, dev, iters, warmup, fp8=False))
+        torch.cuda.empty_cache()
+    if want("moe_fp8_direct"):
+        rows.append(moe_direct_row(torch, coll, inputs, dev, iters, warmup, fp8=True))
+        torch.cuda.empty_cache()
 
     # --- Gather / Scatter, p = 8, 2^23 bf16 per rank (root buffer 128 MiB) ----
     if want("gs"):
@@ -450,7 +457,7 @@ def moe_row(torch, coll, inputs, dev, iters, warmup):
     f_comb = coll.coll_moe_combine(back, pos, wts, out, k, H, residual=out, defer=True)
     t = [stats_us(x)[0] for x in time_launches(torch, [f_pack, f_disp, f_rev, f_comb], iters, warmup)]
     # algorithmic HBM bytes per stage (all ranks)
-    b_pack = p * (A * H * d * 2 + A * 4 * 2)          # gather A rows, write A rows, read dest, write pos
+    b_pack = p * (T * H * d + A * H * d + A * 4 * 2)  # tokens once, A rows out, dest, pos
     b_xchg = p * 2 * A * H * d                       # each exchange reads and writes every row once
     b_comb = p * (A * H * d + 2 * T * H * d + A * 8)  # A rows + residual in, T rows out, pos + weights
     stage = {}
@@ -513,6 +520,58 @@ def moe_fp8_row(torch, coll, inputs, dev, iters, warmup):
             "hbm_bytes": tot_b, "hbm_GBps": round(tot_b / (tot_us * 1e-6) / 1e9, 1),
             "pct_hbm_peak": round(100.0 * tot_b / (tot_us * 1e-6) / 1e9 / HBM_PEAK, 1), "stages": stage,
             "workload": "FP8 pack -> byte Alltoallv -> dequant -> bf16 reverse Alltoallv -> combine + residual"}
+
+
+def moe_direct_row(torch, coll, inputs, dev, iters, warmup, fp8: bool):
+    """The MoE layer without staging copies: the dispatch writes rows straight
+    into the receive buffers (bf16, or FP8 with one scale per 128 elements
+    followed by the dequant the experts read), the combine reads the expert
+    outputs in place; p = 8, 4096 tokens x 7168 per rank, top-2."""
+    p, T, H, k, G = 8, 4096, 7168, 2, 128
+    A = T * k
+    toks = [to_dev(torch, x, dev) for x in inputs.rank_buffers(inputs.WL_MOE_A2A, p, T * H, inputs.BF16,
+                                                               dist="normal")]
+    dest = [torch.from_numpy(r).to(dev) for r in inputs.moe_routes(p, T, k)]
+    wts = [torch.from_numpy(w).to(dev) for w in inputs.moe_weights(p, T, k)]
+    cnt = inputs.moe_routes(p, T, k)
+    rows = np.zeros(p, dtype=np.int64)
+    for r in cnt:
+        rows += np.bincount(r, minlength=p)
+    loc = [torch.empty(A, dtype=torch.int64, device=dev) for _ in range(p)]
+    counts = torch.empty(p * p, dtype=torch.int64, device=dev)
+    out = [torch.empty(T * H, dtype=torch.bfloat16, device=dev).normal_() for _ in range(p)]
+    cap = [int(r) for r in rows]
+    if fp8:
+        R = coll.coll_moe_fp8_row_bytes(H, G)
+        recv = [torch.empty(c * R, dtype=torch.uint8, device=dev) for c in cap]
+        ex = [torch.empty(c * H, dtype=torch.bfloat16, device=dev) for c in cap]
+        f_disp = coll.coll_moe_dispatch_fp8(toks, dest, recv, loc, counts, k, H, G, recv_cap=cap, defer=True)
+        f_deq = coll.coll_moe_dequant_fp8(recv, ex, counts, cap, H, G, defer=True)
+        fns = [f_disp, f_deq]
+        b_disp = p * (T * H * 2 + A * R + A * 20)
+        stages = [("dispatch_fp8_direct", b_disp), ("dequant_fp8", p * (A * R + A * H * 2))]
+    else:
+        R = H * 2
+        recv = [torch.empty(c * H, dtype=torch.bfloat16, device=dev) for c in cap]
+        ex = recv
+        f_disp = coll.coll_moe_dispatch(toks, dest, recv, loc, counts, k, H, recv_cap=cap, defer=True)
+        fns = [f_disp]
+        stages = [("dispatch_direct", p * (T * H * 2 + A * H * 2 + A * 20))]
+    f_comb = coll.coll_moe_combine_direct(ex, loc, wts, out, k, H, y_rows=cap, residual=out, defer=True)
+    fns.append(f_comb)
+    stages.append(("combine_direct", p * (A * H * 2 + 2 * T * H * 2 + A * 12)))
+    t = [stats_us(x)[0] for x in time_launches(torch, fns, iters, warmup)]
+    st = {}
+    for (name, b), us in zip(stages, t):
+        st[name] = {"t_med_us": round(us, 2), "hbm_bytes": b, "hbm_GBps": round(b / (us * 1e-6) / 1e9, 1)}
+    tot_us = sum(t)
+    tot_b = sum(b for _, b in stages)
+    return {"name": "moe_fp8_direct" if fp8 else "moe_direct", "p": p, "tokens": T, "hidden": H, "top_k": k,
+            "dtype": "fp8e4m3/bf16" if fp8 else "bf16", "t_med_us": round(tot_us, 2), "hbm_bytes": tot_b,
+            "hbm_GBps": round(tot_b / (tot_us * 1e-6) / 1e9, 1),
+            "pct_hbm_peak": round(100.0 * tot_b / (tot_us * 1e-6) / 1e9 / HBM_PEAK, 1), "stages": st,
+            "workload": ("direct FP8 dispatch -> dequant -> combine reading expert outputs in place" if fp8 else
+                         "direct dispatch -> combine reading expert outputs in place")}
 
 
 def batch_row(torch, coll, inputs, dev, iters=5, warmup=2):

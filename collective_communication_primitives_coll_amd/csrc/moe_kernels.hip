@@ -16,9 +16,11 @@
 // packed row, stable in assignment order.  Destinations outside [0, p)
 // reject the rank: its counts are 0 and every pos is -1.
 //
-// Payload pack and combine: one wave per row (a token's hidden vector),
-// rows spread over every wave of the grid, so a workgroup keeps four rows
-// in flight.
+// Payload copy and combine: one wave per token row, rows spread over every
+// wave of the grid, so a workgroup keeps four rows in flight.  The copy
+// reads a token once and writes it to each of its k slots: rows of the
+// rank's packed buffer (the pack) or rows of the destinations' receive
+// buffers (the direct dispatch, which replaces pack + exchange).
 #include "copy_tile.h"
 #include "moe_direct.h"
 
@@ -172,63 +174,126 @@ __device__ __forceinline__ void copy_row_wave(const typename Word<B>::T* src, ty
   }
 }
 
-// packed[rank][pos[a] * H ...] = tokens[rank][(a / k) * H ...], one row per
-// wave.  Token rows are read through the cache (a token with k > 1 slots
-// is read k times).
-template <int B>
-COLL_STREAM_KERNEL void moe_pack_kernel(MoeRowArgs a) {
-  using W = typename Word<B>::T;
-  const int lane = (int)(threadIdx.x % kWaveLanes);
-  const uint64_t A = a.tokens * (uint64_t)a.k;
-  const uint64_t rows = A * (uint64_t)a.p;
-  for (uint64_t r = wave_id(); r < rows; r += wave_count()) {
-    const int rank = (int)(r / A);
-    const uint64_t x = r - (uint64_t)rank * A;
+// Where a token's slot rows go.  SlotRows<MoeRowArgs>: the rank's packed
+// buffer at row pos (the pack).  SlotRows<MoeDirectArgs>: the destination's
+// receive buffer at row roff[i][j] + ps - soff[i][j] (the direct dispatch,
+// ps = the index pass's packed row, kept in the low word of the location),
+// with loc[i][x] = (j << 32) | row written back once the token is done.
+template <class Args> struct SlotRows;
+
+template <> struct SlotRows<MoeRowArgs> {
+  const MoeRowArgs& a;
+  __device__ void* row(int rank, uint64_t x, uint64_t row_bytes, int64_t& loc, uint64_t& off) const {
+    loc = -1;
     const int32_t ps = a.pos[rank][x];
-    if (ps < 0 || (uint64_t)ps >= A) continue;
-    const uint64_t t = x / (uint64_t)a.k;
-    const uint64_t so = t * a.hidden, dof = (uint64_t)ps * a.hidden;
-    const int mis = seg_mis(a.src_mis, a.dst_mis, so * B, dof * B);
-    copy_row_wave<B>((const W*)a.src[rank] + so, (W*)a.dst[rank] + dof, a.hidden, mis, lane);
+    if (ps < 0 || (uint64_t)ps >= a.tokens * (uint64_t)a.k) return nullptr;
+    off = (uint64_t)ps * row_bytes;
+    return (uint8_t*)a.dst[rank] + off;
   }
+  __device__ void finish(int, uint64_t, const int64_t (&)[kMaxTopK], int) const {}
+};
+
+template <> struct SlotRows<MoeDirectArgs> {
+  const MoeDirectArgs& a;
+  const int32_t* soff;
+  const int32_t* roff;
+  bool reject;
+  __device__ void* row(int rank, uint64_t x, uint64_t row_bytes, int64_t& loc, uint64_t& off) const {
+    loc = -1;
+    if (reject) return nullptr;
+    // every lane reads the same words: keep them in scalar registers
+    const int32_t ps = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)(uint64_t)a.loc[rank][x]);
+    if (ps < 0 || (uint64_t)ps >= a.tokens * (uint64_t)a.k) return nullptr;
+    const int j = __builtin_amdgcn_readfirstlane(a.dest[rank][x]);
+    if (j < 0 || j >= a.p) return nullptr;
+    const int64_t rw = (int64_t)roff[rank * a.p + j] + (ps - soff[rank * a.p + j]);
+    loc = direct_loc(j, rw);
+    off = (uint64_t)rw * row_bytes;
+    return (uint8_t*)a.dst[j] + off;
+  }
+  // after every read of the token's locations
+  __device__ void finish(int rank, uint64_t x0, const int64_t (&loc)[kMaxTopK], int lane) const {
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s)
+      if (s < a.k && lane == 0) a.loc[rank][x0 + s] = loc[s];
+  }
+};
+
+__device__ __forceinline__ SlotRows<MoeRowArgs> make_slot_rows(const MoeRowArgs& a, int32_t*, int*) {
+  return SlotRows<MoeRowArgs>{a};
+}
+__device__ __forceinline__ SlotRows<MoeDirectArgs> make_slot_rows(const MoeDirectArgs& a, int32_t* tabs, int* flag) {
+  const bool reject = direct_tables(a, tabs, tabs + a.p * a.p, flag);
+  return SlotRows<MoeDirectArgs>{a, tabs, tabs + a.p * a.p, reject};
 }
 
-// Direct dispatch: assignment x of rank i (token x / k) is copied straight
-// to row roff[i][j] + ps - soff[i][j] of recv[j], j = dest[i][x], ps its
-// packed row from the index pass; loc[i][x] becomes (j << 32) | row.  One
-// row per wave, as the pack.  Nothing is delivered (every loc -1) when a
-// receive buffer is too small; a rejected rank's assignments stay -1.
-template <int B>
-COLL_STREAM_KERNEL void moe_dispatch_kernel(MoeDirectArgs a) {
+// Token rows copied to their k slots, one token per wave: the row is read
+// once, kRowBatch 16-byte vectors per lane at a time, and each batch is
+// stored to every slot.  Rows that are not all 16-byte aligned (row bytes
+// not a multiple of 16, or a base off a 16-byte boundary) go slot by slot
+// through copy_row_wave, which handles heads and tails.
+template <int B, class Args>
+COLL_STREAM_KERNEL void moe_token_copy_kernel(Args a) {
   using W = typename Word<B>::T;
-  extern __shared__ int32_t tabs[];
+  extern __shared__ int32_t tabs[];  // direct dispatch: placement tables
   __shared__ int flag;
-  const int p = a.p;
-  int32_t* soff = tabs;
-  int32_t* roff = tabs + p * p;
-  const bool reject = direct_tables(a, soff, roff, &flag);
+  const SlotRows<Args> tgt = make_slot_rows(a, tabs, &flag);
   const int lane = (int)(threadIdx.x % kWaveLanes);
-  const uint64_t A = a.tokens * (uint64_t)a.k;
-  const uint64_t rows = A * (uint64_t)p;
   const uint64_t H = a.hidden;
+  const uint64_t RB = H * B;
+  const bool aligned = RB % 16 == 0 && a.src_mis == 0 && a.dst_mis == 0;
+  const uint64_t nvec = RB / 16;
+  const uint64_t rows = a.tokens * (uint64_t)a.p;
   for (uint64_t r = wave_id(); r < rows; r += wave_count()) {
-    const int rank = (int)(r / A);
-    const uint64_t x = r - (uint64_t)rank * A;
-    int64_t* lp = a.loc[rank] + x;
-    // every lane reads the same words: keep them in scalar registers
-    const int32_t ps = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)(uint64_t)*lp);  // packed row (low word)
-    int64_t out = -1;
-    if (!reject && ps >= 0 && (uint64_t)ps < A) {
-      const int j = __builtin_amdgcn_readfirstlane(a.dest[rank][x]);
-      if (j >= 0 && j < p) {
-        const int64_t row = (int64_t)roff[rank * p + j] + (ps - soff[rank * p + j]);
-        const uint64_t t = x / (uint64_t)a.k;
-        const int mis = seg_mis(a.src_mis, a.dst_mis, t * H * B, (uint64_t)row * H * B);
-        copy_row_wave<B>((const W*)a.src[rank] + t * H, (W*)a.dst[j] + (uint64_t)row * H, H, mis, lane);
-        out = direct_loc(j, row);
+    const int rank = (int)(r / a.tokens);
+    const uint64_t t = r - (uint64_t)rank * a.tokens;
+    void* drow[kMaxTopK];
+    int64_t loc[kMaxTopK];
+    uint64_t off[kMaxTopK];
+    bool any = false;
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s) {
+      drow[s] = nullptr;
+      loc[s] = -1;
+      off[s] = 0;
+      if (s < a.k) {
+        drow[s] = tgt.row(rank, t * (uint64_t)a.k + s, RB, loc[s], off[s]);
+        any |= drow[s] != nullptr;
       }
     }
-    if (lane == 0) *lp = out;
+    if (any) {
+      const W* src = (const W*)a.src[rank] + t * H;
+      if (aligned) {
+        const u32x4* vs = reinterpret_cast<const u32x4*>(src);
+        for (uint64_t j0 = 0; j0 < nvec; j0 += (uint64_t)kRowBatch * kWaveLanes) {
+          u32x4 v[kRowBatch];
+#pragma unroll
+          for (int u = 0; u < kRowBatch; ++u) {
+            const uint64_t j = j0 + (uint64_t)u * kWaveLanes + lane;
+            if (j < nvec) v[u] = ld16<true>(vs + j);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int s = 0; s < kMaxTopK; ++s) {
+            if (!drow[s]) continue;
+            u32x4* vd = reinterpret_cast<u32x4*>(drow[s]);
+#pragma unroll
+            for (int u = 0; u < kRowBatch; ++u) {
+              const uint64_t j = j0 + (uint64_t)u * kWaveLanes + lane;
+              if (j < nvec) st16<true>(vd + j, v[u]);
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < kMaxTopK; ++s) {
+          if (!drow[s]) continue;
+          const int mis = seg_mis(a.src_mis, a.dst_mis, t * RB, off[s]);
+          copy_row_wave<B>(src, (W*)drow[s], H, mis, lane);
+        }
+      }
+    }
+    tgt.finish(rank, t * (uint64_t)a.k, loc, lane);
   }
 }
 
@@ -362,20 +427,25 @@ int launch_moe_index(const MoeIndexArgs& a, void* stream) {
   return (int)hipGetLastError();
 }
 
-int launch_moe_pack(int elem_bytes, const MoeRowArgs& a, int max_grid, void* stream) {
-  const uint64_t rows = a.tokens * (uint64_t)a.k * (uint64_t)a.p;
+template <class Args>
+static int launch_token_copy(int elem_bytes, const Args& a, int max_grid, size_t shm, hipStream_t s) {
+  const uint64_t rows = a.tokens * (uint64_t)a.p;
   if (!rows) return 0;
-  const int grid = (int)(rows < (uint64_t)max_grid ? rows : (uint64_t)max_grid);
-  hipStream_t s = (hipStream_t)stream;
+  const uint64_t wgs = (rows + (kBlock / kWaveLanes) - 1) / (kBlock / kWaveLanes);
+  const int grid = (int)(wgs < (uint64_t)max_grid ? wgs : (uint64_t)max_grid);
   if (elem_bytes == 1)
-    hipLaunchKernelGGL((moe_pack_kernel<1>), dim3(grid), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((moe_token_copy_kernel<1, Args>), dim3(grid), dim3(kBlock), shm, s, a);
   else if (elem_bytes == 2)
-    hipLaunchKernelGGL((moe_pack_kernel<2>), dim3(grid), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((moe_token_copy_kernel<2, Args>), dim3(grid), dim3(kBlock), shm, s, a);
   else if (elem_bytes == 4)
-    hipLaunchKernelGGL((moe_pack_kernel<4>), dim3(grid), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((moe_token_copy_kernel<4, Args>), dim3(grid), dim3(kBlock), shm, s, a);
   else
     return (int)hipErrorInvalidValue;
   return (int)hipGetLastError();
+}
+
+int launch_moe_pack(int elem_bytes, const MoeRowArgs& a, int max_grid, void* stream) {
+  return launch_token_copy(elem_bytes, a, max_grid, 0, (hipStream_t)stream);
 }
 
 int launch_moe_combine(int dtype, const MoeRowArgs& a, int max_grid, void* stream) {
@@ -407,20 +477,7 @@ int launch_moe_combine_direct(int dtype, const MoeRowArgs& a, int max_grid, void
 }
 
 int launch_moe_dispatch(int elem_bytes, const MoeDirectArgs& a, int max_grid, void* stream) {
-  const uint64_t rows = a.tokens * (uint64_t)a.k * (uint64_t)a.p;
-  if (!rows) return 0;
-  const int grid = (int)(rows < (uint64_t)max_grid ? rows : (uint64_t)max_grid);
-  const size_t shm = direct_tables_bytes(a.p);
-  hipStream_t s = (hipStream_t)stream;
-  if (elem_bytes == 1)
-    hipLaunchKernelGGL((moe_dispatch_kernel<1>), dim3(grid), dim3(kBlock), shm, s, a);
-  else if (elem_bytes == 2)
-    hipLaunchKernelGGL((moe_dispatch_kernel<2>), dim3(grid), dim3(kBlock), shm, s, a);
-  else if (elem_bytes == 4)
-    hipLaunchKernelGGL((moe_dispatch_kernel<4>), dim3(grid), dim3(kBlock), shm, s, a);
-  else
-    return (int)hipErrorInvalidValue;
-  return (int)hipGetLastError();
+  return launch_token_copy(elem_bytes, a, max_grid, direct_tables_bytes(a.p), (hipStream_t)stream);
 }
 
 }  // namespace coll

@@ -285,3 +285,54 @@ def test_moe_fp8_round_trip_full_size(env):
             expect = ref.moe_combine(back_t, np.arange(k), weights[i][t * k:(t + 1) * k], k, H, BF16,
                                      residual[i][t * H:(t + 1) * H])
             assert_bits_equal(ot[t], expect, f"combined token rank {i} token {t}")
+
+
+def test_moe_direct_full_size(env):
+    """Direct dispatch and in-place combine at p=8, 4096 tokens x 7168 bf16
+    per rank, top-2: counts and every location whole; received rows,
+    combined tokens on a seeded sample (expert = identity, so the combine
+    reads the received rows)."""
+    torch, coll = env
+    p, T, H, k = 8, 4096, 7168, 2
+    A = T * k
+    toks = inputs.rank_buffers(inputs.WL_MOE_A2A, p, T * H, inputs.BF16, dist="normal")
+    routes = inputs.moe_routes(p, T, k)
+    weights = inputs.moe_weights(p, T, k)
+    rows = np.zeros(p, dtype=np.int64)
+    for r in routes:
+        rows += np.bincount(r, minlength=p)
+    recv = [torch.empty(int(r) * H, dtype=torch.bfloat16, device="cuda") for r in rows]
+    loc = [torch.empty(A, dtype=torch.int64, device="cuda") for _ in range(p)]
+    counts = torch.empty(p * p, dtype=torch.int64, device="cuda")
+    status = torch.full((p + 1,), -1, dtype=torch.int32, device="cuda")
+    coll.coll_moe_dispatch([dev(torch, x) for x in toks], [dev(torch, r) for r in routes], recv, loc, counts, k, H,
+                           status_dev=status)
+    residual = inputs.rank_buffers(inputs.WL_MOE_A2A, p, T * H, inputs.BF16, dist="normal", extra=(11,))
+    out = [dev(torch, r) for r in residual]
+    coll.coll_moe_combine_direct(recv, loc, [dev(torch, w) for w in weights], out, k, H, residual=out)
+    torch.cuda.synchronize()
+    assert status.cpu().tolist() == [0] * (p + 1)
+    C = counts.cpu().numpy().reshape(p, p)
+    exp_rows = np.stack([np.bincount(r, minlength=p) for r in routes])
+    assert np.array_equal(C, exp_rows * H)
+    roff = np.concatenate([np.zeros((1, p), np.int64), np.cumsum(exp_rows, axis=0)[:-1]])
+    rng = np.random.default_rng(23)
+    for i in range(p):
+        got = loc[i].cpu().numpy()
+        d = routes[i].astype(np.int64)
+        # row of assignment a in recv[d]: sources before i, then i's earlier assignments to d
+        nth = np.zeros(A, dtype=np.int64)
+        seen = np.zeros(p, dtype=np.int64)
+        for a in range(A):
+            nth[a] = seen[d[a]]
+            seen[d[a]] += 1
+        assert np.array_equal(got, (d << 32) | (roff[i, d] + nth)), f"locations rank {i}"
+        ot = to_host(out[i], BF16).reshape(T, H)
+        for t in rng.choice(T, 24, replace=False).tolist() + [0, T - 1]:
+            for s in range(k):
+                a = t * k + s
+                row = recv[d[a]][int(got[a] & 0xffffffff) * H:(int(got[a] & 0xffffffff) + 1) * H]
+                assert_bits_equal(to_host(row, BF16), toks[i][(a // k) * H:(a // k + 1) * H], f"row rank {i} a {a}")
+            expect = ref.moe_combine(np.concatenate([toks[i][t * H:(t + 1) * H]] * k), np.arange(k),
+                                     weights[i][t * k:(t + 1) * k], k, H, BF16, residual[i][t * H:(t + 1) * H])
+            assert_bits_equal(ot[t], expect, f"combined token rank {i} token {t}")
