@@ -306,7 +306,8 @@ constexpr int kCombBatch = 4;
 // DIRECT: pos[rank] is an int64 location array from the direct dispatch;
 // slot s reads row (loc & 0xffffffff) of src[loc >> 32] (skipped when the
 // location is -1 or outside the rank count or the row capacity cap[j]).
-template <int DT, bool DIRECT>
+// K: slots held in registers, the smallest power of two >= k.
+template <int DT, bool DIRECT, int K>
 COLL_STREAM_KERNEL void moe_combine_kernel(MoeRowArgs a) {
 #pragma clang fp contract(off)
   using T = Traits<DT>;
@@ -321,13 +322,13 @@ COLL_STREAM_KERNEL void moe_combine_kernel(MoeRowArgs a) {
   for (uint64_t r = wave_id(); r < rows; r += wave_count()) {
     const int rank = (int)(r / a.tokens);
     const uint64_t t = r - (uint64_t)rank * a.tokens;
-    const S* yrow[kMaxTopK];
-    float wt[kMaxTopK];
-    bool ok[kMaxTopK];
+    const S* yrow[K];
+    float wt[K];
+    bool ok[K];
     int mis = a.dst_mis < 0 ? -1 : (int)((a.dst_mis + t * H * T::B) & 15);
     if (a.has_residual) mis = seg_mis(mis, a.res_mis, 0, t * H * T::B);
 #pragma unroll
-    for (int s = 0; s < kMaxTopK; ++s) {
+    for (int s = 0; s < K; ++s) {
       ok[s] = false;
       wt[s] = 0.0f;
       yrow[s] = nullptr;
@@ -359,7 +360,7 @@ COLL_STREAM_KERNEL void moe_combine_kernel(MoeRowArgs a) {
       for (uint64_t e = from + lane; e < from + cnt; e += kWaveLanes) {
         A acc = res ? widen1<DT>(ld1<true>(res + e)) : A(0.0f);
 #pragma unroll
-        for (int s = 0; s < kMaxTopK; ++s)
+        for (int s = 0; s < K; ++s)
           if (ok[s]) {
             const A prod = wt[s] * widen1<DT>(ld1<true>(yrow[s] + e));
             acc = acc + prod;
@@ -375,7 +376,7 @@ COLL_STREAM_KERNEL void moe_combine_kernel(MoeRowArgs a) {
     for (uint64_t j0 = 0; j0 < sp.nvec; j0 += (uint64_t)kCombBatch * kWaveLanes) {
       // every load of the batch (residual and all slots) before any arithmetic
       u32x4 rr[kCombBatch];
-      u32x4 y[kMaxTopK][kCombBatch];
+      u32x4 y[K][kCombBatch];
 #pragma unroll
       for (int u = 0; u < kCombBatch; ++u) {
         const uint64_t j = j0 + (uint64_t)u * kWaveLanes + lane;
@@ -383,7 +384,7 @@ COLL_STREAM_KERNEL void moe_combine_kernel(MoeRowArgs a) {
         if (res && j < sp.nvec) rr[u] = ld16<true>(res + sp.head + j * V);
       }
 #pragma unroll
-      for (int s = 0; s < kMaxTopK; ++s)
+      for (int s = 0; s < K; ++s)
 #pragma unroll
         for (int u = 0; u < kCombBatch; ++u) {
           const uint64_t j = j0 + (uint64_t)u * kWaveLanes + lane;
@@ -400,7 +401,7 @@ COLL_STREAM_KERNEL void moe_combine_kernel(MoeRowArgs a) {
           for (int x = 0; x < V; ++x) acc[x] = 0.0f;
         }
 #pragma unroll
-        for (int s = 0; s < kMaxTopK; ++s) {
+        for (int s = 0; s < K; ++s) {
           if (!ok[s]) continue;
           A v[V];
           widen<DT>(y[s][u], v);
@@ -448,32 +449,31 @@ int launch_moe_pack(int elem_bytes, const MoeRowArgs& a, int max_grid, void* str
   return launch_token_copy(elem_bytes, a, max_grid, 0, (hipStream_t)stream);
 }
 
-int launch_moe_combine(int dtype, const MoeRowArgs& a, int max_grid, void* stream) {
+template <int DT, bool DIRECT>
+static void launch_combine_k(const MoeRowArgs& a, int grid, hipStream_t s) {
+  if (a.k <= 1) hipLaunchKernelGGL((moe_combine_kernel<DT, DIRECT, 1>), dim3(grid), dim3(kBlock), 0, s, a);
+  else if (a.k <= 2) hipLaunchKernelGGL((moe_combine_kernel<DT, DIRECT, 2>), dim3(grid), dim3(kBlock), 0, s, a);
+  else if (a.k <= 4) hipLaunchKernelGGL((moe_combine_kernel<DT, DIRECT, 4>), dim3(grid), dim3(kBlock), 0, s, a);
+  else hipLaunchKernelGGL((moe_combine_kernel<DT, DIRECT, kMaxTopK>), dim3(grid), dim3(kBlock), 0, s, a);
+}
+
+template <bool DIRECT>
+static int launch_combine(int dtype, const MoeRowArgs& a, int max_grid, hipStream_t s) {
   const uint64_t rows = a.tokens * (uint64_t)a.p;
   if (!rows) return 0;
   const int grid = (int)(rows < (uint64_t)max_grid ? rows : (uint64_t)max_grid);
-  hipStream_t s = (hipStream_t)stream;
-  if (dtype == kF32)
-    hipLaunchKernelGGL((moe_combine_kernel<kF32, false>), dim3(grid), dim3(kBlock), 0, s, a);
-  else if (dtype == kBF16)
-    hipLaunchKernelGGL((moe_combine_kernel<kBF16, false>), dim3(grid), dim3(kBlock), 0, s, a);
-  else
-    return (int)hipErrorInvalidValue;
+  if (dtype == kF32) launch_combine_k<kF32, DIRECT>(a, grid, s);
+  else if (dtype == kBF16) launch_combine_k<kBF16, DIRECT>(a, grid, s);
+  else return (int)hipErrorInvalidValue;
   return (int)hipGetLastError();
 }
 
+int launch_moe_combine(int dtype, const MoeRowArgs& a, int max_grid, void* stream) {
+  return launch_combine<false>(dtype, a, max_grid, (hipStream_t)stream);
+}
+
 int launch_moe_combine_direct(int dtype, const MoeRowArgs& a, int max_grid, void* stream) {
-  const uint64_t rows = a.tokens * (uint64_t)a.p;
-  if (!rows) return 0;
-  const int grid = (int)(rows < (uint64_t)max_grid ? rows : (uint64_t)max_grid);
-  hipStream_t s = (hipStream_t)stream;
-  if (dtype == kF32)
-    hipLaunchKernelGGL((moe_combine_kernel<kF32, true>), dim3(grid), dim3(kBlock), 0, s, a);
-  else if (dtype == kBF16)
-    hipLaunchKernelGGL((moe_combine_kernel<kBF16, true>), dim3(grid), dim3(kBlock), 0, s, a);
-  else
-    return (int)hipErrorInvalidValue;
-  return (int)hipGetLastError();
+  return launch_combine<true>(dtype, a, max_grid, (hipStream_t)stream);
 }
 
 int launch_moe_dispatch(int elem_bytes, const MoeDirectArgs& a, int max_grid, void* stream) {
