@@ -514,6 +514,62 @@ def halving_doubling_simulated(xs: list[np.ndarray], op: int, dtype: int) -> lis
     return [_finish(b, op, dtype, p) for b in buf]
 
 
+# ----------------------------------------------------------------------------
+# Tree AllReduce and the double binary tree (hpc/04 page, sections 2.3 and
+# 2.4; the "Collective Communication" page's Tree AllReduce: reduce up the
+# tree to the root, then broadcast down)
+# ----------------------------------------------------------------------------
+
+def tree_reduce_to_root(vals: list[np.ndarray], ranks: list[int], op: int, dtype: int):
+    """Binary tree in heap order over the listed ranks: node v (rank
+    ranks[v]) has children 2v+1 and 2v+2.  Each node waits for its
+    children's partials and sends partial(v) = (x_v (+) partial(2v+1))
+    (+) partial(2v+2) to its parent (reading: own value first, then the
+    left subtree, then the right).  Returns the root's partial, widened."""
+    p = len(ranks)
+    partial = [None] * p
+    for v in range(p - 1, -1, -1):          # leaves first: every child is done before its parent
+        acc = _widen(vals[ranks[v]], dtype).copy()
+        for c in (2 * v + 1, 2 * v + 2):
+            if c < p:
+                acc = _combine(acc, partial[c], op)
+        partial[v] = acc
+    return partial[0]
+
+
+def tree_allreduce_simulated(xs: list[np.ndarray], op: int, dtype: int) -> list[np.ndarray]:
+    """Tree AllReduce: reduce up the heap-ordered binary tree rooted at rank
+    0, then broadcast the root's result down the same tree."""
+    p = len(xs)
+    root = _finish(tree_reduce_to_root(xs, list(range(p)), op, dtype), op, dtype, p)
+    return [root.copy() for _ in range(p)]
+
+
+def double_binary_tree_simulated(xs: list[np.ndarray], op: int, dtype: int) -> list[np.ndarray]:
+    """Double binary tree (section 2.4): two complementary trees, tree A the
+    heap order over ranks 0, 1, ..., p-1 and tree B its mirror (node v on
+    rank p-1-v), so every rank is inner in one tree and a leaf in the
+    other.  Reading of how the data is split between them: the AllReduce
+    chunks c < p/2 (chunk c = elements [c*q, (c+1)*q), q = ceil(n/p)) go
+    through tree A, the others through tree B; each tree reduces its chunks
+    to its root and broadcasts them back."""
+    p = len(xs)
+    n = len(xs[0])
+    if n == 0:
+        return [xs[0][:0].copy() for _ in range(p)]
+    q = chunk_len(n, p)
+    out_parts = []
+    for c in range(p):
+        lo, hi = min(n, c * q), min(n, (c + 1) * q)
+        if lo == hi:
+            continue
+        ranks = list(range(p)) if c < p // 2 else list(range(p - 1, -1, -1))
+        part = tree_reduce_to_root([x[lo:hi] for x in xs], ranks, op, dtype)
+        out_parts.append(_finish(part, op, dtype, p))
+    res = np.concatenate(out_parts)
+    return [res.copy() for _ in range(p)]
+
+
 def fold_tree(vals: list[np.ndarray], op: int, dtype: int, first_stride: str) -> np.ndarray:
     """Balanced pairwise tree over ranks 0..p-1 (p a power of two).
 

@@ -854,3 +854,94 @@ def test_direct_fp8_dispatch_equals_pack_then_exchange():
     via = ref.alltoallv([pk[2] for pk in packs], C)
     for j in range(p):
         assert np.array_equal(recv[j], via[j])
+
+
+# ----------------------------------------------------------------------------
+# Tree AllReduce and the double binary tree
+# ----------------------------------------------------------------------------
+
+def _py_heap_tree(vals_by_rank, ranks, dtype):
+    """The heap-ordered tree fold written out with struct-rounded Python
+    floats: partial(v) = (x_v + partial(2v+1)) + partial(2v+2)."""
+    def part(v):
+        acc = vals_by_rank[ranks[v]]
+        for c in (2 * v + 1, 2 * v + 2):
+            if c < len(ranks):
+                acc = _py_add_f32(acc, part(c))
+        return acc
+    r = part(0)
+    return _py_bf16_rne(r) if dtype == ref.BF16 else _f32(r)
+
+
+@pytest.mark.parametrize("dtype", [ref.F32, ref.BF16])
+@pytest.mark.parametrize("p", [2, 3, 4, 7, 8, 16])
+def test_tree_allreduce_against_pure_python(dtype, p):
+    rng = np.random.default_rng(80 + p)
+    n = 2 * p + 3
+    xs = [_as_dtype((rng.standard_normal(n) * 1e3).astype(np.float64), dtype) for _ in range(p)]
+    got = ref.tree_allreduce_simulated(xs, ref.SUM, dtype)
+    dbt = ref.double_binary_tree_simulated(xs, ref.SUM, dtype)
+    q = ref.chunk_len(n, p)
+    for i in range(n):
+        vals = [float(_to_float([x[i]], dtype)[0]) for x in xs]
+        a = _py_heap_tree(vals, list(range(p)), dtype)
+        b = _py_heap_tree(vals, list(range(p - 1, -1, -1)), dtype) if i // q >= p // 2 else a
+        for r in range(p):
+            assert float(_to_float([got[r][i]], dtype)[0]) == a
+            assert float(_to_float([dbt[r][i]], dtype)[0]) == b
+
+
+def test_tree_orders_written_out_at_p4():
+    """p = 4, heap order: partial(1) = x1 + x3, partial(0) = (x0 + partial(1)) + x2;
+    the mirror (tree B) gives (x3 + (x2 + x0)) + x1."""
+    big, one = np.float32(2.0 ** 24), np.float32(1.0)
+    xs = [np.array([v], dtype=np.float32) for v in (big, one, -big, one)]
+    # tree A: x1 + x3 = 2 exactly; big + 2 = big + 2; + (-big) = 2
+    assert ref.tree_allreduce_simulated(xs, ref.SUM, ref.F32)[0][0] == np.float32(2.0)
+    # a case that separates the two trees:
+    zs = [np.array([v], dtype=np.float32) for v in (big, one, one, -big)]
+    a = ref.tree_reduce_to_root(zs, [0, 1, 2, 3], ref.SUM, ref.F32)
+    b = ref.tree_reduce_to_root(zs, [3, 2, 1, 0], ref.SUM, ref.F32)
+    # tree A: x1 + x3 = 1 - big = -(big - 1) exact; x0 + that = 1; + x2 = 2
+    assert a[0] == np.float32(2.0)
+    # tree B: x2 + x0 = 1 + big -> big (round to even); x3 + big = 0; + x1 = 1
+    assert b[0] == np.float32(1.0)
+
+
+@pytest.mark.parametrize("op", [ref.SUM, ref.MIN, ref.MAX, ref.AVG])
+def test_tree_orders_exact_on_integers(op):
+    rng = np.random.default_rng(90)
+    p, n = 8, 50
+    xs = [rng.integers(-100, 100, n).astype(np.int32) for _ in range(p)]
+    expect = ref.allreduce(xs, op, ref.I32)
+    for sim in (ref.tree_allreduce_simulated, ref.double_binary_tree_simulated):
+        got = sim(xs, op, ref.I32)
+        for r in range(p):
+            assert np.array_equal(got[r], expect[r])
+
+
+def test_tree_orders_differ_from_the_others_on_floats():
+    rng = np.random.default_rng(91)
+    p, n = 8, 4096
+    xs = [(rng.standard_normal(n) * np.exp(rng.uniform(-8, 8, n))).astype(np.float32) for _ in range(p)]
+    results = [ref.allreduce(xs, ref.SUM, ref.F32)[0], ref.recursive_doubling_simulated(xs, ref.SUM, ref.F32)[0],
+               ref.halving_doubling_simulated(xs, ref.SUM, ref.F32)[0],
+               ref.tree_allreduce_simulated(xs, ref.SUM, ref.F32)[0],
+               ref.double_binary_tree_simulated(xs, ref.SUM, ref.F32)[0]]
+    for i in range(len(results)):
+        for j in range(i + 1, len(results)):
+            assert not np.array_equal(results[i], results[j]), (i, j)
+
+
+def test_tree_shapes_match_the_figure(monkeypatch):
+    """The hpc/04 page's double-binary-tree figure (section 2.4): tree A has
+    0 -> (1, 2), 1 -> (3, 4), 2 -> (5, 6); tree B has 7 -> (6, 5),
+    6 -> (4, 3), 5 -> (2, 1).  Symbolic operands record every combine;
+    at p = 8 the heap order adds 3 -> 7 (tree A) and 4 -> 0 (tree B)."""
+    monkeypatch.setattr(ref, "_widen", lambda v, dtype: np.asarray(v, dtype=object))
+    monkeypatch.setattr(ref, "_combine", lambda a, b, op: np.array([f"({x}+{y})" for x, y in zip(a, b)], dtype=object))
+    xs = [np.array([f"x{r}"], dtype=object) for r in range(8)]
+    a = ref.tree_reduce_to_root(xs, list(range(8)), ref.SUM, ref.F32)[0]
+    b = ref.tree_reduce_to_root(xs, list(range(7, -1, -1)), ref.SUM, ref.F32)[0]
+    assert a == "((x0+((x1+(x3+x7))+x4))+((x2+x5)+x6))"
+    assert b == "((x7+((x6+(x4+x0))+x3))+((x5+x2)+x1))"
