@@ -21,6 +21,7 @@ COLL_SUM, COLL_MIN, COLL_MAX, COLL_AVG = 0, 1, 2, 3
 COLL_OK, COLL_ERR_INVALID_ARG, COLL_ERR_UNSUPPORTED, COLL_ERR_ALIAS, COLL_ERR_HIP = 0, 1, 2, 3, 4
 COLL_ALGO_RING, COLL_ALGO_ONEPASS, COLL_ALGO_RING_LITERAL, COLL_ALGO_HALVING_DOUBLING = 0, 1, 2, 3
 COLL_ALGO_RECURSIVE_DOUBLING = COLL_ALGO_ONEPASS
+COLL_ALGO_TREE, COLL_ALGO_DOUBLE_BINARY_TREE = 4, 5
 COLL_MAX_RANKS = 64
 COLL_BATCH_CHECK_ALIAS = 1
 

@@ -166,6 +166,17 @@ coll::RankPtrs make_ptrs(const void* const* src, int ns, void* const* dst, int n
 
 coll_status_t finish(int err) { return err ? hip_fail(err) : COLL_OK; }
 
+// Summation order of an AllReduce schedule (RING_LITERAL has its own kernels).
+int order_of(coll_algo_t algo) {
+  switch (algo) {
+    case COLL_ALGO_RECURSIVE_DOUBLING: return coll::kOrdRD;
+    case COLL_ALGO_HALVING_DOUBLING: return coll::kOrdHD;
+    case COLL_ALGO_TREE: return coll::kOrdTree;
+    case COLL_ALGO_DOUBLE_BINARY_TREE: return coll::kOrdDBT;
+    default: return coll::kOrdRing;
+  }
+}
+
 // AllReduce validation shared by the single and the batched entry points.
 coll_status_t check_allreduce(const void* const* send, void* const* recv, int p, size_t n, int dtype,
                               int op) {
@@ -194,10 +205,10 @@ coll_status_t check_allreduce(const void* const* send, void* const* recv, int p,
 COLL_EXPORT coll_status_t coll_allreduce_algo(const void* const* send, void* const* recv, int p, size_t n,
                                               coll_dtype_t dtype, coll_op_t op, coll_algo_t algo,
                                               void* stream) {
-  if ((int)algo < COLL_ALGO_RING || (int)algo > COLL_ALGO_HALVING_DOUBLING) return COLL_ERR_INVALID_ARG;
+  if ((int)algo < COLL_ALGO_RING || (int)algo > COLL_ALGO_DOUBLE_BINARY_TREE) return COLL_ERR_INVALID_ARG;
   coll_status_t st = check_allreduce(send, recv, p, n, dtype, op);
   if (st != COLL_OK || n == 0) return st;
-  const bool tree_algo = algo == COLL_ALGO_RECURSIVE_DOUBLING || algo == COLL_ALGO_HALVING_DOUBLING;
+  const bool tree_algo = algo != COLL_ALGO_RING && algo != COLL_ALGO_RING_LITERAL;
   if (tree_algo && !(p == 2 || p == 4 || p == 8 || p == 16)) return COLL_ERR_UNSUPPORTED;
   if (algo == COLL_ALGO_RING_LITERAL && dtype == COLL_BF16) return COLL_ERR_UNSUPPORTED;
   int grid;
@@ -234,9 +245,7 @@ COLL_EXPORT coll_status_t coll_allreduce_algo(const void* const* send, void* con
   g.dst_mode = coll::kDstAll;
   g.src_mis = smis;
   g.dst_mis = dmis;
-  const int order = algo == COLL_ALGO_RECURSIVE_DOUBLING ? coll::kOrdRD
-                    : algo == COLL_ALGO_HALVING_DOUBLING  ? coll::kOrdHD
-                                                          : coll::kOrdRing;
+  const int order = order_of(algo);
   return finish(coll::launch_reduce(dtype, op, order, P, g, grid, stream));
 }
 
@@ -248,12 +257,12 @@ COLL_EXPORT coll_status_t coll_allreduce(const void* const* send, void* const* r
 COLL_EXPORT coll_status_t coll_allreduce_premul(const void* const* send, void* const* recv, int p, size_t n,
                                                 coll_dtype_t dtype, const float* scale, coll_algo_t algo,
                                                 void* stream) {
-  if ((int)algo < COLL_ALGO_RING || (int)algo > COLL_ALGO_HALVING_DOUBLING) return COLL_ERR_INVALID_ARG;
+  if ((int)algo < COLL_ALGO_RING || (int)algo > COLL_ALGO_DOUBLE_BINARY_TREE) return COLL_ERR_INVALID_ARG;
   coll_status_t st = check_allreduce(send, recv, p, n, dtype, COLL_SUM);
   if (st != COLL_OK || n == 0) return st;
   if (!scale) return COLL_ERR_INVALID_ARG;
   if (dtype == COLL_I32 || algo == COLL_ALGO_RING_LITERAL) return COLL_ERR_UNSUPPORTED;
-  const bool tree_algo = algo == COLL_ALGO_RECURSIVE_DOUBLING || algo == COLL_ALGO_HALVING_DOUBLING;
+  const bool tree_algo = algo != COLL_ALGO_RING && algo != COLL_ALGO_RING_LITERAL;
   if (tree_algo && !(p == 2 || p == 4 || p == 8 || p == 16)) return COLL_ERR_UNSUPPORTED;
   int grid;
   int e = max_grid(&grid, kFamReduce);
@@ -267,9 +276,7 @@ COLL_EXPORT coll_status_t coll_allreduce_premul(const void* const* send, void* c
   g.src_mis = common_mis(send, p);
   g.dst_mis = common_mis((const void* const*)recv, p);
   for (int r = 0; r < p; ++r) g.scale[r] = scale[r];
-  const int order = algo == COLL_ALGO_RECURSIVE_DOUBLING ? coll::kOrdRD
-                    : algo == COLL_ALGO_HALVING_DOUBLING  ? coll::kOrdHD
-                                                          : coll::kOrdRing;
+  const int order = order_of(algo);
   return finish(coll::launch_reduce(dtype, coll::kPreMul, order, P, g, grid, stream));
 }
 

@@ -17,7 +17,9 @@ enum DType : int { kF32 = 0, kBF16 = 1, kI32 = 2 };
 enum Order : int {
   kOrdRing = 0,  // left fold over the rotated ring order x_{c+1}, ..., x_c
   kOrdRD = 1,    // balanced tree pairing ranks (0,1), (2,3), ... first (recursive doubling)
-  kOrdHD = 2     // balanced tree pairing ranks (k, k + p/2) first (halving-doubling)
+  kOrdHD = 2,    // balanced tree pairing ranks (k, k + p/2) first (halving-doubling)
+  kOrdTree = 3,  // binary tree in heap order: node v = (x_v + subtree 2v+1) + subtree 2v+2
+  kOrdDBT = 4    // double binary tree: chunks c < p/2 on the heap tree, the others on its mirror
 };
 // Reductions.  kAvg: the sum, then divided by the rank count; kPreMul:
 // every operand times its rank's scale, then the sum.

@@ -18,6 +18,16 @@
 
 namespace coll {
 
+// Rank listed k-th for chunk c: the ring rotation x_{c+1}, ..., x_c, or
+// rank order for the trees (mirrored for the double binary tree's second
+// half of the chunks).
+template <int ORD, int P>
+__device__ __forceinline__ int listed_rank(int c, int k) {
+  if constexpr (ORD == kOrdRing) return (c + 1 + k) % P;
+  else if constexpr (ORD == kOrdDBT) return c < P / 2 ? k : P - 1 - k;
+  else return k;
+}
+
 __device__ __forceinline__ void chunk_range(const ReduceGeom& g, int c, uint64_t* lo, uint64_t* len) {
   uint64_t a = (uint64_t)c * g.stride;
   uint64_t b = a + g.stride;
@@ -41,7 +51,7 @@ COLL_STREAM_KERNEL void reduce_kernel(RankPtrs ptrs, ReduceGeom g) {
     const uint64_t doff = (DMODE == kDstOwner) ? 0 : lo;
     const S* src[P];
 #pragma unroll
-    for (int k = 0; k < P; ++k) src[k] = (const S*)ptrs.src[ORD != kOrdRing ? k : (c + 1 + k) % P] + lo;
+    for (int k = 0; k < P; ++k) src[k] = (const S*)ptrs.src[listed_rank<ORD, P>(c, k)] + lo;
     S* dst[ND];
     if constexpr (ALL) {
 #pragma unroll
@@ -53,7 +63,7 @@ COLL_STREAM_KERNEL void reduce_kernel(RankPtrs ptrs, ReduceGeom g) {
     }
     Scales<P> sc;
 #pragma unroll
-    for (int k = 0; k < P; ++k) sc.s[k] = OP == kPreMul ? g.scale[ORD != kOrdRing ? k : (c + 1 + k) % P] : 1.0f;
+    for (int k = 0; k < P; ++k) sc.s[k] = OP == kPreMul ? g.scale[listed_rank<ORD, P>(c, k)] : 1.0f;
     const int mis = seg_mis(g.src_mis, g.dst_mis, lo * T::B, doff * T::B);
     base += reduce_segment<DT, OP, P, ORD, ND, ALL>(src, dst, len, mis, base, sc, P);
   }
@@ -229,6 +239,8 @@ static int launch_dt_op(int order, const RankPtrs& ptrs, const ReduceGeom& g, in
   if constexpr ((DT == kF32 || DT == kBF16) && (OP == kSum || OP == kAvg || OP == kPreMul)) {
     if (order == kOrdRD) return launch_tree<DT, OP, kOrdRD>(ptrs, g, max_grid, s);
     if (order == kOrdHD) return launch_tree<DT, OP, kOrdHD>(ptrs, g, max_grid, s);
+    if (order == kOrdTree) return launch_tree<DT, OP, kOrdTree>(ptrs, g, max_grid, s);
+    if (order == kOrdDBT) return launch_tree<DT, OP, kOrdDBT>(ptrs, g, max_grid, s);
   }
   switch (g.p) {
     case 2: return launch_p<DT, OP, 2, kOrdRing>(ptrs, g, max_grid, s);

@@ -10,7 +10,11 @@
 // balanced pairwise tree: kOrdRD pairs neighbours first, as recursive
 // doubling does (section 2.3 there: exchange at distance 1, 2, 4, ...);
 // kOrdHD pairs ranks p/2 apart first, as the recursive-halving
-// reduce-scatter of halving-doubling does.
+// reduce-scatter of halving-doubling does.  kOrdTree and kOrdDBT fold the
+// listed operands as a binary tree in heap order (the tree all-reduce's
+// reduce to the root; section 2.4's double binary tree lists the ranks in
+// mirrored order for its second tree): operand v adds its left subtree
+// (2v+1) and then its right subtree (2v+2), leaves first.
 //
 // A lane handles U vectors of a tile.  It issues all P*U loads before the
 // first combine, source by source, so it keeps P*U 16-byte requests in
@@ -83,6 +87,17 @@ __device__ __forceinline__ u32x4 fold_vectors(const u32x4 (&r)[P], const Scales<
     for (int st = P / 2; st >= 1; st /= 2)
 #pragma unroll
       for (int k = 0; k < st; ++k) combine_vec<OP, DT>(a[k], a[k + st]);
+#pragma unroll
+    for (int x = 0; x < V; ++x) acc[x] = a[0][x];
+  } else if constexpr (ORD == kOrdTree || ORD == kOrdDBT) {
+    A a[P][V];
+#pragma unroll
+    for (int k = 0; k < P; ++k) operand<DT, OP, P>(r[k], sc, k, a[k]);
+#pragma unroll
+    for (int v = P - 1; v >= 0; --v) {
+      if (2 * v + 1 < P) combine_vec<OP, DT>(a[v], a[2 * v + 1]);
+      if (2 * v + 2 < P) combine_vec<OP, DT>(a[v], a[2 * v + 2]);
+    }
 #pragma unroll
     for (int x = 0; x < V; ++x) acc[x] = a[0][x];
   } else {
@@ -160,6 +175,13 @@ __device__ __forceinline__ void reduce_elems(const typename Traits<DT>::S* const
       for (int st = P / 2; st >= 1; st /= 2)
 #pragma unroll
         for (int k = 0; k < st; ++k) a[k] = combine<OP>(a[k], a[k + st]);
+      acc = a[0];
+    } else if constexpr (ORD == kOrdTree || ORD == kOrdDBT) {
+#pragma unroll
+      for (int v = P - 1; v >= 0; --v) {
+        if (2 * v + 1 < P) a[v] = combine<OP>(a[v], a[2 * v + 1]);
+        if (2 * v + 2 < P) a[v] = combine<OP>(a[v], a[2 * v + 2]);
+      }
       acc = a[0];
     } else {
       acc = a[0];

@@ -95,13 +95,23 @@ typedef enum {
  *   recursive-halving reduce-scatter pairing ranks at distance p/2, p/4,
  *   ..., 1 followed by a recursive-doubling all-gather:
  *   (x0 + x_{p/2}), (x1 + x_{p/2+1}), ... first.  p in {2,4,8,16}.
+ * TREE: the tree all-reduce ([B] Tree AllReduce: reduce up a binary tree
+ *   to the root, then broadcast down), the tree in heap order (rank v's
+ *   children 2v+1 and 2v+2): each node adds its own value, then its left
+ *   subtree, then its right.  p in {2,4,8,16}.
+ * DOUBLE_BINARY_TREE: [A] 2.4's two complementary trees, tree A as TREE
+ *   and tree B its mirror (node v on rank p-1-v); chunks c < p/2 of q =
+ *   ceil(n/p) elements are reduced on tree A, the others on tree B.
+ *   p in {2,4,8,16}.
  * Integer sums and min/max give the same bits under every schedule. */
 typedef enum {
   COLL_ALGO_RING = 0,
   COLL_ALGO_ONEPASS = 1,
   COLL_ALGO_RECURSIVE_DOUBLING = 1,
   COLL_ALGO_RING_LITERAL = 2,
-  COLL_ALGO_HALVING_DOUBLING = 3
+  COLL_ALGO_HALVING_DOUBLING = 3,
+  COLL_ALGO_TREE = 4,
+  COLL_ALGO_DOUBLE_BINARY_TREE = 5
 } coll_algo_t;
 
 #define COLL_MAX_RANKS 64
@@ -121,8 +131,7 @@ coll_status_t coll_allreduce_algo(const void* const* send, void* const* recv, in
 /* Pre-multiplied AllReduce ([B] numerics: NCCL's PreMulSum, the one
  * constrained custom reduction): recv[r][i] = sum_k scale[k] * send[k][i],
  * each operand multiplied by its rank's scale in fp32 and rounded on its
- * own, then summed in the order of `algo` (RING, RECURSIVE_DOUBLING or
- * HALVING_DOUBLING).  scale: HOST array of p floats.  fp32 and bf16 only
+ * own, then summed in the order of `algo` (any schedule but RING_LITERAL).  scale: HOST array of p floats.  fp32 and bf16 only
  * (COLL_ERR_UNSUPPORTED for int32 and RING_LITERAL).  In place as
  * coll_allreduce.  scale = 1/p for every rank is the average of DDP. */
 coll_status_t coll_allreduce_premul(const void* const* send, void* const* recv, int p, size_t n,

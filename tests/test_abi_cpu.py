@@ -93,6 +93,9 @@ def test_invalid_arguments_rejected():
     assert L.coll_allreduce_premul(s, r, 4, n, 0, one, 2, None) == coll.COLL_ERR_UNSUPPORTED  # literal ring
     assert L.coll_reduce_scatter_premul(s, r, 4, n, 2, one, None) == coll.COLL_ERR_UNSUPPORTED
     assert L.coll_allreduce_algo(s, r, 4, n, 0, 0, 7, None) == INV    # bad algo
+    assert L.coll_allreduce_algo(s, r, 4, n, 0, 0, 6, None) == INV
+    assert L.coll_allreduce_algo(s, r, 3, n, 0, 0, 4, None) == coll.COLL_ERR_UNSUPPORTED   # tree, p = 3
+    assert L.coll_allreduce_algo(s, r, 3, n, 0, 0, 5, None) == coll.COLL_ERR_UNSUPPORTED   # double tree, p = 3
     assert L.coll_allreduce(None, r, 4, n, 0, 0, None) == INV         # null array
     assert L.coll_allreduce(s, r, 4, 1 << 61, 0, 0, None) == INV      # size overflow
     z, _kz = _arr([base, 0, base + 0x200000, base + 0x300000])

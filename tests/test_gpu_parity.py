@@ -145,10 +145,13 @@ def test_allreduce_ring_literal_in_place(coll):
 @pytest.mark.parametrize("p", [2, 4, 8, 16])
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("algo,sim", [("RECURSIVE_DOUBLING", "recursive_doubling_simulated"),
-                                      ("HALVING_DOUBLING", "halving_doubling_simulated")])
+                                      ("HALVING_DOUBLING", "halving_doubling_simulated"),
+                                      ("TREE", "tree_allreduce_simulated"),
+                                      ("DOUBLE_BINARY_TREE", "double_binary_tree_simulated")])
 def test_allreduce_doubling_schedules_bitexact(coll, p, dtype, algo, sim):
     """The tree schedules against step-by-step simulations of recursive
-    doubling and halving-doubling, bit for bit, on every rank."""
+    doubling, halving-doubling, the tree all-reduce and the double binary
+    tree, bit for bit, on every rank."""
     n = p * 3000 + 11
     hx = gen(p, n, dtype, 6)
     send = [to_dev(x, dtype) for x in hx]
@@ -170,6 +173,14 @@ def test_doubling_schedules_misaligned_and_in_place(coll):
     expect = ref.halving_doubling_simulated(hx, ref.SUM, F32)
     for r in range(p):
         assert_bits_equal(to_host(send[r], F32), expect[r], f"HD in place misaligned r={r}")
+    # the double binary tree on bf16, misaligned by one element and in place
+    hb = gen(p, n, BF16, 61)
+    keep2, sendb = zip(*[upload_offset(x, BF16, 1) for x in hb])
+    coll.coll_allreduce_algo(list(sendb), list(sendb), coll.COLL_ALGO_DOUBLE_BINARY_TREE, coll.COLL_SUM)
+    sync()
+    expect = ref.double_binary_tree_simulated(hb, ref.SUM, BF16)
+    for r in range(p):
+        assert_bits_equal(to_host(sendb[r], BF16), expect[r], f"DBT in place misaligned r={r}")
 
 
 def test_onepass_unsupported_rank_count(coll):
@@ -191,7 +202,8 @@ def test_onepass_unsupported_rank_count(coll):
 # ----------------------------------------------------------------------------
 
 SCHEDULES = [("RING", None), ("RECURSIVE_DOUBLING", "recursive_doubling_simulated"),
-             ("HALVING_DOUBLING", "halving_doubling_simulated"), ("RING_LITERAL", "ring_allreduce_simulated")]
+             ("HALVING_DOUBLING", "halving_doubling_simulated"), ("TREE", "tree_allreduce_simulated"),
+             ("DOUBLE_BINARY_TREE", "double_binary_tree_simulated"), ("RING_LITERAL", "ring_allreduce_simulated")]
 
 
 @pytest.mark.parametrize("p,n", [(1, 50), (2, 4097), (3, 1001), (5, 777), (8, 8 * 1024 + 17), (16, 16 * 257), (33, 999)])
@@ -201,7 +213,7 @@ def test_allreduce_avg_every_schedule(coll, p, n, dtype):
     send = [to_dev(x, dtype) for x in hx]
     pow2 = p in (2, 4, 8, 16)
     for algo, sim in SCHEDULES:
-        if algo in ("RECURSIVE_DOUBLING", "HALVING_DOUBLING") and not pow2:
+        if algo not in ("RING", "RING_LITERAL") and not pow2:
             continue
         if algo == "RING_LITERAL" and dtype == BF16:
             continue
@@ -243,7 +255,7 @@ def test_allreduce_premul_every_schedule(coll, p, dtype):
     send = [to_dev(x, dtype) for x in hx]
     rng = np.random.default_rng(p)
     scales = (rng.random(p) * 2 - 0.5).astype(np.float32)
-    for algo, sim in SCHEDULES[:3]:
+    for algo, sim in SCHEDULES[:5]:
         if algo != "RING" and p not in (2, 4, 8, 16):
             continue
         recv = [empty(n, dtype, fill=0) for _ in range(p)]
