@@ -58,8 +58,8 @@ def parse_args(argv=None):
     ap.add_argument("--no-collectives", action="store_true", help="time only the main step")
     ap.add_argument("--only", default=None,
                     help="comma list of extra collectives to time (ar_ring, ar_onepass, ar_hd, "
-                         "ar_literal, ar_avg, ar_premul, a2a, a2av, moe, moe_fp8, moe_direct, moe_fp8_direct, gs, ar_small, "
-                         "batch, copy, ce)")
+                         "ar_tree, ar_dbt, ar_literal, ar_avg, ar_premul, a2a, a2av, moe, moe_fp8, moe_direct, moe_fp8_direct, "
+                         "gs, ar_small, ar_latency, batch, copy, ce)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
     return ap.parse_args(argv)
 
@@ -241,12 +241,37 @@ def cpu_baseline(wl, cpu_seconds: float):
     }
 
 
+def graph_us_per_call(torch, coll, send, recv, algo, calls=10, replays=20):
+    """Device time per AllReduce call without host overhead: `calls` calls
+    captured back to back in one HIP graph, replayed `replays` times."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):          # warm-up off the capture
+        coll.coll_allreduce_algo(send, recv, algo, coll.COLL_SUM)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            coll.coll_allreduce_algo(send, recv, algo, coll.COLL_SUM)
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(replays):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / (calls * replays)
+
+
 def extra_collectives(torch, coll, inputs, metrics, dev, which, iters=10, warmup=3):
     rows = []
     want = lambda k: which is None or k in which  # noqa: E731
 
     # --- DP gradient AllReduce, p = 8, 256 MiB fp32 per rank ~ N(0, 1) -------
-    if any(want(k) for k in ("ar_ring", "ar_onepass", "ar_hd", "ar_literal", "ar_avg", "ar_premul")):
+    if any(want(k) for k in ("ar_ring", "ar_onepass", "ar_hd", "ar_tree", "ar_dbt", "ar_literal", "ar_avg",
+                             "ar_premul")):
         p, n = 8, 1 << 26
         send = [to_dev(torch, x, dev) for x in inputs.rank_buffers(inputs.WL_DP_RING_AR, p, n, inputs.F32,
                                                                     dist="normal")]
@@ -255,6 +280,8 @@ def extra_collectives(torch, coll, inputs, metrics, dev, which, iters=10, warmup
                 ("ar_ring", coll.COLL_ALGO_RING, "allreduce_ring_fused", "ring"),
                 ("ar_onepass", coll.COLL_ALGO_RECURSIVE_DOUBLING, "allreduce_recursive_doubling_order", "ring"),
                 ("ar_hd", coll.COLL_ALGO_HALVING_DOUBLING, "allreduce_halving_doubling_order", "ring"),
+                ("ar_tree", coll.COLL_ALGO_TREE, "allreduce_tree_order", "ring"),
+                ("ar_dbt", coll.COLL_ALGO_DOUBLE_BINARY_TREE, "allreduce_double_binary_tree_order", "ring"),
                 ("ar_literal", coll.COLL_ALGO_RING_LITERAL, "allreduce_ring_literal_14_steps",
                  "ring_literal")):
             if not want(key):
@@ -366,6 +393,32 @@ def extra_collectives(torch, coll, inputs, metrics, dev, which, iters=10, warmup
             rows.append(coll_entry(metrics, f"allreduce_small_{oname}", "allreduce", p, n, 4, med, "ring",
                                    {"dtype": dname, "op": oname, "t_p95_us": round(p95, 2),
                                     "workload": "AllReduce p=4, 2^20 per rank, back to back (warm)"}))
+
+    # --- latency of every schedule at the batch's small sizes, p = 16 ---------
+    # The alpha-beta view of the schedules (hpc/04 page, sections 2.1 and
+    # 2.6): on one device every single-pass schedule is one launch whatever
+    # its hop count; the literal ring pays 2(p-1) launches.
+    if want("ar_latency"):
+        p = 16
+        table = []
+        for nbytes in (4096, 65536, 1 << 20):
+            n = nbytes // 4
+            send = [to_dev(torch, x, dev) for x in inputs.rank_buffers(inputs.WL_AR_SMALL, p, n, inputs.F32,
+                                                                        extra=(nbytes,))]
+            recv = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(p)]
+            entry = {"bytes_per_rank": nbytes}
+            for key, algo in (("ring", coll.COLL_ALGO_RING), ("recursive_doubling", coll.COLL_ALGO_RECURSIVE_DOUBLING),
+                              ("halving_doubling", coll.COLL_ALGO_HALVING_DOUBLING), ("tree", coll.COLL_ALGO_TREE),
+                              ("double_binary_tree", coll.COLL_ALGO_DOUBLE_BINARY_TREE),
+                              ("ring_literal", coll.COLL_ALGO_RING_LITERAL)):
+                f = coll.coll_allreduce_algo(send, recv, algo, coll.COLL_SUM, defer=True)
+                med, _, _ = stats_us(time_launches(torch, [f], 50, 10)[0])
+                entry[key + "_us"] = round(med, 2)
+                entry[key + "_graph_us"] = round(graph_us_per_call(torch, coll, send, recv, algo), 2)
+            table.append(entry)
+            del send, recv
+        rows.append({"name": "allreduce_schedule_latency", "p": p, "dtype": "f32", "op": "sum", "table": table,
+                     "workload": "AllReduce p=16, 4 KiB / 64 KiB / 1 MiB per rank, each schedule, back to back"})
 
     # --- 10,000 small AllReduces in one launch, p = 16 -----------------------
     if want("batch"):

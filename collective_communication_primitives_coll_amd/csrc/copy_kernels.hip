@@ -31,9 +31,14 @@ COLL_STREAM_KERNEL void fanout_kernel(RankPtrs ptrs, CopyGeom g) {
   const int nseg = KIND == kCopyAllGather ? p : 1;
   uint64_t base = 0;
   for (int s = 0; s < nseg; ++s) {
-    const W* src = (const W*)ptrs.src[s];
     const uint64_t dst_off = KIND == kCopyAllGather ? (uint64_t)s * g.n : 0;
     const int mis = seg_mis(g.src_mis, g.dst_mis, 0, dst_off * B);
+    uint64_t nt;
+    if (!copy_segment_owned<B>(g.n, mis, base, &nt)) {
+      base += nt;
+      continue;
+    }
+    const W* src = (const W*)ptrs.src[s];
     if constexpr (P > 0) {
       W* dst[P];
 #pragma unroll
@@ -79,6 +84,11 @@ COLL_STREAM_KERNEL void pair_copy_kernel(RankPtrs ptrs, CopyGeom g) {
       dst = (W*)ptrs.dst[sgi];
     }
     const int mis = seg_mis(g.src_mis, g.dst_mis, src_off * B, dst_off * B);
+    uint64_t nt;
+    if (!copy_segment_owned<B>(g.n, mis, base, &nt)) {
+      base += nt;
+      continue;
+    }
     auto gdst = [&](int) -> W* { return dst; };
     base += copy_segment<B, true, 1>(src, gdst, 1, g.n, mis, base);
   }

@@ -57,6 +57,18 @@ __device__ __forceinline__ void copy_vec_tile(const u32x4* src, const GD& gdst, 
 // if it owns the segment, the element-wise head and tail.  gdst(d) gives
 // destination d's element pointer at the segment start.  Returns the
 // segment's tile count.
+// Tiles of a copy segment as copy_segment counts them, and whether this
+// workgroup works any of them or the head and tail (see copy_segment);
+// lets a workgroup skip a segment's pointer setup.
+template <int B>
+__device__ __forceinline__ bool copy_segment_owned(uint64_t len, int mis, uint64_t base, uint64_t* nt_out) {
+  const SegSpan sp = seg_span<B>(len, mis);
+  const uint64_t nt = sp.vec ? ceil_div(sp.nvec, kCopyTV) : ceil_div(len, (uint64_t)kBlock * 4);
+  *nt_out = nt;
+  const uint64_t ft = first_tile32(base, blockIdx.x, gridDim.x);
+  return ft < nt || (ft == 0 && (sp.head || sp.tail));
+}
+
 template <int B, bool NTL, int ND, typename GD>
 __device__ __forceinline__ uint64_t copy_segment(const typename Word<B>::T* src, const GD& gdst, int nd,
                                                  uint64_t len, int mis, uint64_t base) {

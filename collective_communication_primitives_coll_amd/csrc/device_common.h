@@ -206,4 +206,15 @@ __device__ __forceinline__ uint64_t first_tile(uint64_t base, uint64_t wg, uint6
   return (wg + grid - r) % grid;
 }
 
+// The same with one 32-bit remainder, for the per-segment ownership
+// checks that every workgroup makes for every segment: tile counts of a
+// call stay below 2^32 (a tile covers at least 1 KiB and a call at most
+// the device's memory), and 64-bit division is a long software sequence.
+// (The tile loops keep the 64-bit form: their code measured faster so.)
+__device__ __forceinline__ uint32_t first_tile32(uint64_t base, uint32_t wg, uint32_t grid) {
+  const uint32_t r = (uint32_t)base % grid;
+  const uint32_t t = wg + grid - r;
+  return t >= grid ? t - grid : t;
+}
+
 }  // namespace coll

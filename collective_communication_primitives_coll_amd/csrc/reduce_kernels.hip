@@ -49,6 +49,12 @@ COLL_STREAM_KERNEL void reduce_kernel(RankPtrs ptrs, ReduceGeom g) {
     chunk_range(g, c, &lo, &len);
     if (len == 0) continue;
     const uint64_t doff = (DMODE == kDstOwner) ? 0 : lo;
+    const int mis = seg_mis(g.src_mis, g.dst_mis, lo * T::B, doff * T::B);
+    uint64_t nt;
+    if (!segment_owned<DT, P, ND>(len, mis, base, &nt)) {
+      base += nt;
+      continue;
+    }
     const S* src[P];
 #pragma unroll
     for (int k = 0; k < P; ++k) src[k] = (const S*)ptrs.src[listed_rank<ORD, P>(c, k)] + lo;
@@ -64,7 +70,6 @@ COLL_STREAM_KERNEL void reduce_kernel(RankPtrs ptrs, ReduceGeom g) {
     Scales<P> sc;
 #pragma unroll
     for (int k = 0; k < P; ++k) sc.s[k] = OP == kPreMul ? g.scale[listed_rank<ORD, P>(c, k)] : 1.0f;
-    const int mis = seg_mis(g.src_mis, g.dst_mis, lo * T::B, doff * T::B);
     base += reduce_segment<DT, OP, P, ORD, ND, ALL>(src, dst, len, mis, base, sc, P);
   }
 }

@@ -194,6 +194,22 @@ __device__ __forceinline__ void reduce_elems(const typename Traits<DT>::S* const
   }
 }
 
+// Tiles of a segment as reduce_segment counts them, and whether workgroup
+// wg (of grid) works any of them, or the head and tail, when the segment's
+// flat tile indices start at base.  Lets a workgroup skip a segment's
+// pointer setup when it has nothing to do there (small calls, where the
+// setup would dominate).
+template <int DT, int P, int ND>
+__device__ __forceinline__ bool segment_owned(uint64_t len, int mis, uint64_t base, uint64_t* nt_out) {
+  constexpr int U = ReduceUnroll<P, (ND > 1)>::value;
+  constexpr uint64_t TV = (uint64_t)U * kBlock;
+  const SegSpan sp = seg_span<Traits<DT>::B>(len, mis);
+  const uint64_t nt = sp.vec ? ceil_div(sp.nvec, TV) : ceil_div(len, (uint64_t)kBlock * 4);
+  *nt_out = nt;
+  const uint64_t ft = first_tile32(base, blockIdx.x, gridDim.x);
+  return ft < nt || (ft == 0 && (sp.head || sp.tail));
+}
+
 // A whole segment as seen by one workgroup: its share of the vector tiles
 // (flat tile indices congruent to the workgroup id modulo the grid,
 // counting from `base`) and, for the owning workgroup, the head and tail.
