@@ -830,8 +830,9 @@ COLL_EXPORT coll_status_t coll_moe_dequant_fp8(const void* const* recv, void* co
 // Direct MoE dispatch and combine
 // ---------------------------------------------------------------------------
 namespace {
-// Dynamic LDS of the direct dispatch kernels: two p x p int32 placement tables.
-size_t direct_lds_bytes(int p) { return (size_t)2 * p * p * sizeof(int32_t); }
+// Dynamic LDS of the direct dispatch kernels: the row counts and the two
+// placement tables, p x p int32 each.
+size_t direct_lds_bytes(int p) { return (size_t)3 * p * p * sizeof(int32_t); }
 
 // Shared validation of the direct dispatches.  elem: payload bytes per
 // token element (tokens); row_bytes: bytes per delivered row (recv).

@@ -314,17 +314,20 @@ COLL_STREAM_KERNEL void moe_dequant_fp8_kernel(Fp8Args a) {
 #pragma clang fp contract(off)
   __shared__ int64_t start[kMaxRanks + 1];
   __shared__ int bad;
+  extern __shared__ int64_t cnt[];  // the p x p byte counts
   const int p = a.p;
   const int tid = threadIdx.x;
   const uint64_t H = a.hidden, R = a.row_bytes;
   if (tid == 0) bad = 0;
+  // one load per thread, then the per-rank sums from LDS
+  for (int x = tid; x < p * p; x += kBlock) cnt[x] = a.counts[x];
   __syncthreads();
   if (tid < p) {
     const int64_t cap = a.rows_cap[tid] * (int64_t)R;
     int64_t tot = 0;
     bool ok = true;
     for (int i = 0; i < p; ++i) {
-      const int64_t c = a.counts[(int64_t)i * p + tid];
+      const int64_t c = cnt[i * p + tid];
       if (c < 0 || c > cap || c % (int64_t)R) ok = false;
       else tot += c;
     }
@@ -459,7 +462,8 @@ int launch_moe_dispatch_fp8(const MoeDirectArgs& a, int max_grid, void* stream) 
 
 int launch_moe_dequant_fp8(const Fp8Args& a, int max_grid, void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  hipLaunchKernelGGL((moe_dequant_fp8_kernel<kDeqUnits>), dim3(max_grid), dim3(kBlock), 0, s, a);
+  const size_t shm = (size_t)a.p * a.p * sizeof(int64_t);
+  hipLaunchKernelGGL((moe_dequant_fp8_kernel<kDeqUnits>), dim3(max_grid), dim3(kBlock), shm, s, a);
   return (int)hipGetLastError();
 }
 

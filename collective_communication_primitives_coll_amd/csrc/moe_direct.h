@@ -9,8 +9,9 @@
 // so that packed row ps of an assignment to j lands on row
 // roff[i][j] + ps - soff[i][j] of recv[j]: the receive layout of the
 // ragged exchange (sources in rank order, each source's rows in its packed
-// order).  Each workgroup builds both tables in dynamic LDS (2 p^2 int32)
-// and checks every receive buffer's capacity.
+// order).  Each workgroup builds both tables in dynamic LDS (3 p^2 int32:
+// the row counts, loaded by all threads at once, then the two scans) and
+// checks every receive buffer's capacity.
 #pragma once
 
 #include "device_common.h"
@@ -18,7 +19,7 @@
 namespace coll {
 
 // LDS bytes the tables need for p ranks.
-__host__ __device__ constexpr size_t direct_tables_bytes(int p) { return (size_t)2 * p * p * sizeof(int32_t); }
+__host__ __device__ constexpr size_t direct_tables_bytes(int p) { return (size_t)3 * p * p * sizeof(int32_t); }
 
 // Fills soff and roff (each p*p, row-major [i][j]); returns true if some
 // receive buffer is too small, in which case nothing may be delivered.
@@ -28,20 +29,24 @@ __device__ __forceinline__ bool direct_tables(const MoeDirectArgs& a, int32_t* s
   const int p = a.p;
   const int tid = threadIdx.x;
   const int64_t unit = (int64_t)a.count_unit;
+  int32_t* rows = roff + p * p;  // third table: the row counts
   if (tid == 0) *flag = 0;
+  // one load per thread (a dependent chain of p loads per thread would
+  // cost every workgroup p memory latencies before its first row)
+  for (int x = tid; x < p * p; x += blockDim.x) rows[x] = (int32_t)(a.counts[x] / unit);
   __syncthreads();
   if (tid < p) {
-    int64_t s = 0;
+    int32_t s = 0;
     for (int j = 0; j < p; ++j) {
-      soff[tid * p + j] = (int32_t)s;
-      s += a.counts[tid * p + j] / unit;
+      soff[tid * p + j] = s;
+      s += rows[tid * p + j];
     }
   } else if (tid >= 64 && tid < 64 + p) {
     const int j = tid - 64;
     int64_t s = 0;
     for (int i = 0; i < p; ++i) {
       roff[i * p + j] = (int32_t)(s < 0x7fffffff ? s : 0x7fffffff);
-      s += a.counts[i * p + j] / unit;
+      s += rows[i * p + j];
     }
     if (s > a.cap[j]) *flag = 1;
   }
