@@ -81,7 +81,8 @@ def test_zero_rs_ag_full_size(env):
 
 def test_dp_allreduce_full_size(env):
     """AllReduce sum, p=8, 2^26 fp32 per rank ~ N(0,1): fused ring, recursive
-    doubling, halving-doubling and the literal 14-step ring, each bit-exact
+    doubling, halving-doubling, the tree, the double binary tree and the
+    literal 14-step ring, each bit-exact
     against the oracle's order for that schedule; the recursive-doubling
     result is also held to 1e-5 * sum|x| of the ring order."""
     torch, coll = env
@@ -96,10 +97,14 @@ def test_dp_allreduce_full_size(env):
     expect = ref.reduce_elements(cols, ref.chunk_of(j, n, p), ref.SUM, ref.F32)
     abs_sum = np.sum(np.abs(cols.astype(np.float64)), axis=0)
     per_rank = [cols[r] for r in range(p)]
+    tree_a = ref.tree_reduce_to_root(per_rank, list(range(p)), ref.SUM, ref.F32)
+    tree_b = ref.tree_reduce_to_root(per_rank, list(range(p - 1, -1, -1)), ref.SUM, ref.F32)
     trees = {coll.COLL_ALGO_RECURSIVE_DOUBLING: ref.fold_tree(per_rank, ref.SUM, ref.F32, "low"),
-             coll.COLL_ALGO_HALVING_DOUBLING: ref.fold_tree(per_rank, ref.SUM, ref.F32, "high")}
+             coll.COLL_ALGO_HALVING_DOUBLING: ref.fold_tree(per_rank, ref.SUM, ref.F32, "high"),
+             coll.COLL_ALGO_TREE: tree_a,
+             coll.COLL_ALGO_DOUBLE_BINARY_TREE: np.where(ref.chunk_of(j, n, p) < p // 2, tree_a, tree_b)}
     for algo in (coll.COLL_ALGO_RING, coll.COLL_ALGO_RECURSIVE_DOUBLING, coll.COLL_ALGO_HALVING_DOUBLING,
-                 coll.COLL_ALGO_RING_LITERAL):
+                 coll.COLL_ALGO_TREE, coll.COLL_ALGO_DOUBLE_BINARY_TREE, coll.COLL_ALGO_RING_LITERAL):
         for t in recv:
             t.fill_(float("nan"))
         coll.coll_allreduce_algo(send, recv, algo, coll.COLL_SUM)
