@@ -8,10 +8,10 @@
 //
 // The host lays out, per call, p chunks of ceil(n/p) elements, each cut
 // into tiles_per_chunk tiles, and a prefix of tile counts over the calls.
-// Each wave (64 lanes) is an independent worker that takes one contiguous
-// run of the flat tile range, finds its first call by binary search and
-// then walks forward call by call and chunk by chunk, so descriptors,
-// rotated pointers and chunk geometry are read once per chunk of its run.
+// Each wave (64 lanes) is an independent worker that takes short runs of
+// the flat tile range, finds a run's first call by binary search and then
+// walks forward call by call and chunk by chunk, so descriptors, rotated
+// pointers and chunk geometry are read once per chunk of a run.
 // Wave-sized tiles keep lanes busy on the many chunks of a few hundred
 // elements that small calls produce.
 // Within a tile the work is the single-call AllReduce's: ring order,
@@ -57,8 +57,8 @@ __device__ __forceinline__ void batch_run(const BatchCall& bc, const void* const
       S* dst[P];
 #pragma unroll
       for (int k = 0; k < P; ++k) {
-        src[k] = (const S*)pt[(c + 1 + k) % P] + lo;
-        dst[k] = (S*)pt[P + k] + lo;
+        src[k] = as_global((const S*)ld_const(&pt[(c + 1 + k) % P])) + lo;
+        dst[k] = as_global((S*)ld_const(&pt[P + k])) + lo;
       }
       const int mis = bc.mis < 0 ? -1 : (int)((bc.mis + lo * T::B) & 15);
       const SegSpan sp = seg_span<T::B>(len, mis);
@@ -86,12 +86,9 @@ __device__ __forceinline__ void batch_run(const BatchCall& bc, const void* const
           else if (i * TV < sp.nvec)
             reduce_vec_tile<DT, OP, P, kOrdRing, P, true, U, false, kWave>(vs, vd, j0, sp.nvec, sc, P);
         }
-        if (t == 0) {
-          if (sp.head) reduce_elems<DT, OP, P, kOrdRing, P, true, kWave>(src, dst, 0, sp.head, sc, P, lane);
-          if (sp.tail)
-            reduce_elems<DT, OP, P, kOrdRing, P, true, kWave>(src, dst, sp.head + sp.nvec * V, sp.tail, sc, P,
-                                                              lane);
-        }
+        if (t == 0 && (sp.head || sp.tail))
+          reduce_edges<DT, OP, P, kOrdRing, P, true>(src, dst, sp.head, sp.head + sp.nvec * V, sp.tail, sc, P,
+                                                     lane);
       }
     }
     left -= cnt;
@@ -118,11 +115,11 @@ __device__ __forceinline__ void batch_run_any(const BatchCall& bc, const void* c
     if (hi > bc.n) hi = bc.n;
     const uint64_t len = hi - lo;
     for (uint64_t e = t * TE + lane; e < len && e < (t + 1) * TE; e += kWave) {
-      A acc = widen1<DT>(ld1<true>((const S*)pt[(c + 1) % p] + lo + e));
+      A acc = widen1<DT>(ld1<true>(as_global((const S*)ld_const(&pt[(c + 1) % p])) + lo + e));
       for (int k = 1; k < p; ++k)
-        acc = combine<OP>(acc, widen1<DT>(ld1<true>((const S*)pt[(c + 1 + k) % p] + lo + e)));
+        acc = combine<OP>(acc, widen1<DT>(ld1<true>(as_global((const S*)ld_const(&pt[(c + 1 + k) % p])) + lo + e)));
       const S out = narrow1<DT>(finish<OP>(acc, p));
-      for (int k = 0; k < p; ++k) st1<true>((S*)pt[p + k] + lo + e, out);
+      for (int k = 0; k < p; ++k) st1<true>(as_global((S*)ld_const(&pt[p + k])) + lo + e, out);
     }
   }
 }
@@ -153,9 +150,27 @@ __device__ __forceinline__ void batch_dispatch(const BatchCall& bc, const void* 
 #undef COLL_BATCH_CASE
 }
 
-// Every wave is an independent worker: it takes one contiguous run of the
-// flat tile range, finds its first call by binary search and walks
+// A call record, read with scalar loads (the table is not written while
+// the kernel runs).
+__device__ __forceinline__ BatchCall load_call(const BatchCall* c) {
+  BatchCall b;
+  b.n = ld_const(&c->n);
+  b.first_tile = ld_const(&c->first_tile);
+  b.dtype = ld_const(&c->dtype);
+  b.op = ld_const(&c->op);
+  b.tiles_per_chunk = ld_const(&c->tiles_per_chunk);
+  b.mis = ld_const(&c->mis);
+  return b;
+}
+
+// Every wave is an independent worker.  The flat tile range is cut into
+// runs of kBatchRun tiles; wave w takes runs w, w + W, w + 2W, ... (W waves
+// in the grid), so at any moment the waves work on one window of the range
+// and move through it front to back together.  A wave finds a run's first
+// call by binary search (from its previous run's call onward) and walks
 // forward call by call.
+constexpr uint64_t kBatchRun = 32;
+
 template <int P>
 COLL_STREAM_KERNEL void batch_kernel(BatchArgs a) {
   const int p = P ? P : a.p;
@@ -163,26 +178,28 @@ COLL_STREAM_KERNEL void batch_kernel(BatchArgs a) {
   const uint64_t waves = (uint64_t)gridDim.x * (kBlock / kWave);
   const uint64_t wid =
       (uint64_t)blockIdx.x * (kBlock / kWave) + (uint64_t)__builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const uint64_t total = a.calls[a.ncalls].first_tile;
-  const uint64_t per = (total + waves - 1) / waves;
-  uint64_t t = wid * per;
-  uint64_t end = t + per;
-  if (end > total) end = total;
-  if (t >= end) return;
-  // binary search: last call whose first tile is <= t
-  int lo = 0, hi = a.ncalls;  // answer in [lo, hi)
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (a.calls[mid].first_tile <= t) lo = mid;
-    else hi = mid;
-  }
-  for (int k = lo; t < end; ++k) {
-    const BatchCall bc = a.calls[k];
-    const uint64_t next = a.calls[k + 1].first_tile;
-    const uint64_t stop = next < end ? next : end;
-    if (stop > t)
-      batch_dispatch<P>(bc, a.ptrs + (size_t)k * 2 * p, p, t - bc.first_tile, stop - bc.first_tile, lane);
-    t = stop > t ? stop : t;
+  const uint64_t total = ld_const(&a.calls[a.ncalls].first_tile);
+  int from_call = 0;
+  for (uint64_t run = wid; run * kBatchRun < total; run += waves) {
+    uint64_t t = run * kBatchRun;
+    const uint64_t end = t + kBatchRun < total ? t + kBatchRun : total;
+    // last call whose first tile is <= t
+    int lo = from_call, hi = a.ncalls;  // answer in [lo, hi)
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (ld_const(&a.calls[mid].first_tile) <= t) lo = mid;
+      else hi = mid;
+    }
+    from_call = lo;
+    // calls[ncalls].first_tile == total >= end, so k stays below ncalls
+    for (int k = lo; t < end; ++k) {
+      const BatchCall bc = load_call(a.calls + k);
+      const uint64_t next = ld_const(&a.calls[k + 1].first_tile);
+      const uint64_t stop = next < end ? next : end;
+      if (stop > t)
+        batch_dispatch<P>(bc, a.ptrs + (size_t)k * 2 * p, p, t - bc.first_tile, stop - bc.first_tile, lane);
+      t = stop > t ? stop : t;
+    }
   }
 }
 

@@ -76,13 +76,13 @@ __device__ __forceinline__ uint64_t copy_segment(const typename Word<B>::T* src,
   constexpr uint64_t V = 16 / B;
   const uint64_t grid = gridDim.x, wg = blockIdx.x;
   const int ndst = ND ? ND : nd;
-  auto elems = [&](uint64_t from, uint64_t cnt) {
-    for (uint64_t i = threadIdx.x; i < cnt; i += kBlock) {
-      const uint64_t e = from + i;
-      const W w = ld1<NTL>(src + e);
+  auto elem_at = [&](uint64_t e) {
+    const W w = ld1<NTL>(src + e);
 #pragma unroll
-      for (int d = 0; d < ndst; ++d) st1<true>(gdst(d) + e, w);
-    }
+    for (int d = 0; d < ndst; ++d) st1<true>(gdst(d) + e, w);
+  };
+  auto elems = [&](uint64_t from, uint64_t cnt) {
+    for (uint64_t i = threadIdx.x; i < cnt; i += kBlock) elem_at(from + i);
   };
   const SegSpan sp = seg_span<B>(len, mis);
   if (!sp.vec) {
@@ -106,8 +106,9 @@ __device__ __forceinline__ uint64_t copy_segment(const typename Word<B>::T* src,
     }
   }
   if ((sp.head || sp.tail) && first_tile(base, wg, grid) == 0) {
-    if (sp.head) elems(0, sp.head);
-    if (sp.tail) elems(sp.head + sp.nvec * V, sp.tail);
+    // head and tail in one pass (each is shorter than a vector)
+    const uint64_t i = threadIdx.x;
+    if (i < sp.head + sp.tail) elem_at(i < sp.head ? i : sp.head + sp.nvec * V + (i - sp.head));
   }
   return nt;
 }

@@ -77,6 +77,25 @@ __device__ __forceinline__ void st1(S* p, S v) {
   else *p = v;
 }
 
+// A pointer that a kernel reads from device memory (not from its
+// arguments) has no known address space, so accesses through it compile to
+// FLAT instructions.  Those also count against the scalar-memory counter:
+// a later scalar load then waits for every outstanding FLAT store.  Every
+// buffer here is device-visible global memory, so such pointers are
+// declared global, which gives GLOBAL loads and stores.
+template <typename T>
+__device__ __forceinline__ T* as_global(T* p) {
+  return (T*)(__attribute__((address_space(1))) T*)(uintptr_t)p;
+}
+
+// Load from memory that no thread writes during the kernel (descriptor
+// tables uploaded before the launch): read through the constant address
+// space, a uniform address becomes a scalar load.
+template <typename T>
+__device__ __forceinline__ T ld_const(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)(uintptr_t)p;
+}
+
 // ---------------------------------------------------------------------------
 // Widening and narrowing.  bf16 widens exactly (the pattern is the upper
 // half of the fp32 pattern) and narrows with round-to-nearest-even through

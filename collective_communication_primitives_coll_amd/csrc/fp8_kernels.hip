@@ -90,9 +90,9 @@ template <> struct Rows<Fp8Args> {
   const Fp8Args& a;
   __device__ uint8_t* slot_row(int rank, uint64_t x, int64_t& loc) const {
     loc = -1;
-    const int32_t ps = a.pos[rank][x];
+    const int32_t ps = as_global(a.pos[rank])[x];
     if (ps < 0 || (uint64_t)ps >= a.tokens * (uint64_t)a.k) return nullptr;
-    return (uint8_t*)a.dst[rank] + (uint64_t)ps * a.row_bytes;
+    return as_global((uint8_t*)a.dst[rank]) + (uint64_t)ps * a.row_bytes;
   }
   __device__ void finish(int, uint64_t, const int64_t (&)[kMaxTopK], int) const {}
 };
@@ -106,19 +106,19 @@ template <> struct Rows<MoeDirectArgs> {
     loc = -1;
     if (reject) return nullptr;
     // every lane reads the same words: keep them in scalar registers
-    const int32_t ps = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)(uint64_t)a.loc[rank][x]);
+    const int32_t ps = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)(uint64_t)as_global(a.loc[rank])[x]);
     if (ps < 0 || (uint64_t)ps >= a.tokens * (uint64_t)a.k) return nullptr;
-    const int j = __builtin_amdgcn_readfirstlane(a.dest[rank][x]);
+    const int j = __builtin_amdgcn_readfirstlane(as_global(a.dest[rank])[x]);
     if (j < 0 || j >= a.p) return nullptr;
     const int64_t row = (int64_t)roff[rank * a.p + j] + (ps - soff[rank * a.p + j]);
     loc = direct_loc(j, row);
-    return (uint8_t*)a.dst[j] + (uint64_t)row * a.row_bytes;
+    return as_global((uint8_t*)a.dst[j]) + (uint64_t)row * a.row_bytes;
   }
   // after every read of the token's locations
   __device__ void finish(int rank, uint64_t x0, const int64_t (&loc)[kMaxTopK], int lane) const {
 #pragma unroll
     for (int s = 0; s < kMaxTopK; ++s)
-      if (s < a.k && lane == 0) a.loc[rank][x0 + s] = loc[s];
+      if (s < a.k && lane == 0) as_global(a.loc[rank])[x0 + s] = loc[s];
   }
 };
 
@@ -171,7 +171,7 @@ COLL_STREAM_KERNEL void moe_pack_fp8_cols_kernel(Args a) {
     uint8_t* drow[kMaxTopK];
     int64_t loc[kMaxTopK];
     if (slot_rows(tgt, a, rank, t, drow, loc)) {
-      const u32x4* src = reinterpret_cast<const u32x4*>((const uint16_t*)a.src[rank] + t * H);
+      const u32x4* src = reinterpret_cast<const u32x4*>(as_global((const uint16_t*)a.src[rank]) + t * H);
       for (uint32_t c0 = 0; c0 < ncols; c0 += CB) {
         u32x4 x[CB][2];
         uint32_t mb[CB];
@@ -201,8 +201,8 @@ COLL_STREAM_KERNEL void moe_pack_fp8_cols_kernel(Args a) {
 #pragma unroll
         for (int s = 0; s < kMaxTopK; ++s) {
           if (!drow[s]) continue;
-          u32x4* vc = reinterpret_cast<u32x4*>(drow[s]);
-          float* scales = reinterpret_cast<float*>(drow[s] + H);
+          u32x4* vc = as_global(reinterpret_cast<u32x4*>(drow[s]));
+          float* scales = as_global(reinterpret_cast<float*>(drow[s] + H));
 #pragma unroll
           for (int u = 0; u < CB; ++u) {
             const uint32_t j = (c0 + u) * kLanes + lane;
@@ -216,7 +216,7 @@ COLL_STREAM_KERNEL void moe_pack_fp8_cols_kernel(Args a) {
       if ((uint32_t)lane < npad) {
 #pragma unroll
         for (int s = 0; s < kMaxTopK; ++s)
-          if (drow[s]) reinterpret_cast<float*>(drow[s] + H)[ngroups + lane] = 0.0f;
+          if (drow[s]) as_global(reinterpret_cast<float*>(drow[s] + H))[ngroups + lane] = 0.0f;
       }
     }
     tgt.finish(rank, t * (uint64_t)a.k, loc, lane);
@@ -247,7 +247,7 @@ COLL_STREAM_KERNEL void moe_pack_fp8_rows_kernel(Args a) {
     uint8_t* drow[kMaxTopK];
     int64_t loc[kMaxTopK];
     if (slot_rows(tgt, a, rank, t, drow, loc)) {
-      const u32x4* src = reinterpret_cast<const u32x4*>((const uint16_t*)a.src[rank] + t * H);
+      const u32x4* src = reinterpret_cast<const u32x4*>(as_global((const uint16_t*)a.src[rank]) + t * H);
       u32x4 x[UMAX][2];
 #pragma unroll
       for (int u = 0; u < UMAX; ++u) {
@@ -287,8 +287,8 @@ COLL_STREAM_KERNEL void moe_pack_fp8_rows_kernel(Args a) {
 #pragma unroll
       for (int s = 0; s < kMaxTopK; ++s) {
         if (!drow[s]) continue;
-        u32x4* vc = reinterpret_cast<u32x4*>(drow[s]);
-        float* scales = reinterpret_cast<float*>(drow[s] + H);
+        u32x4* vc = as_global(reinterpret_cast<u32x4*>(drow[s]));
+        float* scales = as_global(reinterpret_cast<float*>(drow[s] + H));
 #pragma unroll
         for (int u = 0; u < UMAX; ++u) {
           const uint32_t j = (uint32_t)(u * kLanes + lane);
@@ -360,10 +360,10 @@ COLL_STREAM_KERNEL void moe_dequant_fp8_kernel(Fp8Args a) {
     int rk = 0;
     while ((uint64_t)start[rk + 1] <= g) ++rk;
     const uint64_t row = g - (uint64_t)start[rk];
-    const uint8_t* src = (const uint8_t*)a.src[rk] + row * R;
+    const uint8_t* src = as_global((const uint8_t*)a.src[rk]) + row * R;
     vc = reinterpret_cast<const u32x4*>(src);
     sc = reinterpret_cast<const float*>(src + H);
-    dst = reinterpret_cast<u32x4*>((uint16_t*)a.dst[rk] + row * H);
+    dst = reinterpret_cast<u32x4*>(as_global((uint16_t*)a.dst[rk]) + row * H);
   };
   auto load = [&](const u32x4* vc, const float* sc, uint32_t j0, u32x4 (&c)[DB], float (&s)[DB]) {
 #pragma unroll

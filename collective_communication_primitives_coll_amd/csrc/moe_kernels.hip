@@ -38,8 +38,8 @@ __global__ __launch_bounds__(kIdxThreads) void moe_index_kernel(MoeIndexArgs a) 
   const int rank = blockIdx.x;
   const int p = a.p;
   const uint64_t A = a.assignments;
-  const int32_t* dest = a.dest[rank];
-  int32_t* pos = a.pos[rank];
+  const int32_t* dest = as_global(a.dest[rank]);
+  int32_t* pos = as_global(a.pos[rank]);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const uint64_t below = (1ull << lane) - 1ull;
   for (int x = tid; x < kIdxWaves * kMaxRanks; x += kIdxThreads) (&wofs[0][0])[x] = 0;
@@ -185,10 +185,10 @@ template <> struct SlotRows<MoeRowArgs> {
   const MoeRowArgs& a;
   __device__ void* row(int rank, uint64_t x, uint64_t row_bytes, int64_t& loc, uint64_t& off) const {
     loc = -1;
-    const int32_t ps = a.pos[rank][x];
+    const int32_t ps = as_global(a.pos[rank])[x];
     if (ps < 0 || (uint64_t)ps >= a.tokens * (uint64_t)a.k) return nullptr;
     off = (uint64_t)ps * row_bytes;
-    return (uint8_t*)a.dst[rank] + off;
+    return as_global((uint8_t*)a.dst[rank]) + off;
   }
   __device__ void finish(int, uint64_t, const int64_t (&)[kMaxTopK], int) const {}
 };
@@ -202,20 +202,20 @@ template <> struct SlotRows<MoeDirectArgs> {
     loc = -1;
     if (reject) return nullptr;
     // every lane reads the same words: keep them in scalar registers
-    const int32_t ps = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)(uint64_t)a.loc[rank][x]);
+    const int32_t ps = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)(uint64_t)as_global(a.loc[rank])[x]);
     if (ps < 0 || (uint64_t)ps >= a.tokens * (uint64_t)a.k) return nullptr;
-    const int j = __builtin_amdgcn_readfirstlane(a.dest[rank][x]);
+    const int j = __builtin_amdgcn_readfirstlane(as_global(a.dest[rank])[x]);
     if (j < 0 || j >= a.p) return nullptr;
     const int64_t rw = (int64_t)roff[rank * a.p + j] + (ps - soff[rank * a.p + j]);
     loc = direct_loc(j, rw);
     off = (uint64_t)rw * row_bytes;
-    return (uint8_t*)a.dst[j] + off;
+    return as_global((uint8_t*)a.dst[j]) + off;
   }
   // after every read of the token's locations
   __device__ void finish(int rank, uint64_t x0, const int64_t (&loc)[kMaxTopK], int lane) const {
 #pragma unroll
     for (int s = 0; s < kMaxTopK; ++s)
-      if (s < a.k && lane == 0) a.loc[rank][x0 + s] = loc[s];
+      if (s < a.k && lane == 0) as_global(a.loc[rank])[x0 + s] = loc[s];
   }
 };
 
@@ -262,7 +262,7 @@ COLL_STREAM_KERNEL void moe_token_copy_kernel(Args a) {
       }
     }
     if (any) {
-      const W* src = (const W*)a.src[rank] + t * H;
+      const W* src = as_global((const W*)a.src[rank]) + t * H;
       if (aligned) {
         const u32x4* vs = reinterpret_cast<const u32x4*>(src);
         for (uint64_t j0 = 0; j0 < nvec; j0 += (uint64_t)kRowBatch * kWaveLanes) {
@@ -276,7 +276,7 @@ COLL_STREAM_KERNEL void moe_token_copy_kernel(Args a) {
 #pragma unroll
           for (int s = 0; s < kMaxTopK; ++s) {
             if (!drow[s]) continue;
-            u32x4* vd = reinterpret_cast<u32x4*>(drow[s]);
+            u32x4* vd = as_global(reinterpret_cast<u32x4*>(drow[s]));
 #pragma unroll
             for (int u = 0; u < kRowBatch; ++u) {
               const uint64_t j = j0 + (uint64_t)u * kWaveLanes + lane;
@@ -289,7 +289,7 @@ COLL_STREAM_KERNEL void moe_token_copy_kernel(Args a) {
         for (int s = 0; s < kMaxTopK; ++s) {
           if (!drow[s]) continue;
           const int mis = seg_mis(a.src_mis, a.dst_mis, t * RB, off[s]);
-          copy_row_wave<B>(src, (W*)drow[s], H, mis, lane);
+          copy_row_wave<B>(src, as_global((W*)drow[s]), H, mis, lane);
         }
       }
     }
@@ -337,25 +337,25 @@ COLL_STREAM_KERNEL void moe_combine_kernel(MoeRowArgs a) {
         int64_t row;
         if constexpr (DIRECT) {
           // the same location in every lane: read it into scalar registers
-          const uint64_t lw = reinterpret_cast<const uint64_t*>(a.pos[rank])[t * k + s];
+          const uint64_t lw = as_global(reinterpret_cast<const uint64_t*>(a.pos[rank]))[t * k + s];
           const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)lw);
           const int32_t hi = __builtin_amdgcn_readfirstlane((int32_t)(lw >> 32));
           j = hi;
           row = lo;
           ok[s] = hi >= 0 && hi < a.p && row < a.cap[hi];
         } else {
-          row = a.pos[rank][t * k + s];
+          row = as_global(a.pos[rank])[t * k + s];
           ok[s] = row >= 0 && (uint64_t)row < Aa;
         }
         if (ok[s]) {
-          wt[s] = a.weights[rank][t * k + s];
-          yrow[s] = (const S*)a.src[j] + (uint64_t)row * H;
+          wt[s] = as_global(a.weights[rank])[t * k + s];
+          yrow[s] = as_global((const S*)a.src[j]) + (uint64_t)row * H;
           mis = seg_mis(mis, a.src_mis, 0, (uint64_t)row * H * T::B);
         }
       }
     }
-    const S* res = a.has_residual ? (const S*)a.residual[rank] + t * H : nullptr;
-    S* out = (S*)a.dst[rank] + t * H;
+    const S* res = a.has_residual ? as_global((const S*)a.residual[rank]) + t * H : nullptr;
+    S* out = as_global((S*)a.dst[rank]) + t * H;
     auto elems = [&](uint64_t from, uint64_t cnt) {
       for (uint64_t e = from + lane; e < from + cnt; e += kWaveLanes) {
         A acc = res ? widen1<DT>(ld1<true>(res + e)) : A(0.0f);

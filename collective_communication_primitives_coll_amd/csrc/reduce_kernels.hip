@@ -101,20 +101,20 @@ COLL_STREAM_KERNEL void reduce_kernel_any(RankPtrs ptrs, ReduceGeom g) {
     const int nd = ALL ? p : 1;
     const SegSpan sp = seg_span<T::B>(len, seg_mis(g.src_mis, g.dst_mis, lo * T::B, doff * T::B));
     auto scale_of = [&](int k) -> float { return g.scale[(c + 1 + k) % p]; };
-    auto elems = [&](uint64_t from, uint64_t cnt) {
+    auto elem_at = [&](uint64_t e) {
 #pragma clang fp contract(off)
-      for (uint64_t i = threadIdx.x; i < cnt; i += kBlock) {
-        const uint64_t e = from + i;
-        A acc = widen1<DT>(ld1<true>(sp_src(0) + e));
-        if constexpr (OP == kPreMul) acc = scale_of(0) * acc;
-        for (int k = 1; k < p; ++k) {
-          A v = widen1<DT>(ld1<true>(sp_src(k) + e));
-          if constexpr (OP == kPreMul) v = scale_of(k) * v;
-          acc = combine<OP>(acc, v);
-        }
-        const auto out = narrow1<DT>(finish<OP>(acc, p));
-        for (int d = 0; d < nd; ++d) st1<ALL>(sp_dst(d) + e, out);
+      A acc = widen1<DT>(ld1<true>(sp_src(0) + e));
+      if constexpr (OP == kPreMul) acc = scale_of(0) * acc;
+      for (int k = 1; k < p; ++k) {
+        A v = widen1<DT>(ld1<true>(sp_src(k) + e));
+        if constexpr (OP == kPreMul) v = scale_of(k) * v;
+        acc = combine<OP>(acc, v);
       }
+      const auto out = narrow1<DT>(finish<OP>(acc, p));
+      for (int d = 0; d < nd; ++d) st1<ALL>(sp_dst(d) + e, out);
+    };
+    auto elems = [&](uint64_t from, uint64_t cnt) {
+      for (uint64_t i = threadIdx.x; i < cnt; i += kBlock) elem_at(from + i);
     };
     if (!sp.vec) {
       constexpr uint64_t TE = (uint64_t)kBlock * 4;
@@ -160,8 +160,9 @@ COLL_STREAM_KERNEL void reduce_kernel_any(RankPtrs ptrs, ReduceGeom g) {
       for (int d = 0; d < nd; ++d) st16<ALL>(sp_dst(d) + e, out);
     }
     if ((sp.head || sp.tail) && first_tile(base, wg, grid) == 0) {
-      if (sp.head) elems(0, sp.head);
-      if (sp.tail) elems(sp.head + sp.nvec * V, sp.tail);
+      // head and tail in one pass (each is shorter than a vector)
+      const uint64_t i = threadIdx.x;
+      if (i < sp.head + sp.tail) elem_at(i < sp.head ? i : sp.head + sp.nvec * V + (i - sp.head));
     }
     base += nt;
   }

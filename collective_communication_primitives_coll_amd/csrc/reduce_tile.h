@@ -145,6 +145,50 @@ __device__ __forceinline__ void reduce_vec_tile(const typename Traits<DT>::S* co
     }
 }
 
+// One element e of the segment (src/dst at the segment start): the p
+// operands in the schedule's order, the result to every destination.
+template <int DT, int OP, int P, int ORD, int ND, bool NTS>
+__device__ __forceinline__ void reduce_elem_at(const typename Traits<DT>::S* const (&src)[P],
+                                               typename Traits<DT>::S* const (&dst)[ND], uint64_t e,
+                                               const Scales<P>& sc, int avg_p) {
+#pragma clang fp contract(off)
+  using A = typename Traits<DT>::A;
+  A a[P];
+#pragma unroll
+  for (int k = 0; k < P; ++k) {
+    a[k] = widen1<DT>(ld1<true>(src[k] + e));
+    if constexpr (OP == kPreMul) a[k] = sc.s[k] * a[k];
+  }
+  A acc;
+  if constexpr (ORD == kOrdRD) {
+#pragma unroll
+    for (int st = 1; st < P; st *= 2)
+#pragma unroll
+      for (int k = 0; k + st < P; k += 2 * st) a[k] = combine<OP>(a[k], a[k + st]);
+    acc = a[0];
+  } else if constexpr (ORD == kOrdHD) {
+#pragma unroll
+    for (int st = P / 2; st >= 1; st /= 2)
+#pragma unroll
+      for (int k = 0; k < st; ++k) a[k] = combine<OP>(a[k], a[k + st]);
+    acc = a[0];
+  } else if constexpr (ORD == kOrdTree || ORD == kOrdDBT) {
+#pragma unroll
+    for (int v = P - 1; v >= 0; --v) {
+      if (2 * v + 1 < P) a[v] = combine<OP>(a[v], a[2 * v + 1]);
+      if (2 * v + 2 < P) a[v] = combine<OP>(a[v], a[2 * v + 2]);
+    }
+    acc = a[0];
+  } else {
+    acc = a[0];
+#pragma unroll
+    for (int k = 1; k < P; ++k) acc = combine<OP>(acc, a[k]);
+  }
+  const auto out = narrow1<DT>(finish<OP>(acc, avg_p));
+#pragma unroll
+  for (int d = 0; d < ND; ++d) st1<NTS>(dst[d] + e, out);
+}
+
 // Element-wise path: cnt elements from element offset `from` of the
 // segment (src/dst at the segment start), one element per lane; `lane`
 // of LANES lanes.
@@ -152,46 +196,23 @@ template <int DT, int OP, int P, int ORD, int ND, bool NTS, int LANES = kBlock>
 __device__ __forceinline__ void reduce_elems(const typename Traits<DT>::S* const (&src)[P],
                                              typename Traits<DT>::S* const (&dst)[ND], uint64_t from,
                                              uint64_t cnt, const Scales<P>& sc, int avg_p, int lane = -1) {
-#pragma clang fp contract(off)
-  using A = typename Traits<DT>::A;
   const uint64_t l0 = lane < 0 ? threadIdx.x : (uint64_t)lane;
-  for (uint64_t i = l0; i < cnt; i += LANES) {
-    const uint64_t e = from + i;
-    A a[P];
-#pragma unroll
-    for (int k = 0; k < P; ++k) {
-      a[k] = widen1<DT>(ld1<true>(src[k] + e));
-      if constexpr (OP == kPreMul) a[k] = sc.s[k] * a[k];
-    }
-    A acc;
-    if constexpr (ORD == kOrdRD) {
-#pragma unroll
-      for (int st = 1; st < P; st *= 2)
-#pragma unroll
-        for (int k = 0; k + st < P; k += 2 * st) a[k] = combine<OP>(a[k], a[k + st]);
-      acc = a[0];
-    } else if constexpr (ORD == kOrdHD) {
-#pragma unroll
-      for (int st = P / 2; st >= 1; st /= 2)
-#pragma unroll
-        for (int k = 0; k < st; ++k) a[k] = combine<OP>(a[k], a[k + st]);
-      acc = a[0];
-    } else if constexpr (ORD == kOrdTree || ORD == kOrdDBT) {
-#pragma unroll
-      for (int v = P - 1; v >= 0; --v) {
-        if (2 * v + 1 < P) a[v] = combine<OP>(a[v], a[2 * v + 1]);
-        if (2 * v + 2 < P) a[v] = combine<OP>(a[v], a[2 * v + 2]);
-      }
-      acc = a[0];
-    } else {
-      acc = a[0];
-#pragma unroll
-      for (int k = 1; k < P; ++k) acc = combine<OP>(acc, a[k]);
-    }
-    const auto out = narrow1<DT>(finish<OP>(acc, avg_p));
-#pragma unroll
-    for (int d = 0; d < ND; ++d) st1<NTS>(dst[d] + e, out);
-  }
+  for (uint64_t i = l0; i < cnt; i += LANES)
+    reduce_elem_at<DT, OP, P, ORD, ND, NTS>(src, dst, from + i, sc, avg_p);
+}
+
+// The misaligned head (elements [0, head)) and tail (tail elements from
+// tail_from) of a vectorized segment in one pass: lane i < head takes
+// element i, lane head + i element tail_from + i.  Both are shorter than
+// one 16-byte vector, so one pass of any wave covers them, and the two
+// cost one memory round trip instead of two.
+template <int DT, int OP, int P, int ORD, int ND, bool NTS>
+__device__ __forceinline__ void reduce_edges(const typename Traits<DT>::S* const (&src)[P],
+                                             typename Traits<DT>::S* const (&dst)[ND], uint64_t head,
+                                             uint64_t tail_from, uint64_t tail, const Scales<P>& sc, int avg_p,
+                                             int lane) {
+  const uint64_t i = (uint64_t)lane;
+  if (i < head + tail) reduce_elem_at<DT, OP, P, ORD, ND, NTS>(src, dst, i < head ? i : tail_from + (i - head), sc, avg_p);
 }
 
 // Tiles of a segment as reduce_segment counts them, and whether workgroup
@@ -251,10 +272,9 @@ __device__ __forceinline__ uint64_t reduce_segment(const typename Traits<DT>::S*
       else reduce_vec_tile<DT, OP, P, ORD, ND, NTS, U, false>(vs, vd, j0, sp.nvec, sc, avg_p);
     }
   }
-  if ((sp.head || sp.tail) && first_tile(base, wg, grid) == 0) {
-    if (sp.head) reduce_elems<DT, OP, P, ORD, ND, NTS>(src, dst, 0, sp.head, sc, avg_p);
-    if (sp.tail) reduce_elems<DT, OP, P, ORD, ND, NTS>(src, dst, sp.head + sp.nvec * V, sp.tail, sc, avg_p);
-  }
+  if ((sp.head || sp.tail) && first_tile(base, wg, grid) == 0)
+    reduce_edges<DT, OP, P, ORD, ND, NTS>(src, dst, sp.head, sp.head + sp.nvec * V, sp.tail, sc, avg_p,
+                                          (int)threadIdx.x);
   return nt;
 }
 

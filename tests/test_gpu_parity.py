@@ -1141,6 +1141,35 @@ def test_allreduce_batch(coll, p):
             assert_bits_equal(to_host(recv[r], dtype)[:n], expect[r], f"batch call {k} rank {r}")
 
 
+def test_allreduce_batch_misaligned_views(coll):
+    """Calls whose buffers share a misalignment (vector path with a head and
+    a tail in most chunks, including chunks shorter than one vector) and a
+    call whose ranks disagree (element path); sizes spanning many tiles."""
+    p = 8
+    calls, host, keep = [], [], []
+    specs = [(F32, 1, 1, 3 * p + 5), (BF16, 3, 3, 7 * p + 3), (I32, 2, 2, 50001), (BF16, 1, 1, 4 * p),
+             (F32, 1, 1, 2 * p + 1), (F32, None, 1, 777), (BF16, 5, 5, 70003)]
+    for k, (dtype, so, ro, n) in enumerate(specs):
+        hx = gen(p, n, dtype, 900 + k)
+        # so None: rank r's send view starts r % 4 elements in (misalignments differ)
+        send, recv = [], []
+        for r, x in enumerate(hx):
+            base, view = upload_offset(x, dtype, (r % 4) if so is None else so)
+            keep.append(base)
+            send.append(view)
+            base, view = upload_offset(np.zeros(n, dtype=x.dtype), dtype, ro)
+            keep.append(base)
+            recv.append(view)
+        calls.append((send, recv, n, dtype, k % 3))
+        host.append(hx)
+    coll.coll_allreduce_batch(calls, p)
+    sync()
+    for k, ((send, recv, n, dtype, op), hx) in enumerate(zip(calls, host)):
+        expect = ref.allreduce(hx, op, dtype)
+        for r in range(p):
+            assert_bits_equal(to_host(recv[r], dtype), expect[r], f"misaligned batch call {k} rank {r}")
+
+
 def test_allreduce_batch_reuses_descriptors(coll):
     """Consecutive batches of different sizes (buffer growth and reuse)."""
     p = 4
