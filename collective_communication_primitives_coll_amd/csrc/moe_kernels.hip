@@ -11,9 +11,10 @@
 // Index pass (one 1024-thread workgroup per source rank): every wave owns
 // a contiguous run of the rank's assignments.  It counts destinations 64
 // assignments at a time, grouping equal destinations of a group with
-// ballots; the per-wave counts are turned into exclusive offsets (by
-// destination, then by wave); a second walk gives every assignment its
-// packed row, stable in assignment order.  Destinations outside [0, p)
+// ballots, into per-lane registers (lane d counts destination d); the
+// per-wave counts are turned into exclusive offsets (by destination, then
+// by wave); a second walk gives every assignment its packed row, stable in
+// assignment order.  Destinations outside [0, p)
 // reject the rank: its counts are 0 and every pos is -1.
 //
 // Payload copy and combine: one wave per token row, rows spread over every
@@ -42,14 +43,16 @@ __global__ __launch_bounds__(kIdxThreads) void moe_index_kernel(MoeIndexArgs a) 
   int32_t* pos = as_global(a.pos[rank]);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const uint64_t below = (1ull << lane) - 1ull;
-  for (int x = tid; x < kIdxWaves * kMaxRanks; x += kIdxThreads) (&wofs[0][0])[x] = 0;
   if (tid == 0) bad = 0;
   __syncthreads();
   const uint64_t per = ((A + kIdxWaves - 1) / kIdxWaves + 63) / 64 * 64;
   uint64_t lo = (uint64_t)w * per, hi = lo + per;
   if (lo > A) lo = A;
   if (hi > A) hi = A;
-  // pass 1: per-wave destination counts (kIdxBatch groups of 64 loaded together)
+  // pass 1: per-wave destination counts (kIdxBatch groups of 64 loaded
+  // together).  p <= 64, so lane d keeps the wave's count for destination
+  // d in a register.
+  int cnt = 0;
   for (uint64_t b0 = lo; b0 < hi; b0 += 64 * kIdxBatch) {
     int dv[kIdxBatch];
 #pragma unroll
@@ -69,11 +72,12 @@ __global__ __launch_bounds__(kIdxThreads) void moe_index_kernel(MoeIndexArgs a) 
         const int leader = __ffsll((unsigned long long)rem) - 1;
         const int dl = __builtin_amdgcn_readlane(d, leader);
         const uint64_t m = __ballot(d == dl) & rem;
-        if (lane == leader) wofs[w][dl] += __popcll(m);
+        if (lane == dl) cnt += __popcll(m);
         rem &= ~m;
       }
     }
   }
+  if (lane < p) wofs[w][lane] = cnt;
   __syncthreads();
   if (tid < p) {
     int t = 0;
@@ -105,7 +109,9 @@ __global__ __launch_bounds__(kIdxThreads) void moe_index_kernel(MoeIndexArgs a) 
     for (uint64_t x = tid; x < A; x += kIdxThreads) pos[x << a.pos_shift] = -1;
     return;
   }
-  // pass 2: packed row of every assignment
+  // pass 2: packed row of every assignment; lane d holds the wave's next
+  // row for destination d
+  int next = lane < p ? wofs[w][lane] : 0;
   for (uint64_t b0 = lo; b0 < hi; b0 += 64 * kIdxBatch) {
     int dv[kIdxBatch];
 #pragma unroll
@@ -123,8 +129,9 @@ __global__ __launch_bounds__(kIdxThreads) void moe_index_kernel(MoeIndexArgs a) 
         const int leader = __ffsll((unsigned long long)rem) - 1;
         const int dl = __builtin_amdgcn_readlane(d, leader);
         const uint64_t m = __ballot(d == dl) & rem;
-        if (d == dl) mine = wofs[w][dl] + __popcll(m & below);
-        if (lane == leader) wofs[w][dl] += __popcll(m);
+        const int at = __builtin_amdgcn_readlane(next, dl);
+        if (d == dl) mine = at + __popcll(m & below);
+        if (lane == dl) next += __popcll(m);
         rem &= ~m;
       }
       if (d >= 0) pos[x << a.pos_shift] = mine;
