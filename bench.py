@@ -68,6 +68,10 @@ def parse_args(argv=None):
 KERNEL_SOURCES = {
     "reduce_scatter": ["coll_api.cpp", "kernel_args.h", "device_common.h", "reduce_tile.h", "reduce_kernels.hip"],
     "allgather": ["coll_api.cpp", "kernel_args.h", "device_common.h", "copy_tile.h", "copy_kernels.hip"],
+    "alltoall": ["coll_api.cpp", "kernel_args.h", "device_common.h", "copy_tile.h", "copy_kernels.hip"],
+    "alltoall_lds": ["coll_api.cpp", "kernel_args.h", "device_common.h", "copy_tile.h", "a2a_lds_kernels.hip"],
+    "alltoallv": ["coll_api.cpp", "kernel_args.h", "device_common.h", "copy_tile.h", "copy_kernels.hip"],
+    "allreduce": ["coll_api.cpp", "kernel_args.h", "device_common.h", "reduce_tile.h", "reduce_kernels.hip"],
 }
 
 
@@ -322,6 +326,13 @@ def extra_collectives(torch, coll, inputs, metrics, dev, which, iters=10, warmup
             rows.append(coll_entry(metrics, "alltoall_equal", "alltoall", p, per // p, 2, med, "ring",
                                    {"dtype": "bf16", "t_p95_us": round(p95, 2),
                                     "workload": "MoE dispatch, 512 tokens x 7168 per destination"}))
+            # the same transpose with every vector staged in LDS (gfx950
+            # global-to-LDS loads), timed on the same buffers
+            f = coll.coll_alltoall_algo(send, recv, coll.COLL_A2A_LDS_STAGED, per // p, defer=True)
+            med, p95, _ = stats_us(time_launches(torch, [f], iters, warmup)[0])
+            rows.append(coll_entry(metrics, "alltoall_equal_lds_staged", "alltoall", p, per // p, 2, med, "ring",
+                                   {"dtype": "bf16", "t_p95_us": round(p95, 2),
+                                    "workload": "MoE dispatch, 512 tokens x 7168 per destination"}))
             del recv
         if want("a2av"):
             ctok = inputs.moe_token_counts(p, tokens)
@@ -382,6 +393,10 @@ def extra_collectives(torch, coll, inputs, metrics, dev, which, iters=10, warmup
     # --- small AllReduce, p = 4, 2^20 per rank (Infinity-Cache resident) ------
     if want("ar_small"):
         p, n = 4, 1 << 20
+        # 32 MiB of buffers fit in the 256 MB Infinity Cache: back-to-back
+        # calls run warm.  A 512 MiB overwrite before each call evicts them
+        # (cold); events bracket only the AllReduce.
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         for dt, op, dname, oname in ((inputs.F32, coll.COLL_SUM, "f32", "sum"),
                                      (inputs.I32, coll.COLL_MIN, "i32", "min"),
                                      (inputs.I32, coll.COLL_MAX, "i32", "max")):
@@ -390,9 +405,23 @@ def extra_collectives(torch, coll, inputs, metrics, dev, which, iters=10, warmup
             recv = [torch.empty(n, dtype=tdt, device=dev) for _ in range(p)]
             f = coll.coll_allreduce(send, recv, op, defer=True)
             med, p95, _ = stats_us(time_launches(torch, [f], 50, 10)[0])
+            cold = []
+            for i in range(30):
+                scratch.fill_(i & 0xFF)
+                ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                ev[0].record()
+                f()
+                ev[1].record()
+                cold.append(ev)
+            torch.cuda.synchronize()
+            cmed, cp95, _ = stats_us([a.elapsed_time(b) for a, b in cold])
             rows.append(coll_entry(metrics, f"allreduce_small_{oname}", "allreduce", p, n, 4, med, "ring",
                                    {"dtype": dname, "op": oname, "t_p95_us": round(p95, 2),
-                                    "workload": "AllReduce p=4, 2^20 per rank, back to back (warm)"}))
+                                    "t_cold_med_us": round(cmed, 2), "t_cold_p95_us": round(cp95, 2),
+                                    "hbm_GBps_cold": round(2 * p * n * 4 / (cmed * 1e-6) / 1e9, 1),
+                                    "workload": "AllReduce p=4, 2^20 per rank; t_med back to back (warm, "
+                                                "Infinity-Cache resident), t_cold after a 512 MiB overwrite"}))
+        del scratch
 
     # --- latency of every schedule at the batch's small sizes, p = 16 ---------
     # The alpha-beta view of the schedules (hpc/04 page, sections 2.1 and

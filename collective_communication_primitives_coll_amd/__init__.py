@@ -26,6 +26,7 @@ COLL_MAX_RANKS = 64
 COLL_BATCH_CHECK_ALIAS = 1
 
 COLL_U8 = 3
+COLL_A2A_DIRECT, COLL_A2A_LDS_STAGED = 0, 1
 ELEM_BYTES = {COLL_F32: 4, COLL_BF16: 2, COLL_I32: 4, COLL_U8: 1}
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcoll.so")
@@ -68,6 +69,7 @@ def lib() -> ctypes.CDLL:
         "coll_reduce_scatter": [pp, pp, i32, sz, i32, i32, vp],
         "coll_allgather": [pp, pp, i32, sz, i32, vp],
         "coll_alltoall": [pp, pp, i32, sz, i32, vp],
+        "coll_alltoall_algo": [pp, pp, i32, sz, i32, i32, vp],
         "coll_alltoallv": [pp, pp, i32, vp, i64p, i64p, vp, i32, vp],
         "coll_gather": [pp, vp, i32, sz, i32, i32, vp],
         "coll_allreduce_premul": [pp, pp, i32, sz, i32, ctypes.POINTER(ctypes.c_float), i32, vp],
@@ -324,6 +326,22 @@ def coll_alltoall(send, recv, n_block: int | None = None, dtype: int | None = No
     r, k2 = _ptr_array(recv)
     return _run("coll_alltoall", (s, r, p, int(n_block), dt, _stream(stream)), "coll_alltoall", defer,
                 (k1, k2))
+
+
+def coll_alltoall_algo(send, recv, algo: int, n_block: int | None = None, dtype: int | None = None, stream=None,
+                       defer: bool = False):
+    """coll_alltoall with an explicit data path (COLL_A2A_DIRECT or
+    COLL_A2A_LDS_STAGED)."""
+    p = len(send)
+    dt = _dtype_of(send[0], dtype)
+    if n_block is None:
+        n_block = _numel(send[0], None) // p
+    _same_dtype([*send, *recv], dt)
+    _check_sizes([*send, *recv], p * n_block, "alltoall")
+    s, k1 = _ptr_array(send)
+    r, k2 = _ptr_array(recv)
+    return _run("coll_alltoall_algo", (s, r, p, int(n_block), dt, int(algo), _stream(stream)),
+                "coll_alltoall_algo", defer, (k1, k2))
 
 
 def coll_gather(send, recv_root, root: int, n: int | None = None, dtype: int | None = None, stream=None,

@@ -22,6 +22,7 @@ SOURCES = [
     "coll_api.cpp",
     "reduce_kernels.hip",
     "copy_kernels.hip",
+    "a2a_lds_kernels.hip",
     "ring_literal.hip",
     "batch_kernels.hip",
     "moe_kernels.hip",

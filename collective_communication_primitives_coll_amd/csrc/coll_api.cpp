@@ -416,7 +416,13 @@ COLL_EXPORT coll_status_t coll_allgather(const void* const* send, void* const* r
 
 COLL_EXPORT coll_status_t coll_alltoall(const void* const* send, void* const* recv, int p, size_t n_block,
                                         coll_dtype_t dtype, void* stream) {
+  return coll_alltoall_algo(send, recv, p, n_block, dtype, COLL_A2A_DIRECT, stream);
+}
+
+COLL_EXPORT coll_status_t coll_alltoall_algo(const void* const* send, void* const* recv, int p, size_t n_block,
+                                             coll_dtype_t dtype, coll_a2a_algo_t algo, void* stream) {
   if (p < 1 || p > kMaxRanks || !dtype_ok(dtype)) return COLL_ERR_INVALID_ARG;
+  if (algo != COLL_A2A_DIRECT && algo != COLL_A2A_LDS_STAGED) return COLL_ERR_INVALID_ARG;
   if (n_block == 0) return COLL_OK;
   size_t bytes;
   if (!mul_ok(n_block, dsize(dtype), (size_t)p * p, &bytes)) return COLL_ERR_INVALID_ARG;
@@ -434,6 +440,8 @@ COLL_EXPORT coll_status_t coll_alltoall(const void* const* send, void* const* re
   coll::RankPtrs P = make_ptrs(send, p, recv, p);
   coll::CopyGeom g{n_block, p, coll::kCopyAllToAll, common_mis(send, p),
                    common_mis((const void* const*)recv, p)};
+  if (algo == COLL_A2A_LDS_STAGED && coll::can_stage_alltoall((int)dsize(dtype), g))
+    return finish(coll::launch_alltoall_lds((int)dsize(dtype), P, g, grid, stream));
   return finish(coll::launch_copy((int)dsize(dtype), P, g, grid, stream));
 }
 

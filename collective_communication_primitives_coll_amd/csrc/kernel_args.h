@@ -186,6 +186,10 @@ int launch_reduce(int dtype, int op, int order, const RankPtrs& ptrs, const Redu
                   int max_grid, void* stream);
 int launch_copy(int elem_bytes, const RankPtrs& ptrs, const CopyGeom& g, int max_grid, void* stream);
 int launch_alltoallv(int elem_bytes, const RankPtrs& ptrs, const A2avArgs& a, int grid, void* stream);
+// All-to-All staged through LDS; only for layouts where every block shares
+// one 16-byte misalignment (can_stage_alltoall).
+bool can_stage_alltoall(int elem_bytes, const CopyGeom& g);
+int launch_alltoall_lds(int elem_bytes, const RankPtrs& ptrs, const CopyGeom& g, int max_grid, void* stream);
 int launch_ring_step(int dtype, int op, const RankPtrs& ptrs, const RingStepGeom& g, int max_grid,
                      void* stream);
 int launch_batch(const BatchArgs& a, int grid, void* stream);

@@ -174,6 +174,24 @@ coll_status_t coll_allgather(const void* const* send, void* const* recv, int p, 
 coll_status_t coll_alltoall(const void* const* send, void* const* recv, int p, size_t n_block,
                             coll_dtype_t dtype, void* stream);
 
+/* How the All-to-All block transpose moves its bytes.  Both give the same
+ * result (a bit copy).
+ * DIRECT: 16-byte vectors go from the source block to the destination
+ *   block through registers (what coll_alltoall does).
+ * LDS_STAGED: every vector is staged in LDS on the way: gfx950 loads
+ *   global memory straight into LDS, each wave alternating two private
+ *   stages of 8 KiB, one filling while the other is written out.  It needs
+ *   every block to share one 16-byte misalignment: the send and the recv
+ *   buffers share a misalignment and n_block * element size is a multiple
+ *   of 16.  Other layouts run the DIRECT kernel. */
+typedef enum { COLL_A2A_DIRECT = 0, COLL_A2A_LDS_STAGED = 1 } coll_a2a_algo_t;
+
+/* All-to-All ([A] 1.6) with an explicit data path (see coll_a2a_algo_t);
+ * arguments, layout and errors as coll_alltoall, plus
+ * COLL_ERR_INVALID_ARG for an unknown algo. */
+coll_status_t coll_alltoall_algo(const void* const* send, void* const* recv, int p, size_t n_block,
+                                 coll_dtype_t dtype, coll_a2a_algo_t algo, void* stream);
+
 /* Gather ([C] section 4.3; [A] note after 1.6): AllGather whose result
  * only the root keeps.  send[s] holds n elements, recv_root holds p*n;
  * recv_root[s*n + j] = send[s][j] (rank-order concatenation).  root in

@@ -145,6 +145,12 @@ def test_moe_alltoall_full_size(env):
     expect = ref.alltoall(hx)
     for jr in range(p):
         assert_bits_equal(to_host(recv[jr], BF16), expect[jr], f"A2A full size dest {jr}")
+    for r in recv:
+        r.zero_()
+    coll.coll_alltoall_algo(send, recv, coll.COLL_A2A_LDS_STAGED, per // p)
+    torch.cuda.synchronize()
+    for jr in range(p):
+        assert_bits_equal(to_host(recv[jr], BF16), expect[jr], f"A2A LDS-staged full size dest {jr}")
     del recv, expect
     counts = inputs.moe_token_counts(p, tokens) * hidden
     cols = counts.sum(axis=0)

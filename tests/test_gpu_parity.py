@@ -511,6 +511,66 @@ def test_alltoall(coll, p, m, dtype):
         assert_bits_equal(to_host(back[i], dtype), hx[i], "A2A twice")
 
 
+# The LDS-staged data path: wave tiles of 512 vectors (8 KiB), full and
+# partial, many tiles per block, and block sizes that are not a multiple of
+# 16 bytes (those run the direct kernel).
+@pytest.mark.parametrize("p,m", [(1, 8), (2, 4096), (3, 8 * 1000), (4, 8 * 512 * 3 + 8), (8, 7168),
+                                 (8, 7168 * 8 + 24), (16, 40), (64, 16), (5, 7), (8, 7168 + 5)])
+@pytest.mark.parametrize("dtype", [BF16, F32])
+def test_alltoall_lds_staged(coll, p, m, dtype):
+    hx = gen(p, p * m, dtype, 16)
+    send = [to_dev(x, dtype) for x in hx]
+    recv = [empty(p * m, dtype, fill=0) for _ in range(p)]
+    coll.coll_alltoall_algo(send, recv, coll.COLL_A2A_LDS_STAGED)
+    sync()
+    expect = ref.alltoall(hx)
+    for j in range(p):
+        assert_bits_equal(to_host(recv[j], dtype), expect[j], f"A2A LDS p={p} m={m} j={j}")
+    back = [empty(p * m, dtype, fill=0) for _ in range(p)]
+    coll.coll_alltoall_algo(recv, back, coll.COLL_A2A_LDS_STAGED)
+    sync()
+    for i in range(p):
+        assert_bits_equal(to_host(back[i], dtype), hx[i], "A2A LDS twice")
+
+
+@pytest.mark.parametrize("soff,roff", [(1, 1), (3, 3), (1, 2), (0, 5)])
+def test_alltoall_lds_staged_misaligned(coll, soff, roff):
+    """Bases off a 16-byte boundary: a shared misalignment takes the staged
+    vector path with element-wise heads and tails; differing ones the
+    direct kernel.  Bytes outside the receive views stay untouched."""
+    p, m = 4, 8 * 700
+    hx = gen(p, p * m, BF16, 17)
+    keep = [upload_offset(x, BF16, soff) for x in hx]
+    send = [v for _, v in keep]
+    outs = [empty(p * m + roff + 8, BF16, fill=0x1234) for _ in range(p)]
+    recv = [o[roff:roff + p * m] for o in outs]
+    coll.coll_alltoall_algo(send, recv, coll.COLL_A2A_LDS_STAGED)
+    sync()
+    expect = ref.alltoall(hx)
+    for j in range(p):
+        full = to_host(outs[j], BF16)
+        assert_bits_equal(full[roff:roff + p * m], expect[j], f"A2A LDS misaligned j={j}")
+        assert np.all(full[:roff] == 0x1234) and np.all(full[roff + p * m:] == 0x1234), "guard bytes"
+
+
+def test_alltoall_lds_staged_bytes_and_rejections(coll):
+    import torch
+    p, n = 6, 16 * 333
+    hx = [np.random.default_rng(500 + r).integers(0, 256, p * n).astype(np.uint8) for r in range(p)]
+    send = [torch.from_numpy(x).cuda() for x in hx]
+    recv = [_u8(p * n) for _ in range(p)]
+    coll.coll_alltoall_algo(send, recv, coll.COLL_A2A_LDS_STAGED, n)
+    sync()
+    for j, e in enumerate(ref.alltoall(hx)):
+        assert_bits_equal(recv[j].cpu().numpy(), e, f"u8 alltoall LDS {j}")
+    with pytest.raises(coll.CollError) as ei:
+        coll.coll_alltoall_algo(send, recv, 7, n)
+    assert ei.value.status == coll.COLL_ERR_INVALID_ARG
+    with pytest.raises(coll.CollError) as ei:
+        coll.coll_alltoall_algo(send, send, coll.COLL_A2A_LDS_STAGED, n)
+    assert ei.value.status == coll.COLL_ERR_ALIAS
+
+
 def _counts(p, rng, scale, zero_frac=0.25):
     c = rng.integers(0, scale, size=(p, p)).astype(np.int64)
     c[rng.random((p, p)) < zero_frac] = 0
