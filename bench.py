@@ -241,8 +241,21 @@ def cpu_baseline(wl, cpu_seconds: float):
                    f"{reps} repetitions in {el:.1f} s; GB/s of the same algorithmic HBM bytes"),
         "ms_per_sample": round(per * 1e3, 1),
         "host_cpus": os.cpu_count(),
+        "cpu_model": host_cpu_model(),
         "gpu_matches_oracle_on_sample": bool(agree),
     }
+
+
+def host_cpu_model() -> str | None:
+    """The host CPU's model name from /proc/cpuinfo (None if unreadable)."""
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def graph_us_per_call(torch, coll, send, recv, algo, calls=10, replays=20):

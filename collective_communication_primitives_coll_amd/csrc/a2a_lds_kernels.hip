@@ -54,8 +54,8 @@ COLL_STREAM_KERNEL void alltoall_lds_kernel(RankPtrs ptrs, CopyGeom g, uint64_t 
   const uint64_t n = g.n;
   const int lane = (int)(threadIdx.x & 63);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // Tile counts stay below 2^32: a wave tile covers 8 KiB and a call at
-  // most the device's memory, so 32-bit division suffices.
+  // The host sends calls with 2^32 or more wave tiles to the direct
+  // kernel, so tile indices fit 32 bits (and 32-bit division).
   const uint32_t nw = gridDim.x * (uint32_t)kWavesPerWg;
   const uint32_t wid = blockIdx.x * (uint32_t)kWavesPerWg + (uint32_t)wave;
   const uint32_t tps = (uint32_t)((nvec + kA2aLdsTV - 1) / kA2aLdsTV);  // wave tiles per segment
@@ -133,8 +133,12 @@ COLL_STREAM_KERNEL void alltoall_lds_kernel(RankPtrs ptrs, CopyGeom g, uint64_t 
 // Host side.  Returns hipErrorInvalidValue when the layout needs the
 // direct kernel (the caller checks can_stage_alltoall first).
 bool can_stage_alltoall(int elem_bytes, const CopyGeom& g) {
-  return g.src_mis >= 0 && g.src_mis == g.dst_mis && g.src_mis % elem_bytes == 0 &&
-         (g.n * (uint64_t)elem_bytes) % 16 == 0;
+  if (!(g.src_mis >= 0 && g.src_mis == g.dst_mis && g.src_mis % elem_bytes == 0 &&
+        (g.n * (uint64_t)elem_bytes) % 16 == 0))
+    return false;
+  // the kernel counts wave tiles in 32 bits
+  const uint64_t tiles = (uint64_t)g.p * g.p * ((g.n * (uint64_t)elem_bytes / 16 + kA2aLdsTV - 1) / kA2aLdsTV);
+  return tiles < (uint64_t{1} << 32);
 }
 
 int launch_alltoall_lds(int elem_bytes, const RankPtrs& ptrs, const CopyGeom& g, int max_grid, void* stream) {
