@@ -53,13 +53,18 @@ __device__ __forceinline__ void batch_run(const BatchCall& bc, const void* const
     if (hi > bc.n) hi = bc.n;
     const uint64_t len = hi - lo;
     if (len) {
+      // the call's pointers at constant offsets, then the ring rotation
+      // of chunk c in registers
       const S* src[P];
       S* dst[P];
 #pragma unroll
       for (int k = 0; k < P; ++k) {
-        src[k] = as_global((const S*)ld_const(&pt[(c + 1 + k) % P])) + lo;
+        src[k] = (const S*)ld_const(&pt[k]);
         dst[k] = as_global((S*)ld_const(&pt[P + k])) + lo;
       }
+      rotate_left<P>(src, (c + 1) & (P - 1));
+#pragma unroll
+      for (int k = 0; k < P; ++k) src[k] = as_global(src[k]) + lo;
       const int mis = bc.mis < 0 ? -1 : (int)((bc.mis + lo * T::B) & 15);
       const SegSpan sp = seg_span<T::B>(len, mis);
       if (!sp.vec) {

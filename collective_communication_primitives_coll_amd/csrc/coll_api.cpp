@@ -44,9 +44,12 @@ std::atomic<int> g_wg_per_cu{0};
 // move one token row (a few KiB) per workgroup step and need more
 // workgroups to keep enough bytes in flight; the FP8 pack and dequant,
 // with a short conversion step between their loads and stores, gain a
-// few percent more at sixteen.
-enum Family { kFamReduce = 0, kFamCopy = 1, kFamRow = 2, kFamFp8 = 3 };
-constexpr int kDefaultWgPerCu[4] = {1, 2, 8, 16};
+// few percent more at sixteen.  The direct FP8 dispatch (quantizing
+// straight into the receive buffers, placement tables staged per
+// workgroup) measured best at two: 221 us against 237 us at sixteen for
+// 4096 x 7168 tokens, p = 8, top-2.
+enum Family { kFamReduce = 0, kFamCopy = 1, kFamRow = 2, kFamFp8 = 3, kFamFp8Direct = 4 };
+constexpr int kDefaultWgPerCu[5] = {1, 2, 8, 16, 2};
 
 int current_device(int* dev) { return (int)hipGetDevice(dev); }
 
@@ -977,7 +980,7 @@ COLL_EXPORT coll_status_t coll_moe_dispatch_fp8(const void* const* tokens, const
   if (e) return hip_fail(e);
   if (direct_lds_bytes(p) > (size_t)g_dev[dev].lds_per_block.load()) return COLL_ERR_UNSUPPORTED;
   int grid;
-  e = max_grid(&grid, kFamFp8);
+  e = max_grid(&grid, kFamFp8Direct);
   if (e) return hip_fail(e);
   coll::MoeDirectArgs a =
       direct_args(tokens, dest, recv, loc, counts_dev, status_dev, p, tokens_per_rank, k, hidden, recv_cap, R);

@@ -12,21 +12,11 @@
 //   fixed  the root buffer at the segment offset (Reduce),
 //   owner  rank c's buffer from its start (ReduceScatter, block c lands on
 //          rank c: "集合通信：原语、算法、NCCL 实现与拓扑映射", section 1.5).
-// The rotated source list of a segment is read from the kernel arguments
-// once per segment and kept in scalar registers.
+// A segment's sources are read from the kernel arguments with constant
+// offsets and put in the schedule's order in registers (list_for_chunk).
 #include "reduce_tile.h"
 
 namespace coll {
-
-// Rank listed k-th for chunk c: the ring rotation x_{c+1}, ..., x_c, or
-// rank order for the trees (mirrored for the double binary tree's second
-// half of the chunks).
-template <int ORD, int P>
-__device__ __forceinline__ int listed_rank(int c, int k) {
-  if constexpr (ORD == kOrdRing) return (c + 1 + k) % P;
-  else if constexpr (ORD == kOrdDBT) return c < P / 2 ? k : P - 1 - k;
-  else return k;
-}
 
 __device__ __forceinline__ void chunk_range(const ReduceGeom& g, int c, uint64_t* lo, uint64_t* len) {
   uint64_t a = (uint64_t)c * g.stride;
@@ -57,7 +47,10 @@ COLL_STREAM_KERNEL void reduce_kernel(RankPtrs ptrs, ReduceGeom g) {
     }
     const S* src[P];
 #pragma unroll
-    for (int k = 0; k < P; ++k) src[k] = (const S*)ptrs.src[listed_rank<ORD, P>(c, k)] + lo;
+    for (int k = 0; k < P; ++k) src[k] = (const S*)ptrs.src[k];
+    list_for_chunk<ORD, P>(src, c);
+#pragma unroll
+    for (int k = 0; k < P; ++k) src[k] += lo;
     S* dst[ND];
     if constexpr (ALL) {
 #pragma unroll
@@ -69,7 +62,8 @@ COLL_STREAM_KERNEL void reduce_kernel(RankPtrs ptrs, ReduceGeom g) {
     }
     Scales<P> sc;
 #pragma unroll
-    for (int k = 0; k < P; ++k) sc.s[k] = OP == kPreMul ? g.scale[listed_rank<ORD, P>(c, k)] : 1.0f;
+    for (int k = 0; k < P; ++k) sc.s[k] = OP == kPreMul ? g.scale[k] : 1.0f;
+    if constexpr (OP == kPreMul) list_for_chunk<ORD, P>(sc.s, c);
     base += reduce_segment<DT, OP, P, ORD, ND, ALL>(src, dst, len, mis, base, sc, P);
   }
 }

@@ -34,6 +34,46 @@ struct ReduceUnroll {
   static constexpr int value = raw < 1 ? 1 : (raw > 8 ? 8 : raw);
 };
 
+// a[k] <- a[(k + s) mod P] for a wave-uniform s in [0, P), P a power of
+// two: log2(P) conditional rotations by 1, 2, 4, ... whose indices are all
+// compile-time constants, so the array stays in scalar registers and its
+// elements can be fetched with constant offsets (wide scalar loads issued
+// together).  Indexing the source array with a run-time rank instead makes
+// the compiler fetch every element with its own dependent scalar load.
+template <int P, typename T>
+__device__ __forceinline__ void rotate_left(T (&a)[P], int s) {
+  static_assert((P & (P - 1)) == 0, "rotate_left needs a power-of-two length");
+#pragma unroll
+  for (int b = 1; b < P; b <<= 1) {
+    const bool on = (s & b) != 0;
+    T t[P];
+#pragma unroll
+    for (int k = 0; k < P; ++k) t[k] = a[(k + b) & (P - 1)];
+#pragma unroll
+    for (int k = 0; k < P; ++k) a[k] = on ? t[k] : a[k];
+  }
+}
+
+// a[k] <- a[P - 1 - k] when `on` (wave-uniform).
+template <int P, typename T>
+__device__ __forceinline__ void reverse_if(T (&a)[P], bool on) {
+  T t[P];
+#pragma unroll
+  for (int k = 0; k < P; ++k) t[k] = a[P - 1 - k];
+#pragma unroll
+  for (int k = 0; k < P; ++k) a[k] = on ? t[k] : a[k];
+}
+
+// Per-rank values (pointers, scales) a[r], indexed by rank, reordered in
+// place into the order in which chunk c lists its operands: the ring
+// rotation x_{c+1}, ..., x_c, or rank order for the trees (mirrored for
+// the double binary tree's second half of the chunks).
+template <int ORD, int P, typename T>
+__device__ __forceinline__ void list_for_chunk(T (&a)[P], int c) {
+  if constexpr (ORD == kOrdRing) rotate_left<P>(a, (c + 1) & (P - 1));
+  else if constexpr (ORD == kOrdDBT) reverse_if<P>(a, c >= P / 2);
+}
+
 // Per-operand scales of a pre-multiplied sum, in the order the operands
 // are listed.
 template <int P>

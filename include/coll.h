@@ -402,8 +402,10 @@ int coll_last_hip_error(void);
 int coll_version(void);
 
 /* Occupancy target used to size grids: workgroups (256 threads) per
- * compute unit; 0 restores the default (8).  Applies to later calls from
- * every thread; results do not depend on it. */
+ * compute unit, for every kernel; 0 restores each kernel family's
+ * measured default (1 for reductions, 2 for copies and the direct FP8
+ * dispatch, 8 for the MoE row kernels, 16 for the FP8 pack and dequant).
+ * Applies to later calls from every thread; results do not depend on it. */
 void coll_set_grid_limit(int workgroups_per_cu);
 
 /* Release library-owned device and pinned host memory (batch descriptors).
