@@ -18,6 +18,14 @@
 
 namespace coll {
 
+// Rank listed k-th for chunk c (the order list_for_chunk produces).
+template <int ORD, int P>
+__device__ __forceinline__ int listed_rank(int c, int k) {
+  if constexpr (ORD == kOrdRing) return (c + 1 + k) & (P - 1);
+  else if constexpr (ORD == kOrdDBT) return c < P / 2 ? k : P - 1 - k;
+  else return k;
+}
+
 __device__ __forceinline__ void chunk_range(const ReduceGeom& g, int c, uint64_t* lo, uint64_t* len) {
   uint64_t a = (uint64_t)c * g.stride;
   uint64_t b = a + g.stride;
@@ -60,10 +68,12 @@ COLL_STREAM_KERNEL void reduce_kernel(RankPtrs ptrs, ReduceGeom g) {
     } else {
       dst[0] = (S*)ptrs.dst[0] + lo;
     }
+    // The scales (pre-multiplied sums only) are indexed by the listed rank
+    // directly: reordering them in registers as the pointers are left an
+    // unused stack reservation in some kernels.
     Scales<P> sc;
 #pragma unroll
-    for (int k = 0; k < P; ++k) sc.s[k] = OP == kPreMul ? g.scale[k] : 1.0f;
-    if constexpr (OP == kPreMul) list_for_chunk<ORD, P>(sc.s, c);
+    for (int k = 0; k < P; ++k) sc.s[k] = OP == kPreMul ? g.scale[listed_rank<ORD, P>(c, k)] : 1.0f;
     base += reduce_segment<DT, OP, P, ORD, ND, ALL>(src, dst, len, mis, base, sc, P);
   }
 }
