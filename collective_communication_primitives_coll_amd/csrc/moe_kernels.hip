@@ -10,12 +10,13 @@
 //
 // Index pass (one 1024-thread workgroup per source rank): every wave owns
 // a contiguous run of the rank's assignments.  It counts destinations 64
-// assignments at a time, grouping equal destinations of a group with
-// ballots, into per-lane registers (lane d counts destination d); the
-// per-wave counts are turned into exclusive offsets (by destination, then
-// by wave); a second walk gives every assignment its packed row, stable in
-// assignment order.  Destinations outside [0, p)
-// reject the rank: its counts are 0 and every pos is -1.
+// assignments at a time with ballots (one per destination for rank counts
+// 2, 4, 8 and 16; otherwise one per distinct destination of the group,
+// lane d counting destination d).  The per-wave counts are turned into
+// exclusive offsets (by destination, then by wave); a second walk gives
+// every assignment its packed row, stable in assignment order.
+// Destinations outside [0, p) reject the rank: its counts are 0 and every
+// pos is -1.
 //
 // Payload copy and combine: one wave per token row, rows spread over every
 // wave of the grid, so a workgroup keeps four rows in flight.  The copy
@@ -31,6 +32,13 @@ constexpr int kIdxThreads = 1024;
 constexpr int kIdxWaves = kIdxThreads / 64;
 constexpr int kIdxBatch = 8;  // groups of 64 assignments whose destinations a wave loads together
 
+// PC: the rank count when it is 2, 4, 8 or 16 (0: any).  With a known,
+// small rank count a group of 64 assignments is counted and placed with
+// one compare-and-ballot per destination, the per-destination counts and
+// running offsets in scalar registers.  Otherwise the wave elects one
+// destination of the group at a time (a chain of dependent lane reads and
+// ballots) and lane d keeps destination d's count.
+template <int PC>
 __global__ __launch_bounds__(kIdxThreads) void moe_index_kernel(MoeIndexArgs a) {
   __shared__ int wofs[kIdxWaves][kMaxRanks];  // per-wave counts, then offsets
   __shared__ int total[kMaxRanks];
@@ -53,6 +61,9 @@ __global__ __launch_bounds__(kIdxThreads) void moe_index_kernel(MoeIndexArgs a) 
   // together).  p <= 64, so lane d keeps the wave's count for destination
   // d in a register.
   int cnt = 0;
+  int cntd[PC > 0 ? PC : 1];
+#pragma unroll
+  for (int dd = 0; dd < (PC > 0 ? PC : 1); ++dd) cntd[dd] = 0;
   for (uint64_t b0 = lo; b0 < hi; b0 += 64 * kIdxBatch) {
     int dv[kIdxBatch];
 #pragma unroll
@@ -67,15 +78,25 @@ __global__ __launch_bounds__(kIdxThreads) void moe_index_kernel(MoeIndexArgs a) 
         bad = 1;
         d = -1;
       }
-      uint64_t rem = __ballot(d >= 0);
-      while (rem) {
-        const int leader = __ffsll((unsigned long long)rem) - 1;
-        const int dl = __builtin_amdgcn_readlane(d, leader);
-        const uint64_t m = __ballot(d == dl) & rem;
-        if (lane == dl) cnt += __popcll(m);
-        rem &= ~m;
+      if constexpr (PC > 0) {
+#pragma unroll
+        for (int dd = 0; dd < PC; ++dd) cntd[dd] += __popcll(__ballot(d == dd));
+      } else {
+        uint64_t rem = __ballot(d >= 0);
+        while (rem) {
+          const int leader = __ffsll((unsigned long long)rem) - 1;
+          const int dl = __builtin_amdgcn_readlane(d, leader);
+          const uint64_t m = __ballot(d == dl) & rem;
+          if (lane == dl) cnt += __popcll(m);
+          rem &= ~m;
+        }
       }
     }
+  }
+  if constexpr (PC > 0) {
+#pragma unroll
+    for (int dd = 0; dd < PC; ++dd)
+      if (lane == dd) cnt = cntd[dd];
   }
   if (lane < p) wofs[w][lane] = cnt;
   __syncthreads();
@@ -109,9 +130,12 @@ __global__ __launch_bounds__(kIdxThreads) void moe_index_kernel(MoeIndexArgs a) 
     for (uint64_t x = tid; x < A; x += kIdxThreads) pos[x << a.pos_shift] = -1;
     return;
   }
-  // pass 2: packed row of every assignment; lane d holds the wave's next
-  // row for destination d
+  // pass 2: packed row of every assignment; lane d (or, with a known rank
+  // count, scalar register d) holds the wave's next row for destination d
   int next = lane < p ? wofs[w][lane] : 0;
+  int nextd[PC > 0 ? PC : 1];
+#pragma unroll
+  for (int dd = 0; dd < (PC > 0 ? PC : 1); ++dd) nextd[dd] = PC > 0 ? wofs[w][dd] : 0;
   for (uint64_t b0 = lo; b0 < hi; b0 += 64 * kIdxBatch) {
     int dv[kIdxBatch];
 #pragma unroll
@@ -124,15 +148,24 @@ __global__ __launch_bounds__(kIdxThreads) void moe_index_kernel(MoeIndexArgs a) 
       const uint64_t x = b0 + (uint64_t)i * 64 + lane;
       const int d = dv[i];
       int mine = 0;
-      uint64_t rem = __ballot(d >= 0);
-      while (rem) {
-        const int leader = __ffsll((unsigned long long)rem) - 1;
-        const int dl = __builtin_amdgcn_readlane(d, leader);
-        const uint64_t m = __ballot(d == dl) & rem;
-        const int at = __builtin_amdgcn_readlane(next, dl);
-        if (d == dl) mine = at + __popcll(m & below);
-        if (lane == dl) next += __popcll(m);
-        rem &= ~m;
+      if constexpr (PC > 0) {
+#pragma unroll
+        for (int dd = 0; dd < PC; ++dd) {
+          const uint64_t m = __ballot(d == dd);
+          if (d == dd) mine = nextd[dd] + __popcll(m & below);
+          nextd[dd] += __popcll(m);
+        }
+      } else {
+        uint64_t rem = __ballot(d >= 0);
+        while (rem) {
+          const int leader = __ffsll((unsigned long long)rem) - 1;
+          const int dl = __builtin_amdgcn_readlane(d, leader);
+          const uint64_t m = __ballot(d == dl) & rem;
+          const int at = __builtin_amdgcn_readlane(next, dl);
+          if (d == dl) mine = at + __popcll(m & below);
+          if (lane == dl) next += __popcll(m);
+          rem &= ~m;
+        }
       }
       if (d >= 0) pos[x << a.pos_shift] = mine;
     }
@@ -443,7 +476,14 @@ COLL_STREAM_KERNEL void moe_combine_kernel(MoeRowArgs a) {
 // Host-side launch
 // ---------------------------------------------------------------------------
 int launch_moe_index(const MoeIndexArgs& a, void* stream) {
-  hipLaunchKernelGGL(moe_index_kernel, dim3(a.p), dim3(kIdxThreads), 0, (hipStream_t)stream, a);
+  hipStream_t s = (hipStream_t)stream;
+  switch (a.p) {
+    case 2: hipLaunchKernelGGL(moe_index_kernel<2>, dim3(a.p), dim3(kIdxThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL(moe_index_kernel<4>, dim3(a.p), dim3(kIdxThreads), 0, s, a); break;
+    case 8: hipLaunchKernelGGL(moe_index_kernel<8>, dim3(a.p), dim3(kIdxThreads), 0, s, a); break;
+    case 16: hipLaunchKernelGGL(moe_index_kernel<16>, dim3(a.p), dim3(kIdxThreads), 0, s, a); break;
+    default: hipLaunchKernelGGL(moe_index_kernel<0>, dim3(a.p), dim3(kIdxThreads), 0, s, a); break;
+  }
   return (int)hipGetLastError();
 }
 
