@@ -160,6 +160,18 @@ def moe_routes(p: int, tokens: int, k: int, workload: int = WL_MOE_A2A, extra: i
     return [rng_for(workload, r, 2000 + extra, k).integers(0, p, tokens * k).astype(np.int32) for r in range(p)]
 
 
+def moe_routes_skewed(p: int, tokens: int, k: int, alpha: float, extra: int = 0) -> list[np.ndarray]:
+    """Per rank, int32 [tokens*k]: destinations drawn from probabilities that
+    are themselves drawn from a symmetric Dirichlet(alpha) per source rank;
+    small alpha concentrates most assignments on a few hot destinations."""
+    out = []
+    for r in range(p):
+        g = rng_for(WL_TEST, r, 4000 + extra, k)
+        prob = g.dirichlet(np.full(p, alpha))
+        out.append(g.choice(p, size=tokens * k, p=prob).astype(np.int32))
+    return out
+
+
 def moe_weights(p: int, tokens: int, k: int, workload: int = WL_MOE_A2A, extra: int = 0) -> list[np.ndarray]:
     """Per rank, fp32 [tokens*k] combine weights uniform in [0, 1)."""
     return [rng_for(workload, r, 3000 + extra, k).random(tokens * k, dtype=np.float32) for r in range(p)]

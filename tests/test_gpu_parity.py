@@ -707,6 +707,34 @@ def test_moe_pack(coll, p, T, k, H, dtype):
         assert_bits_equal(to_host(packed[i], dtype), epk, f"packed rank {i}")
 
 
+@pytest.mark.parametrize("p", [2, 4, 5, 8, 16])
+@pytest.mark.parametrize("routing", ["one_hot_destination", "dirichlet_0.3"])
+def test_moe_pack_skewed_routing(coll, p, routing):
+    """Hot destinations: every assignment to one rank, or Dirichlet-skewed
+    probabilities; 9000 assignments per rank, so each wave of the index
+    pass walks several batches."""
+    import torch
+    T, k, H = 4500, 2, 16
+    toks = inputs.rank_buffers(inputs.WL_TEST, p, T * H, BF16, dist="normal", extra=(77, p))
+    if routing == "one_hot_destination":
+        routes = [np.full(T * k, (r + 1) % p, dtype=np.int32) for r in range(p)]
+    else:
+        routes = inputs.moe_routes_skewed(p, T, k, 0.3, extra=p)
+    dtok = [to_dev(x, BF16) for x in toks]
+    ddest = [_i32dev(r) for r in routes]
+    packed = [empty(T * k * H, BF16, fill=0x1111) for _ in range(p)]
+    pos = [torch.full((T * k,), -5, dtype=torch.int32, device="cuda") for _ in range(p)]
+    counts = torch.full((p * p,), -1, dtype=torch.int64, device="cuda")
+    coll.coll_moe_pack(dtok, ddest, packed, pos, counts, k, H)
+    sync()
+    c = counts.cpu().numpy().reshape(p, p)
+    for i in range(p):
+        ec, epos, epk = ref.moe_pack(toks[i], routes[i], k, H, p)
+        assert list(c[i]) == list(ec), f"counts rank {i}"
+        assert pos[i].cpu().numpy().tolist() == epos.tolist(), f"pos rank {i}"
+        assert_bits_equal(to_host(packed[i], BF16), epk, f"packed rank {i}")
+
+
 def test_moe_pack_rejects_bad_destination(coll):
     import torch
     p, T, k, H = 4, 33, 2, 16
