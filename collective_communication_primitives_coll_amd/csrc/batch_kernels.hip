@@ -23,10 +23,22 @@ namespace coll {
 
 constexpr int kWave = 64;  // lanes of a wave: the batch's unit of work
 
+// Vectors per lane of a batch tile: 64 / P, at most 8 (4 at p = 16, 278
+// VGPRs, no spills).  A wave tile is small (64 lanes), so its fixed cost
+// (2P 64-bit addresses, the bounds and the loop) is paid per few hundred
+// bytes; larger tiles amortise it.  The 10,000-call p = 16 plan took
+// 14.56 ms at 1 vector per lane (the single-call AllReduce's 16 / P),
+// 13.65 ms at 2 and 13.21 ms at 4; 8 spills.
+template <int P>
+struct BatchUnroll {
+  static constexpr int raw = P == 0 ? 1 : 64 / P;
+  static constexpr int value = raw < 1 ? 1 : (raw > 8 ? 8 : raw);
+};
+
 // Elements of a batch tile: one wave's share, U vectors per lane.
 template <int DT, int P>
 __host__ __device__ constexpr uint64_t batch_tile_elems() {
-  return (uint64_t)ReduceUnroll<P, true>::value * kWave * Traits<DT>::V;
+  return (uint64_t)BatchUnroll<P>::value * kWave * Traits<DT>::V;
 }
 
 // Tiles [from, to) of one call (tile indices local to the call), walked
@@ -37,7 +49,7 @@ __device__ __forceinline__ void batch_run(const BatchCall& bc, const void* const
                                           uint64_t to, int lane) {
   using T = Traits<DT>;
   using S = typename T::S;
-  constexpr int U = ReduceUnroll<P, true>::value;
+  constexpr int U = BatchUnroll<P>::value;
   constexpr uint64_t TV = (uint64_t)U * kWave;
   constexpr int V = T::V;
   const uint64_t tpc = bc.tiles_per_chunk;
