@@ -1222,7 +1222,7 @@ COLL_EXPORT const char* coll_status_string(coll_status_t s) {
 
 COLL_EXPORT int coll_last_hip_error(void) { return g_last_hip; }
 
-COLL_EXPORT int coll_version(void) { return 100; }
+COLL_EXPORT int coll_version(void) { return 200; }
 
 COLL_EXPORT void coll_set_grid_limit(int workgroups_per_cu) {
   g_wg_per_cu.store(workgroups_per_cu > 0 ? workgroups_per_cu : 0, std::memory_order_relaxed);
