@@ -164,6 +164,47 @@ def test_allreduce_doubling_schedules_bitexact(coll, p, dtype, algo, sim):
             assert_bits_equal(to_host(recv[r], dtype), expect[r], f"{algo} p={p} dt={dtype} op={op} r={r}")
 
 
+@pytest.mark.parametrize("p", [2, 4, 8, 16])
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_allreduce_small_call_boundary(coll, p, dtype):
+    """AllReduces whose tiles fit the grid (one 256-thread workgroup per CU)
+    run one tile per workgroup; larger ones the general kernel.  Sizes at,
+    just above and below that boundary and at one tile per chunk, a
+    misaligned base, ring and tree orders: bit-exact."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    at = 32768 if dtype == BF16 else 16384  # 64 KiB per rank: one tile per chunk
+    edge = cus * at // p                      # tiles per chunk * p == CUs
+    for n in (at, at + 1, at - 3, 5, p * 64 + 1, edge, edge + 1, edge - 3):
+        hx = gen(p, n, dtype, 70 + n % 97)
+        send = [to_dev(x, dtype) for x in hx]
+        recv = [empty(n, dtype, fill=0x5A5A5A5A) for _ in range(p)]
+        coll.coll_allreduce(send, recv, ref.SUM)
+        sync()
+        expect = ref.allreduce(hx, ref.SUM, dtype)
+        for r in range(p):
+            assert_bits_equal(to_host(recv[r], dtype), expect[r], f"AR small p={p} n={n} rank {r}")
+        if dtype != I32 and n <= at + 1:
+            recv = [empty(n, dtype, fill=0x5A5A5A5A) for _ in range(p)]
+            coll.coll_allreduce_algo(send, recv, coll.COLL_ALGO_TREE, ref.SUM)
+            sync()
+            expect = ref.tree_allreduce_simulated(hx, ref.SUM, dtype)
+            for r in range(p):
+                assert_bits_equal(to_host(recv[r], dtype), expect[r], f"AR small tree p={p} n={n} rank {r}")
+    n = at - 8
+    hx = gen(p, n, dtype, 79)
+    keep, send = zip(*[upload_offset(x, dtype, 3) for x in hx])
+    outs = [empty(n + 8, dtype, fill=0x1234) for _ in range(p)]
+    recv = [o[3:3 + n] for o in outs]
+    coll.coll_allreduce(list(send), recv, ref.MAX)
+    sync()
+    expect = ref.allreduce(hx, ref.MAX, dtype)
+    for r in range(p):
+        full = to_host(outs[r], dtype)
+        assert_bits_equal(full[3:3 + n], expect[r], f"AR small misaligned p={p} rank {r}")
+        assert np.all(full[:3] == to_host(empty(3, dtype, fill=0x1234), dtype)), "guard"
+
+
 def test_doubling_schedules_misaligned_and_in_place(coll):
     p, n = 8, 5003
     hx = gen(p, n, F32, 60)
