@@ -94,6 +94,42 @@ COLL_STREAM_KERNEL void pair_copy_kernel(RankPtrs ptrs, CopyGeom g) {
   }
 }
 
+// AllGather calls with at most one tile per workgroup likewise, when
+// every segment shares one 16-byte misalignment (common source and
+// destination misalignment, n * B a multiple of 16): flat tile f is tile
+// f mod tps of segment f / tps (rank s's block, stored to every
+// destination at s * n), instead of a walk over the p segments (p = 16,
+// 4 KiB per rank: 6.4 -> 3.5 us).  Loads through the cache, non-temporal
+// stores, as the walking kernel.
+template <int B, int P>
+COLL_STREAM_KERNEL void allgather_flat_kernel(RankPtrs ptrs, CopyGeom g, uint64_t head, uint64_t nvec, uint64_t tail,
+                                              uint32_t tps) {
+  using W = typename Word<B>::T;
+  constexpr uint64_t V = 16 / B;
+  const uint32_t total = (uint32_t)P * tps;
+  for (uint32_t f = blockIdx.x; f < total; f += gridDim.x) {
+    const uint32_t sgi = f / tps, t = f - sgi * tps;
+    const W* src = (const W*)ptrs.src[sgi];
+    W* dst[P];
+#pragma unroll
+    for (int k = 0; k < P; ++k) dst[k] = (W*)ptrs.dst[k] + (uint64_t)sgi * g.n;
+    const u32x4* vs = reinterpret_cast<const u32x4*>(src + head);
+    auto gdst = [&](int d) -> u32x4* { return reinterpret_cast<u32x4*>(dst[d] + head); };
+    const uint64_t j0 = (uint64_t)t * kCopyTV + threadIdx.x;
+    if ((uint64_t)(t + 1) * kCopyTV <= nvec) copy_vec_tile<false, true, P>(vs, gdst, P, j0, nvec);
+    else if ((uint64_t)t * kCopyTV < nvec) copy_vec_tile<false, false, P>(vs, gdst, P, j0, nvec);
+    if (t == 0 && (head || tail)) {
+      const uint64_t i = threadIdx.x;
+      if (i < head + tail) {
+        const uint64_t x = i < head ? i : head + nvec * V + (i - head);
+        const W w = ld1<false>(src + x);
+#pragma unroll
+        for (int k = 0; k < P; ++k) st1<true>(dst[k] + x, w);
+      }
+    }
+  }
+}
+
 // The same 1:1 block copies when every segment shares one 16-byte
 // misalignment (common source and destination misalignment, n * B a
 // multiple of 16), so every segment has the same head, vector count and
@@ -265,6 +301,23 @@ static bool uniform_pair_layout(const CopyGeom& g, uint64_t nseg, uint64_t* head
 template <int B>
 static int launch_copy_b(const RankPtrs& ptrs, const CopyGeom& g, int max_grid, hipStream_t s) {
   const uint64_t nseg = g.kind == kCopyBroadcast ? 1 : (g.kind == kCopyAllToAll ? (uint64_t)g.p * g.p : g.p);
+  if (g.kind == kCopyAllGather && (g.p == 2 || g.p == 4 || g.p == 8 || g.p == 16)) {
+    uint64_t head, nvec, tail, tps;
+    // only while every workgroup has at most one tile: larger AllGathers
+    // keep the walking kernel, whose cost there is spread over many tiles
+    if (uniform_pair_layout<B>(g, nseg, &head, &nvec, &tail, &tps) && nseg * tps <= (uint64_t)max_grid) {
+      const int grid = clamp_grid(nseg * tps, max_grid);
+      if (!grid) return 0;
+      const uint32_t t32 = (uint32_t)tps;
+      switch (g.p) {
+        case 2: hipLaunchKernelGGL((allgather_flat_kernel<B, 2>), dim3(grid), dim3(kBlock), 0, s, ptrs, g, head, nvec, tail, t32); break;
+        case 4: hipLaunchKernelGGL((allgather_flat_kernel<B, 4>), dim3(grid), dim3(kBlock), 0, s, ptrs, g, head, nvec, tail, t32); break;
+        case 8: hipLaunchKernelGGL((allgather_flat_kernel<B, 8>), dim3(grid), dim3(kBlock), 0, s, ptrs, g, head, nvec, tail, t32); break;
+        default: hipLaunchKernelGGL((allgather_flat_kernel<B, 16>), dim3(grid), dim3(kBlock), 0, s, ptrs, g, head, nvec, tail, t32); break;
+      }
+      return (int)hipGetLastError();
+    }
+  }
   if (g.kind == kCopyAllToAll || g.kind == kCopyGather || g.kind == kCopyScatter) {
     uint64_t head, nvec, tail, tps;
     if (uniform_pair_layout<B>(g, nseg, &head, &nvec, &tail, &tps)) {
