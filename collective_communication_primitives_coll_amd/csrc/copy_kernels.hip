@@ -193,22 +193,23 @@ COLL_STREAM_KERNEL void pair_copy_flat_kernel(RankPtrs ptrs, CopyGeom g, uint64_
 // Alltoallv.  Every workgroup stages the p x p count matrix in LDS, checks
 // it against the buffer capacities, and derives the send offsets (row
 // exclusive prefix sums) and receive offsets (column exclusive prefix sums
-// in source order).  Then the segments (i, j) are walked like the equal
-// split.  Invalid counts make every workgroup return before any payload
-// is written.
+// in source order).  Invalid counts make every workgroup return before any
+// payload is written.  Then the segments (i, j) are copied: by flat tile
+// index for p <= 16, else walked like the equal split.
 // ---------------------------------------------------------------------------
-template <int B>
-COLL_STREAM_KERNEL void alltoallv_kernel(RankPtrs ptrs, A2avArgs a) {
-  using W = typename Word<B>::T;
-  extern __shared__ int64_t lds[];
-  __shared__ int bad;
+// Stages the p x p count matrix in LDS (cnt), with the send offsets (soff,
+// row exclusive prefix sums) and receive offsets (roff, column exclusive
+// prefix sums in source order), and checks it against the capacities.
+// Returns true when the call is rejected (every workgroup then returns
+// before any payload is written); workgroup 0 reports the status.
+__device__ __forceinline__ bool stage_a2av_counts(const A2avArgs& a, int64_t* lds, int* bad) {
   const int p = a.p;
   const int pp = p * p;
   int64_t* cnt = lds;
   int64_t* soff = lds + pp;
   int64_t* roff = lds + 2 * pp;
   const int tid = threadIdx.x;
-  if (tid == 0) bad = 0;
+  if (tid == 0) *bad = 0;
   for (int i = tid; i < pp; i += kBlock) {
     const int src = i / p, dst = i - (i / p) * p;
     cnt[i] = a.transposed ? a.counts[dst * p + src] : a.counts[i];
@@ -225,7 +226,7 @@ COLL_STREAM_KERNEL void alltoallv_kernel(RankPtrs ptrs, A2avArgs a) {
       s += (c < 0 ? 0 : c);
     }
     if (s > a.send_cap[i]) ok = false;
-    if (!ok) bad = 1;
+    if (!ok) *bad = 1;
   } else if (tid >= 64 && tid < 64 + p) {
     const int j = tid - 64;
     int64_t s = 0;
@@ -237,13 +238,25 @@ COLL_STREAM_KERNEL void alltoallv_kernel(RankPtrs ptrs, A2avArgs a) {
       s += (c < 0 ? 0 : c);
     }
     if (s > a.recv_cap[j]) ok = false;
-    if (!ok) bad = 1;
+    if (!ok) *bad = 1;
   }
   __syncthreads();
-  const bool reject = bad != 0;
+  const bool reject = *bad != 0;
   if (blockIdx.x == 0 && tid == 0 && a.status) *a.status = reject ? 1 : 0;
-  if (reject) return;
+  return reject;
+}
 
+template <int B>
+COLL_STREAM_KERNEL void alltoallv_kernel(RankPtrs ptrs, A2avArgs a) {
+  using W = typename Word<B>::T;
+  extern __shared__ int64_t lds[];
+  __shared__ int bad;
+  if (stage_a2av_counts(a, lds, &bad)) return;
+  const int p = a.p;
+  const int pp = p * p;
+  const int64_t* cnt = lds;
+  const int64_t* soff = lds + pp;
+  const int64_t* roff = lds + 2 * pp;
   uint64_t base = 0;
   for (int sgi = 0; sgi < pp; ++sgi) {
     const int i = sgi / p, j = sgi - (sgi / p) * p;
@@ -256,6 +269,86 @@ COLL_STREAM_KERNEL void alltoallv_kernel(RankPtrs ptrs, A2avArgs a) {
     const int mis = seg_mis(a.src_mis, a.dst_mis, so * B, ro * B);
     auto gdst = [&](int) -> W* { return dst; };
     base += copy_segment<B, true, 1>(src, gdst, 1, len, mis, base);
+  }
+}
+
+// Alltoallv for p <= 16 (p^2 <= kBlock segments): after staging the
+// counts, thread s computes segment s's tile count (from its own
+// misalignment; a segment with only an unaligned head or tail gets one
+// tile), a workgroup-wide scan turns the counts into tile starts, and
+// each flat tile finds its segment by binary search over the starts.  The
+// walking kernel above has every workgroup run the segment routine for
+// all p^2 segments, which made small calls take 40 us at p = 8 and 149 us
+// at p = 16.
+template <int B>
+COLL_STREAM_KERNEL void alltoallv_flat_kernel(RankPtrs ptrs, A2avArgs a) {
+  using W = typename Word<B>::T;
+  constexpr uint64_t V = 16 / B;
+  constexpr uint64_t TE = (uint64_t)kBlock * 4;  // elements per tile of the element path
+  extern __shared__ int64_t lds[];
+  __shared__ int bad;
+  __shared__ uint64_t tstart[kBlock + 1];
+  if (stage_a2av_counts(a, lds, &bad)) return;
+  const int p = a.p;
+  const int pp = p * p;
+  const int64_t* cnt = lds;
+  const int64_t* soff = lds + pp;
+  const int64_t* roff = lds + 2 * pp;
+  const int tid = threadIdx.x;
+  uint64_t nt = 0;
+  if (tid < pp && cnt[tid] > 0) {
+    const uint64_t len = (uint64_t)cnt[tid];
+    const SegSpan sp = seg_span<B>(len, seg_mis(a.src_mis, a.dst_mis, (uint64_t)soff[tid] * B, (uint64_t)roff[tid] * B));
+    nt = sp.vec ? ceil_div(sp.nvec, kCopyTV) : ceil_div(len, TE);
+    if (nt == 0) nt = 1;
+  }
+  // inclusive scan of nt over the workgroup: tstart[s + 1] = tiles of segments 0..s
+  tstart[tid + 1] = nt;
+  if (tid == 0) tstart[0] = 0;
+  __syncthreads();
+  for (int off = 1; off < kBlock; off <<= 1) {
+    const uint64_t v = tid >= off ? tstart[tid + 1 - off] : 0;
+    __syncthreads();
+    tstart[tid + 1] += v;
+    __syncthreads();
+  }
+  const uint64_t total = tstart[pp];
+  for (uint64_t f = blockIdx.x; f < total; f += gridDim.x) {
+    // segment sgi with tstart[sgi] <= f < tstart[sgi + 1] (it has tiles)
+    int lo = 0, hi = pp;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (tstart[mid] <= f) lo = mid;
+      else hi = mid;
+    }
+    const int sgi = lo;
+    const uint64_t t = f - tstart[sgi];
+    const int i = sgi / p, j = sgi - (sgi / p) * p;
+    const uint64_t len = (uint64_t)cnt[sgi];
+    const uint64_t so = (uint64_t)soff[sgi];
+    const uint64_t ro = (uint64_t)roff[sgi];
+    const W* src = (const W*)ptrs.src[i] + so;
+    W* dst = (W*)ptrs.dst[j] + ro;
+    const SegSpan sp = seg_span<B>(len, seg_mis(a.src_mis, a.dst_mis, so * B, ro * B));
+    if (!sp.vec) {
+      const uint64_t from = t * TE;
+      const uint64_t n = (len - from) < TE ? (len - from) : TE;
+      for (uint64_t e = tid; e < n; e += kBlock) st1<true>(dst + from + e, ld1<true>(src + from + e));
+      continue;
+    }
+    const u32x4* vs = reinterpret_cast<const u32x4*>(src + sp.head);
+    u32x4* vd = reinterpret_cast<u32x4*>(dst + sp.head);
+    auto gdst = [&](int) -> u32x4* { return vd; };
+    const uint64_t j0 = t * kCopyTV + tid;
+    if ((t + 1) * kCopyTV <= sp.nvec) copy_vec_tile<true, true, 1>(vs, gdst, 1, j0, sp.nvec);
+    else if (t * kCopyTV < sp.nvec) copy_vec_tile<true, false, 1>(vs, gdst, 1, j0, sp.nvec);
+    if (t == 0 && (sp.head || sp.tail)) {
+      const uint64_t e = tid;
+      if (e < sp.head + sp.tail) {
+        const uint64_t x = e < sp.head ? e : sp.head + sp.nvec * V + (e - sp.head);
+        st1<true>(dst + x, ld1<true>(src + x));
+      }
+    }
   }
 }
 
@@ -364,14 +457,19 @@ int launch_copy(int elem_bytes, const RankPtrs& ptrs, const CopyGeom& g, int max
 int launch_alltoallv(int elem_bytes, const RankPtrs& ptrs, const A2avArgs& a, int grid, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   const size_t shm = (size_t)3 * a.p * a.p * sizeof(int64_t);
-  if (elem_bytes == 1)
-    hipLaunchKernelGGL((alltoallv_kernel<1>), dim3(grid), dim3(kBlock), shm, s, ptrs, a);
-  else if (elem_bytes == 2)
-    hipLaunchKernelGGL((alltoallv_kernel<2>), dim3(grid), dim3(kBlock), shm, s, ptrs, a);
-  else if (elem_bytes == 4)
-    hipLaunchKernelGGL((alltoallv_kernel<4>), dim3(grid), dim3(kBlock), shm, s, ptrs, a);
-  else
+  const bool flat = a.p * a.p <= kBlock;
+  if (elem_bytes == 1) {
+    if (flat) hipLaunchKernelGGL((alltoallv_flat_kernel<1>), dim3(grid), dim3(kBlock), shm, s, ptrs, a);
+    else hipLaunchKernelGGL((alltoallv_kernel<1>), dim3(grid), dim3(kBlock), shm, s, ptrs, a);
+  } else if (elem_bytes == 2) {
+    if (flat) hipLaunchKernelGGL((alltoallv_flat_kernel<2>), dim3(grid), dim3(kBlock), shm, s, ptrs, a);
+    else hipLaunchKernelGGL((alltoallv_kernel<2>), dim3(grid), dim3(kBlock), shm, s, ptrs, a);
+  } else if (elem_bytes == 4) {
+    if (flat) hipLaunchKernelGGL((alltoallv_flat_kernel<4>), dim3(grid), dim3(kBlock), shm, s, ptrs, a);
+    else hipLaunchKernelGGL((alltoallv_kernel<4>), dim3(grid), dim3(kBlock), shm, s, ptrs, a);
+  } else {
     return (int)hipErrorInvalidValue;
+  }
   return (int)hipGetLastError();
 }
 
