@@ -575,17 +575,19 @@ def test_alltoall_lds_staged(coll, p, m, dtype):
 
 
 @pytest.mark.parametrize("soff,roff", [(1, 1), (3, 3), (1, 2), (0, 5)])
-def test_alltoall_lds_staged_misaligned(coll, soff, roff):
-    """Bases off a 16-byte boundary: a shared misalignment takes the staged
-    vector path with element-wise heads and tails; differing ones the
-    direct kernel.  Bytes outside the receive views stay untouched."""
+@pytest.mark.parametrize("algo", ["LDS_STAGED", "DIRECT"])
+def test_alltoall_misaligned(coll, soff, roff, algo):
+    """Bases off a 16-byte boundary: a shared misalignment takes the vector
+    path (staged, or the flat-indexed direct kernel) with element-wise heads
+    and tails; differing ones the walking direct kernel.  Bytes outside the
+    receive views stay untouched."""
     p, m = 4, 8 * 700
     hx = gen(p, p * m, BF16, 17)
     keep = [upload_offset(x, BF16, soff) for x in hx]
     send = [v for _, v in keep]
     outs = [empty(p * m + roff + 8, BF16, fill=0x1234) for _ in range(p)]
     recv = [o[roff:roff + p * m] for o in outs]
-    coll.coll_alltoall_algo(send, recv, coll.COLL_A2A_LDS_STAGED)
+    coll.coll_alltoall_algo(send, recv, getattr(coll, "COLL_A2A_" + algo))
     sync()
     expect = ref.alltoall(hx)
     for j in range(p):
