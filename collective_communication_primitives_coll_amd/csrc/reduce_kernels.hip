@@ -140,8 +140,11 @@ COLL_STREAM_KERNEL void reduce_tile_kernel(RankPtrs ptrs, ReduceGeom g, uint32_t
 
 // Any rank count (the slow general path): one vector per lane per tile,
 // operands in groups of 8 loads, pointers read from the kernel arguments.
-template <int DT, int OP, int DMODE>
-COLL_STREAM_KERNEL void reduce_kernel_any(RankPtrs ptrs, ReduceGeom g) {
+// TILE: at most one tile per workgroup (AllReduce only): workgroup b works
+// tile b % tpc of chunk b / tpc instead of walking every chunk, as
+// reduce_tile_kernel does for the specialised rank counts.
+template <int DT, int OP, int DMODE, bool TILE = false>
+COLL_STREAM_KERNEL void reduce_kernel_any(RankPtrs ptrs, ReduceGeom g, uint32_t tpc = 0) {
 #pragma clang fp contract(off)
   using T = Traits<DT>;
   using S = typename T::S;
@@ -150,8 +153,14 @@ COLL_STREAM_KERNEL void reduce_kernel_any(RankPtrs ptrs, ReduceGeom g) {
   constexpr bool ALL = DMODE == kDstAll;
   const int p = g.p;
   const uint64_t grid = gridDim.x, wg = blockIdx.x;
+  const int c_first = TILE ? (int)(blockIdx.x / tpc) : 0;
+  const int c_end = TILE ? c_first + 1 : p;
+  const uint64_t my_tile = TILE ? blockIdx.x - (uint64_t)c_first * tpc : 0;
+  // first tile and stride of this workgroup in a segment of nt tiles
+  auto tile0 = [&](uint64_t base) -> uint64_t { return TILE ? my_tile : first_tile(base, wg, grid); };
+  auto tstep = [&](uint64_t nt) -> uint64_t { return TILE ? nt : grid; };
   uint64_t base = 0;
-  for (int c = 0; c < p; ++c) {
+  for (int c = c_first; c < c_end; ++c) {
     uint64_t lo, len;
     chunk_range(g, c, &lo, &len);
     if (len == 0) continue;
@@ -183,7 +192,7 @@ COLL_STREAM_KERNEL void reduce_kernel_any(RankPtrs ptrs, ReduceGeom g) {
     if (!sp.vec) {
       constexpr uint64_t TE = (uint64_t)kBlock * 4;
       const uint64_t nt = ceil_div(len, TE);
-      for (uint64_t t = first_tile(base, wg, grid); t < nt; t += grid) {
+      for (uint64_t t = tile0(base); t < nt; t += tstep(nt)) {
         const uint64_t from = t * TE;
         elems(from, (len - from) < TE ? (len - from) : TE);
       }
@@ -191,7 +200,7 @@ COLL_STREAM_KERNEL void reduce_kernel_any(RankPtrs ptrs, ReduceGeom g) {
       continue;
     }
     const uint64_t nt = ceil_div(sp.nvec, (uint64_t)kBlock);
-    for (uint64_t t = first_tile(base, wg, grid); t < nt; t += grid) {
+    for (uint64_t t = tile0(base); t < nt; t += tstep(nt)) {
       const uint64_t j = t * kBlock + threadIdx.x;
       if (j >= sp.nvec) continue;
       const uint64_t e = sp.head + j * V;
@@ -223,7 +232,7 @@ COLL_STREAM_KERNEL void reduce_kernel_any(RankPtrs ptrs, ReduceGeom g) {
       const u32x4 out = narrow<DT>(acc);
       for (int d = 0; d < nd; ++d) st16<ALL>(sp_dst(d) + e, out);
     }
-    if ((sp.head || sp.tail) && first_tile(base, wg, grid) == 0) {
+    if ((sp.head || sp.tail) && tile0(base) == 0) {
       // head and tail in one pass (each is shorter than a vector)
       const uint64_t i = threadIdx.x;
       if (i < sp.head + sp.tail) elem_at(i < sp.head ? i : sp.head + sp.nvec * V + (i - sp.head));
@@ -305,6 +314,19 @@ static int launch_p(const RankPtrs& ptrs, const ReduceGeom& g, int max_grid, hip
 
 template <int DT, int OP>
 static int launch_any(const RankPtrs& ptrs, const ReduceGeom& g, int max_grid, hipStream_t s) {
+  if (g.dst_mode == kDstAll) {
+    // at most one tile per workgroup: no chunk walk.  Tiles of kBlock * 4
+    // elements (the element path's) also bound the vector path's tiles of
+    // kBlock vectors.
+    const uint64_t te = (uint64_t)kBlock * 4;
+    const uint64_t tpc = (g.stride + te - 1) / te;
+    if (tpc * (uint64_t)g.p <= (uint64_t)max_grid) {
+      if (tpc)
+        hipLaunchKernelGGL((reduce_kernel_any<DT, OP, kDstAll, true>), dim3((unsigned)(tpc * g.p)), dim3(kBlock),
+                           0, s, ptrs, g, (uint32_t)tpc);
+      return (int)hipGetLastError();
+    }
+  }
   const int grid = clamp_grid(count_tiles<DT, 0, false>(g), max_grid);
   if (!grid) return 0;
   if (g.dst_mode == kDstAll)
