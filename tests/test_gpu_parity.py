@@ -506,6 +506,50 @@ def test_scatter_every_root(coll, p, n, dtype):
             assert_bits_equal(to_host(recv[r], dtype), expect[r], f"scatter p={p} n={n} root={root} r={r}")
 
 
+@pytest.mark.parametrize("p", [1, 2, 8, 16])
+@pytest.mark.parametrize("dtype", [BF16, F32])
+@pytest.mark.parametrize("off", [0, 3])
+def test_uniform_copies_flat_paths(coll, p, dtype, off):
+    """AllGather, All-to-All, Gather and Scatter on buffers whose blocks all
+    share one 16-byte misalignment (n * element size a multiple of 16, the
+    same element offset in every buffer): the flat-indexed kernels, with
+    heads and tails when off > 0, from one vector to several tiles."""
+    for n in (8, 8 * 300, 8 * 1100):
+        hx = gen(p, p * n, dtype, 90 + n)
+
+        def views(count, size, fill):
+            bases = [empty(size + off + 8, dtype, fill=fill) for _ in range(count)]
+            return bases, [b[off:off + size] for b in bases]
+
+        _, send = views(p, p * n, 0)
+        for v, x in zip(send, hx):
+            v.copy_(to_dev(x, dtype))
+        # All-to-All
+        _, recv = views(p, p * n, 0x1111)
+        coll.coll_alltoall(send, recv, n)
+        sync()
+        for j, e in enumerate(ref.alltoall(hx)):
+            assert_bits_equal(to_host(recv[j], dtype), e, f"A2A p={p} n={n} off={off} j={j}")
+        # AllGather of the first n elements of every rank
+        shards = [v[:n] for v in send]
+        _, full = views(p, p * n, 0x2222)
+        coll.coll_allgather(shards, full, n)
+        sync()
+        for j, e in enumerate(ref.allgather([x[:n] for x in hx])):
+            assert_bits_equal(to_host(full[j], dtype), e, f"AG p={p} n={n} off={off} j={j}")
+        # Gather and Scatter at the last root
+        root = p - 1
+        _, (groot,) = views(1, p * n, 0x3333)
+        coll.coll_gather(shards, groot, root, n)
+        sync()
+        assert_bits_equal(to_host(groot, dtype), ref.gather([x[:n] for x in hx], root), f"gather p={p} n={n}")
+        _, outs = views(p, n, 0x4444)
+        coll.coll_scatter(send[root], outs, root, n)
+        sync()
+        for r, e in enumerate(ref.scatter(hx[root], p, root)):
+            assert_bits_equal(to_host(outs[r], dtype), e, f"scatter p={p} n={n} r={r}")
+
+
 def test_gather_scatter_in_place_and_misaligned(coll):
     p, n, root = 8, 3001, 5
     hx = gen(p, n, F32, 72)
