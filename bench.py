@@ -819,6 +819,16 @@ def main(argv=None) -> int:
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK, 4), "traffic": read_traffic(kkey, dom_bytes),
                 "kernel": dom, "algorithmic_bytes_per_launch": dom_bytes, "mean_launch_us": round(dom_us, 2)}
+    # An attainable reference measured in the same run: a 1 GiB device copy
+    # (1 read : 1 write) by the library's copy kernel (Broadcast at p = 1).
+    cbytes = 1 << 30
+    ca = torch.empty(cbytes // 4, dtype=torch.int32, device=dev).fill_(1)
+    cb = torch.empty_like(ca)
+    cmed, _, _ = stats_us(time_launches(torch, [coll.coll_broadcast(ca, [cb], 0, defer=True)], 10, 3)[0])
+    copy_gbps = 2 * cbytes / (cmed * 1e-6) / 1e9
+    roofline["attainable_copy_GBps"] = round(copy_gbps, 1)
+    roofline["frac_of_copy"] = round(achieved / copy_gbps, 4)
+    del ca, cb
 
     cpu = None
     if not args.no_cpu_baseline:
