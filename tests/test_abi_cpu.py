@@ -96,6 +96,11 @@ def test_invalid_arguments_rejected():
     assert L.coll_allreduce_algo(s, r, 4, n, 0, 0, 6, None) == INV
     assert L.coll_allreduce_algo(s, r, 3, n, 0, 0, 4, None) == coll.COLL_ERR_UNSUPPORTED   # tree, p = 3
     assert L.coll_allreduce_algo(s, r, 3, n, 0, 0, 5, None) == coll.COLL_ERR_UNSUPPORTED   # double tree, p = 3
+    assert L.coll_alltoall_algo(s, r, 4, n, 1, 2, None) == INV       # bad All-to-All data path
+    assert L.coll_alltoall_algo(s, r, 4, n, 1, -1, None) == INV
+    assert L.coll_alltoall_algo(s, r, 4, n, 4, 1, None) == INV       # bad dtype
+    assert L.coll_alltoall_algo(s, r, 0, n, 1, 1, None) == INV       # p = 0
+    assert L.coll_alltoall_algo(s, r, 4, 0, 1, 7, None) == INV       # algo checked before the n = 0 no-op
     assert L.coll_allreduce(None, r, 4, n, 0, 0, None) == INV         # null array
     assert L.coll_allreduce(s, r, 4, 1 << 61, 0, 0, None) == INV      # size overflow
     z, _kz = _arr([base, 0, base + 0x200000, base + 0x300000])
