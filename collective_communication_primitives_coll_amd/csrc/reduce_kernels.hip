@@ -89,9 +89,9 @@ COLL_STREAM_KERNEL void reduce_kernel(RankPtrs ptrs, ReduceGeom g) {
   }
 }
 
-// AllReduce and ReduceScatter calls whose tiles fit the grid (at most one
-// tile per workgroup): workgroup b works tile b % tpc of chunk b / tpc,
-// tpc tiles per chunk, and nothing else.  The general kernel gives such calls the
+// AllReduce, ReduceScatter and Reduce calls whose tiles fit the grid (at
+// most one tile per workgroup): workgroup b works tile b % tpc of chunk
+// b / tpc, tpc tiles per chunk, and nothing else.  The general kernel gives such calls the
 // same tiles but has every workgroup walk all P chunks to find its tile,
 // and for small calls that walk (ownership tests, a run-time remainder
 // per chunk) outlasts the data movement: at p = 16 a 4 KiB call took
@@ -285,13 +285,16 @@ static int launch_p(const RankPtrs& ptrs, const ReduceGeom& g, int max_grid, hip
     }
   }
   if constexpr (ORD == kOrdRing) {
-    // ReduceScatter (ring order only) likewise
-    if (g.dst_mode == kDstOwner) {
+    // ReduceScatter and Reduce (ring order only) likewise
+    if (g.dst_mode == kDstOwner || g.dst_mode == kDstFixed) {
       const uint64_t te = tile_elems<DT, P, false>();
       const uint64_t tpc = (g.stride + te - 1) / te;
       if (tpc * P <= (uint64_t)max_grid) {
-        if (tpc)
+        if (tpc && g.dst_mode == kDstOwner)
           hipLaunchKernelGGL((reduce_tile_kernel<DT, OP, P, ORD, kDstOwner>), dim3((unsigned)(tpc * P)),
+                             dim3(kBlock), 0, s, ptrs, g, (uint32_t)tpc);
+        else if (tpc)
+          hipLaunchKernelGGL((reduce_tile_kernel<DT, OP, P, ORD, kDstFixed>), dim3((unsigned)(tpc * P)),
                              dim3(kBlock), 0, s, ptrs, g, (uint32_t)tpc);
         return (int)hipGetLastError();
       }
