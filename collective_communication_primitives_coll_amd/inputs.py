@@ -175,3 +175,82 @@ def moe_routes_skewed(p: int, tokens: int, k: int, alpha: float, extra: int = 0)
 def moe_weights(p: int, tokens: int, k: int, workload: int = WL_MOE_A2A, extra: int = 0) -> list[np.ndarray]:
     """Per rank, fp32 [tokens*k] combine weights uniform in [0, 1)."""
     return [rng_for(workload, r, 3000 + extra, k).random(tokens * k, dtype=np.float32) for r in range(p)]
+
+
+# ----------------------------------------------------------------------------
+# Special values: operands that exercise the numeric edge cases of the
+# reductions (wrap-around, subnormals, overflow, rounding ties, signed zeros,
+# NaN and infinities).  These only draw bit patterns from fixed pools.
+# ----------------------------------------------------------------------------
+
+EDGE_KINDS = ("int_wrap", "subnormal", "overflow", "ties", "zero_nan_inf")
+
+_F32_SPECIAL = np.array([0x00000000, 0x80000000, 0x7FC00000, 0xFFC00000, 0x7F800000, 0xFF800000,
+                         0x3F800000, 0xBF800000, 0x40000000, 0xC0000000], dtype=np.uint32)
+_BF16_SPECIAL = np.array([0x0000, 0x8000, 0x7FC0, 0xFFC0, 0x7F80, 0xFF80, 0x3F80, 0xBF80, 0x4000, 0xC000],
+                         dtype=np.uint16)
+# zero, -zero, quiet NaN (both signs), +-inf, +-1, +-2; weights favour the zeros
+_SPECIAL_P = np.array([0.2, 0.2, 0.06, 0.04, 0.05, 0.05, 0.1, 0.1, 0.1, 0.1])
+# bf16 values whose fp32 sums often land exactly halfway between two bf16
+# neighbours: +-1, +-2^-8, +-2^-7, +-(1 + 2^-7), +-3*2^-9, +-2^-9
+_BF16_TIES = np.array([0x3F80, 0xBF80, 0x3B80, 0xBB80, 0x3C00, 0xBC00, 0x3F81, 0xBF81, 0x3BC0, 0xBBC0, 0x3B00,
+                       0xBB00], dtype=np.uint16)
+
+
+def edge_buffers(p: int, n: int, dtype: int, kind: str, seed: int = 0) -> list[np.ndarray]:
+    """Per rank, n elements of special operands (bit patterns for bf16):
+
+    int_wrap      int32 within 1000 of INT32_MAX or INT32_MIN (sums wrap);
+    subnormal     fp32 / bf16 subnormals of either sign, with some normals
+                  of the smallest exponents;
+    overflow      fp32 / bf16 values within a few ulps of the largest finite
+                  value, either sign (sums overflow);
+    ties          bf16 values whose fp32 sums often fall halfway between two
+                  bf16 neighbours;
+    zero_nan_inf  fp32 / bf16 +-0, quiet NaN, +-inf, +-1, +-2.
+    """
+    out = []
+    for r in range(p):
+        g = rng_for(WL_TEST, r, 7000 + EDGE_KINDS.index(kind), seed)
+        if kind == "int_wrap":
+            if dtype != I32:
+                raise ValueError("int_wrap is int32")
+            hi = g.integers(2**31 - 1000, 2**31, n, dtype=np.int64)
+            lo = g.integers(-2**31, -2**31 + 1000, n, dtype=np.int64)
+            out.append(np.where(g.random(n) < 0.5, hi, lo).astype(np.int32))
+            continue
+        if dtype == I32:
+            raise ValueError(f"{kind} is a floating-point kind")
+        if kind == "subnormal":
+            if dtype == F32:
+                mant = g.integers(1, 1 << 23, n, dtype=np.uint32)
+                normal = g.integers(0x00800000, 0x00A00000, n, dtype=np.uint32)  # exponent field 1
+                bits = np.where(g.random(n) < 0.8, mant, normal)
+                out.append((bits | (g.integers(0, 2, n, dtype=np.uint32) << np.uint32(31))).view(np.float32))
+            else:
+                mant = g.integers(1, 0x80, n, dtype=np.uint16)
+                normal = g.integers(0x0080, 0x00A0, n, dtype=np.uint16)
+                bits = np.where(g.random(n) < 0.8, mant, normal).astype(np.uint16)
+                out.append(bits | (g.integers(0, 2, n, dtype=np.uint16) << np.uint16(15)))
+        elif kind == "overflow":
+            sign = g.integers(0, 2, n)
+            if dtype == F32:
+                bits = g.integers(0x7F7FFFF0, 0x7F800000, n, dtype=np.uint32)
+                bits = np.where(g.random(n) < 0.7, bits, g.integers(0x7F000000, 0x7F7FFFFF, n, dtype=np.uint32))
+                out.append((bits.astype(np.uint32) | (sign.astype(np.uint32) << np.uint32(31))).view(np.float32))
+            else:
+                bits = g.integers(0x7F70, 0x7F80, n, dtype=np.uint16)
+                bits = np.where(g.random(n) < 0.7, bits, g.integers(0x7E00, 0x7F70, n, dtype=np.uint16))
+                out.append((bits.astype(np.uint16) | (sign.astype(np.uint16) << np.uint16(15))).astype(np.uint16))
+        elif kind == "ties":
+            if dtype != BF16:
+                raise ValueError("ties is bf16")
+            out.append(g.choice(_BF16_TIES, n))
+        elif kind == "zero_nan_inf":
+            if dtype == F32:
+                out.append(g.choice(_F32_SPECIAL, n, p=_SPECIAL_P).view(np.float32))
+            else:
+                out.append(g.choice(_BF16_SPECIAL, n, p=_SPECIAL_P))
+        else:
+            raise ValueError(kind)
+    return out

@@ -111,7 +111,7 @@ def _widen(v: np.ndarray, dtype: int) -> np.ndarray:
 
 def _combine(acc: np.ndarray, v: np.ndarray, op: int) -> np.ndarray:
     if op in (SUM, AVG):
-        with np.errstate(over="ignore"):
+        with np.errstate(over="ignore", invalid="ignore"):
             return acc + v          # fp32 IEEE add (RNE) / int32 add mod 2^32
     if op == MIN:
         return np.where(v < acc, v, acc)
