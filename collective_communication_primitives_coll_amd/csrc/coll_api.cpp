@@ -50,6 +50,10 @@ std::atomic<int> g_wg_per_cu{0};
 // 4096 x 7168 tokens, p = 8, top-2.
 enum Family { kFamReduce = 0, kFamCopy = 1, kFamRow = 2, kFamFp8 = 3, kFamFp8Direct = 4 };
 constexpr int kDefaultWgPerCu[5] = {1, 2, 8, 16, 2};
+// Largest accepted override (coll_set_grid_limit clamps to it).  A CU
+// holds far fewer 256-thread workgroups at once, so larger values would
+// only queue workgroups; the clamp also keeps CUs * limit within int.
+constexpr int kMaxWgPerCu = 64;
 
 int current_device(int* dev) { return (int)hipGetDevice(dev); }
 
@@ -78,7 +82,9 @@ int max_grid(int* out, Family fam) {
   if (e) return e;
   int w = g_wg_per_cu.load(std::memory_order_relaxed);
   if (w <= 0) w = kDefaultWgPerCu[fam];
-  *out = cus * w;
+  const int64_t g = (int64_t)cus * w;  // w <= kMaxWgPerCu: no overflow
+  if (g <= 0) return (int)hipErrorInvalidConfiguration;
+  *out = (int)g;
   return 0;
 }
 
@@ -1225,7 +1231,9 @@ COLL_EXPORT int coll_last_hip_error(void) { return g_last_hip; }
 COLL_EXPORT int coll_version(void) { return 200; }
 
 COLL_EXPORT void coll_set_grid_limit(int workgroups_per_cu) {
-  g_wg_per_cu.store(workgroups_per_cu > 0 ? workgroups_per_cu : 0, std::memory_order_relaxed);
+  int w = workgroups_per_cu > 0 ? workgroups_per_cu : 0;
+  if (w > kMaxWgPerCu) w = kMaxWgPerCu;
+  g_wg_per_cu.store(w, std::memory_order_relaxed);
 }
 
 COLL_EXPORT void coll_finalize(void) {

@@ -156,13 +156,21 @@ __device__ __forceinline__ typename Traits<DT>::S narrow1(typename Traits<DT>::A
 
 // ---------------------------------------------------------------------------
 // The elementwise operation.  acc is the running partial, v the next
-// rank's value; min/max keep acc on ties; avg and pre-multiplied sums add.
+// rank's value; min/max are compare-selects that keep acc on ties and when
+// either operand is NaN (the comparison is then false); avg and
+// pre-multiplied sums add.  int32 sums add through uint32_t, so they wrap
+// modulo 2^32 by definition rather than by signed overflow.
 // ---------------------------------------------------------------------------
 template <int OP, typename A>
 __device__ __forceinline__ A combine(A acc, A v) {
-  if constexpr (OP == kSum || OP == kAvg || OP == kPreMul) return acc + v;
-  else if constexpr (OP == kMin) return (v < acc) ? v : acc;
-  else return (v > acc) ? v : acc;
+  if constexpr (OP == kSum || OP == kAvg || OP == kPreMul) {
+    if constexpr (__is_same(A, int32_t)) return (int32_t)((uint32_t)acc + (uint32_t)v);
+    else return acc + v;
+  } else if constexpr (OP == kMin) {
+    return (v < acc) ? v : acc;
+  } else {
+    return (v > acc) ? v : acc;
+  }
 }
 
 template <int OP, int DT>

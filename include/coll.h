@@ -366,7 +366,7 @@ coll_status_t coll_moe_combine_direct(const void* const* y, const int64_t* const
                                       void* const* out, int p, size_t tokens_per_rank, int k, size_t hidden,
                                       const int64_t* y_rows, coll_dtype_t dtype, void* stream);
 
-/* One AllReduce of a batch (host-side view). *//* One AllReduce of a batch (host-side view). */
+/* One AllReduce of a batch (host-side view). */
 typedef struct {
   const void* const* send;  /* host array of p device pointers */
   void* const* recv;        /* host array of p device pointers */
@@ -405,6 +405,7 @@ int coll_version(void);
  * compute unit, for every kernel; 0 restores each kernel family's
  * measured default (1 for reductions, 2 for copies and the direct FP8
  * dispatch, 8 for the MoE row kernels, 16 for the FP8 pack and dequant).
+ * Negative values count as 0; values above 64 are clamped to 64.
  * Applies to later calls from every thread; results do not depend on it. */
 void coll_set_grid_limit(int workgroups_per_cu);
 

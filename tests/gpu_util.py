@@ -80,3 +80,25 @@ def assert_bf16_within_ulp(got: np.ndarray, expect: np.ndarray, ulps: int = 1, w
     if not np.all(diff <= ulps):
         i = int(np.argmax(diff))
         raise AssertionError(f"{what}: element {i} differs by {diff[i]} bf16 ulps")
+
+
+def nan_mask(a: np.ndarray) -> np.ndarray:
+    """NaN positions of an fp32 array or of bf16 bit patterns (uint16)."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return ((a & 0x7F80) == 0x7F80) & ((a & 0x007F) != 0)
+    if a.dtype == np.float32:
+        return np.isnan(a)
+    return np.zeros(a.shape, dtype=bool)
+
+
+def assert_bits_equal_nan(got: np.ndarray, expect: np.ndarray, what: str = "") -> None:
+    """Bit-exact except where the oracle's result is a NaN made by an
+    addition: IEEE 754 leaves the sign and payload of such a NaN open, so
+    there the kernel's result only has to be a NaN too."""
+    gm, em = nan_mask(got), nan_mask(expect)
+    if not np.array_equal(gm, em):
+        i = int(np.nonzero(gm != em)[0][0])
+        raise AssertionError(f"{what}: NaN positions differ; first at {i}: got {got[i]!r} expected {expect[i]!r}")
+    keep = ~em
+    assert_bits_equal(np.asarray(got)[keep], np.asarray(expect)[keep], what)
