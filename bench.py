@@ -16,13 +16,20 @@ the part of the network.  The JSON line reports
   mean duration (HIP events on the launch stream) against 8 TB/s, plus
   the HBM traffic read from rocprofv3 FETCH_SIZE / WRITE_SIZE counters
   when a counter summary for the current kernel sources is on file;
-* cpu_baseline: the CPU oracle on a bounded slice of the same workload;
+* cpu_baseline: the threaded C++ oracle on the whole step (all host
+  threads, and one thread), checked against the GPU output;
 * collectives: the other p = 8 collectives (AllReduce in four
   schedules, All-to-All, Alltoallv, the MoE pack -> exchange -> reverse
   exchange -> combine path, Gather, Scatter), the small
   AllReduce at p = 4, the 10,000-call batched AllReduce at p = 16 (also
   as individual calls, with latency percentiles and an alpha-beta fit)
-  and the box's copy ceiling, each timed with HIP events.
+  and the box's copy ceiling, each timed with HIP events.  Every row
+  carries the attainable ceiling of its read:write stream mix, measured in
+  the same run with the library's direction-mix probe (coll_stream_probe:
+  the collectives' own tile code), and its fraction of that ceiling.
+
+The JSON line on stdout is a compact summary; the full per-collective
+tables go to stderr as "# detail" lines.
 
 Only one GPU is used; --gpus above 1 is refused.
 """
@@ -46,6 +53,7 @@ if ROOT not in sys.path:
 METRIC = "busbw and achieved HBM GB/s (% of peak) per collective at p=8, 1 GPU"
 HBM_PEAK = 8000.0  # GB/s, MI355X HBM3E published peak
 PROFILES = os.path.join(ROOT, "profiles")
+NO_GRAPHS = False   # set by --no-graphs
 CSRC = os.path.join(ROOT, "collective_communication_primitives_coll_amd", "csrc")
 
 
@@ -60,7 +68,9 @@ def parse_args(argv=None):
                     help="comma list of extra collectives to time (ar_ring, ar_onepass, ar_hd, "
                          "ar_tree, ar_dbt, ar_literal, ar_avg, ar_premul, a2a, a2av, moe, moe_fp8, moe_direct, moe_fp8_direct, "
                          "gs, ar_small, ar_latency, batch, copy, ce)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget (all threads)")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the direction-mix ceilings")
+    ap.add_argument("--no-graphs", action="store_true", help="skip the HIP-graph replays (for counter runs)")
     return ap.parse_args(argv)
 
 
@@ -127,6 +137,63 @@ def time_launches(torch, fns, iters: int, warmup: int):
 def stats_us(ms_list):
     a = np.asarray(ms_list, dtype=np.float64) * 1e3
     return float(np.median(a)), float(np.percentile(a, 95)), float(a.mean())
+
+
+class Ceilings:
+    """Attainable HBM GB/s of a read:write stream mix, measured in this run
+    with the library's direction-mix probe (coll_stream_probe: the
+    collectives' 16-byte tiles, launch bounds and grid sizing): ns source and
+    nd destination streams of stream_bytes each, best over tiles of 1, 2, 4
+    and 8 vectors per lane, the four cache policies (cached or non-temporal
+    loads and stores) and one, two or four workgroups per CU.  Results are cached per (ns, nd, stream_bytes)."""
+
+    def __init__(self, torch, coll, dev, enabled=True):
+        self.torch, self.coll, self.dev, self.enabled = torch, coll, dev, enabled
+        self.cache = {}
+
+    def get(self, ns: int, nd: int, stream_bytes: int):
+        if not self.enabled:
+            return None
+        key = (ns, nd, int(stream_bytes))
+        if key in self.cache:
+            return self.cache[key]
+        torch, coll = self.torch, self.coll
+        words = stream_bytes // 4
+        src = [torch.empty(words, dtype=torch.int32, device=self.dev) for _ in range(ns)]
+        for i, t in enumerate(src):
+            t.fill_(i + 1)
+        dst = [torch.empty(words, dtype=torch.int32, device=self.dev) for _ in range(nd)]
+        sink = torch.zeros(4, dtype=torch.int32, device=self.dev)
+        best = None
+        try:
+            for w in (1, 2, 4):
+                coll.coll_set_grid_limit(w)
+                for unroll in (1, 2, 4, 8):
+                    if ns * unroll > 32:
+                        continue
+                    for flags in (0, 1, 2, 3):
+                        f = coll.coll_stream_probe(src, dst, stream_bytes, unroll, flags, sink, defer=True)
+                        med = stats_us(time_launches(torch, [f], 4, 1)[0])[0]
+                        gbps = (ns + nd) * stream_bytes / (med * 1e-6) / 1e9
+                        if best is None or gbps > best[0]:
+                            best = (gbps, w, flags, unroll)
+        finally:
+            coll.coll_set_grid_limit(0)
+        del src, dst
+        torch.cuda.empty_cache()
+        res = {"GBps": round(best[0], 1), "mix": f"{ns}r:{nd}w x {stream_bytes >> 20} MiB",
+               "wg_per_cu": best[1], "unroll": best[3], "nt_loads": bool(best[2] & 1), "nt_stores": bool(best[2] & 2)}
+        self.cache[key] = res
+        return res
+
+    def attach(self, row: dict, ns: int, nd: int, stream_bytes: int, gbps_key: str = "hbm_GBps") -> dict:
+        """Add the mix ceiling and the row's fraction of it to row."""
+        c = self.get(ns, nd, stream_bytes)
+        if c is not None and row.get(gbps_key):
+            row["mix"] = c["mix"]
+            row["mix_ceiling_GBps"] = c["GBps"]
+            row["frac_of_mix_ceiling"] = round(row[gbps_key] / c["GBps"], 4)
+        return row
 
 
 def coll_entry(metrics, name, coll_kind, p, n, d, t_us, algo="ring", extra=None):
@@ -203,46 +270,54 @@ def zero_workload(torch, coll, inputs, dev):
     return dict(p=p, n=n, total=total, hx=hx, send=send, shard=shard, full=full, rs=rs, ag=ag)
 
 
-def cpu_baseline(wl, cpu_seconds: float):
-    """The CPU oracle on a slice of the ZeRO workload: the first m elements
-    of every rank's block r, for all r (ReduceScatter then AllGather of
-    that slice), repeated until cpu_seconds have passed.  Also checks the
-    GPU output on the same slice."""
-    from oracle import ref
+def cpu_baseline(torch, wl, cpu_seconds: float):
+    """The threaded C++ oracle (oracle/oracle.cpp, as it stands) on the whole
+    timed step: ReduceScatter of the full p = 8, 2^26-element bf16 inputs,
+    then AllGather of the shards.  Timed with every host thread (repeated
+    for about cpu_seconds) and with one thread (once); its result is
+    compared with the GPU's whole output."""
+    from oracle import native
     from collective_communication_primitives_coll_amd import metrics
 
     p, n, hx = wl["p"], wl["n"], wl["hx"]
-    m = 1 << 19
-    xs = [np.concatenate([x[r * n:r * n + m] for r in range(p)]) for x in hx]
+    nt = native.hardware_threads()
+
+    def step(threads):
+        shards = native.reduce_scatter(hx, native.SUM, native.BF16, nthreads=threads)
+        return shards, native.allgather(shards, nthreads=threads)
+
     reps, t0 = 0, time.perf_counter()
     while True:
-        shards = ref.reduce_scatter(xs, ref.SUM, ref.BF16)
-        gathered = ref.allgather(shards)
+        shards, gathered = step(nt)
         reps += 1
         el = time.perf_counter() - t0
         if el >= cpu_seconds:
             break
-    per = el / reps
-    # algorithmic HBM-equivalent bytes of the slice: RS (p*p*m read, p*m written)
-    # plus AG (p*m read, p*p*m written), bf16
-    alg = metrics.hbm_bytes("reduce_scatter", p, m, 2) + metrics.hbm_bytes("allgather", p, m, 2)
-    agree = all(np.array_equal(to_host_bits(wl["shard"][r][:m]), shards[r]) for r in range(p))
-    j = p - 1
-    got = to_host_bits(wl["full"][j])
-    agree = agree and all(np.array_equal(got[r * n:r * n + m], gathered[j][r * m:(r + 1) * m])
-                          for r in range(p))
+    per_all = el / reps
+    t1 = time.perf_counter()
+    step(1)
+    per_one = time.perf_counter() - t1
+    alg = metrics.hbm_bytes("reduce_scatter", p, n, 2) + metrics.hbm_bytes("allgather", p, n, 2)
+
+    def same(t, a):
+        e = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(t.device)
+        return bool(torch.equal(t.view(torch.int16), e))
+    agree = all(same(wl["shard"][r], shards[r]) for r in range(p)) and \
+        all(same(wl["full"][r], gathered[r]) for r in range(p))
     return {
-        "value": round(alg / per / 1e9, 3),
+        "value": round(alg / per_all / 1e9, 3),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": nt,
         "kind": "oracle",
-        "sample": (f"oracle/ref.py (NumPy, single thread) ReduceScatter+AllGather on the first "
-                   f"{m} elements of each of the 8 blocks of every rank (1/16 of the step), "
-                   f"{reps} repetitions in {el:.1f} s; GB/s of the same algorithmic HBM bytes"),
-        "ms_per_sample": round(per * 1e3, 1),
+        "sample": (f"the whole step: oracle/oracle.cpp ReduceScatter + AllGather of the full p=8, 2^26 bf16 "
+                   f"per rank inputs, {nt} threads, {reps} repetitions in {el:.1f} s; GB/s of the step's "
+                   f"algorithmic HBM bytes"),
+        "ms_per_step": round(per_all * 1e3, 1),
+        "value_1_thread": round(alg / per_one / 1e9, 3),
+        "ms_per_step_1_thread": round(per_one * 1e3, 1),
         "host_cpus": os.cpu_count(),
         "cpu_model": host_cpu_model(),
-        "gpu_matches_oracle_on_sample": bool(agree),
+        "gpu_matches_oracle_whole_step": agree,
     }
 
 
@@ -258,19 +333,20 @@ def host_cpu_model() -> str | None:
     return None
 
 
-def graph_us_per_call(torch, coll, send, recv, algo, calls=10, replays=20):
+def graph_us_per_call(torch, coll, send, recv, algo, calls=10, replays=20, op=None):
     """Device time per AllReduce call without host overhead: `calls` calls
     captured back to back in one HIP graph, replayed `replays` times."""
+    op = coll.COLL_SUM if op is None else op
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):          # warm-up off the capture
-        coll.coll_allreduce_algo(send, recv, algo, coll.COLL_SUM)
+        coll.coll_allreduce_algo(send, recv, algo, op)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for _ in range(calls):
-            coll.coll_allreduce_algo(send, recv, algo, coll.COLL_SUM)
+            coll.coll_allreduce_algo(send, recv, algo, op)
     g.replay()
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -282,8 +358,9 @@ def graph_us_per_call(torch, coll, send, recv, algo, calls=10, replays=20):
     return a.elapsed_time(b) * 1e3 / (calls * replays)
 
 
-def extra_collectives(torch, coll, inputs, metrics, dev, which, iters=10, warmup=3):
+def extra_collectives(torch, coll, inputs, metrics, dev, which, ceil, iters=10, warmup=3):
     rows = []
+    MiB = 1 << 20
     want = lambda k: which is None or k in which  # noqa: E731
 
     # --- DP gradient AllReduce, p = 8, 256 MiB fp32 per rank ~ N(0, 1) -------
@@ -305,24 +382,29 @@ def extra_collectives(torch, coll, inputs, metrics, dev, which, iters=10, warmup
                 continue
             f = coll.coll_allreduce_algo(send, recv, algo, coll.COLL_SUM, defer=True)
             med, p95, _ = stats_us(time_launches(torch, [f], iters, warmup)[0])
-            rows.append(coll_entry(metrics, label, "allreduce", p, n, 4, med, aname,
-                                   {"dtype": "f32", "op": "sum", "t_p95_us": round(p95, 2),
-                                    "workload": "DP gradient AllReduce, 256 MiB fp32 per rank"}))
+            row = coll_entry(metrics, label, "allreduce", p, n, 4, med, aname,
+                             {"dtype": "f32", "op": "sum", "t_p95_us": round(p95, 2),
+                              "workload": "DP gradient AllReduce, 256 MiB fp32 per rank"})
+            if aname == "ring":
+                ceil.attach(row, p, p, n * 4)
+            rows.append(row)
         # Scaled variants on the same buffers: AVG (sum then one division by
         # p) and PreMulSum with per-rank weights w_r = 1/p.
         if want("ar_avg"):
             f = coll.coll_allreduce_algo(send, recv, coll.COLL_ALGO_RING, coll.COLL_AVG, defer=True)
             med, p95, _ = stats_us(time_launches(torch, [f], iters, warmup)[0])
-            rows.append(coll_entry(metrics, "allreduce_avg_ring", "allreduce", p, n, 4, med, "ring",
-                                   {"dtype": "f32", "op": "avg", "t_p95_us": round(p95, 2),
-                                    "workload": "DP gradient AllReduce, 256 MiB fp32 per rank"}))
+            rows.append(ceil.attach(coll_entry(metrics, "allreduce_avg_ring", "allreduce", p, n, 4, med, "ring",
+                                               {"dtype": "f32", "op": "avg", "t_p95_us": round(p95, 2),
+                                                "workload": "DP gradient AllReduce, 256 MiB fp32 per rank"}),
+                                    p, p, n * 4))
         if want("ar_premul"):
             scales = np.full(p, 1.0 / p, dtype=np.float32)
             f = coll.coll_allreduce_premul(send, recv, scales, coll.COLL_ALGO_RING, defer=True)
             med, p95, _ = stats_us(time_launches(torch, [f], iters, warmup)[0])
-            rows.append(coll_entry(metrics, "allreduce_premulsum_ring", "allreduce", p, n, 4, med, "ring",
-                                   {"dtype": "f32", "op": "premulsum", "t_p95_us": round(p95, 2),
-                                    "workload": "DP gradient AllReduce, 256 MiB fp32 per rank"}))
+            rows.append(ceil.attach(coll_entry(metrics, "allreduce_premulsum_ring", "allreduce", p, n, 4, med,
+                                               "ring", {"dtype": "f32", "op": "premulsum", "t_p95_us": round(p95, 2),
+                                                        "workload": "DP gradient AllReduce, 256 MiB fp32 per rank"}),
+                                    p, p, n * 4))
         del send, recv
         torch.cuda.empty_cache()
 
@@ -336,16 +418,18 @@ def extra_collectives(torch, coll, inputs, metrics, dev, which, iters=10, warmup
             recv = [torch.empty(per, dtype=torch.bfloat16, device=dev) for _ in range(p)]
             f = coll.coll_alltoall(send, recv, per // p, defer=True)
             med, p95, _ = stats_us(time_launches(torch, [f], iters, warmup)[0])
-            rows.append(coll_entry(metrics, "alltoall_equal", "alltoall", p, per // p, 2, med, "ring",
-                                   {"dtype": "bf16", "t_p95_us": round(p95, 2),
-                                    "workload": "MoE dispatch, 512 tokens x 7168 per destination"}))
+            rows.append(ceil.attach(coll_entry(metrics, "alltoall_equal", "alltoall", p, per // p, 2, med, "ring",
+                                               {"dtype": "bf16", "t_p95_us": round(p95, 2),
+                                                "workload": "MoE dispatch, 512 tokens x 7168 per destination"}),
+                                    1, 1, p * per * 2))
             # the same transpose with every vector staged in LDS (gfx950
             # global-to-LDS loads), timed on the same buffers
             f = coll.coll_alltoall_algo(send, recv, coll.COLL_A2A_LDS_STAGED, per // p, defer=True)
             med, p95, _ = stats_us(time_launches(torch, [f], iters, warmup)[0])
-            rows.append(coll_entry(metrics, "alltoall_equal_lds_staged", "alltoall", p, per // p, 2, med, "ring",
-                                   {"dtype": "bf16", "t_p95_us": round(p95, 2),
-                                    "workload": "MoE dispatch, 512 tokens x 7168 per destination"}))
+            rows.append(ceil.attach(coll_entry(metrics, "alltoall_equal_lds_staged", "alltoall", p, per // p, 2, med,
+                                               "ring", {"dtype": "bf16", "t_p95_us": round(p95, 2),
+                                                        "workload": "MoE dispatch, 512 tokens x 7168 per destination"}),
+                                    1, 1, p * per * 2))
             del recv
         if want("a2av"):
             ctok = inputs.moe_token_counts(p, tokens)
@@ -369,22 +453,23 @@ def extra_collectives(torch, coll, inputs, metrics, dev, which, iters=10, warmup
                 "zero_ratio": float((ctok == 0).mean()),
                 "workload": "MoE dispatch, per-source token counts ~ Multinomial(4096, 1/8)",
             })
+            ceil.attach(rows[-1], 1, 1, p * per * 2)
             del recv, cdev
         del send
         torch.cuda.empty_cache()
 
     # --- MoE dispatch and combine around the ragged exchange -----------------
     if want("moe"):
-        rows.append(moe_row(torch, coll, inputs, dev, iters, warmup))
+        rows.append(moe_row(torch, coll, inputs, dev, iters, warmup, ceil))
         torch.cuda.empty_cache()
     if want("moe_fp8"):
-        rows.append(moe_fp8_row(torch, coll, inputs, dev, iters, warmup))
+        rows.append(moe_fp8_row(torch, coll, inputs, dev, iters, warmup, ceil))
         torch.cuda.empty_cache()
     if want("moe_direct"):
-        rows.append(moe_direct_row(torch, coll, inputs, dev, iters, warmup, fp8=False))
+        rows.append(moe_direct_row(torch, coll, inputs, dev, iters, warmup, ceil, fp8=False))
         torch.cuda.empty_cache()
     if want("moe_fp8_direct"):
-        rows.append(moe_direct_row(torch, coll, inputs, dev, iters, warmup, fp8=True))
+        rows.append(moe_direct_row(torch, coll, inputs, dev, iters, warmup, ceil, fp8=True))
         torch.cuda.empty_cache()
 
     # --- Gather / Scatter, p = 8, 2^23 bf16 per rank (root buffer 128 MiB) ----
@@ -397,9 +482,10 @@ def extra_collectives(torch, coll, inputs, metrics, dev, which, iters=10, warmup
         tg, ts = time_launches(torch, [fg, fs], iters, warmup)
         for name, kind, ms in (("gather", "gather", tg), ("scatter", "scatter", ts)):
             med, p95, _ = stats_us(ms)
-            rows.append(coll_entry(metrics, name, kind, p, n, 2, med, "ring",
-                                   {"dtype": "bf16", "t_p95_us": round(p95, 2), "root": 0,
-                                    "workload": "p=8, 2^23 bf16 per rank, 128 MiB root buffer"}))
+            rows.append(ceil.attach(coll_entry(metrics, name, kind, p, n, 2, med, "ring",
+                                               {"dtype": "bf16", "t_p95_us": round(p95, 2), "root": 0,
+                                                "workload": "p=8, 2^23 bf16 per rank, 128 MiB root buffer"}),
+                                    1, 1, p * n * 2))
         del ranks, root_buf
         torch.cuda.empty_cache()
 
@@ -428,12 +514,18 @@ def extra_collectives(torch, coll, inputs, metrics, dev, which, iters=10, warmup
                 cold.append(ev)
             torch.cuda.synchronize()
             cmed, cp95, _ = stats_us([a.elapsed_time(b) for a, b in cold])
-            rows.append(coll_entry(metrics, f"allreduce_small_{oname}", "allreduce", p, n, 4, med, "ring",
-                                   {"dtype": dname, "op": oname, "t_p95_us": round(p95, 2),
-                                    "t_cold_med_us": round(cmed, 2), "t_cold_p95_us": round(cp95, 2),
-                                    "hbm_GBps_cold": round(2 * p * n * 4 / (cmed * 1e-6) / 1e9, 1),
-                                    "workload": "AllReduce p=4, 2^20 per rank; t_med back to back (warm, "
-                                                "Infinity-Cache resident), t_cold after a 512 MiB overwrite"}))
+            g_us = None if NO_GRAPHS else graph_us_per_call(torch, coll, send, recv, coll.COLL_ALGO_RING, calls=20,
+                                                            replays=20, op=op)
+            rows.append(ceil.attach(coll_entry(
+                metrics, f"allreduce_small_{oname}", "allreduce", p, n, 4, med, "ring",
+                {"dtype": dname, "op": oname, "t_p95_us": round(p95, 2),
+                 "t_cold_med_us": round(cmed, 2), "t_cold_p95_us": round(cp95, 2),
+                 "hbm_GBps_cold": round(2 * p * n * 4 / (cmed * 1e-6) / 1e9, 1),
+                 "t_graph_us": g_us and round(g_us, 2),
+                 "hbm_GBps_graph": g_us and round(2 * p * n * 4 / (g_us * 1e-6) / 1e9, 1),
+                 "workload": "AllReduce p=4, 2^20 per rank; t_med back to back (warm, Infinity-Cache resident), "
+                             "t_cold after a 512 MiB overwrite, t_graph per call replayed from a HIP graph"}),
+                p, p, n * 4))
         del scratch
 
     # --- latency of every schedule at the batch's small sizes, p = 16 ---------
@@ -456,7 +548,8 @@ def extra_collectives(torch, coll, inputs, metrics, dev, which, iters=10, warmup
                 f = coll.coll_allreduce_algo(send, recv, algo, coll.COLL_SUM, defer=True)
                 med, _, _ = stats_us(time_launches(torch, [f], 50, 10)[0])
                 entry[key + "_us"] = round(med, 2)
-                entry[key + "_graph_us"] = round(graph_us_per_call(torch, coll, send, recv, algo), 2)
+                if not NO_GRAPHS:
+                    entry[key + "_graph_us"] = round(graph_us_per_call(torch, coll, send, recv, algo), 2)
             table.append(entry)
             del send, recv
         rows.append({"name": "allreduce_schedule_latency", "p": p, "dtype": "f32", "op": "sum", "table": table,
@@ -464,7 +557,7 @@ def extra_collectives(torch, coll, inputs, metrics, dev, which, iters=10, warmup
 
     # --- 10,000 small AllReduces in one launch, p = 16 -----------------------
     if want("batch"):
-        rows.append(batch_row(torch, coll, inputs, dev))
+        rows.append(batch_row(torch, coll, inputs, dev, ceil))
 
     # --- copy ceiling ---------------------------------------------------------
     if want("copy"):
@@ -497,7 +590,7 @@ def extra_collectives(torch, coll, inputs, metrics, dev, which, iters=10, warmup
                     full[r][s_ * n:(s_ + 1) * n].copy_(shard[s_])
         f = coll.coll_allgather(shard, full, defer=True)
         t_ce, t_k = [stats_us(x)[0] for x in time_launches(torch, [ag_memcpy, f], iters, warmup)]
-        b_ag = 2 * p * p * n * 2
+        b_ag = (p + p * p) * n * 2   # each shard read once, written p times (the copy engine reads it p times)
         rows.append({"name": "allgather_vs_copy_engine", "p": p, "elem_bytes": 2, "hbm_bytes": b_ag,
                      "memcpy_64_calls_us": round(t_ce, 2), "coll_allgather_us": round(t_k, 2),
                      "memcpy_GBps": round(b_ag / (t_ce * 1e-6) / 1e9, 1),
@@ -526,7 +619,7 @@ def extra_collectives(torch, coll, inputs, metrics, dev, which, iters=10, warmup
     return rows
 
 
-def moe_row(torch, coll, inputs, dev, iters, warmup):
+def moe_row(torch, coll, inputs, dev, iters, warmup, ceil):
     """Pack -> dispatch Alltoallv -> reverse Alltoallv -> weighted combine
     (in place on a residual), p = 8, 4096 tokens x 7168 bf16 per rank,
     top-2 routing uniform over ranks; each stage timed on its own."""
@@ -556,9 +649,12 @@ def moe_row(torch, coll, inputs, dev, iters, warmup):
     b_xchg = p * 2 * A * H * d                       # each exchange reads and writes every row once
     b_comb = p * (A * H * d + 2 * T * H * d + A * 8)  # A rows + residual in, T rows out, pos + weights
     stage = {}
-    for name, us, b in (("pack", t[0], b_pack), ("dispatch_alltoallv", t[1], b_xchg),
-                        ("reverse_alltoallv", t[2], b_xchg), ("combine", t[3], b_comb)):
-        stage[name] = {"t_med_us": round(us, 2), "hbm_bytes": b, "hbm_GBps": round(b / (us * 1e-6) / 1e9, 1)}
+    tok_bytes = p * T * H * d
+    for name, us, b, mix in (("pack", t[0], b_pack, (1, 2)), ("dispatch_alltoallv", t[1], b_xchg, (1, 1)),
+                             ("reverse_alltoallv", t[2], b_xchg, (1, 1)), ("combine", t[3], b_comb, (3, 1))):
+        stage[name] = ceil.attach({"t_med_us": round(us, 2), "hbm_bytes": b,
+                                   "hbm_GBps": round(b / (us * 1e-6) / 1e9, 1)}, *mix,
+                                  tok_bytes * (k if mix == (1, 1) else 1))
     tot_us = sum(t)
     tot_b = b_pack + 2 * b_xchg + b_comb
     return {"name": "moe_dispatch_combine", "p": p, "tokens": T, "hidden": H, "top_k": k, "dtype": "bf16",
@@ -567,7 +663,7 @@ def moe_row(torch, coll, inputs, dev, iters, warmup):
             "workload": "pack -> Alltoallv -> reverse Alltoallv -> weighted combine + residual"}
 
 
-def moe_fp8_row(torch, coll, inputs, dev, iters, warmup):
+def moe_fp8_row(torch, coll, inputs, dev, iters, warmup, ceil):
     """The same MoE layer with the dispatch in FP8 e4m3 (one fp32 scale per
     128 elements): quantizing pack -> byte Alltoallv -> dequant (the experts'
     bf16 input) -> bf16 reverse Alltoallv -> weighted combine + residual."""
@@ -602,10 +698,14 @@ def moe_fp8_row(torch, coll, inputs, dev, iters, warmup):
     b_rev = p * 2 * A * H * 2
     b_comb = p * (A * H * 2 + 2 * T * H * 2 + A * 8)
     stage = {}
-    for name, us, b in (("pack_fp8", t[0], b_pack), ("dispatch_alltoallv_fp8", t[1], b_disp),
-                        ("dequant_fp8", t[2], b_deq), ("reverse_alltoallv_bf16", t[3], b_rev),
-                        ("combine", t[4], b_comb)):
-        stage[name] = {"t_med_us": round(us, 2), "hbm_bytes": b, "hbm_GBps": round(b / (us * 1e-6) / 1e9, 1)}
+    tok_bytes = p * T * H * 2
+    for name, us, b, mix, sb in (("pack_fp8", t[0], b_pack, (1, 1), tok_bytes),
+                                 ("dispatch_alltoallv_fp8", t[1], b_disp, (1, 1), tok_bytes),
+                                 ("dequant_fp8", t[2], b_deq, (1, 2), tok_bytes),
+                                 ("reverse_alltoallv_bf16", t[3], b_rev, (1, 1), 2 * tok_bytes),
+                                 ("combine", t[4], b_comb, (3, 1), tok_bytes)):
+        stage[name] = ceil.attach({"t_med_us": round(us, 2), "hbm_bytes": b,
+                                   "hbm_GBps": round(b / (us * 1e-6) / 1e9, 1)}, *mix, sb)
     tot_us = sum(t)
     tot_b = b_pack + b_disp + b_deq + b_rev + b_comb
     return {"name": "moe_fp8_dispatch_bf16_combine", "p": p, "tokens": T, "hidden": H, "top_k": k, "group": G,
@@ -617,7 +717,7 @@ def moe_fp8_row(torch, coll, inputs, dev, iters, warmup):
             "workload": "FP8 pack -> byte Alltoallv -> dequant -> bf16 reverse Alltoallv -> combine + residual"}
 
 
-def moe_direct_row(torch, coll, inputs, dev, iters, warmup, fp8: bool):
+def moe_direct_row(torch, coll, inputs, dev, iters, warmup, ceil, fp8: bool):
     """The MoE layer without staging copies: the dispatch writes rows straight
     into the receive buffers (bf16, or FP8 with one scale per 128 elements
     followed by the dequant the experts read), the combine reads the expert
@@ -657,8 +757,10 @@ def moe_direct_row(torch, coll, inputs, dev, iters, warmup, fp8: bool):
     stages.append(("combine_direct", p * (A * H * 2 + 2 * T * H * 2 + A * 12)))
     t = [stats_us(x)[0] for x in time_launches(torch, fns, iters, warmup)]
     st = {}
+    mixes = {"dispatch_fp8_direct": (1, 1), "dequant_fp8": (1, 2), "dispatch_direct": (1, 2), "combine_direct": (3, 1)}
     for (name, b), us in zip(stages, t):
-        st[name] = {"t_med_us": round(us, 2), "hbm_bytes": b, "hbm_GBps": round(b / (us * 1e-6) / 1e9, 1)}
+        st[name] = ceil.attach({"t_med_us": round(us, 2), "hbm_bytes": b, "hbm_GBps": round(b / (us * 1e-6) / 1e9, 1)},
+                               *mixes[name], p * T * H * 2)
     tot_us = sum(t)
     tot_b = sum(b for _, b in stages)
     return {"name": "moe_fp8_direct" if fp8 else "moe_direct", "p": p, "tokens": T, "hidden": H, "top_k": k,
@@ -669,7 +771,7 @@ def moe_direct_row(torch, coll, inputs, dev, iters, warmup, fp8: bool):
                          "direct dispatch -> combine reading expert outputs in place")}
 
 
-def batch_row(torch, coll, inputs, dev, iters=5, warmup=2):
+def batch_row(torch, coll, inputs, dev, ceil, iters=5, warmup=2):
     p = 16
     plan, out_elems = inputs.small_batch_plan(10000)
     pf, pi = inputs.small_batch_pools(p)
@@ -697,7 +799,9 @@ def batch_row(torch, coll, inputs, dev, iters=5, warmup=2):
     med, p95, _ = stats_us(time_launches(torch, [f], iters, 1)[0])
     hbm = 2 * p * total_bytes
     indiv = individual_calls(torch, coll, calls, p)
-    return {
+    del dpf, dpi, outs
+    torch.cuda.empty_cache()
+    row = {
         "name": "allreduce_batch_10000", "p": p, "calls": len(plan), "dtype": "f32/i32", "op": "sum/min/max",
         "payload_bytes": total_bytes,
         "t_med_us": round(med, 1), "t_p95_us": round(p95, 1), "wall_us_per_batch": round(wall_us, 1),
@@ -708,6 +812,13 @@ def batch_row(torch, coll, inputs, dev, iters=5, warmup=2):
         "workload": "10,000 AllReduces, sizes log-uniform 4 KiB-1 MiB, one launch",
         "individual_calls": indiv,
     }
+    # ceilings: p reads : p writes at the plan's output footprint (streams of
+    # the per-rank output pool), and at a 128 MiB footprint
+    ceil.attach(row, p, p, (out_elems * 4 + 255) // 256 * 256)
+    small = ceil.get(p, p, 128 << 20)
+    if small is not None:
+        row["mix_ceiling_128MiB_streams_GBps"] = small["GBps"]
+    return row
 
 
 def individual_calls(torch, coll, calls, p, sample=1000):
@@ -757,7 +868,9 @@ def individual_calls(torch, coll, calls, p, sample=1000):
 # ----------------------------------------------------------------------------
 
 def main(argv=None) -> int:
+    global NO_GRAPHS
     args = parse_args(argv)
+    NO_GRAPHS = args.no_graphs
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: all p logical ranks live in one device's HBM and "
               "nothing here runs across GPUs; run it with --gpus 1.", file=sys.stderr)
@@ -819,8 +932,18 @@ def main(argv=None) -> int:
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK, 4), "traffic": read_traffic(kkey, dom_bytes),
                 "kernel": dom, "algorithmic_bytes_per_launch": dom_bytes, "mean_launch_us": round(dom_us, 2)}
-    # An attainable reference measured in the same run: a 1 GiB device copy
-    # (1 read : 1 write) by the library's copy kernel (Broadcast at p = 1).
+    # Attainable references measured in the same run: the dominant kernel's
+    # own read:write stream mix at its stream size (the library's
+    # direction-mix probe), and a 1 GiB device copy by the library's copy
+    # kernel (Broadcast at p = 1).
+    ceil = Ceilings(torch, coll, dev, enabled=not args.no_ceilings)
+    mix = ceil.get(p, 1, total * 2) if kkey == "reduce_scatter" else ceil.get(1, p, p * n * 2)
+    if mix is not None:
+        roofline["attainable_mix_GBps"] = mix["GBps"]
+        roofline["mix"] = mix["mix"]
+        roofline["frac_of_mix_ceiling"] = round(achieved / mix["GBps"], 4)
+        ceil.attach(per_coll["reduce_scatter"], p, 1, total * 2)
+        ceil.attach(per_coll["allgather"], 1, p, p * n * 2)
     cbytes = 1 << 30
     ca = torch.empty(cbytes // 4, dtype=torch.int32, device=dev).fill_(1)
     cb = torch.empty_like(ca)
@@ -832,8 +955,8 @@ def main(argv=None) -> int:
 
     cpu = None
     if not args.no_cpu_baseline:
-        print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(wl, args.cpu_seconds)
+        print("# cpu baseline (threaded C++ oracle, whole step)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(torch, wl, args.cpu_seconds)
 
     del wl, rs, ag
     torch.cuda.empty_cache()
@@ -841,7 +964,11 @@ def main(argv=None) -> int:
     if not args.no_collectives:
         which = set(args.only.split(",")) if args.only else None
         print("# per-collective table", file=sys.stderr, flush=True)
-        rows = extra_collectives(torch, coll, inputs, metrics, dev, which)
+        rows = extra_collectives(torch, coll, inputs, metrics, dev, which, ceil)
+    for row in rows:
+        print("# detail " + json.dumps(row), file=sys.stderr, flush=True)
+    print("# ceilings " + json.dumps({f"{k[0]}r:{k[1]}w:{k[2]}": v for k, v in ceil.cache.items()}),
+          file=sys.stderr, flush=True)
 
     line = {
         "metric": METRIC,
@@ -854,7 +981,7 @@ def main(argv=None) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16 (fp32 accumulation)",
         "data": "synthetic (seeded NumPy PCG64, bf16 ~ N(0, 1e-3))",
         "config": {
             "workload": "zero_rs_ag: ReduceScatter(sum) then AllGather, p=8 logical ranks, "
@@ -863,14 +990,37 @@ def main(argv=None) -> int:
             "hbm_bytes_per_step": hbm_rs + hbm_ag,
             "pct_hbm_peak": round(100.0 * value / HBM_PEAK, 1),
         },
-        "per_collective": per_coll,
+        "per_collective": {k: compact_row(v) for k, v in per_coll.items()},
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "collectives": rows,
+        "collectives": [compact_row(r) for r in rows],
         "source_hash": {k: source_hash(k) for k in KERNEL_SOURCES},
     }
-    print(json.dumps(line), flush=True)
+    print(json.dumps(line, separators=(",", ":")), flush=True)
     return 0
+
+
+def compact_row(row: dict) -> dict:
+    """The figures of a table row that the summary line keeps: time, HBM
+    GB/s and share of peak, busbw, and the fraction of the row's mix
+    ceiling; nested stages and latency tables in the same short form."""
+    keep = ("name", "t_med_us", "hbm_GBps", "pct_hbm_peak", "busbw_GBps", "mix_ceiling_GBps",
+            "frac_of_mix_ceiling", "t_cold_med_us", "t_graph_us", "mix_ceiling_128MiB_streams_GBps")
+    out = {k: row[k] for k in keep if k in row}
+    if "stages" in row:
+        out["stages"] = {k: {kk: v[kk] for kk in ("t_med_us", "hbm_GBps", "frac_of_mix_ceiling") if kk in v}
+                         for k, v in row["stages"].items()}
+    if "table" in row:
+        out["table"] = [{k: v for k, v in e.items() if k.endswith("graph_us") or k == "bytes_per_rank"}
+                        for e in row["table"]]
+    if "individual_calls" in row:
+        ic = row["individual_calls"]
+        out["individual_calls"] = {k: ic[k] for k in ("back_to_back_us_per_call", "latency_p50_us",
+                                                     "latency_p99_us", "alpha_us") if k in ic}
+    for k in ("memcpy_GBps", "coll_GBps", "speedup", "torch_copy_GBps", "coll_copy_kernel_GBps"):
+        if k in row:
+            out[k] = row[k]
+    return out
 
 
 if __name__ == "__main__":

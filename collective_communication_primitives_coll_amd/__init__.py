@@ -27,6 +27,7 @@ COLL_BATCH_CHECK_ALIAS = 1
 
 COLL_U8 = 3
 COLL_A2A_DIRECT, COLL_A2A_LDS_STAGED = 0, 1
+COLL_PROBE_NT_LOADS, COLL_PROBE_NT_STORES = 1, 2
 ELEM_BYTES = {COLL_F32: 4, COLL_BF16: 2, COLL_I32: 4, COLL_U8: 1}
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcoll.so")
@@ -84,6 +85,7 @@ def lib() -> ctypes.CDLL:
         "coll_moe_dispatch": [pp, pp, pp, pp, vp, vp, i32, sz, i32, sz, i64p, i32, vp],
         "coll_moe_dispatch_fp8": [pp, pp, pp, pp, vp, vp, vp, i32, sz, i32, sz, sz, i64p, vp],
         "coll_moe_combine_direct": [pp, pp, pp, pp, pp, i32, sz, i32, sz, i64p, i32, vp],
+        "coll_stream_probe": [pp, i32, pp, i32, sz, i32, ctypes.c_uint, vp, vp],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -623,6 +625,18 @@ def coll_last_hip_error() -> int:
 
 def coll_version() -> int:
     return lib().coll_version()
+
+
+def coll_stream_probe(src, dst, nbytes: int, unroll: int = 4, flags: int = 0, sink=None, stream=None,
+                      defer: bool = False):
+    """Direction-mix bandwidth probe: len(src) read and len(dst) write
+    streams of nbytes each, `unroll` vectors per lane per tile (a
+    measurement helper, not a collective)."""
+    s, ks = _ptr_array(src) if len(src) else (None, None)
+    d, kd = _ptr_array(dst) if len(dst) else (None, None)
+    return _run("coll_stream_probe", (s, len(src), d, len(dst), int(nbytes), int(unroll), int(flags),
+                                      _addr(sink) if sink is not None else None, _stream(stream)),
+                "coll_stream_probe", defer, (ks, kd, src, dst, sink))
 
 
 def coll_set_grid_limit(workgroups_per_cu: int) -> None:

@@ -27,6 +27,7 @@ SOURCES = [
     "batch_kernels.hip",
     "moe_kernels.hip",
     "fp8_kernels.hip",
+    "probe_kernels.hip",
 ]
 
 ARCH = "gfx950"

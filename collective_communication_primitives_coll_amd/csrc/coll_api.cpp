@@ -1213,6 +1213,36 @@ COLL_EXPORT coll_status_t coll_allreduce_batch(const coll_call_t* calls, int nca
 }
 
 // ---------------------------------------------------------------------------
+// Direction-mix bandwidth probe (measurement helper)
+// ---------------------------------------------------------------------------
+COLL_EXPORT coll_status_t coll_stream_probe(const void* const* src, int nsrc, void* const* dst, int ndst,
+                                            size_t bytes, int unroll, unsigned flags, void* sink, void* stream) {
+  if (nsrc < 0 || ndst < 0 || nsrc > kMaxRanks || ndst > kMaxRanks || nsrc + ndst == 0) return COLL_ERR_INVALID_ARG;
+  if (flags & ~(unsigned)(COLL_PROBE_NT_LOADS | COLL_PROBE_NT_STORES)) return COLL_ERR_INVALID_ARG;
+  if (bytes % 16 || unroll < 1) return COLL_ERR_INVALID_ARG;
+  if (!coll::probe_mix_supported(nsrc, ndst) || !coll::probe_unroll_supported(nsrc, unroll))
+    return COLL_ERR_UNSUPPORTED;
+  if (bytes == 0) return COLL_OK;
+  if (nsrc && !all_non_null(src, nsrc)) return COLL_ERR_INVALID_ARG;
+  if (ndst && !all_non_null(dst, ndst)) return COLL_ERR_INVALID_ARG;
+  if (ndst == 0 && (!sink || (uintptr_t)sink % 16)) return COLL_ERR_INVALID_ARG;
+  for (int k = 0; k < nsrc; ++k)
+    if ((uintptr_t)src[k] % 16) return COLL_ERR_INVALID_ARG;
+  for (int d = 0; d < ndst; ++d)
+    if ((uintptr_t)dst[d] % 16) return COLL_ERR_INVALID_ARG;
+  std::vector<Range> rs;
+  for (int k = 0; k < nsrc; ++k) rs.push_back(rng(src[k], bytes, false, k));
+  for (int d = 0; d < ndst; ++d) rs.push_back(rng(dst[d], bytes, true, d));
+  if (!ranges_disjoint_sorted(rs)) return COLL_ERR_ALIAS;
+  int grid;
+  int e = max_grid(&grid, kFamReduce);
+  if (e) return hip_fail(e);
+  coll::RankPtrs P = make_ptrs(src, nsrc, dst, ndst);
+  return finish(coll::launch_probe(nsrc, ndst, P, bytes / 16, unroll, flags & COLL_PROBE_NT_LOADS,
+                                   flags & COLL_PROBE_NT_STORES, sink, grid, stream));
+}
+
+// ---------------------------------------------------------------------------
 // Misc
 // ---------------------------------------------------------------------------
 COLL_EXPORT const char* coll_status_string(coll_status_t s) {

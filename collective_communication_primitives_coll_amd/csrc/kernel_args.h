@@ -215,6 +215,14 @@ int launch_moe_dispatch(int elem_bytes, const MoeDirectArgs& a, int max_grid, vo
 int launch_moe_dispatch_fp8(const MoeDirectArgs& a, int max_grid, void* stream);
 int launch_moe_combine_direct(int dtype, const MoeRowArgs& a, int max_grid, void* stream);
 
+// Direction-mix bandwidth probe: ns source and nd destination streams of
+// nvec 16-byte vectors each, `unroll` vectors per lane per tile
+// (probe_mix_supported and probe_unroll_supported list what is built).
+bool probe_mix_supported(int ns, int nd);
+bool probe_unroll_supported(int ns, int unroll);
+int launch_probe(int ns, int nd, const RankPtrs& ptrs, uint64_t nvec, int unroll, bool nt_loads, bool nt_stores,
+                 void* sink, int max_grid, void* stream);
+
 // 16-byte vectors each lane of a copy kernel keeps in flight.
 constexpr uint64_t kCopyUnroll = 4;
 

@@ -391,6 +391,31 @@ typedef struct {
 coll_status_t coll_allreduce_batch(const coll_call_t* calls, int ncalls, int p,
                                    unsigned flags, void* stream);
 
+/* Direction-mix bandwidth probe: a measurement helper, not a collective.
+ * [A] 4.1 models a collective's time by the bandwidth of each resource it
+ * uses, and [A] 2.5 compares bus bandwidth with what the hardware
+ * sustains; on one device the resource is HBM, and what it sustains
+ * depends on how many read and write streams are in flight.  This call
+ * streams `nsrc` sources and `ndst` destinations of `bytes` bytes each
+ * through the collectives' 16-byte vector tiles of `unroll` vectors per
+ * lane (1, 2, 4 or 8, with nsrc * unroll <= 32; every load of a tile is
+ * issued before its first store), with the reductions' launch bounds and
+ * default grid (coll_set_grid_limit applies):
+ * every destination receives the XOR of the sources' 32-bit words (a
+ * fixed pattern when nsrc == 0).  With ndst == 0 the loads are folded into
+ * one value per lane that is written to `sink` (16 device bytes, 16-byte
+ * aligned) only if it equals an internal pattern, so the reads stay.
+ * flags: COLL_PROBE_NT_LOADS / COLL_PROBE_NT_STORES select non-temporal
+ * loads / stores (else cached).  Supported (nsrc, ndst): (1|4|8|16, 0),
+ * (0, 1|4|8|16), (1|2|3|4|8|16, 1), (1, 2|4|8|16), (4, 4), (8, 8),
+ * (16, 16); other pairs and tile sizes return COLL_ERR_UNSUPPORTED.  Every pointer
+ * 16-byte aligned and bytes a multiple of 16 (else COLL_ERR_INVALID_ARG);
+ * destinations may not overlap each other or a source (COLL_ERR_ALIAS). */
+#define COLL_PROBE_NT_LOADS 1u
+#define COLL_PROBE_NT_STORES 2u
+coll_status_t coll_stream_probe(const void* const* src, int nsrc, void* const* dst, int ndst, size_t bytes,
+                                int unroll, unsigned flags, void* sink, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* coll_status_string(coll_status_t status);
 

@@ -296,3 +296,31 @@ def test_direct_moe_invalid_arguments_rejected():
     assert L.coll_moe_combine_direct(rcv, odd, w, None, out, 4, T, k, H, caps, 1, None) == INV
     assert L.coll_moe_combine_direct(rcv, loc, w, None, rcv, 4, T, k, H, caps, 1, None) == AL      # out = y
     assert L.coll_moe_combine_direct(rcv, loc, w, None, out, 4, 0, k, H, caps, 1, None) == coll.COLL_OK  # T = 0
+
+
+@host_only
+def test_stream_probe_rejects_invalid_calls():
+    L = coll.lib()
+    a, ka = _arr([0x10000, 0x20000])
+    b, kb = _arr([0x40000])
+    sink = 0x80000
+    # no stream at all, bytes not a multiple of 16, unknown flag
+    assert L.coll_stream_probe(None, 0, None, 0, 64, 4, 0, sink, None) == coll.COLL_ERR_INVALID_ARG
+    assert L.coll_stream_probe(a, 1, b, 1, 40, 4, 0, None, None) == coll.COLL_ERR_INVALID_ARG
+    assert L.coll_stream_probe(a, 1, b, 1, 64, 4, 4, None, None) == coll.COLL_ERR_INVALID_ARG
+    assert L.coll_stream_probe(a, 1, b, 1, 64, 0, 0, None, None) == coll.COLL_ERR_INVALID_ARG
+    # a mix or a tile size the probe does not build
+    assert L.coll_stream_probe(a, 2, None, 0, 64, 4, 0, sink, None) == coll.COLL_ERR_UNSUPPORTED
+    assert L.coll_stream_probe(a, 1, b, 1, 64, 3, 0, None, None) == coll.COLL_ERR_UNSUPPORTED
+    big, kbig = _arr([0x100000 * (i + 1) for i in range(16)])
+    assert L.coll_stream_probe(big, 16, b, 1, 64, 4, 0, None, None) == coll.COLL_ERR_UNSUPPORTED  # 64 loads
+    # read-only mixes need an aligned sink; pointers must be 16-byte aligned
+    assert L.coll_stream_probe(a, 1, None, 0, 64, 4, 0, None, None) == coll.COLL_ERR_INVALID_ARG
+    assert L.coll_stream_probe(a, 1, None, 0, 64, 4, 0, sink + 4, None) == coll.COLL_ERR_INVALID_ARG
+    c, kc = _arr([0x10004])
+    assert L.coll_stream_probe(c, 1, b, 1, 64, 4, 0, None, None) == coll.COLL_ERR_INVALID_ARG
+    # a destination overlapping a source
+    d, kd = _arr([0x10010])
+    assert L.coll_stream_probe(a, 1, d, 1, 64, 4, 0, None, None) == coll.COLL_ERR_ALIAS
+    # zero bytes is a no-op
+    assert L.coll_stream_probe(a, 1, b, 1, 0, 4, 0, None, None) == coll.COLL_OK

@@ -1433,3 +1433,38 @@ def test_alias_rejections(coll):
         s = [empty(p * n, F32) for _ in range(p)]
         coll.coll_alltoall(s, s)
     assert e.value.status == coll.COLL_ERR_ALIAS
+
+
+# ----------------------------------------------------------------------------
+# Direction-mix probe (measurement helper): what it writes
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("ns,nd", [(1, 1), (3, 1), (8, 8), (1, 4), (0, 4), (8, 0)])
+def test_stream_probe_writes_the_xor_of_its_sources(coll, ns, nd):
+    import torch
+    nbytes = 3 * 4096 * 16 + 48          # several tiles and a ragged last tile
+    words = nbytes // 4
+    rng = np.random.default_rng(ns * 10 + nd)
+    hs = [rng.integers(0, 2**32, words, dtype=np.uint64).astype(np.uint32) for _ in range(ns)]
+    src = [torch.from_numpy(h.view(np.int32)).cuda() for h in hs]
+    dst = [torch.full((words + 4,), 7, dtype=torch.int32, device="cuda") for _ in range(nd)]
+    sink = torch.full((4,), 5, dtype=torch.int32, device="cuda")
+    for flags, unroll in ((0, 1), (3, 2), (1, 4), (2, 8)):
+        if ns * unroll > 32:
+            continue
+        for d in dst:
+            d.fill_(7)
+        coll.coll_stream_probe(src, [d[:words] for d in dst], nbytes, unroll, flags, sink)
+        sync()
+        if ns:
+            want = hs[0].copy()
+            for h in hs[1:]:
+                want ^= h
+        else:
+            j = np.arange(words // 4, dtype=np.uint32)
+            want = np.stack([j, j ^ np.uint32(0x9E3779B9), j, j ^ np.uint32(0x9E3779B9)], axis=1).reshape(-1)
+        for d in dst:
+            got = d.cpu().numpy().view(np.uint32)
+            assert np.array_equal(got[:words], want)
+            assert np.all(got[words:] == 7)            # nothing past the streams
+        assert sink.cpu().tolist() == [5, 5, 5, 5]
