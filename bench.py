@@ -82,6 +82,11 @@ KERNEL_SOURCES = {
     "alltoall_lds": ["coll_api.cpp", "kernel_args.h", "device_common.h", "copy_tile.h", "a2a_lds_kernels.hip"],
     "alltoallv": ["coll_api.cpp", "kernel_args.h", "device_common.h", "copy_tile.h", "copy_kernels.hip"],
     "allreduce": ["coll_api.cpp", "kernel_args.h", "device_common.h", "reduce_tile.h", "reduce_kernels.hip"],
+    "allreduce_small": ["coll_api.cpp", "kernel_args.h", "device_common.h", "reduce_tile.h", "reduce_kernels.hip"],
+    "gather_scatter": ["coll_api.cpp", "kernel_args.h", "device_common.h", "copy_tile.h", "copy_kernels.hip"],
+    "moe": ["coll_api.cpp", "kernel_args.h", "device_common.h", "copy_tile.h", "moe_direct.h", "moe_kernels.hip"],
+    "fp8": ["coll_api.cpp", "kernel_args.h", "device_common.h", "moe_direct.h", "moe_kernels.hip", "fp8_kernels.hip"],
+    "batch": ["coll_api.cpp", "kernel_args.h", "device_common.h", "reduce_tile.h", "batch_kernels.hip"],
 }
 
 
