@@ -24,6 +24,7 @@ COLL_ALGO_RECURSIVE_DOUBLING = COLL_ALGO_ONEPASS
 COLL_ALGO_TREE, COLL_ALGO_DOUBLE_BINARY_TREE = 4, 5
 COLL_MAX_RANKS = 64
 COLL_BATCH_CHECK_ALIAS = 1
+COLL_BATCH_NOALLOC_MAX_BYTES = 4 << 20
 
 COLL_U8 = 3
 COLL_A2A_DIRECT, COLL_A2A_LDS_STAGED = 0, 1
@@ -80,6 +81,7 @@ def lib() -> ctypes.CDLL:
         "coll_moe_combine": [pp, pp, pp, pp, pp, i32, sz, i32, sz, i32, vp],
         "coll_scatter": [vp, pp, i32, sz, i32, i32, vp],
         "coll_allreduce_batch": [ctypes.POINTER(coll_call_t), i32, i32, ctypes.c_uint, vp],
+        "coll_allreduce_batch_noalloc": [ctypes.POINTER(coll_call_t), i32, i32, ctypes.c_uint, vp],
         "coll_moe_pack_fp8": [pp, pp, pp, pp, vp, vp, vp, i32, sz, i32, sz, sz, vp],
         "coll_moe_dequant_fp8": [pp, pp, i32, vp, i64p, vp, sz, sz, vp],
         "coll_moe_dispatch": [pp, pp, pp, pp, vp, vp, i32, sz, i32, sz, i64p, i32, vp],
@@ -599,8 +601,10 @@ def coll_moe_combine(back, pos, weights, out, k: int, hidden: int, residual=None
 
 
 def coll_allreduce_batch(calls: Sequence[tuple], p: int, flags: int = 0, stream=None,
-                         defer: bool = False):
-    """calls: (send list, recv list, n, dtype, op) per AllReduce."""
+                         defer: bool = False, noalloc: bool = False):
+    """calls: (send list, recv list, n, dtype, op) per AllReduce.  noalloc:
+    use coll_allreduce_batch_noalloc (descriptor table in the library's
+    static device array; nothing allocated)."""
     keep = []
     arr = (coll_call_t * len(calls))()
     for k, (send, recv, n, dtype, op) in enumerate(calls):
@@ -611,8 +615,8 @@ def coll_allreduce_batch(calls: Sequence[tuple], p: int, flags: int = 0, stream=
         keep.append((ks, kr))
         arr[k].send, arr[k].recv = s, r
         arr[k].n, arr[k].dtype, arr[k].op = int(n), int(dtype), int(op)
-    return _run("coll_allreduce_batch", (arr, len(calls), int(p), int(flags), _stream(stream)),
-                "coll_allreduce_batch", defer, (arr, keep))
+    fname = "coll_allreduce_batch_noalloc" if noalloc else "coll_allreduce_batch"
+    return _run(fname, (arr, len(calls), int(p), int(flags), _stream(stream)), fname, defer, (arr, keep))
 
 
 def coll_status_string(status: int) -> str:

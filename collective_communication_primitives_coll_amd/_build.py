@@ -28,6 +28,7 @@ SOURCES = [
     "moe_kernels.hip",
     "fp8_kernels.hip",
     "probe_kernels.hip",
+    "batch_noalloc.hip",
 ]
 
 ARCH = "gfx950"

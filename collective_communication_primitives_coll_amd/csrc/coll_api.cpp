@@ -1102,15 +1102,34 @@ bool ranges_disjoint_sorted(std::vector<Range>& rs) {
 
 }  // namespace
 
-COLL_EXPORT coll_status_t coll_allreduce_batch(const coll_call_t* calls, int ncalls, int p, unsigned flags,
-                                               void* stream) {
+namespace {
+
+// Descriptor table of a batch: (ncalls + 1) BatchCall records (the last
+// holds the total tile count), then, 256-byte aligned, ncalls * 2p pointers
+// (per call: p sources, then p destinations).
+struct BatchLayout {
+  size_t rec_bytes = 0;
+  size_t ptr_off = 0;
+  size_t total = 0;
+  uint64_t tiles = 0;
+};
+
+// Checks every call (and, with COLL_BATCH_CHECK_ALIAS, overlaps between
+// calls) and sizes the descriptor table.  Touches no device state.
+coll_status_t batch_validate(const coll_call_t* calls, int ncalls, int p, unsigned flags, BatchLayout* L) {
   if (p < 1 || p > kMaxRanks || ncalls < 0 || (ncalls > 0 && !calls)) return COLL_ERR_INVALID_ARG;
   if (flags & ~COLL_BATCH_CHECK_ALIAS) return COLL_ERR_INVALID_ARG;
-  if (ncalls == 0) return COLL_OK;
+  uint64_t tiles = 0;
   for (int k = 0; k < ncalls; ++k) {
     const coll_call_t& c = calls[k];
     coll_status_t st = check_allreduce(c.send, c.recv, p, c.n, c.dtype, c.op);
     if (st != COLL_OK) return st;
+    if (!c.n) continue;
+    const uint64_t te = coll::batch_tile_elems_host(c.dtype, p);
+    const uint64_t q = (c.n + p - 1) / p;
+    const uint64_t tpc = std::max<uint64_t>(1, (q + te - 1) / te);
+    if (tpc > 0xffffffffull) return COLL_ERR_INVALID_ARG;
+    tiles += (uint64_t)p * tpc;
   }
   if (flags & COLL_BATCH_CHECK_ALIAS) {
     std::vector<Range> rs;
@@ -1127,12 +1146,21 @@ COLL_EXPORT coll_status_t coll_allreduce_batch(const coll_call_t* calls, int nca
     }
     if (!ranges_disjoint_sorted(rs)) return COLL_ERR_ALIAS;
   }
-  // Pack: (ncalls + 1) BatchCall records, then ncalls * 2p pointers.
-  std::vector<coll::BatchCall> recs((size_t)ncalls + 1);
+  L->rec_bytes = ((size_t)ncalls + 1) * sizeof(coll::BatchCall);
+  L->ptr_off = (L->rec_bytes + 255) & ~size_t(255);
+  L->total = L->ptr_off + (size_t)ncalls * 2 * p * sizeof(void*);
+  L->tiles = tiles;
+  return COLL_OK;
+}
+
+// Writes the descriptor table of validated calls into host memory h
+// (L.total bytes).
+void batch_pack(const coll_call_t* calls, int ncalls, int p, const BatchLayout& L, char* h) {
+  coll::BatchCall* recs = (coll::BatchCall*)h;
   uint64_t tiles = 0;
   for (int k = 0; k < ncalls; ++k) {
     const coll_call_t& c = calls[k];
-    coll::BatchCall& b = recs[k];
+    coll::BatchCall b{};
     b.n = c.n;
     b.first_tile = tiles;
     b.dtype = (uint32_t)c.dtype;
@@ -1141,23 +1169,48 @@ COLL_EXPORT coll_status_t coll_allreduce_batch(const coll_call_t* calls, int nca
     const uint64_t te = coll::batch_tile_elems_host(c.dtype, p);
     const uint64_t q = (c.n + p - 1) / p;
     b.tiles_per_chunk = c.n ? (uint32_t)std::max<uint64_t>(1, (q + te - 1) / te) : 0;
-    if (c.n && (q + te - 1) / te > 0xffffffffull) return COLL_ERR_INVALID_ARG;
     tiles += (uint64_t)p * b.tiles_per_chunk;
+    std::memcpy(&recs[k], &b, sizeof(b));
   }
-  recs[ncalls] = coll::BatchCall{};
-  recs[ncalls].first_tile = tiles;
-  if (tiles == 0) return COLL_OK;
-  const size_t rec_bytes = recs.size() * sizeof(coll::BatchCall);
-  const size_t ptr_off = (rec_bytes + 255) & ~size_t(255);
-  const size_t total = ptr_off + (size_t)ncalls * 2 * p * sizeof(void*);
+  coll::BatchCall last{};
+  last.first_tile = tiles;
+  std::memcpy(&recs[ncalls], &last, sizeof(last));
+  std::memset(h + L.rec_bytes, 0, L.ptr_off - L.rec_bytes);
+  const void** hp = (const void**)(h + L.ptr_off);
+  for (int k = 0; k < ncalls; ++k) {
+    for (int r = 0; r < p; ++r) {
+      hp[(size_t)k * 2 * p + r] = calls[k].n ? calls[k].send[r] : nullptr;
+      hp[(size_t)k * 2 * p + p + r] = calls[k].n ? (const void*)calls[k].recv[r] : nullptr;
+    }
+  }
+}
+
+// Launches the batch kernel over a descriptor table already in device
+// memory (or enqueued to arrive there on `stream` first).
+coll_status_t batch_launch(void* table, const BatchLayout& L, int ncalls, int p, void* stream) {
+  int grid;
+  int e = max_grid(&grid, kFamReduce);
+  if (e) return hip_fail(e);
+  coll::BatchArgs a;
+  a.calls = (const coll::BatchCall*)table;
+  a.ptrs = (const void* const*)((char*)table + L.ptr_off);
+  a.ncalls = ncalls;
+  a.p = p;
+  const int g = (int)std::min<uint64_t>(L.tiles, (uint64_t)grid);
+  return finish(coll::launch_batch(a, g, stream));
+}
+
+}  // namespace
+
+COLL_EXPORT coll_status_t coll_allreduce_batch(const coll_call_t* calls, int ncalls, int p, unsigned flags,
+                                               void* stream) {
+  BatchLayout L;
+  coll_status_t st = batch_validate(calls, ncalls, p, flags, &L);
+  if (st != COLL_OK || ncalls == 0 || L.tiles == 0) return st;
 
   int dev = 0;
   int e = current_device(&dev);
   if (e) return hip_fail(e);
-  int grid;
-  e = max_grid(&grid, kFamReduce);
-  if (e) return hip_fail(e);
-
   std::lock_guard<std::mutex> lock(g_batch.mu);
   if (g_batch.device != -1 && g_batch.device != dev) batch_release();
   g_batch.device = dev;
@@ -1170,8 +1223,8 @@ COLL_EXPORT coll_status_t coll_allreduce_batch(const coll_call_t* calls, int nca
     e = (int)hipEventCreateWithFlags(&g_batch.done, hipEventDisableTiming);
     if (e) return hip_fail(e);
   }
-  if (g_batch.dev_cap < total) {
-    const size_t cap = std::max(total, g_batch.dev_cap * 2);
+  if (g_batch.dev_cap < L.total) {
+    const size_t cap = std::max(L.total, g_batch.dev_cap * 2);
     if (g_batch.dev_buf) hipFree(g_batch.dev_buf);
     g_batch.dev_buf = nullptr;
     g_batch.dev_cap = 0;
@@ -1179,7 +1232,7 @@ COLL_EXPORT coll_status_t coll_allreduce_batch(const coll_call_t* calls, int nca
     if (e) return hip_fail(e);
     g_batch.dev_cap = cap;
   }
-  if (g_batch.host_cap < total) {
+  if (g_batch.host_cap < L.total) {
     if (g_batch.host_buf) hipHostFree(g_batch.host_buf);
     g_batch.host_buf = nullptr;
     g_batch.host_cap = 0;
@@ -1187,29 +1240,47 @@ COLL_EXPORT coll_status_t coll_allreduce_batch(const coll_call_t* calls, int nca
     if (e) return hip_fail(e);
     g_batch.host_cap = g_batch.dev_cap;
   }
-  char* h = (char*)g_batch.host_buf;
-  std::memcpy(h, recs.data(), rec_bytes);
-  const void** hp = (const void**)(h + ptr_off);
-  for (int k = 0; k < ncalls; ++k) {
-    for (int r = 0; r < p; ++r) {
-      hp[(size_t)k * 2 * p + r] = calls[k].n ? calls[k].send[r] : nullptr;
-      hp[(size_t)k * 2 * p + p + r] = calls[k].n ? (const void*)calls[k].recv[r] : nullptr;
-    }
-  }
+  batch_pack(calls, ncalls, p, L, (char*)g_batch.host_buf);
   hipStream_t s = (hipStream_t)stream;
-  e = (int)hipMemcpyAsync(g_batch.dev_buf, h, total, hipMemcpyHostToDevice, s);
+  e = (int)hipMemcpyAsync(g_batch.dev_buf, g_batch.host_buf, L.total, hipMemcpyHostToDevice, s);
   if (e) return hip_fail(e);
-  coll::BatchArgs a;
-  a.calls = (const coll::BatchCall*)g_batch.dev_buf;
-  a.ptrs = (const void* const*)((char*)g_batch.dev_buf + ptr_off);
-  a.ncalls = ncalls;
-  a.p = p;
-  const int g = (int)std::min<uint64_t>(tiles, (uint64_t)grid);
-  e = coll::launch_batch(a, g, stream);
-  if (e) return hip_fail(e);
+  st = batch_launch(g_batch.dev_buf, L, ncalls, p, stream);
+  if (st != COLL_OK) return st;
   e = (int)hipEventRecord(g_batch.done, s);
   if (e) return hip_fail(e);
   return COLL_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Batched AllReduce that allocates nothing: the descriptor table goes to a
+// static device array (batch_noalloc.hip), staged through a static host
+// buffer with a copy from pageable memory, which HIP has read before the
+// copy call returns.
+// ---------------------------------------------------------------------------
+namespace {
+std::mutex g_noalloc_mu;
+alignas(256) char g_noalloc_host[coll::kNoAllocScratchBytes];
+}  // namespace
+
+COLL_EXPORT coll_status_t coll_allreduce_batch_noalloc(const coll_call_t* calls, int ncalls, int p, unsigned flags,
+                                                       void* stream) {
+  BatchLayout L;
+  coll_status_t st = batch_validate(calls, ncalls, p, flags, &L);
+  if (st != COLL_OK || ncalls == 0 || L.tiles == 0) return st;
+  if (L.total > coll::kNoAllocScratchBytes) return COLL_ERR_INVALID_ARG;
+  int dev = 0;
+  int e = current_device(&dev);
+  if (e) return hip_fail(e);
+  void* table = nullptr;
+  e = coll::noalloc_scratch(dev, &table);
+  if (e) return hip_fail(e);
+  {
+    std::lock_guard<std::mutex> lock(g_noalloc_mu);
+    batch_pack(calls, ncalls, p, L, g_noalloc_host);
+    e = (int)hipMemcpyAsync(table, g_noalloc_host, L.total, hipMemcpyHostToDevice, (hipStream_t)stream);
+    if (e) return hip_fail(e);
+  }
+  return batch_launch(table, L, ncalls, p, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -198,6 +198,13 @@ int launch_batch(const BatchArgs& a, int grid, void* stream);
 // each call's chunks into tiles of this size).
 uint64_t batch_tile_elems_host(int dtype, int p);
 
+// The batch descriptor table of the entry point that allocates nothing: a
+// static device array of kNoAllocScratchBytes per GPU.  noalloc_scratch
+// returns its address on device `dev` (which must be current), looked up
+// once per device.
+constexpr size_t kNoAllocScratchBytes = size_t{4} << 20;
+int noalloc_scratch(int dev, void** out);
+
 // MoE: the index pass (one workgroup per rank), the payload pack and the
 // weighted combine.
 int launch_moe_index(const MoeIndexArgs& a, void* stream);

@@ -391,6 +391,27 @@ typedef struct {
 coll_status_t coll_allreduce_batch(const coll_call_t* calls, int ncalls, int p,
                                    unsigned flags, void* stream);
 
+/* Batched AllReduce that allocates nothing, for callers that cannot call
+ * hipMalloc (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments, validation, semantics, order
+ * and kernels as coll_allreduce_batch, but the descriptor table (call
+ * records and pointer lists) goes to a static device array of
+ * COLL_BATCH_NOALLOC_MAX_BYTES that every GPU the library runs on holds
+ * until the process ends; nothing is allocated and nothing waits on the
+ * host for earlier batches.  The table takes
+ *   ((32 * (ncalls + 1) + 255) / 256) * 256 + 16 * p * ncalls   bytes
+ * (10,000 calls at p = 16 fit); a larger batch returns
+ * COLL_ERR_INVALID_ARG before anything is enqueued.  The table is copied
+ * with hipMemcpyAsync on `stream` from a static host buffer (pageable
+ * memory: HIP has read it when the copy call returns; calls from several
+ * host threads take turns).  All calls on one GPU share that GPU's table,
+ * which keeps the last call's contents: calls on one stream are ordered,
+ * while calls that overlap on different streams of one GPU race (a later
+ * upload can overwrite descriptors an earlier kernel still reads). */
+#define COLL_BATCH_NOALLOC_MAX_BYTES (4u << 20)
+coll_status_t coll_allreduce_batch_noalloc(const coll_call_t* calls, int ncalls, int p, unsigned flags,
+                                           void* stream);
+
 /* Direction-mix bandwidth probe: a measurement helper, not a collective.
  * [A] 4.1 models a collective's time by the bandwidth of each resource it
  * uses, and [A] 2.5 compares bus bandwidth with what the hardware

@@ -324,3 +324,19 @@ def test_stream_probe_rejects_invalid_calls():
     assert L.coll_stream_probe(a, 1, d, 1, 64, 4, 0, None, None) == coll.COLL_ERR_ALIAS
     # zero bytes is a no-op
     assert L.coll_stream_probe(a, 1, b, 1, 0, 4, 0, None, None) == coll.COLL_OK
+
+
+def test_noalloc_batch_rejects_invalid_calls_on_the_host():
+    L = coll.lib()
+    assert L.coll_allreduce_batch_noalloc(None, 0, 4, 0, None) == coll.COLL_OK        # nothing to do
+    assert L.coll_allreduce_batch_noalloc(None, 1, 4, 0, None) == coll.COLL_ERR_INVALID_ARG
+    assert L.coll_allreduce_batch_noalloc(None, -1, 4, 0, None) == coll.COLL_ERR_INVALID_ARG
+    assert L.coll_allreduce_batch_noalloc(None, 0, 0, 0, None) == coll.COLL_ERR_INVALID_ARG
+    assert L.coll_allreduce_batch_noalloc(None, 0, 4, 8, None) == coll.COLL_ERR_INVALID_ARG
+    # calls of n == 0 are valid and launch nothing
+    calls = (coll.coll_call_t * 3)()
+    for c in calls:
+        c.n, c.dtype, c.op = 0, coll.COLL_F32, coll.COLL_SUM
+    assert L.coll_allreduce_batch_noalloc(calls, 3, 4, 0, None) == coll.COLL_OK
+    calls[1].op = 9
+    assert L.coll_allreduce_batch_noalloc(calls, 3, 4, 0, None) == coll.COLL_ERR_INVALID_ARG
