@@ -67,7 +67,7 @@ def parse_args(argv=None):
     ap.add_argument("--only", default=None,
                     help="comma list of extra collectives to time (ar_ring, ar_onepass, ar_hd, "
                          "ar_tree, ar_dbt, ar_literal, ar_avg, ar_premul, a2a, a2av, moe, moe_fp8, moe_direct, moe_fp8_direct, "
-                         "gs, ar_small, ar_latency, batch, copy, ce)")
+                         "gs, ar_small, ar_latency, anyp, batch, copy, ce)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget (all threads)")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the direction-mix ceilings")
     ap.add_argument("--no-graphs", action="store_true", help="skip the HIP-graph replays (for counter runs)")
@@ -560,6 +560,39 @@ def extra_collectives(torch, coll, inputs, metrics, dev, which, ceil, iters=10, 
         rows.append({"name": "allreduce_schedule_latency", "p": p, "dtype": "f32", "op": "sum", "table": table,
                      "workload": "AllReduce p=16, 4 KiB / 64 KiB / 1 MiB per rank, each schedule, back to back"})
 
+    # --- rank counts that are not powers of two: AllReduce 256 MiB fp32 per
+    # rank and ReduceScatter 2^26 bf16 per rank, p = 3, 5, 6, 7, 12 ---------
+    if want("anyp"):
+        table = []
+        for p in (3, 5, 6, 7, 12):
+            n = 1 << 26
+            send = [torch.empty(n, dtype=torch.float32, device=dev).normal_() for _ in range(p)]
+            recv = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(p)]
+            f = coll.coll_allreduce(send, recv, coll.COLL_SUM, defer=True)
+            ar_us = stats_us(time_launches(torch, [f], iters, warmup)[0])[0]
+            del send, recv
+            torch.cuda.empty_cache()
+            # blocks of a whole number of 16-byte vectors (2^26 / p rounded down to a multiple of 4)
+            blk = (1 << 26) // (4 * p) * 4
+            send = [torch.empty(p * blk, dtype=torch.float32, device=dev).normal_() for _ in range(p)]
+            shard = [torch.empty(blk, dtype=torch.float32, device=dev) for _ in range(p)]
+            f = coll.coll_reduce_scatter(send, shard, coll.COLL_SUM, defer=True)
+            rs_us = stats_us(time_launches(torch, [f], iters, warmup)[0])[0]
+            del send, shard
+            torch.cuda.empty_cache()
+            ar_b = metrics.hbm_bytes("allreduce", p, n, 4)
+            rs_b = metrics.hbm_bytes("reduce_scatter", p, blk, 4)
+            e = {"p": p, "allreduce_us": round(ar_us, 1), "allreduce_GBps": round(ar_b / (ar_us * 1e-6) / 1e9, 1),
+                 "reduce_scatter_us": round(rs_us, 1), "reduce_scatter_GBps": round(rs_b / (rs_us * 1e-6) / 1e9, 1)}
+            c1, c2 = ceil.get(p, p, n * 4), ceil.get(p, 1, p * blk * 4)
+            if c1 and c2:
+                e["allreduce_frac_of_mix_ceiling"] = round(e["allreduce_GBps"] / c1["GBps"], 4)
+                e["reduce_scatter_frac_of_mix_ceiling"] = round(e["reduce_scatter_GBps"] / c2["GBps"], 4)
+            table.append(e)
+        rows.append({"name": "other_rank_counts", "table": table,
+                     "workload": "AllReduce sum 2^26 fp32 per rank and ReduceScatter sum of about 2^26 fp32 per "
+                                 "rank (blocks of 2^26/p rounded down to whole vectors), p = 3, 5, 6, 7, 12"})
+
     # --- 10,000 small AllReduces in one launch, p = 16 -----------------------
     if want("batch"):
         rows.append(batch_row(torch, coll, inputs, dev, ceil))
@@ -1015,7 +1048,10 @@ def compact_row(row: dict) -> dict:
     if "stages" in row:
         out["stages"] = {k: {kk: v[kk] for kk in ("t_med_us", "hbm_GBps", "frac_of_mix_ceiling") if kk in v}
                          for k, v in row["stages"].items()}
-    if "table" in row:
+    if "table" in row and row["name"] == "other_rank_counts":
+        out["table"] = [{k: v for k, v in e.items() if k == "p" or k.endswith("GBps") or k.endswith("ceiling")}
+                        for e in row["table"]]
+    elif "table" in row:
         out["table"] = [{k: v for k, v in e.items() if k.endswith("graph_us") or k == "bytes_per_rank"}
                         for e in row["table"]]
     if "individual_calls" in row:

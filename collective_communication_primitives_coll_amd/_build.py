@@ -21,6 +21,9 @@ LIB = os.path.join(PKG, "libcoll.so")
 SOURCES = [
     "coll_api.cpp",
     "reduce_kernels.hip",
+    "reduce_kernels_p3_7.hip",
+    "reduce_kernels_p9_12.hip",
+    "reduce_kernels_p13_15.hip",
     "copy_kernels.hip",
     "a2a_lds_kernels.hip",
     "ring_literal.hip",

@@ -74,11 +74,12 @@ __device__ __forceinline__ void batch_run(const BatchCall& bc, const void* const
         src[k] = (const S*)ld_const(&pt[k]);
         dst[k] = as_global((S*)ld_const(&pt[P + k])) + lo;
       }
-      rotate_left<P>(src, (c + 1) & (P - 1));
+      rotate_left<P>(src, (c + 1) % P);
 #pragma unroll
       for (int k = 0; k < P; ++k) src[k] = as_global(src[k]) + lo;
-      const int mis = bc.mis < 0 ? -1 : (int)((bc.mis + lo * T::B) & 15);
-      const SegSpan sp = seg_span<T::B>(len, mis);
+      const int mis = bc.mis < 0 ? -1 : (int)(((bc.mis & 255) + lo * T::B) & 15);
+      const int amis = (bc.mis < 0 || bc.mis >= 256) ? -1 : seg_amis(bc.mis, lo * T::B);
+      const SegSpan sp = seg_span_a<T::B>(len, mis, amis);
       if (!sp.vec) {
         for (uint64_t i = t; i < t + cnt; ++i) {
           const uint64_t e0 = i * TV * V;
@@ -104,8 +105,8 @@ __device__ __forceinline__ void batch_run(const BatchCall& bc, const void* const
             reduce_vec_tile<DT, OP, P, kOrdRing, P, true, U, false, kWave>(vs, vd, j0, sp.nvec, sc, P);
         }
         if (t == 0 && (sp.head || sp.tail))
-          reduce_edges<DT, OP, P, kOrdRing, P, true>(src, dst, sp.head, sp.head + sp.nvec * V, sp.tail, sc, P,
-                                                     lane);
+          reduce_edges<DT, OP, P, kOrdRing, P, true, kWave>(src, dst, sp.head, sp.head + sp.nvec * V, sp.tail,
+                                                            sc, P, lane);
       }
     }
     left -= cnt;

@@ -134,6 +134,15 @@ int common_mis(const void* const* arr, int p) {
 }
 int common_mis2(int a, int b) { return (a < 0 || b < 0 || a != b) ? -1 : a; }
 
+// Common address modulo 256 of a set of pointers, or -1: the reductions
+// start their vector tiles on 256-byte lines of the sources when known.
+int common_amis(const void* const* arr, int p) {
+  const int m = (int)((uintptr_t)arr[0] & 255);
+  for (int r = 1; r < p; ++r)
+    if ((int)((uintptr_t)arr[r] & 255) != m) return -1;
+  return m;
+}
+
 // ---------------------------------------------------------------------------
 // Aliasing.  Every buffer becomes a byte range tagged (input|output, rank).
 // Outputs must not overlap anything, except pairs the operation allows
@@ -254,6 +263,7 @@ COLL_EXPORT coll_status_t coll_allreduce_algo(const void* const* send, void* con
   g.dst_mode = coll::kDstAll;
   g.src_mis = smis;
   g.dst_mis = dmis;
+  g.src_amis = common_amis(send, p);
   const int order = order_of(algo);
   return finish(coll::launch_reduce(dtype, op, order, P, g, grid, stream));
 }
@@ -284,6 +294,7 @@ COLL_EXPORT coll_status_t coll_allreduce_premul(const void* const* send, void* c
   g.dst_mode = coll::kDstAll;
   g.src_mis = common_mis(send, p);
   g.dst_mis = common_mis((const void* const*)recv, p);
+  g.src_amis = common_amis(send, p);
   for (int r = 0; r < p; ++r) g.scale[r] = scale[r];
   const int order = order_of(algo);
   return finish(coll::launch_reduce(dtype, coll::kPreMul, order, P, g, grid, stream));
@@ -318,6 +329,7 @@ COLL_EXPORT coll_status_t coll_reduce(const void* const* send, void* recv_root, 
   g.dst_mode = coll::kDstFixed;
   g.src_mis = common_mis(send, p);
   g.dst_mis = (int)((uintptr_t)recv_root & 15);
+  g.src_amis = common_amis(send, p);
   return finish(coll::launch_reduce(dtype, op, coll::kOrdRing, P, g, grid, stream));
 }
 
@@ -376,6 +388,7 @@ coll_status_t reduce_scatter_impl(const void* const* send, void* const* recv, in
   g.dst_mode = coll::kDstOwner;
   g.src_mis = common_mis(send, p);
   g.dst_mis = common_mis((const void* const*)recv, p);
+  g.src_amis = common_amis(send, p);
   if (scale)
     for (int r = 0; r < p; ++r) g.scale[r] = scale[r];
   return finish(coll::launch_reduce(dtype, op, coll::kOrdRing, P, g, grid, stream));
@@ -1165,7 +1178,11 @@ void batch_pack(const coll_call_t* calls, int ncalls, int p, const BatchLayout& 
     b.first_tile = tiles;
     b.dtype = (uint32_t)c.dtype;
     b.op = (uint32_t)c.op;
-    b.mis = c.n ? common_mis2(common_mis(c.send, p), common_mis((const void* const*)c.recv, p)) : -1;
+    // BatchCall::mis: -1, the sources' common address mod 256, or 256 + the
+    // common misalignment mod 16
+    const int m16 = c.n ? common_mis2(common_mis(c.send, p), common_mis((const void* const*)c.recv, p)) : -1;
+    const int m256 = m16 < 0 ? -1 : common_amis(c.send, p);
+    b.mis = m16 < 0 ? -1 : (m256 >= 0 ? m256 : 256 + m16);
     const uint64_t te = coll::batch_tile_elems_host(c.dtype, p);
     const uint64_t q = (c.n + p - 1) / p;
     b.tiles_per_chunk = c.n ? (uint32_t)std::max<uint64_t>(1, (q + te - 1) / te) : 0;

@@ -46,6 +46,7 @@ struct ReduceGeom {
   int dst_mode;
   int src_mis;  // common byte misalignment of the source bases, or -1
   int dst_mis;  // common byte misalignment of the destination bases, or -1
+  int src_amis; // common source base address modulo kLineAlign (256), or -1
   float scale[kMaxRanks];  // kPreMul: scale of rank r's operand
 };
 
@@ -169,7 +170,10 @@ struct BatchCall {
   uint32_t dtype;
   uint32_t op;
   uint32_t tiles_per_chunk;
-  int32_t mis;           // common misalignment of the call's buffers, or -1
+  // -1: the buffers disagree modulo 16 (element path); 0..255: every
+  // source base's address modulo 256 (destinations agree modulo 16);
+  // 256 + m: only a common misalignment m modulo 16.
+  int32_t mis;
 };
 
 struct BatchArgs {

@@ -90,8 +90,9 @@ COLL_STREAM_KERNEL void probe_kernel(RankPtrs ptrs, uint64_t nvec, u32x4* sink, 
 
 // The (sources, destinations) mixes the benchmark measures.
 #define COLL_PROBE_MIXES(X) \
-  X(1, 0) X(4, 0) X(8, 0) X(16, 0) X(0, 1) X(0, 4) X(0, 8) X(0, 16) X(1, 1) X(2, 1) X(3, 1) X(4, 1) X(8, 1) \
-  X(16, 1) X(1, 2) X(1, 4) X(1, 8) X(1, 16) X(4, 4) X(8, 8) X(16, 16)
+  X(1, 0) X(4, 0) X(8, 0) X(16, 0) X(0, 1) X(0, 4) X(0, 8) X(0, 16) X(1, 1) X(2, 1) X(3, 1) X(4, 1) X(5, 1) \
+  X(6, 1) X(7, 1) X(8, 1) X(12, 1) X(16, 1) X(1, 2) X(1, 4) X(1, 8) X(1, 16) X(3, 3) X(4, 4) X(5, 5) X(6, 6) \
+  X(7, 7) X(8, 8) X(12, 12) X(16, 16)
 
 bool probe_mix_supported(int ns, int nd) {
 #define COLL_PROBE_HAS(A, B) if (ns == A && nd == B) return true;

@@ -1,345 +1,18 @@
-// AllReduce, Reduce and ReduceScatter: one kernel family.
-//
-// Segment c is chunk c of the operation: for AllReduce and Reduce the
-// elements [c*q, (c+1)*q) with q = ceil(n/p); for ReduceScatter block c of
-// every rank's [p*n] input.  Every workgroup walks the segments in order
-// and takes the tiles whose flat index is congruent to its id modulo the
-// grid, so all p segments spread over the whole chip.  The destination
-// mode picks where a segment's result goes:
-//   all    every rank's buffer at the segment offset (AllReduce: the
-//          reduce-scatter result of chunk c and its all-gather to every
-//          rank come out of one pass; stores are non-temporal),
-//   fixed  the root buffer at the segment offset (Reduce),
-//   owner  rank c's buffer from its start (ReduceScatter, block c lands on
-//          rank c: "集合通信：原语、算法、NCCL 实现与拓扑映射", section 1.5).
-// A segment's sources are read from the kernel arguments with constant
-// offsets and put in the schedule's order in registers (list_for_chunk).
-#include "reduce_tile.h"
+// Reduction launch for every rank count: the power-of-two counts (every
+// schedule) here, the other counts up to 16 in ring order in
+// reduce_kernels_p*.hip (compiled separately so the build runs in
+// parallel), and counts above 16 with the general any-p kernel.
+#include "reduce_impl.h"
 
 namespace coll {
 
-// Rank listed k-th for chunk c (the order list_for_chunk produces).
-template <int ORD, int P>
-__device__ __forceinline__ int listed_rank(int c, int k) {
-  if constexpr (ORD == kOrdRing) return (c + 1 + k) & (P - 1);
-  else if constexpr (ORD == kOrdDBT) return c < P / 2 ? k : P - 1 - k;
-  else return k;
-}
-
-__device__ __forceinline__ void chunk_range(const ReduceGeom& g, int c, uint64_t* lo, uint64_t* len) {
-  uint64_t a = (uint64_t)c * g.stride;
-  uint64_t b = a + g.stride;
-  if (a > g.total) a = g.total;
-  if (b > g.total) b = g.total;
-  *lo = a;
-  *len = b - a;
-}
-
-// Operands of chunk c starting lo elements into every buffer: the p
-// sources in the schedule's order, the destinations of the mode, and the
-// per-operand scales.
-template <int DT, int OP, int P, int ORD, int DMODE, int ND>
-__device__ __forceinline__ void chunk_operands(const RankPtrs& ptrs, const ReduceGeom& g, int c, uint64_t lo,
-                                               const typename Traits<DT>::S* (&src)[P],
-                                               typename Traits<DT>::S* (&dst)[ND], Scales<P>& sc) {
-  using S = typename Traits<DT>::S;
-#pragma unroll
-  for (int k = 0; k < P; ++k) src[k] = (const S*)ptrs.src[k];
-  list_for_chunk<ORD, P>(src, c);
-#pragma unroll
-  for (int k = 0; k < P; ++k) src[k] += lo;
-  if constexpr (DMODE == kDstAll) {
-#pragma unroll
-    for (int k = 0; k < P; ++k) dst[k] = (S*)ptrs.dst[k] + lo;
-  } else if constexpr (DMODE == kDstOwner) {
-    dst[0] = (S*)ptrs.dst[c];
-  } else {
-    dst[0] = (S*)ptrs.dst[0] + lo;
-  }
-  // The scales (pre-multiplied sums only) are indexed by the listed rank
-  // directly: reordering them in registers as the pointers are left an
-  // unused stack reservation in some kernels.
-#pragma unroll
-  for (int k = 0; k < P; ++k) sc.s[k] = OP == kPreMul ? g.scale[listed_rank<ORD, P>(c, k)] : 1.0f;
-}
-
-template <int DT, int OP, int P, int ORD, int DMODE>
-COLL_STREAM_KERNEL void reduce_kernel(RankPtrs ptrs, ReduceGeom g) {
-  using T = Traits<DT>;
-  using S = typename T::S;
-  constexpr bool ALL = DMODE == kDstAll;
-  constexpr int ND = ALL ? P : 1;
-  uint64_t base = 0;
-  for (int c = 0; c < P; ++c) {
-    uint64_t lo, len;
-    chunk_range(g, c, &lo, &len);
-    if (len == 0) continue;
-    const uint64_t doff = (DMODE == kDstOwner) ? 0 : lo;
-    const int mis = seg_mis(g.src_mis, g.dst_mis, lo * T::B, doff * T::B);
-    uint64_t nt;
-    if (!segment_owned<DT, P, ND>(len, mis, base, &nt)) {
-      base += nt;
-      continue;
-    }
-    const S* src[P];
-    S* dst[ND];
-    Scales<P> sc;
-    chunk_operands<DT, OP, P, ORD, DMODE, ND>(ptrs, g, c, lo, src, dst, sc);
-    base += reduce_segment<DT, OP, P, ORD, ND, ALL>(src, dst, len, mis, base, sc, P);
-  }
-}
-
-// AllReduce, ReduceScatter and Reduce calls whose tiles fit the grid (at
-// most one tile per workgroup): workgroup b works tile b % tpc of chunk
-// b / tpc, tpc tiles per chunk, and nothing else.  The general kernel gives such calls the
-// same tiles but has every workgroup walk all P chunks to find its tile,
-// and for small calls that walk (ownership tests, a run-time remainder
-// per chunk) outlasts the data movement: at p = 16 a 4 KiB call took
-// 8.7 us against 4.3 us, a 64 KiB call 9.3 us against 4.6 us.
-template <int DT, int OP, int P, int ORD, int DMODE>
-COLL_STREAM_KERNEL void reduce_tile_kernel(RankPtrs ptrs, ReduceGeom g, uint32_t tpc) {
-  using T = Traits<DT>;
-  using S = typename T::S;
-  constexpr bool ALL = DMODE == kDstAll;
-  constexpr int ND = ALL ? P : 1;
-  constexpr int U = ReduceUnroll<P, ALL>::value;
-  constexpr uint64_t TV = (uint64_t)U * kBlock;
-  const int c = (int)(blockIdx.x / tpc);
-  const uint64_t t = blockIdx.x - (uint64_t)c * tpc;
-  uint64_t lo, len;
-  chunk_range(g, c, &lo, &len);
-  if (len == 0) return;
-  const uint64_t doff = (DMODE == kDstOwner) ? 0 : lo;
-  const int mis = seg_mis(g.src_mis, g.dst_mis, lo * T::B, doff * T::B);
-  const S* src[P];
-  S* dst[ND];
-  Scales<P> sc;
-  chunk_operands<DT, OP, P, ORD, DMODE, ND>(ptrs, g, c, lo, src, dst, sc);
-  const SegSpan sp = seg_span<T::B>(len, mis);
-  if (!sp.vec) {
-    // element path: tile t covers TV * V elements of the chunk
-    const uint64_t from = t * TV * T::V;
-    if (from < len)
-      reduce_elems<DT, OP, P, ORD, ND, ALL>(src, dst, from, (len - from) < TV * T::V ? (len - from) : TV * T::V,
-                                            sc, P);
-    return;
-  }
-  if (t * TV < sp.nvec) {
-    const S* vs[P];
-    S* vd[ND];
-#pragma unroll
-    for (int k = 0; k < P; ++k) vs[k] = src[k] + sp.head;
-#pragma unroll
-    for (int d = 0; d < ND; ++d) vd[d] = dst[d] + sp.head;
-    reduce_vec_tile<DT, OP, P, ORD, ND, ALL, U, false>(vs, vd, t * TV + threadIdx.x, sp.nvec, sc, P);
-  }
-  if (t == 0 && (sp.head || sp.tail))
-    reduce_edges<DT, OP, P, ORD, ND, ALL>(src, dst, sp.head, sp.head + sp.nvec * T::V, sp.tail, sc, P,
-                                          (int)threadIdx.x);
-}
-
-// Any rank count (the slow general path): one vector per lane per tile,
-// operands in groups of 8 loads, pointers read from the kernel arguments.
-// TILE: at most one tile per workgroup (AllReduce only): workgroup b works
-// tile b % tpc of chunk b / tpc instead of walking every chunk, as
-// reduce_tile_kernel does for the specialised rank counts.
-template <int DT, int OP, int DMODE, bool TILE = false>
-COLL_STREAM_KERNEL void reduce_kernel_any(RankPtrs ptrs, ReduceGeom g, uint32_t tpc = 0) {
-#pragma clang fp contract(off)
-  using T = Traits<DT>;
-  using S = typename T::S;
-  using A = typename T::A;
-  constexpr int V = T::V;
-  constexpr bool ALL = DMODE == kDstAll;
-  const int p = g.p;
-  const uint64_t grid = gridDim.x, wg = blockIdx.x;
-  const int c_first = TILE ? (int)(blockIdx.x / tpc) : 0;
-  const int c_end = TILE ? c_first + 1 : p;
-  const uint64_t my_tile = TILE ? blockIdx.x - (uint64_t)c_first * tpc : 0;
-  // first tile and stride of this workgroup in a segment of nt tiles
-  auto tile0 = [&](uint64_t base) -> uint64_t { return TILE ? my_tile : first_tile(base, wg, grid); };
-  auto tstep = [&](uint64_t nt) -> uint64_t { return TILE ? nt : grid; };
-  uint64_t base = 0;
-  for (int c = c_first; c < c_end; ++c) {
-    uint64_t lo, len;
-    chunk_range(g, c, &lo, &len);
-    if (len == 0) continue;
-    const uint64_t doff = (DMODE == kDstOwner) ? 0 : lo;
-    auto sp_src = [&](int k) -> const S* { return (const S*)ptrs.src[(c + 1 + k) % p] + lo; };
-    auto sp_dst = [&](int k) -> S* {
-      if constexpr (ALL) return (S*)ptrs.dst[k] + lo;
-      else if constexpr (DMODE == kDstOwner) return (S*)ptrs.dst[c];
-      else return (S*)ptrs.dst[0] + lo;
-    };
-    const int nd = ALL ? p : 1;
-    const SegSpan sp = seg_span<T::B>(len, seg_mis(g.src_mis, g.dst_mis, lo * T::B, doff * T::B));
-    auto scale_of = [&](int k) -> float { return g.scale[(c + 1 + k) % p]; };
-    auto elem_at = [&](uint64_t e) {
-#pragma clang fp contract(off)
-      A acc = widen1<DT>(ld1<true>(sp_src(0) + e));
-      if constexpr (OP == kPreMul) acc = scale_of(0) * acc;
-      for (int k = 1; k < p; ++k) {
-        A v = widen1<DT>(ld1<true>(sp_src(k) + e));
-        if constexpr (OP == kPreMul) v = scale_of(k) * v;
-        acc = combine<OP>(acc, v);
-      }
-      const auto out = narrow1<DT>(finish<OP>(acc, p));
-      for (int d = 0; d < nd; ++d) st1<ALL>(sp_dst(d) + e, out);
-    };
-    auto elems = [&](uint64_t from, uint64_t cnt) {
-      for (uint64_t i = threadIdx.x; i < cnt; i += kBlock) elem_at(from + i);
-    };
-    if (!sp.vec) {
-      constexpr uint64_t TE = (uint64_t)kBlock * 4;
-      const uint64_t nt = ceil_div(len, TE);
-      for (uint64_t t = tile0(base); t < nt; t += tstep(nt)) {
-        const uint64_t from = t * TE;
-        elems(from, (len - from) < TE ? (len - from) : TE);
-      }
-      base += nt;
-      continue;
-    }
-    const uint64_t nt = ceil_div(sp.nvec, (uint64_t)kBlock);
-    for (uint64_t t = tile0(base); t < nt; t += tstep(nt)) {
-      const uint64_t j = t * kBlock + threadIdx.x;
-      if (j >= sp.nvec) continue;
-      const uint64_t e = sp.head + j * V;
-      A acc[V];
-      widen<DT>(ld16<true>(sp_src(0) + e), acc);
-      if constexpr (OP == kPreMul) {
-#pragma unroll
-        for (int x = 0; x < V; ++x) acc[x] = scale_of(0) * acc[x];
-      }
-      for (int k0 = 1; k0 < p; k0 += 8) {
-        u32x4 r[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          if (k0 + q < p) r[q] = ld16<true>(sp_src(k0 + q) + e);
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          if (k0 + q < p) {
-            A t2[V];
-            widen<DT>(r[q], t2);
-            if constexpr (OP == kPreMul) {
-#pragma unroll
-              for (int x = 0; x < V; ++x) t2[x] = scale_of(k0 + q) * t2[x];
-            }
-            combine_vec<OP, DT>(acc, t2);
-          }
-      }
-#pragma unroll
-      for (int x = 0; x < V; ++x) acc[x] = finish<OP>(acc[x], p);
-      const u32x4 out = narrow<DT>(acc);
-      for (int d = 0; d < nd; ++d) st16<ALL>(sp_dst(d) + e, out);
-    }
-    if ((sp.head || sp.tail) && tile0(base) == 0) {
-      // head and tail in one pass (each is shorter than a vector)
-      const uint64_t i = threadIdx.x;
-      if (i < sp.head + sp.tail) elem_at(i < sp.head ? i : sp.head + sp.nvec * V + (i - sp.head));
-    }
-    base += nt;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Host-side launch
-// ---------------------------------------------------------------------------
-template <int DT, int P, bool ALL>
-static uint64_t tile_elems() {
-  return (uint64_t)ReduceUnroll<P, ALL>::value * kBlock * Traits<DT>::V;
-}
-
-// Upper bound on the tiles of all segments (vector tiles plus one for a
-// misaligned head), used only to size the grid.
-template <int DT, int P, bool ALL>
-static uint64_t count_tiles(const ReduceGeom& g) {
-  const uint64_t te = P ? tile_elems<DT, P, ALL>() : (uint64_t)kBlock * Traits<DT>::V;
-  uint64_t total = 0;
-  for (int c = 0; c < g.p; ++c) {
-    uint64_t lo = (uint64_t)c * g.stride, hi = lo + g.stride;
-    if (lo > g.total) lo = g.total;
-    if (hi > g.total) hi = g.total;
-    if (hi > lo) total += (hi - lo + te - 1) / te + 1;
-  }
-  return total;
-}
-
-static int clamp_grid(uint64_t tiles, int max_grid) {
-  if (tiles == 0) return 0;
-  return (int)(tiles < (uint64_t)max_grid ? tiles : (uint64_t)max_grid);
-}
-
-template <int DT, int OP, int P, int ORD>
-static int launch_p(const RankPtrs& ptrs, const ReduceGeom& g, int max_grid, hipStream_t s) {
-  if (g.dst_mode == kDstAll) {
-    // at most one tile per workgroup: each workgroup goes straight to its
-    // tile (for the default grid of one workgroup per CU on 256 CUs: up to
-    // 1 MiB per rank at p = 16, 2 MiB at 8, 4 MiB at 4)
-    const uint64_t te = tile_elems<DT, P, true>();
-    const uint64_t tpc = (g.stride + te - 1) / te;
-    if (tpc * P <= (uint64_t)max_grid) {
-      if (tpc)
-        hipLaunchKernelGGL((reduce_tile_kernel<DT, OP, P, ORD, kDstAll>), dim3((unsigned)(tpc * P)), dim3(kBlock),
-                           0, s, ptrs, g, (uint32_t)tpc);
-      return (int)hipGetLastError();
-    }
-  }
-  if constexpr (ORD == kOrdRing) {
-    // ReduceScatter and Reduce (ring order only) likewise
-    if (g.dst_mode == kDstOwner || g.dst_mode == kDstFixed) {
-      const uint64_t te = tile_elems<DT, P, false>();
-      const uint64_t tpc = (g.stride + te - 1) / te;
-      if (tpc * P <= (uint64_t)max_grid) {
-        if (tpc && g.dst_mode == kDstOwner)
-          hipLaunchKernelGGL((reduce_tile_kernel<DT, OP, P, ORD, kDstOwner>), dim3((unsigned)(tpc * P)),
-                             dim3(kBlock), 0, s, ptrs, g, (uint32_t)tpc);
-        else if (tpc)
-          hipLaunchKernelGGL((reduce_tile_kernel<DT, OP, P, ORD, kDstFixed>), dim3((unsigned)(tpc * P)),
-                             dim3(kBlock), 0, s, ptrs, g, (uint32_t)tpc);
-        return (int)hipGetLastError();
-      }
-    }
-  }
-  if (g.dst_mode == kDstAll) {
-    const int grid = clamp_grid(count_tiles<DT, P, true>(g), max_grid);
-    if (grid)
-      hipLaunchKernelGGL((reduce_kernel<DT, OP, P, ORD, kDstAll>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
-    return (int)hipGetLastError();
-  }
-  const int grid = clamp_grid(count_tiles<DT, P, false>(g), max_grid);
-  if (!grid) return 0;
-  if (g.dst_mode == kDstOwner)
-    hipLaunchKernelGGL((reduce_kernel<DT, OP, P, ORD, kDstOwner>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
-  else
-    hipLaunchKernelGGL((reduce_kernel<DT, OP, P, ORD, kDstFixed>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
-  return (int)hipGetLastError();
-}
-
-template <int DT, int OP>
-static int launch_any(const RankPtrs& ptrs, const ReduceGeom& g, int max_grid, hipStream_t s) {
-  if (g.dst_mode == kDstAll) {
-    // at most one tile per workgroup: no chunk walk.  Tiles of kBlock * 4
-    // elements (the element path's) also bound the vector path's tiles of
-    // kBlock vectors.
-    const uint64_t te = (uint64_t)kBlock * 4;
-    const uint64_t tpc = (g.stride + te - 1) / te;
-    if (tpc * (uint64_t)g.p <= (uint64_t)max_grid) {
-      if (tpc)
-        hipLaunchKernelGGL((reduce_kernel_any<DT, OP, kDstAll, true>), dim3((unsigned)(tpc * g.p)), dim3(kBlock),
-                           0, s, ptrs, g, (uint32_t)tpc);
-      return (int)hipGetLastError();
-    }
-  }
-  const int grid = clamp_grid(count_tiles<DT, 0, false>(g), max_grid);
-  if (!grid) return 0;
-  if (g.dst_mode == kDstAll)
-    hipLaunchKernelGGL((reduce_kernel_any<DT, OP, kDstAll>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
-  else if (g.dst_mode == kDstOwner)
-    hipLaunchKernelGGL((reduce_kernel_any<DT, OP, kDstOwner>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
-  else
-    hipLaunchKernelGGL((reduce_kernel_any<DT, OP, kDstFixed>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
-  return (int)hipGetLastError();
-}
+// Ring order at compile-time rank counts that are not powers of two.
+int launch_reduce_p3_7(int p, int dtype, int op, const RankPtrs& ptrs, const ReduceGeom& g, int max_grid,
+                       void* stream);
+int launch_reduce_p9_12(int p, int dtype, int op, const RankPtrs& ptrs, const ReduceGeom& g, int max_grid,
+                        void* stream);
+int launch_reduce_p13_15(int p, int dtype, int op, const RankPtrs& ptrs, const ReduceGeom& g, int max_grid,
+                         void* stream);
 
 // Tree orders only change the result of floating-point sums (plain,
 // averaged or pre-multiplied); integer sums and min/max give the same bits
@@ -390,6 +63,16 @@ static int launch_dt(int op, int order, const RankPtrs& ptrs, const ReduceGeom& 
 int launch_reduce(int dtype, int op, int order, const RankPtrs& ptrs, const ReduceGeom& g,
                   int max_grid, void* stream) {
   hipStream_t s = (hipStream_t)stream;
+  if (order == kOrdRing) {
+    switch (g.p) {
+      case 3: case 5: case 6: case 7:
+        return launch_reduce_p3_7(g.p, dtype, op, ptrs, g, max_grid, stream);
+      case 9: case 10: case 11: case 12:
+        return launch_reduce_p9_12(g.p, dtype, op, ptrs, g, max_grid, stream);
+      case 13: case 14: case 15:
+        return launch_reduce_p13_15(g.p, dtype, op, ptrs, g, max_grid, stream);
+    }
+  }
   switch (dtype) {
     case kF32: return launch_dt<kF32>(op, order, ptrs, g, max_grid, s);
     case kBF16: return launch_dt<kBF16>(op, order, ptrs, g, max_grid, s);

@@ -34,21 +34,21 @@ struct ReduceUnroll {
   static constexpr int value = raw < 1 ? 1 : (raw > 8 ? 8 : raw);
 };
 
-// a[k] <- a[(k + s) mod P] for a wave-uniform s in [0, P), P a power of
-// two: log2(P) conditional rotations by 1, 2, 4, ... whose indices are all
+// a[k] <- a[(k + s) mod P] for a wave-uniform s in [0, P): one conditional
+// rotation per bit of s (by 1, 2, 4, ...), each with indices that are
 // compile-time constants, so the array stays in scalar registers and its
 // elements can be fetched with constant offsets (wide scalar loads issued
-// together).  Indexing the source array with a run-time rank instead makes
-// the compiler fetch every element with its own dependent scalar load.
+// together).  Rotations compose modulo P, so this holds for any P, not only
+// powers of two.  Indexing the source array with a run-time rank instead
+// makes the compiler fetch every element with its own dependent scalar load.
 template <int P, typename T>
 __device__ __forceinline__ void rotate_left(T (&a)[P], int s) {
-  static_assert((P & (P - 1)) == 0, "rotate_left needs a power-of-two length");
 #pragma unroll
   for (int b = 1; b < P; b <<= 1) {
     const bool on = (s & b) != 0;
     T t[P];
 #pragma unroll
-    for (int k = 0; k < P; ++k) t[k] = a[(k + b) & (P - 1)];
+    for (int k = 0; k < P; ++k) t[k] = a[(k + b) % P];
 #pragma unroll
     for (int k = 0; k < P; ++k) a[k] = on ? t[k] : a[k];
   }
@@ -70,7 +70,7 @@ __device__ __forceinline__ void reverse_if(T (&a)[P], bool on) {
 // the double binary tree's second half of the chunks).
 template <int ORD, int P, typename T>
 __device__ __forceinline__ void list_for_chunk(T (&a)[P], int c) {
-  if constexpr (ORD == kOrdRing) rotate_left<P>(a, (c + 1) & (P - 1));
+  if constexpr (ORD == kOrdRing) rotate_left<P>(a, (c + 1) % P);
   else if constexpr (ORD == kOrdDBT) reverse_if<P>(a, c >= P / 2);
 }
 
@@ -241,18 +241,19 @@ __device__ __forceinline__ void reduce_elems(const typename Traits<DT>::S* const
     reduce_elem_at<DT, OP, P, ORD, ND, NTS>(src, dst, from + i, sc, avg_p);
 }
 
-// The misaligned head (elements [0, head)) and tail (tail elements from
-// tail_from) of a vectorized segment in one pass: lane i < head takes
-// element i, lane head + i element tail_from + i.  Both are shorter than
-// one 16-byte vector, so one pass of any wave covers them, and the two
-// cost one memory round trip instead of two.
-template <int DT, int OP, int P, int ORD, int ND, bool NTS>
+// The element-wise head (elements [0, head)) and tail (tail elements from
+// tail_from) of a vectorized segment together: lane i < head takes element
+// i, lane head + i element tail_from + i, LANES lanes at a time.  The head
+// reaches the next line boundary (below kLineAlign bytes) and the tail is
+// shorter than one vector, so a workgroup covers both in one pass and a
+// wave in at most three, one memory round trip each.
+template <int DT, int OP, int P, int ORD, int ND, bool NTS, int LANES = kBlock>
 __device__ __forceinline__ void reduce_edges(const typename Traits<DT>::S* const (&src)[P],
                                              typename Traits<DT>::S* const (&dst)[ND], uint64_t head,
                                              uint64_t tail_from, uint64_t tail, const Scales<P>& sc, int avg_p,
                                              int lane) {
-  const uint64_t i = (uint64_t)lane;
-  if (i < head + tail) reduce_elem_at<DT, OP, P, ORD, ND, NTS>(src, dst, i < head ? i : tail_from + (i - head), sc, avg_p);
+  for (uint64_t i = (uint64_t)lane; i < head + tail; i += LANES)
+    reduce_elem_at<DT, OP, P, ORD, ND, NTS>(src, dst, i < head ? i : tail_from + (i - head), sc, avg_p);
 }
 
 // Tiles of a segment as reduce_segment counts them, and whether workgroup
@@ -261,10 +262,10 @@ __device__ __forceinline__ void reduce_edges(const typename Traits<DT>::S* const
 // pointer setup when it has nothing to do there (small calls, where the
 // setup would dominate).
 template <int DT, int P, int ND>
-__device__ __forceinline__ bool segment_owned(uint64_t len, int mis, uint64_t base, uint64_t* nt_out) {
+__device__ __forceinline__ bool segment_owned(uint64_t len, int mis, int amis, uint64_t base, uint64_t* nt_out) {
   constexpr int U = ReduceUnroll<P, (ND > 1)>::value;
   constexpr uint64_t TV = (uint64_t)U * kBlock;
-  const SegSpan sp = seg_span<Traits<DT>::B>(len, mis);
+  const SegSpan sp = seg_span_a<Traits<DT>::B>(len, mis, amis);
   const uint64_t nt = sp.vec ? ceil_div(sp.nvec, TV) : ceil_div(len, (uint64_t)kBlock * 4);
   *nt_out = nt;
   const uint64_t ft = first_tile32(base, blockIdx.x, gridDim.x);
@@ -274,18 +275,19 @@ __device__ __forceinline__ bool segment_owned(uint64_t len, int mis, uint64_t ba
 // A whole segment as seen by one workgroup: its share of the vector tiles
 // (flat tile indices congruent to the workgroup id modulo the grid,
 // counting from `base`) and, for the owning workgroup, the head and tail.
+// amis: the sources' address modulo kLineAlign at the segment start, or -1.
 // Returns the segment's tile count (the caller advances base by it).
 template <int DT, int OP, int P, int ORD, int ND, bool NTS>
 __device__ __forceinline__ uint64_t reduce_segment(const typename Traits<DT>::S* const (&src)[P],
                                                    typename Traits<DT>::S* const (&dst)[ND],
-                                                   uint64_t len, int mis, uint64_t base, const Scales<P>& sc,
-                                                   int avg_p) {
+                                                   uint64_t len, int mis, int amis, uint64_t base,
+                                                   const Scales<P>& sc, int avg_p) {
   using S = typename Traits<DT>::S;
   constexpr int V = Traits<DT>::V;
   constexpr int U = ReduceUnroll<P, (ND > 1)>::value;
   constexpr uint64_t TV = (uint64_t)U * kBlock;
   const uint64_t grid = gridDim.x, wg = blockIdx.x;
-  const SegSpan sp = seg_span<Traits<DT>::B>(len, mis);
+  const SegSpan sp = seg_span_a<Traits<DT>::B>(len, mis, amis);
   if (!sp.vec) {
     // element path over tiles of kBlock * 4 elements
     constexpr uint64_t TE = (uint64_t)kBlock * 4;

@@ -44,9 +44,9 @@ COLL_STREAM_KERNEL void ring_step_kernel(RankPtrs ptrs, RingStepGeom g) {
       S* dst[1] = {d};
       const Scales<2> sc{};
       if (OP == kAvg && g.step == p - 1)
-        base += reduce_segment<DT, kAvg, 2, kOrdRing, 1, false>(src, dst, len, mis, base, sc, p);
+        base += reduce_segment<DT, kAvg, 2, kOrdRing, 1, false>(src, dst, len, mis, -1, base, sc, p);
       else
-        base += reduce_segment<DT, OP == kAvg ? kSum : OP, 2, kOrdRing, 1, false>(src, dst, len, mis, base, sc, p);
+        base += reduce_segment<DT, OP == kAvg ? kSum : OP, 2, kOrdRing, 1, false>(src, dst, len, mis, -1, base, sc, p);
     } else {
       using W = typename Word<T::B>::T;
       auto gdst = [&](int) -> W* { return (W*)d; };

@@ -428,8 +428,9 @@ coll_status_t coll_allreduce_batch_noalloc(const coll_call_t* calls, int ncalls,
  * aligned) only if it equals an internal pattern, so the reads stay.
  * flags: COLL_PROBE_NT_LOADS / COLL_PROBE_NT_STORES select non-temporal
  * loads / stores (else cached).  Supported (nsrc, ndst): (1|4|8|16, 0),
- * (0, 1|4|8|16), (1|2|3|4|8|16, 1), (1, 2|4|8|16), (4, 4), (8, 8),
- * (16, 16); other pairs and tile sizes return COLL_ERR_UNSUPPORTED.  Every pointer
+ * (0, 1|4|8|16), (1|2|3|4|5|6|7|8|12|16, 1), (1, 2|4|8|16) and (k, k) for
+ * k in 3, 4, 5, 6, 7, 8, 12, 16; other pairs and tile sizes return
+ * COLL_ERR_UNSUPPORTED.  Every pointer
  * 16-byte aligned and bytes a multiple of 16 (else COLL_ERR_INVALID_ARG);
  * destinations may not overlap each other or a source (COLL_ERR_ALIAS). */
 #define COLL_PROBE_NT_LOADS 1u

@@ -1468,3 +1468,117 @@ def test_stream_probe_writes_the_xor_of_its_sources(coll, ns, nd):
             assert np.array_equal(got[:words], want)
             assert np.all(got[words:] == 7)            # nothing past the streams
         assert sink.cpu().tolist() == [5, 5, 5, 5]
+
+
+# ----------------------------------------------------------------------------
+# Rank counts that are not powers of two: the specialised ring-order kernels
+# ----------------------------------------------------------------------------
+
+ANY_P = [3, 5, 6, 7, 9, 10, 11, 12, 13, 14, 15]
+
+
+@pytest.mark.parametrize("p", ANY_P)
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_ring_kernels_at_every_rank_count(coll, p, dtype):
+    """AllReduce (sum, min, max, AVG) at a size with one tile per workgroup
+    and at one above that bound (chunk walk), ReduceScatter and Reduce (root
+    one element off the sends), ragged sizes, against the oracle."""
+    for n in (p * 4096 * 3 + 5, 3_000_007):
+        hx = gen(p, n, dtype, 300 + p)
+        send = [to_dev(x, dtype) for x in hx]
+        recv = [empty(n, dtype, fill=0) for _ in range(p)]
+        for op in (native.SUM, native.MIN, native.MAX, native.AVG):
+            coll.coll_allreduce(send, recv, op)
+            sync()
+            expect = native.allreduce(hx, op, dtype)
+            for r in sorted({0, p // 2, p - 1}):
+                assert_bits_equal(to_host(recv[r], dtype), expect, f"AR p={p} n={n} op={op} rank {r}")
+        base, out = upload_offset(np.zeros(n, dtype=hx[0].dtype), dtype, 1)
+        coll.coll_reduce(send, out, p - 1, native.SUM)
+        sync()
+        assert_bits_equal(to_host(out, dtype), native.allreduce(hx, native.SUM, dtype), f"Reduce p={p} n={n}")
+        del send, recv, base, out
+    for n in (4099, 200_003):
+        hx = gen(p, p * n, dtype, 400 + p)
+        send = [to_dev(x, dtype) for x in hx]
+        shard = [empty(n, dtype, fill=0) for _ in range(p)]
+        for op in (native.SUM, native.MAX):
+            coll.coll_reduce_scatter(send, shard, op)
+            sync()
+            expect = native.reduce_scatter(hx, op, dtype)
+            for r in range(p):
+                assert_bits_equal(to_host(shard[r], dtype), expect[r], f"RS p={p} n={n} op={op} block {r}")
+
+
+@pytest.mark.parametrize("p", [3, 6, 12])
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_premulsum_at_other_rank_counts(coll, p, dtype):
+    n = 50_001
+    hx = gen(p, n, dtype, 500 + p)
+    send = [to_dev(x, dtype) for x in hx]
+    recv = [empty(n, dtype, fill=0) for _ in range(p)]
+    scales = np.random.default_rng(p).random(p, dtype=np.float32) * 2 - 0.5
+    coll.coll_allreduce_premul(send, recv, scales)
+    sync()
+    expect = native.allreduce(hx, native.SUM, dtype, scales=scales)
+    for r in (0, p - 1):
+        assert_bits_equal(to_host(recv[r], dtype), expect, f"PreMulSum p={p} rank {r}")
+
+
+# ----------------------------------------------------------------------------
+# Vector tiles start on 256-byte source lines: long element-wise heads
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("off", [1, 3, 17, 63, 64, 100, 127])
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_line_aligned_heads(coll, off, dtype):
+    """Buffers `off` elements into their allocations (all ranks alike), so
+    every chunk starts at a different offset within a 256-byte line and its
+    element-wise head runs up to the next line: AllReduce at p = 3, 6 and 8,
+    ReduceScatter with blocks that are not whole lines, Reduce, and a batch
+    whose heads exceed one wave; against the oracle."""
+    keep = []
+
+    def views(hx):
+        out = []
+        for x in hx:
+            base, v = upload_offset(x, dtype, off)
+            keep.append(base)
+            out.append(v)
+        return out
+
+    for p, n in ((3, 3 * 4096 + 77), (6, 100_003), (8, 8 * 1024 * 9 + 5), (8, (1 << 20) + 37)):
+        hx = gen(p, n, dtype, 600 + off)
+        send = views(hx)
+        recv = views([np.zeros(n, dtype=hx[0].dtype)] * p)
+        for op in (native.SUM, native.MAX):
+            coll.coll_allreduce(send, recv, op)
+            sync()
+            expect = native.allreduce(hx, op, dtype)
+            for r in (0, p - 1):
+                assert_bits_equal(to_host(recv[r], dtype), expect, f"AR p={p} n={n} off={off} op={op}")
+        out = views([np.zeros(n, dtype=hx[0].dtype)])[0]
+        coll.coll_reduce(send, out, 1, native.SUM)
+        sync()
+        assert_bits_equal(to_host(out, dtype), native.allreduce(hx, native.SUM, dtype), f"Reduce p={p} off={off}")
+    for p, n in ((3, 4096 + 37), (8, 3 * 8192 + 11)):
+        hx = gen(p, p * n, dtype, 700 + off)
+        send = views(hx)
+        shard = views([np.zeros(n, dtype=hx[0].dtype)] * p)
+        coll.coll_reduce_scatter(send, shard, native.SUM)
+        sync()
+        expect = native.reduce_scatter(hx, native.SUM, dtype)
+        for r in range(p):
+            assert_bits_equal(to_host(shard[r], dtype), expect[r], f"RS p={p} off={off} block {r}")
+    p = 16
+    calls, host = [], []
+    for k, n in enumerate((5, 63, 64, 65, 200, 1000, 4096 + 7, 50_001)):
+        hx = gen(p, n, dtype, 800 + off + k)
+        calls.append((views(hx), views([np.zeros(n, dtype=hx[0].dtype)] * p), n, dtype, k % 3))
+        host.append(hx)
+    coll.coll_allreduce_batch(calls, p)
+    sync()
+    for k, ((_, recv, n, _, op), hx) in enumerate(zip(calls, host)):
+        expect = native.allreduce(hx, op, dtype)
+        for r in (0, p - 1):
+            assert_bits_equal(to_host(recv[r], dtype), expect, f"batch call {k} n={n} off={off} rank {r}")
