@@ -298,7 +298,8 @@ COLL_STREAM_KERNEL void alltoallv_flat_kernel(RankPtrs ptrs, A2avArgs a) {
   uint64_t nt = 0;
   if (tid < pp && cnt[tid] > 0) {
     const uint64_t len = (uint64_t)cnt[tid];
-    const SegSpan sp = seg_span<B>(len, seg_mis(a.src_mis, a.dst_mis, (uint64_t)soff[tid] * B, (uint64_t)roff[tid] * B));
+    const SegSpan sp = seg_span_a<B>(len, seg_mis(a.src_mis, a.dst_mis, (uint64_t)soff[tid] * B, (uint64_t)roff[tid] * B),
+                                     seg_amis(a.dst_amis, (uint64_t)roff[tid] * B));
     nt = sp.vec ? ceil_div(sp.nvec, kCopyTV) : ceil_div(len, TE);
     if (nt == 0) nt = 1;
   }
@@ -329,7 +330,7 @@ COLL_STREAM_KERNEL void alltoallv_flat_kernel(RankPtrs ptrs, A2avArgs a) {
     const uint64_t ro = (uint64_t)roff[sgi];
     const W* src = (const W*)ptrs.src[i] + so;
     W* dst = (W*)ptrs.dst[j] + ro;
-    const SegSpan sp = seg_span<B>(len, seg_mis(a.src_mis, a.dst_mis, so * B, ro * B));
+    const SegSpan sp = seg_span_a<B>(len, seg_mis(a.src_mis, a.dst_mis, so * B, ro * B), seg_amis(a.dst_amis, ro * B));
     if (!sp.vec) {
       const uint64_t from = t * TE;
       const uint64_t n = (len - from) < TE ? (len - from) : TE;
@@ -343,8 +344,9 @@ COLL_STREAM_KERNEL void alltoallv_flat_kernel(RankPtrs ptrs, A2avArgs a) {
     if ((t + 1) * kCopyTV <= sp.nvec) copy_vec_tile<true, true, 1>(vs, gdst, 1, j0, sp.nvec);
     else if (t * kCopyTV < sp.nvec) copy_vec_tile<true, false, 1>(vs, gdst, 1, j0, sp.nvec);
     if (t == 0 && (sp.head || sp.tail)) {
-      const uint64_t e = tid;
-      if (e < sp.head + sp.tail) {
+      // the head (up to the next 256-byte line of the receive buffer) and
+      // the tail (under one vector)
+      for (uint64_t e = tid; e < sp.head + sp.tail; e += kBlock) {
         const uint64_t x = e < sp.head ? e : sp.head + sp.nvec * V + (e - sp.head);
         st1<true>(dst + x, ld1<true>(src + x));
       }

@@ -148,6 +148,12 @@ __device__ __forceinline__ bool slot_rows(const Rows<Args>& tgt, const Args& a, 
 // Groups of at most 1024 elements (g16 <= 64 units): every group lies in
 // one unit column (64 adjacent units), so a row streams through in
 // batches of CB columns and any hidden size works.
+//
+// A wave walks its (row, batch) steps with the next step's loads issued
+// before the current step's amax, encoding and stores, so the token reads
+// of one row overlap the code writes of the previous one (gfx9 counts
+// loads and stores on one counter: loads issued after a store would wait
+// for it).  Rows whose slots are all undelivered load nothing.
 constexpr int kPackCols = 8;
 
 template <int CB, class Args>
@@ -165,61 +171,93 @@ COLL_STREAM_KERNEL void moe_pack_fp8_cols_kernel(Args a) {
   const uint32_t ngroups = (uint32_t)(H / a.group);
   const uint32_t npad = (uint32_t)((a.row_bytes - H) / 4) - ngroups;
   const uint64_t rows = a.tokens * (uint64_t)a.p;
-  for (uint64_t r = fp8_wave_id(); r < rows; r += fp8_wave_count()) {
-    const int rank = (int)(r / a.tokens);
-    const uint64_t t = r - (uint64_t)rank * a.tokens;
+  const uint64_t waves = fp8_wave_count();
+
+  // the row of step (r, c0): its source and slot destinations
+  struct RowState {
+    uint64_t r;
+    int rank;
+    uint64_t t;
+    bool any;
+    const u32x4* src;
     uint8_t* drow[kMaxTopK];
     int64_t loc[kMaxTopK];
-    if (slot_rows(tgt, a, rank, t, drow, loc)) {
-      const u32x4* src = reinterpret_cast<const u32x4*>(as_global((const uint16_t*)a.src[rank]) + t * H);
-      for (uint32_t c0 = 0; c0 < ncols; c0 += CB) {
-        u32x4 x[CB][2];
-        uint32_t mb[CB];
+  };
+  auto open_row = [&](uint64_t r, RowState& st) {
+    st.r = r;
+    st.rank = (int)(r / a.tokens);
+    st.t = r - (uint64_t)st.rank * a.tokens;
+    st.any = slot_rows(tgt, a, st.rank, st.t, st.drow, st.loc);
+    st.src = reinterpret_cast<const u32x4*>(as_global((const uint16_t*)a.src[st.rank]) + st.t * H);
+  };
+  auto load = [&](const RowState& st, uint32_t c0, u32x4 (&x)[CB][2]) {
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const uint32_t j = (c0 + u) * kLanes + lane;
+      if (st.any && j < nunits) {
+        x[u][0] = ld16<true>(st.src + 2 * j);
+        x[u][1] = ld16<true>(st.src + 2 * j + 1);
+      } else {
+        x[u][0] = u32x4{0, 0, 0, 0};
+        x[u][1] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+
+  uint64_t r = fp8_wave_id();
+  if (r >= rows) return;
+  RowState cur, nxt;
+  open_row(r, cur);
+  uint32_t c0 = 0;
+  u32x4 x[CB][2];
+  load(cur, c0, x);
+  while (true) {
+    // the next step: the next batch of this row, or the wave's next row
+    const bool row_done = c0 + CB >= ncols;
+    const uint32_t cn = row_done ? 0u : c0 + CB;
+    const bool more = !row_done || cur.r + waves < rows;
+    if (row_done && more) open_row(cur.r + waves, nxt);
+    u32x4 xn[CB][2];
+    if (more) load(row_done ? nxt : cur, cn, xn);
+    if (cur.any) {
+      uint32_t mb[CB];
+#pragma unroll
+      for (int u = 0; u < CB; ++u) {
+        mb[u] = unit_amax_bits(x[u][0], x[u][1]);
+        for (uint32_t off = 1; off < g16; off <<= 1) mb[u] = max(mb[u], (uint32_t)__shfl_xor((int)mb[u], (int)off));
+      }
+      float sc[CB];
+#pragma unroll
+      for (int u = 0; u < CB; ++u) {
+        const float amax = fmaxf(__uint_as_float(mb[u] << 16), 0x1p-110f);
+        x[u][0] = unit_codes(x[u][0], x[u][1], 448.0f / amax);
+        sc[u] = amax / 448.0f;
+      }
+#pragma unroll
+      for (int s = 0; s < kMaxTopK; ++s) {
+        if (!cur.drow[s]) continue;
+        u32x4* vc = as_global(reinterpret_cast<u32x4*>(cur.drow[s]));
+        float* scales = as_global(reinterpret_cast<float*>(cur.drow[s] + H));
 #pragma unroll
         for (int u = 0; u < CB; ++u) {
           const uint32_t j = (c0 + u) * kLanes + lane;
           if (j < nunits) {
-            x[u][0] = ld16<true>(src + 2 * j);
-            x[u][1] = ld16<true>(src + 2 * j + 1);
-          } else {
-            x[u][0] = u32x4{0, 0, 0, 0};
-            x[u][1] = u32x4{0, 0, 0, 0};
+            st16<true>(vc + j, x[u][0]);
+            if ((j & (g16 - 1)) == 0) scales[j >> gsh] = sc[u];
           }
         }
-#pragma unroll
-        for (int u = 0; u < CB; ++u) {
-          mb[u] = unit_amax_bits(x[u][0], x[u][1]);
-          for (uint32_t off = 1; off < g16; off <<= 1) mb[u] = max(mb[u], (uint32_t)__shfl_xor((int)mb[u], (int)off));
-        }
-        float sc[CB];
-#pragma unroll
-        for (int u = 0; u < CB; ++u) {
-          const float amax = fmaxf(__uint_as_float(mb[u] << 16), 0x1p-110f);
-          x[u][0] = unit_codes(x[u][0], x[u][1], 448.0f / amax);
-          sc[u] = amax / 448.0f;
-        }
-#pragma unroll
-        for (int s = 0; s < kMaxTopK; ++s) {
-          if (!drow[s]) continue;
-          u32x4* vc = as_global(reinterpret_cast<u32x4*>(drow[s]));
-          float* scales = as_global(reinterpret_cast<float*>(drow[s] + H));
-#pragma unroll
-          for (int u = 0; u < CB; ++u) {
-            const uint32_t j = (c0 + u) * kLanes + lane;
-            if (j < nunits) {
-              st16<true>(vc + j, x[u][0]);
-              if ((j & (g16 - 1)) == 0) scales[j >> gsh] = sc[u];
-            }
-          }
-        }
-      }
-      if ((uint32_t)lane < npad) {
-#pragma unroll
-        for (int s = 0; s < kMaxTopK; ++s)
-          if (drow[s]) as_global(reinterpret_cast<float*>(drow[s] + H))[ngroups + lane] = 0.0f;
+        if (row_done && (uint32_t)lane < npad) scales[ngroups + lane] = 0.0f;
       }
     }
-    tgt.finish(rank, t * (uint64_t)a.k, loc, lane);
+    if (row_done) tgt.finish(cur.rank, cur.t * (uint64_t)a.k, cur.loc, lane);
+    if (!more) break;
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      x[u][0] = xn[u][0];
+      x[u][1] = xn[u][1];
+    }
+    if (row_done) cur = nxt;
+    c0 = cn;
   }
 }
 

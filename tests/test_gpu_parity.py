@@ -1582,3 +1582,30 @@ def test_line_aligned_heads(coll, off, dtype):
         expect = native.allreduce(hx, op, dtype)
         for r in (0, p - 1):
             assert_bits_equal(to_host(recv[r], dtype), expect, f"batch call {k} n={n} off={off} rank {r}")
+
+
+@pytest.mark.parametrize("roff", [0, 1, 7, 100, 255])
+def test_alltoallv_bytes_line_aligned_receive(coll, roff):
+    """Byte Alltoallv (the FP8 exchange's element type) into receive
+    buffers `roff` bytes into their allocations, with counts of whole
+    7392-byte rows and ragged counts: every segment's head runs up to the
+    receive buffer's next 256-byte line (heads longer than a workgroup's
+    lanes at one byte per element); against the oracle."""
+    import torch
+    p = 8
+    g = np.random.default_rng(roff)
+    for counts in (g.integers(0, 40, (p, p)) * 7392, g.integers(0, 3000, (p, p))):
+        xs = [g.integers(0, 256, int(counts[i].sum()), dtype=np.uint8) for i in range(p)]
+        send = [torch.from_numpy(x).cuda() for x in xs]
+        keep, recv = [], []
+        for c in counts.sum(axis=0):
+            base = torch.full((int(c) + roff + 64,), 0xAB, dtype=torch.uint8, device="cuda")
+            keep.append(base)
+            recv.append(base[roff:roff + int(c)])
+        coll.coll_alltoallv(send, recv, torch.from_numpy(counts.reshape(-1).astype(np.int64)).cuda())
+        sync()
+        expect = native.alltoallv(xs, counts)
+        for j in range(p):
+            got = keep[j].cpu().numpy()
+            assert np.array_equal(got[roff:roff + len(expect[j])], expect[j]), f"dest {j} roff {roff}"
+            assert np.all(got[:roff] == 0xAB) and np.all(got[roff + len(expect[j]):] == 0xAB), "outside the receive range"
