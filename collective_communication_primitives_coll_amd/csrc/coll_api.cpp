@@ -567,7 +567,6 @@ coll_status_t alltoallv_impl(const void* const* send, void* const* recv, int p, 
   a.p = p;
   a.src_mis = common_mis(send, p);
   a.dst_mis = common_mis((const void* const*)recv, p);
-  a.dst_amis = common_amis((const void* const*)recv, p);
   a.transposed = transposed;
   return finish(coll::launch_alltoallv((int)d, P, a, grid, stream));
 }

@@ -24,7 +24,7 @@ namespace coll {
 // AllGather / Broadcast with a compile-time rank count P (0: any).
 // Destination pointers of a segment are read once into registers.  With
 // one rank the fan-out is a 1:1 copy and loads non-temporally too.
-template <int B, int KIND, int P>
+template <int B, int KIND, int P, bool SHIFT>
 COLL_STREAM_KERNEL void fanout_kernel(RankPtrs ptrs, CopyGeom g) {
   using W = typename Word<B>::T;
   const int p = P ? P : g.p;
@@ -32,7 +32,7 @@ COLL_STREAM_KERNEL void fanout_kernel(RankPtrs ptrs, CopyGeom g) {
   uint64_t base = 0;
   for (int s = 0; s < nseg; ++s) {
     const uint64_t dst_off = KIND == kCopyAllGather ? (uint64_t)s * g.n : 0;
-    const int mis = seg_mis(g.src_mis, g.dst_mis, 0, dst_off * B);
+    const int mis = g.dst_mis < 0 ? -1 : (int)((g.dst_mis + dst_off * B) & 15);
     uint64_t nt;
     if (!copy_segment_owned<B>(g.n, mis, base, &nt)) {
       base += nt;
@@ -44,10 +44,10 @@ COLL_STREAM_KERNEL void fanout_kernel(RankPtrs ptrs, CopyGeom g) {
 #pragma unroll
       for (int k = 0; k < P; ++k) dst[k] = (W*)ptrs.dst[k] + dst_off;
       auto gdst = [&](int d) -> W* { return dst[d]; };
-      base += copy_segment<B, P == 1, P>(src, gdst, P, g.n, mis, base);
+      base += copy_segment<B, P == 1, P, SHIFT>(src, gdst, P, g.n, mis, base);
     } else {
       auto gdst = [&](int d) -> W* { return (W*)ptrs.dst[d] + dst_off; };
-      base += copy_segment<B, false, 0>(src, gdst, p, g.n, mis, base);
+      base += copy_segment<B, false, 0, SHIFT>(src, gdst, p, g.n, mis, base);
     }
   }
 }
@@ -58,7 +58,7 @@ COLL_STREAM_KERNEL void fanout_kernel(RankPtrs ptrs, CopyGeom g) {
 //               receiver, "详解分布式训练8大集合通信原语" section 4.3);
 //   Scatter     p segments r: send_root + r*n -> recv[r] (section 3.3).
 // The in-place forms copy the root's own block onto itself.
-template <int B, int KIND>
+template <int B, int KIND, bool SHIFT>
 COLL_STREAM_KERNEL void pair_copy_kernel(RankPtrs ptrs, CopyGeom g) {
   using W = typename Word<B>::T;
   const int p = g.p;
@@ -83,14 +83,15 @@ COLL_STREAM_KERNEL void pair_copy_kernel(RankPtrs ptrs, CopyGeom g) {
       src = (const W*)ptrs.src[0] + src_off;
       dst = (W*)ptrs.dst[sgi];
     }
-    const int mis = seg_mis(g.src_mis, g.dst_mis, src_off * B, dst_off * B);
+    (void)src_off;
+    const int mis = (int)((uintptr_t)dst & 15);
     uint64_t nt;
     if (!copy_segment_owned<B>(g.n, mis, base, &nt)) {
       base += nt;
       continue;
     }
     auto gdst = [&](int) -> W* { return dst; };
-    base += copy_segment<B, true, 1>(src, gdst, 1, g.n, mis, base);
+    base += copy_segment<B, true, 1, SHIFT>(src, gdst, 1, g.n, mis, base);
   }
 }
 
@@ -266,17 +267,18 @@ COLL_STREAM_KERNEL void alltoallv_kernel(RankPtrs ptrs, A2avArgs a) {
     const uint64_t ro = (uint64_t)roff[sgi];
     const W* src = (const W*)ptrs.src[i] + so;
     W* dst = (W*)ptrs.dst[j] + ro;
-    const int mis = seg_mis(a.src_mis, a.dst_mis, so * B, ro * B);
+    const int mis = (int)((uintptr_t)dst & 15);
     auto gdst = [&](int) -> W* { return dst; };
-    base += copy_segment<B, true, 1>(src, gdst, 1, len, mis, base);
+    base += copy_segment<B, true, 1, true>(src, gdst, 1, len, mis, base);
   }
 }
 
 // Alltoallv for p <= 16 (p^2 <= kBlock segments): after staging the
-// counts, thread s computes segment s's tile count (from its own
-// misalignment; a segment with only an unaligned head or tail gets one
-// tile), a workgroup-wide scan turns the counts into tile starts, and
-// each flat tile finds its segment by binary search over the starts.  The
+// counts, thread s computes segment s's geometry from its pointers (a head
+// up to the receive buffer's next 256-byte line, aligned destination
+// vectors, a tail) and its tile count (a segment with only a head or tail
+// gets one tile); workgroup-wide scans turn the counts into tile starts,
+// and each flat tile finds its segment by binary search over the starts.  The
 // walking kernel above has every workgroup run the segment routine for
 // all p^2 segments, which made small calls take 40 us at p = 8 and 149 us
 // at p = 16.
@@ -284,10 +286,13 @@ template <int B>
 COLL_STREAM_KERNEL void alltoallv_flat_kernel(RankPtrs ptrs, A2avArgs a) {
   using W = typename Word<B>::T;
   constexpr uint64_t V = 16 / B;
-  constexpr uint64_t TE = (uint64_t)kBlock * 4;  // elements per tile of the element path
   extern __shared__ int64_t lds[];
   __shared__ int bad;
-  __shared__ uint64_t tstart[kBlock + 1];
+  // tile starts of the segments whose sources share the destinations'
+  // 16-byte alignment (plain vector tiles) and of the others (byte-shifted
+  // tiles): two separate loops below, so the common aligned loop keeps its
+  // own waits (one loop holding both paths cost the aligned case 4%)
+  __shared__ uint64_t tstart[2][kBlock + 1];
   if (stage_a2av_counts(a, lds, &bad)) return;
   const int p = a.p;
   const int pp = p * p;
@@ -295,62 +300,80 @@ COLL_STREAM_KERNEL void alltoallv_flat_kernel(RankPtrs ptrs, A2avArgs a) {
   const int64_t* soff = lds + pp;
   const int64_t* roff = lds + 2 * pp;
   const int tid = threadIdx.x;
-  uint64_t nt = 0;
+  uint64_t nt[2] = {0, 0};
   if (tid < pp && cnt[tid] > 0) {
     const uint64_t len = (uint64_t)cnt[tid];
-    const SegSpan sp = seg_span_a<B>(len, seg_mis(a.src_mis, a.dst_mis, (uint64_t)soff[tid] * B, (uint64_t)roff[tid] * B),
-                                     seg_amis(a.dst_amis, (uint64_t)roff[tid] * B));
-    nt = sp.vec ? ceil_div(sp.nvec, kCopyTV) : ceil_div(len, TE);
-    if (nt == 0) nt = 1;
+    const int si = tid / p, sj = tid - (tid / p) * p;
+    const ShiftSpan sp = shift_span<B>((const W*)ptrs.src[si] + soff[tid], (W*)ptrs.dst[sj] + roff[tid], len);
+    const uint64_t n = sp.nvec ? ceil_div(sp.nvec, kCopyTV) : 1;
+    nt[(sp.m != 0 && sp.nvec != 0) ? 1 : 0] = n;
   }
-  // inclusive scan of nt over the workgroup: tstart[s + 1] = tiles of segments 0..s
-  tstart[tid + 1] = nt;
-  if (tid == 0) tstart[0] = 0;
+  // inclusive scans: tstart[c][s + 1] = tiles of class c among segments 0..s
+  for (int c = 0; c < 2; ++c) {
+    tstart[c][tid + 1] = nt[c];
+    if (tid == 0) tstart[c][0] = 0;
+  }
   __syncthreads();
   for (int off = 1; off < kBlock; off <<= 1) {
-    const uint64_t v = tid >= off ? tstart[tid + 1 - off] : 0;
+    const uint64_t v0 = tid >= off ? tstart[0][tid + 1 - off] : 0;
+    const uint64_t v1 = tid >= off ? tstart[1][tid + 1 - off] : 0;
     __syncthreads();
-    tstart[tid + 1] += v;
+    tstart[0][tid + 1] += v0;
+    tstart[1][tid + 1] += v1;
     __syncthreads();
   }
-  const uint64_t total = tstart[pp];
-  for (uint64_t f = blockIdx.x; f < total; f += gridDim.x) {
-    // segment sgi with tstart[sgi] <= f < tstart[sgi + 1] (it has tiles)
+  // segment of class c holding that class's tile f, and the tile's index in it
+  auto find = [&](int c, uint64_t f, int* sgi, uint64_t* t) {
     int lo = 0, hi = pp;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (tstart[mid] <= f) lo = mid;
+      if (tstart[c][mid] <= f) lo = mid;
       else hi = mid;
     }
-    const int sgi = lo;
-    const uint64_t t = f - tstart[sgi];
-    const int i = sgi / p, j = sgi - (sgi / p) * p;
-    const uint64_t len = (uint64_t)cnt[sgi];
-    const uint64_t so = (uint64_t)soff[sgi];
-    const uint64_t ro = (uint64_t)roff[sgi];
-    const W* src = (const W*)ptrs.src[i] + so;
-    W* dst = (W*)ptrs.dst[j] + ro;
-    const SegSpan sp = seg_span_a<B>(len, seg_mis(a.src_mis, a.dst_mis, so * B, ro * B), seg_amis(a.dst_amis, ro * B));
-    if (!sp.vec) {
-      const uint64_t from = t * TE;
-      const uint64_t n = (len - from) < TE ? (len - from) : TE;
-      for (uint64_t e = tid; e < n; e += kBlock) st1<true>(dst + from + e, ld1<true>(src + from + e));
-      continue;
+    *sgi = lo;
+    *t = f - tstart[c][lo];
+  };
+  auto edges = [&](const W* src, W* dst, const ShiftSpan& sp) {
+    // the head (up to the next 256-byte line of the receive buffer) and
+    // the tail (under one vector)
+    for (uint64_t e = tid; e < sp.head + sp.tail; e += kBlock) {
+      const uint64_t x = e < sp.head ? e : sp.head + sp.nvec * V + (e - sp.head);
+      st1<true>(dst + x, ld1<true>(src + x));
     }
+  };
+  const uint64_t total0 = tstart[0][pp], total = total0 + tstart[1][pp];
+  uint64_t f = blockIdx.x;
+  for (; f < total0; f += gridDim.x) {
+    int sgi;
+    uint64_t t;
+    find(0, f, &sgi, &t);
+    const int i = sgi / p, j = sgi - (sgi / p) * p;
+    const W* src = (const W*)ptrs.src[i] + soff[sgi];
+    W* dst = (W*)ptrs.dst[j] + roff[sgi];
+    const ShiftSpan sp = shift_span<B>(src, dst, (uint64_t)cnt[sgi]);
     const u32x4* vs = reinterpret_cast<const u32x4*>(src + sp.head);
     u32x4* vd = reinterpret_cast<u32x4*>(dst + sp.head);
     auto gdst = [&](int) -> u32x4* { return vd; };
     const uint64_t j0 = t * kCopyTV + tid;
     if ((t + 1) * kCopyTV <= sp.nvec) copy_vec_tile<true, true, 1>(vs, gdst, 1, j0, sp.nvec);
     else if (t * kCopyTV < sp.nvec) copy_vec_tile<true, false, 1>(vs, gdst, 1, j0, sp.nvec);
-    if (t == 0 && (sp.head || sp.tail)) {
-      // the head (up to the next 256-byte line of the receive buffer) and
-      // the tail (under one vector)
-      for (uint64_t e = tid; e < sp.head + sp.tail; e += kBlock) {
-        const uint64_t x = e < sp.head ? e : sp.head + sp.nvec * V + (e - sp.head);
-        st1<true>(dst + x, ld1<true>(src + x));
-      }
-    }
+    if (t == 0 && (sp.head || sp.tail)) edges(src, dst, sp);
+  }
+  for (; f < total; f += gridDim.x) {
+    int sgi;
+    uint64_t t;
+    find(1, f - total0, &sgi, &t);
+    const int i = sgi / p, j = sgi - (sgi / p) * p;
+    const W* src = (const W*)ptrs.src[i] + soff[sgi];
+    W* dst = (W*)ptrs.dst[j] + roff[sgi];
+    const ShiftSpan sp = shift_span<B>(src, dst, (uint64_t)cnt[sgi]);
+    const u32x4* vs = reinterpret_cast<const u32x4*>((uintptr_t)(src + sp.head) & ~(uintptr_t)15);
+    u32x4* vd = reinterpret_cast<u32x4*>(dst + sp.head);
+    auto gdst = [&](int) -> u32x4* { return vd; };
+    const uint64_t j0 = t * kCopyTV + tid;
+    if ((t + 1) * kCopyTV <= sp.nvec) copy_shift_tile<true, 1>(vs, gdst, 1, j0, sp.nvec, sp.m);
+    else if (t * kCopyTV < sp.nvec) copy_shift_tile<false, 1>(vs, gdst, 1, j0, sp.nvec, sp.m);
+    if (t == 0 && (sp.head || sp.tail)) edges(src, dst, sp);
   }
 }
 
@@ -362,16 +385,28 @@ static int clamp_grid(uint64_t tiles, int max_grid) {
   return (int)(tiles < (uint64_t)max_grid ? tiles : (uint64_t)max_grid);
 }
 
-template <int B, int KIND>
+template <int B, int KIND, bool SHIFT>
 static void launch_fanout(int p, int grid, const RankPtrs& ptrs, const CopyGeom& g, hipStream_t s) {
   switch (p) {
-    case 1: hipLaunchKernelGGL((fanout_kernel<B, KIND, 1>), dim3(grid), dim3(kBlock), 0, s, ptrs, g); break;
-    case 2: hipLaunchKernelGGL((fanout_kernel<B, KIND, 2>), dim3(grid), dim3(kBlock), 0, s, ptrs, g); break;
-    case 4: hipLaunchKernelGGL((fanout_kernel<B, KIND, 4>), dim3(grid), dim3(kBlock), 0, s, ptrs, g); break;
-    case 8: hipLaunchKernelGGL((fanout_kernel<B, KIND, 8>), dim3(grid), dim3(kBlock), 0, s, ptrs, g); break;
-    case 16: hipLaunchKernelGGL((fanout_kernel<B, KIND, 16>), dim3(grid), dim3(kBlock), 0, s, ptrs, g); break;
-    default: hipLaunchKernelGGL((fanout_kernel<B, KIND, 0>), dim3(grid), dim3(kBlock), 0, s, ptrs, g); break;
+    case 1: hipLaunchKernelGGL((fanout_kernel<B, KIND, 1, SHIFT>), dim3(grid), dim3(kBlock), 0, s, ptrs, g); break;
+    case 2: hipLaunchKernelGGL((fanout_kernel<B, KIND, 2, SHIFT>), dim3(grid), dim3(kBlock), 0, s, ptrs, g); break;
+    case 4: hipLaunchKernelGGL((fanout_kernel<B, KIND, 4, SHIFT>), dim3(grid), dim3(kBlock), 0, s, ptrs, g); break;
+    case 8: hipLaunchKernelGGL((fanout_kernel<B, KIND, 8, SHIFT>), dim3(grid), dim3(kBlock), 0, s, ptrs, g); break;
+    case 16: hipLaunchKernelGGL((fanout_kernel<B, KIND, 16, SHIFT>), dim3(grid), dim3(kBlock), 0, s, ptrs, g); break;
+    default: hipLaunchKernelGGL((fanout_kernel<B, KIND, 0, SHIFT>), dim3(grid), dim3(kBlock), 0, s, ptrs, g); break;
   }
+}
+
+// Whether some segment's source disagrees modulo 16 with its destinations
+// (the walking kernels then compile the byte-shift path).  Segment
+// offsets are multiples of n elements: s * n for AllGather destinations,
+// Gather destinations and Scatter sources, (j * n, i * n) for All-to-All.
+template <int B>
+static bool copy_needs_shift(const CopyGeom& g) {
+  if (g.src_mis < 0 || g.dst_mis < 0) return true;
+  if (g.src_mis != g.dst_mis) return true;
+  if (g.kind == kCopyBroadcast || g.p == 1) return false;
+  return ((g.n * (uint64_t)B) & 15) != 0;
 }
 
 // Uniform segments (see pair_copy_flat_kernel): the common head, vector
@@ -391,6 +426,20 @@ static bool uniform_pair_layout(const CopyGeom& g, uint64_t nseg, uint64_t* head
   const uint64_t t = (*nvec + kCopyTV - 1) / kCopyTV;
   *tps = t ? t : 1;
   return nseg * *tps < (uint64_t{1} << 32);
+}
+
+template <int B, bool SHIFT>
+static void launch_walking(const RankPtrs& ptrs, const CopyGeom& g, int grid, hipStream_t s) {
+  if (g.kind == kCopyAllToAll)
+    hipLaunchKernelGGL((pair_copy_kernel<B, kCopyAllToAll, SHIFT>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
+  else if (g.kind == kCopyGather)
+    hipLaunchKernelGGL((pair_copy_kernel<B, kCopyGather, SHIFT>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
+  else if (g.kind == kCopyScatter)
+    hipLaunchKernelGGL((pair_copy_kernel<B, kCopyScatter, SHIFT>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
+  else if (g.kind == kCopyAllGather)
+    launch_fanout<B, kCopyAllGather, SHIFT>(g.p, grid, ptrs, g, s);
+  else
+    launch_fanout<B, kCopyBroadcast, SHIFT>(g.p, grid, ptrs, g, s);
 }
 
 template <int B>
@@ -435,16 +484,8 @@ static int launch_copy_b(const RankPtrs& ptrs, const CopyGeom& g, int max_grid, 
   const uint64_t te = kCopyTV * (16 / B);
   const int grid = clamp_grid(nseg * ((g.n + te - 1) / te + 1), max_grid);
   if (!grid) return 0;
-  if (g.kind == kCopyAllToAll)
-    hipLaunchKernelGGL((pair_copy_kernel<B, kCopyAllToAll>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
-  else if (g.kind == kCopyGather)
-    hipLaunchKernelGGL((pair_copy_kernel<B, kCopyGather>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
-  else if (g.kind == kCopyScatter)
-    hipLaunchKernelGGL((pair_copy_kernel<B, kCopyScatter>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
-  else if (g.kind == kCopyAllGather)
-    launch_fanout<B, kCopyAllGather>(g.p, grid, ptrs, g, s);
-  else
-    launch_fanout<B, kCopyBroadcast>(g.p, grid, ptrs, g, s);
+  if (copy_needs_shift<B>(g)) launch_walking<B, true>(ptrs, g, grid, s);
+  else launch_walking<B, false>(ptrs, g, grid, s);
   return (int)hipGetLastError();
 }
 

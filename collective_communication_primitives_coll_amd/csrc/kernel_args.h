@@ -75,7 +75,6 @@ struct A2avArgs {
   int p;
   int src_mis;
   int dst_mis;
-  int dst_amis;                  // common receive base address modulo 256, or -1
   int transposed;                // elements from i to j are counts[j*p + i]
 };
 

@@ -1609,3 +1609,95 @@ def test_alltoallv_bytes_line_aligned_receive(coll, roff):
             got = keep[j].cpu().numpy()
             assert np.array_equal(got[roff:roff + len(expect[j])], expect[j]), f"dest {j} roff {roff}"
             assert np.all(got[:roff] == 0xAB) and np.all(got[roff + len(expect[j]):] == 0xAB), "outside the receive range"
+
+
+# ----------------------------------------------------------------------------
+# Copies whose sources and destinations disagree modulo 16 bytes: aligned
+# destination vectors assembled from two source vectors (byte shifts)
+# ----------------------------------------------------------------------------
+
+def _bytes_dtype(dt):
+    return {F32: np.float32, BF16: np.uint16, I32: np.int32}[dt]
+
+
+@pytest.mark.parametrize("dtype", [BF16, F32, 3])
+@pytest.mark.parametrize("soff,doff", [(1, 0), (0, 3), (5, 2), (7, 11)])
+def test_copies_with_disagreeing_alignment(coll, dtype, soff, doff):
+    """AllGather, Broadcast, All-to-All, Gather, Scatter and Alltoallv with
+    send buffers `soff` and receive buffers `doff` elements into their
+    allocations and block sizes that are not whole 16-byte vectors, so
+    sources and destinations sit at different offsets within 16 bytes (every
+    shift 1..15 bytes for the byte type); whole outputs against the oracle,
+    bytes outside the outputs untouched."""
+    import torch
+    ebytes = {BF16: 2, F32: 4, 3: 1}[dtype]
+    npdt = {BF16: np.uint16, F32: np.uint32, 3: np.uint8}[dtype]
+    tdt = {BF16: torch.bfloat16, F32: torch.float32, 3: torch.uint8}[dtype]
+    g = np.random.default_rng(soff * 100 + doff * 10 + ebytes)
+    keep = []
+
+    def dev_view(x, off):
+        base = torch.zeros(len(x) + off + 64, dtype=tdt, device="cuda")
+        base.view(torch.uint8)[:] = 0x5A
+        if len(x):
+            base.view(torch.uint8)[off * ebytes:(off + len(x)) * ebytes] = torch.from_numpy(
+                np.ascontiguousarray(x).view(np.uint8)).cuda()
+        keep.append(base)
+        return base, base[off:off + len(x)]
+
+    def host(base):
+        return base.view(torch.uint8).cpu().numpy().view(npdt)
+
+    def check(base, off, expect, what):
+        h = host(base)
+        assert np.array_equal(h[off:off + len(expect)], expect), what
+        pad = base.view(torch.uint8).cpu().numpy()
+        assert np.all(pad[:off * ebytes] == 0x5A) and np.all(pad[(off + len(expect)) * ebytes:] == 0x5A), what
+
+    cdt = {BF16: coll.COLL_BF16, F32: coll.COLL_F32, 3: coll.COLL_U8}[dtype]
+    for p, n in ((3, 1001), (8, 4 * 1024 + 5), (4, 3 * 8192 + 7)):
+        xs = [g.integers(0, 2**(8 * ebytes), n, dtype=np.uint64).astype(npdt) for _ in range(p)]
+        # AllGather
+        send = [dev_view(x, soff)[1] for x in xs]
+        rb = [dev_view(np.zeros(p * n, npdt), doff) for _ in range(p)]
+        coll.coll_allgather(send, [v for _, v in rb], n=n, dtype=cdt)
+        sync()
+        cat = np.concatenate(xs)
+        for r in range(p):
+            check(rb[r][0], doff, cat, f"AG p={p} rank {r}")
+        # Broadcast from rank p-1
+        rb = [dev_view(np.zeros(n, npdt), doff) for _ in range(p)]
+        coll.coll_broadcast(send[p - 1], [v for _, v in rb], p - 1, n=n, dtype=cdt)
+        sync()
+        for r in range(p):
+            check(rb[r][0], doff, xs[p - 1], f"Bcast p={p} rank {r}")
+        # Gather to root 1 and Scatter from it
+        root = dev_view(np.zeros(p * n, npdt), doff)
+        coll.coll_gather(send, root[1], 1, n=n, dtype=cdt)
+        sync()
+        check(root[0], doff, cat, f"Gather p={p}")
+        sb = [dev_view(np.zeros(n, npdt), doff) for _ in range(p)]
+        src_root = dev_view(cat, soff)[1]
+        coll.coll_scatter(src_root, [v for _, v in sb], 1, n=n, dtype=cdt)
+        sync()
+        for r in range(p):
+            check(sb[r][0], doff, xs[r] if r != 1 else cat[n:2 * n], f"Scatter p={p} rank {r}")
+        # All-to-All with blocks of nb elements
+        nb = n // p
+        a2s = [dev_view(x[:p * nb], soff)[1] for x in xs]
+        a2r = [dev_view(np.zeros(p * nb, npdt), doff) for _ in range(p)]
+        coll.coll_alltoall(a2s, [v for _, v in a2r], nb, dtype=cdt)
+        sync()
+        exp = native.alltoall([x[:p * nb] for x in xs])
+        for j in range(p):
+            check(a2r[j][0], doff, exp[j], f"A2A p={p} dest {j}")
+        # Alltoallv with ragged counts
+        counts = g.integers(0, n // p, (p, p))
+        vs = [dev_view(xs[i][:int(counts[i].sum())], soff)[1] for i in range(p)]
+        vr = [dev_view(np.zeros(int(c), npdt), doff) for c in counts.sum(axis=0)]
+        coll.coll_alltoallv(vs, [v for _, v in vr], torch.from_numpy(counts.reshape(-1).astype(np.int64)).cuda(),
+                            dtype=cdt)
+        sync()
+        exp = native.alltoallv([xs[i][:int(counts[i].sum())] for i in range(p)], counts)
+        for j in range(p):
+            check(vr[j][0], doff, exp[j], f"A2Av p={p} dest {j}")
