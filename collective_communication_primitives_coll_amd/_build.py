@@ -24,6 +24,9 @@ SOURCES = [
     "reduce_kernels_p3_7.hip",
     "reduce_kernels_p9_12.hip",
     "reduce_kernels_p13_15.hip",
+    "reduce_trees_p3_7.hip",
+    "reduce_trees_p9_12.hip",
+    "reduce_trees_p13_15.hip",
     "copy_kernels.hip",
     "a2a_lds_kernels.hip",
     "ring_literal.hip",
@@ -60,9 +63,17 @@ def common_flags() -> list[str]:
     ]
 
 
+# Per-source flags.  batch_kernels.hip reads each atomic's result well after
+# issuing it; LLVM's atomic optimizer would rewrite the atomic into a
+# wave-wide one whose result is read, and waited for, at once.
+EXTRA_FLAGS = {
+    "batch_kernels.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *common_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *common_flags(), *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -181,14 +181,39 @@ __device__ __forceinline__ BatchCall load_call(const BatchCall* c) {
   return b;
 }
 
+// Lane 0's claim of one run from the counter (the other lanes get 0).  Its
+// result is read with wave_value only at the end of the run it was issued
+// before.  (This file is built without LLVM's atomic optimizer, which would
+// read the result right after the atomic and so wait for it at once.)
+__device__ __forceinline__ unsigned long long issue_claim(unsigned long long* next_run, int lane) {
+  unsigned long long r = 0;
+  if (lane == 0) r = atomicAdd(as_global(next_run), 1ull);
+  return r;
+}
+
+__device__ __forceinline__ uint64_t wave_value(unsigned long long v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
 // Every wave is an independent worker.  The flat tile range is cut into
-// runs of kBatchRun tiles; wave w takes runs w, w + W, w + 2W, ... (W waves
-// in the grid), so at any moment the waves work on one window of the range
-// and move through it front to back together.  A wave finds a run's first
-// call by binary search (from its previous run's call onward) and walks
-// forward call by call.  Short runs keep that window narrow: with 4-vector
-// tiles the 10,000-call p = 16 plan took 13.2 ms with runs of 32 tiles,
-// 13.0 with 8 and 12.9 with 2 (1: 13.1, a search per tile).
+// runs of kBatchRun tiles.  The first runs, about seven eighths of them,
+// are dealt out in turn (wave w takes runs w, w + W, ... for W waves in the
+// grid), so the waves work on one window of the range and move through it
+// front to back together.  The XCDs do not all stream at the same rate:
+// dealt out to the end, the 10,000-call p = 16 plan's waves finished over a
+// spread of 1.2 ms, those of the odd-numbered XCDs last.  So the remaining
+// runs are claimed one at a time from a counter in the descriptor table
+// (zero at launch), and a wave that runs ahead claims more of them.  A
+// claim is issued before the run in hand and read at its end: gfx9 counts
+// loads, stores and atomics on one in-order counter, so reading it waits
+// for that run's stores, which is why claims are kept to the tail.  A wave
+// finds a run's first call by binary search (from its previous run's call
+// onward, as its runs only grow) and walks forward call by call.  Short
+// runs keep the window narrow: with 4-vector tiles the plan took 13.2 ms
+// with runs of 32 tiles, 13.0 with 8 and 12.9 with 2 (1: 13.1, a search
+// per tile).
 constexpr uint64_t kBatchRun = 2;
 
 template <int P>
@@ -199,8 +224,16 @@ COLL_STREAM_KERNEL void batch_kernel(BatchArgs a) {
   const uint64_t wid =
       (uint64_t)blockIdx.x * (kBlock / kWave) + (uint64_t)__builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const uint64_t total = ld_const(&a.calls[a.ncalls].first_tile);
+  const uint64_t nruns = (total + kBatchRun - 1) / kBatchRun;
+  const uint64_t nfixed = nruns / 8 * 7 / waves * waves;  // runs dealt out in turn
   int from_call = 0;
-  for (uint64_t run = wid; run * kBatchRun < total; run += waves) {
+  uint64_t run = wid < nfixed ? wid : nfixed + wave_value(issue_claim(a.next_run, lane));
+  // every claim returns a distinct, larger value, so each wave leaves the
+  // loop after at most nruns / W + 1 dealt runs and nruns + 1 claims
+  while (run < nruns) {
+    const bool dealt = run + waves < nfixed;  // the next run is dealt, not claimed
+    unsigned long long pending = 0;
+    if (!dealt) pending = issue_claim(a.next_run, lane);
     uint64_t t = run * kBatchRun;
     const uint64_t end = t + kBatchRun < total ? t + kBatchRun : total;
     // last call whose first tile is <= t
@@ -220,6 +253,8 @@ COLL_STREAM_KERNEL void batch_kernel(BatchArgs a) {
         batch_dispatch<P>(bc, a.ptrs + (size_t)k * 2 * p, p, t - bc.first_tile, stop - bc.first_tile, lane);
       t = stop > t ? stop : t;
     }
+    if (dealt) run += waves;
+    else run = nfixed + wave_value(pending);
   }
 }
 

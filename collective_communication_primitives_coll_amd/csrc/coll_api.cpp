@@ -185,6 +185,19 @@ coll::RankPtrs make_ptrs(const void* const* src, int ns, void* const* dst, int n
 coll_status_t finish(int err) { return err ? hip_fail(err) : COLL_OK; }
 
 // Summation order of an AllReduce schedule (RING_LITERAL has its own kernels).
+// Rank counts each schedule is built for: the ring at any count; recursive
+// doubling and halving-doubling pair ranks by powers of two, so p in
+// {2, 4, 8, 16}; the heap-ordered trees at any count from 2 to 16.
+bool schedule_supported(coll_algo_t algo, int p) {
+  switch (algo) {
+    case COLL_ALGO_RING:
+    case COLL_ALGO_RING_LITERAL: return true;
+    case COLL_ALGO_TREE:
+    case COLL_ALGO_DOUBLE_BINARY_TREE: return p >= 2 && p <= 16;
+    default: return p == 2 || p == 4 || p == 8 || p == 16;
+  }
+}
+
 int order_of(coll_algo_t algo) {
   switch (algo) {
     case COLL_ALGO_RECURSIVE_DOUBLING: return coll::kOrdRD;
@@ -226,8 +239,7 @@ COLL_EXPORT coll_status_t coll_allreduce_algo(const void* const* send, void* con
   if ((int)algo < COLL_ALGO_RING || (int)algo > COLL_ALGO_DOUBLE_BINARY_TREE) return COLL_ERR_INVALID_ARG;
   coll_status_t st = check_allreduce(send, recv, p, n, dtype, op);
   if (st != COLL_OK || n == 0) return st;
-  const bool tree_algo = algo != COLL_ALGO_RING && algo != COLL_ALGO_RING_LITERAL;
-  if (tree_algo && !(p == 2 || p == 4 || p == 8 || p == 16)) return COLL_ERR_UNSUPPORTED;
+  if (!schedule_supported(algo, p)) return COLL_ERR_UNSUPPORTED;
   if (algo == COLL_ALGO_RING_LITERAL && dtype == COLL_BF16) return COLL_ERR_UNSUPPORTED;
   int grid;
   int e = max_grid(&grid, algo == COLL_ALGO_RING_LITERAL ? kFamCopy : kFamReduce);
@@ -281,8 +293,7 @@ COLL_EXPORT coll_status_t coll_allreduce_premul(const void* const* send, void* c
   if (st != COLL_OK || n == 0) return st;
   if (!scale) return COLL_ERR_INVALID_ARG;
   if (dtype == COLL_I32 || algo == COLL_ALGO_RING_LITERAL) return COLL_ERR_UNSUPPORTED;
-  const bool tree_algo = algo != COLL_ALGO_RING && algo != COLL_ALGO_RING_LITERAL;
-  if (tree_algo && !(p == 2 || p == 4 || p == 8 || p == 16)) return COLL_ERR_UNSUPPORTED;
+  if (!schedule_supported(algo, p)) return COLL_ERR_UNSUPPORTED;
   int grid;
   int e = max_grid(&grid, kFamReduce);
   if (e) return hip_fail(e);
@@ -1072,28 +1083,39 @@ COLL_EXPORT coll_status_t coll_moe_combine_direct(const void* const* y, const in
 // ---------------------------------------------------------------------------
 namespace {
 
-struct BatchState {
-  std::mutex mu;
+// One descriptor table: a device buffer, its pinned staging buffer, and an
+// event recorded after the batch kernel that reads them.
+struct BatchSlot {
   void* dev_buf = nullptr;
   size_t dev_cap = 0;
   void* host_buf = nullptr;
   size_t host_cap = 0;
-  hipEvent_t done = nullptr;  // recorded after the last batch kernel
+  hipEvent_t done = nullptr;
+};
+
+// Two slots used in turn: a batch waits only for the batch two calls
+// before it (which used the same slot), so the host validates and packs
+// the next batch while the previous kernel runs.
+struct BatchState {
+  std::mutex mu;
+  BatchSlot slot[2];
+  int next = 0;
   int device = -1;
 };
 BatchState g_batch;
 
 // Release everything; caller holds the mutex.
 void batch_release() {
-  if (g_batch.done) {
-    hipEventSynchronize(g_batch.done);
-    hipEventDestroy(g_batch.done);
-    g_batch.done = nullptr;
+  for (BatchSlot& b : g_batch.slot) {
+    if (b.done) {
+      hipEventSynchronize(b.done);
+      hipEventDestroy(b.done);
+    }
+    if (b.dev_buf) hipFree(b.dev_buf);
+    if (b.host_buf) hipHostFree(b.host_buf);
+    b = BatchSlot{};
   }
-  if (g_batch.dev_buf) hipFree(g_batch.dev_buf);
-  if (g_batch.host_buf) hipHostFree(g_batch.host_buf);
-  g_batch.dev_buf = g_batch.host_buf = nullptr;
-  g_batch.dev_cap = g_batch.host_cap = 0;
+  g_batch.next = 0;
   g_batch.device = -1;
 }
 
@@ -1118,10 +1140,13 @@ bool ranges_disjoint_sorted(std::vector<Range>& rs) {
 namespace {
 
 // Descriptor table of a batch: (ncalls + 1) BatchCall records (the last
-// holds the total tile count), then, 256-byte aligned, ncalls * 2p pointers
-// (per call: p sources, then p destinations).
+// holds the total tile count); then, 256-byte aligned, a 256-byte block
+// whose first 8 bytes are the kernel's run counter (uploaded as zero with
+// the table); then ncalls * 2p pointers (per call: p sources, then p
+// destinations).
 struct BatchLayout {
   size_t rec_bytes = 0;
+  size_t ctr_off = 0;  // the kernel's run counter (64-bit, zero on upload)
   size_t ptr_off = 0;
   size_t total = 0;
   uint64_t tiles = 0;
@@ -1160,7 +1185,8 @@ coll_status_t batch_validate(const coll_call_t* calls, int ncalls, int p, unsign
     if (!ranges_disjoint_sorted(rs)) return COLL_ERR_ALIAS;
   }
   L->rec_bytes = ((size_t)ncalls + 1) * sizeof(coll::BatchCall);
-  L->ptr_off = (L->rec_bytes + 255) & ~size_t(255);
+  L->ctr_off = (L->rec_bytes + 255) & ~size_t(255);
+  L->ptr_off = L->ctr_off + 256;
   L->total = L->ptr_off + (size_t)ncalls * 2 * p * sizeof(void*);
   L->tiles = tiles;
   return COLL_OK;
@@ -1211,6 +1237,7 @@ coll_status_t batch_launch(void* table, const BatchLayout& L, int ncalls, int p,
   coll::BatchArgs a;
   a.calls = (const coll::BatchCall*)table;
   a.ptrs = (const void* const*)((char*)table + L.ptr_off);
+  a.next_run = (unsigned long long*)((char*)table + L.ctr_off);
   a.ncalls = ncalls;
   a.p = p;
   const int g = (int)std::min<uint64_t>(L.tiles, (uint64_t)grid);
@@ -1231,40 +1258,43 @@ COLL_EXPORT coll_status_t coll_allreduce_batch(const coll_call_t* calls, int nca
   std::lock_guard<std::mutex> lock(g_batch.mu);
   if (g_batch.device != -1 && g_batch.device != dev) batch_release();
   g_batch.device = dev;
-  if (g_batch.done) {
-    // the previous batch kernel reads the device buffer and its upload read
-    // the pinned staging buffer: both must be finished before reuse
-    e = (int)hipEventSynchronize(g_batch.done);
+  BatchSlot& b = g_batch.slot[g_batch.next];
+  if (b.done) {
+    // the last kernel that used this slot reads its device buffer, and that
+    // kernel's upload read its pinned staging buffer: both must be finished
+    // before reuse
+    e = (int)hipEventSynchronize(b.done);
     if (e) return hip_fail(e);
   } else {
-    e = (int)hipEventCreateWithFlags(&g_batch.done, hipEventDisableTiming);
+    e = (int)hipEventCreateWithFlags(&b.done, hipEventDisableTiming);
     if (e) return hip_fail(e);
   }
-  if (g_batch.dev_cap < L.total) {
-    const size_t cap = std::max(L.total, g_batch.dev_cap * 2);
-    if (g_batch.dev_buf) hipFree(g_batch.dev_buf);
-    g_batch.dev_buf = nullptr;
-    g_batch.dev_cap = 0;
-    e = (int)hipMalloc(&g_batch.dev_buf, cap);
+  if (b.dev_cap < L.total) {
+    const size_t cap = std::max(L.total, b.dev_cap * 2);
+    if (b.dev_buf) hipFree(b.dev_buf);
+    b.dev_buf = nullptr;
+    b.dev_cap = 0;
+    e = (int)hipMalloc(&b.dev_buf, cap);
     if (e) return hip_fail(e);
-    g_batch.dev_cap = cap;
+    b.dev_cap = cap;
   }
-  if (g_batch.host_cap < L.total) {
-    if (g_batch.host_buf) hipHostFree(g_batch.host_buf);
-    g_batch.host_buf = nullptr;
-    g_batch.host_cap = 0;
-    e = (int)hipHostMalloc(&g_batch.host_buf, g_batch.dev_cap, hipHostMallocDefault);
+  if (b.host_cap < L.total) {
+    if (b.host_buf) hipHostFree(b.host_buf);
+    b.host_buf = nullptr;
+    b.host_cap = 0;
+    e = (int)hipHostMalloc(&b.host_buf, b.dev_cap, hipHostMallocDefault);
     if (e) return hip_fail(e);
-    g_batch.host_cap = g_batch.dev_cap;
+    b.host_cap = b.dev_cap;
   }
-  batch_pack(calls, ncalls, p, L, (char*)g_batch.host_buf);
+  batch_pack(calls, ncalls, p, L, (char*)b.host_buf);
   hipStream_t s = (hipStream_t)stream;
-  e = (int)hipMemcpyAsync(g_batch.dev_buf, g_batch.host_buf, L.total, hipMemcpyHostToDevice, s);
+  e = (int)hipMemcpyAsync(b.dev_buf, b.host_buf, L.total, hipMemcpyHostToDevice, s);
   if (e) return hip_fail(e);
-  st = batch_launch(g_batch.dev_buf, L, ncalls, p, stream);
+  st = batch_launch(b.dev_buf, L, ncalls, p, stream);
   if (st != COLL_OK) return st;
-  e = (int)hipEventRecord(g_batch.done, s);
+  e = (int)hipEventRecord(b.done, s);
   if (e) return hip_fail(e);
+  g_batch.next ^= 1;
   return COLL_OK;
 }
 

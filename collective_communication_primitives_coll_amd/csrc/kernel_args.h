@@ -179,6 +179,7 @@ struct BatchCall {
 struct BatchArgs {
   const BatchCall* calls;   // ncalls + 1 entries; the last holds the total tile count
   const void* const* ptrs;  // per call: p sources then p destinations
+  unsigned long long* next_run;  // zero at launch; waves claim runs of tiles from it
   int ncalls;
   int p;
 };

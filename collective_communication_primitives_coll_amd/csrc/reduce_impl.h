@@ -311,13 +311,18 @@ static int launch_p(const RankPtrs& ptrs, const ReduceGeom& g, int max_grid, hip
       hipLaunchKernelGGL((reduce_kernel<DT, OP, P, ORD, kDstAll>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
     return (int)hipGetLastError();
   }
-  const int grid = clamp_grid(count_tiles<DT, P, false>(g), max_grid);
-  if (!grid) return 0;
-  if (g.dst_mode == kDstOwner)
-    hipLaunchKernelGGL((reduce_kernel<DT, OP, P, ORD, kDstOwner>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
-  else
-    hipLaunchKernelGGL((reduce_kernel<DT, OP, P, ORD, kDstFixed>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
-  return (int)hipGetLastError();
+  if constexpr (ORD != kOrdRing) {
+    // the schedules other than the ring exist for AllReduce only
+    return (int)hipErrorInvalidValue;
+  } else {
+    const int grid = clamp_grid(count_tiles<DT, P, false>(g), max_grid);
+    if (!grid) return 0;
+    if (g.dst_mode == kDstOwner)
+      hipLaunchKernelGGL((reduce_kernel<DT, OP, P, ORD, kDstOwner>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
+    else
+      hipLaunchKernelGGL((reduce_kernel<DT, OP, P, ORD, kDstFixed>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
+    return (int)hipGetLastError();
+  }
 }
 
 template <int DT, int OP>
@@ -358,6 +363,25 @@ static int launch_ring_fixed(int dtype, int op, const RankPtrs& ptrs, const Redu
   COLL_RING_CASE(kBF16, kPreMul)
   COLL_RING_CASE(kI32, kSum) COLL_RING_CASE(kI32, kMin) COLL_RING_CASE(kI32, kMax) COLL_RING_CASE(kI32, kAvg)
 #undef COLL_RING_CASE
+  return (int)hipErrorInvalidValue;
+}
+
+// The binary tree and the double binary tree at compile-time rank count P.
+// Both are defined for any rank count (heap order over P ranks; the second
+// tree of the double binary tree mirrors the first), and only change the
+// bits of floating-point sums: the caller sends integer sums and min/max
+// to the ring-order kernels.
+template <int P>
+static int launch_tree_fixed(int dtype, int op, int order, const RankPtrs& ptrs, const ReduceGeom& g,
+                             int max_grid, hipStream_t s) {
+#define COLL_TREE_CASE(DTV, OPV)                                                        \
+  if (dtype == DTV && op == OPV) {                                                      \
+    if (order == kOrdTree) return launch_p<DTV, OPV, P, kOrdTree>(ptrs, g, max_grid, s); \
+    if (order == kOrdDBT) return launch_p<DTV, OPV, P, kOrdDBT>(ptrs, g, max_grid, s);   \
+  }
+  COLL_TREE_CASE(kF32, kSum) COLL_TREE_CASE(kF32, kAvg) COLL_TREE_CASE(kF32, kPreMul)
+  COLL_TREE_CASE(kBF16, kSum) COLL_TREE_CASE(kBF16, kAvg) COLL_TREE_CASE(kBF16, kPreMul)
+#undef COLL_TREE_CASE
   return (int)hipErrorInvalidValue;
 }
 

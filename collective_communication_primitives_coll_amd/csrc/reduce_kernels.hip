@@ -1,7 +1,8 @@
 // Reduction launch for every rank count: the power-of-two counts (every
 // schedule) here, the other counts up to 16 in ring order in
-// reduce_kernels_p*.hip (compiled separately so the build runs in
-// parallel), and counts above 16 with the general any-p kernel.
+// reduce_kernels_p*.hip and in the tree orders in reduce_trees_p*.hip
+// (compiled separately so the build runs in parallel), and counts above 16
+// with the general any-p kernel.
 #include "reduce_impl.h"
 
 namespace coll {
@@ -13,6 +14,13 @@ int launch_reduce_p9_12(int p, int dtype, int op, const RankPtrs& ptrs, const Re
                         void* stream);
 int launch_reduce_p13_15(int p, int dtype, int op, const RankPtrs& ptrs, const ReduceGeom& g, int max_grid,
                          void* stream);
+// Tree and double-binary-tree orders at the same rank counts.
+int launch_tree_p3_7(int p, int dtype, int op, int order, const RankPtrs& ptrs, const ReduceGeom& g, int max_grid,
+                     void* stream);
+int launch_tree_p9_12(int p, int dtype, int op, int order, const RankPtrs& ptrs, const ReduceGeom& g,
+                      int max_grid, void* stream);
+int launch_tree_p13_15(int p, int dtype, int op, int order, const RankPtrs& ptrs, const ReduceGeom& g,
+                       int max_grid, void* stream);
 
 // Tree orders only change the result of floating-point sums (plain,
 // averaged or pre-multiplied); integer sums and min/max give the same bits
@@ -63,7 +71,18 @@ static int launch_dt(int op, int order, const RankPtrs& ptrs, const ReduceGeom& 
 int launch_reduce(int dtype, int op, int order, const RankPtrs& ptrs, const ReduceGeom& g,
                   int max_grid, void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  if (order == kOrdRing) {
+  const bool float_sum = (dtype == kF32 || dtype == kBF16) && (op == kSum || op == kAvg || op == kPreMul);
+  if (float_sum && (order == kOrdTree || order == kOrdDBT)) {
+    switch (g.p) {
+      case 3: case 5: case 6: case 7:
+        return launch_tree_p3_7(g.p, dtype, op, order, ptrs, g, max_grid, stream);
+      case 9: case 10: case 11: case 12:
+        return launch_tree_p9_12(g.p, dtype, op, order, ptrs, g, max_grid, stream);
+      case 13: case 14: case 15:
+        return launch_tree_p13_15(g.p, dtype, op, order, ptrs, g, max_grid, stream);
+    }
+  }
+  if (order == kOrdRing || !float_sum) {
     switch (g.p) {
       case 3: case 5: case 6: case 7:
         return launch_reduce_p3_7(g.p, dtype, op, ptrs, g, max_grid, stream);

@@ -98,11 +98,12 @@ typedef enum {
  * TREE: the tree all-reduce ([B] Tree AllReduce: reduce up a binary tree
  *   to the root, then broadcast down), the tree in heap order (rank v's
  *   children 2v+1 and 2v+2): each node adds its own value, then its left
- *   subtree, then its right.  p in {2,4,8,16}.
+ *   subtree, then its right.  2 <= p <= 16.
  * DOUBLE_BINARY_TREE: [A] 2.4's two complementary trees, tree A as TREE
- *   and tree B its mirror (node v on rank p-1-v); chunks c < p/2 of q =
- *   ceil(n/p) elements are reduced on tree A, the others on tree B.
- *   p in {2,4,8,16}.
+ *   and tree B its mirror (node v on rank p-1-v); chunks c < p/2 (rounded
+ *   down) of q = ceil(n/p) elements are reduced on tree A, the others on
+ *   tree B.  2 <= p <= 16.
+ * A schedule outside these rank counts returns COLL_ERR_UNSUPPORTED.
  * Integer sums and min/max give the same bits under every schedule. */
 typedef enum {
   COLL_ALGO_RING = 0,
@@ -384,10 +385,11 @@ typedef struct {
  * and summation order of coll_allreduce; calls may mix dtypes and ops.
  * Within a call the coll_allreduce aliasing rules always apply; overlaps
  * between calls are checked only with COLL_BATCH_CHECK_ALIAS (otherwise
- * overlapping calls race).  The library copies the descriptors into a
- * device buffer it owns (grown on demand, released by coll_finalize); a
- * call waits on the host for the previous batch's kernel to finish before
- * reusing that buffer. */
+ * overlapping calls race).  The library copies the descriptors into one
+ * of two device buffers it owns, used in turn (grown on demand, released
+ * by coll_finalize); a call waits on the host only for the batch kernel
+ * two calls earlier, the last one to use the same buffer, so the host
+ * prepares a batch while the one before it runs. */
 coll_status_t coll_allreduce_batch(const coll_call_t* calls, int ncalls, int p,
                                    unsigned flags, void* stream);
 
@@ -399,7 +401,7 @@ coll_status_t coll_allreduce_batch(const coll_call_t* calls, int ncalls, int p,
  * COLL_BATCH_NOALLOC_MAX_BYTES that every GPU the library runs on holds
  * until the process ends; nothing is allocated and nothing waits on the
  * host for earlier batches.  The table takes
- *   ((32 * (ncalls + 1) + 255) / 256) * 256 + 16 * p * ncalls   bytes
+ *   ((32 * (ncalls + 1) + 255) / 256) * 256 + 256 + 16 * p * ncalls   bytes
  * (10,000 calls at p = 16 fit); a larger batch returns
  * COLL_ERR_INVALID_ARG before anything is enqueued.  The table is copied
  * with hipMemcpyAsync on `stream` from a static host buffer (pageable

@@ -94,8 +94,15 @@ def test_invalid_arguments_rejected():
     assert L.coll_reduce_scatter_premul(s, r, 4, n, 2, one, None) == coll.COLL_ERR_UNSUPPORTED
     assert L.coll_allreduce_algo(s, r, 4, n, 0, 0, 7, None) == INV    # bad algo
     assert L.coll_allreduce_algo(s, r, 4, n, 0, 0, 6, None) == INV
-    assert L.coll_allreduce_algo(s, r, 3, n, 0, 0, 4, None) == coll.COLL_ERR_UNSUPPORTED   # tree, p = 3
-    assert L.coll_allreduce_algo(s, r, 3, n, 0, 0, 5, None) == coll.COLL_ERR_UNSUPPORTED   # double tree, p = 3
+    # schedules outside their rank counts (pointer lists of 32 ranks)
+    s32, _ks32 = _arr([base + 0x100000 * i for i in range(32)])
+    r32, _kr32 = _arr([base + 0x10000000 + 0x100000 * i for i in range(32)])
+    one32 = (ctypes.c_float * 32)(*([1.0] * 32))
+    assert L.coll_allreduce_algo(s32, r32, 3, n, 0, 0, 1, None) == coll.COLL_ERR_UNSUPPORTED   # recursive doubling, p = 3
+    assert L.coll_allreduce_algo(s32, r32, 6, n, 0, 0, 3, None) == coll.COLL_ERR_UNSUPPORTED   # halving-doubling, p = 6
+    assert L.coll_allreduce_algo(s32, r32, 17, n, 0, 0, 4, None) == coll.COLL_ERR_UNSUPPORTED  # tree, p = 17
+    assert L.coll_allreduce_algo(s32, r32, 32, n, 0, 0, 5, None) == coll.COLL_ERR_UNSUPPORTED  # double tree, p = 32
+    assert L.coll_allreduce_premul(s32, r32, 5, n, 0, one32, 1, None) == coll.COLL_ERR_UNSUPPORTED  # RD, p = 5
     assert L.coll_alltoall_algo(s, r, 4, n, 1, 2, None) == INV       # bad All-to-All data path
     assert L.coll_alltoall_algo(s, r, 4, n, 1, -1, None) == INV
     assert L.coll_alltoall_algo(s, r, 4, n, 4, 1, None) == INV       # bad dtype

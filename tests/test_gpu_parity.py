@@ -1400,6 +1400,41 @@ def test_allreduce_batch_reuses_descriptors(coll):
             assert_bits_equal(to_host(calls[k][1][1], F32), expect[1], f"round {rounds} call {k}")
 
 
+def test_allreduce_batch_back_to_back(coll):
+    """Batches enqueued without synchronising in between (the descriptor
+    tables alternate between two slots; the third batch reuses the first's
+    slot once that batch is done), each checked afterwards.  Under grids of
+    1, 2 and 4 workgroups per CU and batches from a few tiles to thousands,
+    the runs split between dealt and claimed ones in many proportions (all
+    claimed when there are fewer runs than waves)."""
+    p = 8
+    try:
+        for w in (1, 2, 4):
+            coll.coll_set_grid_limit(w)
+            batches = []
+            for b, (ncalls, nmax) in enumerate(((40, 300_000), (3, 100), (120, 20_000), (9, 1_000_000))):
+                rng = np.random.default_rng(1000 * w + b)
+                calls, host = [], []
+                for k in range(ncalls):
+                    n = int(rng.integers(1, nmax))
+                    dtype = (F32, BF16, I32)[(k + b) % 3]
+                    op = int(rng.integers(0, 3))
+                    hx = gen(p, n, dtype, 3000 + 100 * b + k)
+                    calls.append(([to_dev(x, dtype) for x in hx], [empty(n, dtype, fill=0) for _ in range(p)], n,
+                                  dtype, op))
+                    host.append((hx, op, dtype))
+                coll.coll_allreduce_batch(calls, p)
+                batches.append((calls, host))
+            sync()
+            for b, (calls, host) in enumerate(batches):
+                for k, ((send, recv, n, dtype, op), (hx, _, _)) in enumerate(zip(calls, host)):
+                    expect = native.allreduce(hx, op, dtype)
+                    for r in (0, k % p):
+                        assert_bits_equal(to_host(recv[r], dtype), expect, f"wg/cu={w} batch {b} call {k} rank {r}")
+    finally:
+        coll.coll_set_grid_limit(0)
+
+
 def test_allreduce_batch_alias_check(coll):
     p, n = 2, 100
     a = [empty(n, F32) for _ in range(p)]
@@ -1523,6 +1558,66 @@ def test_premulsum_at_other_rank_counts(coll, p, dtype):
     expect = native.allreduce(hx, native.SUM, dtype, scales=scales)
     for r in (0, p - 1):
         assert_bits_equal(to_host(recv[r], dtype), expect, f"PreMulSum p={p} rank {r}")
+
+
+@pytest.mark.parametrize("p", ANY_P)
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_tree_orders_at_every_rank_count(coll, p, dtype):
+    """The binary tree and the double binary tree (heap order over any p;
+    the second tree mirrored, chunks below p/2 rounded down on the first) at
+    rank counts that are not powers of two: sum and AVG at a size with one
+    tile per workgroup and at one above it, PreMulSum, and integer and
+    min/max calls under a tree schedule, which take ring order; against the
+    oracle's tree folds."""
+    algos = ((coll.COLL_ALGO_TREE, native.ORD_TREE), (coll.COLL_ALGO_DOUBLE_BINARY_TREE, native.ORD_DBT))
+    for n in (p * 4096 * 2 + 3, 1_000_003):
+        hx = gen(p, n, dtype, 700 + p)
+        send = [to_dev(x, dtype) for x in hx]
+        recv = [empty(n, dtype, fill=0) for _ in range(p)]
+        for algo, order in algos:
+            for op in (native.SUM, native.AVG):
+                coll.coll_allreduce_algo(send, recv, algo, op)
+                sync()
+                expect = native.allreduce(hx, op, dtype, order=order)
+                for r in (0, p - 1):
+                    assert_bits_equal(to_host(recv[r], dtype), expect, f"algo={algo} p={p} n={n} op={op} rank {r}")
+        scales = np.random.default_rng(p).random(p, dtype=np.float32) * 2 - 0.5
+        coll.coll_allreduce_premul(send, recv, scales, coll.COLL_ALGO_DOUBLE_BINARY_TREE)
+        sync()
+        expect = native.allreduce(hx, native.SUM, dtype, order=native.ORD_DBT, scales=scales)
+        assert_bits_equal(to_host(recv[p // 2], dtype), expect, f"PreMulSum DBT p={p} n={n}")
+        coll.coll_allreduce_algo(send, recv, coll.COLL_ALGO_TREE, native.MAX)
+        sync()
+        assert_bits_equal(to_host(recv[1], dtype), native.allreduce(hx, native.MAX, dtype), f"max tree p={p}")
+        del send, recv
+    n = 30_011
+    hx = gen(p, n, I32, 750 + p)
+    send = [to_dev(x, I32) for x in hx]
+    recv = [empty(n, I32, fill=0) for _ in range(p)]
+    coll.coll_allreduce_algo(send, recv, coll.COLL_ALGO_DOUBLE_BINARY_TREE, native.SUM)
+    sync()
+    assert_bits_equal(to_host(recv[0], I32), native.allreduce(hx, native.SUM, I32), f"int32 DBT p={p}")
+
+
+@pytest.mark.parametrize("p", [3, 6, 12])
+def test_tree_orders_differ_from_ring(coll, p):
+    """The tree orders at these rank counts are not the ring order in
+    disguise: on the same inputs the three give different bits somewhere,
+    and each matches its own oracle order."""
+    n = 65_537
+    hx = gen(p, n, F32, 800 + p)
+    send = [to_dev(x, F32) for x in hx]
+    recv = [empty(n, F32, fill=0) for _ in range(p)]
+    got = {}
+    for algo, order in ((coll.COLL_ALGO_RING, native.ORD_RING), (coll.COLL_ALGO_TREE, native.ORD_TREE),
+                        (coll.COLL_ALGO_DOUBLE_BINARY_TREE, native.ORD_DBT)):
+        coll.coll_allreduce_algo(send, recv, algo, native.SUM)
+        sync()
+        got[order] = to_host(recv[0], F32)
+        assert_bits_equal(got[order], native.allreduce(hx, native.SUM, F32, order=order), f"order {order} p={p}")
+    v = {k: x.view(np.uint32) for k, x in got.items()}
+    assert (v[native.ORD_RING] != v[native.ORD_TREE]).any()
+    assert (v[native.ORD_TREE] != v[native.ORD_DBT]).any()
 
 
 # ----------------------------------------------------------------------------
