@@ -35,6 +35,7 @@ SOURCES = [
     "fp8_kernels.hip",
     "probe_kernels.hip",
     "batch_noalloc.hip",
+    "claim_slots.hip",
 ]
 
 ARCH = "gfx950"
@@ -63,17 +64,16 @@ def common_flags() -> list[str]:
     ]
 
 
-# Per-source flags.  batch_kernels.hip reads each atomic's result well after
-# issuing it; LLVM's atomic optimizer would rewrite the atomic into a
-# wave-wide one whose result is read, and waited for, at once.
-EXTRA_FLAGS = {
-    "batch_kernels.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
-}
+# Device code flags.  The kernels read the result of a work-claiming atomic
+# well after issuing it; LLVM's atomic optimizer would rewrite the atomic
+# into a wave-wide one whose result is read, and waited for, at once.
+DEVICE_FLAGS = ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *common_flags(), *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+    extra = DEVICE_FLAGS if src.endswith(".hip") else []
+    cmd = [hipcc(), *common_flags(), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -21,8 +21,6 @@
 
 namespace coll {
 
-constexpr int kWave = 64;  // lanes of a wave: the batch's unit of work
-
 // Vectors per lane of a batch tile: 64 / P, at most 8 (4 at p = 16, 278
 // VGPRs, no spills).  A wave tile is small (64 lanes), so its fixed cost
 // (2P 64-bit addresses, the bounds and the loop) is paid per few hundred
@@ -179,22 +177,6 @@ __device__ __forceinline__ BatchCall load_call(const BatchCall* c) {
   b.tiles_per_chunk = ld_const(&c->tiles_per_chunk);
   b.mis = ld_const(&c->mis);
   return b;
-}
-
-// Lane 0's claim of one run from the counter (the other lanes get 0).  Its
-// result is read with wave_value only at the end of the run it was issued
-// before.  (This file is built without LLVM's atomic optimizer, which would
-// read the result right after the atomic and so wait for it at once.)
-__device__ __forceinline__ unsigned long long issue_claim(unsigned long long* next_run, int lane) {
-  unsigned long long r = 0;
-  if (lane == 0) r = atomicAdd(as_global(next_run), 1ull);
-  return r;
-}
-
-__device__ __forceinline__ uint64_t wave_value(unsigned long long v) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return ((uint64_t)hi << 32) | lo;
 }
 
 // Every wave is an independent worker.  The flat tile range is cut into

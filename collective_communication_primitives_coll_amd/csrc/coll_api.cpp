@@ -57,6 +57,37 @@ constexpr int kMaxWgPerCu = 64;
 
 int current_device(int* dev) { return (int)hipGetDevice(dev); }
 
+// Claim slot of a stream on the current device.  Streams get slots in
+// order of first use, one each, so that the launches that share a slot are
+// ordered by their stream and each finds it zeroed by the one before.
+// Null (every tile dealt out in turn) for the per-thread default stream,
+// whose handle names a different stream in every thread, once all slots
+// are taken, or on any error.
+std::mutex g_claim_mu;
+std::vector<std::pair<void*, int>> g_claim_map[64];
+
+unsigned long long* stream_claim_slot(void* stream) {
+  if ((hipStream_t)stream == hipStreamPerThread) return nullptr;
+  int dev = 0;
+  if (current_device(&dev) || dev < 0 || dev >= 64) return nullptr;
+  unsigned long long* base = nullptr;
+  if (coll::claim_slots_base(dev, &base)) return nullptr;
+  std::lock_guard<std::mutex> lock(g_claim_mu);
+  std::vector<std::pair<void*, int>>& m = g_claim_map[dev];
+  int idx = -1;
+  for (const auto& e : m)
+    if (e.first == stream) {
+      idx = e.second;
+      break;
+    }
+  if (idx < 0) {
+    if ((int)m.size() >= coll::kClaimSlots) return nullptr;
+    idx = (int)m.size();
+    m.emplace_back(stream, idx);
+  }
+  return base + (size_t)idx * coll::kClaimSlotWords;
+}
+
 int device_cus(int dev, int* out) {
   if (dev < 0 || dev >= 64) return (int)hipErrorInvalidDevice;
   int c = g_dev[dev].cus.load(std::memory_order_relaxed);
@@ -276,6 +307,7 @@ COLL_EXPORT coll_status_t coll_allreduce_algo(const void* const* send, void* con
   g.src_mis = smis;
   g.dst_mis = dmis;
   g.src_amis = common_amis(send, p);
+  g.claim = stream_claim_slot(stream);
   const int order = order_of(algo);
   return finish(coll::launch_reduce(dtype, op, order, P, g, grid, stream));
 }
@@ -306,6 +338,7 @@ COLL_EXPORT coll_status_t coll_allreduce_premul(const void* const* send, void* c
   g.src_mis = common_mis(send, p);
   g.dst_mis = common_mis((const void* const*)recv, p);
   g.src_amis = common_amis(send, p);
+  g.claim = stream_claim_slot(stream);
   for (int r = 0; r < p; ++r) g.scale[r] = scale[r];
   const int order = order_of(algo);
   return finish(coll::launch_reduce(dtype, coll::kPreMul, order, P, g, grid, stream));
@@ -341,6 +374,7 @@ COLL_EXPORT coll_status_t coll_reduce(const void* const* send, void* recv_root, 
   g.src_mis = common_mis(send, p);
   g.dst_mis = (int)((uintptr_t)recv_root & 15);
   g.src_amis = common_amis(send, p);
+  g.claim = stream_claim_slot(stream);
   return finish(coll::launch_reduce(dtype, op, coll::kOrdRing, P, g, grid, stream));
 }
 
@@ -400,6 +434,7 @@ coll_status_t reduce_scatter_impl(const void* const* send, void* const* recv, in
   g.src_mis = common_mis(send, p);
   g.dst_mis = common_mis((const void* const*)recv, p);
   g.src_amis = common_amis(send, p);
+  g.claim = stream_claim_slot(stream);
   if (scale)
     for (int r = 0; r < p; ++r) g.scale[r] = scale[r];
   return finish(coll::launch_reduce(dtype, op, coll::kOrdRing, P, g, grid, stream));

@@ -276,4 +276,58 @@ __device__ __forceinline__ uint32_t first_tile32(uint64_t base, uint32_t wg, uin
   return t >= grid ? t - grid : t;
 }
 
+// ---------------------------------------------------------------------------
+// Claimed work.  The XCDs do not all stream at the same rate (with tiles
+// dealt out in turn, the workgroups of the odd-numbered XCDs finish a large
+// ReduceScatter or AllReduce 3-5% after the others), so the streaming
+// kernels deal out about seven eighths of their tiles in turn and let the
+// workers (workgroups, or waves in the batch) claim the rest, one at a
+// time, from a counter: a worker that runs ahead claims more.  Each launch
+// gets a counter slot of two words (claims, finished workers), zero at
+// launch; the last worker to finish zeroes both for the next launch that
+// uses the slot.
+// ---------------------------------------------------------------------------
+constexpr int kWave = 64;  // lanes of a wave
+
+// Tiles dealt out in turn when `tiles` tiles are shared by a grid of
+// `grid` workgroups: seven eighths, rounded down to whole rounds of the
+// grid.  The rest are claimed.
+__device__ __forceinline__ uint64_t dealt_tiles(uint64_t tiles, uint64_t grid) {
+  return tiles / 8 * 7 / grid * grid;
+}
+
+// Lane 0's claim of one unit (the other lanes get 0).  Read its result
+// with wave_value only after a wait that covers it: gfx9 counts loads,
+// stores and atomics on one in-order counter, so the wait for the loads
+// of the work issued after the claim also covers the claim, whereas
+// reading the result at the end of that work would also wait for its
+// stores.  (Sources using this are built without LLVM's atomic
+// optimizer, which would read the result right after the atomic.)
+__device__ __forceinline__ unsigned long long issue_claim(unsigned long long* slot, int lane) {
+  unsigned long long r = 0;
+  if (lane == 0) r = atomicAdd(as_global(slot), 1ull);
+  return r;
+}
+
+__device__ __forceinline__ uint64_t wave_value(unsigned long long v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// A worker that has made its last claim: the last of the launch's nworkers
+// workers zeroes the slot.  Every worker has read the result of its last
+// claim before it counts itself finished, so no claim is in flight then.
+__device__ __forceinline__ void claim_finish(unsigned long long* slot, uint64_t nworkers, int lane) {
+  if (lane == 0 && atomicAdd(as_global(slot + 1), 1ull) == nworkers - 1) {
+    atomicExch(as_global(slot), 0ull);
+    atomicExch(as_global(slot + 1), 0ull);
+  }
+}
+
+// A callable that does nothing: the default mid-tile hook.
+struct NoHook {
+  __device__ __forceinline__ void operator()(uint32_t) const {}
+};
+
 }  // namespace coll

@@ -48,6 +48,9 @@ struct ReduceGeom {
   int dst_mis;  // common byte misalignment of the destination bases, or -1
   int src_amis; // common source base address modulo kLineAlign (256), or -1
   float scale[kMaxRanks];  // kPreMul: scale of rank r's operand
+  // Claim slot (two zeroed words) for the claimed tail of reduce_kernel
+  // (AllReduce, ReduceScatter), or null to deal out every tile in turn.
+  unsigned long long* claim;
 };
 
 // Copy kinds.
@@ -209,6 +212,16 @@ uint64_t batch_tile_elems_host(int dtype, int p);
 // once per device.
 constexpr size_t kNoAllocScratchBytes = size_t{4} << 20;
 int noalloc_scratch(int dev, void** out);
+
+// Claim slots (claim_slots.hip): kClaimSlots slots of kClaimSlotWords
+// 64-bit words (two used, the rest keep slots on separate 128-byte lines)
+// in a static device array per GPU.  claim_slots_base gives device dev's
+// array (dev current).  AllReduce and ReduceScatter launches with at
+// least kClaimMinTilesPerWg tiles per workgroup use their slot.
+constexpr int kClaimSlots = 1024;
+constexpr int kClaimSlotWords = 16;
+constexpr uint64_t kClaimMinTilesPerWg = 8;
+int claim_slots_base(int dev, unsigned long long** out);
 
 // MoE: the index pass (one workgroup per rank), the payload pack and the
 // weighted combine.

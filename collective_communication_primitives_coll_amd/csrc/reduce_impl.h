@@ -67,12 +67,144 @@ __device__ __forceinline__ void chunk_operands(const RankPtrs& ptrs, const Reduc
   for (int k = 0; k < P; ++k) sc.s[k] = OP == kPreMul ? g.scale[listed_rank<ORD, P>(c, k)] : 1.0f;
 }
 
+// Geometry of segment c: its range, the vector/element split and its
+// workgroup tile count.
+template <int DT, int P, int DMODE>
+struct SegGeom {
+  uint64_t lo, len, nt;
+  int mis, amis;
+  SegSpan sp;
+  __device__ __forceinline__ SegGeom(const ReduceGeom& g, int c) {
+    constexpr int ND = DMODE == kDstAll ? P : 1;
+    chunk_range(g, c, &lo, &len);
+    const uint64_t doff = (DMODE == kDstOwner) ? 0 : lo;
+    mis = seg_mis(g.src_mis, g.dst_mis, lo * Traits<DT>::B, doff * Traits<DT>::B);
+    amis = seg_amis(g.src_amis, lo * Traits<DT>::B);
+    sp = seg_span_a<Traits<DT>::B>(len, mis, amis);
+    nt = segment_tiles<DT, P, ND>(sp, len);
+  }
+};
+
+// The claimed tiles [dealt, total) of reduce_kernel (AllReduce and
+// ReduceScatter), one workgroup tile per claim.
+// - Thread 0 claims; the value reaches the other threads through LDS at a
+//   barrier (on gfx950 a workgroup barrier waits for LDS operations only,
+//   not for the tile's stores).  It goes to one of two LDS words in turn,
+//   so a fast wave cannot overwrite it before a slow one has read it.
+// - A single counter serves about 83 claims per microsecond (12 ns each,
+//   serialized), so claims are per workgroup and per whole tile: claiming
+//   quarter tiles per wave made a ReduceScatter (p = 8, 2^26 bf16 per
+//   rank) 20% slower.
+// - The next claim is issued before the loads of the tile in hand and read
+//   after they have returned (the tile's hook), and its register is kept
+//   live past the tile's stores, so the loop waits for nothing the dealt
+//   loop does not.
+// - Claims only grow, so the segment cursor only moves forward.
+template <int DT, int OP, int P, int ORD, int DMODE>
+__device__ __forceinline__ void reduce_claimed(const RankPtrs& ptrs, const ReduceGeom& g, uint64_t dealt,
+                                               uint64_t total, unsigned long long first) {
+  using T = Traits<DT>;
+  using S = typename T::S;
+  constexpr bool ALL = DMODE == kDstAll;
+  constexpr int ND = ALL ? P : 1;
+  constexpr int U = ReduceUnroll<P, ALL>::value;
+  constexpr uint64_t TV = (uint64_t)U * kBlock;  // vectors of a tile
+  __shared__ uint64_t next_tile[2];
+  // every wave reads its `first` (only thread 0's is a claim), so that no
+  // path leaves the atomic unread
+  const uint64_t first_tile_claimed = wave_value(first);
+  if (threadIdx.x == 0) next_tile[0] = first_tile_claimed;
+  __syncthreads();
+  const uint64_t units = total - dealt;
+  uint64_t u = next_tile[0];
+  int par = 1;
+  int c = -1;
+  uint64_t cbase = 0, cnt = 0;
+  SegSpan sp{};
+  const S* src[P];
+  S* dst[ND];
+  Scales<P> sc;
+  while (u < units) {
+    // thread 0 claims; every wave reads its own value of `next` in the
+    // hook (only thread 0's is a claim), so that no path leaves the atomic
+    // unread when the register is set again in the next iteration
+    const unsigned long long next = issue_claim(g.claim, (int)threadIdx.x);
+    const uint64_t f = dealt + u;
+    if (f >= cbase + cnt) {
+      // f < total, the sum of the segments' tile counts, so a segment
+      // below P holds it (the bound on c only keeps reads in range)
+      uint64_t lo = 0;
+      do {
+        cbase += cnt;
+        ++c;
+        const SegGeom<DT, P, DMODE> s(g, c);
+        lo = s.lo;
+        sp = s.sp;
+        cnt = s.nt;
+      } while (f >= cbase + cnt && c < P - 1);
+      chunk_operands<DT, OP, P, ORD, DMODE, ND>(ptrs, g, c, lo, src, dst, sc);
+    }
+    const uint64_t t = f - cbase;
+    const auto publish = [&](uint32_t tok) {
+      const uint64_t v = wave_value(next + tok);
+      if (threadIdx.x == 0) next_tile[par] = v;
+    };
+    // only whole vector tiles are worked here (the partial last tile of a
+    // segment is dealt out, and claims are off when a segment is on the
+    // element path), so the loop body has one path with loads, whose wait
+    // for them covers the claim
+    if (t < sp.nvec / TV) {
+      // pointers carried across iterations lose their address space:
+      // restate it so the tile uses global, not flat, instructions
+      const S* gs[P];
+      S* gd[ND];
+#pragma unroll
+      for (int k = 0; k < P; ++k) gs[k] = as_global(src[k] + sp.head);
+#pragma unroll
+      for (int d = 0; d < ND; ++d) gd[d] = as_global(dst[d] + sp.head);
+      reduce_vec_tile<DT, OP, P, ORD, ND, ALL, U, true>(gs, gd, t * TV + threadIdx.x, sp.nvec, sc, P, publish);
+    } else {
+      publish(0);
+    }
+    // keep the claim's register live past the tile's stores: reused for
+    // their addresses, it would have to wait for them before the next
+    // claim could be written into it
+    asm volatile("" ::"v"(next));
+    __syncthreads();
+    u = next_tile[par];
+    par ^= 1;
+  }
+  if (threadIdx.x == 0) claim_finish(g.claim, gridDim.x, 0);
+}
+
 template <int DT, int OP, int P, int ORD, int DMODE>
 COLL_STREAM_KERNEL void reduce_kernel(RankPtrs ptrs, ReduceGeom g) {
   using T = Traits<DT>;
   using S = typename T::S;
   constexpr bool ALL = DMODE == kDstAll;
   constexpr int ND = ALL ? P : 1;
+  // With a claim slot, about seven eighths of the tiles are dealt out in
+  // turn and the rest claimed (reduce_claimed); the workgroup's first claim
+  // is issued now and read after its dealt tiles.
+  uint64_t dealt = ~0ull, total = 0;
+  unsigned long long first = 0;
+  // AllReduce and ReduceScatter.  Same-box A/Bs against tiles all dealt
+  // out: AllReduce 3% faster at p = 8 (256 MiB fp32 per rank) and 1-4% at
+  // p = 3, 5, 6, 7, 12; ReduceScatter 1.5% faster at p = 8 (2^26 bf16 per
+  // rank) and within 1% either way at the other counts.
+  const bool claims = (ALL || DMODE == kDstOwner) && g.claim;
+  if (claims) {
+    first = issue_claim(g.claim, (int)threadIdx.x);
+    // only whole vector tiles are claimed: with a segment on the element
+    // path (buffers that disagree modulo 16) every tile is dealt out
+    bool vec = true;
+    for (int c = 0; c < P; ++c) {
+      const SegGeom<DT, P, DMODE> s(g, c);
+      total += s.nt;
+      vec = vec && (s.sp.vec || s.len == 0);
+    }
+    dealt = vec ? dealt_tiles(total, gridDim.x) : total;
+  }
   uint64_t base = 0;
   for (int c = 0; c < P; ++c) {
     uint64_t lo, len;
@@ -81,8 +213,9 @@ COLL_STREAM_KERNEL void reduce_kernel(RankPtrs ptrs, ReduceGeom g) {
     const uint64_t doff = (DMODE == kDstOwner) ? 0 : lo;
     const int mis = seg_mis(g.src_mis, g.dst_mis, lo * T::B, doff * T::B);
     const int amis = seg_amis(g.src_amis, lo * T::B);
+    const uint64_t lim = dealt > base ? dealt - base : 0;
     uint64_t nt;
-    if (!segment_owned<DT, P, ND>(len, mis, amis, base, &nt)) {
+    if (!segment_owned<DT, P, ND>(len, mis, amis, base, &nt, lim)) {
       base += nt;
       continue;
     }
@@ -90,7 +223,10 @@ COLL_STREAM_KERNEL void reduce_kernel(RankPtrs ptrs, ReduceGeom g) {
     S* dst[ND];
     Scales<P> sc;
     chunk_operands<DT, OP, P, ORD, DMODE, ND>(ptrs, g, c, lo, src, dst, sc);
-    base += reduce_segment<DT, OP, P, ORD, ND, ALL>(src, dst, len, mis, amis, base, sc, P);
+    base += reduce_segment<DT, OP, P, ORD, ND, ALL>(src, dst, len, mis, amis, base, sc, P, lim);
+  }
+  if constexpr (ALL || DMODE == kDstOwner) {
+    if (claims) reduce_claimed<DT, OP, P, ORD, DMODE>(ptrs, g, dealt, total, first);
   }
 }
 
@@ -305,10 +441,15 @@ static int launch_p(const RankPtrs& ptrs, const ReduceGeom& g, int max_grid, hip
       }
     }
   }
+  // claimed tails only for calls with many tiles per workgroup, where the
+  // spread between XCDs outweighs the claims
   if (g.dst_mode == kDstAll) {
-    const int grid = clamp_grid(count_tiles<DT, P, true>(g), max_grid);
+    const uint64_t tiles = count_tiles<DT, P, true>(g);
+    const int grid = clamp_grid(tiles, max_grid);
+    ReduceGeom gk = g;
+    if (tiles < kClaimMinTilesPerWg * (uint64_t)grid) gk.claim = nullptr;
     if (grid)
-      hipLaunchKernelGGL((reduce_kernel<DT, OP, P, ORD, kDstAll>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
+      hipLaunchKernelGGL((reduce_kernel<DT, OP, P, ORD, kDstAll>), dim3(grid), dim3(kBlock), 0, s, ptrs, gk);
     return (int)hipGetLastError();
   }
   if constexpr (ORD != kOrdRing) {
@@ -317,10 +458,13 @@ static int launch_p(const RankPtrs& ptrs, const ReduceGeom& g, int max_grid, hip
   } else {
     const int grid = clamp_grid(count_tiles<DT, P, false>(g), max_grid);
     if (!grid) return 0;
+    ReduceGeom gk = g;
+    if (g.dst_mode != kDstOwner || count_tiles<DT, P, false>(g) < kClaimMinTilesPerWg * (uint64_t)grid)
+      gk.claim = nullptr;  // claimed tails are for AllReduce and ReduceScatter
     if (g.dst_mode == kDstOwner)
-      hipLaunchKernelGGL((reduce_kernel<DT, OP, P, ORD, kDstOwner>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
+      hipLaunchKernelGGL((reduce_kernel<DT, OP, P, ORD, kDstOwner>), dim3(grid), dim3(kBlock), 0, s, ptrs, gk);
     else
-      hipLaunchKernelGGL((reduce_kernel<DT, OP, P, ORD, kDstFixed>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
+      hipLaunchKernelGGL((reduce_kernel<DT, OP, P, ORD, kDstFixed>), dim3(grid), dim3(kBlock), 0, s, ptrs, gk);
     return (int)hipGetLastError();
   }
 }

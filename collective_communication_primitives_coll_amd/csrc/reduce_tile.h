@@ -21,6 +21,8 @@
 // flight.
 #pragma once
 
+#include <type_traits>
+
 #include "device_common.h"
 
 namespace coll {
@@ -158,11 +160,18 @@ __device__ __forceinline__ u32x4 fold_vectors(const u32x4 (&r)[P], const Scales<
 // src[k] and dst[d] point at the segment's first aligned vector;
 // j0 = tile * U * LANES + lane is this lane's first vector index.
 // FULL: every vector of the tile lies inside the segment (nvec unused).
-template <int DT, int OP, int P, int ORD, int ND, bool NTS, int U, bool FULL, int LANES = kBlock>
+// hook(tok) runs after the fold, before the stores: every load of the tile
+// has then returned, and with it everything the wave issued before them.
+// tok is a zero the compiler cannot see through, produced after the fold:
+// adding it to what the hook reads keeps that read after the fold (code
+// motion would otherwise hoist it among the loads, where it would wait
+// for them).
+template <int DT, int OP, int P, int ORD, int ND, bool NTS, int U, bool FULL, int LANES = kBlock,
+          typename Hook = NoHook>
 __device__ __forceinline__ void reduce_vec_tile(const typename Traits<DT>::S* const (&src)[P],
                                                 typename Traits<DT>::S* const (&dst)[ND],
                                                 uint64_t j0, uint64_t nvec, const Scales<P>& sc,
-                                                int avg_p) {
+                                                int avg_p, const Hook& hook = Hook{}) {
   constexpr int V = Traits<DT>::V;
   u32x4 raw[U][P];
 #pragma unroll
@@ -176,6 +185,11 @@ __device__ __forceinline__ void reduce_vec_tile(const typename Traits<DT>::S* co
   u32x4 out[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) out[u] = fold_vectors<DT, OP, P, ORD>(raw[u], sc, avg_p);
+  if constexpr (!std::is_same<Hook, NoHook>::value) {
+    uint32_t tok = 0;
+    asm volatile("" : "+v"(tok) : "v"(out[0]), "v"(out[U - 1]));
+    hook(tok);
+  }
 #pragma unroll
   for (int d = 0; d < ND; ++d)
 #pragma unroll
@@ -256,32 +270,52 @@ __device__ __forceinline__ void reduce_edges(const typename Traits<DT>::S* const
     reduce_elem_at<DT, OP, P, ORD, ND, NTS>(src, dst, i < head ? i : tail_from + (i - head), sc, avg_p);
 }
 
+// Workgroup tiles of a segment (vector tiles of U * kBlock vectors, or
+// element tiles of 4 * kBlock elements when the buffers disagree modulo 16).
+template <int DT, int P, int ND>
+__device__ __forceinline__ uint64_t segment_tiles(const SegSpan& sp, uint64_t len) {
+  constexpr int U = ReduceUnroll<P, (ND > 1)>::value;
+  constexpr uint64_t TV = (uint64_t)U * kBlock;
+  return sp.vec ? ceil_div(sp.nvec, TV) : ceil_div(len, (uint64_t)kBlock * 4);
+}
+
+// Whether this workgroup is the one tile nfull of a vectorized segment
+// (its last tile, when partial) is dealt to although it lies at or beyond
+// lim: partial tiles are never claimed.  Flat indices stay below 2^32.
+template <int P, int ND>
+__device__ __forceinline__ bool owns_partial(const SegSpan& sp, uint64_t base, uint64_t lim) {
+  constexpr uint64_t TV = (uint64_t)ReduceUnroll<P, (ND > 1)>::value * kBlock;
+  const uint64_t nfull = sp.nvec / TV;
+  return sp.vec && nfull * TV < sp.nvec && nfull >= lim && (uint32_t)(base + nfull) % gridDim.x == blockIdx.x;
+}
+
 // Tiles of a segment as reduce_segment counts them, and whether workgroup
 // wg (of grid) works any of them, or the head and tail, when the segment's
-// flat tile indices start at base.  Lets a workgroup skip a segment's
+// flat tile indices start at base and only its first lim tiles (and its
+// partial last tile) are dealt out.  Lets a workgroup skip a segment's
 // pointer setup when it has nothing to do there (small calls, where the
 // setup would dominate).
 template <int DT, int P, int ND>
-__device__ __forceinline__ bool segment_owned(uint64_t len, int mis, int amis, uint64_t base, uint64_t* nt_out) {
-  constexpr int U = ReduceUnroll<P, (ND > 1)>::value;
-  constexpr uint64_t TV = (uint64_t)U * kBlock;
+__device__ __forceinline__ bool segment_owned(uint64_t len, int mis, int amis, uint64_t base, uint64_t* nt_out,
+                                              uint64_t lim = ~0ull) {
   const SegSpan sp = seg_span_a<Traits<DT>::B>(len, mis, amis);
-  const uint64_t nt = sp.vec ? ceil_div(sp.nvec, TV) : ceil_div(len, (uint64_t)kBlock * 4);
+  const uint64_t nt = segment_tiles<DT, P, ND>(sp, len);
   *nt_out = nt;
   const uint64_t ft = first_tile32(base, blockIdx.x, gridDim.x);
-  return ft < nt || (ft == 0 && (sp.head || sp.tail));
+  return ft < (nt < lim ? nt : lim) || (ft == 0 && (sp.head || sp.tail)) || owns_partial<P, ND>(sp, base, lim);
 }
 
-// A whole segment as seen by one workgroup: its share of the vector tiles
-// (flat tile indices congruent to the workgroup id modulo the grid,
-// counting from `base`) and, for the owning workgroup, the head and tail.
-// amis: the sources' address modulo kLineAlign at the segment start, or -1.
-// Returns the segment's tile count (the caller advances base by it).
+// A whole segment as seen by one workgroup: its share of the segment's
+// first lim tiles (flat tile indices congruent to the workgroup id modulo
+// the grid, counting from `base`), the partial last tile if that is its
+// and lies beyond lim, and, for the owning workgroup, the head and tail.
+// amis: the sources' address modulo kLineAlign at the segment start, or
+// -1.  Returns the segment's tile count (the caller advances base by it).
 template <int DT, int OP, int P, int ORD, int ND, bool NTS>
 __device__ __forceinline__ uint64_t reduce_segment(const typename Traits<DT>::S* const (&src)[P],
                                                    typename Traits<DT>::S* const (&dst)[ND],
                                                    uint64_t len, int mis, int amis, uint64_t base,
-                                                   const Scales<P>& sc, int avg_p) {
+                                                   const Scales<P>& sc, int avg_p, uint64_t lim = ~0ull) {
   using S = typename Traits<DT>::S;
   constexpr int V = Traits<DT>::V;
   constexpr int U = ReduceUnroll<P, (ND > 1)>::value;
@@ -292,7 +326,8 @@ __device__ __forceinline__ uint64_t reduce_segment(const typename Traits<DT>::S*
     // element path over tiles of kBlock * 4 elements
     constexpr uint64_t TE = (uint64_t)kBlock * 4;
     const uint64_t nt = ceil_div(len, TE);
-    for (uint64_t t = first_tile(base, wg, grid); t < nt; t += grid) {
+    const uint64_t nd = nt < lim ? nt : lim;
+    for (uint64_t t = first_tile(base, wg, grid); t < nd; t += grid) {
       const uint64_t from = t * TE;
       const uint64_t cnt = (len - from) < TE ? (len - from) : TE;
       reduce_elems<DT, OP, P, ORD, ND, NTS>(src, dst, from, cnt, sc, avg_p);
@@ -308,11 +343,14 @@ __device__ __forceinline__ uint64_t reduce_segment(const typename Traits<DT>::S*
 #pragma unroll
     for (int d = 0; d < ND; ++d) vd[d] = dst[d] + sp.head;
     const uint64_t nfull = sp.nvec / TV;
-    for (uint64_t t = first_tile(base, wg, grid); t < nt; t += grid) {
+    const uint64_t nd = nt < lim ? nt : lim;
+    for (uint64_t t = first_tile(base, wg, grid); t < nd; t += grid) {
       const uint64_t j0 = t * TV + threadIdx.x;
       if (t < nfull) reduce_vec_tile<DT, OP, P, ORD, ND, NTS, U, true>(vs, vd, j0, sp.nvec, sc, avg_p);
       else reduce_vec_tile<DT, OP, P, ORD, ND, NTS, U, false>(vs, vd, j0, sp.nvec, sc, avg_p);
     }
+    if (owns_partial<P, ND>(sp, base, nd))
+      reduce_vec_tile<DT, OP, P, ORD, ND, NTS, U, false>(vs, vd, nfull * TV + threadIdx.x, sp.nvec, sc, avg_p);
   }
   if ((sp.head || sp.tail) && first_tile(base, wg, grid) == 0)
     reduce_edges<DT, OP, P, ORD, ND, NTS>(src, dst, sp.head, sp.head + sp.nvec * V, sp.tail, sc, avg_p,

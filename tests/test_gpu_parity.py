@@ -1621,6 +1621,93 @@ def test_tree_orders_differ_from_ring(coll, p):
 
 
 # ----------------------------------------------------------------------------
+# Claimed tails: AllReduce and ReduceScatter calls with at least 8 tiles
+# per workgroup deal out about seven eighths of their tiles in turn and let
+# the workgroups claim the rest.  Sizes give at least 8 tiles per workgroup
+# for a grid of 256 workgroups (one per CU); the Reduce case checks the
+# same large, ragged shape on the dealt-out path.
+# ----------------------------------------------------------------------------
+
+CLAIM_CASES = [
+    # (what, p, n, dtype, op, algo, send offset, recv offset)
+    ("AR ring", 8, 5_000_003, F32, native.SUM, "RING", 0, 0),
+    ("AR ring max", 8, 5_000_003, F32, native.MAX, "RING", 0, 0),
+    ("AR tree", 8, 5_000_003, F32, native.SUM, "TREE", 0, 0),
+    ("AR double binary tree", 6, 10_000_005, BF16, native.SUM, "DOUBLE_BINARY_TREE", 0, 0),
+    ("AR bf16 p=16", 16, 8_000_001, BF16, native.SUM, "RING", 0, 0),
+    ("AR p=5 int32", 5, 7_000_037, I32, native.SUM, "RING", 0, 0),
+    ("AR recursive doubling", 4, 9_000_005, F32, native.SUM, "RECURSIVE_DOUBLING", 0, 0),
+    ("AR element path", 8, 4_200_001, F32, native.SUM, "RING", 0, 1),
+    ("AR line heads", 8, 9_000_011, BF16, native.AVG, "RING", 3, 3),
+    ("RS", 8, 2_100_001, BF16, native.SUM, None, 0, 0),
+    ("RS p=12", 12, 1_500_007, F32, native.MAX, None, 0, 0),
+    ("Reduce", 8, 9_000_003, F32, native.SUM, "REDUCE", 0, 0),
+]
+
+
+@pytest.mark.parametrize("case", CLAIM_CASES, ids=[c[0] for c in CLAIM_CASES])
+def test_claimed_tails(coll, case):
+    what, p, n, dtype, op, algo, so, ro = case
+    keep = []
+
+    def views(arrays, off):
+        out = []
+        for x in arrays:
+            base, v = upload_offset(x, dtype, off)
+            keep.append(base)
+            out.append(v)
+        return out
+
+    if algo is None:
+        hx = gen(p, p * n, dtype, 1100 + p)
+        send = views(hx, so)
+        shard = views([np.zeros(n, dtype=hx[0].dtype)] * p, ro)
+        coll.coll_reduce_scatter(send, shard, op)
+        sync()
+        expect = native.reduce_scatter(hx, op, dtype)
+        for r in range(p):
+            assert_bits_equal(to_host(shard[r], dtype), expect[r], f"{what} block {r}")
+        return
+    hx = gen(p, n, dtype, 1200 + p)
+    send = views(hx, so)
+    if algo == "REDUCE":
+        out = views([np.zeros(n, dtype=hx[0].dtype)], ro)[0]
+        coll.coll_reduce(send, out, 3, op)
+        sync()
+        assert_bits_equal(to_host(out, dtype), native.allreduce(hx, op, dtype), what)
+        return
+    recv = views([np.zeros(n, dtype=hx[0].dtype)] * p, ro)
+    order = {"RING": native.ORD_RING, "TREE": native.ORD_TREE, "DOUBLE_BINARY_TREE": native.ORD_DBT,
+             "RECURSIVE_DOUBLING": native.ORD_RD}[algo]
+    coll.coll_allreduce_algo(send, recv, getattr(coll, "COLL_ALGO_" + algo), op)
+    sync()
+    expect = native.allreduce(hx, op, dtype, order=order)
+    for r in sorted({0, p // 2, p - 1}):
+        assert_bits_equal(to_host(recv[r], dtype), expect, f"{what} rank {r}")
+
+
+def test_claimed_tails_back_to_back_and_on_two_streams(coll):
+    """Claimed launches back to back on one stream (each finds its stream's
+    counter slot zeroed by the one before) and on two streams at once (one
+    slot each); every result checked after one synchronisation."""
+    import torch
+    p, n = 8, 4_500_007
+    hx = [gen(p, n, F32, 1300 + k) for k in range(4)]
+    send = [[to_dev(x, F32) for x in h] for h in hx]
+    recv = [[empty(n, F32, fill=0) for _ in range(p)] for _ in hx]
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for rep in range(2):
+        for k in range(4):
+            coll.coll_allreduce(send[k], recv[k], native.SUM, stream=s1 if k % 2 == 0 else s2)
+    torch.cuda.synchronize()
+    for k in range(4):
+        expect = native.allreduce(hx[k], native.SUM, F32)
+        for r in (0, p - 1):
+            assert_bits_equal(to_host(recv[k][r], F32), expect, f"call {k} rank {r}")
+
+
+# ----------------------------------------------------------------------------
 # Vector tiles start on 256-byte source lines: long element-wise heads
 # ----------------------------------------------------------------------------
 
