@@ -48,8 +48,10 @@ std::atomic<int> g_wg_per_cu{0};
 // straight into the receive buffers, placement tables staged per
 // workgroup) measured best at two: 221 us against 237 us at sixteen for
 // 4096 x 7168 tokens, p = 8, top-2.
-enum Family { kFamReduce = 0, kFamCopy = 1, kFamRow = 2, kFamFp8 = 3, kFamFp8Direct = 4 };
-constexpr int kDefaultWgPerCu[5] = {1, 2, 8, 16, 2};
+// AllGather and Broadcast calls that walk their segments claim their last
+// tiles dynamically and balance best at one workgroup per CU (kFamFanout).
+enum Family { kFamReduce = 0, kFamCopy = 1, kFamRow = 2, kFamFp8 = 3, kFamFp8Direct = 4, kFamFanout = 5 };
+constexpr int kDefaultWgPerCu[6] = {1, 2, 8, 16, 2, 1};
 // Largest accepted override (coll_set_grid_limit clamps to it).  A CU
 // holds far fewer 256-thread workgroups at once, so larger values would
 // only queue workgroups; the clamp also keeps CUs * limit within int.
@@ -400,8 +402,12 @@ COLL_EXPORT coll_status_t coll_broadcast(const void* send_root, void* const* rec
   const void* src[1] = {send_root};
   coll::RankPtrs P = make_ptrs(src, 1, recv, p);
   coll::CopyGeom g{n, p, coll::kCopyBroadcast, (int)((uintptr_t)send_root & 15),
-                   common_mis((const void* const*)recv, p)};
-  return finish(coll::launch_copy((int)dsize(dtype), P, g, grid, stream));
+                   common_mis((const void* const*)recv, p), nullptr};
+  g.claim = stream_claim_slot(stream);
+  int fgrid;
+  e = max_grid(&fgrid, kFamFanout);
+  if (e) return hip_fail(e);
+  return finish(coll::launch_copy((int)dsize(dtype), P, g, grid, stream, fgrid));
 }
 
 namespace {
@@ -478,8 +484,13 @@ COLL_EXPORT coll_status_t coll_allgather(const void* const* send, void* const* r
   int e = max_grid(&grid, kFamCopy);
   if (e) return hip_fail(e);
   coll::RankPtrs P = make_ptrs(send, p, recv, p);
-  coll::CopyGeom g{n, p, coll::kCopyAllGather, common_mis(send, p), common_mis((const void* const*)recv, p)};
-  return finish(coll::launch_copy((int)dsize(dtype), P, g, grid, stream));
+  coll::CopyGeom g{n, p, coll::kCopyAllGather, common_mis(send, p), common_mis((const void* const*)recv, p),
+                   nullptr};
+  g.claim = stream_claim_slot(stream);
+  int fgrid;
+  e = max_grid(&fgrid, kFamFanout);
+  if (e) return hip_fail(e);
+  return finish(coll::launch_copy((int)dsize(dtype), P, g, grid, stream, fgrid));
 }
 
 COLL_EXPORT coll_status_t coll_alltoall(const void* const* send, void* const* recv, int p, size_t n_block,

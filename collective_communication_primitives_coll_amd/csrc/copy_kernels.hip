@@ -21,20 +21,107 @@
 
 namespace coll {
 
+// Destination misalignment of fan-out segment s.
+template <int B, int KIND>
+__device__ __forceinline__ int fanout_mis(const CopyGeom& g, int s) {
+  const uint64_t dst_off = KIND == kCopyAllGather ? (uint64_t)s * g.n : 0;
+  return g.dst_mis < 0 ? -1 : (int)((g.dst_mis + dst_off * B) & 15);
+}
+
+// The claimed tiles [dealt, total) of fanout_kernel, one workgroup tile per
+// claim, as reduce_claimed does for the reductions (thread 0 claims before
+// the tile's loads and publishes after them through LDS; only whole
+// vector tiles are claimed).
+template <int B, int KIND, int P>
+__device__ __forceinline__ void fanout_claimed(const RankPtrs& ptrs, const CopyGeom& g, uint64_t dealt,
+                                               uint64_t total, unsigned long long first) {
+  using W = typename Word<B>::T;
+  constexpr int NSEG = KIND == kCopyAllGather ? P : 1;
+  __shared__ uint64_t next_tile[2];
+  const uint64_t first_claim = wave_value(first);
+  if (threadIdx.x == 0) next_tile[0] = first_claim;
+  __syncthreads();
+  const uint64_t units = total - dealt;
+  uint64_t u = next_tile[0];
+  int par = 1;
+  int s = -1;
+  uint64_t sbase = 0, cnt = 0;
+  SegSpan sp{};
+  const W* src = nullptr;
+  W* dst[P];
+  while (u < units) {
+    const unsigned long long next = issue_claim(g.claim, (int)threadIdx.x);
+    const uint64_t f = dealt + u;
+    if (f >= sbase + cnt) {
+      do {
+        sbase += cnt;
+        ++s;
+        sp = seg_span<B>(g.n, fanout_mis<B, KIND>(g, s));
+        cnt = copy_segment_tiles<B>(sp, g.n);
+      } while (f >= sbase + cnt && s < NSEG - 1);  // the bound only keeps reads in range
+      const uint64_t dst_off = KIND == kCopyAllGather ? (uint64_t)s * g.n : 0;
+      src = (const W*)ptrs.src[KIND == kCopyAllGather ? s : 0] + sp.head;
+#pragma unroll
+      for (int k = 0; k < P; ++k) dst[k] = (W*)ptrs.dst[k] + dst_off + sp.head;
+    }
+    const uint64_t t = f - sbase;
+    const auto publish = [&](uint32_t tok) {
+      const uint64_t v = wave_value(next + tok);
+      if (threadIdx.x == 0) next_tile[par] = v;
+    };
+    if (t < sp.nvec / kCopyTV) {
+      // pointers carried across iterations lose their address space:
+      // restate it so the tile uses global, not flat, instructions
+      const u32x4* vs = reinterpret_cast<const u32x4*>(as_global(src));
+      u32x4* vd[P];
+#pragma unroll
+      for (int k = 0; k < P; ++k) vd[k] = reinterpret_cast<u32x4*>(as_global(dst[k]));
+      auto gdst = [&](int d) -> u32x4* { return vd[d]; };
+      copy_vec_tile<P == 1, true, P>(vs, gdst, P, t * kCopyTV + threadIdx.x, sp.nvec, publish);
+    } else {
+      publish(0);
+    }
+    asm volatile("" ::"v"(next));  // keep the claim's register out of the stores' reach
+    __syncthreads();
+    u = next_tile[par];
+    par ^= 1;
+  }
+  if (threadIdx.x == 0) claim_finish(g.claim, gridDim.x, 0);
+}
+
 // AllGather / Broadcast with a compile-time rank count P (0: any).
 // Destination pointers of a segment are read once into registers.  With
-// one rank the fan-out is a 1:1 copy and loads non-temporally too.
+// one rank the fan-out is a 1:1 copy and loads non-temporally too.  With a
+// claim slot (compile-time P, sources and destinations agreeing modulo
+// 16), part of the tiles are dealt out in turn and the rest claimed
+// (fanout_claimed): its workgroups otherwise finish far apart (an
+// AllGather at p = 8 with 16 MiB shards: from 80 to 193 us, median 140).
 template <int B, int KIND, int P, bool SHIFT>
 COLL_STREAM_KERNEL void fanout_kernel(RankPtrs ptrs, CopyGeom g) {
   using W = typename Word<B>::T;
+  constexpr bool CLAIMS = P > 0 && !SHIFT;
   const int p = P ? P : g.p;
   const int nseg = KIND == kCopyAllGather ? p : 1;
+  uint64_t dealt = ~0ull, total = 0;
+  unsigned long long first = 0;
+  const bool claims = CLAIMS && g.claim;
+  if (claims) {
+    first = issue_claim(g.claim, (int)threadIdx.x);
+    bool vec = true;
+    for (int s = 0; s < nseg; ++s) {
+      const SegSpan sp = seg_span<B>(g.n, fanout_mis<B, KIND>(g, s));
+      total += copy_segment_tiles<B>(sp, g.n);
+      vec = vec && (sp.vec || g.n == 0);
+    }
+    dealt = vec ? total / 8 * kCopyDealtEighths / gridDim.x * gridDim.x : total;
+  }
   uint64_t base = 0;
   for (int s = 0; s < nseg; ++s) {
     const uint64_t dst_off = KIND == kCopyAllGather ? (uint64_t)s * g.n : 0;
-    const int mis = g.dst_mis < 0 ? -1 : (int)((g.dst_mis + dst_off * B) & 15);
+    const int mis = fanout_mis<B, KIND>(g, s);
+    const uint64_t lim = dealt > base ? dealt - base : 0;
     uint64_t nt;
-    if (!copy_segment_owned<B>(g.n, mis, base, &nt)) {
+    if (!copy_segment_owned<B>(g.n, mis, base, &nt, lim)) {
       base += nt;
       continue;
     }
@@ -44,11 +131,14 @@ COLL_STREAM_KERNEL void fanout_kernel(RankPtrs ptrs, CopyGeom g) {
 #pragma unroll
       for (int k = 0; k < P; ++k) dst[k] = (W*)ptrs.dst[k] + dst_off;
       auto gdst = [&](int d) -> W* { return dst[d]; };
-      base += copy_segment<B, P == 1, P, SHIFT>(src, gdst, P, g.n, mis, base);
+      base += copy_segment<B, P == 1, P, SHIFT>(src, gdst, P, g.n, mis, base, lim);
     } else {
       auto gdst = [&](int d) -> W* { return (W*)ptrs.dst[d] + dst_off; };
       base += copy_segment<B, false, 0, SHIFT>(src, gdst, p, g.n, mis, base);
     }
+  }
+  if constexpr (CLAIMS) {
+    if (claims) fanout_claimed<B, KIND, P>(ptrs, g, dealt, total, first);
   }
 }
 
@@ -429,7 +519,13 @@ static bool uniform_pair_layout(const CopyGeom& g, uint64_t nseg, uint64_t* head
 }
 
 template <int B, bool SHIFT>
-static void launch_walking(const RankPtrs& ptrs, const CopyGeom& g, int grid, hipStream_t s) {
+static void launch_walking(const RankPtrs& ptrs, const CopyGeom& g0, int grid, hipStream_t s) {
+  // claimed tails for fan-outs with many tiles per workgroup
+  CopyGeom g = g0;
+  const uint64_t te = kCopyTV * (16 / B);
+  const uint64_t nseg = g.kind == kCopyAllGather ? (uint64_t)g.p : 1;
+  if (g.kind != kCopyAllGather && g.kind != kCopyBroadcast) g.claim = nullptr;
+  if (nseg * ((g.n + te - 1) / te) < kClaimMinTilesPerWg * (uint64_t)grid) g.claim = nullptr;
   if (g.kind == kCopyAllToAll)
     hipLaunchKernelGGL((pair_copy_kernel<B, kCopyAllToAll, SHIFT>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
   else if (g.kind == kCopyGather)
@@ -443,7 +539,7 @@ static void launch_walking(const RankPtrs& ptrs, const CopyGeom& g, int grid, hi
 }
 
 template <int B>
-static int launch_copy_b(const RankPtrs& ptrs, const CopyGeom& g, int max_grid, hipStream_t s) {
+static int launch_copy_b(const RankPtrs& ptrs, const CopyGeom& g, int max_grid, hipStream_t s, int fanout_grid) {
   const uint64_t nseg = g.kind == kCopyBroadcast ? 1 : (g.kind == kCopyAllToAll ? (uint64_t)g.p * g.p : g.p);
   if (g.kind == kCopyAllGather && (g.p == 2 || g.p == 4 || g.p == 8 || g.p == 16)) {
     uint64_t head, nvec, tail, tps;
@@ -482,18 +578,20 @@ static int launch_copy_b(const RankPtrs& ptrs, const CopyGeom& g, int max_grid, 
     }
   }
   const uint64_t te = kCopyTV * (16 / B);
-  const int grid = clamp_grid(nseg * ((g.n + te - 1) / te + 1), max_grid);
+  const bool fan = g.kind == kCopyAllGather || g.kind == kCopyBroadcast;
+  const int grid = clamp_grid(nseg * ((g.n + te - 1) / te + 1), fan && fanout_grid > 0 ? fanout_grid : max_grid);
   if (!grid) return 0;
   if (copy_needs_shift<B>(g)) launch_walking<B, true>(ptrs, g, grid, s);
   else launch_walking<B, false>(ptrs, g, grid, s);
   return (int)hipGetLastError();
 }
 
-int launch_copy(int elem_bytes, const RankPtrs& ptrs, const CopyGeom& g, int max_grid, void* stream) {
+int launch_copy(int elem_bytes, const RankPtrs& ptrs, const CopyGeom& g, int max_grid, void* stream,
+                int fanout_grid) {
   hipStream_t s = (hipStream_t)stream;
-  if (elem_bytes == 1) return launch_copy_b<1>(ptrs, g, max_grid, s);
-  if (elem_bytes == 2) return launch_copy_b<2>(ptrs, g, max_grid, s);
-  if (elem_bytes == 4) return launch_copy_b<4>(ptrs, g, max_grid, s);
+  if (elem_bytes == 1) return launch_copy_b<1>(ptrs, g, max_grid, s, fanout_grid);
+  if (elem_bytes == 2) return launch_copy_b<2>(ptrs, g, max_grid, s, fanout_grid);
+  if (elem_bytes == 4) return launch_copy_b<4>(ptrs, g, max_grid, s, fanout_grid);
   return (int)hipErrorInvalidValue;
 }
 

@@ -6,6 +6,8 @@
 // non-temporal; the caller picks the load policy.
 #pragma once
 
+#include <type_traits>
+
 #include "device_common.h"
 
 namespace coll {
@@ -30,10 +32,12 @@ constexpr uint64_t kCopyTV = (uint64_t)kCopyU * kBlock;  // vectors per copy til
 
 // Copy tile: U vectors per lane from src (at the segment's first aligned
 // vector) to ND destinations (ND = 0: nd, known only at run time).
-// j0 = tile * kCopyTV + lane.
-template <bool NTL, bool FULL, int ND, typename GD>
+// j0 = tile * kCopyTV + lane.  hook(tok) runs once the loads have returned,
+// before the stores (as in reduce_vec_tile; tok is an opaque zero that
+// keeps what the hook reads after the loads).
+template <bool NTL, bool FULL, int ND, typename GD, typename Hook = NoHook>
 __device__ __forceinline__ void copy_vec_tile(const u32x4* src, const GD& gdst, int nd, uint64_t j0,
-                                              uint64_t nvec) {
+                                              uint64_t nvec, const Hook& hook = Hook{}) {
   u32x4 r[kCopyU];
 #pragma unroll
   for (int u = 0; u < kCopyU; ++u) {
@@ -41,6 +45,11 @@ __device__ __forceinline__ void copy_vec_tile(const u32x4* src, const GD& gdst, 
     if (FULL || j < nvec) r[u] = ld16<NTL>(src + j);
   }
   __builtin_amdgcn_sched_barrier(0);  // all loads of the tile before the first store
+  if constexpr (!std::is_same<Hook, NoHook>::value) {
+    uint32_t tok = 0;
+    asm volatile("" : "+v"(tok) : "v"(r[0]), "v"(r[kCopyU - 1]));
+    hook(tok);
+  }
   const int ndst = ND ? ND : nd;
 #pragma unroll
   for (int d = 0; d < ndst; ++d) {
@@ -156,21 +165,38 @@ __device__ __forceinline__ ShiftSpan shift_span(const void* src, const void* dst
 // workgroup works any of them or the head and tail (see copy_segment);
 // lets a workgroup skip a segment's pointer setup.
 template <int B>
-__device__ __forceinline__ bool copy_segment_owned(uint64_t len, int dmis, uint64_t base, uint64_t* nt_out) {
-  const SegSpan sp = seg_span<B>(len, dmis);
-  const uint64_t nt = sp.vec ? ceil_div(sp.nvec, kCopyTV) : ceil_div(len, (uint64_t)kBlock * 4);
-  *nt_out = nt;
-  const uint64_t ft = first_tile32(base, blockIdx.x, gridDim.x);
-  return ft < nt || (ft == 0 && (sp.head || sp.tail));
+__device__ __forceinline__ uint64_t copy_segment_tiles(const SegSpan& sp, uint64_t len) {
+  return sp.vec ? ceil_div(sp.nvec, kCopyTV) : ceil_div(len, (uint64_t)kBlock * 4);
 }
 
-// Copy one segment of len elements: this workgroup's vector tiles and,
-// if it owns the segment, the element-wise head and tail.  gdst(d) gives
-// destination d's element pointer at the segment start.  Returns the
-// segment's tile count.
+// Whether this workgroup is the one the partial last tile of a vectorized
+// segment is dealt to although it lies at or beyond lim (partial tiles
+// are never claimed).  Flat indices stay below 2^32.
+__device__ __forceinline__ bool copy_owns_partial(const SegSpan& sp, uint64_t base, uint64_t lim) {
+  const uint64_t nfull = sp.nvec / kCopyTV;
+  return sp.vec && nfull * kCopyTV < sp.nvec && nfull >= lim &&
+         (uint32_t)(base + nfull) % gridDim.x == blockIdx.x;
+}
+
+template <int B>
+__device__ __forceinline__ bool copy_segment_owned(uint64_t len, int dmis, uint64_t base, uint64_t* nt_out,
+                                                   uint64_t lim = ~0ull) {
+  const SegSpan sp = seg_span<B>(len, dmis);
+  const uint64_t nt = copy_segment_tiles<B>(sp, len);
+  *nt_out = nt;
+  const uint64_t ft = first_tile32(base, blockIdx.x, gridDim.x);
+  return ft < (nt < lim ? nt : lim) || (ft == 0 && (sp.head || sp.tail)) || copy_owns_partial(sp, base, lim);
+}
+
+// Copy one segment of len elements: this workgroup's share of the first
+// lim vector tiles (and of the partial last tile when that lies beyond
+// lim) and, if it owns the segment, the element-wise head and tail.
+// gdst(d) gives destination d's element pointer at the segment start.
+// Returns the segment's tile count.  lim applies to vector tiles without
+// SHIFT only (the claimed tails copy no other kind).
 template <int B, bool NTL, int ND, bool SHIFT, typename GD>
 __device__ __forceinline__ uint64_t copy_segment(const typename Word<B>::T* src, const GD& gdst, int nd,
-                                                 uint64_t len, int dmis, uint64_t base) {
+                                                 uint64_t len, int dmis, uint64_t base, uint64_t lim = ~0ull) {
   using W = typename Word<B>::T;
   constexpr uint64_t V = 16 / B;
   const uint64_t grid = gridDim.x, wg = blockIdx.x;
@@ -200,11 +226,14 @@ __device__ __forceinline__ uint64_t copy_segment(const typename Word<B>::T* src,
     const uint64_t nfull = sp.nvec / kCopyTV;
     if (m == 0) {
       const u32x4* vs = reinterpret_cast<const u32x4*>(src + sp.head);
-      for (uint64_t t = first_tile(base, wg, grid); t < nt; t += grid) {
+      const uint64_t nd_t = nt < lim ? nt : lim;
+      for (uint64_t t = first_tile(base, wg, grid); t < nd_t; t += grid) {
         const uint64_t j0 = t * kCopyTV + threadIdx.x;
         if (t < nfull) copy_vec_tile<NTL, true, ND>(vs, vd, nd, j0, sp.nvec);
         else copy_vec_tile<NTL, false, ND>(vs, vd, nd, j0, sp.nvec);
       }
+      if (copy_owns_partial(sp, base, nd_t))
+        copy_vec_tile<NTL, false, ND>(vs, vd, nd, nfull * kCopyTV + threadIdx.x, sp.nvec);
     } else if constexpr (SHIFT) {
       const u32x4* vs = reinterpret_cast<const u32x4*>((uintptr_t)(src + sp.head) & ~(uintptr_t)15);
       for (uint64_t t = first_tile(base, wg, grid); t < nt; t += grid) {

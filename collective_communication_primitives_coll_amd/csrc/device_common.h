@@ -277,11 +277,12 @@ __device__ __forceinline__ uint32_t first_tile32(uint64_t base, uint32_t wg, uin
 }
 
 // ---------------------------------------------------------------------------
-// Claimed work.  The XCDs do not all stream at the same rate (with tiles
-// dealt out in turn, the workgroups of the odd-numbered XCDs finish a large
-// ReduceScatter or AllReduce 3-5% after the others), so the streaming
-// kernels deal out about seven eighths of their tiles in turn and let the
-// workers (workgroups, or waves in the batch) claim the rest, one at a
+// Claimed work.  Workgroups do not all stream at the same rate: with tiles
+// dealt out in turn, those of the odd-numbered XCDs finish a large
+// ReduceScatter or AllReduce 3-5% after the others, and an AllGather's
+// workgroups finish anywhere between 40% and 100% of the kernel's time.
+// So the streaming kernels deal out part of their tiles in turn and let
+// the workers (workgroups, or waves in the batch) claim the rest, one at a
 // time, from a counter: a worker that runs ahead claims more.  Each launch
 // gets a counter slot of two words (claims, finished workers), zero at
 // launch; the last worker to finish zeroes both for the next launch that
@@ -289,11 +290,14 @@ __device__ __forceinline__ uint32_t first_tile32(uint64_t base, uint32_t wg, uin
 // ---------------------------------------------------------------------------
 constexpr int kWave = 64;  // lanes of a wave
 
-// Tiles dealt out in turn when `tiles` tiles are shared by a grid of
-// `grid` workgroups: seven eighths, rounded down to whole rounds of the
-// grid.  The rest are claimed.
+// Tiles of a reduction dealt out in turn when `tiles` tiles are shared by
+// a grid of `grid` workgroups: a quarter, rounded down to whole rounds of
+// the grid; the rest are claimed.  Same-box A/B against 7/8 and 4/8 dealt:
+// AllReduce p = 8 (2^26 fp32 per rank) 755, 741, 737 us; at p = 3 and 12
+// 274, 263, 256 us and 1147, 1097, 1076 us; ReduceScatter p = 8 (2^26
+// bf16 per rank) 203, 200, 199 us, other rank counts within 1%.
 __device__ __forceinline__ uint64_t dealt_tiles(uint64_t tiles, uint64_t grid) {
-  return tiles / 8 * 7 / grid * grid;
+  return tiles / 8 * 2 / grid * grid;
 }
 
 // Lane 0's claim of one unit (the other lanes get 0).  Read its result

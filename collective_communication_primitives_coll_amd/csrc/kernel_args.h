@@ -68,6 +68,9 @@ struct CopyGeom {
   int kind;
   int src_mis;
   int dst_mis;
+  // Claim slot for the claimed tail of fanout_kernel (AllGather,
+  // Broadcast), or null to deal out every tile in turn.
+  unsigned long long* claim;
 };
 
 struct A2avArgs {
@@ -192,7 +195,11 @@ struct BatchArgs {
 // number of tiles.  launch_alltoallv and launch_batch take the grid as is.
 int launch_reduce(int dtype, int op, int order, const RankPtrs& ptrs, const ReduceGeom& g,
                   int max_grid, void* stream);
-int launch_copy(int elem_bytes, const RankPtrs& ptrs, const CopyGeom& g, int max_grid, void* stream);
+// fanout_grid (> 0): the grid bound for AllGather and Broadcast calls that
+// walk their segments (the claimed tails balance best at one workgroup
+// per CU); 0: max_grid.
+int launch_copy(int elem_bytes, const RankPtrs& ptrs, const CopyGeom& g, int max_grid, void* stream,
+                int fanout_grid = 0);
 int launch_alltoallv(int elem_bytes, const RankPtrs& ptrs, const A2avArgs& a, int grid, void* stream);
 // All-to-All staged through LDS; only for layouts where every block shares
 // one 16-byte misalignment (can_stage_alltoall).
@@ -216,8 +223,9 @@ int noalloc_scratch(int dev, void** out);
 // Claim slots (claim_slots.hip): kClaimSlots slots of kClaimSlotWords
 // 64-bit words (two used, the rest keep slots on separate 128-byte lines)
 // in a static device array per GPU.  claim_slots_base gives device dev's
-// array (dev current).  AllReduce and ReduceScatter launches with at
-// least kClaimMinTilesPerWg tiles per workgroup use their slot.
+// array (dev current).  AllReduce, ReduceScatter, AllGather and
+// Broadcast launches with at least kClaimMinTilesPerWg tiles per
+// workgroup use their slot.
 constexpr int kClaimSlots = 1024;
 constexpr int kClaimSlotWords = 16;
 constexpr uint64_t kClaimMinTilesPerWg = 8;
@@ -250,5 +258,11 @@ int launch_probe(int ns, int nd, const RankPtrs& ptrs, uint64_t nvec, int unroll
 
 // 16-byte vectors each lane of a copy kernel keeps in flight.
 constexpr uint64_t kCopyUnroll = 4;
+// Eighths of a fan-out's tiles dealt out in turn when it claims the rest.
+// AllGather at p = 8, 16 MiB bf16 shards, same-box A/B: 193-199 us all
+// dealt out (two workgroups per CU); with claims, one workgroup per CU,
+// 7/8 dealt ~190, 4/8 178-180, 2/8 175-176, 0/8 175-176 (at two per CU
+// 2/8 gave 186-187 and 0/8 193-194).
+constexpr uint64_t kCopyDealtEighths = 2;
 
 }  // namespace coll

@@ -183,15 +183,15 @@ COLL_STREAM_KERNEL void reduce_kernel(RankPtrs ptrs, ReduceGeom g) {
   using S = typename T::S;
   constexpr bool ALL = DMODE == kDstAll;
   constexpr int ND = ALL ? P : 1;
-  // With a claim slot, about seven eighths of the tiles are dealt out in
-  // turn and the rest claimed (reduce_claimed); the workgroup's first claim
-  // is issued now and read after its dealt tiles.
+  // With a claim slot, a quarter of the tiles are dealt out in turn and the
+  // rest claimed (reduce_claimed); the workgroup's first claim is issued
+  // now and read after its dealt tiles.
   uint64_t dealt = ~0ull, total = 0;
   unsigned long long first = 0;
   // AllReduce and ReduceScatter.  Same-box A/Bs against tiles all dealt
-  // out: AllReduce 3% faster at p = 8 (256 MiB fp32 per rank) and 1-4% at
-  // p = 3, 5, 6, 7, 12; ReduceScatter 1.5% faster at p = 8 (2^26 bf16 per
-  // rank) and within 1% either way at the other counts.
+  // out: AllReduce 5-7% faster at p = 8 (256 MiB fp32 per rank) and 6-9%
+  // at p = 3, 5, 6, 7, 12; ReduceScatter 3-4% faster at p = 8 (2^26 bf16
+  // per rank) and within 1% either way at the other counts.
   const bool claims = (ALL || DMODE == kDstOwner) && g.claim;
   if (claims) {
     first = issue_claim(g.claim, (int)threadIdx.x);

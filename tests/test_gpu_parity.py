@@ -1622,8 +1622,8 @@ def test_tree_orders_differ_from_ring(coll, p):
 
 # ----------------------------------------------------------------------------
 # Claimed tails: AllReduce and ReduceScatter calls with at least 8 tiles
-# per workgroup deal out about seven eighths of their tiles in turn and let
-# the workgroups claim the rest.  Sizes give at least 8 tiles per workgroup
+# per workgroup deal out a quarter of their tiles in turn and let the
+# workgroups claim the rest.  Sizes give at least 8 tiles per workgroup
 # for a grid of 256 workgroups (one per CU); the Reduce case checks the
 # same large, ragged shape on the dealt-out path.
 # ----------------------------------------------------------------------------
@@ -1684,6 +1684,43 @@ def test_claimed_tails(coll, case):
     expect = native.allreduce(hx, op, dtype, order=order)
     for r in sorted({0, p // 2, p - 1}):
         assert_bits_equal(to_host(recv[r], dtype), expect, f"{what} rank {r}")
+
+
+COPY_CLAIM_CASES = [
+    # (what, p, n, dtype): AllGather shards / Broadcast elements, with at
+    # least 8 tiles per workgroup for 512 workgroups (two per CU)
+    ("AllGather bf16", 8, 4_500_003, BF16),
+    ("AllGather fp32 p=4", 4, 9_000_001, F32),
+    ("AllGather bytes p=16", 16, 4_200_017, 3),
+    ("Broadcast fp32", 4, 17_000_003, F32),
+]
+
+
+@pytest.mark.parametrize("case", COPY_CLAIM_CASES, ids=[c[0] for c in COPY_CLAIM_CASES])
+def test_claimed_tails_fanout(coll, case):
+    """Fan-outs large enough to claim their last tiles: every byte of every
+    receive buffer equals its source (AllGather: rank order; Broadcast: the
+    root's buffer), with ragged sizes."""
+    import torch
+    what, p, n, dtype = case
+    tdt = {F32: torch.float32, BF16: torch.bfloat16, 3: torch.uint8}[dtype]
+    g = torch.Generator(device="cuda").manual_seed(p * 1000 + n % 997)
+    if what.startswith("AllGather"):
+        shards = [torch.randint(0, 255, (n * (4 if dtype == F32 else 2 if dtype == BF16 else 1),), dtype=torch.uint8,
+                                device="cuda", generator=g).view(tdt) for _ in range(p)]
+        full = [torch.zeros(p * n, dtype=tdt, device="cuda") for _ in range(p)]
+        coll.coll_allgather(shards, full)
+        sync()
+        expect = torch.cat(shards).view(torch.uint8)
+        for r in range(p):
+            assert torch.equal(full[r].view(torch.uint8), expect), f"{what} rank {r}"
+    else:
+        src = torch.randint(0, 255, (n * 4,), dtype=torch.uint8, device="cuda", generator=g).view(tdt)
+        outs = [torch.zeros(n, dtype=tdt, device="cuda") for _ in range(p)]
+        coll.coll_broadcast(src, outs, 0)
+        sync()
+        for r in range(p):
+            assert torch.equal(outs[r].view(torch.uint8), src.view(torch.uint8)), f"{what} rank {r}"
 
 
 def test_claimed_tails_back_to_back_and_on_two_streams(coll):
