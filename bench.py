@@ -150,7 +150,9 @@ class Ceilings:
     collectives' 16-byte tiles, launch bounds and grid sizing): ns source and
     nd destination streams of stream_bytes each, best over tiles of 1, 2, 4
     and 8 vectors per lane, the four cache policies (cached or non-temporal
-    loads and stores) and one, two or four workgroups per CU.  Results are cached per (ns, nd, stream_bytes)."""
+    loads and stores), tiles all dealt out in turn or three quarters claimed
+    (as the large collectives balance their workgroups), and one, two or
+    four workgroups per CU.  Results are cached per (ns, nd, stream_bytes)."""
 
     def __init__(self, torch, coll, dev, enabled=True):
         self.torch, self.coll, self.dev, self.enabled = torch, coll, dev, enabled
@@ -176,7 +178,7 @@ class Ceilings:
                 for unroll in (1, 2, 4, 8):
                     if ns * unroll > 32:
                         continue
-                    for flags in (0, 1, 2, 3):
+                    for flags in range(8):  # cached / non-temporal loads and stores, dealt or claimed tiles
                         f = coll.coll_stream_probe(src, dst, stream_bytes, unroll, flags, sink, defer=True)
                         med = stats_us(time_launches(torch, [f], 4, 1)[0])[0]
                         gbps = (ns + nd) * stream_bytes / (med * 1e-6) / 1e9
@@ -187,7 +189,8 @@ class Ceilings:
         del src, dst
         torch.cuda.empty_cache()
         res = {"GBps": round(best[0], 1), "mix": f"{ns}r:{nd}w x {stream_bytes >> 20} MiB",
-               "wg_per_cu": best[1], "unroll": best[3], "nt_loads": bool(best[2] & 1), "nt_stores": bool(best[2] & 2)}
+               "wg_per_cu": best[1], "unroll": best[3], "nt_loads": bool(best[2] & 1), "nt_stores": bool(best[2] & 2),
+               "claimed": bool(best[2] & 4)}
         self.cache[key] = res
         return res
 

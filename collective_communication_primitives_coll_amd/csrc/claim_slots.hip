@@ -1,8 +1,8 @@
 // Counter slots for the claimed tails of the streaming kernels: each slot
-// is two words (claims handed out, waves finished), zero at launch and
-// zeroed again by the last wave of the launch that used it.  A static
-// device array, so that no call allocates; every GPU the library runs on
-// holds its own copy until the process ends.
+// holds a claim counter, zero at launch and zeroed again by the worker that
+// makes the launch's last claim.  A static device array, so that no call
+// allocates; every GPU the library runs on holds its own copy until the
+// process ends.
 #include <hip/hip_runtime.h>
 
 #include <mutex>

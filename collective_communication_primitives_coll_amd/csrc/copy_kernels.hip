@@ -86,20 +86,28 @@ __device__ __forceinline__ void fanout_claimed(const RankPtrs& ptrs, const CopyG
     u = next_tile[par];
     par ^= 1;
   }
-  if (threadIdx.x == 0) claim_finish(g.claim, gridDim.x, 0);
+  if (threadIdx.x == 0) claim_last(g.claim, u, units, gridDim.x);
 }
+
+// Fan-outs claim tiles at compile-time rank counts of 8 and 16 only: a
+// tile then moves (1 + p) * 16 KiB >= 144 KiB, so one claim per tile stays
+// well under what a single counter serves (about 83 claims per
+// microsecond, 12 ns each).  At p = 1 (a 32 KiB tile) claiming every tile
+// capped a 1 GiB copy at about 3 TB/s.
+template <int P>
+constexpr bool kFanoutClaims = P >= 8;
 
 // AllGather / Broadcast with a compile-time rank count P (0: any).
 // Destination pointers of a segment are read once into registers.  With
 // one rank the fan-out is a 1:1 copy and loads non-temporally too.  With a
-// claim slot (compile-time P, sources and destinations agreeing modulo
-// 16), part of the tiles are dealt out in turn and the rest claimed
+// claim slot (P of 8 or 16, sources and destinations agreeing modulo 16),
+// a quarter of the tiles are dealt out in turn and the rest claimed
 // (fanout_claimed): its workgroups otherwise finish far apart (an
 // AllGather at p = 8 with 16 MiB shards: from 80 to 193 us, median 140).
 template <int B, int KIND, int P, bool SHIFT>
 COLL_STREAM_KERNEL void fanout_kernel(RankPtrs ptrs, CopyGeom g) {
   using W = typename Word<B>::T;
-  constexpr bool CLAIMS = P > 0 && !SHIFT;
+  constexpr bool CLAIMS = kFanoutClaims<P> && !SHIFT;
   const int p = P ? P : g.p;
   const int nseg = KIND == kCopyAllGather ? p : 1;
   uint64_t dealt = ~0ull, total = 0;
@@ -582,7 +590,8 @@ static int launch_copy_b(const RankPtrs& ptrs, const CopyGeom& g, int max_grid, 
     }
   }
   const uint64_t te = kCopyTV * (16 / B);
-  const bool fan = g.kind == kCopyAllGather || g.kind == kCopyBroadcast;
+  // fan-outs that may claim tiles take fanout_grid
+  const bool fan = (g.kind == kCopyAllGather || g.kind == kCopyBroadcast) && (g.p == 8 || g.p == 16) && g.claim;
   const int grid = clamp_grid(nseg * ((g.n + te - 1) / te + 1), fan && fanout_grid > 0 ? fanout_grid : max_grid);
   if (!grid) return 0;
   if (copy_needs_shift<B>(g)) launch_walking<B, true>(ptrs, g, grid, s);

@@ -284,9 +284,12 @@ __device__ __forceinline__ uint32_t first_tile32(uint64_t base, uint32_t wg, uin
 // So the streaming kernels deal out part of their tiles in turn and let
 // the workers (workgroups, or waves in the batch) claim the rest, one at a
 // time, from a counter: a worker that runs ahead claims more.  Each launch
-// gets a counter slot of two words (claims, finished workers), zero at
-// launch; the last worker to finish zeroes both for the next launch that
-// uses the slot.
+// gets a counter slot, zero at launch.  Every worker claims until a claim
+// comes back past the last unit, so a launch with `units` claimable units
+// and W workers makes exactly units + W claims; the worker whose claim
+// returns units + W - 1 makes the last one and zeroes the counter for the
+// next launch that uses the slot (claim_last), without waiting for the
+// other workers to finish their tiles.
 // ---------------------------------------------------------------------------
 constexpr int kWave = 64;  // lanes of a wave
 
@@ -319,14 +322,11 @@ __device__ __forceinline__ uint64_t wave_value(unsigned long long v) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// A worker that has made its last claim: the last of the launch's nworkers
-// workers zeroes the slot.  Every worker has read the result of its last
-// claim before it counts itself finished, so no claim is in flight then.
-__device__ __forceinline__ void claim_finish(unsigned long long* slot, uint64_t nworkers, int lane) {
-  if (lane == 0 && atomicAdd(as_global(slot + 1), 1ull) == nworkers - 1) {
-    atomicExch(as_global(slot), 0ull);
-    atomicExch(as_global(slot + 1), 0ull);
-  }
+// A worker whose claim v came back past the last of `units` units: if it
+// was the launch's last claim, zero the counter.
+__device__ __forceinline__ void claim_last(unsigned long long* slot, uint64_t v, uint64_t units,
+                                           uint64_t nworkers) {
+  if (v == units + nworkers - 1) atomicExch(as_global(slot), 0ull);
 }
 
 // A callable that does nothing: the default mid-tile hook.

@@ -48,7 +48,7 @@ struct ReduceGeom {
   int dst_mis;  // common byte misalignment of the destination bases, or -1
   int src_amis; // common source base address modulo kLineAlign (256), or -1
   float scale[kMaxRanks];  // kPreMul: scale of rank r's operand
-  // Claim slot (two zeroed words) for the claimed tail of reduce_kernel
+  // Claim slot (a zeroed counter) for the claimed tail of reduce_kernel
   // (AllReduce, ReduceScatter), or null to deal out every tile in turn.
   unsigned long long* claim;
 };
@@ -195,9 +195,9 @@ struct BatchArgs {
 // number of tiles.  launch_alltoallv and launch_batch take the grid as is.
 int launch_reduce(int dtype, int op, int order, const RankPtrs& ptrs, const ReduceGeom& g,
                   int max_grid, void* stream);
-// fanout_grid (> 0): the grid bound for AllGather and Broadcast calls that
-// walk their segments (the claimed tails balance best at one workgroup
-// per CU); 0: max_grid.
+// fanout_grid (> 0): the grid bound for AllGather and Broadcast calls at
+// p = 8 or 16 that walk their segments (their claimed tails balance best
+// at one workgroup per CU); 0: max_grid.
 int launch_copy(int elem_bytes, const RankPtrs& ptrs, const CopyGeom& g, int max_grid, void* stream,
                 int fanout_grid = 0);
 int launch_alltoallv(int elem_bytes, const RankPtrs& ptrs, const A2avArgs& a, int grid, void* stream);
@@ -221,7 +221,7 @@ constexpr size_t kNoAllocScratchBytes = size_t{4} << 20;
 int noalloc_scratch(int dev, void** out);
 
 // Claim slots (claim_slots.hip): kClaimSlots slots of kClaimSlotWords
-// 64-bit words (two used, the rest keep slots on separate 128-byte lines)
+// 64-bit words (one used, the rest keep slots on separate 128-byte lines)
 // in a static device array per GPU.  claim_slots_base gives device dev's
 // array (dev current).  AllReduce, ReduceScatter, AllGather and
 // Broadcast launches with at least kClaimMinTilesPerWg tiles per
@@ -254,7 +254,7 @@ int launch_moe_combine_direct(int dtype, const MoeRowArgs& a, int max_grid, void
 bool probe_mix_supported(int ns, int nd);
 bool probe_unroll_supported(int ns, int unroll);
 int launch_probe(int ns, int nd, const RankPtrs& ptrs, uint64_t nvec, int unroll, bool nt_loads, bool nt_stores,
-                 void* sink, int max_grid, void* stream);
+                 void* sink, int max_grid, unsigned long long* claim, void* stream);
 
 // 16-byte vectors each lane of a copy kernel keeps in flight.
 constexpr uint64_t kCopyUnroll = 4;

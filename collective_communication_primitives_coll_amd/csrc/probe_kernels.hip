@@ -16,6 +16,8 @@
 // destination the loaded words are folded into one value per lane that
 // is stored to a sink only if it equals a run-time pattern, so the loads
 // cannot be optimised away.
+#include <type_traits>
+
 #include "device_common.h"
 
 namespace coll {
@@ -27,11 +29,13 @@ constexpr bool probe_unroll_ok(int ns, int u) { return (u == 1 || u == 2 || u ==
 
 // One tile: U vectors per lane from every source, folded, then stored to
 // every destination.  FULL: every vector lies inside the streams (no
-// bounds checks, as in the collectives' full tiles).
-template <int NS, int ND, bool NTL, bool NTS, int U, bool FULL>
+// bounds checks, as in the collectives' full tiles).  hook(tok) runs after
+// the loads have returned, before the stores (the claimed tiles' hook, as
+// in the collectives).
+template <int NS, int ND, bool NTL, bool NTS, int U, bool FULL, typename Hook = NoHook>
 __device__ __forceinline__ void probe_tile(const u32x4* const (&src)[NS > 0 ? NS : 1],
                                            u32x4* const (&dst)[ND > 0 ? ND : 1], uint64_t j0, uint64_t nvec,
-                                           u32x4* sink, uint32_t pattern) {
+                                           u32x4* sink, uint32_t pattern, const Hook& hook = Hook{}) {
   constexpr int NSA = NS > 0 ? NS : 1;
   u32x4 v[U][NSA];
 #pragma unroll
@@ -42,6 +46,11 @@ __device__ __forceinline__ void probe_tile(const u32x4* const (&src)[NS > 0 ? NS
       v[u][k] = (FULL || j < nvec) ? ld16<NTL>(src[k] + j) : u32x4{0, 0, 0, 0};
     }
   __builtin_amdgcn_sched_barrier(0);  // every load of the tile before the first store
+  if constexpr (!std::is_same<Hook, NoHook>::value) {
+    uint32_t tok = 0;
+    if constexpr (NS > 0) asm volatile("" : "+v"(tok) : "v"(v[0][0]), "v"(v[U - 1][NS - 1]));
+    hook(tok);
+  }
   u32x4 x[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -71,21 +80,59 @@ __device__ __forceinline__ void probe_tile(const u32x4* const (&src)[NS > 0 ? NS
   }
 }
 
+// claim: null to deal out every tile in turn, else a claim slot: a quarter
+// of the tiles dealt out in turn and the rest claimed one at a time by
+// workgroups, as the reductions and fan-outs do (thread 0 claims before a
+// tile's loads and publishes after them through LDS).
 template <int NS, int ND, bool NTL, bool NTS, int U>
-COLL_STREAM_KERNEL void probe_kernel(RankPtrs ptrs, uint64_t nvec, u32x4* sink, uint32_t pattern) {
+COLL_STREAM_KERNEL void probe_kernel(RankPtrs ptrs, uint64_t nvec, u32x4* sink, uint32_t pattern,
+                                     unsigned long long* claim) {
   constexpr uint64_t TV = (uint64_t)U * kBlock;
   const uint64_t nt = ceil_div(nvec, TV), nfull = nvec / TV;
+  const uint64_t dealt = claim ? dealt_tiles(nfull, gridDim.x) : nt;
+  unsigned long long first = 0;
+  if (claim) first = issue_claim(claim, (int)threadIdx.x);
   const u32x4* src[NS > 0 ? NS : 1];
   u32x4* dst[ND > 0 ? ND : 1];
 #pragma unroll
   for (int k = 0; k < NS; ++k) src[k] = (const u32x4*)ptrs.src[k];
 #pragma unroll
   for (int d = 0; d < ND; ++d) dst[d] = (u32x4*)ptrs.dst[d];
-  for (uint64_t t = blockIdx.x; t < nt; t += gridDim.x) {
+  for (uint64_t t = blockIdx.x; t < dealt; t += gridDim.x) {
     const uint64_t j0 = t * TV + threadIdx.x;
     if (t < nfull) probe_tile<NS, ND, NTL, NTS, U, true>(src, dst, j0, nvec, sink, pattern);
     else probe_tile<NS, ND, NTL, NTS, U, false>(src, dst, j0, nvec, sink, pattern);
   }
+  if (!claim) return;
+  // the partial last tile is dealt out; the whole tiles [dealt, nfull) are claimed
+  if (nfull < nt && nfull % gridDim.x == blockIdx.x)
+    probe_tile<NS, ND, NTL, NTS, U, false>(src, dst, nfull * TV + threadIdx.x, nvec, sink, pattern);
+  __shared__ uint64_t next_tile[2];
+  const uint64_t first_claim = wave_value(first);
+  if (threadIdx.x == 0) next_tile[0] = first_claim;
+  __syncthreads();
+  uint64_t u = next_tile[0];
+  int par = 1;
+  const uint64_t units = nfull - dealt;
+  while (u < units) {
+    const unsigned long long next = issue_claim(claim, (int)threadIdx.x);
+    const auto publish = [&](uint32_t tok) {
+      const uint64_t v = wave_value(next + tok);
+      if (threadIdx.x == 0) next_tile[par] = v;
+    };
+    const u32x4* gs[NS > 0 ? NS : 1];
+    u32x4* gd[ND > 0 ? ND : 1];
+#pragma unroll
+    for (int k = 0; k < NS; ++k) gs[k] = as_global(src[k]);
+#pragma unroll
+    for (int d = 0; d < ND; ++d) gd[d] = as_global(dst[d]);
+    probe_tile<NS, ND, NTL, NTS, U, true>(gs, gd, (dealt + u) * TV + threadIdx.x, nvec, sink, pattern, publish);
+    asm volatile("" ::"v"(next));  // keep the claim's register out of the stores' reach
+    __syncthreads();
+    u = next_tile[par];
+    par ^= 1;
+  }
+  if (threadIdx.x == 0) claim_last(claim, u, units, gridDim.x);
 }
 
 // The (sources, destinations) mixes the benchmark measures.
@@ -103,7 +150,7 @@ bool probe_mix_supported(int ns, int nd) {
 
 template <int NS, int ND, int U>
 static int launch_mix_u(const RankPtrs& ptrs, uint64_t nvec, bool ntl, bool nts, void* sink, int max_grid,
-                        hipStream_t s) {
+                        unsigned long long* claim, hipStream_t s) {
   if constexpr (!probe_unroll_ok(NS, U)) {
     return (int)hipErrorInvalidValue;
   } else {
@@ -114,22 +161,24 @@ static int launch_mix_u(const RankPtrs& ptrs, uint64_t nvec, bool ntl, bool nts,
     u32x4* sk = (u32x4*)sink;
     const uint32_t pat = 0x9e3779b9u;
     const dim3 g(grid), b(kBlock);
-    if (ntl && nts) hipLaunchKernelGGL((probe_kernel<NS, ND, true, true, U>), g, b, 0, s, ptrs, nvec, sk, pat);
-    else if (ntl) hipLaunchKernelGGL((probe_kernel<NS, ND, true, false, U>), g, b, 0, s, ptrs, nvec, sk, pat);
-    else if (nts) hipLaunchKernelGGL((probe_kernel<NS, ND, false, true, U>), g, b, 0, s, ptrs, nvec, sk, pat);
-    else hipLaunchKernelGGL((probe_kernel<NS, ND, false, false, U>), g, b, 0, s, ptrs, nvec, sk, pat);
+    // claims only with enough whole tiles per workgroup
+    unsigned long long* cl = nvec / TV >= kClaimMinTilesPerWg * (uint64_t)grid ? claim : nullptr;
+    if (ntl && nts) hipLaunchKernelGGL((probe_kernel<NS, ND, true, true, U>), g, b, 0, s, ptrs, nvec, sk, pat, cl);
+    else if (ntl) hipLaunchKernelGGL((probe_kernel<NS, ND, true, false, U>), g, b, 0, s, ptrs, nvec, sk, pat, cl);
+    else if (nts) hipLaunchKernelGGL((probe_kernel<NS, ND, false, true, U>), g, b, 0, s, ptrs, nvec, sk, pat, cl);
+    else hipLaunchKernelGGL((probe_kernel<NS, ND, false, false, U>), g, b, 0, s, ptrs, nvec, sk, pat, cl);
     return (int)hipGetLastError();
   }
 }
 
 template <int NS, int ND>
 static int launch_mix(const RankPtrs& ptrs, uint64_t nvec, int unroll, bool ntl, bool nts, void* sink,
-                      int max_grid, hipStream_t s) {
+                      int max_grid, unsigned long long* claim, hipStream_t s) {
   switch (unroll) {
-    case 1: return launch_mix_u<NS, ND, 1>(ptrs, nvec, ntl, nts, sink, max_grid, s);
-    case 2: return launch_mix_u<NS, ND, 2>(ptrs, nvec, ntl, nts, sink, max_grid, s);
-    case 4: return launch_mix_u<NS, ND, 4>(ptrs, nvec, ntl, nts, sink, max_grid, s);
-    case 8: return launch_mix_u<NS, ND, 8>(ptrs, nvec, ntl, nts, sink, max_grid, s);
+    case 1: return launch_mix_u<NS, ND, 1>(ptrs, nvec, ntl, nts, sink, max_grid, claim, s);
+    case 2: return launch_mix_u<NS, ND, 2>(ptrs, nvec, ntl, nts, sink, max_grid, claim, s);
+    case 4: return launch_mix_u<NS, ND, 4>(ptrs, nvec, ntl, nts, sink, max_grid, claim, s);
+    case 8: return launch_mix_u<NS, ND, 8>(ptrs, nvec, ntl, nts, sink, max_grid, claim, s);
   }
   return (int)hipErrorInvalidValue;
 }
@@ -137,10 +186,10 @@ static int launch_mix(const RankPtrs& ptrs, uint64_t nvec, int unroll, bool ntl,
 bool probe_unroll_supported(int ns, int unroll) { return probe_unroll_ok(ns, unroll); }
 
 int launch_probe(int ns, int nd, const RankPtrs& ptrs, uint64_t nvec, int unroll, bool nt_loads, bool nt_stores,
-                 void* sink, int max_grid, void* stream) {
+                 void* sink, int max_grid, unsigned long long* claim, void* stream) {
   hipStream_t s = (hipStream_t)stream;
 #define COLL_PROBE_CASE(A, B) \
-  if (ns == A && nd == B) return launch_mix<A, B>(ptrs, nvec, unroll, nt_loads, nt_stores, sink, max_grid, s);
+  if (ns == A && nd == B) return launch_mix<A, B>(ptrs, nvec, unroll, nt_loads, nt_stores, sink, max_grid, claim, s);
   COLL_PROBE_MIXES(COLL_PROBE_CASE)
 #undef COLL_PROBE_CASE
   return (int)hipErrorInvalidValue;

@@ -174,7 +174,7 @@ __device__ __forceinline__ void reduce_claimed(const RankPtrs& ptrs, const Reduc
     u = next_tile[par];
     par ^= 1;
   }
-  if (threadIdx.x == 0) claim_finish(g.claim, gridDim.x, 0);
+  if (threadIdx.x == 0) claim_last(g.claim, u, units, gridDim.x);
 }
 
 template <int DT, int OP, int P, int ORD, int DMODE>

@@ -429,7 +429,11 @@ coll_status_t coll_allreduce_batch_noalloc(const coll_call_t* calls, int ncalls,
  * one value per lane that is written to `sink` (16 device bytes, 16-byte
  * aligned) only if it equals an internal pattern, so the reads stay.
  * flags: COLL_PROBE_NT_LOADS / COLL_PROBE_NT_STORES select non-temporal
- * loads / stores (else cached).  Supported (nsrc, ndst): (1|4|8|16, 0),
+ * loads / stores (else cached); COLL_PROBE_CLAIM deals out a quarter of
+ * the tiles in turn and lets workgroups claim the rest one at a time, as
+ * the large AllReduce, ReduceScatter, AllGather and Broadcast calls do
+ * (with at least 8 whole tiles per workgroup; else every tile is dealt
+ * out).  Supported (nsrc, ndst): (1|4|8|16, 0),
  * (0, 1|4|8|16), (1|2|3|4|5|6|7|8|12|16, 1), (1, 2|4|8|16) and (k, k) for
  * k in 3, 4, 5, 6, 7, 8, 12, 16; other pairs and tile sizes return
  * COLL_ERR_UNSUPPORTED.  Every pointer
@@ -437,6 +441,7 @@ coll_status_t coll_allreduce_batch_noalloc(const coll_call_t* calls, int ncalls,
  * destinations may not overlap each other or a source (COLL_ERR_ALIAS). */
 #define COLL_PROBE_NT_LOADS 1u
 #define COLL_PROBE_NT_STORES 2u
+#define COLL_PROBE_CLAIM 4u
 coll_status_t coll_stream_probe(const void* const* src, int nsrc, void* const* dst, int ndst, size_t bytes,
                                 int unroll, unsigned flags, void* sink, void* stream);
 

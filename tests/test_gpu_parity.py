@@ -1475,16 +1475,21 @@ def test_alias_rejections(coll):
 # ----------------------------------------------------------------------------
 
 @pytest.mark.parametrize("ns,nd", [(1, 1), (3, 1), (8, 8), (1, 4), (0, 4), (8, 0)])
-def test_stream_probe_writes_the_xor_of_its_sources(coll, ns, nd):
+@pytest.mark.parametrize("big", [False, True])
+def test_stream_probe_writes_the_xor_of_its_sources(coll, ns, nd, big):
+    """Several tiles and a ragged last tile; big: 16 whole tiles per
+    workgroup and more at one vector per lane, where COLL_PROBE_CLAIM
+    (flag 4) claims three quarters of them."""
     import torch
-    nbytes = 3 * 4096 * 16 + 48          # several tiles and a ragged last tile
+    nbytes = (4096 * 4096 if big else 3 * 4096 * 16) + 48
     words = nbytes // 4
     rng = np.random.default_rng(ns * 10 + nd)
     hs = [rng.integers(0, 2**32, words, dtype=np.uint64).astype(np.uint32) for _ in range(ns)]
     src = [torch.from_numpy(h.view(np.int32)).cuda() for h in hs]
     dst = [torch.full((words + 4,), 7, dtype=torch.int32, device="cuda") for _ in range(nd)]
     sink = torch.full((4,), 5, dtype=torch.int32, device="cuda")
-    for flags, unroll in ((0, 1), (3, 2), (1, 4), (2, 8)):
+    cases = ((4, 1), (7, 2)) if big else ((0, 1), (3, 2), (1, 4), (2, 8), (4, 1))
+    for flags, unroll in cases:
         if ns * unroll > 32:
             continue
         for d in dst:
@@ -1688,11 +1693,13 @@ def test_claimed_tails(coll, case):
 
 COPY_CLAIM_CASES = [
     # (what, p, n, dtype): AllGather shards / Broadcast elements, with at
-    # least 8 tiles per workgroup for 512 workgroups (two per CU)
+    # least 8 tiles per workgroup for 256 workgroups (one per CU); p = 8 and
+    # 16 claim tiles, p = 4 deals every tile out
     ("AllGather bf16", 8, 4_500_003, BF16),
     ("AllGather fp32 p=4", 4, 9_000_001, F32),
     ("AllGather bytes p=16", 16, 4_200_017, 3),
-    ("Broadcast fp32", 4, 17_000_003, F32),
+    ("Broadcast fp32", 8, 17_000_003, F32),
+    ("Broadcast bf16 p=16", 16, 20_000_001, BF16),
 ]
 
 
@@ -1704,10 +1711,11 @@ def test_claimed_tails_fanout(coll, case):
     import torch
     what, p, n, dtype = case
     tdt = {F32: torch.float32, BF16: torch.bfloat16, 3: torch.uint8}[dtype]
+    esz = {F32: 4, BF16: 2, 3: 1}[dtype]
     g = torch.Generator(device="cuda").manual_seed(p * 1000 + n % 997)
     if what.startswith("AllGather"):
-        shards = [torch.randint(0, 255, (n * (4 if dtype == F32 else 2 if dtype == BF16 else 1),), dtype=torch.uint8,
-                                device="cuda", generator=g).view(tdt) for _ in range(p)]
+        shards = [torch.randint(0, 255, (n * esz,), dtype=torch.uint8, device="cuda", generator=g).view(tdt)
+                  for _ in range(p)]
         full = [torch.zeros(p * n, dtype=tdt, device="cuda") for _ in range(p)]
         coll.coll_allgather(shards, full)
         sync()
@@ -1715,7 +1723,7 @@ def test_claimed_tails_fanout(coll, case):
         for r in range(p):
             assert torch.equal(full[r].view(torch.uint8), expect), f"{what} rank {r}"
     else:
-        src = torch.randint(0, 255, (n * 4,), dtype=torch.uint8, device="cuda", generator=g).view(tdt)
+        src = torch.randint(0, 255, (n * esz,), dtype=torch.uint8, device="cuda", generator=g).view(tdt)
         outs = [torch.zeros(n, dtype=tdt, device="cuda") for _ in range(p)]
         coll.coll_broadcast(src, outs, 0)
         sync()
