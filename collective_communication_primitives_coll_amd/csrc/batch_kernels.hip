@@ -180,22 +180,23 @@ __device__ __forceinline__ BatchCall load_call(const BatchCall* c) {
 }
 
 // Every wave is an independent worker.  The flat tile range is cut into
-// runs of kBatchRun tiles.  The first runs, about seven eighths of them,
-// are dealt out in turn (wave w takes runs w, w + W, ... for W waves in the
-// grid), so the waves work on one window of the range and move through it
-// front to back together.  The XCDs do not all stream at the same rate:
-// dealt out to the end, the 10,000-call p = 16 plan's waves finished over a
-// spread of 1.2 ms, those of the odd-numbered XCDs last.  So the remaining
-// runs are claimed one at a time from a counter in the descriptor table
-// (zero at launch), and a wave that runs ahead claims more of them.  A
-// claim is issued before the run in hand and read at its end: gfx9 counts
-// loads, stores and atomics on one in-order counter, so reading it waits
-// for that run's stores, which is why claims are kept to the tail.  A wave
-// finds a run's first call by binary search (from its previous run's call
-// onward, as its runs only grow) and walks forward call by call.  Short
-// runs keep the window narrow: with 4-vector tiles the plan took 13.2 ms
-// with runs of 32 tiles, 13.0 with 8 and 12.9 with 2 (1: 13.1, a search
-// per tile).
+// runs of kBatchRun tiles.  The first quarter of the runs are dealt out in
+// turn (wave w takes runs w, w + W, ... for W waves in the grid), so the
+// waves work on one window of the range and move through it front to back
+// together.  Waves do not all stream at the same rate (dealt out to the
+// end, the 10,000-call p = 16 plan's waves finished over a spread of 1.2
+// ms, those of the odd-numbered XCDs last), so the remaining runs are
+// claimed one at a time from a counter in the descriptor table (zero at
+// launch), and a wave that runs ahead claims more of them; claims come in
+// increasing order, so the window stays narrow.  Same-box A/B of the plan:
+// 11.86 ms with 7/8 of the runs dealt out, 11.72 with 5/8, 11.53 with 2/8.
+// A claim is issued before the run in hand and read at its end (gfx9
+// counts loads, stores and atomics on one in-order counter, so that read
+// also waits for the run's stores).  A wave finds a run's first call by
+// binary search (from its previous run's call onward, as its runs only
+// grow) and walks forward call by call.  Short runs keep the window
+// narrow: with 4-vector tiles the plan took 13.2 ms with runs of 32 tiles,
+// 13.0 with 8 and 12.9 with 2 (1: 13.1, a search per tile; all dealt out).
 constexpr uint64_t kBatchRun = 2;
 
 template <int P>
@@ -207,7 +208,7 @@ COLL_STREAM_KERNEL void batch_kernel(BatchArgs a) {
       (uint64_t)blockIdx.x * (kBlock / kWave) + (uint64_t)__builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const uint64_t total = ld_const(&a.calls[a.ncalls].first_tile);
   const uint64_t nruns = (total + kBatchRun - 1) / kBatchRun;
-  const uint64_t nfixed = nruns / 8 * 7 / waves * waves;  // runs dealt out in turn
+  const uint64_t nfixed = nruns / 8 * 2 / waves * waves;  // runs dealt out in turn
   int from_call = 0;
   uint64_t run = wid < nfixed ? wid : nfixed + wave_value(issue_claim(a.next_run, lane));
   // every claim returns a distinct, larger value, so each wave leaves the
