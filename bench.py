@@ -144,13 +144,21 @@ def stats_us(ms_list):
     return float(np.median(a)), float(np.percentile(a, 95)), float(a.mean())
 
 
+# Probe options swept for each mix: cached or non-temporal loads (1); plain,
+# non-temporal (2), device-scope (8) or non-temporal device-scope (2 | 8)
+# stores; tiles dealt out or claimed (4).
+PROBE_FLAGS = list(range(16))
+
+
 class Ceilings:
     """Attainable HBM GB/s of a read:write stream mix, measured in this run
     with the library's direction-mix probe (coll_stream_probe: the
     collectives' 16-byte tiles, launch bounds and grid sizing): ns source and
     nd destination streams of stream_bytes each, best over tiles of 1, 2, 4
-    and 8 vectors per lane, the four cache policies (cached or non-temporal
-    loads and stores), tiles all dealt out in turn or three quarters claimed
+    and 8 vectors per lane, the cache policies (cached or non-temporal
+    loads; plain, non-temporal, device-scope or non-temporal device-scope
+    stores), tiles all dealt out
+    in turn or three quarters claimed
     (as the large collectives balance their workgroups), and one, two or
     four workgroups per CU.  Results are cached per (ns, nd, stream_bytes)."""
 
@@ -178,7 +186,7 @@ class Ceilings:
                 for unroll in (1, 2, 4, 8):
                     if ns * unroll > 32:
                         continue
-                    for flags in range(8):  # cached / non-temporal loads and stores, dealt or claimed tiles
+                    for flags in PROBE_FLAGS:
                         f = coll.coll_stream_probe(src, dst, stream_bytes, unroll, flags, sink, defer=True)
                         med = stats_us(time_launches(torch, [f], 4, 1)[0])[0]
                         gbps = (ns + nd) * stream_bytes / (med * 1e-6) / 1e9
@@ -189,7 +197,8 @@ class Ceilings:
         del src, dst
         torch.cuda.empty_cache()
         res = {"GBps": round(best[0], 1), "mix": f"{ns}r:{nd}w x {stream_bytes >> 20} MiB",
-               "wg_per_cu": best[1], "unroll": best[3], "nt_loads": bool(best[2] & 1), "nt_stores": bool(best[2] & 2),
+               "wg_per_cu": best[1], "unroll": best[3], "nt_loads": bool(best[2] & 1),
+               "stores": {0: "plain", 2: "non-temporal", 8: "device scope", 10: "non-temporal device scope"}[best[2] & 10],
                "claimed": bool(best[2] & 4)}
         self.cache[key] = res
         return res

@@ -28,7 +28,7 @@ COLL_BATCH_NOALLOC_MAX_BYTES = 4 << 20
 
 COLL_U8 = 3
 COLL_A2A_DIRECT, COLL_A2A_LDS_STAGED = 0, 1
-COLL_PROBE_NT_LOADS, COLL_PROBE_NT_STORES, COLL_PROBE_CLAIM = 1, 2, 4
+COLL_PROBE_NT_LOADS, COLL_PROBE_NT_STORES, COLL_PROBE_CLAIM, COLL_PROBE_DEVICE_STORES = 1, 2, 4, 8
 ELEM_BYTES = {COLL_F32: 4, COLL_BF16: 2, COLL_I32: 4, COLL_U8: 1}
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcoll.so")

@@ -1382,7 +1382,8 @@ COLL_EXPORT coll_status_t coll_allreduce_batch_noalloc(const coll_call_t* calls,
 COLL_EXPORT coll_status_t coll_stream_probe(const void* const* src, int nsrc, void* const* dst, int ndst,
                                             size_t bytes, int unroll, unsigned flags, void* sink, void* stream) {
   if (nsrc < 0 || ndst < 0 || nsrc > kMaxRanks || ndst > kMaxRanks || nsrc + ndst == 0) return COLL_ERR_INVALID_ARG;
-  if (flags & ~(unsigned)(COLL_PROBE_NT_LOADS | COLL_PROBE_NT_STORES | COLL_PROBE_CLAIM)) return COLL_ERR_INVALID_ARG;
+  if (flags & ~(unsigned)(COLL_PROBE_NT_LOADS | COLL_PROBE_NT_STORES | COLL_PROBE_CLAIM | COLL_PROBE_DEVICE_STORES))
+    return COLL_ERR_INVALID_ARG;
   if (bytes % 16 || unroll < 1) return COLL_ERR_INVALID_ARG;
   if (!coll::probe_mix_supported(nsrc, ndst) || !coll::probe_unroll_supported(nsrc, unroll))
     return COLL_ERR_UNSUPPORTED;
@@ -1403,8 +1404,10 @@ COLL_EXPORT coll_status_t coll_stream_probe(const void* const* src, int nsrc, vo
   if (e) return hip_fail(e);
   coll::RankPtrs P = make_ptrs(src, nsrc, dst, ndst);
   unsigned long long* claim = (flags & COLL_PROBE_CLAIM) ? stream_claim_slot(stream) : nullptr;
-  return finish(coll::launch_probe(nsrc, ndst, P, bytes / 16, unroll, flags & COLL_PROBE_NT_LOADS,
-                                   flags & COLL_PROBE_NT_STORES, sink, grid, claim, stream));
+  const bool nts = flags & COLL_PROBE_NT_STORES, dev = flags & COLL_PROBE_DEVICE_STORES;
+  const int sp = nts && dev ? coll::kStNTDevice : nts ? coll::kStNT : dev ? coll::kStDevice : coll::kStPlain;
+  return finish(coll::launch_probe(nsrc, ndst, P, bytes / 16, unroll, flags & COLL_PROBE_NT_LOADS, sp, sink, grid,
+                                   claim, stream));
 }
 
 // ---------------------------------------------------------------------------

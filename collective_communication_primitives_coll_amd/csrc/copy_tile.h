@@ -31,7 +31,8 @@ constexpr int kCopyU = (int)kCopyUnroll;
 constexpr uint64_t kCopyTV = (uint64_t)kCopyU * kBlock;  // vectors per copy tile
 
 // Copy tile: U vectors per lane from src (at the segment's first aligned
-// vector) to ND destinations (ND = 0: nd, known only at run time).
+// vector) to ND destinations (ND = 0: nd, known only at run time), with
+// non-temporal stores, of device scope for the fan-outs (ND != 1).
 // j0 = tile * kCopyTV + lane.  hook(tok) runs once the loads have returned,
 // before the stores (as in reduce_vec_tile; tok is an opaque zero that
 // keeps what the hook reads after the loads).
@@ -54,10 +55,15 @@ __device__ __forceinline__ void copy_vec_tile(const u32x4* src, const GD& gdst, 
 #pragma unroll
   for (int d = 0; d < ndst; ++d) {
     u32x4* dv = gdst(d);
+    if constexpr (ND != 1) {
+      // fan-outs: non-temporal stores of device scope
+      store_tile<kStNTDevice, kCopyU, kBlock, FULL>(dv, j0, nvec, r);
+    } else {
 #pragma unroll
-    for (int u = 0; u < kCopyU; ++u) {
-      const uint64_t j = j0 + (uint64_t)u * kBlock;
-      if (FULL || j < nvec) st16<true>(dv + j, r[u]);
+      for (int u = 0; u < kCopyU; ++u) {
+        const uint64_t j = j0 + (uint64_t)u * kBlock;
+        if (FULL || j < nvec) st16<true>(dv + j, r[u]);
+      }
     }
   }
 }

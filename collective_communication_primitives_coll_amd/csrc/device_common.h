@@ -322,6 +322,69 @@ __device__ __forceinline__ uint64_t wave_value(unsigned long long v) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// ---------------------------------------------------------------------------
+// Store policy of a tile's 16-byte vectors (kStPlain, kStNT, kStDevice in
+// kernel_args.h).  A CDNA3/CDNA4 store carries a
+// coherence scope (its sc0 and sc1 bits) and a non-temporal hint (nt):
+//   kStPlain   plain store: the line stays dirty in the XCD's L2 and is
+//              written back when evicted;
+//   kStNT      non-temporal: streams past the caches;
+//   kStDevice  device scope (sc1): written through the L2 at once, into the
+//              memory-side Infinity Cache;
+//   kStNTDevice  both (nt and sc1).
+// Measured on MI355X with a ReduceScatter (p = 8, 2^26 bf16 per rank)
+// followed by the AllGather of its shards: plain 199-203 us, then 175 us;
+// non-temporal 187-191 us, but the AllGather took 210-211 us because its
+// 128 MiB of shards no longer came from the Infinity Cache; device scope
+// 187-190 us and 174-175 us.  The same store of device scope made an
+// AllReduce (p = 8, 256 MiB fp32 per rank) slower than non-temporal stores
+// (756 against 737 us).  AllGather's fan-out (1 GiB written) took 172-173 us
+// with non-temporal stores of device scope against 174-175 us with
+// non-temporal ones.  Each kernel takes the policy it measured best.
+// ---------------------------------------------------------------------------
+
+// HIP's global stores cannot carry sc1, so device-scope stores go through a
+// buffer resource over one wave-uniform range [base, base + bytes):
+// offsets are bytes from base, and a store past the range is dropped by the
+// hardware's range check.  Word 3 of a gfx9 buffer descriptor: 32-bit data
+// format, no swizzle or index stride (a raw byte range).
+constexpr int kBufferWord3 = 0x00020000;
+// the builtin's cache-policy operand: bit 1 nt, bit 4 sc1
+constexpr int kCachePolicySc1 = 16, kCachePolicyNtSc1 = 18;
+
+template <int CPOL>
+struct DeviceScopeStores {
+  __amdgpu_buffer_rsrc_t rsrc;
+  __device__ __forceinline__ DeviceScopeStores(uint64_t base, uint32_t bytes)
+      : rsrc(__builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(wave_value(base)), 0, (int)bytes,
+                                               kBufferWord3)) {}
+  __device__ __forceinline__ void put(uint32_t off, u32x4 v) const {
+    __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, (int)off, 0, CPOL);
+  }
+};
+
+// The stores of one tile: vector u of this lane goes to dst[j0 + u * LANES],
+// where j0 = tile start + lane and lane = threadIdx.x % LANES (so j0 - lane
+// is the same on every lane of the tile).  FULL: every vector lies below
+// nvec (else those at or past nvec are skipped).
+template <int SP, int U, int LANES, bool FULL>
+__device__ __forceinline__ void store_tile(u32x4* dst, uint64_t j0, uint64_t nvec, const u32x4 (&v)[U]) {
+  if constexpr (SP == kStDevice || SP == kStNTDevice) {
+    const uint32_t lane = threadIdx.x % LANES;
+    const DeviceScopeStores<SP == kStDevice ? kCachePolicySc1 : kCachePolicyNtSc1> st(
+        (uint64_t)(dst + (j0 - lane)), (uint32_t)U * LANES * 16);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (FULL || j0 + (uint64_t)u * LANES < nvec) st.put(((uint32_t)u * LANES + lane) * 16, v[u]);
+  } else {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint64_t j = j0 + (uint64_t)u * LANES;
+      if (FULL || j < nvec) st16<SP == kStNT>(dst + j, v[u]);
+    }
+  }
+}
+
 // A worker whose claim v came back past the last of `units` units: if it
 // was the launch's last claim, zero the counter.
 __device__ __forceinline__ void claim_last(unsigned long long* slot, uint64_t v, uint64_t units,

@@ -253,7 +253,12 @@ int launch_moe_combine_direct(int dtype, const MoeRowArgs& a, int max_grid, void
 // (probe_mix_supported and probe_unroll_supported list what is built).
 bool probe_mix_supported(int ns, int nd);
 bool probe_unroll_supported(int ns, int unroll);
-int launch_probe(int ns, int nd, const RankPtrs& ptrs, uint64_t nvec, int unroll, bool nt_loads, bool nt_stores,
+// Store policies of 16-byte vector stores: plain, non-temporal, device
+// scope, non-temporal of device scope (device_common.h describes each).
+constexpr int kStPlain = 0, kStNT = 1, kStDevice = 2, kStNTDevice = 3;
+
+// store_policy: one of the kSt* policies.
+int launch_probe(int ns, int nd, const RankPtrs& ptrs, uint64_t nvec, int unroll, bool nt_loads, int store_policy,
                  void* sink, int max_grid, unsigned long long* claim, void* stream);
 
 // 16-byte vectors each lane of a copy kernel keeps in flight.

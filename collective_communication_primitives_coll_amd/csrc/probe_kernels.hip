@@ -10,7 +10,9 @@
 // length through the same 16-byte vector tiles as the collectives (U
 // vectors per lane, every load of a tile issued before its first store,
 // the same launch bounds and grid sizing).  The caller sweeps the tile size
-// U, the cache policy per direction and the grid, and takes the best, so a
+// U, the cache policy of the loads and of the stores (plain, non-temporal,
+// device scope or both, as the collectives use them) and the grid, and
+// takes the best, so a
 // collective's throughput can be set against the ceiling of its own mix.  It is a measurement helper: destinations
 // receive the XOR of the sources (a fixed pattern when NS = 0).  With no
 // destination the loaded words are folded into one value per lane that
@@ -32,7 +34,7 @@ constexpr bool probe_unroll_ok(int ns, int u) { return (u == 1 || u == 2 || u ==
 // bounds checks, as in the collectives' full tiles).  hook(tok) runs after
 // the loads have returned, before the stores (the claimed tiles' hook, as
 // in the collectives).
-template <int NS, int ND, bool NTL, bool NTS, int U, bool FULL, typename Hook = NoHook>
+template <int NS, int ND, bool NTL, int SP, int U, bool FULL, typename Hook = NoHook>
 __device__ __forceinline__ void probe_tile(const u32x4* const (&src)[NS > 0 ? NS : 1],
                                            u32x4* const (&dst)[ND > 0 ? ND : 1], uint64_t j0, uint64_t nvec,
                                            u32x4* sink, uint32_t pattern, const Hook& hook = Hook{}) {
@@ -71,12 +73,7 @@ __device__ __forceinline__ void probe_tile(const u32x4* const (&src)[NS > 0 ? NS
     }
   } else {
 #pragma unroll
-    for (int d = 0; d < ND; ++d)
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const uint64_t j = j0 + (uint64_t)u * kBlock;
-        if (FULL || j < nvec) st16<NTS>(dst[d] + j, x[u]);
-      }
+    for (int d = 0; d < ND; ++d) store_tile<SP, U, kBlock, FULL>(dst[d], j0, nvec, x);
   }
 }
 
@@ -84,7 +81,7 @@ __device__ __forceinline__ void probe_tile(const u32x4* const (&src)[NS > 0 ? NS
 // of the tiles dealt out in turn and the rest claimed one at a time by
 // workgroups, as the reductions and fan-outs do (thread 0 claims before a
 // tile's loads and publishes after them through LDS).
-template <int NS, int ND, bool NTL, bool NTS, int U>
+template <int NS, int ND, bool NTL, int SP, int U>
 COLL_STREAM_KERNEL void probe_kernel(RankPtrs ptrs, uint64_t nvec, u32x4* sink, uint32_t pattern,
                                      unsigned long long* claim) {
   constexpr uint64_t TV = (uint64_t)U * kBlock;
@@ -100,13 +97,13 @@ COLL_STREAM_KERNEL void probe_kernel(RankPtrs ptrs, uint64_t nvec, u32x4* sink, 
   for (int d = 0; d < ND; ++d) dst[d] = (u32x4*)ptrs.dst[d];
   for (uint64_t t = blockIdx.x; t < dealt; t += gridDim.x) {
     const uint64_t j0 = t * TV + threadIdx.x;
-    if (t < nfull) probe_tile<NS, ND, NTL, NTS, U, true>(src, dst, j0, nvec, sink, pattern);
-    else probe_tile<NS, ND, NTL, NTS, U, false>(src, dst, j0, nvec, sink, pattern);
+    if (t < nfull) probe_tile<NS, ND, NTL, SP, U, true>(src, dst, j0, nvec, sink, pattern);
+    else probe_tile<NS, ND, NTL, SP, U, false>(src, dst, j0, nvec, sink, pattern);
   }
   if (!claim) return;
   // the partial last tile is dealt out; the whole tiles [dealt, nfull) are claimed
   if (nfull < nt && nfull % gridDim.x == blockIdx.x)
-    probe_tile<NS, ND, NTL, NTS, U, false>(src, dst, nfull * TV + threadIdx.x, nvec, sink, pattern);
+    probe_tile<NS, ND, NTL, SP, U, false>(src, dst, nfull * TV + threadIdx.x, nvec, sink, pattern);
   __shared__ uint64_t next_tile[2];
   const uint64_t first_claim = wave_value(first);
   if (threadIdx.x == 0) next_tile[0] = first_claim;
@@ -126,7 +123,7 @@ COLL_STREAM_KERNEL void probe_kernel(RankPtrs ptrs, uint64_t nvec, u32x4* sink, 
     for (int k = 0; k < NS; ++k) gs[k] = as_global(src[k]);
 #pragma unroll
     for (int d = 0; d < ND; ++d) gd[d] = as_global(dst[d]);
-    probe_tile<NS, ND, NTL, NTS, U, true>(gs, gd, (dealt + u) * TV + threadIdx.x, nvec, sink, pattern, publish);
+    probe_tile<NS, ND, NTL, SP, U, true>(gs, gd, (dealt + u) * TV + threadIdx.x, nvec, sink, pattern, publish);
     asm volatile("" ::"v"(next));  // keep the claim's register out of the stores' reach
     __syncthreads();
     u = next_tile[par];
@@ -149,7 +146,7 @@ bool probe_mix_supported(int ns, int nd) {
 }
 
 template <int NS, int ND, int U>
-static int launch_mix_u(const RankPtrs& ptrs, uint64_t nvec, bool ntl, bool nts, void* sink, int max_grid,
+static int launch_mix_u(const RankPtrs& ptrs, uint64_t nvec, bool ntl, int sp, void* sink, int max_grid,
                         unsigned long long* claim, hipStream_t s) {
   if constexpr (!probe_unroll_ok(NS, U)) {
     return (int)hipErrorInvalidValue;
@@ -163,33 +160,47 @@ static int launch_mix_u(const RankPtrs& ptrs, uint64_t nvec, bool ntl, bool nts,
     const dim3 g(grid), b(kBlock);
     // claims only with enough whole tiles per workgroup
     unsigned long long* cl = nvec / TV >= kClaimMinTilesPerWg * (uint64_t)grid ? claim : nullptr;
-    if (ntl && nts) hipLaunchKernelGGL((probe_kernel<NS, ND, true, true, U>), g, b, 0, s, ptrs, nvec, sk, pat, cl);
-    else if (ntl) hipLaunchKernelGGL((probe_kernel<NS, ND, true, false, U>), g, b, 0, s, ptrs, nvec, sk, pat, cl);
-    else if (nts) hipLaunchKernelGGL((probe_kernel<NS, ND, false, true, U>), g, b, 0, s, ptrs, nvec, sk, pat, cl);
-    else hipLaunchKernelGGL((probe_kernel<NS, ND, false, false, U>), g, b, 0, s, ptrs, nvec, sk, pat, cl);
+    if (ntl == false && sp == kStPlain)
+      hipLaunchKernelGGL((probe_kernel<NS, ND, false, kStPlain, U>), g, b, 0, s, ptrs, nvec, sk, pat, cl);
+    else if (ntl == false && sp == kStNT)
+      hipLaunchKernelGGL((probe_kernel<NS, ND, false, kStNT, U>), g, b, 0, s, ptrs, nvec, sk, pat, cl);
+    else if (ntl == false && sp == kStDevice)
+      hipLaunchKernelGGL((probe_kernel<NS, ND, false, kStDevice, U>), g, b, 0, s, ptrs, nvec, sk, pat, cl);
+    else if (ntl == true && sp == kStPlain)
+      hipLaunchKernelGGL((probe_kernel<NS, ND, true, kStPlain, U>), g, b, 0, s, ptrs, nvec, sk, pat, cl);
+    else if (ntl == true && sp == kStNT)
+      hipLaunchKernelGGL((probe_kernel<NS, ND, true, kStNT, U>), g, b, 0, s, ptrs, nvec, sk, pat, cl);
+    else if (ntl == true && sp == kStDevice)
+      hipLaunchKernelGGL((probe_kernel<NS, ND, true, kStDevice, U>), g, b, 0, s, ptrs, nvec, sk, pat, cl);
+    else if (ntl == false && sp == kStNTDevice)
+      hipLaunchKernelGGL((probe_kernel<NS, ND, false, kStNTDevice, U>), g, b, 0, s, ptrs, nvec, sk, pat, cl);
+    else if (ntl == true && sp == kStNTDevice)
+      hipLaunchKernelGGL((probe_kernel<NS, ND, true, kStNTDevice, U>), g, b, 0, s, ptrs, nvec, sk, pat, cl);
+    else
+      return (int)hipErrorInvalidValue;
     return (int)hipGetLastError();
   }
 }
 
 template <int NS, int ND>
-static int launch_mix(const RankPtrs& ptrs, uint64_t nvec, int unroll, bool ntl, bool nts, void* sink,
+static int launch_mix(const RankPtrs& ptrs, uint64_t nvec, int unroll, bool ntl, int sp, void* sink,
                       int max_grid, unsigned long long* claim, hipStream_t s) {
   switch (unroll) {
-    case 1: return launch_mix_u<NS, ND, 1>(ptrs, nvec, ntl, nts, sink, max_grid, claim, s);
-    case 2: return launch_mix_u<NS, ND, 2>(ptrs, nvec, ntl, nts, sink, max_grid, claim, s);
-    case 4: return launch_mix_u<NS, ND, 4>(ptrs, nvec, ntl, nts, sink, max_grid, claim, s);
-    case 8: return launch_mix_u<NS, ND, 8>(ptrs, nvec, ntl, nts, sink, max_grid, claim, s);
+    case 1: return launch_mix_u<NS, ND, 1>(ptrs, nvec, ntl, sp, sink, max_grid, claim, s);
+    case 2: return launch_mix_u<NS, ND, 2>(ptrs, nvec, ntl, sp, sink, max_grid, claim, s);
+    case 4: return launch_mix_u<NS, ND, 4>(ptrs, nvec, ntl, sp, sink, max_grid, claim, s);
+    case 8: return launch_mix_u<NS, ND, 8>(ptrs, nvec, ntl, sp, sink, max_grid, claim, s);
   }
   return (int)hipErrorInvalidValue;
 }
 
 bool probe_unroll_supported(int ns, int unroll) { return probe_unroll_ok(ns, unroll); }
 
-int launch_probe(int ns, int nd, const RankPtrs& ptrs, uint64_t nvec, int unroll, bool nt_loads, bool nt_stores,
+int launch_probe(int ns, int nd, const RankPtrs& ptrs, uint64_t nvec, int unroll, bool nt_loads, int store_policy,
                  void* sink, int max_grid, unsigned long long* claim, void* stream) {
   hipStream_t s = (hipStream_t)stream;
 #define COLL_PROBE_CASE(A, B) \
-  if (ns == A && nd == B) return launch_mix<A, B>(ptrs, nvec, unroll, nt_loads, nt_stores, sink, max_grid, claim, s);
+  if (ns == A && nd == B) return launch_mix<A, B>(ptrs, nvec, unroll, nt_loads, store_policy, sink, max_grid, claim, s);
   COLL_PROBE_MIXES(COLL_PROBE_CASE)
 #undef COLL_PROBE_CASE
   return (int)hipErrorInvalidValue;

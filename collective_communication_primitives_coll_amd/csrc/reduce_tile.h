@@ -160,6 +160,8 @@ __device__ __forceinline__ u32x4 fold_vectors(const u32x4 (&r)[P], const Scales<
 // src[k] and dst[d] point at the segment's first aligned vector;
 // j0 = tile * U * LANES + lane is this lane's first vector index.
 // FULL: every vector of the tile lies inside the segment (nvec unused).
+// NTS: non-temporal stores (AllReduce); otherwise device-scope stores
+// (ReduceScatter, Reduce; see kStDevice).
 // hook(tok) runs after the fold, before the stores: every load of the tile
 // has then returned, and with it everything the wave issued before them.
 // tok is a zero the compiler cannot see through, produced after the fold:
@@ -190,13 +192,19 @@ __device__ __forceinline__ void reduce_vec_tile(const typename Traits<DT>::S* co
     asm volatile("" : "+v"(tok) : "v"(out[0]), "v"(out[U - 1]));
     hook(tok);
   }
+  if constexpr (NTS) {
 #pragma unroll
-  for (int d = 0; d < ND; ++d)
+    for (int d = 0; d < ND; ++d)
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint64_t j = j0 + (uint64_t)u * LANES;
-      if (FULL || j < nvec) st16<NTS>(dst[d] + j * V, out[u]);
-    }
+      for (int u = 0; u < U; ++u) {
+        const uint64_t j = j0 + (uint64_t)u * LANES;
+        if (FULL || j < nvec) st16<true>(dst[d] + j * V, out[u]);
+      }
+  } else {
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+      store_tile<kStDevice, U, LANES, FULL>(reinterpret_cast<u32x4*>(dst[d]), j0, nvec, out);
+  }
 }
 
 // One element e of the segment (src/dst at the segment start): the p

@@ -429,7 +429,11 @@ coll_status_t coll_allreduce_batch_noalloc(const coll_call_t* calls, int ncalls,
  * one value per lane that is written to `sink` (16 device bytes, 16-byte
  * aligned) only if it equals an internal pattern, so the reads stay.
  * flags: COLL_PROBE_NT_LOADS / COLL_PROBE_NT_STORES select non-temporal
- * loads / stores (else cached); COLL_PROBE_CLAIM deals out a quarter of
+ * loads / stores (else cached); COLL_PROBE_DEVICE_STORES makes the stores
+ * of device scope, written through the L2 as ReduceScatter and Reduce
+ * store (with COLL_PROBE_NT_STORES: non-temporal stores of device scope,
+ * as AllGather and Broadcast at p >= 2 store);
+ * COLL_PROBE_CLAIM deals out a quarter of
  * the tiles in turn and lets workgroups claim the rest one at a time, as
  * the large AllReduce, ReduceScatter, AllGather and Broadcast calls do
  * (with at least 8 whole tiles per workgroup; else every tile is dealt
@@ -442,6 +446,7 @@ coll_status_t coll_allreduce_batch_noalloc(const coll_call_t* calls, int ncalls,
 #define COLL_PROBE_NT_LOADS 1u
 #define COLL_PROBE_NT_STORES 2u
 #define COLL_PROBE_CLAIM 4u
+#define COLL_PROBE_DEVICE_STORES 8u
 coll_status_t coll_stream_probe(const void* const* src, int nsrc, void* const* dst, int ndst, size_t bytes,
                                 int unroll, unsigned flags, void* sink, void* stream);
 

@@ -314,7 +314,7 @@ def test_stream_probe_rejects_invalid_calls():
     # no stream at all, bytes not a multiple of 16, unknown flag
     assert L.coll_stream_probe(None, 0, None, 0, 64, 4, 0, sink, None) == coll.COLL_ERR_INVALID_ARG
     assert L.coll_stream_probe(a, 1, b, 1, 40, 4, 0, None, None) == coll.COLL_ERR_INVALID_ARG
-    assert L.coll_stream_probe(a, 1, b, 1, 64, 4, 8, None, None) == coll.COLL_ERR_INVALID_ARG
+    assert L.coll_stream_probe(a, 1, b, 1, 64, 4, 16, None, None) == coll.COLL_ERR_INVALID_ARG
     assert L.coll_stream_probe(a, 1, b, 1, 64, 0, 0, None, None) == coll.COLL_ERR_INVALID_ARG
     # a mix or a tile size the probe does not build
     assert L.coll_stream_probe(a, 2, None, 0, 64, 4, 0, sink, None) == coll.COLL_ERR_UNSUPPORTED

@@ -1477,9 +1477,11 @@ def test_alias_rejections(coll):
 @pytest.mark.parametrize("ns,nd", [(1, 1), (3, 1), (8, 8), (1, 4), (0, 4), (8, 0)])
 @pytest.mark.parametrize("big", [False, True])
 def test_stream_probe_writes_the_xor_of_its_sources(coll, ns, nd, big):
-    """Several tiles and a ragged last tile; big: 16 whole tiles per
-    workgroup and more at one vector per lane, where COLL_PROBE_CLAIM
-    (flag 4) claims three quarters of them."""
+    """Several tiles and a ragged last tile, under each load and store
+    policy (flag 8: device-scope stores, 10: non-temporal ones of device
+    scope); big: 16 whole tiles per workgroup
+    and more at one vector per lane, where COLL_PROBE_CLAIM (flag 4) claims
+    three quarters of them."""
     import torch
     nbytes = (4096 * 4096 if big else 3 * 4096 * 16) + 48
     words = nbytes // 4
@@ -1488,7 +1490,8 @@ def test_stream_probe_writes_the_xor_of_its_sources(coll, ns, nd, big):
     src = [torch.from_numpy(h.view(np.int32)).cuda() for h in hs]
     dst = [torch.full((words + 4,), 7, dtype=torch.int32, device="cuda") for _ in range(nd)]
     sink = torch.full((4,), 5, dtype=torch.int32, device="cuda")
-    cases = ((4, 1), (7, 2)) if big else ((0, 1), (3, 2), (1, 4), (2, 8), (4, 1))
+    cases = ((4, 1), (7, 2), (12, 1), (14, 4)) if big else ((0, 1), (3, 2), (1, 4), (2, 8), (4, 1), (8, 2), (9, 8),
+                                                             (10, 4), (11, 1))
     for flags, unroll in cases:
         if ns * unroll > 32:
             continue
