@@ -340,7 +340,11 @@ __device__ __forceinline__ uint64_t wave_value(unsigned long long v) {
 // AllReduce (p = 8, 256 MiB fp32 per rank) slower than non-temporal stores
 // (756 against 737 us).  AllGather's fan-out (1 GiB written) took 172-173 us
 // with non-temporal stores of device scope against 174-175 us with
-// non-temporal ones.  Each kernel takes the policy it measured best.
+// non-temporal ones.  Stores that leave dirty lines in the Infinity Cache
+// move part of their cost to whichever later kernel evicts them (a MoE
+// pack with device-scope stores was 8 us faster but made the exchange after
+// it 26 us slower), so each kernel takes the policy that measured best
+// over the path it sits in, not alone.
 // ---------------------------------------------------------------------------
 
 // HIP's global stores cannot carry sc1, so device-scope stores go through a

@@ -365,10 +365,15 @@ struct CombBatch {
 // DIRECT: pos[rank] is an int64 location array from the direct dispatch;
 // slot s reads row (loc & 0xffffffff) of src[loc >> 32] (skipped when the
 // location is -1 or outside the rank count or the row capacity cap[j]).
-// Vector stores are of device scope, non-temporal for DIRECT.  Same-box
-// A/B, 4096 x 7168 bf16 per rank, p = 8, top-2, after the reverse
-// exchange: 304 us with device-scope stores, 330 us non-temporal of device
-// scope, 356 us plain; DIRECT 330, 350 and 356 us.
+// Vector stores are non-temporal of device scope.  Same-box A/B, 4096 x
+// 7168 bf16 per rank, p = 8, top-2, timed as a stage of the whole path
+// (pack, exchange, reverse exchange, combine): combine 332-333 us against
+// 339 us with device-scope stores and 355 us with plain ones (path 1256-1259
+// against 1270 and 1294-1296 us); DIRECT 330-333 us against 339-343 and
+// 354 us.  Device-scope stores alone had made the combine faster still
+// when measured after a pack that stored the same way (304 us), but that
+// pack then slowed the exchange after it by 26 us: dirty lines left in the
+// Infinity Cache are written back during a later kernel.
 // K: slots held in registers, the smallest power of two >= k.
 template <int DT, bool DIRECT, int K>
 COLL_STREAM_KERNEL void moe_combine_kernel(MoeRowArgs a) {
@@ -455,7 +460,7 @@ COLL_STREAM_KERNEL void moe_combine_kernel(MoeRowArgs a) {
           y[s][u] = u32x4{0, 0, 0, 0};
           if (ok[s] && j < sp.nvec) y[s][u] = ld16<true>(yrow[s] + sp.head + j * V);
         }
-      const DeviceScopeStores<DIRECT ? kCachePolicyNtSc1 : kCachePolicySc1> st(
+      const DeviceScopeStores<kCachePolicyNtSc1> st(
           (uint64_t)(out + sp.head) + j0 * 16, (uint32_t)kCB * kWaveLanes * 16);
 #pragma unroll
       for (int u = 0; u < kCB; ++u) {

@@ -160,8 +160,11 @@ __device__ __forceinline__ u32x4 fold_vectors(const u32x4 (&r)[P], const Scales<
 // src[k] and dst[d] point at the segment's first aligned vector;
 // j0 = tile * U * LANES + lane is this lane's first vector index.
 // FULL: every vector of the tile lies inside the segment (nvec unused).
-// NTS: non-temporal stores (AllReduce); otherwise device-scope stores
-// (ReduceScatter, Reduce; see kStDevice).
+// NTS: non-temporal stores (AllReduce with workgroup tiles; of device
+// scope for wave tiles, i.e. the batch: 11.48 against 11.54 ms for 10,000
+// calls at p = 16, while the single AllReduce took 742-756 us against
+// 737 us with either device-scope policy at p = 8, 256 MiB fp32 per rank);
+// otherwise device-scope stores (ReduceScatter, Reduce; see kStDevice).
 // hook(tok) runs after the fold, before the stores: every load of the tile
 // has then returned, and with it everything the wave issued before them.
 // tok is a zero the compiler cannot see through, produced after the fold:
@@ -192,7 +195,8 @@ __device__ __forceinline__ void reduce_vec_tile(const typename Traits<DT>::S* co
     asm volatile("" : "+v"(tok) : "v"(out[0]), "v"(out[U - 1]));
     hook(tok);
   }
-  if constexpr (NTS) {
+  constexpr int SP = !NTS ? kStDevice : LANES == kBlock ? kStNT : kStNTDevice;
+  if constexpr (SP == kStNT) {
 #pragma unroll
     for (int d = 0; d < ND; ++d)
 #pragma unroll
@@ -203,7 +207,7 @@ __device__ __forceinline__ void reduce_vec_tile(const typename Traits<DT>::S* co
   } else {
 #pragma unroll
     for (int d = 0; d < ND; ++d)
-      store_tile<kStDevice, U, LANES, FULL>(reinterpret_cast<u32x4*>(dst[d]), j0, nvec, out);
+      store_tile<SP, U, LANES, FULL>(reinterpret_cast<u32x4*>(dst[d]), j0, nvec, out);
   }
 }
 
