@@ -11,7 +11,8 @@ the part of the network.  The JSON line reports
   input element read once, every output element written once, self
   copies included), with busbw/algbw per collective after the bus
   bandwidth conventions of "集合通信：原语、算法、NCCL 实现与拓扑映射"
-  (hpc/04, section 2.5);
+  (hpc/04, section 2.5), and each kernel's time also cold (after a
+  512 MiB overwrite that evicts the Infinity Cache);
 * roofline: the dominant kernel's algorithmic bytes per launch over its
   mean duration (HIP events on the launch stream) against 8 TB/s, plus
   the HBM traffic read from rocprofv3 FETCH_SIZE / WRITE_SIZE counters
@@ -23,7 +24,7 @@ the part of the network.  The JSON line reports
   exchange -> combine path, Gather, Scatter), the small
   AllReduce at p = 4, the 10,000-call batched AllReduce at p = 16 (also
   as individual calls, with latency percentiles and an alpha-beta fit)
-  and the box's copy ceiling, each timed with HIP events.  Every row
+  and the device copy ceiling, each timed with HIP events.  Every row
   carries the attainable ceiling of its read:write stream mix, measured in
   the same run with the library's direction-mix probe (coll_stream_probe:
   the collectives' own tile code), and its fraction of that ceiling.
@@ -973,6 +974,27 @@ def main(argv=None) -> int:
         "allgather": coll_entry(metrics, "allgather", "allgather", p, n, 2, ag_med, "ring",
                                 {"t_p95_us": round(ag_p95, 2), "t_mean_us": round(ag_mean, 2)}),
     }
+    # Cold step (outside the timed loop): a 512 MiB overwrite before each
+    # step evicts the Infinity Cache; events bracket ReduceScatter and
+    # AllGather as above.  ReduceScatter's shards still reach AllGather
+    # through the cache within the step.
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = []
+    for i in range(max(K, 5)):
+        scratch.fill_(i & 0xFF)
+        ce = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ce[0].record()
+        rs()
+        ce[1].record()
+        ag()
+        ce[2].record()
+        cold.append(ce)
+    torch.cuda.synchronize()
+    rs_cold = stats_us([c[0].elapsed_time(c[1]) for c in cold])[0]
+    ag_cold = stats_us([c[1].elapsed_time(c[2]) for c in cold])[0]
+    del scratch
+    per_coll["reduce_scatter"]["t_cold_med_us"] = round(rs_cold, 2)
+    per_coll["allgather"]["t_cold_med_us"] = round(ag_cold, 2)
     # dominant kernel: the longer of the two launches
     if rs_mean >= ag_mean:
         dom, dom_bytes, dom_us, kkey = "reduce_kernel<bf16,sum,p=8> (coll_reduce_scatter)", hbm_rs, rs_mean, "reduce_scatter"

@@ -519,6 +519,7 @@ COLL_EXPORT coll_status_t coll_alltoall_algo(const void* const* send, void* cons
   coll::RankPtrs P = make_ptrs(send, p, recv, p);
   coll::CopyGeom g{n_block, p, coll::kCopyAllToAll, common_mis(send, p),
                    common_mis((const void* const*)recv, p)};
+  g.claim = stream_claim_slot(stream);
   if (algo == COLL_A2A_LDS_STAGED && coll::can_stage_alltoall((int)dsize(dtype), g))
     return finish(coll::launch_alltoall_lds((int)dsize(dtype), P, g, grid, stream));
   return finish(coll::launch_copy((int)dsize(dtype), P, g, grid, stream));
@@ -547,6 +548,7 @@ COLL_EXPORT coll_status_t coll_gather(const void* const* send, void* recv_root, 
   void* dst[1] = {recv_root};
   coll::RankPtrs P = make_ptrs(send, p, dst, 1);
   coll::CopyGeom g{n, p, coll::kCopyGather, common_mis(send, p), (int)((uintptr_t)recv_root & 15)};
+  g.claim = stream_claim_slot(stream);
   return finish(coll::launch_copy((int)dsize(dtype), P, g, grid, stream));
 }
 
@@ -574,6 +576,7 @@ COLL_EXPORT coll_status_t coll_scatter(const void* send_root, void* const* recv,
   coll::RankPtrs P = make_ptrs(src, 1, recv, p);
   coll::CopyGeom g{n, p, coll::kCopyScatter, (int)((uintptr_t)send_root & 15),
                    common_mis((const void* const*)recv, p)};
+  g.claim = stream_claim_slot(stream);
   return finish(coll::launch_copy((int)dsize(dtype), P, g, grid, stream));
 }
 
@@ -625,6 +628,7 @@ coll_status_t alltoallv_impl(const void* const* send, void* const* recv, int p, 
   a.src_mis = common_mis(send, p);
   a.dst_mis = common_mis((const void* const*)recv, p);
   a.transposed = transposed;
+  a.claim = stream_claim_slot(stream);
   return finish(coll::launch_alltoallv((int)d, P, a, grid, stream));
 }
 }  // namespace

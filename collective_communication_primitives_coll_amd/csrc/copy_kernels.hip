@@ -255,10 +255,17 @@ __device__ __forceinline__ void pair_segment(const RankPtrs& ptrs, const CopyGeo
   }
 }
 
-// The 1:1 copies deal out every tile: claiming tiles (8 consecutive tiles
-// per claim, a quarter dealt out first) made an All-to-All (p = 8, 56 MiB
-// per rank) 10% slower and a Gather or Scatter (p = 8, 16 MiB blocks) 27%
-// slower in same-box A/Bs, unlike the fan-outs and the reductions.
+// The uniform 1:1 copies deal out kPairDealtEighths of their flat tiles in
+// turn and claim the rest one tile at a time.  Dealt out alone, the
+// workgroups of an All-to-All (p = 8, 56 MiB per rank, 512 workgroups)
+// finished between 140 and 153 us and those of a Gather or Scatter (p = 8,
+// 16 MiB blocks) between 35 and 43 us.  One counter serves about 83 claims
+// per microsecond, fewer than these copies make (a tile moves 32 KiB), so
+// the claimed tiles are split into kClaimPools pools: workgroup b claims
+// from counter b mod kClaimPools, and claim c of pool x is flat tile
+// dealt + x + kClaimPools * c, so the pools advance through the same
+// region together.  (Claiming runs of 8 consecutive tiles from one counter
+// had been 10% slower for All-to-All and 27% for Gather and Scatter.)
 template <int B, int KIND>
 COLL_STREAM_KERNEL void pair_copy_flat_kernel(RankPtrs ptrs, CopyGeom g, uint64_t head, uint64_t nvec,
                                               uint64_t tail, uint32_t tps) {
@@ -266,10 +273,17 @@ COLL_STREAM_KERNEL void pair_copy_flat_kernel(RankPtrs ptrs, CopyGeom g, uint64_
   constexpr uint64_t V = 16 / B;
   const uint32_t nseg = KIND == kCopyAllToAll ? (uint32_t)g.p * (uint32_t)g.p : (uint32_t)g.p;
   const uint32_t total = nseg * tps;
+  // claims: per tiles from each pool, the first `dealt` tiles dealt out
+  const uint32_t per = g.claim ? total / 8 * (8 - kPairDealtEighths) / kClaimPools : 0;
+  const uint32_t dealt = total - per * kClaimPools;
+  const uint32_t pool = blockIdx.x % kClaimPools;
+  unsigned long long* ctr = g.claim ? g.claim + pool * kClaimPoolWords : nullptr;
+  unsigned long long first = 0;
+  if (per) first = issue_claim(ctr, (int)threadIdx.x);
   uint32_t cur = 0xffffffffu;
   const W* src = nullptr;
   W* dst = nullptr;
-  for (uint32_t f = blockIdx.x; f < total; f += gridDim.x) {
+  for (uint32_t f = blockIdx.x; f < dealt; f += gridDim.x) {
     const uint32_t sgi = f / tps, t = f - sgi * tps;
     if (sgi != cur) {
       cur = sgi;
@@ -290,6 +304,53 @@ COLL_STREAM_KERNEL void pair_copy_flat_kernel(RankPtrs ptrs, CopyGeom g, uint64_
       }
     }
   }
+  if (!per) return;
+  // claimed tiles: thread 0 claims the next tile before the current tile's
+  // loads and publishes it through LDS once they have returned
+  __shared__ uint64_t next_tile[2];
+  const uint64_t first_claim = wave_value(first);
+  if (threadIdx.x == 0) next_tile[0] = first_claim;
+  __syncthreads();
+  uint64_t c = next_tile[0];
+  int par = 1;
+  while (c < per) {
+    const unsigned long long next = issue_claim(ctr, (int)threadIdx.x);
+    const uint32_t f = dealt + pool + kClaimPools * (uint32_t)c;
+    const uint32_t sgi = f / tps, t = f - sgi * tps;
+    if (sgi != cur) {
+      cur = sgi;
+      pair_segment<B, KIND>(ptrs, g, sgi, &src, &dst);
+    }
+    const auto publish = [&](uint32_t tok) {
+      const uint64_t v = wave_value(next + tok);
+      if (threadIdx.x == 0) next_tile[par] = v;
+    };
+    // pointers carried across iterations lose their address space:
+    // restate it so the tile uses global, not flat, instructions
+    const W* gs = as_global(src);
+    W* gd = as_global(dst);
+    const u32x4* vs = reinterpret_cast<const u32x4*>(gs + head);
+    u32x4* vd = reinterpret_cast<u32x4*>(gd + head);
+    auto gdst = [&](int) -> u32x4* { return vd; };
+    const uint64_t j0 = (uint64_t)t * kCopyTV + threadIdx.x;
+    if ((uint64_t)(t + 1) * kCopyTV <= nvec) copy_vec_tile<true, true, 1>(vs, gdst, 1, j0, nvec, publish);
+    else if ((uint64_t)t * kCopyTV < nvec) copy_vec_tile<true, false, 1>(vs, gdst, 1, j0, nvec, publish);
+    else publish(0);
+    if (t == 0 && (head || tail)) {
+      const uint64_t i = threadIdx.x;
+      if (i < head + tail) {
+        const uint64_t x = i < head ? i : head + nvec * V + (i - head);
+        st1<true>(gd + x, ld1<true>(gs + x));
+      }
+    }
+    asm volatile("" ::"v"(next));  // keep the claim's register out of the stores' reach
+    __syncthreads();
+    c = next_tile[par];
+    par ^= 1;
+  }
+  // the workgroups of pool `pool`: b < gridDim.x with b mod kClaimPools == pool
+  const uint64_t workers = (gridDim.x - pool + kClaimPools - 1) / kClaimPools;
+  if (threadIdx.x == 0) claim_last(ctr, c, per, workers);
 }
 
 // ---------------------------------------------------------------------------
@@ -383,7 +444,11 @@ COLL_STREAM_KERNEL void alltoallv_kernel(RankPtrs ptrs, A2avArgs a) {
 // and each flat tile finds its segment by binary search over the starts.  The
 // walking kernel above has every workgroup run the segment routine for
 // all p^2 segments, which made small calls take 40 us at p = 8 and 149 us
-// at p = 16.
+// at p = 16.  With a claim slot and at least kClaimMinTilesPerWg aligned
+// tiles per workgroup, the aligned tiles are split as in
+// pair_copy_flat_kernel: kPairDealtEighths of them dealt out in turn, the
+// rest claimed one at a time from kClaimPools pooled counters (every
+// workgroup computes the same tile counts, so all agree on the split).
 template <int B>
 COLL_STREAM_KERNEL void alltoallv_flat_kernel(RankPtrs ptrs, A2avArgs a) {
   using W = typename Word<B>::T;
@@ -444,8 +509,14 @@ COLL_STREAM_KERNEL void alltoallv_flat_kernel(RankPtrs ptrs, A2avArgs a) {
     }
   };
   const uint64_t total0 = tstart[0][pp], total = total0 + tstart[1][pp];
-  uint64_t f = blockIdx.x;
-  for (; f < total0; f += gridDim.x) {
+  const bool claims = a.claim && total0 >= kClaimMinTilesPerWg * gridDim.x && gridDim.x >= 4 * kClaimPools;
+  const uint64_t per = claims ? total0 / 8 * (8 - kPairDealtEighths) / kClaimPools : 0;
+  const uint64_t dealt0 = total0 - per * kClaimPools;
+  const uint32_t pool = blockIdx.x % kClaimPools;
+  unsigned long long* ctr = per ? a.claim + pool * kClaimPoolWords : nullptr;
+  unsigned long long first = 0;
+  if (per) first = issue_claim(ctr, tid);
+  for (uint64_t f = blockIdx.x; f < dealt0; f += gridDim.x) {
     int sgi;
     uint64_t t;
     find(0, f, &sgi, &t);
@@ -461,7 +532,7 @@ COLL_STREAM_KERNEL void alltoallv_flat_kernel(RankPtrs ptrs, A2avArgs a) {
     else if (t * kCopyTV < sp.nvec) copy_vec_tile<true, false, 1>(vs, gdst, 1, j0, sp.nvec);
     if (t == 0 && (sp.head || sp.tail)) edges(src, dst, sp);
   }
-  for (; f < total; f += gridDim.x) {
+  for (uint64_t f = total0 + blockIdx.x; f < total; f += gridDim.x) {
     int sgi;
     uint64_t t;
     find(1, f - total0, &sgi, &t);
@@ -477,6 +548,43 @@ COLL_STREAM_KERNEL void alltoallv_flat_kernel(RankPtrs ptrs, A2avArgs a) {
     else if (t * kCopyTV < sp.nvec) copy_shift_tile<false, 1>(vs, gdst, 1, j0, sp.nvec, sp.m);
     if (t == 0 && (sp.head || sp.tail)) edges(src, dst, sp);
   }
+  if (!per) return;
+  // claimed aligned tiles (thread 0 claims before a tile's loads and
+  // publishes after them, as in pair_copy_flat_kernel)
+  __shared__ uint64_t next_tile[2];
+  const uint64_t first_claim = wave_value(first);
+  if (tid == 0) next_tile[0] = first_claim;
+  __syncthreads();
+  uint64_t c = next_tile[0];
+  int par = 1;
+  while (c < per) {
+    const unsigned long long next = issue_claim(ctr, tid);
+    int sgi;
+    uint64_t t;
+    find(0, dealt0 + pool + (uint64_t)kClaimPools * c, &sgi, &t);
+    const int i = sgi / p, j = sgi - (sgi / p) * p;
+    const W* src = as_global((const W*)ptrs.src[i] + soff[sgi]);
+    W* dst = as_global((W*)ptrs.dst[j] + roff[sgi]);
+    const ShiftSpan sp = shift_span<B>(src, dst, (uint64_t)cnt[sgi]);
+    const auto publish = [&](uint32_t tok) {
+      const uint64_t v = wave_value(next + tok);
+      if (tid == 0) next_tile[par] = v;
+    };
+    const u32x4* vs = reinterpret_cast<const u32x4*>(src + sp.head);
+    u32x4* vd = reinterpret_cast<u32x4*>(dst + sp.head);
+    auto gdst = [&](int) -> u32x4* { return vd; };
+    const uint64_t j0 = t * kCopyTV + tid;
+    if ((t + 1) * kCopyTV <= sp.nvec) copy_vec_tile<true, true, 1>(vs, gdst, 1, j0, sp.nvec, publish);
+    else if (t * kCopyTV < sp.nvec) copy_vec_tile<true, false, 1>(vs, gdst, 1, j0, sp.nvec, publish);
+    else publish(0);
+    if (t == 0 && (sp.head || sp.tail)) edges(src, dst, sp);
+    asm volatile("" ::"v"(next));  // keep the claim's register out of the stores' reach
+    __syncthreads();
+    c = next_tile[par];
+    par ^= 1;
+  }
+  const uint64_t workers = (gridDim.x - pool + kClaimPools - 1) / kClaimPools;
+  if (tid == 0) claim_last(ctr, c, per, workers);
 }
 
 // ---------------------------------------------------------------------------
@@ -577,14 +685,18 @@ static int launch_copy_b(const RankPtrs& ptrs, const CopyGeom& g, int max_grid, 
       const int grid = clamp_grid(tiles, max_grid);
       if (!grid) return 0;
       const uint32_t t32 = (uint32_t)tps;
+      // claims only with enough whole tiles per workgroup and every pool
+      // served by several workgroups
+      CopyGeom gc = g;
+      if (tiles < kClaimMinTilesPerWg * (uint64_t)grid || grid < 4 * kClaimPools) gc.claim = nullptr;
       if (g.kind == kCopyAllToAll)
-        hipLaunchKernelGGL((pair_copy_flat_kernel<B, kCopyAllToAll>), dim3(grid), dim3(kBlock), 0, s, ptrs, g, head,
+        hipLaunchKernelGGL((pair_copy_flat_kernel<B, kCopyAllToAll>), dim3(grid), dim3(kBlock), 0, s, ptrs, gc, head,
                            nvec, tail, t32);
       else if (g.kind == kCopyGather)
-        hipLaunchKernelGGL((pair_copy_flat_kernel<B, kCopyGather>), dim3(grid), dim3(kBlock), 0, s, ptrs, g, head,
+        hipLaunchKernelGGL((pair_copy_flat_kernel<B, kCopyGather>), dim3(grid), dim3(kBlock), 0, s, ptrs, gc, head,
                            nvec, tail, t32);
       else
-        hipLaunchKernelGGL((pair_copy_flat_kernel<B, kCopyScatter>), dim3(grid), dim3(kBlock), 0, s, ptrs, g, head,
+        hipLaunchKernelGGL((pair_copy_flat_kernel<B, kCopyScatter>), dim3(grid), dim3(kBlock), 0, s, ptrs, gc, head,
                            nvec, tail, t32);
       return (int)hipGetLastError();
     }

@@ -39,14 +39,16 @@ constexpr uint64_t kCopyTV = (uint64_t)kCopyU * kBlock;  // vectors per copy til
 template <bool NTL, bool FULL, int ND, typename GD, typename Hook = NoHook>
 __device__ __forceinline__ void copy_vec_tile(const u32x4* src, const GD& gdst, int nd, uint64_t j0,
                                               uint64_t nvec, const Hook& hook = Hook{}) {
+  constexpr bool kHook = !std::is_same<Hook, NoHook>::value;
   u32x4 r[kCopyU];
 #pragma unroll
   for (int u = 0; u < kCopyU; ++u) {
     const uint64_t j = j0 + (uint64_t)u * kBlock;
     if (FULL || j < nvec) r[u] = ld16<NTL>(src + j);
+    else if (kHook) r[u] = u32x4{0, 0, 0, 0};  // defined input for the hook's token
   }
   __builtin_amdgcn_sched_barrier(0);  // all loads of the tile before the first store
-  if constexpr (!std::is_same<Hook, NoHook>::value) {
+  if constexpr (kHook) {
     uint32_t tok = 0;
     asm volatile("" : "+v"(tok) : "v"(r[0]), "v"(r[kCopyU - 1]));
     hook(tok);

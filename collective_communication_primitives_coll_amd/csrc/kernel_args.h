@@ -68,8 +68,9 @@ struct CopyGeom {
   int kind;
   int src_mis;
   int dst_mis;
-  // Claim slot for the claimed tail of fanout_kernel (AllGather,
-  // Broadcast), or null to deal out every tile in turn.
+  // Claim slot for the claimed tails of fanout_kernel (AllGather,
+  // Broadcast) and pair_copy_flat_kernel (All-to-All, Gather, Scatter), or
+  // null to deal out every tile in turn.
   unsigned long long* claim;
 };
 
@@ -82,6 +83,7 @@ struct A2avArgs {
   int src_mis;
   int dst_mis;
   int transposed;                // elements from i to j are counts[j*p + i]
+  unsigned long long* claim;     // claim slot (pooled claims of the flat kernel), or null
 };
 
 // MoE dispatch pack and combine.
@@ -220,14 +222,17 @@ uint64_t batch_tile_elems_host(int dtype, int p);
 constexpr size_t kNoAllocScratchBytes = size_t{4} << 20;
 int noalloc_scratch(int dev, void** out);
 
-// Claim slots (claim_slots.hip): kClaimSlots slots of kClaimSlotWords
-// 64-bit words (one used, the rest keep slots on separate 128-byte lines)
-// in a static device array per GPU.  claim_slots_base gives device dev's
+// Claim slots (claim_slots.hip): kClaimSlots slots in a static device
+// array per GPU, each of kClaimPools counters kClaimPoolWords 64-bit words
+// apart (one 128-byte line each).  claim_slots_base gives device dev's
 // array (dev current).  AllReduce, ReduceScatter, AllGather and
 // Broadcast launches with at least kClaimMinTilesPerWg tiles per
-// workgroup use their slot.
+// workgroup use the slot's first counter; the uniform 1:1 copies use all
+// kClaimPools of them.
 constexpr int kClaimSlots = 1024;
-constexpr int kClaimSlotWords = 16;
+constexpr int kClaimPools = 8;
+constexpr int kClaimPoolWords = 16;
+constexpr int kClaimSlotWords = kClaimPools * kClaimPoolWords;
 constexpr uint64_t kClaimMinTilesPerWg = 8;
 int claim_slots_base(int dev, unsigned long long** out);
 
@@ -269,5 +274,8 @@ constexpr uint64_t kCopyUnroll = 4;
 // 7/8 dealt ~190, 4/8 178-180, 2/8 175-176, 0/8 175-176 (at two per CU
 // 2/8 gave 186-187 and 0/8 193-194).
 constexpr uint64_t kCopyDealtEighths = 2;
+// The uniform 1:1 copies (pair_copy_flat_kernel) deal out this many
+// eighths of their tiles and claim the rest from kClaimPools counters.
+constexpr uint32_t kPairDealtEighths = 4;
 
 }  // namespace coll

@@ -1931,3 +1931,89 @@ def test_copies_with_disagreeing_alignment(coll, dtype, soff, doff):
         exp = native.alltoallv([xs[i][:int(counts[i].sum())] for i in range(p)], counts)
         for j in range(p):
             check(vr[j][0], doff, exp[j], f"A2Av p={p} dest {j}")
+
+
+PAIR_CLAIM_CASES = [
+    # (what, p, n, dtype, off): All-to-All block / Gather-Scatter block
+    # elements, n * element size a multiple of 16, every buffer `off`
+    # elements into its allocation; at least 8 tiles per workgroup for
+    # 512 workgroups, so the last quarter of the tiles is claimed from the
+    # pooled counters, partial last tiles of every block included
+    ("All-to-All bf16", 8, 1_200_008, BF16, 0),
+    ("All-to-All fp32 heads and tails", 8, 600_004, F32, 3),
+    ("Gather fp32", 8, 4_400_004, F32, 0),
+    ("Scatter bf16 p=16 heads and tails", 16, 4_000_008, BF16, 5),
+]
+
+
+def _bits(a: np.ndarray) -> np.ndarray:
+    return a.view(np.uint16) if a.dtype == np.uint16 else a.view(np.uint32)
+
+
+@pytest.mark.parametrize("case", PAIR_CLAIM_CASES, ids=[c[0] for c in PAIR_CLAIM_CASES])
+def test_claimed_tails_pair_copies(coll, case):
+    """1:1 copies large enough to claim their last tiles, twice in a row
+    with different data (the pooled counters must be back at zero for the
+    second call): every element equals the oracle's, and nothing past the
+    buffers is written."""
+    what, p, n, dtype, off = case
+    for rep in range(2):
+        if what.startswith("All-to-All"):
+            hx = gen(p, p * n, dtype, 300 + rep)
+            send = [upload_offset(x, dtype, off) for x in hx]
+            bases = [empty(p * n + off + 8, dtype, fill=0x55) for _ in range(p)]
+            coll.coll_alltoall([v for _, v in send], [b[off:off + p * n] for b in bases])
+            sync()
+            expect = ref.alltoall(hx)
+            for j in range(p):
+                got = to_host(bases[j], dtype)
+                assert_bits_equal(got[off:off + p * n], expect[j], f"{what} rep {rep} j={j}")
+                assert np.all(_bits(got[off + p * n:]) == 0x55), f"{what}: wrote past the end"
+        elif what.startswith("Gather"):
+            hx = gen(p, n, dtype, 310 + rep)
+            send = [upload_offset(x, dtype, off) for x in hx]
+            base = empty(p * n + off + 8, dtype, fill=0x55)
+            coll.coll_gather([v for _, v in send], base[off:off + p * n], rep % p)
+            sync()
+            got = to_host(base, dtype)
+            assert_bits_equal(got[off:off + p * n], ref.gather(hx, rep % p), f"{what} rep {rep}")
+            assert np.all(_bits(got[off + p * n:]) == 0x55), f"{what}: wrote past the end"
+        else:
+            whole = gen(1, p * n, dtype, 320 + rep)[0]
+            _, src = upload_offset(whole, dtype, off)
+            bases = [empty(n + off + 8, dtype, fill=0x55) for _ in range(p)]
+            coll.coll_scatter(src, [b[off:off + n] for b in bases], rep % p)
+            sync()
+            expect = ref.scatter(whole, p, rep % p)
+            for r in range(p):
+                got = to_host(bases[r], dtype)
+                assert_bits_equal(got[off:off + n], expect[r], f"{what} rep {rep} r={r}")
+                assert np.all(_bits(got[off + n:]) == 0x55), f"{what}: wrote past the end"
+
+
+@pytest.mark.parametrize("p,dtype", [(8, BF16), (16, F32)])
+def test_claimed_tails_alltoallv(coll, p, dtype):
+    """Alltoallv large enough for the pooled claims of its aligned tiles,
+    with ragged multinomial counts (partial last tiles, receive heads and
+    tails), twice in a row with different counts: every element equals
+    the oracle's and nothing past the packed blocks is written."""
+    import torch
+    esz = 2 if dtype == BF16 else 4
+    per_src = (128 << 20) // p // esz      # 128 MiB in all: over 8 aligned tiles per workgroup
+    for rep in range(2):
+        rng = np.random.default_rng(400 + rep * 7 + p)
+        counts = np.stack([rng.multinomial(per_src, np.full(p, 1.0 / p)) for _ in range(p)]).astype(np.int64)
+        counts[0, 0] += 3                  # odd sizes: heads and tails in the receive buffers
+        rows = counts.sum(axis=1)
+        cols = counts.sum(axis=0)
+        hx = [gen(1, int(rows[i]), dtype, 410 + i + rep)[0] for i in range(p)]
+        send = [to_dev(x, dtype) for x in hx]
+        recv = [empty(int(cols[j]) + 5, dtype, fill=0x1234) for j in range(p)]
+        cdev = torch.from_numpy(counts.reshape(-1)).cuda()
+        coll.coll_alltoallv(send, recv, cdev, send_cap=[int(r) for r in rows], recv_cap=[int(c) + 5 for c in cols])
+        sync()
+        expect = ref.alltoallv(hx, counts)
+        for j in range(p):
+            got = to_host(recv[j], dtype)
+            assert_bits_equal(got[:int(cols[j])], expect[j], f"A2Av p={p} rep {rep} j={j}")
+            assert np.all(_bits(got[int(cols[j]):]) == 0x1234), "wrote past the end"
