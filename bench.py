@@ -1066,35 +1066,50 @@ def main(argv=None) -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
         "collectives": [compact_row(r) for r in rows],
-        "source_hash": {k: source_hash(k) for k in KERNEL_SOURCES},
     }
+    print("# source_hash " + json.dumps({k: source_hash(k) for k in KERNEL_SOURCES}), file=sys.stderr, flush=True)
     print(json.dumps(line, separators=(",", ":")), flush=True)
     return 0
 
 
+def _short(v, key: str = ""):
+    """A number as the summary line keeps it: GB/s as integers, times to
+    0.1 us (0.01 below 10 us), fractions and ratios to three decimals."""
+    if not isinstance(v, float):
+        return v
+    if key.endswith("GBps"):
+        return round(v)
+    if key.startswith("t_") or key.endswith("_us") or key.endswith("us_per_call"):
+        return round(v, 2 if abs(v) < 10 else 1)
+    return round(v, 3)
+
+
 def compact_row(row: dict) -> dict:
     """The figures of a table row that the summary line keeps: time, HBM
-    GB/s and share of peak, busbw, and the fraction of the row's mix
-    ceiling; nested stages and latency tables in the same short form."""
-    keep = ("name", "t_med_us", "hbm_GBps", "pct_hbm_peak", "busbw_GBps", "mix_ceiling_GBps",
-            "frac_of_mix_ceiling", "t_cold_med_us", "t_graph_us", "mix_ceiling_128MiB_streams_GBps")
-    out = {k: row[k] for k in keep if k in row}
+    GB/s, busbw, and the fraction of the row's mix ceiling (share of peak
+    and the ceiling itself follow from these); nested stages and latency
+    tables in the same short form.  The full rows go to stderr."""
+    keep = ("name", "t_med_us", "hbm_GBps", "busbw_GBps", "frac_of_mix_ceiling", "t_cold_med_us", "t_graph_us")
+    out = {k: _short(row[k], k) for k in keep if k in row}
     if "stages" in row:
-        out["stages"] = {k: {kk: v[kk] for kk in ("t_med_us", "hbm_GBps", "frac_of_mix_ceiling") if kk in v}
+        out["stages"] = {k: [_short(v.get(f), f) for f in ("t_med_us", "hbm_GBps", "frac_of_mix_ceiling")]
                          for k, v in row["stages"].items()}
+        out["stage_fields"] = ["t_med_us", "hbm_GBps", "frac_of_mix_ceiling"]
     if "table" in row and row["name"] == "other_rank_counts":
-        out["table"] = [{k: v for k, v in e.items() if k == "p" or k.endswith("GBps") or k.endswith("ceiling")}
-                        for e in row["table"]]
+        out["table_fields"] = ["p", "allreduce_GBps", "reduce_scatter_GBps", "allreduce_frac_of_mix_ceiling",
+                               "reduce_scatter_frac_of_mix_ceiling"]
+        out["table"] = [[_short(e.get(k), k) for k in out["table_fields"]] for e in row["table"]]
     elif "table" in row:
-        out["table"] = [{k: v for k, v in e.items() if k.endswith("graph_us") or k == "bytes_per_rank"}
-                        for e in row["table"]]
+        keys = [k for k in row["table"][0] if k.endswith("graph_us")]
+        out["bytes_per_rank"] = [e["bytes_per_rank"] for e in row["table"]]
+        out["graph_us"] = {k[:-len("_graph_us")]: [_short(e[k], k) for e in row["table"]] for k in keys}
     if "individual_calls" in row:
         ic = row["individual_calls"]
-        out["individual_calls"] = {k: ic[k] for k in ("back_to_back_us_per_call", "latency_p50_us",
-                                                     "latency_p99_us", "alpha_us") if k in ic}
+        out["individual_calls"] = {k: _short(ic[k], k) for k in ("back_to_back_us_per_call", "latency_p50_us",
+                                                                "latency_p99_us", "alpha_us") if k in ic}
     for k in ("memcpy_GBps", "coll_GBps", "speedup", "torch_copy_GBps", "coll_copy_kernel_GBps"):
         if k in row:
-            out[k] = row[k]
+            out[k] = _short(row[k], k)
     return out
 
 
