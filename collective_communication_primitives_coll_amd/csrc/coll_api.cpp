@@ -50,8 +50,19 @@ std::atomic<int> g_wg_per_cu{0};
 // 4096 x 7168 tokens, p = 8, top-2.
 // AllGather and Broadcast calls that walk their segments claim their last
 // tiles dynamically and balance best at one workgroup per CU (kFamFanout).
-enum Family { kFamReduce = 0, kFamCopy = 1, kFamRow = 2, kFamFp8 = 3, kFamFp8Direct = 4, kFamFanout = 5 };
-constexpr int kDefaultWgPerCu[6] = {1, 2, 8, 16, 2, 1};
+// The bf16 MoE token copies that claim rows run two per CU (kFamRowClaim):
+// all their workgroups are then resident at once (the row kernels hold at
+// most two waves per SIMD), so the dealt rows start together.
+enum Family {
+  kFamReduce = 0,
+  kFamCopy = 1,
+  kFamRow = 2,
+  kFamFp8 = 3,
+  kFamFp8Direct = 4,
+  kFamFanout = 5,
+  kFamRowClaim = 6
+};
+constexpr int kDefaultWgPerCu[7] = {1, 2, 8, 16, 2, 1, 2};
 // Largest accepted override (coll_set_grid_limit clamps to it).  A CU
 // holds far fewer 256-thread workgroups at once, so larger values would
 // only queue workgroups; the clamp also keeps CUs * limit within int.
@@ -713,6 +724,11 @@ COLL_EXPORT coll_status_t coll_moe_pack(const void* const* tokens, const int32_t
   ra.p = p;
   ra.src_mis = common_mis(tokens, p);
   ra.dst_mis = common_mis((const void* const*)packed, p);
+  ra.claim = stream_claim_slot(stream);
+  if (ra.claim) {
+    e = max_grid(&grid, kFamRowClaim);
+    if (e) return hip_fail(e);
+  }
   return finish(coll::launch_moe_pack((int)d, ra, grid, stream));
 }
 
@@ -1034,8 +1050,13 @@ COLL_EXPORT coll_status_t coll_moe_dispatch(const void* const* tokens, const int
   int grid;
   e = max_grid(&grid, kFamRow);
   if (e) return hip_fail(e);
-  const coll::MoeDirectArgs a =
+  coll::MoeDirectArgs a =
       direct_args(tokens, dest, recv, loc, counts_dev, status_dev, p, tokens_per_rank, k, hidden, recv_cap, hidden);
+  a.claim = stream_claim_slot(stream);
+  if (a.claim) {
+    e = max_grid(&grid, kFamRowClaim);
+    if (e) return hip_fail(e);
+  }
   return finish(coll::launch_moe_dispatch((int)d, a, grid, stream));
 }
 

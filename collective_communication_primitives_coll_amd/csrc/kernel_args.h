@@ -117,6 +117,7 @@ struct MoeRowArgs {
   int dst_mis;
   int res_mis;
   int32_t cap[kMaxRanks];          // direct combine: rows each src[j] holds
+  unsigned long long* claim;       // pack: claim slot (pooled row claims), or null
 };
 
 // Direct dispatch: token rows written straight into the destinations'
@@ -140,6 +141,7 @@ struct MoeDirectArgs {
   int p;
   int src_mis;
   int dst_mis;
+  unsigned long long* claim;       // bf16 dispatch: claim slot (pooled row claims), or null
 };
 
 // Quantized dispatch: FP8 e4m3 rows with one fp32 scale per group of
@@ -277,5 +279,11 @@ constexpr uint64_t kCopyDealtEighths = 2;
 // The uniform 1:1 copies (pair_copy_flat_kernel) deal out this many
 // eighths of their tiles and claim the rest from kClaimPools counters.
 constexpr uint32_t kPairDealtEighths = 4;
+// The MoE token copies (pack, direct dispatch) deal out this many eighths
+// of their rows to the waves in turn and claim the rest one row at a time
+// from kClaimPools counters, given at least kClaimMinRowsPerWave rows per
+// wave.
+constexpr uint64_t kRowDealtEighths = 4;
+constexpr uint64_t kClaimMinRowsPerWave = 4;
 
 }  // namespace coll

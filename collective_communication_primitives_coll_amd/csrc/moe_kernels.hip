@@ -288,7 +288,17 @@ COLL_STREAM_KERNEL void moe_token_copy_kernel(Args a) {
   const bool aligned = RB % 16 == 0 && a.src_mis == 0 && a.dst_mis == 0;
   const uint64_t nvec = RB / 16;
   const uint64_t rows = a.tokens * (uint64_t)a.p;
-  for (uint64_t r = wave_id(); r < rows; r += wave_count()) {
+  const uint64_t nw = wave_count(), w = wave_id();
+  // claimed rows: `per` from each of kClaimPools pools, after `dealt` rows
+  // dealt out in turn (see kRowDealtEighths)
+  const uint32_t pool = (uint32_t)(w % kClaimPools);
+  const uint64_t per = a.claim && rows >= kClaimMinRowsPerWave * nw ? rows / 8 * (8 - kRowDealtEighths) / kClaimPools : 0;
+  const uint64_t dealt = rows - per * kClaimPools;
+  unsigned long long* ctr = per ? a.claim + pool * kClaimPoolWords : nullptr;
+  const unsigned long long first = per ? issue_claim(ctr, lane) : 0;
+  // one row; after_loads(tok) runs once the row's first batch of loads has
+  // returned (tok: an opaque zero produced after them), if there are loads
+  auto copy_row = [&](uint64_t r, auto&& after_loads) {
     const int rank = (int)(r / a.tokens);
     const uint64_t t = r - (uint64_t)rank * a.tokens;
     void* drow[kMaxTopK];
@@ -317,6 +327,11 @@ COLL_STREAM_KERNEL void moe_token_copy_kernel(Args a) {
             if (j < nvec) v[u] = ld16<true>(vs + j);
           }
           __builtin_amdgcn_sched_barrier(0);
+          if (j0 == 0) {
+            uint32_t tok = 0;
+            asm volatile("" : "+v"(tok) : "v"(v[0]));
+            after_loads(tok);
+          }
 #pragma unroll
           for (int s = 0; s < kMaxTopK; ++s) {
             if (!drow[s]) continue;
@@ -342,7 +357,25 @@ COLL_STREAM_KERNEL void moe_token_copy_kernel(Args a) {
       }
     }
     tgt.finish(rank, t * (uint64_t)a.k, loc, lane);
+  };
+  for (uint64_t r = w; r < dealt; r += nw) copy_row(r, [](uint32_t) {});
+  if (!per) return;
+  // the next claim is issued before a row's loads and read once they have
+  // returned (or after the row, when it had none)
+  uint64_t c = wave_value(first);
+  while (c < per) {
+    const unsigned long long next = issue_claim(ctr, lane);
+    uint64_t cn = 0;
+    bool got = false;
+    copy_row(dealt + pool + (uint64_t)kClaimPools * c, [&](uint32_t tok) {
+      cn = wave_value(next + tok);
+      got = true;
+    });
+    if (!got) cn = wave_value(next);
+    asm volatile("" ::"v"(next));  // keep the claim's register out of the stores' reach
+    c = cn;
   }
+  if (lane == 0) claim_last(ctr, c, per, (nw - pool + kClaimPools - 1) / kClaimPools);
 }
 
 // out[rank][t] = residual[rank][t] (or +0) + sum_s w[t*k+s] * back[rank][pos[t*k+s]],

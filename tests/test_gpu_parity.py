@@ -2017,3 +2017,42 @@ def test_claimed_tails_alltoallv(coll, p, dtype):
             got = to_host(recv[j], dtype)
             assert_bits_equal(got[:int(cols[j])], expect[j], f"A2Av p={p} rep {rep} j={j}")
             assert np.all(_bits(got[int(cols[j]):]) == 0x1234), "wrote past the end"
+
+
+@pytest.mark.parametrize("dtype", [BF16, F32])
+def test_claimed_rows_moe_pack_and_dispatch(coll, dtype):
+    """MoE pack and direct dispatch with enough token rows for the pooled
+    row claims (p = 8, 4096 tokens per rank), twice in a row with different
+    routing: packed rows, positions, counts, received rows and locations
+    equal the oracle's."""
+    import torch
+    p, T, k, H = 8, 4096, 2, 72
+    for rep in range(2):
+        toks, routes, _ = _moe_case(p, T, k, H, dtype, 500 + rep)
+        dtok = [to_dev(x, dtype) for x in toks]
+        ddest = [_i32dev(r) for r in routes]
+        packed = [empty(T * k * H, dtype, fill=0x1111) for _ in range(p)]
+        pos = [torch.full((T * k,), -5, dtype=torch.int32, device="cuda") for _ in range(p)]
+        counts = torch.full((p * p,), -1, dtype=torch.int64, device="cuda")
+        coll.coll_moe_pack(dtok, ddest, packed, pos, counts, k, H)
+        sync()
+        c = counts.cpu().numpy().reshape(p, p)
+        for i in range(p):
+            ec, epos, epk = ref.moe_pack(toks[i], routes[i], k, H, p)
+            assert list(c[i]) == list(ec), f"rep {rep} counts rank {i}"
+            assert pos[i].cpu().numpy().tolist() == epos.tolist(), f"rep {rep} pos rank {i}"
+            assert_bits_equal(to_host(packed[i], dtype), epk, f"rep {rep} packed rank {i}")
+        dcounts, slots, recv = ref.moe_dispatch_direct(toks, routes, k, H)
+        rows = dcounts.sum(axis=0) // H
+        cap = [int(r) + 3 for r in rows]
+        drecv = [empty(cp * H, dtype, fill=0x5A5A5A5A) for cp in cap]
+        loc = [torch.full((T * k,), 77, dtype=torch.int64, device="cuda") for _ in range(p)]
+        cdev = torch.full((p * p,), -1, dtype=torch.int64, device="cuda")
+        coll.coll_moe_dispatch(dtok, ddest, drecv, loc, cdev, k, H, recv_cap=cap)
+        sync()
+        assert np.array_equal(cdev.cpu().numpy().reshape(p, p), dcounts)
+        for j in range(p):
+            got = to_host(drecv[j], dtype)
+            assert_bits_equal(got[:int(rows[j]) * H], recv[j], f"rep {rep} direct recv {j}")
+        for i, e in enumerate(_expected_locs(routes, slots)):
+            assert np.array_equal(loc[i].cpu().numpy(), e), f"rep {rep} locations rank {i}"
