@@ -50,9 +50,10 @@ std::atomic<int> g_wg_per_cu{0};
 // 4096 x 7168 tokens, p = 8, top-2.
 // AllGather and Broadcast calls that walk their segments claim their last
 // tiles dynamically and balance best at one workgroup per CU (kFamFanout).
-// The bf16 MoE token copies that claim rows run two per CU (kFamRowClaim):
-// all their workgroups are then resident at once (the row kernels hold at
-// most two waves per SIMD), so the dealt rows start together.
+// The bf16 MoE token copies, which claim rows, run two per CU
+// (kFamRowClaim): all their workgroups are then resident at once (the row
+// kernels hold at most two waves per SIMD), so the dealt rows start
+// together.
 enum Family {
   kFamReduce = 0,
   kFamCopy = 1,

@@ -276,6 +276,15 @@ __device__ __forceinline__ SlotRows<MoeDirectArgs> make_slot_rows(const MoeDirec
 // per rank, p = 8, top-2: 282-284 us against 290-293 us non-temporal, the
 // exchange after it unchanged); the direct dispatch keeps non-temporal
 // ones (290-292 us against 297-303 us with either device-scope policy).
+// Rows: with a claim slot, kRowDealtEighths of them are dealt out to the
+// waves in turn and the rest claimed one row at a time from kClaimPools
+// pooled counters (wave w claims from pool w mod kClaimPools; claim c of
+// pool x is row dealt + x + kClaimPools * c), at two workgroups per CU so
+// that every wave is resident from the start.  Dealt out alone at two per
+// CU, the waves of the pack above ended between 239 and 268 us.  Same-box
+// A/B: pack 276-277 us against 284 us (eight workgroups per CU, dealt),
+// direct dispatch 282-283 against 286 us.  The combines gained nothing
+// from the same claims (328-330 us either way) and deal out every row.
 template <int B, class Args>
 COLL_STREAM_KERNEL void moe_token_copy_kernel(Args a) {
   using W = typename Word<B>::T;

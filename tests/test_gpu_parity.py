@@ -2021,10 +2021,10 @@ def test_claimed_tails_alltoallv(coll, p, dtype):
 
 @pytest.mark.parametrize("dtype", [BF16, F32])
 def test_claimed_rows_moe_pack_and_dispatch(coll, dtype):
-    """MoE pack and direct dispatch with enough token rows for the pooled
-    row claims (p = 8, 4096 tokens per rank), twice in a row with different
-    routing: packed rows, positions, counts, received rows and locations
-    equal the oracle's."""
+    """MoE pack, direct dispatch and both combines with enough token rows for
+    the pooled row claims (p = 8, 4096 tokens per rank), twice in a row with
+    different routing: packed rows, positions, counts, received rows,
+    locations and combined tokens equal the oracle's."""
     import torch
     p, T, k, H = 8, 4096, 2, 72
     for rep in range(2):
@@ -2056,3 +2056,19 @@ def test_claimed_rows_moe_pack_and_dispatch(coll, dtype):
             assert_bits_equal(got[:int(rows[j]) * H], recv[j], f"rep {rep} direct recv {j}")
         for i, e in enumerate(_expected_locs(routes, slots)):
             assert np.array_equal(loc[i].cpu().numpy(), e), f"rep {rep} locations rank {i}"
+        # combine of the packed rows (as if returned unchanged), in place on
+        # a residual, and the direct combine reading the received rows
+        _, _, weights = _moe_case(p, T, k, H, dtype, 500 + rep)
+        dw = [_f32dev(wt) for wt in weights]
+        resid = gen(p, T * H, dtype, 520 + rep)
+        out = [to_dev(x, dtype) for x in resid]
+        coll.coll_moe_combine(packed, pos, dw, out, k, H, residual=out)
+        dout = [empty(T * H, dtype, fill=0) for _ in range(p)]
+        coll.coll_moe_combine_direct(drecv, loc, dw, dout, k, H, y_rows=cap)
+        sync()
+        for i in range(p):
+            _, epos, epk = ref.moe_pack(toks[i], routes[i], k, H, p)
+            expect = ref.moe_combine(epk, epos, weights[i], k, H, dtype, resid[i])
+            assert_bits_equal(to_host(out[i], dtype), expect, f"rep {rep} combine rank {i}")
+            assert_bits_equal(to_host(dout[i], dtype), ref.moe_combine(epk, epos, weights[i], k, H, dtype),
+                              f"rep {rep} direct combine rank {i}")
