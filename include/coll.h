@@ -42,6 +42,14 @@
  * - Thread safety: every entry point may be called from several host
  *   threads, except coll_finalize, which must not run concurrently with
  *   any other call.
+ * - Work balancing: large calls hand part of their tiles (or token rows)
+ *   to workgroups through counters in a static device array, one slot of
+ *   eight counters per stream (assigned on first use, up to 1024 streams
+ *   per device; later streams and hipStreamPerThread deal out all their
+ *   work in turn instead).  Each launch leaves its counters at zero when
+ *   it completes, so the calls of one stream, which run in order, share a
+ *   slot; nothing is allocated for it.  Results do not depend on how the
+ *   work was handed out.
  */
 #ifndef COLL_H_
 #define COLL_H_
