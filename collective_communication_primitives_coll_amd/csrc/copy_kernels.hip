@@ -262,7 +262,7 @@ __device__ __forceinline__ void pair_segment(const RankPtrs& ptrs, const CopyGeo
 // 16 MiB blocks) between 35 and 43 us.  One counter serves about 83 claims
 // per microsecond, fewer than these copies make (a tile moves 32 KiB), so
 // the claimed tiles are split into kClaimPools pools: workgroup b claims
-// from counter b mod kClaimPools, and claim c of pool x is flat tile
+// from the counter of pool claim_pool(b), and claim c of pool x is flat tile
 // dealt + x + kClaimPools * c, so the pools advance through the same
 // region together.  (Claiming runs of 8 consecutive tiles from one counter
 // had been 10% slower for All-to-All and 27% for Gather and Scatter.)
@@ -276,7 +276,7 @@ COLL_STREAM_KERNEL void pair_copy_flat_kernel(RankPtrs ptrs, CopyGeom g, uint64_
   // claims: per tiles from each pool, the first `dealt` tiles dealt out
   const uint32_t per = g.claim ? total / 8 * (8 - kPairDealtEighths) / kClaimPools : 0;
   const uint32_t dealt = total - per * kClaimPools;
-  const uint32_t pool = blockIdx.x % kClaimPools;
+  const uint32_t pool = claim_pool(blockIdx.x);
   unsigned long long* ctr = g.claim ? g.claim + pool * kClaimPoolWords : nullptr;
   unsigned long long first = 0;
   if (per) first = issue_claim(ctr, (int)threadIdx.x);
@@ -348,9 +348,7 @@ COLL_STREAM_KERNEL void pair_copy_flat_kernel(RankPtrs ptrs, CopyGeom g, uint64_
     c = next_tile[par];
     par ^= 1;
   }
-  // the workgroups of pool `pool`: b < gridDim.x with b mod kClaimPools == pool
-  const uint64_t workers = (gridDim.x - pool + kClaimPools - 1) / kClaimPools;
-  if (threadIdx.x == 0) claim_last(ctr, c, per, workers);
+  if (threadIdx.x == 0) claim_last(ctr, c, per, claim_pool_members(gridDim.x, pool));
 }
 
 // ---------------------------------------------------------------------------
@@ -509,10 +507,11 @@ COLL_STREAM_KERNEL void alltoallv_flat_kernel(RankPtrs ptrs, A2avArgs a) {
     }
   };
   const uint64_t total0 = tstart[0][pp], total = total0 + tstart[1][pp];
-  const bool claims = a.claim && total0 >= kClaimMinTilesPerWg * gridDim.x && gridDim.x >= 4 * kClaimPools;
+  const bool claims =
+      a.claim && total0 >= kClaimMinTilesPerWg * gridDim.x && gridDim.x >= (uint32_t)(kClaimPools * kClaimPools);
   const uint64_t per = claims ? total0 / 8 * (8 - kPairDealtEighths) / kClaimPools : 0;
   const uint64_t dealt0 = total0 - per * kClaimPools;
-  const uint32_t pool = blockIdx.x % kClaimPools;
+  const uint32_t pool = claim_pool(blockIdx.x);
   unsigned long long* ctr = per ? a.claim + pool * kClaimPoolWords : nullptr;
   unsigned long long first = 0;
   if (per) first = issue_claim(ctr, tid);
@@ -583,8 +582,7 @@ COLL_STREAM_KERNEL void alltoallv_flat_kernel(RankPtrs ptrs, A2avArgs a) {
     c = next_tile[par];
     par ^= 1;
   }
-  const uint64_t workers = (gridDim.x - pool + kClaimPools - 1) / kClaimPools;
-  if (tid == 0) claim_last(ctr, c, per, workers);
+  if (tid == 0) claim_last(ctr, c, per, claim_pool_members(gridDim.x, pool));
 }
 
 // ---------------------------------------------------------------------------
@@ -688,7 +686,7 @@ static int launch_copy_b(const RankPtrs& ptrs, const CopyGeom& g, int max_grid, 
       // claims only with enough whole tiles per workgroup and every pool
       // served by several workgroups
       CopyGeom gc = g;
-      if (tiles < kClaimMinTilesPerWg * (uint64_t)grid || grid < 4 * kClaimPools) gc.claim = nullptr;
+      if (tiles < kClaimMinTilesPerWg * (uint64_t)grid || grid < kClaimPools * kClaimPools) gc.claim = nullptr;
       if (g.kind == kCopyAllToAll)
         hipLaunchKernelGGL((pair_copy_flat_kernel<B, kCopyAllToAll>), dim3(grid), dim3(kBlock), 0, s, ptrs, gc, head,
                            nvec, tail, t32);

@@ -389,6 +389,20 @@ __device__ __forceinline__ void store_tile(u32x4* dst, uint64_t j0, uint64_t nve
   }
 }
 
+// Pooled claims: the pool of workgroup b.  Runs of kClaimPools consecutive
+// workgroups share a pool, so that every pool draws its workgroups from
+// all XCDs (workgroups are dispatched to the XCDs in turn, and some XCDs
+// stream a few percent slower than others).  Needs at least
+// kClaimPools^2 workgroups for every pool to have one.
+__device__ __forceinline__ uint32_t claim_pool(uint32_t b) { return (b / kClaimPools) % kClaimPools; }
+// The number of workgroups among the first n in pool x.
+__device__ __forceinline__ uint64_t claim_pool_members(uint64_t n, uint32_t x) {
+  constexpr uint64_t span = (uint64_t)kClaimPools * kClaimPools;
+  const uint64_t rem = n % span, lo = (uint64_t)x * kClaimPools;
+  const uint64_t extra = rem > lo ? (rem - lo < (uint64_t)kClaimPools ? rem - lo : (uint64_t)kClaimPools) : 0;
+  return n / span * kClaimPools + extra;
+}
+
 // A worker whose claim v came back past the last of `units` units: if it
 // was the launch's last claim, zero the counter.
 __device__ __forceinline__ void claim_last(unsigned long long* slot, uint64_t v, uint64_t units,

@@ -278,8 +278,8 @@ __device__ __forceinline__ SlotRows<MoeDirectArgs> make_slot_rows(const MoeDirec
 // ones (290-292 us against 297-303 us with either device-scope policy).
 // Rows: with a claim slot, kRowDealtEighths of them are dealt out to the
 // waves in turn and the rest claimed one row at a time from kClaimPools
-// pooled counters (wave w claims from pool w mod kClaimPools; claim c of
-// pool x is row dealt + x + kClaimPools * c), at two workgroups per CU so
+// pooled counters (the waves of workgroup b claim from pool claim_pool(b);
+// claim c of pool x is row dealt + x + kClaimPools * c), at two workgroups per CU so
 // that every wave is resident from the start.  Dealt out alone at two per
 // CU, the waves of the pack above ended between 239 and 268 us.  Same-box
 // A/B: pack 276-277 us against 284 us (eight workgroups per CU, dealt),
@@ -300,8 +300,10 @@ COLL_STREAM_KERNEL void moe_token_copy_kernel(Args a) {
   const uint64_t nw = wave_count(), w = wave_id();
   // claimed rows: `per` from each of kClaimPools pools, after `dealt` rows
   // dealt out in turn (see kRowDealtEighths)
-  const uint32_t pool = (uint32_t)(w % kClaimPools);
-  const uint64_t per = a.claim && rows >= kClaimMinRowsPerWave * nw ? rows / 8 * (8 - kRowDealtEighths) / kClaimPools : 0;
+  const uint32_t pool = claim_pool(blockIdx.x);
+  const uint64_t per = a.claim && rows >= kClaimMinRowsPerWave * nw && gridDim.x >= (uint32_t)(kClaimPools * kClaimPools)
+                           ? rows / 8 * (8 - kRowDealtEighths) / kClaimPools
+                           : 0;
   const uint64_t dealt = rows - per * kClaimPools;
   unsigned long long* ctr = per ? a.claim + pool * kClaimPoolWords : nullptr;
   const unsigned long long first = per ? issue_claim(ctr, lane) : 0;
@@ -384,7 +386,7 @@ COLL_STREAM_KERNEL void moe_token_copy_kernel(Args a) {
     asm volatile("" ::"v"(next));  // keep the claim's register out of the stores' reach
     c = cn;
   }
-  if (lane == 0) claim_last(ctr, c, per, (nw - pool + kClaimPools - 1) / kClaimPools);
+  if (lane == 0) claim_last(ctr, c, per, (kBlock / kWaveLanes) * claim_pool_members(gridDim.x, pool));
 }
 
 // out[rank][t] = residual[rank][t] (or +0) + sum_s w[t*k+s] * back[rank][pos[t*k+s]],
