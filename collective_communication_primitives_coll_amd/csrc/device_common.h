@@ -282,14 +282,16 @@ __device__ __forceinline__ uint32_t first_tile32(uint64_t base, uint32_t wg, uin
 // ReduceScatter or AllReduce 3-5% after the others, and an AllGather's
 // workgroups finish anywhere between 40% and 100% of the kernel's time.
 // So the streaming kernels deal out part of their tiles in turn and let
-// the workers (workgroups, or waves in the batch) claim the rest, one at a
-// time, from a counter: a worker that runs ahead claims more.  Each launch
-// gets a counter slot, zero at launch.  Every worker claims until a claim
-// comes back past the last unit, so a launch with `units` claimable units
-// and W workers makes exactly units + W claims; the worker whose claim
-// returns units + W - 1 makes the last one and zeroes the counter for the
-// next launch that uses the slot (claim_last), without waiting for the
-// other workers to finish their tiles.
+// the workers (workgroups, or waves) claim the rest, one at a time, from a
+// counter: a worker that runs ahead claims more.  Each launch gets a
+// counter slot, zero at launch; the 1:1 copies, Alltoallv, the MoE token
+// copies and AllReduce at p = 8 split their claimed work over the slot's
+// kClaimPools counters (claim_pool), the other kernels use one counter.  Every worker claims until a claim comes back past the last
+// unit of its counter, so a counter with `units` claimable units and W
+// workers takes exactly units + W claims; the worker whose claim returns
+// units + W - 1 makes the last one and zeroes the counter for the next
+// launch that uses the slot (claim_last), without waiting for the other
+// workers to finish their tiles.
 // ---------------------------------------------------------------------------
 constexpr int kWave = 64;  // lanes of a wave
 

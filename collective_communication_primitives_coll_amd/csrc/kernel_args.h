@@ -227,10 +227,10 @@ int noalloc_scratch(int dev, void** out);
 // Claim slots (claim_slots.hip): kClaimSlots slots in a static device
 // array per GPU, each of kClaimPools counters kClaimPoolWords 64-bit words
 // apart (one 128-byte line each).  claim_slots_base gives device dev's
-// array (dev current).  AllReduce, ReduceScatter, AllGather and
-// Broadcast launches with at least kClaimMinTilesPerWg tiles per
-// workgroup use the slot's first counter; the uniform 1:1 copies use all
-// kClaimPools of them.
+// array (dev current).  Launches with at least kClaimMinTilesPerWg tiles
+// per workgroup use their slot: the uniform 1:1 copies, Alltoallv, the MoE
+// token copies and AllReduce at p = 8 all kClaimPools counters of it, the
+// other reductions and AllGather and Broadcast at p >= 8 the first.
 constexpr int kClaimSlots = 1024;
 constexpr int kClaimPools = 8;
 constexpr int kClaimPoolWords = 16;

@@ -77,18 +77,23 @@ __device__ __forceinline__ void probe_tile(const u32x4* const (&src)[NS > 0 ? NS
   }
 }
 
-// claim: null to deal out every tile in turn, else a claim slot: a quarter
-// of the tiles dealt out in turn and the rest claimed one at a time by
-// workgroups, as the reductions and fan-outs do (thread 0 claims before a
-// tile's loads and publishes after them through LDS).
+// claim: null to deal out every tile in turn, else a claim slot: about a
+// quarter of the tiles dealt out in turn and the rest claimed one at a time
+// by workgroups from the slot's kClaimPools pooled counters, as the 1:1
+// copies claim theirs (workgroup b from pool claim_pool(b); claim c of pool
+// x is tile dealt + x + kClaimPools * c).  Thread 0 claims before a tile's
+// loads and publishes after them through LDS.
 template <int NS, int ND, bool NTL, int SP, int U>
 COLL_STREAM_KERNEL void probe_kernel(RankPtrs ptrs, uint64_t nvec, u32x4* sink, uint32_t pattern,
                                      unsigned long long* claim) {
   constexpr uint64_t TV = (uint64_t)U * kBlock;
   const uint64_t nt = ceil_div(nvec, TV), nfull = nvec / TV;
-  const uint64_t dealt = claim ? dealt_tiles(nfull, gridDim.x) : nt;
+  const uint64_t per = claim ? (nfull - dealt_tiles(nfull, gridDim.x)) / kClaimPools : 0;
+  const uint64_t dealt = claim ? nfull - per * kClaimPools : nt;
+  const uint32_t pool = claim_pool(blockIdx.x);
+  unsigned long long* ctr = claim ? claim + pool * kClaimPoolWords : nullptr;
   unsigned long long first = 0;
-  if (claim) first = issue_claim(claim, (int)threadIdx.x);
+  if (claim) first = issue_claim(ctr, (int)threadIdx.x);
   const u32x4* src[NS > 0 ? NS : 1];
   u32x4* dst[ND > 0 ? ND : 1];
 #pragma unroll
@@ -110,9 +115,8 @@ COLL_STREAM_KERNEL void probe_kernel(RankPtrs ptrs, uint64_t nvec, u32x4* sink, 
   __syncthreads();
   uint64_t u = next_tile[0];
   int par = 1;
-  const uint64_t units = nfull - dealt;
-  while (u < units) {
-    const unsigned long long next = issue_claim(claim, (int)threadIdx.x);
+  while (u < per) {
+    const unsigned long long next = issue_claim(ctr, (int)threadIdx.x);
     const auto publish = [&](uint32_t tok) {
       const uint64_t v = wave_value(next + tok);
       if (threadIdx.x == 0) next_tile[par] = v;
@@ -123,13 +127,14 @@ COLL_STREAM_KERNEL void probe_kernel(RankPtrs ptrs, uint64_t nvec, u32x4* sink, 
     for (int k = 0; k < NS; ++k) gs[k] = as_global(src[k]);
 #pragma unroll
     for (int d = 0; d < ND; ++d) gd[d] = as_global(dst[d]);
-    probe_tile<NS, ND, NTL, SP, U, true>(gs, gd, (dealt + u) * TV + threadIdx.x, nvec, sink, pattern, publish);
+    probe_tile<NS, ND, NTL, SP, U, true>(gs, gd, (dealt + pool + (uint64_t)kClaimPools * u) * TV + threadIdx.x, nvec,
+                                         sink, pattern, publish);
     asm volatile("" ::"v"(next));  // keep the claim's register out of the stores' reach
     __syncthreads();
     u = next_tile[par];
     par ^= 1;
   }
-  if (threadIdx.x == 0) claim_last(claim, u, units, gridDim.x);
+  if (threadIdx.x == 0) claim_last(ctr, u, per, claim_pool_members(gridDim.x, pool));
 }
 
 // The (sources, destinations) mixes the benchmark measures.
@@ -158,8 +163,10 @@ static int launch_mix_u(const RankPtrs& ptrs, uint64_t nvec, bool ntl, int sp, v
     u32x4* sk = (u32x4*)sink;
     const uint32_t pat = 0x9e3779b9u;
     const dim3 g(grid), b(kBlock);
-    // claims only with enough whole tiles per workgroup
-    unsigned long long* cl = nvec / TV >= kClaimMinTilesPerWg * (uint64_t)grid ? claim : nullptr;
+    // claims only with enough whole tiles per workgroup, and a workgroup in
+    // every pool
+    unsigned long long* cl =
+        nvec / TV >= kClaimMinTilesPerWg * (uint64_t)grid && grid >= kClaimPools * kClaimPools ? claim : nullptr;
     if (ntl == false && sp == kStPlain)
       hipLaunchKernelGGL((probe_kernel<NS, ND, false, kStPlain, U>), g, b, 0, s, ptrs, nvec, sk, pat, cl);
     else if (ntl == false && sp == kStNT)

@@ -100,9 +100,10 @@ struct SegGeom {
 //   live past the tile's stores, so the loop waits for nothing the dealt
 //   loop does not.
 // - Claims only grow, so the segment cursor only moves forward.
-template <int DT, int OP, int P, int ORD, int DMODE>
+template <int DT, int OP, int P, int ORD, int DMODE, uint32_t NPOOLS>
 __device__ __forceinline__ void reduce_claimed(const RankPtrs& ptrs, const ReduceGeom& g, uint64_t dealt,
-                                               uint64_t total, unsigned long long first) {
+                                               uint64_t per, uint32_t pool, unsigned long long* ctr,
+                                               unsigned long long first) {
   using T = Traits<DT>;
   using S = typename T::S;
   constexpr bool ALL = DMODE == kDstAll;
@@ -115,7 +116,6 @@ __device__ __forceinline__ void reduce_claimed(const RankPtrs& ptrs, const Reduc
   const uint64_t first_tile_claimed = wave_value(first);
   if (threadIdx.x == 0) next_tile[0] = first_tile_claimed;
   __syncthreads();
-  const uint64_t units = total - dealt;
   uint64_t u = next_tile[0];
   int par = 1;
   int c = -1;
@@ -124,12 +124,12 @@ __device__ __forceinline__ void reduce_claimed(const RankPtrs& ptrs, const Reduc
   const S* src[P];
   S* dst[ND];
   Scales<P> sc;
-  while (u < units) {
+  while (u < per) {
     // thread 0 claims; every wave reads its own value of `next` in the
     // hook (only thread 0's is a claim), so that no path leaves the atomic
     // unread when the register is set again in the next iteration
-    const unsigned long long next = issue_claim(g.claim, (int)threadIdx.x);
-    const uint64_t f = dealt + u;
+    const unsigned long long next = issue_claim(ctr, (int)threadIdx.x);
+    const uint64_t f = dealt + pool + (uint64_t)NPOOLS * u;
     if (f >= cbase + cnt) {
       // f < total, the sum of the segments' tile counts, so a segment
       // below P holds it (the bound on c only keeps reads in range)
@@ -174,7 +174,7 @@ __device__ __forceinline__ void reduce_claimed(const RankPtrs& ptrs, const Reduc
     u = next_tile[par];
     par ^= 1;
   }
-  if (threadIdx.x == 0) claim_last(g.claim, u, units, gridDim.x);
+  if (threadIdx.x == 0) claim_last(ctr, u, per, NPOOLS > 1 ? claim_pool_members(gridDim.x, pool) : gridDim.x);
 }
 
 template <int DT, int OP, int P, int ORD, int DMODE>
@@ -183,18 +183,28 @@ COLL_STREAM_KERNEL void reduce_kernel(RankPtrs ptrs, ReduceGeom g) {
   using S = typename T::S;
   constexpr bool ALL = DMODE == kDstAll;
   constexpr int ND = ALL ? P : 1;
-  // With a claim slot, a quarter of the tiles are dealt out in turn and the
-  // rest claimed (reduce_claimed); the workgroup's first claim is issued
-  // now and read after its dealt tiles.
-  uint64_t dealt = ~0ull, total = 0;
+  // With a claim slot, about a quarter of the tiles are dealt out in turn
+  // and the rest claimed (reduce_claimed); the workgroup's first claim is
+  // issued now and read after its dealt tiles.  AllReduce at p = 8 claims
+  // from the slot's kClaimPools pooled counters (workgroup b from pool
+  // claim_pool(b), claim c of pool x being tile dealt + x + kClaimPools * c),
+  // the other calls from its first counter.  Same-box A/B, pooled against
+  // one counter, AllReduce of 256 MiB fp32 per rank: p = 8 713-714 against
+  // 737 us; p = 2 169 against 169, p = 4 354 against 350, p = 12 1132-1136
+  // against 1074, p = 16 1544-1580 against 1446-1455 us; ReduceScatter and
+  // AllGather within 1% or slower with pools.
+  constexpr uint32_t NPOOLS = (ALL && P == 8) ? (uint32_t)kClaimPools : 1u;
+  uint64_t dealt = ~0ull, total = 0, per = 0;
   unsigned long long first = 0;
+  const uint32_t pool = NPOOLS > 1 ? claim_pool(blockIdx.x) : 0u;
   // AllReduce and ReduceScatter.  Same-box A/Bs against tiles all dealt
   // out: AllReduce 5-7% faster at p = 8 (256 MiB fp32 per rank) and 6-9%
   // at p = 3, 5, 6, 7, 12; ReduceScatter 3-4% faster at p = 8 (2^26 bf16
   // per rank) and within 1% either way at the other counts.
   const bool claims = (ALL || DMODE == kDstOwner) && g.claim;
+  unsigned long long* ctr = claims ? g.claim + pool * kClaimPoolWords : nullptr;  // pool 0: the first counter
   if (claims) {
-    first = issue_claim(g.claim, (int)threadIdx.x);
+    first = issue_claim(ctr, (int)threadIdx.x);
     // only whole vector tiles are claimed: with a segment on the element
     // path (buffers that disagree modulo 16) every tile is dealt out
     bool vec = true;
@@ -203,7 +213,8 @@ COLL_STREAM_KERNEL void reduce_kernel(RankPtrs ptrs, ReduceGeom g) {
       total += s.nt;
       vec = vec && (s.sp.vec || s.len == 0);
     }
-    dealt = vec ? dealt_tiles(total, gridDim.x) : total;
+    per = vec ? (total - dealt_tiles(total, gridDim.x)) / NPOOLS : 0;
+    dealt = total - per * NPOOLS;
   }
   uint64_t base = 0;
   for (int c = 0; c < P; ++c) {
@@ -226,7 +237,7 @@ COLL_STREAM_KERNEL void reduce_kernel(RankPtrs ptrs, ReduceGeom g) {
     base += reduce_segment<DT, OP, P, ORD, ND, ALL>(src, dst, len, mis, amis, base, sc, P, lim);
   }
   if constexpr (ALL || DMODE == kDstOwner) {
-    if (claims) reduce_claimed<DT, OP, P, ORD, DMODE>(ptrs, g, dealt, total, first);
+    if (claims) reduce_claimed<DT, OP, P, ORD, DMODE, NPOOLS>(ptrs, g, dealt, per, pool, ctr, first);
   }
 }
 
@@ -447,7 +458,7 @@ static int launch_p(const RankPtrs& ptrs, const ReduceGeom& g, int max_grid, hip
     const uint64_t tiles = count_tiles<DT, P, true>(g);
     const int grid = clamp_grid(tiles, max_grid);
     ReduceGeom gk = g;
-    if (tiles < kClaimMinTilesPerWg * (uint64_t)grid) gk.claim = nullptr;
+    if (tiles < kClaimMinTilesPerWg * (uint64_t)grid || grid < kClaimPools * kClaimPools) gk.claim = nullptr;
     if (grid)
       hipLaunchKernelGGL((reduce_kernel<DT, OP, P, ORD, kDstAll>), dim3(grid), dim3(kBlock), 0, s, ptrs, gk);
     return (int)hipGetLastError();
@@ -459,7 +470,8 @@ static int launch_p(const RankPtrs& ptrs, const ReduceGeom& g, int max_grid, hip
     const int grid = clamp_grid(count_tiles<DT, P, false>(g), max_grid);
     if (!grid) return 0;
     ReduceGeom gk = g;
-    if (g.dst_mode != kDstOwner || count_tiles<DT, P, false>(g) < kClaimMinTilesPerWg * (uint64_t)grid)
+    if (g.dst_mode != kDstOwner || count_tiles<DT, P, false>(g) < kClaimMinTilesPerWg * (uint64_t)grid ||
+        grid < kClaimPools * kClaimPools)
       gk.claim = nullptr;  // claimed tails are for AllReduce and ReduceScatter
     if (g.dst_mode == kDstOwner)
       hipLaunchKernelGGL((reduce_kernel<DT, OP, P, ORD, kDstOwner>), dim3(grid), dim3(kBlock), 0, s, ptrs, gk);

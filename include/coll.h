@@ -441,11 +441,11 @@ coll_status_t coll_allreduce_batch_noalloc(const coll_call_t* calls, int ncalls,
  * of device scope, written through the L2 as ReduceScatter and Reduce
  * store (with COLL_PROBE_NT_STORES: non-temporal stores of device scope,
  * as AllGather and Broadcast at p >= 2 store);
- * COLL_PROBE_CLAIM deals out a quarter of
- * the tiles in turn and lets workgroups claim the rest one at a time, as
- * the large AllReduce, ReduceScatter, AllGather and Broadcast calls do
- * (with at least 8 whole tiles per workgroup; else every tile is dealt
- * out).  Supported (nsrc, ndst): (1|4|8|16, 0),
+ * COLL_PROBE_CLAIM deals out about a quarter
+ * of the tiles in turn and lets workgroups claim the rest one at a time
+ * from eight pooled counters, as the large copies and reductions balance
+ * their work (with at least 8 whole tiles per workgroup and 64 workgroups;
+ * else every tile is dealt out).  Supported (nsrc, ndst): (1|4|8|16, 0),
  * (0, 1|4|8|16), (1|2|3|4|5|6|7|8|12|16, 1), (1, 2|4|8|16) and (k, k) for
  * k in 3, 4, 5, 6, 7, 8, 12, 16; other pairs and tile sizes return
  * COLL_ERR_UNSUPPORTED.  Every pointer
