@@ -28,20 +28,22 @@ __device__ __forceinline__ int fanout_mis(const CopyGeom& g, int s) {
   return g.dst_mis < 0 ? -1 : (int)((g.dst_mis + dst_off * B) & 15);
 }
 
-// The claimed tiles [dealt, total) of fanout_kernel, one workgroup tile per
-// claim, as reduce_claimed does for the reductions (thread 0 claims before
-// the tile's loads and publishes after them through LDS; only whole
-// vector tiles are claimed).
-template <int B, int KIND, int P>
+// The claimed tiles of fanout_kernel (tiles of FU vectors per lane), one
+// workgroup tile per claim from the workgroup's pool (claim c of pool x is
+// tile dealt + x + kClaimPools * c), as reduce_claimed does for the
+// reductions (thread 0 claims before the tile's loads and publishes after
+// them through LDS; only whole vector tiles are claimed).
+template <int B, int KIND, int P, int FU>
 __device__ __forceinline__ void fanout_claimed(const RankPtrs& ptrs, const CopyGeom& g, uint64_t dealt,
-                                               uint64_t total, unsigned long long first) {
+                                               uint64_t per, uint32_t pool, unsigned long long* ctr,
+                                               unsigned long long first) {
   using W = typename Word<B>::T;
   constexpr int NSEG = KIND == kCopyAllGather ? P : 1;
   __shared__ uint64_t next_tile[2];
   const uint64_t first_claim = wave_value(first);
   if (threadIdx.x == 0) next_tile[0] = first_claim;
   __syncthreads();
-  const uint64_t units = total - dealt;
+  constexpr uint64_t TVF = (uint64_t)FU * kBlock;  // vectors of a tile
   uint64_t u = next_tile[0];
   int par = 1;
   int s = -1;
@@ -49,15 +51,15 @@ __device__ __forceinline__ void fanout_claimed(const RankPtrs& ptrs, const CopyG
   SegSpan sp{};
   const W* src = nullptr;
   W* dst[P];
-  while (u < units) {
-    const unsigned long long next = issue_claim(g.claim, (int)threadIdx.x);
-    const uint64_t f = dealt + u;
+  while (u < per) {
+    const unsigned long long next = issue_claim(ctr, (int)threadIdx.x);
+    const uint64_t f = dealt + pool + (uint64_t)kClaimPools * u;
     if (f >= sbase + cnt) {
       do {
         sbase += cnt;
         ++s;
         sp = seg_span<B>(g.n, fanout_mis<B, KIND>(g, s));
-        cnt = copy_segment_tiles<B>(sp, g.n);
+        cnt = copy_segment_tiles<B, FU>(sp, g.n);
       } while (f >= sbase + cnt && s < NSEG - 1);  // the bound only keeps reads in range
       const uint64_t dst_off = KIND == kCopyAllGather ? (uint64_t)s * g.n : 0;
       src = (const W*)ptrs.src[KIND == kCopyAllGather ? s : 0] + sp.head;
@@ -69,7 +71,7 @@ __device__ __forceinline__ void fanout_claimed(const RankPtrs& ptrs, const CopyG
       const uint64_t v = wave_value(next + tok);
       if (threadIdx.x == 0) next_tile[par] = v;
     };
-    if (t < sp.nvec / kCopyTV) {
+    if (t < sp.nvec / TVF) {
       // pointers carried across iterations lose their address space:
       // restate it so the tile uses global, not flat, instructions
       const u32x4* vs = reinterpret_cast<const u32x4*>(as_global(src));
@@ -77,7 +79,7 @@ __device__ __forceinline__ void fanout_claimed(const RankPtrs& ptrs, const CopyG
 #pragma unroll
       for (int k = 0; k < P; ++k) vd[k] = reinterpret_cast<u32x4*>(as_global(dst[k]));
       auto gdst = [&](int d) -> u32x4* { return vd[d]; };
-      copy_vec_tile<P == 1, true, P>(vs, gdst, P, t * kCopyTV + threadIdx.x, sp.nvec, publish);
+      copy_vec_tile<P == 1, true, P, FU>(vs, gdst, P, t * TVF + threadIdx.x, sp.nvec, publish);
     } else {
       publish(0);
     }
@@ -86,16 +88,23 @@ __device__ __forceinline__ void fanout_claimed(const RankPtrs& ptrs, const CopyG
     u = next_tile[par];
     par ^= 1;
   }
-  if (threadIdx.x == 0) claim_last(g.claim, u, units, gridDim.x);
+  if (threadIdx.x == 0) claim_last(ctr, u, per, claim_pool_members(gridDim.x, pool));
 }
 
-// Fan-outs claim tiles at compile-time rank counts of 8 and 16 only: a
-// tile then moves (1 + p) * 16 KiB >= 144 KiB, so one claim per tile stays
-// well under what a single counter serves (about 83 claims per
-// microsecond, 12 ns each).  At p = 1 (a 32 KiB tile) claiming every tile
-// capped a 1 GiB copy at about 3 TB/s.
+// Fan-outs claim tiles at compile-time rank counts of 8 and 16 only, where
+// a tile moves (1 + p) * 8 KiB >= 72 KiB (tiles of kFanoutUnroll vectors
+// per lane), from the pooled counters.  At p = 1 (a 32 KiB tile) claiming
+// every tile from one counter (about 83 claims per microsecond, 12 ns
+// each) capped a 1 GiB copy at about 3 TB/s.
 template <int P>
 constexpr bool kFanoutClaims = P >= 8;
+// Vectors per lane of a claiming fan-out's tile, with claims from the
+// pooled counters.  AllGather p = 8, 16 MiB bf16 shards, same-box A/B:
+// 4 per lane and one counter 171-172 us; with pools, 4 per lane 174-175,
+// 2 per lane 163-164, 1 per lane 177-185 us.  (The other copies keep 4:
+// at 2, All-to-All took 153 against 146 us and Alltoallv 183-186 against
+// 155-156 us.)
+constexpr int kFanoutUnroll = 2;
 
 // AllGather / Broadcast with a compile-time rank count P (0: any).
 // Destination pointers of a segment are read once into registers.  With
@@ -110,18 +119,22 @@ COLL_STREAM_KERNEL void fanout_kernel(RankPtrs ptrs, CopyGeom g) {
   constexpr bool CLAIMS = kFanoutClaims<P> && !SHIFT;
   const int p = P ? P : g.p;
   const int nseg = KIND == kCopyAllGather ? p : 1;
-  uint64_t dealt = ~0ull, total = 0;
+  constexpr int FU = CLAIMS ? kFanoutUnroll : kCopyU;  // vectors per lane of a tile
+  uint64_t dealt = ~0ull, total = 0, per = 0;
   unsigned long long first = 0;
   const bool claims = CLAIMS && g.claim;
+  const uint32_t pool = claim_pool(blockIdx.x);
+  unsigned long long* ctr = claims ? g.claim + pool * kClaimPoolWords : nullptr;
   if (claims) {
-    first = issue_claim(g.claim, (int)threadIdx.x);
+    first = issue_claim(ctr, (int)threadIdx.x);
     bool vec = true;
     for (int s = 0; s < nseg; ++s) {
       const SegSpan sp = seg_span<B>(g.n, fanout_mis<B, KIND>(g, s));
-      total += copy_segment_tiles<B>(sp, g.n);
+      total += copy_segment_tiles<B, FU>(sp, g.n);
       vec = vec && (sp.vec || g.n == 0);
     }
-    dealt = vec ? total / 8 * kCopyDealtEighths / gridDim.x * gridDim.x : total;
+    per = vec ? (total - total / 8 * kCopyDealtEighths / gridDim.x * gridDim.x) / kClaimPools : 0;
+    dealt = total - per * kClaimPools;
   }
   uint64_t base = 0;
   for (int s = 0; s < nseg; ++s) {
@@ -129,7 +142,7 @@ COLL_STREAM_KERNEL void fanout_kernel(RankPtrs ptrs, CopyGeom g) {
     const int mis = fanout_mis<B, KIND>(g, s);
     const uint64_t lim = dealt > base ? dealt - base : 0;
     uint64_t nt;
-    if (!copy_segment_owned<B>(g.n, mis, base, &nt, lim)) {
+    if (!copy_segment_owned<B, FU>(g.n, mis, base, &nt, lim)) {
       base += nt;
       continue;
     }
@@ -139,14 +152,14 @@ COLL_STREAM_KERNEL void fanout_kernel(RankPtrs ptrs, CopyGeom g) {
 #pragma unroll
       for (int k = 0; k < P; ++k) dst[k] = (W*)ptrs.dst[k] + dst_off;
       auto gdst = [&](int d) -> W* { return dst[d]; };
-      base += copy_segment<B, P == 1, P, SHIFT>(src, gdst, P, g.n, mis, base, lim);
+      base += copy_segment<B, P == 1, P, SHIFT, FU>(src, gdst, P, g.n, mis, base, lim);
     } else {
       auto gdst = [&](int d) -> W* { return (W*)ptrs.dst[d] + dst_off; };
       base += copy_segment<B, false, 0, SHIFT>(src, gdst, p, g.n, mis, base);
     }
   }
   if constexpr (CLAIMS) {
-    if (claims) fanout_claimed<B, KIND, P>(ptrs, g, dealt, total, first);
+    if (claims) fanout_claimed<B, KIND, P, FU>(ptrs, g, dealt, per, pool, ctr, first);
   }
 }
 
@@ -643,7 +656,8 @@ static void launch_walking(const RankPtrs& ptrs, const CopyGeom& g0, int grid, h
   const uint64_t te = kCopyTV * (16 / B);
   const uint64_t nseg = g.kind == kCopyAllGather ? (uint64_t)g.p : 1;
   if (g.kind != kCopyAllGather && g.kind != kCopyBroadcast) g.claim = nullptr;
-  if (nseg * ((g.n + te - 1) / te) < kClaimMinTilesPerWg * (uint64_t)grid) g.claim = nullptr;
+  if (nseg * ((g.n + te - 1) / te) < kClaimMinTilesPerWg * (uint64_t)grid || grid < kClaimPools * kClaimPools)
+    g.claim = nullptr;
   if (g.kind == kCopyAllToAll)
     hipLaunchKernelGGL((pair_copy_kernel<B, kCopyAllToAll, SHIFT>), dim3(grid), dim3(kBlock), 0, s, ptrs, g);
   else if (g.kind == kCopyGather)

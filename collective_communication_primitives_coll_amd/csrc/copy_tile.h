@@ -36,13 +36,13 @@ constexpr uint64_t kCopyTV = (uint64_t)kCopyU * kBlock;  // vectors per copy til
 // j0 = tile * kCopyTV + lane.  hook(tok) runs once the loads have returned,
 // before the stores (as in reduce_vec_tile; tok is an opaque zero that
 // keeps what the hook reads after the loads).
-template <bool NTL, bool FULL, int ND, typename GD, typename Hook = NoHook>
+template <bool NTL, bool FULL, int ND, int CU = kCopyU, typename GD, typename Hook = NoHook>
 __device__ __forceinline__ void copy_vec_tile(const u32x4* src, const GD& gdst, int nd, uint64_t j0,
                                               uint64_t nvec, const Hook& hook = Hook{}) {
   constexpr bool kHook = !std::is_same<Hook, NoHook>::value;
-  u32x4 r[kCopyU];
+  u32x4 r[CU];
 #pragma unroll
-  for (int u = 0; u < kCopyU; ++u) {
+  for (int u = 0; u < CU; ++u) {
     const uint64_t j = j0 + (uint64_t)u * kBlock;
     if (FULL || j < nvec) r[u] = ld16<NTL>(src + j);
     else if (kHook) r[u] = u32x4{0, 0, 0, 0};  // defined input for the hook's token
@@ -50,7 +50,7 @@ __device__ __forceinline__ void copy_vec_tile(const u32x4* src, const GD& gdst, 
   __builtin_amdgcn_sched_barrier(0);  // all loads of the tile before the first store
   if constexpr (kHook) {
     uint32_t tok = 0;
-    asm volatile("" : "+v"(tok) : "v"(r[0]), "v"(r[kCopyU - 1]));
+    asm volatile("" : "+v"(tok) : "v"(r[0]), "v"(r[CU - 1]));
     hook(tok);
   }
   const int ndst = ND ? ND : nd;
@@ -59,10 +59,10 @@ __device__ __forceinline__ void copy_vec_tile(const u32x4* src, const GD& gdst, 
     u32x4* dv = gdst(d);
     if constexpr (ND != 1) {
       // fan-outs: non-temporal stores of device scope
-      store_tile<kStNTDevice, kCopyU, kBlock, FULL>(dv, j0, nvec, r);
+      store_tile<kStNTDevice, CU, kBlock, FULL>(dv, j0, nvec, r);
     } else {
 #pragma unroll
-      for (int u = 0; u < kCopyU; ++u) {
+      for (int u = 0; u < CU; ++u) {
         const uint64_t j = j0 + (uint64_t)u * kBlock;
         if (FULL || j < nvec) st16<true>(dv + j, r[u]);
       }
@@ -106,12 +106,12 @@ __device__ __forceinline__ u32x4 shift_bytes(const u32x4& lo, const u32x4& hi, i
 // only at run time).  The second load of the last vector reads at most 15
 // bytes past the segment, inside the aligned 16-byte block that holds its
 // last byte.
-template <bool FULL, int ND, typename GD>
+template <bool FULL, int ND, int CU = kCopyU, typename GD>
 __device__ __forceinline__ void copy_shift_tile(const u32x4* vs, const GD& gdst, int nd, uint64_t j0, uint64_t nvec,
                                                 int m) {
-  u32x4 a[kCopyU], b[kCopyU];
+  u32x4 a[CU], b[CU];
 #pragma unroll
-  for (int u = 0; u < kCopyU; ++u) {
+  for (int u = 0; u < CU; ++u) {
     const uint64_t j = j0 + (uint64_t)u * kBlock;
     if (FULL || j < nvec) {
       a[u] = ld16<false>(vs + j);
@@ -121,13 +121,13 @@ __device__ __forceinline__ void copy_shift_tile(const u32x4* vs, const GD& gdst,
   __builtin_amdgcn_sched_barrier(0);
   const int q = m >> 2, r = m & 3;
 #pragma unroll
-  for (int u = 0; u < kCopyU; ++u) a[u] = shift_bytes(a[u], b[u], q, r);
+  for (int u = 0; u < CU; ++u) a[u] = shift_bytes(a[u], b[u], q, r);
   const int ndst = ND ? ND : nd;
 #pragma unroll
   for (int d = 0; d < ndst; ++d) {
     u32x4* dv = gdst(d);
 #pragma unroll
-    for (int u = 0; u < kCopyU; ++u) {
+    for (int u = 0; u < CU; ++u) {
       const uint64_t j = j0 + (uint64_t)u * kBlock;
       if (FULL || j < nvec) st16<true>(dv + j, a[u]);
     }
@@ -172,28 +172,30 @@ __device__ __forceinline__ ShiftSpan shift_span(const void* src, const void* dst
 // Tiles of a copy segment as copy_segment counts them, and whether this
 // workgroup works any of them or the head and tail (see copy_segment);
 // lets a workgroup skip a segment's pointer setup.
-template <int B>
+template <int B, int CU = kCopyU>
 __device__ __forceinline__ uint64_t copy_segment_tiles(const SegSpan& sp, uint64_t len) {
-  return sp.vec ? ceil_div(sp.nvec, kCopyTV) : ceil_div(len, (uint64_t)kBlock * 4);
+  return sp.vec ? ceil_div(sp.nvec, (uint64_t)CU * kBlock) : ceil_div(len, (uint64_t)kBlock * 4);
 }
 
 // Whether this workgroup is the one the partial last tile of a vectorized
 // segment is dealt to although it lies at or beyond lim (partial tiles
 // are never claimed).  Flat indices stay below 2^32.
+template <int CU = kCopyU>
 __device__ __forceinline__ bool copy_owns_partial(const SegSpan& sp, uint64_t base, uint64_t lim) {
-  const uint64_t nfull = sp.nvec / kCopyTV;
-  return sp.vec && nfull * kCopyTV < sp.nvec && nfull >= lim &&
+  constexpr uint64_t TV = (uint64_t)CU * kBlock;
+  const uint64_t nfull = sp.nvec / TV;
+  return sp.vec && nfull * TV < sp.nvec && nfull >= lim &&
          (uint32_t)(base + nfull) % gridDim.x == blockIdx.x;
 }
 
-template <int B>
+template <int B, int CU = kCopyU>
 __device__ __forceinline__ bool copy_segment_owned(uint64_t len, int dmis, uint64_t base, uint64_t* nt_out,
                                                    uint64_t lim = ~0ull) {
   const SegSpan sp = seg_span<B>(len, dmis);
-  const uint64_t nt = copy_segment_tiles<B>(sp, len);
+  const uint64_t nt = copy_segment_tiles<B, CU>(sp, len);
   *nt_out = nt;
   const uint64_t ft = first_tile32(base, blockIdx.x, gridDim.x);
-  return ft < (nt < lim ? nt : lim) || (ft == 0 && (sp.head || sp.tail)) || copy_owns_partial(sp, base, lim);
+  return ft < (nt < lim ? nt : lim) || (ft == 0 && (sp.head || sp.tail)) || copy_owns_partial<CU>(sp, base, lim);
 }
 
 // Copy one segment of len elements: this workgroup's share of the first
@@ -202,11 +204,12 @@ __device__ __forceinline__ bool copy_segment_owned(uint64_t len, int dmis, uint6
 // gdst(d) gives destination d's element pointer at the segment start.
 // Returns the segment's tile count.  lim applies to vector tiles without
 // SHIFT only (the claimed tails copy no other kind).
-template <int B, bool NTL, int ND, bool SHIFT, typename GD>
+template <int B, bool NTL, int ND, bool SHIFT, int CU = kCopyU, typename GD>
 __device__ __forceinline__ uint64_t copy_segment(const typename Word<B>::T* src, const GD& gdst, int nd,
                                                  uint64_t len, int dmis, uint64_t base, uint64_t lim = ~0ull) {
   using W = typename Word<B>::T;
   constexpr uint64_t V = 16 / B;
+  constexpr uint64_t TVU = (uint64_t)CU * kBlock;  // vectors per tile
   const uint64_t grid = gridDim.x, wg = blockIdx.x;
   const int ndst = ND ? ND : nd;
   auto elem_at = [&](uint64_t e) {
@@ -227,27 +230,27 @@ __device__ __forceinline__ uint64_t copy_segment(const typename Word<B>::T* src,
     }
     return nt;
   }
-  const uint64_t nt = ceil_div(sp.nvec, kCopyTV);
+  const uint64_t nt = ceil_div(sp.nvec, TVU);
   if (sp.nvec) {
     const int m = SHIFT ? (int)(((uintptr_t)src + sp.head * B) & 15) : 0;
     auto vd = [&](int d) -> u32x4* { return reinterpret_cast<u32x4*>(gdst(d) + sp.head); };
-    const uint64_t nfull = sp.nvec / kCopyTV;
+    const uint64_t nfull = sp.nvec / TVU;
     if (m == 0) {
       const u32x4* vs = reinterpret_cast<const u32x4*>(src + sp.head);
       const uint64_t nd_t = nt < lim ? nt : lim;
       for (uint64_t t = first_tile(base, wg, grid); t < nd_t; t += grid) {
-        const uint64_t j0 = t * kCopyTV + threadIdx.x;
-        if (t < nfull) copy_vec_tile<NTL, true, ND>(vs, vd, nd, j0, sp.nvec);
-        else copy_vec_tile<NTL, false, ND>(vs, vd, nd, j0, sp.nvec);
+        const uint64_t j0 = t * TVU + threadIdx.x;
+        if (t < nfull) copy_vec_tile<NTL, true, ND, CU>(vs, vd, nd, j0, sp.nvec);
+        else copy_vec_tile<NTL, false, ND, CU>(vs, vd, nd, j0, sp.nvec);
       }
-      if (copy_owns_partial(sp, base, nd_t))
-        copy_vec_tile<NTL, false, ND>(vs, vd, nd, nfull * kCopyTV + threadIdx.x, sp.nvec);
+      if (copy_owns_partial<CU>(sp, base, nd_t))
+        copy_vec_tile<NTL, false, ND, CU>(vs, vd, nd, nfull * TVU + threadIdx.x, sp.nvec);
     } else if constexpr (SHIFT) {
       const u32x4* vs = reinterpret_cast<const u32x4*>((uintptr_t)(src + sp.head) & ~(uintptr_t)15);
       for (uint64_t t = first_tile(base, wg, grid); t < nt; t += grid) {
-        const uint64_t j0 = t * kCopyTV + threadIdx.x;
-        if (t < nfull) copy_shift_tile<true, ND>(vs, vd, nd, j0, sp.nvec, m);
-        else copy_shift_tile<false, ND>(vs, vd, nd, j0, sp.nvec, m);
+        const uint64_t j0 = t * TVU + threadIdx.x;
+        if (t < nfull) copy_shift_tile<true, ND, CU>(vs, vd, nd, j0, sp.nvec, m);
+        else copy_shift_tile<false, ND, CU>(vs, vd, nd, j0, sp.nvec, m);
       }
     }
   }

@@ -284,7 +284,7 @@ __device__ __forceinline__ uint32_t first_tile32(uint64_t base, uint32_t wg, uin
 // So the streaming kernels deal out part of their tiles in turn and let
 // the workers (workgroups, or waves) claim the rest, one at a time, from a
 // counter: a worker that runs ahead claims more.  Each launch gets a
-// counter slot, zero at launch; the 1:1 copies, Alltoallv, the MoE token
+// counter slot, zero at launch; the copies, Alltoallv, the MoE token
 // copies and AllReduce at p = 8 split their claimed work over the slot's
 // kClaimPools counters (claim_pool), the other kernels use one counter.  Every worker claims until a claim comes back past the last
 // unit of its counter, so a counter with `units` claimable units and W

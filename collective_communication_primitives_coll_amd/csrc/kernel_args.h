@@ -229,8 +229,8 @@ int noalloc_scratch(int dev, void** out);
 // apart (one 128-byte line each).  claim_slots_base gives device dev's
 // array (dev current).  Launches with at least kClaimMinTilesPerWg tiles
 // per workgroup use their slot: the uniform 1:1 copies, Alltoallv, the MoE
-// token copies and AllReduce at p = 8 all kClaimPools counters of it, the
-// other reductions and AllGather and Broadcast at p >= 8 the first.
+// token copies, AllGather and Broadcast at p >= 8 and AllReduce at p = 8
+// all kClaimPools counters of it, the other reductions the first.
 constexpr int kClaimSlots = 1024;
 constexpr int kClaimPools = 8;
 constexpr int kClaimPoolWords = 16;
