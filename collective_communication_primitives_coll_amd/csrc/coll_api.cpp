@@ -416,6 +416,7 @@ COLL_EXPORT coll_status_t coll_broadcast(const void* send_root, void* const* rec
   coll::CopyGeom g{n, p, coll::kCopyBroadcast, (int)((uintptr_t)send_root & 15),
                    common_mis((const void* const*)recv, p), nullptr};
   g.claim = stream_claim_slot(stream);
+  g.dst_amis = common_amis((const void* const*)recv, p);
   int fgrid;
   e = max_grid(&fgrid, kFamFanout);
   if (e) return hip_fail(e);
@@ -499,6 +500,7 @@ COLL_EXPORT coll_status_t coll_allgather(const void* const* send, void* const* r
   coll::CopyGeom g{n, p, coll::kCopyAllGather, common_mis(send, p), common_mis((const void* const*)recv, p),
                    nullptr};
   g.claim = stream_claim_slot(stream);
+  g.dst_amis = common_amis((const void* const*)recv, p);
   int fgrid;
   e = max_grid(&fgrid, kFamFanout);
   if (e) return hip_fail(e);

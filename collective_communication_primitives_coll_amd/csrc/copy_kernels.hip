@@ -27,6 +27,12 @@ __device__ __forceinline__ int fanout_mis(const CopyGeom& g, int s) {
   const uint64_t dst_off = KIND == kCopyAllGather ? (uint64_t)s * g.n : 0;
   return g.dst_mis < 0 ? -1 : (int)((g.dst_mis + dst_off * B) & 15);
 }
+// ... and their common address modulo kLineAlign (-1: unknown).
+template <int B, int KIND>
+__device__ __forceinline__ int fanout_amis(const CopyGeom& g, int s) {
+  const uint64_t dst_off = KIND == kCopyAllGather ? (uint64_t)s * g.n : 0;
+  return seg_amis(g.dst_amis, dst_off * B);
+}
 
 // The claimed tiles of fanout_kernel (tiles of FU vectors per lane), one
 // workgroup tile per claim from the workgroup's pool (claim c of pool x is
@@ -58,7 +64,7 @@ __device__ __forceinline__ void fanout_claimed(const RankPtrs& ptrs, const CopyG
       do {
         sbase += cnt;
         ++s;
-        sp = seg_span<B>(g.n, fanout_mis<B, KIND>(g, s));
+        sp = seg_span_a<B>(g.n, fanout_mis<B, KIND>(g, s), fanout_amis<B, KIND>(g, s));
         cnt = copy_segment_tiles<B, FU>(sp, g.n);
       } while (f >= sbase + cnt && s < NSEG - 1);  // the bound only keeps reads in range
       const uint64_t dst_off = KIND == kCopyAllGather ? (uint64_t)s * g.n : 0;
@@ -129,7 +135,7 @@ COLL_STREAM_KERNEL void fanout_kernel(RankPtrs ptrs, CopyGeom g) {
     first = issue_claim(ctr, (int)threadIdx.x);
     bool vec = true;
     for (int s = 0; s < nseg; ++s) {
-      const SegSpan sp = seg_span<B>(g.n, fanout_mis<B, KIND>(g, s));
+      const SegSpan sp = seg_span_a<B>(g.n, fanout_mis<B, KIND>(g, s), fanout_amis<B, KIND>(g, s));
       total += copy_segment_tiles<B, FU>(sp, g.n);
       vec = vec && (sp.vec || g.n == 0);
     }
@@ -139,10 +145,10 @@ COLL_STREAM_KERNEL void fanout_kernel(RankPtrs ptrs, CopyGeom g) {
   uint64_t base = 0;
   for (int s = 0; s < nseg; ++s) {
     const uint64_t dst_off = KIND == kCopyAllGather ? (uint64_t)s * g.n : 0;
-    const int mis = fanout_mis<B, KIND>(g, s);
+    const int mis = fanout_mis<B, KIND>(g, s), amis = fanout_amis<B, KIND>(g, s);
     const uint64_t lim = dealt > base ? dealt - base : 0;
     uint64_t nt;
-    if (!copy_segment_owned<B, FU>(g.n, mis, base, &nt, lim)) {
+    if (!copy_segment_owned<B, FU>(g.n, mis, amis, base, &nt, lim)) {
       base += nt;
       continue;
     }
@@ -152,10 +158,10 @@ COLL_STREAM_KERNEL void fanout_kernel(RankPtrs ptrs, CopyGeom g) {
 #pragma unroll
       for (int k = 0; k < P; ++k) dst[k] = (W*)ptrs.dst[k] + dst_off;
       auto gdst = [&](int d) -> W* { return dst[d]; };
-      base += copy_segment<B, P == 1, P, SHIFT, FU>(src, gdst, P, g.n, mis, base, lim);
+      base += copy_segment<B, P == 1, P, SHIFT, FU>(src, gdst, P, g.n, mis, amis, base, lim);
     } else {
       auto gdst = [&](int d) -> W* { return (W*)ptrs.dst[d] + dst_off; };
-      base += copy_segment<B, false, 0, SHIFT>(src, gdst, p, g.n, mis, base);
+      base += copy_segment<B, false, 0, SHIFT>(src, gdst, p, g.n, mis, amis, base);
     }
   }
   if constexpr (CLAIMS) {
@@ -195,14 +201,14 @@ COLL_STREAM_KERNEL void pair_copy_kernel(RankPtrs ptrs, CopyGeom g) {
       dst = (W*)ptrs.dst[sgi];
     }
     (void)src_off;
-    const int mis = (int)((uintptr_t)dst & 15);
+    const int mis = (int)((uintptr_t)dst & 15), amis = (int)((uintptr_t)dst & (kLineAlign - 1));
     uint64_t nt;
-    if (!copy_segment_owned<B>(g.n, mis, base, &nt)) {
+    if (!copy_segment_owned<B>(g.n, mis, amis, base, &nt)) {
       base += nt;
       continue;
     }
     auto gdst = [&](int) -> W* { return dst; };
-    base += copy_segment<B, true, 1, SHIFT>(src, gdst, 1, g.n, mis, base);
+    base += copy_segment<B, true, 1, SHIFT>(src, gdst, 1, g.n, mis, amis, base);
   }
 }
 
@@ -441,9 +447,9 @@ COLL_STREAM_KERNEL void alltoallv_kernel(RankPtrs ptrs, A2avArgs a) {
     const uint64_t ro = (uint64_t)roff[sgi];
     const W* src = (const W*)ptrs.src[i] + so;
     W* dst = (W*)ptrs.dst[j] + ro;
-    const int mis = (int)((uintptr_t)dst & 15);
+    const int mis = (int)((uintptr_t)dst & 15), amis = (int)((uintptr_t)dst & (kLineAlign - 1));
     auto gdst = [&](int) -> W* { return dst; };
-    base += copy_segment<B, true, 1, true>(src, gdst, 1, len, mis, base);
+    base += copy_segment<B, true, 1, true>(src, gdst, 1, len, mis, amis, base);
   }
 }
 

@@ -162,8 +162,12 @@ __device__ __forceinline__ ShiftSpan shift_span(const void* src, const void* dst
 // segment's tile count.
 // A copy segment's geometry follows its destinations: `mis` is their
 // common address modulo 16 at the segment start (-1: the segment goes
-// element by element).  The head runs to the destinations' 16-byte
-// alignment.  SHIFT: a source that then sits m bytes past its own
+// element by element), `damis` their common address modulo kLineAlign
+// (-1: unknown).  The head runs to the destinations' next kLineAlign
+// boundary when damis is known, else to their 16-byte alignment: a wave
+// whose stores start off a 128-byte line shares a partly written line
+// with each neighbouring wave, and those lines cost far more than their
+// bytes.  SHIFT: a source that then sits m bytes past its own
 // alignment takes copy_shift_tile, otherwise plain vector tiles; without
 // SHIFT (the launcher found every segment's source and destinations
 // agreeing modulo 16) only plain vector tiles are compiled, so the common
@@ -189,9 +193,9 @@ __device__ __forceinline__ bool copy_owns_partial(const SegSpan& sp, uint64_t ba
 }
 
 template <int B, int CU = kCopyU>
-__device__ __forceinline__ bool copy_segment_owned(uint64_t len, int dmis, uint64_t base, uint64_t* nt_out,
-                                                   uint64_t lim = ~0ull) {
-  const SegSpan sp = seg_span<B>(len, dmis);
+__device__ __forceinline__ bool copy_segment_owned(uint64_t len, int dmis, int damis, uint64_t base,
+                                                   uint64_t* nt_out, uint64_t lim = ~0ull) {
+  const SegSpan sp = seg_span_a<B>(len, dmis, damis);
   const uint64_t nt = copy_segment_tiles<B, CU>(sp, len);
   *nt_out = nt;
   const uint64_t ft = first_tile32(base, blockIdx.x, gridDim.x);
@@ -206,7 +210,8 @@ __device__ __forceinline__ bool copy_segment_owned(uint64_t len, int dmis, uint6
 // SHIFT only (the claimed tails copy no other kind).
 template <int B, bool NTL, int ND, bool SHIFT, int CU = kCopyU, typename GD>
 __device__ __forceinline__ uint64_t copy_segment(const typename Word<B>::T* src, const GD& gdst, int nd,
-                                                 uint64_t len, int dmis, uint64_t base, uint64_t lim = ~0ull) {
+                                                 uint64_t len, int dmis, int damis, uint64_t base,
+                                                 uint64_t lim = ~0ull) {
   using W = typename Word<B>::T;
   constexpr uint64_t V = 16 / B;
   constexpr uint64_t TVU = (uint64_t)CU * kBlock;  // vectors per tile
@@ -220,7 +225,7 @@ __device__ __forceinline__ uint64_t copy_segment(const typename Word<B>::T* src,
   auto elems = [&](uint64_t from, uint64_t cnt) {
     for (uint64_t i = threadIdx.x; i < cnt; i += kBlock) elem_at(from + i);
   };
-  const SegSpan sp = seg_span<B>(len, dmis);
+  const SegSpan sp = seg_span_a<B>(len, dmis, damis);
   if (!sp.vec) {
     constexpr uint64_t TE = (uint64_t)kBlock * 4;
     const uint64_t nt = ceil_div(len, TE);
@@ -255,9 +260,9 @@ __device__ __forceinline__ uint64_t copy_segment(const typename Word<B>::T* src,
     }
   }
   if ((sp.head || sp.tail) && first_tile(base, wg, grid) == 0) {
-    // head and tail in one pass (each is shorter than a vector)
-    const uint64_t i = threadIdx.x;
-    if (i < sp.head + sp.tail) elem_at(i < sp.head ? i : sp.head + sp.nvec * V + (i - sp.head));
+    // head and tail together (below kLineAlign + 16 bytes)
+    for (uint64_t i = threadIdx.x; i < sp.head + sp.tail; i += kBlock)
+      elem_at(i < sp.head ? i : sp.head + sp.nvec * V + (i - sp.head));
   }
   return nt;
 }

@@ -222,12 +222,12 @@ __device__ __forceinline__ SegSpan seg_span(uint64_t len, int mis) {
 // boundary, 5.5 TB/s on it).
 constexpr int kLineAlign = 256;
 
-// seg_span with the element-wise head extended until the sources reach a
-// kLineAlign boundary.  amis is the sources' common address modulo
-// kLineAlign at the segment start, or -1 if unknown (then as seg_span).
-// The head stays below kLineAlign / B elements; after it every source is
-// kLineAlign-aligned and every destination 16-byte aligned (they agree
-// modulo 16 whenever mis >= 0).
+// seg_span with the element-wise head extended until one side (the
+// reductions' sources, the copies' destinations) reaches a kLineAlign
+// boundary.  amis is that side's common address modulo kLineAlign at the
+// segment start, or -1 if unknown (then as seg_span).  The head stays
+// below kLineAlign / B elements; after it that side is kLineAlign-aligned
+// and the other 16-byte aligned whenever they agree modulo 16 (mis >= 0).
 template <int B>
 __device__ __forceinline__ SegSpan seg_span_a(uint64_t len, int mis, int amis) {
   SegSpan s = seg_span<B>(len, mis);

@@ -72,6 +72,9 @@ struct CopyGeom {
   // Broadcast) and pair_copy_flat_kernel (All-to-All, Gather, Scatter), or
   // null to deal out every tile in turn.
   unsigned long long* claim;
+  // Fan-outs: the destinations' common address modulo kLineAlign, or -1
+  // (vector tiles then start on their 16-byte alignment only).
+  int dst_amis = -1;
 };
 
 struct A2avArgs {

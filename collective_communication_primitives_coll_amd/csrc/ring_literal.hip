@@ -50,7 +50,7 @@ COLL_STREAM_KERNEL void ring_step_kernel(RankPtrs ptrs, RingStepGeom g) {
     } else {
       using W = typename Word<T::B>::T;
       auto gdst = [&](int) -> W* { return (W*)d; };
-      base += copy_segment<T::B, true, 1, false>((const W*)partial, gdst, 1, len, mis, base);
+      base += copy_segment<T::B, true, 1, false>((const W*)partial, gdst, 1, len, mis, -1, base);
     }
   }
 }

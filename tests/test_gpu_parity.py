@@ -1695,14 +1695,22 @@ def test_claimed_tails(coll, case):
 
 
 COPY_CLAIM_CASES = [
-    # (what, p, n, dtype): AllGather shards / Broadcast elements, with at
-    # least 8 tiles per workgroup for 256 workgroups (one per CU); p = 8 and
-    # 16 claim tiles, p = 4 deals every tile out
-    ("AllGather bf16", 8, 4_500_003, BF16),
-    ("AllGather fp32 p=4", 4, 9_000_001, F32),
-    ("AllGather bytes p=16", 16, 4_200_017, 3),
-    ("Broadcast fp32", 8, 17_000_003, F32),
-    ("Broadcast bf16 p=16", 16, 20_000_001, BF16),
+    # (what, p, n, dtype, off): AllGather shards / Broadcast elements, with
+    # at least 8 tiles per workgroup for 256 workgroups (one per CU), every
+    # receive buffer `off` elements into its allocation; p = 8 and 16 claim
+    # tiles when sources and destinations agree modulo 16 bytes, p = 4 deals
+    # every tile out.  The off-line cases put the destinations a multiple of
+    # 16 bytes off a 256-byte line (segment heads of up to 255 bytes before
+    # the claimed vector tiles).
+    ("AllGather bf16", 8, 4_500_003, BF16, 0),
+    ("AllGather fp32 p=4", 4, 9_000_001, F32, 0),
+    ("AllGather bytes p=16", 16, 4_200_017, 3, 0),
+    ("Broadcast fp32", 8, 17_000_003, F32, 0),
+    ("Broadcast bf16 p=16", 16, 20_000_001, BF16, 0),
+    ("AllGather bf16 off-line shards", 8, 4_500_008, BF16, 0),
+    ("AllGather fp32 p=16 off-line shards", 16, 2_250_004, F32, 4),
+    ("Broadcast bytes off-line receivers", 8, 17_000_005, 3, 16),
+    ("Broadcast bf16 off-line receivers p=16", 16, 9_000_011, BF16, 120),
 ]
 
 
@@ -1710,28 +1718,29 @@ COPY_CLAIM_CASES = [
 def test_claimed_tails_fanout(coll, case):
     """Fan-outs large enough to claim their last tiles: every byte of every
     receive buffer equals its source (AllGather: rank order; Broadcast: the
-    root's buffer), with ragged sizes."""
+    root's buffer), with ragged sizes, and the bytes before each receive
+    buffer are untouched."""
     import torch
-    what, p, n, dtype = case
+    what, p, n, dtype, off = case
     tdt = {F32: torch.float32, BF16: torch.bfloat16, 3: torch.uint8}[dtype]
     esz = {F32: 4, BF16: 2, 3: 1}[dtype]
     g = torch.Generator(device="cuda").manual_seed(p * 1000 + n % 997)
+    m = p * n if what.startswith("AllGather") else n
+    bases = [torch.full(((off + m) * esz,), 0x5A, dtype=torch.uint8, device="cuda") for _ in range(p)]
+    outs = [b[off * esz:].view(tdt) for b in bases]
     if what.startswith("AllGather"):
         shards = [torch.randint(0, 255, (n * esz,), dtype=torch.uint8, device="cuda", generator=g).view(tdt)
                   for _ in range(p)]
-        full = [torch.zeros(p * n, dtype=tdt, device="cuda") for _ in range(p)]
-        coll.coll_allgather(shards, full)
-        sync()
+        coll.coll_allgather(shards, outs)
         expect = torch.cat(shards).view(torch.uint8)
-        for r in range(p):
-            assert torch.equal(full[r].view(torch.uint8), expect), f"{what} rank {r}"
     else:
         src = torch.randint(0, 255, (n * esz,), dtype=torch.uint8, device="cuda", generator=g).view(tdt)
-        outs = [torch.zeros(n, dtype=tdt, device="cuda") for _ in range(p)]
         coll.coll_broadcast(src, outs, 0)
-        sync()
-        for r in range(p):
-            assert torch.equal(outs[r].view(torch.uint8), src.view(torch.uint8)), f"{what} rank {r}"
+        expect = src.view(torch.uint8)
+    sync()
+    for r in range(p):
+        assert torch.equal(bases[r][off * esz:], expect), f"{what} rank {r}"
+        assert bool((bases[r][:off * esz] == 0x5A).all()), f"{what} rank {r}: wrote before the buffer"
 
 
 def test_claimed_tails_back_to_back_and_on_two_streams(coll):
