@@ -960,7 +960,7 @@ FP8_SHAPES = [  # p, T, k, hidden, group
     (1, 3, 1, 16, 16), (2, 5, 2, 48, 16), (3, 100, 2, 256, 128), (4, 33, 3, 7168, 128),
     (2, 9, 2, 7168, 7168), (8, 64, 2, 4096, 2048), (3, 7, 8, 1024, 1024), (2, 6, 1, 16384, 128),
     (2, 4, 2, 16384, 16384), (16, 20, 2, 2048, 64), (5, 50, 4, 960, 32), (2, 3, 2, 20480, 256),
-    (64, 3, 2, 64, 16)]
+    (64, 3, 2, 64, 16), (3, 11, 2, 1536, 512), (2, 7, 2, 3584, 256)]
 
 
 @pytest.mark.parametrize("p,T,k,H,G", FP8_SHAPES)
@@ -1300,7 +1300,8 @@ def _combine_skipping(ys, dest, slot, weights, k, H, dtype, residual, skip):
 
 
 @pytest.mark.parametrize("p,T,k,H,G", [(2, 9, 2, 256, 128), (4, 33, 3, 7168, 128), (3, 7, 8, 1024, 1024),
-                                       (2, 5, 2, 4096, 2048), (8, 20, 2, 2048, 64)])
+                                       (2, 5, 2, 4096, 2048), (8, 20, 2, 2048, 64),
+                                       (3, 11, 2, 1536, 512)])
 def test_moe_dispatch_fp8_direct(coll, p, T, k, H, G):
     import torch
     from oracle import fp8
