@@ -113,3 +113,53 @@ def test_batch_edge_values(coll, p):
         expect = native.allreduce(hx, op, dtype)
         for r in (0, p - 1):
             _check(to_host(recv[r], dtype), expect, op, f"batch call {k} op {op} rank {r}")
+
+
+# Sizes past the one-tile-per-workgroup bound with enough tiles per
+# workgroup that the walking kernel claims part of them (pooled counters
+# for AllReduce at p = 8), so the edge semantics are checked there too.
+# Claims start at 8 tiles per workgroup: 2048 tiles for one workgroup per
+# CU on 256 CUs.  At p = 8 an AllReduce tile holds 2 vectors per lane of
+# 256 lanes and a ReduceScatter tile 4; a vector holds 8 bf16 or 4 others.
+def _vec_elems(dtype):
+    return 8 if dtype == BF16 else 4
+
+
+BIG_CASES = [("int_wrap", I32), ("subnormal", F32), ("overflow", BF16), ("zero_nan_inf", F32),
+             ("zero_nan_inf", BF16)]
+
+
+@pytest.mark.parametrize("kind,dtype", BIG_CASES)
+def test_allreduce_edge_values_claimed_tiles(coll, kind, dtype):
+    te = 2 * 256 * _vec_elems(dtype)
+    p, n = 8, 2048 * te + 3 * te // 2 + 37
+    hx = inputs.edge_buffers(p, n, dtype, kind, seed=21)
+    send = [to_dev(x, dtype) for x in hx]
+    recv = [empty(n, dtype) for _ in range(p)]
+    for op in OPS:
+        for algo, order in ((coll.COLL_ALGO_RING, native.ORD_RING), (coll.COLL_ALGO_RECURSIVE_DOUBLING, native.ORD_RD)):
+            fp_sum = dtype != I32 and op in (native.SUM, native.AVG)
+            expect = native.allreduce(hx, op, dtype, order if fp_sum else native.ORD_RING)
+            coll.coll_allreduce_algo(send, recv, algo, op)
+            sync()
+            for r in range(p):
+                _check(to_host(recv[r], dtype), expect, op, f"{kind} p={p} n={n} op={op} algo={algo} rank {r}")
+
+
+@pytest.mark.parametrize("kind,dtype", BIG_CASES)
+def test_reduce_scatter_and_reduce_edge_values_claimed_tiles(coll, kind, dtype):
+    te = 4 * 256 * _vec_elems(dtype)
+    p, n = 8, 256 * te + 3 * te // 2 + 37  # 8 chunks of n elements
+    hx = inputs.edge_buffers(p, p * n, dtype, kind, seed=22)
+    send = [to_dev(x, dtype) for x in hx]
+    shard = [empty(n, dtype) for _ in range(p)]
+    root_out = empty(p * n, dtype)
+    for op in OPS:
+        expect = native.reduce_scatter(hx, op, dtype)
+        coll.coll_reduce_scatter(send, shard, op)
+        sync()
+        for r in range(p):
+            _check(to_host(shard[r], dtype), expect[r], op, f"RS {kind} p={p} n={n} op={op} block {r}")
+        coll.coll_reduce(send, root_out, 3, op)
+        sync()
+        _check(to_host(root_out, dtype), native.allreduce(hx, op, dtype), op, f"Reduce {kind} p={p} n={n} op={op}")
