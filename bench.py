@@ -574,7 +574,7 @@ def extra_collectives(torch, coll, inputs, metrics, dev, which, ceil, iters=10, 
                      "workload": "AllReduce p=16, 4 KiB / 64 KiB / 1 MiB per rank, each schedule, back to back"})
 
     # --- rank counts that are not powers of two: AllReduce 256 MiB fp32 per
-    # rank and ReduceScatter 2^26 bf16 per rank, p = 3, 5, 6, 7, 12 ---------
+    # rank and ReduceScatter of about 2^26 fp32 per rank, p = 3, 5, 6, 7, 12 -
     if want("anyp"):
         table = []
         for p in (3, 5, 6, 7, 12):

@@ -4,8 +4,8 @@ bench.py times (same entry points, default grids, same seeded inputs).
 Every output is compared whole, element by element, with the threaded C++
 oracle (oracle/oracle.cpp, held bit-identical to oracle/ref.py by the CPU
 tests): the ReduceScatter and AllGather of the timed step, the p=8 256 MiB
-AllReduce under every schedule, the p=4 AllReduces, All-to-All and
-Alltoallv, all 10,000 calls of the batched plan on all 16 ranks, and every
+AllReduce under every schedule, AllReduce and ReduceScatter at p = 3, 5,
+6, 7 and 12, the p=4 AllReduces, All-to-All and Alltoallv, all 10,000 calls of the batched plan on all 16 ranks, and every
 stage of the MoE paths (FP8 included).  Large expected arrays are uploaded
 once and compared on the device with torch.equal on the bit patterns; a
 mismatch is then located on the host for the message.
@@ -343,3 +343,33 @@ def test_moe_direct_full_size(env):
         # expert = identity: y rows are the packed token rows, read at pos
         expect = native.moe_combine(packs[i][2], packs[i][1], weights[i], k, H, native.BF16, residual[i])
         assert_device_equal(torch, out[i], expect, f"combined tokens rank {i}")
+
+
+def test_other_rank_counts_full_size(env):
+    """AllReduce sum of 2^26 fp32 per rank and ReduceScatter sum of blocks of
+    2^26 / p rounded down to whole vectors, p = 3, 5, 6, 7, 12 ~ N(0, 1),
+    the sizes of the benchmark's rank-count rows: every rank's whole output
+    bit-exact against the oracle in ring order.  The twelve rank buffers
+    are drawn once; rank count p uses the first p of them (and each one's
+    first p * block elements for the ReduceScatter)."""
+    torch, coll = env
+    n = 1 << 26
+    hx = inputs.rank_buffers(inputs.WL_TEST, 12, n, inputs.F32, dist="normal", extra=(12,))
+    send = [dev(torch, x) for x in hx]
+    recv = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(12)]
+    for p in (3, 5, 6, 7, 12):
+        for t in recv[:p]:
+            t.fill_(float("nan"))
+        coll.coll_allreduce(send[:p], recv[:p], coll.COLL_SUM)
+        torch.cuda.synchronize()
+        expect = dev(torch, native.allreduce(hx[:p], native.SUM, native.F32))
+        for r in range(p):
+            assert_device_equal(torch, recv[r], expect, f"AllReduce p={p} rank {r}")
+        del expect
+        blk = n // (4 * p) * 4
+        shard = [t[:blk] for t in recv[:p]]
+        coll.coll_reduce_scatter([t[:p * blk] for t in send[:p]], shard, coll.COLL_SUM)
+        torch.cuda.synchronize()
+        expect = native.reduce_scatter([x[:p * blk] for x in hx[:p]], native.SUM, native.F32)
+        for r in range(p):
+            assert_device_equal(torch, shard[r], expect[r], f"ReduceScatter p={p} block {r}")
