@@ -4,8 +4,8 @@ bench.py times (same entry points, default grids, same seeded inputs).
 Every output is compared whole, element by element, with the threaded C++
 oracle (oracle/oracle.cpp, held bit-identical to oracle/ref.py by the CPU
 tests): the ReduceScatter and AllGather of the timed step, the p=8 256 MiB
-AllReduce under every schedule, AllReduce and ReduceScatter at p = 3, 5,
-6, 7 and 12, the p=4 AllReduces, All-to-All and Alltoallv, all 10,000 calls of the batched plan on all 16 ranks, and every
+AllReduce under every schedule and with AVG and PreMulSum, AllReduce and
+ReduceScatter at p = 3, 5, 6, 7 and 12, Gather and Scatter, the p=4 AllReduces, All-to-All and Alltoallv, all 10,000 calls of the batched plan on all 16 ranks, and every
 stage of the MoE paths (FP8 included).  Large expected arrays are uploaded
 once and compared on the device with torch.equal on the bit patterns; a
 mismatch is then located on the host for the message.
@@ -373,3 +373,49 @@ def test_other_rank_counts_full_size(env):
         expect = native.reduce_scatter([x[:p * blk] for x in hx[:p]], native.SUM, native.F32)
         for r in range(p):
             assert_device_equal(torch, shard[r], expect[r], f"ReduceScatter p={p} block {r}")
+
+
+def test_dp_allreduce_avg_and_premul_full_size(env):
+    """AllReduce AVG and PreMulSum (every scale 1/p), ring order, p=8, 2^26
+    fp32 per rank ~ N(0, 1), the inputs and calls of the benchmark's AVG and
+    PreMulSum rows: every rank's whole output bit-exact against the oracle."""
+    torch, coll = env
+    p, n = 8, 1 << 26
+    hx = inputs.rank_buffers(inputs.WL_DP_RING_AR, p, n, inputs.F32, dist="normal")
+    send = [dev(torch, x) for x in hx]
+    recv = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(p)]
+    scales = np.full(p, 1.0 / p, dtype=np.float32)
+    for what in ("avg", "premul"):
+        for t in recv:
+            t.fill_(float("nan"))
+        if what == "avg":
+            coll.coll_allreduce_algo(send, recv, coll.COLL_ALGO_RING, coll.COLL_AVG)
+            expect = native.allreduce(hx, native.AVG, native.F32)
+        else:
+            coll.coll_allreduce_premul(send, recv, scales, coll.COLL_ALGO_RING)
+            expect = native.allreduce(hx, native.SUM, native.F32, scales=scales)
+        torch.cuda.synchronize()
+        exp_dev = dev(torch, expect)
+        for r in range(p):
+            assert_device_equal(torch, recv[r], exp_dev, f"AllReduce {what} full size rank {r}")
+
+
+def test_gather_scatter_full_size(env):
+    """Gather and Scatter at root 0, p=8, 2^23 bf16 per rank ~ N(0, 1) into
+    and out of a 128 MiB root buffer, as the benchmark's rows call them:
+    whole arrays."""
+    torch, coll = env
+    p, n = 8, 1 << 23
+    hx = inputs.rank_buffers(inputs.WL_TEST, p, n, inputs.BF16, dist="normal", extra=(23,))
+    ranks = [dev(torch, x) for x in hx]
+    root_buf = torch.empty(p * n, dtype=torch.bfloat16, device="cuda")
+    coll.coll_gather(ranks, root_buf, 0)
+    torch.cuda.synchronize()
+    gathered = ref.gather(hx, 0)
+    assert_device_equal(torch, root_buf, gathered, "Gather full size")
+    for t in ranks:
+        t.zero_()
+    coll.coll_scatter(root_buf, ranks, 0)
+    torch.cuda.synchronize()
+    for r, blk in enumerate(ref.scatter(gathered, p, 0)):
+        assert_device_equal(torch, ranks[r], blk, f"Scatter full size rank {r}")
