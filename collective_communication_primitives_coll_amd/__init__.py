@@ -60,6 +60,11 @@ def lib() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing; build it with __graft_entry__.build(). "
                            "There is no fallback path.")
+    # torch ships its own HIP runtime.  Loaded first, it also serves this
+    # library; loaded after it, it would be a second runtime in the process,
+    # in which torch's device pointers and streams mean nothing (every call
+    # then fails with hipErrorNoDevice).
+    import torch  # noqa: F401
     L = ctypes.CDLL(LIB_PATH)
     vp, pp, sz, i32 = ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t, ctypes.c_int
     i64p = ctypes.POINTER(ctypes.c_int64)

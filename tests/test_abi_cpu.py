@@ -347,3 +347,20 @@ def test_noalloc_batch_rejects_invalid_calls_on_the_host():
     assert L.coll_allreduce_batch_noalloc(calls, 3, 4, 0, None) == coll.COLL_OK
     calls[1].op = 9
     assert L.coll_allreduce_batch_noalloc(calls, 3, 4, 0, None) == coll.COLL_ERR_INVALID_ARG
+
+
+def test_binding_shares_torchs_hip_runtime():
+    """Loading the library before torch is imported still leaves one HIP
+    runtime in the process (torch's), so torch's device pointers and streams
+    are valid in the library's calls."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "import collective_communication_primitives_coll_amd as c\n"
+            "c.lib()\n"
+            "import torch\n"
+            "m = sorted(set(l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l))\n"
+            "print(len(m), m)\n"
+            "assert len(m) == 1, m\n") % ROOT
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stdout + r.stderr
