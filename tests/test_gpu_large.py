@@ -1,0 +1,68 @@
+"""Calls past 2^31 elements per buffer (more than 4 GiB per rank of bf16),
+where any 32-bit element or byte offset would wrap.
+
+At p = 2 the ring order folds each element as one fp32 sum of the two
+operands, rounded once to bf16, which is exactly torch's bf16 addition
+(fp32 arithmetic, round to nearest even): every output element is checked
+against that on the device, and sampled elements, including those either
+side of 2^31, against the oracle.
+"""
+import numpy as np
+import pytest
+
+from gpu_util import BF16, assert_bits_equal
+from oracle import native
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def coll():
+    import torch
+    import collective_communication_primitives_coll_amd as c
+    torch.cuda.set_device(0)
+    c.lib()
+    return c
+
+
+def _bits(t):
+    import torch
+    return t.view(torch.int16)
+
+
+def _sample_check(send, got, n, what):
+    """got at sampled positions against the oracle's p = 2 fold of the
+    same positions of the inputs."""
+    import torch
+    rng = np.random.default_rng(2031)
+    j = np.unique(np.concatenate([rng.integers(0, n, 100000),
+                                  np.array([0, 1, (1 << 31) - 1, 1 << 31, (1 << 31) + 1, n - 2, n - 1])]))
+    idx = torch.from_numpy(j).cuda()
+    ops = [_bits(s[idx]).cpu().numpy().view(np.uint16) for s in send]
+    expect = native.allreduce(ops, native.SUM, native.BF16)
+    assert_bits_equal(_bits(got[idx]).cpu().numpy().view(np.uint16), expect, what)
+
+
+def test_allreduce_and_reduce_scatter_past_2_31_elements(coll):
+    import torch
+    p, n = 2, (1 << 31) + 4099
+    g = torch.Generator(device="cuda").manual_seed(31)
+    send = [torch.randn(n, generator=g, device="cuda").to(torch.bfloat16) for _ in range(p)]
+    expect = (send[0].float() + send[1].float()).to(torch.bfloat16)
+    recv = [torch.empty(n, dtype=torch.bfloat16, device="cuda") for _ in range(p)]
+    for t in recv:
+        t.fill_(float("nan"))
+    coll.coll_allreduce(send, recv, coll.COLL_SUM)
+    torch.cuda.synchronize()
+    for r in range(p):
+        assert torch.equal(_bits(recv[r]), _bits(expect)), f"AllReduce n={n} rank {r}"
+    _sample_check(send, recv[1], n, f"AllReduce n={n} sampled")
+
+    blk = (1 << 30) + 2049          # send buffers of 2 * blk > 2^31 elements
+    shard = [t[:blk] for t in recv]
+    for t in shard:
+        t.fill_(float("nan"))
+    coll.coll_reduce_scatter([s[:p * blk] for s in send], shard, coll.COLL_SUM)
+    torch.cuda.synchronize()
+    for r in range(p):
+        assert torch.equal(_bits(shard[r]), _bits(expect[r * blk:(r + 1) * blk])), f"ReduceScatter block {r}"
