@@ -1,4 +1,4 @@
-"""Calls past 2^31 elements per buffer (more than 4 GiB per rank of bf16),
+"""Calls past 2^31 elements per buffer (4 GiB and more per rank of bf16),
 where any 32-bit element or byte offset would wrap.
 
 At p = 2 the ring order folds each element as one fp32 sum of the two
@@ -66,3 +66,31 @@ def test_allreduce_and_reduce_scatter_past_2_31_elements(coll):
     torch.cuda.synchronize()
     for r in range(p):
         assert torch.equal(_bits(shard[r]), _bits(expect[r * blk:(r + 1) * blk])), f"ReduceScatter block {r}"
+
+
+def test_allgather_and_alltoall_past_2_31_elements(coll):
+    """AllGather of 2^30 + 2049-element bf16 shards and All-to-All of blocks
+    of that size, p = 2: each receive (and All-to-All send) buffer holds
+    more than 2^31 elements; every element checked against slices of the
+    inputs."""
+    import torch
+    p, blk = 2, (1 << 30) + 2049
+    g = torch.Generator(device="cuda").manual_seed(32)
+    send = [torch.randn(p * blk, generator=g, device="cuda").to(torch.bfloat16) for _ in range(p)]
+    recv = [torch.empty(p * blk, dtype=torch.bfloat16, device="cuda") for _ in range(p)]
+    shards = [s[:blk] for s in send]
+    for t in recv:
+        t.fill_(float("nan"))
+    coll.coll_allgather(shards, recv)
+    torch.cuda.synchronize()
+    for r in range(p):
+        for s in range(p):
+            assert torch.equal(_bits(recv[r][s * blk:(s + 1) * blk]), _bits(shards[s])), f"AllGather rank {r} block {s}"
+    for t in recv:
+        t.fill_(float("nan"))
+    coll.coll_alltoall(send, recv, blk)
+    torch.cuda.synchronize()
+    for j in range(p):
+        for i in range(p):
+            assert torch.equal(_bits(recv[j][i * blk:(i + 1) * blk]), _bits(send[i][j * blk:(j + 1) * blk])), \
+                f"All-to-All dest {j} block {i}"
