@@ -94,3 +94,24 @@ def test_allgather_and_alltoall_past_2_31_elements(coll):
         for i in range(p):
             assert torch.equal(_bits(recv[j][i * blk:(i + 1) * blk]), _bits(send[i][j * blk:(j + 1) * blk])), \
                 f"All-to-All dest {j} block {i}"
+
+
+def test_reduce_and_broadcast_past_2_31_elements(coll):
+    """Reduce to root 1 and Broadcast from root 0, p = 2, 2^31 + 4099 bf16
+    elements: the root's sum against torch's bf16 addition (the p = 2 fold)
+    and every receiver against the root's buffer, whole."""
+    import torch
+    p, n = 2, (1 << 31) + 4099
+    g = torch.Generator(device="cuda").manual_seed(33)
+    send = [torch.randn(n, generator=g, device="cuda").to(torch.bfloat16) for _ in range(p)]
+    out = torch.empty(n, dtype=torch.bfloat16, device="cuda").fill_(float("nan"))
+    coll.coll_reduce(send, out, 1, coll.COLL_SUM)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(out), _bits((send[0].float() + send[1].float()).to(torch.bfloat16))), "Reduce"
+    recv = [out, torch.empty(n, dtype=torch.bfloat16, device="cuda")]
+    for t in recv:
+        t.fill_(float("nan"))
+    coll.coll_broadcast(send[0], recv, 0)
+    torch.cuda.synchronize()
+    for r in range(p):
+        assert torch.equal(_bits(recv[r]), _bits(send[0])), f"Broadcast rank {r}"
