@@ -115,3 +115,30 @@ def test_reduce_and_broadcast_past_2_31_elements(coll):
     torch.cuda.synchronize()
     for r in range(p):
         assert torch.equal(_bits(recv[r]), _bits(send[0])), f"Broadcast rank {r}"
+
+
+def test_alltoallv_past_2_31_elements(coll):
+    """Alltoallv, p = 2, 2^31 + 4099 bf16 elements per send buffer, with
+    counts that leave the blocks at differing 16-byte offsets (so both the
+    aligned and the byte-shifted copy paths run) and receive buffers of more
+    than 2^31 elements: every block checked whole against its source."""
+    import torch
+    p, n = 2, (1 << 31) + 4099
+    counts = np.array([[(1 << 30) + 5, (1 << 30) + 4094], [(1 << 30) + 4000, (1 << 30) + 99]], dtype=np.int64)
+    assert (counts.sum(axis=1) == n).all()
+    g = torch.Generator(device="cuda").manual_seed(34)
+    send = [torch.randn(n, generator=g, device="cuda").to(torch.bfloat16) for _ in range(p)]
+    cols = counts.sum(axis=0)
+    recv = [torch.empty(int(c), dtype=torch.bfloat16, device="cuda").fill_(float("nan")) for c in cols]
+    cdev = torch.from_numpy(counts.reshape(-1).copy()).cuda()
+    status = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    coll.coll_alltoallv(send, recv, cdev, status_dev=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    for j in range(p):
+        ro = 0
+        for i in range(p):
+            so = int(counts[i, :j].sum())
+            c = int(counts[i, j])
+            assert torch.equal(_bits(recv[j][ro:ro + c]), _bits(send[i][so:so + c])), f"Alltoallv {i} -> {j}"
+            ro += c
