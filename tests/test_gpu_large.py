@@ -142,3 +142,23 @@ def test_alltoallv_past_2_31_elements(coll):
             c = int(counts[i, j])
             assert torch.equal(_bits(recv[j][ro:ro + c]), _bits(send[i][so:so + c])), f"Alltoallv {i} -> {j}"
             ro += c
+
+
+def test_gather_and_scatter_past_2_31_elements(coll):
+    """Gather to root 1 and Scatter from root 0, p = 2, blocks of 2^30 + 2049
+    bf16 elements: the root buffer holds more than 2^31 elements; every
+    block checked whole."""
+    import torch
+    p, blk = 2, (1 << 30) + 2049
+    g = torch.Generator(device="cuda").manual_seed(35)
+    ranks = [torch.randn(blk, generator=g, device="cuda").to(torch.bfloat16) for _ in range(p)]
+    root_buf = torch.empty(p * blk, dtype=torch.bfloat16, device="cuda").fill_(float("nan"))
+    coll.coll_gather(ranks, root_buf, 1)
+    torch.cuda.synchronize()
+    for r in range(p):
+        assert torch.equal(_bits(root_buf[r * blk:(r + 1) * blk]), _bits(ranks[r])), f"Gather block {r}"
+    out = [torch.empty(blk, dtype=torch.bfloat16, device="cuda").fill_(float("nan")) for _ in range(p)]
+    coll.coll_scatter(root_buf, out, 0)
+    torch.cuda.synchronize()
+    for r in range(p):
+        assert torch.equal(_bits(out[r]), _bits(ranks[r])), f"Scatter rank {r}"
